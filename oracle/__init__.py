@@ -1,0 +1,9 @@
+"""fp64 CPU oracle of the sampling-transform scoring core (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may use this package; the HIP library never does.
+"""
+from .stce_oracle import (  # noqa: F401
+    MARGIN, backward, canonical_f32, chunk_logits, dlogits, forward, in_support,
+    order_keys, order_row, sample_targets, scale_logits, support, support_row,
+)

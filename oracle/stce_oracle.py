@@ -1,0 +1,324 @@
+"""Plain fp64 CPU oracle of the sampling-transform scoring core.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (``sampling_transform_logprob_amd``) and imports nothing from it.
+
+What it computes, and where each step comes from
+------------------------------------------------
+Sources are the text of the web pages this project was built from:
+
+* [xorl#74] -- togethercomputer/xorl pull request 74, "Consolidate
+  sampling-transform scoring on one shared chunked core; implement
+  top-k/top-p/min-p replay for generic ce_modes".
+* [align-v2] -- viai957/align, "align architecture v2: proposal",
+  section 5.4 A ("Fused head + policy-gradient token loss").
+* [nested-learning] -- nested-learning 0.2.0, ``nested_learning/training.py``,
+  function ``compute_teach_signal`` (closed-form cross-entropy gradient).
+
+The pipeline per scored row t (a token of a replayed rollout):
+
+1. logits ``z = h W^T``                         ([xorl#74] "What this PR does" 2:
+   chunked projection; [align-v2] 5.4 A: logits kept in fp32, not rounded
+   to bf16).  Here: exact fp64 product of the (bf16 or fp32) operands.
+2. temperature first: keys ``s = fl32(fl32(z) / T_t)``, per row, after the
+   projection ([xorl#74] "What this PR does" 1, "temperature-first"; the
+   self-review pass documents the per-row post-GEMM convention).  fp64 has
+   53 >= 2*24+2 bits, so rounding the fp64 quotient of two fp32 numbers to
+   fp32 gives the correctly rounded fp32 quotient.
+3. the support program on the fp32 keys ([xorl#74] "What this PR does" 1):
+   order by key descending with the lower token id first among equal keys
+   (stable token-id tie-break); top-k keeps the first k; top-p keeps the
+   shortest prefix whose mass reaches p of the full-row mass, the crossing
+   token included; min-p keeps tokens whose probability is at least min_p
+   times that of the row maximum taken BEFORE any filter; top_p == 1 is the
+   identity and never looks at a running sum.  The three filters are read as
+   one joint intersection on the single temperature-scaled, unfiltered
+   distribution (each is a prefix of the same order; the support is the
+   shortest of the three prefixes).  Decision arithmetic is fp64 on the fp32
+   keys.
+4. selected logprob on the filtered support, clamped to <= 0 (self-review
+   pass of [xorl#74]); a target outside the support scores -inf and gets an
+   exactly zero gradient ([xorl#74] "What this PR does" 4).
+5. closed-form VJP ([xorl#74] "What this PR does" 2: recompute closed-form
+   VJP; [nested-learning] ``compute_teach_signal``; [align-v2] 5.4 A sign
+   convention): ``d logprob / d z_j = (1[j = y] - q_j) / T`` with ``q`` the
+   softmax of ``z / T`` restricted to the support, then ``dH = dz W`` and
+   ``dW = dz^T h``.
+
+Values (logprob, gradients) use the unrounded fp64 logits ``u = z / T``.
+Support decisions use only the fp32 keys, so a caller may pass the keys of
+another implementation (``keys=``) to compare supports bit for bit.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+_SIGN = np.uint32(0x80000000)
+
+# Relative margin under which a top-p or min-p decision is reported as
+# "within rounding" (several answers are then defensible).
+MARGIN = 1e-12
+
+
+# --------------------------------------------------------------------------
+# keys
+# --------------------------------------------------------------------------
+def canonical_f32(s32: np.ndarray) -> np.ndarray:
+    """fp32 copy with -0.0 replaced by +0.0 (the two compare equal)."""
+    s = np.array(s32, dtype=np.float32, copy=True)
+    s[s == 0] = np.float32(0.0)
+    return s
+
+
+def order_keys(s32: np.ndarray) -> np.ndarray:
+    """Order-preserving uint32 image of finite fp32 values (-0 -> +0).
+
+    A larger float maps to a larger unsigned key: negative floats have their
+    bits inverted, non-negative floats get the sign bit set.
+    """
+    s = canonical_f32(s32)
+    assert np.all(np.isfinite(s)), "oracle inputs must be finite"
+    b = s.view(np.uint32)
+    return np.where(b & _SIGN, ~b, b | _SIGN).astype(np.uint32)
+
+
+def scale_logits(z: np.ndarray, temperature: np.ndarray) -> np.ndarray:
+    """Keys ``fl32(fl32(z) / T)`` per row (temperature first, post-projection)."""
+    z32 = np.asarray(z, dtype=np.float64).astype(np.float32)
+    t = np.asarray(temperature, dtype=np.float32).astype(np.float64)
+    q = z32.astype(np.float64) / t[:, None]
+    return canonical_f32(q.astype(np.float32))
+
+
+def chunk_logits(h: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """``z = h W^T`` in fp64 (the operands are widened exactly)."""
+    return np.asarray(h, dtype=np.float64) @ np.asarray(W, dtype=np.float64).T
+
+
+# --------------------------------------------------------------------------
+# support program (one row)
+# --------------------------------------------------------------------------
+def order_row(s_row: np.ndarray) -> np.ndarray:
+    """Permutation pi: key descending, lower token id first among equal keys."""
+    s = canonical_f32(s_row).astype(np.float64)
+    ids = np.arange(s.shape[0])
+    return np.lexsort((ids, -s))
+
+
+def support_row(s_row: np.ndarray, top_k: int, top_p: float, min_p: float) -> dict:
+    """Support of one row of fp32 keys.
+
+    Returns a dict with the support size ``n``, the boundary token (the last
+    token of the support in order pi) as ``id_thr`` with its key ``key_thr``,
+    the per-filter prefix lengths, the fp64 decision masses and a flag
+    ``near`` set when a binding top-p / min-p decision lies within ``MARGIN``
+    (relative) of flipping.
+    """
+    s = canonical_f32(s_row)
+    V = s.shape[0]
+    s64 = s.astype(np.float64)
+    pi = order_row(s)
+    m = s64[pi[0]]                       # row maximum before any filter
+    w = np.exp(s64[pi] - m)              # decision masses, in order pi
+    cum = np.cumsum(w)
+    Z = cum[-1]
+    k = int(top_k)
+    p = float(np.float32(top_p))
+    mp = float(np.float32(min_p))
+    if k < 0:
+        raise ValueError("top_k must be >= 0")
+    if not (0.0 < p <= 1.0):
+        raise ValueError("top_p must be in (0, 1]")
+    if not (0.0 <= mp <= 1.0):
+        raise ValueError("min_p must be in [0, 1]")
+
+    n_k = k if 0 < k < V else V
+
+    near_p = False
+    if p < 1.0:
+        target = p * Z
+        hit = np.nonzero(cum >= target)[0]
+        r = int(hit[0]) if hit.size else V - 1
+        n_p = r + 1
+        before = cum[r - 1] if r > 0 else 0.0
+        near_p = min(abs(cum[r] - target), abs(target - before)) < MARGIN * Z
+    else:
+        n_p = V                          # identity: no running sum at all
+
+    near_m = False
+    if mp > 0.0:
+        thr = math.log(mp)
+        gap = s64[pi] - m                # <= 0, non-increasing along pi
+        n_m = int(np.count_nonzero(gap >= thr))
+        # ln(1) = 0 is exact everywhere; any other threshold carries the
+        # rounding of the logarithm.
+        scale = MARGIN * max(1.0, abs(thr)) if thr != 0.0 else 0.0
+        if n_m > 0 and abs(gap[n_m - 1] - thr) < scale:
+            near_m = True
+        if n_m < V and abs(gap[n_m] - thr) < scale:
+            near_m = True
+    else:
+        n_m = V
+
+    n = min(n_k, n_p, n_m)
+    b = int(pi[n - 1])
+    near = (near_p and n_p <= min(n_k, n_m) + 1) or (near_m and n_m <= min(n_k, n_p) + 1)
+    return dict(
+        n=n, id_thr=b, key_thr=int(order_keys(s[b:b + 1])[0]),
+        n_k=n_k, n_p=n_p, n_m=n_m, pi=pi, m=m, Z=Z, mass=cum[n - 1], near=bool(near),
+    )
+
+
+def support(keys: np.ndarray, top_k, top_p, min_p) -> dict:
+    """Row-wise support of a [R, V] fp32 key matrix.
+
+    ``top_k``/``top_p``/``min_p`` are per-row arrays (or None for "off").
+    Returns arrays ``n``, ``key_thr``, ``id_thr`` (uint32/int64), ``near``.
+    """
+    keys = np.asarray(keys, dtype=np.float32)
+    R = keys.shape[0]
+    tk, tp, mp = _meta(R, top_k, top_p, min_p)
+    n = np.zeros(R, np.int64)
+    kt = np.zeros(R, np.uint32)
+    it = np.zeros(R, np.int64)
+    near = np.zeros(R, bool)
+    for r in range(R):
+        d = support_row(keys[r], tk[r], tp[r], mp[r])
+        n[r], kt[r], it[r], near[r] = d["n"], d["key_thr"], d["id_thr"], d["near"]
+    return dict(n=n, key_thr=kt, id_thr=it, near=near)
+
+
+def in_support(keys_row: np.ndarray, key_thr: int, id_thr: int) -> np.ndarray:
+    """Membership mask from a boundary: key above it, or equal key and id <= it."""
+    k = order_keys(keys_row).astype(np.int64)
+    ids = np.arange(k.shape[0])
+    return (k > key_thr) | ((k == key_thr) & (ids <= id_thr))
+
+
+def _meta(R, top_k, top_p, min_p):
+    tk = np.zeros(R, np.int64) if top_k is None else np.asarray(top_k, np.int64)
+    tp = np.ones(R, np.float32) if top_p is None else np.asarray(top_p, np.float32)
+    mp = np.zeros(R, np.float32) if min_p is None else np.asarray(min_p, np.float32)
+    assert tk.shape == (R,) and tp.shape == (R,) and mp.shape == (R,)
+    return tk, tp, mp
+
+
+# --------------------------------------------------------------------------
+# forward and backward
+# --------------------------------------------------------------------------
+def forward(h, W, target, temperature=None, top_k=None, top_p=None, min_p=None,
+            keys=None, rows=None) -> dict:
+    """Selected logprob on the filtered support, per row.
+
+    ``h`` [T, H] and ``W`` [V, H] hold the operand values (bf16 or fp32 values,
+    any float dtype); ``target`` [T] token ids; metadata per row or None.
+    ``keys`` optionally supplies the fp32 keys [len(rows), V] the supports are
+    decided on (default: this oracle's own keys).  ``rows`` restricts the
+    computation to a subset of rows (all by default).
+
+    Returns per selected row: ``logprob`` (fp64, -inf out of support),
+    ``lse`` (log-sum-exp of z/T over the support), ``n``, ``key_thr``,
+    ``id_thr``, ``in_support``, ``near``, and the keys used.
+    """
+    h = np.asarray(h)
+    T = h.shape[0]
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    temp = np.ones(T, np.float32) if temperature is None else np.asarray(temperature, np.float32)
+    tk, tp, mp = _meta(T, top_k, top_p, min_p)
+    _check_temperature(temp[rows])
+    z = chunk_logits(h[rows], W)                              # fp64 [R, V]
+    s32 = scale_logits(z, temp[rows]) if keys is None else canonical_f32(keys)
+    u = z / temp[rows].astype(np.float64)[:, None]            # values: fp64
+    R, V = z.shape
+    tgt = np.asarray(target, np.int64)[rows]
+    assert np.all((tgt >= 0) & (tgt < V)), "targets must lie in [0, V)"
+    out = dict(logprob=np.empty(R), lse=np.empty(R), n=np.empty(R, np.int64),
+               key_thr=np.empty(R, np.uint32), id_thr=np.empty(R, np.int64),
+               in_support=np.empty(R, bool), near=np.empty(R, bool), keys=s32,
+               rows=rows)
+    for i, t in enumerate(rows):
+        d = support_row(s32[i], tk[t], tp[t], mp[t])
+        S = d["pi"][: d["n"]]
+        mx = u[i, S].max()
+        lse = mx + math.log(np.exp(u[i, S] - mx).sum())
+        inside = bool(np.isin(tgt[i], S))
+        lp = min(u[i, tgt[i]] - lse, 0.0) if inside else -math.inf
+        out["logprob"][i] = lp
+        out["lse"][i] = lse
+        out["n"][i] = d["n"]
+        out["key_thr"][i] = d["key_thr"]
+        out["id_thr"][i] = d["id_thr"]
+        out["in_support"][i] = inside
+        out["near"][i] = d["near"]
+    return out
+
+
+def dlogits(h, W, target, fwd: dict, grad_logprob, temperature=None) -> np.ndarray:
+    """``dz[r, j] = g_r (1[j = y_r] - q_rj) / T_r`` on the rows of ``fwd``.
+
+    ``q`` is the softmax of ``z / T`` restricted to the support.  Rows whose
+    target is out of support get an exactly zero row whatever ``g`` is.
+    """
+    rows = fwd["rows"]
+    T = np.asarray(h).shape[0]
+    temp = np.ones(T, np.float32) if temperature is None else np.asarray(temperature, np.float32)
+    z = chunk_logits(np.asarray(h)[rows], W)
+    t64 = temp[rows].astype(np.float64)
+    u = z / t64[:, None]
+    g = np.asarray(grad_logprob, np.float64)[rows]
+    tgt = np.asarray(target, np.int64)[rows]
+    dz = np.zeros_like(z)
+    for i in range(len(rows)):
+        if not fwd["in_support"][i]:
+            continue
+        mask = in_support(fwd["keys"][i], int(fwd["key_thr"][i]), int(fwd["id_thr"][i]))
+        q = np.where(mask, np.exp(u[i] - fwd["lse"][i]), 0.0)
+        onehot = np.zeros_like(q)
+        onehot[tgt[i]] = 1.0
+        dz[i] = g[i] * (onehot - q) / t64[i]
+    return dz
+
+
+def backward(h, W, target, fwd: dict, grad_logprob, temperature=None):
+    """VJP of ``sum_r g_r * logprob_r`` with respect to ``h`` and ``W``.
+
+    Returns ``(dH, dW)``: ``dH`` [len(rows), H] for the rows of ``fwd`` and
+    ``dW`` [V, H] summed over those rows.
+    """
+    dz = dlogits(h, W, target, fwd, grad_logprob, temperature)
+    h64 = np.asarray(h, dtype=np.float64)[fwd["rows"]]
+    W64 = np.asarray(W, dtype=np.float64)
+    return dz @ W64, dz.T @ h64
+
+
+def sample_targets(h, W, temperature, top_k, top_p, min_p, u) -> np.ndarray:
+    """Draw one target per row from its filtered distribution.
+
+    Inverse CDF along the order pi over ``q`` (softmax of z/T on the
+    support), with the caller's uniforms ``u`` in [0, 1).
+    """
+    T = np.asarray(h).shape[0]
+    temp = np.ones(T, np.float32) if temperature is None else np.asarray(temperature, np.float32)
+    tk, tp, mp = _meta(T, top_k, top_p, min_p)
+    z = chunk_logits(h, W)
+    s32 = scale_logits(z, temp)
+    uu = z / temp.astype(np.float64)[:, None]
+    out = np.empty(T, np.int64)
+    for t in range(T):
+        d = support_row(s32[t], tk[t], tp[t], mp[t])
+        S = d["pi"][: d["n"]]
+        w = np.exp(uu[t, S] - uu[t, S].max())
+        cdf = np.cumsum(w)
+        i = int(np.searchsorted(cdf, float(u[t]) * cdf[-1], side="right"))
+        out[t] = S[min(i, len(S) - 1)]
+    return out
+
+
+def _check_temperature(t):
+    t = np.asarray(t, np.float32)
+    if not np.all(np.isfinite(t) & (t > 0)):
+        raise ValueError("temperature must be finite and > 0")

@@ -1,0 +1,69 @@
+"""Plant plausible mistakes in a copy of the oracle and check a pin fails.
+
+Each mutant is the oracle's own source with one textual change, loaded as a
+separate module on the CPU; the pin tests of ``test_oracle_pins`` are then
+run against it.  A pin set that lets a mutant pass would not have caught
+that mistake in the real oracle.
+"""
+import importlib.util
+import os
+import types
+
+import numpy as np
+import pytest
+
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "stce_oracle.py")
+
+MUTANTS = {
+    "tie-break by descending id": ("np.lexsort((ids, -s))", "np.lexsort((-ids, -s))",
+                                   ["test_order_matches_pairwise_definition"]),
+    "top-p drops the crossing token": ("n_p = r + 1", "n_p = max(r, 1)",
+                                       ["test_top_p_includes_crossing_token"]),
+    "min-p compared in the wrong space": ("thr = math.log(mp)", "thr = -mp",
+                                          ["test_min_p_closed_form_matches_probability_space"]),
+    "temperature by reciprocal multiply": ("q = z32.astype(np.float64) / t[:, None]",
+                                           "q = z32 * (np.float32(1) / t.astype(np.float32))[:, None]",
+                                           ["test_temperature_division_is_correctly_rounded"]),
+    "gradient misses the 1/T factor": ("dz[i] = g[i] * (onehot - q) / t64[i]", "dz[i] = g[i] * (onehot - q)",
+                                       ["test_gradients_match_central_differences"]),
+    "gradient sign flipped": ("dz[i] = g[i] * (onehot - q) / t64[i]", "dz[i] = g[i] * (q - onehot) / t64[i]",
+                              ["test_gradients_match_torch_autograd", "test_loss_sign_convention"]),
+    "lse over the unfiltered row": ("lse = mx + math.log(np.exp(u[i, S] - mx).sum())",
+                                    "lse = u[i].max() + math.log(np.exp(u[i] - u[i].max()).sum())",
+                                    ["test_filtered_logprob_closed_form"]),
+    "out-of-support rows keep a gradient": ("        if not fwd[\"in_support\"][i]:\n            continue\n", "",
+                                            ["test_out_of_support_has_minus_inf_and_zero_gradient"]),
+    "top-k keeps one token too many": ("n_k = k if 0 < k < V else V", "n_k = min(k + 1, V) if 0 < k < V else V",
+                                       ["test_support_matches_brute_force", "test_tie_group_split_by_token_id"]),
+    "min-p against the second-largest key": ("gap = s64[pi] - m ", "gap = s64[pi] - s64[pi[min(1, V - 1)]] ",
+                                             ["test_min_p_one_keeps_the_whole_max_tie_group",
+                                              "test_min_p_closed_form_matches_probability_space"]),
+    "dW uses the wrong operand": ("return dz @ W64, dz.T @ h64", "return dz @ W64, dz.T @ (h64 * 0.5)",
+                                  ["test_gradients_match_central_differences"]),
+}
+
+
+def _load_mutant(old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, monkeypatch):
+    old, new, tests = MUTANTS[name]
+    mutant = _load_mutant(old, new)
+    monkeypatch.setattr(pins, "oracle", mutant)
+    caught = []
+    for t in tests:
+        rng = np.random.Generator(np.random.PCG64(20261203))
+        fn = getattr(pins, t)
+        try:
+            fn(rng) if fn.__code__.co_argcount else fn()
+        except Exception:  # noqa: BLE001 -- any failure of the pin counts
+            caught.append(t)
+    assert caught, f"mutant '{name}' survived {tests}"

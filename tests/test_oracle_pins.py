@@ -1,0 +1,415 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: exact
+rational arithmetic, brute force on tiny rows, closed forms, a textbook
+library routine (log_softmax, autograd), central finite differences and
+invariants.  The rules come from xorl pull request 74 ("What this PR does"
+item 1: temperature first, stable token-id tie-break, inclusive top-p
+crossing, min-p against the original row maximum, top_p == 1 as the exact
+identity; item 4: out-of-support targets score -inf with zero gradient;
+self-review pass: logprob clamped to <= 0, per-row post-projection
+temperature) and from align "architecture v2: proposal" 5.4 A (gradient
+``softmax - onehot`` and its sign).
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+# ---------------------------------------------------------------- keys
+def test_order_keys_preserve_float_order(rng):
+    vals = np.concatenate([
+        rng.standard_normal(2000).astype(np.float32) * 50,
+        np.array([0.0, -0.0, 1e-45, -1e-45, 3.4e38, -3.4e38, 1.0, -1.0], np.float32),
+    ])
+    keys = oracle.order_keys(vals).astype(np.int64)
+    for _ in range(5000):
+        i, j = rng.integers(0, len(vals), 2)
+        a, b = float(vals[i]), float(vals[j])
+        assert (a < b) == (keys[i] < keys[j]) and (a == b) == (keys[i] == keys[j])
+    assert oracle.order_keys(np.array([-0.0], np.float32))[0] == oracle.order_keys(np.array([0.0], np.float32))[0]
+
+
+def _f32_round_exact(q: Fraction) -> np.float32:
+    """Correct rounding of an exact rational to fp32, ties to even (brute)."""
+    c = np.float32(float(q))
+    best = None
+    for cand in (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))):
+        err = abs(Fraction(float(cand)) - q)
+        even = (cand.view(np.uint32) & 1) == 0
+        if best is None or err < best[0] or (err == best[0] and even):
+            best = (err, cand)
+    return best[1]
+
+
+def test_temperature_division_is_correctly_rounded(rng):
+    z = (rng.standard_normal(3000) * 10).astype(np.float32)
+    t = rng.uniform(0.05, 3.0, 3000).astype(np.float32)
+    s = oracle.scale_logits(z[:, None].astype(np.float64), t)[:, 0]
+    for i in range(len(z)):
+        want = _f32_round_exact(Fraction(float(z[i])) / Fraction(float(t[i])))
+        if want == 0:
+            want = np.float32(0.0)
+        assert s[i].view(np.uint32) == want.view(np.uint32), (z[i], t[i])
+
+
+def test_temperature_one_is_exact(rng):
+    z = (rng.standard_normal((3, 50)) * 7).astype(np.float32).astype(np.float64)
+    s = oracle.scale_logits(z, np.ones(3, np.float32))
+    assert np.array_equal(s, oracle.canonical_f32(z.astype(np.float32)))
+
+
+def test_projection_is_exact_on_small_integers(rng):
+    h = rng.integers(-9, 10, (3, 7)).astype(np.float32)
+    W = rng.integers(-9, 10, (5, 7)).astype(np.float32)
+    z = oracle.chunk_logits(h, W)
+    for t in range(3):
+        for j in range(5):
+            assert z[t, j] == sum(int(h[t, c]) * int(W[j, c]) for c in range(7))
+
+
+# ---------------------------------------------------------------- order and support, brute force
+def _precedes(s, i, j):
+    return s[i] > s[j] or (s[i] == s[j] and i < j)
+
+
+def _brute_order(s):
+    V = len(s)
+    rank = [sum(_precedes(s, j, i) for j in range(V)) for i in range(V)]
+    out = [0] * V
+    for i, r in enumerate(rank):
+        out[r] = i
+    return out
+
+
+def _brute_support(s32, k, p, mp):
+    """Support by definition, written without sorting or running sums."""
+    s = [float(x) for x in oracle.canonical_f32(s32)]
+    V = len(s)
+    order = _brute_order(s)
+    m = max(s)
+    w = [math.exp(x - m) for x in s]
+    Z = math.fsum(w)
+    sizes = [V]
+    if 0 < k < V:
+        sizes.append(k)
+    if p < 1:
+        for n in range(1, V + 1):                       # shortest prefix reaching p of the mass
+            if math.fsum(w[order[r]] for r in range(n)) >= float(np.float32(p)) * Z:
+                sizes.append(n)
+                break
+    if mp > 0:
+        keep = [i for i in range(V) if s[i] - m >= math.log(float(np.float32(mp)))]
+        assert set(keep) == set(order[:len(keep)])      # min-p keeps a prefix
+        sizes.append(len(keep))
+    n = min(sizes)
+    return n, order[n - 1]
+
+
+def test_order_matches_pairwise_definition(rng):
+    for _ in range(200):
+        V = int(rng.integers(1, 12))
+        s = rng.integers(-3, 4, V).astype(np.float32) * np.float32(0.5)   # many ties
+        assert list(oracle.order_row(s)) == _brute_order([float(x) for x in s])
+
+
+def test_support_matches_brute_force(rng):
+    checked = 0
+    for _ in range(600):
+        V = int(rng.integers(1, 11))
+        s = (rng.standard_normal(V) * 2).astype(np.float32)
+        if rng.random() < 0.3:
+            s = np.round(s).astype(np.float32)                      # ties
+        k = int(rng.choice([0, 1, 2, 3, V, V + 3]))
+        p = float(rng.choice([1.0, 0.3, 0.6, 0.9, 0.99]))
+        mp = float(rng.choice([0.0, 0.05, 0.3, 0.9, 1.0]))
+        d = oracle.support_row(s, k, p, mp)
+        if d["near"]:
+            continue
+        n, b = _brute_support(s, k, p, mp)
+        assert (d["n"], d["id_thr"]) == (n, b), (s, k, p, mp)
+        checked += 1
+    assert checked > 500
+
+
+# ---------------------------------------------------------------- rules, closed forms
+def test_top_k_one_is_lowest_argmax_and_logprob_zero():
+    s = np.array([1.0, 3.0, 3.0, -2.0], np.float32)
+    d = oracle.support_row(s, 1, 1.0, 0.0)
+    assert d["n"] == 1 and d["id_thr"] == int(np.argmax(s)) == 1
+    h = np.ones((1, 4), np.float32)                   # z = h W^T = s
+    W = np.diag(s).astype(np.float32)
+    f = oracle.forward(h, W, np.array([1]), top_k=np.array([1]))
+    assert f["logprob"][0] == 0.0 and f["n"][0] == 1
+
+
+def test_top_k_at_least_vocab_is_identity(rng):
+    s = (rng.standard_normal(37) * 3).astype(np.float32)
+    ref = oracle.support_row(s, 0, 1.0, 0.0)
+    for k in (37, 38, 1000):
+        d = oracle.support_row(s, k, 1.0, 0.0)
+        assert (d["n"], d["id_thr"]) == (ref["n"], ref["id_thr"]) == (37, ref["pi"][-1])
+
+
+def test_tie_group_split_by_token_id():
+    # keys: 5 at ids 0 and 4; 2 at ids 1, 2, 6; 0 at 3 and 5
+    s = np.array([5, 2, 2, 0, 5, 0, 2], np.float32)
+    d = oracle.support_row(s, 3, 1.0, 0.0)           # {0, 4} then the lowest id of the 2-group
+    assert d["n"] == 3 and d["id_thr"] == 1
+    mask = oracle.in_support(s, d["key_thr"], d["id_thr"])
+    assert set(np.nonzero(mask)[0]) == {0, 4, 1}
+
+
+def test_top_p_includes_crossing_token():
+    prob = np.array([0.5, 0.3, 0.2])
+    s = np.log(prob).astype(np.float32)
+    # masses before each token: 0, 0.5, 0.8 (up to rounding of the keys)
+    assert oracle.support_row(s, 0, 0.45, 0.0)["n"] == 1
+    assert oracle.support_row(s, 0, 0.55, 0.0)["n"] == 2     # token 1 crosses 0.55: kept
+    assert oracle.support_row(s, 0, 0.79, 0.0)["n"] == 2
+    assert oracle.support_row(s, 0, 0.85, 0.0)["n"] == 3
+
+
+def _overshoot_row():
+    """A row whose fp32 running sum of fp32 softmax probabilities (in order)
+    reaches 1.0 before its last token: a running-sum test with p = 1 would
+    drop the tail."""
+    g = np.random.Generator(np.random.PCG64(7))
+    while True:
+        V = int(g.integers(3, 300))
+        s = (g.standard_normal(V) * g.uniform(0.1, 3)).astype(np.float32)
+        e = np.exp(s - s.max()).astype(np.float32)
+        q = np.sort(e / e.sum(dtype=np.float32))[::-1].astype(np.float32)
+        c = np.cumsum(q, dtype=np.float32)
+        hit = np.nonzero(c >= np.float32(1.0))[0]
+        if hit.size and hit[0] < V - 2:
+            return s
+
+
+def test_top_p_one_is_full_support_despite_fp32_overshoot():
+    s = _overshoot_row()
+    V = len(s)
+    d = oracle.support_row(s, 0, 1.0, 0.0)
+    assert d["n"] == V and d["id_thr"] == int(oracle.order_row(s)[-1])
+
+
+def test_min_p_closed_form_matches_probability_space(rng):
+    from scipy.special import softmax
+    for _ in range(200):
+        V = int(rng.integers(2, 300))
+        s = (rng.standard_normal(V) * 2).astype(np.float32)
+        mp = float(np.float32(rng.choice([0.01, 0.1, 0.5, 0.9])))
+        d = oracle.support_row(s, 0, 1.0, mp)
+        if d["near"]:
+            continue
+        prob = softmax(s.astype(np.float64))
+        assert d["n"] == int(np.count_nonzero(prob >= mp * prob.max() * (1 - 1e-13)))
+
+
+def test_min_p_one_keeps_the_whole_max_tie_group():
+    s = np.array([1.0, 4.0, 2.0, 4.0, 4.0], np.float32)
+    d = oracle.support_row(s, 0, 1.0, 1.0)
+    assert d["n"] == 3 and d["id_thr"] == 4
+
+
+def test_min_p_never_splits_a_tie_group(rng):
+    for _ in range(100):
+        V = 40
+        s = rng.integers(-4, 4, V).astype(np.float32)
+        d = oracle.support_row(s, 0, 1.0, float(np.float32(np.exp(-rng.uniform(0, 6)))))
+        kept = oracle.in_support(s, d["key_thr"], d["id_thr"])
+        for val in np.unique(s):
+            grp = kept[s == val]
+            assert grp.all() or not grp.any()
+
+
+def test_filters_compose_as_shortest_prefix(rng):
+    for _ in range(300):
+        V = int(rng.integers(2, 60))
+        s = (rng.standard_normal(V) * 2).astype(np.float32)
+        k, p, mp = int(rng.integers(0, V + 2)), float(rng.uniform(0.05, 1.0)), float(rng.uniform(0, 0.5))
+        d = oracle.support_row(s, k, p, mp)
+        parts = [oracle.support_row(s, k, 1.0, 0.0)["n"], oracle.support_row(s, 0, p, 0.0)["n"],
+                 oracle.support_row(s, 0, 1.0, mp)["n"]]
+        assert d["n"] == min(parts)
+
+
+def test_support_invariants(rng):
+    for _ in range(200):
+        V = int(rng.integers(1, 200))
+        s = (rng.standard_normal(V) * rng.uniform(0.1, 5)).astype(np.float32)
+        k, p, mp = int(rng.integers(0, V + 2)), float(rng.uniform(0.01, 1.0)), float(rng.uniform(0, 1))
+        d = oracle.support_row(s, k, p, mp)
+        mask = oracle.in_support(s, d["key_thr"], d["id_thr"])
+        assert mask.sum() == d["n"] >= 1
+        assert mask[int(np.argmax(s))]                            # lowest-id argmax kept
+        assert set(np.nonzero(mask)[0]) == set(d["pi"][: d["n"]])  # a prefix of the order
+        e = np.exp(s.astype(np.float64) - s.max())
+        assert abs((e * mask).sum() / (e * mask).sum() - 1.0) < 1e-12
+        q = np.where(mask, e, 0) / (e * mask).sum()
+        assert abs(q.sum() - 1.0) < 1e-12
+
+
+# ---------------------------------------------------------------- values
+def _problem(rng, T=6, H=16, V=40, scale=1.0):
+    h = rng.standard_normal((T, H)).astype(np.float32)
+    W = (rng.standard_normal((V, H)) * 0.3 * scale).astype(np.float32)
+    temp = rng.uniform(0.5, 1.5, T).astype(np.float32)
+    return h, W, temp
+
+
+def test_identity_rows_equal_log_softmax(rng):
+    from scipy.special import log_softmax
+    h, W, temp = _problem(rng, T=8, V=50)
+    y = rng.integers(0, 50, 8)
+    f = oracle.forward(h, W, y, temp)
+    z = h.astype(np.float64) @ W.astype(np.float64).T
+    ref = log_softmax(z / temp.astype(np.float64)[:, None], axis=1)[np.arange(8), y]
+    np.testing.assert_allclose(f["logprob"], np.minimum(ref, 0), rtol=0, atol=1e-13)
+    assert np.all(f["n"] == 50)
+
+
+def test_filtered_logprob_closed_form():
+    # z/T = [3, 1, 1, 0, -2] with T = 1, top-k 2 keeps ids {0, 1}
+    s = np.array([3.0, 1.0, 1.0, 0.0, -2.0])
+    h = np.ones((1, 1), np.float32)
+    W = s[:, None].astype(np.float32)
+    f = oracle.forward(h, W, np.array([1]), top_k=np.array([2]))
+    assert f["n"][0] == 2 and f["id_thr"][0] == 1
+    assert abs(f["logprob"][0] - (-math.log1p(math.exp(2.0)))) < 1e-14
+    # target 2 ties target 1 but loses the id tie-break: out of support
+    f = oracle.forward(h, W, np.array([2]), top_k=np.array([2]))
+    assert f["logprob"][0] == -math.inf and not f["in_support"][0]
+    # temperature 2 then min-p 0.5: keep s/T - max >= ln 0.5, i.e. z >= 3 - 2 ln 2 = 1.61
+    f = oracle.forward(h, W, np.array([0]), np.array([2.0], np.float32), min_p=np.array([0.5]))
+    assert f["n"][0] == 1 and f["logprob"][0] == 0.0
+
+
+def test_out_of_support_has_minus_inf_and_zero_gradient(rng):
+    h, W, temp = _problem(rng, T=4, V=30, scale=3)
+    f0 = oracle.forward(h, W, np.zeros(4, np.int64), temp, top_k=np.full(4, 3))
+    order = [oracle.order_row(f0["keys"][t]) for t in range(4)]
+    y = np.array([order[t][-1] for t in range(4)])             # last token: never in a top-3
+    f = oracle.forward(h, W, y, temp, top_k=np.full(4, 3))
+    assert np.all(f["logprob"] == -np.inf)
+    dH, dW = oracle.backward(h, W, y, f, np.full(4, 7.0), temp)
+    assert not dH.any() and not dW.any()
+
+
+def test_logprob_is_clamped_nonpositive(rng):
+    h, W, temp = _problem(rng, T=10, V=20, scale=4)
+    f = oracle.forward(h, W, rng.integers(0, 20, 10), temp, top_k=np.ones(10, np.int64))
+    assert np.all((f["logprob"] <= 0) | np.isinf(f["logprob"]))
+
+
+# ---------------------------------------------------------------- gradients
+def _loss(h, W, y, temp, meta, g, support_of):
+    """sum_t g_t logprob_t with each row's support frozen to ``support_of``."""
+    z = h @ W.T
+    u = z / temp[:, None]
+    tot = 0.0
+    for t in range(len(y)):
+        S = support_of[t]
+        mx = u[t, S].max()
+        tot += g[t] * (u[t, y[t]] - (mx + math.log(np.exp(u[t, S] - mx).sum())))
+    return tot
+
+
+def test_gradients_match_central_differences(rng):
+    T, H, V = 4, 8, 12
+    h, W, temp = _problem(rng, T, H, V, scale=2)
+    meta = dict(top_k=np.array([0, 5, 0, 3]), top_p=np.array([1.0, 1.0, 0.8, 0.9], np.float32),
+                min_p=np.array([0.0, 0.0, 0.0, 0.05], np.float32))
+    f0 = oracle.forward(h, W, np.zeros(T, np.int64), temp, **meta)
+    y = np.array([f0["keys"][t].argmax() for t in range(T)])
+    f = oracle.forward(h, W, y, temp, **meta)
+    assert f["in_support"].all()
+    S = [oracle.order_row(f["keys"][t])[: f["n"][t]] for t in range(T)]
+    g = rng.standard_normal(T)
+    dH, dW = oracle.backward(h, W, y, f, g, temp)
+    h64, W64, t64 = h.astype(np.float64), W.astype(np.float64), temp.astype(np.float64)
+    eps = 1e-6
+    for (arr, grad) in ((h64, dH), (W64, dW)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + eps
+            fp = _loss(h64, W64, y, t64, meta, g, S)
+            arr[idx] = old - eps
+            fm = _loss(h64, W64, y, t64, meta, g, S)
+            arr[idx] = old
+            num[idx] = (fp - fm) / (2 * eps)
+        rel = np.linalg.norm(num - grad) / np.linalg.norm(grad)
+        assert rel < 1e-6, rel
+    # the supports did not move under the perturbation size used
+    for d in (+eps, -eps):
+        fz = oracle.forward(h + d, W, y, temp, **meta)
+        assert np.array_equal(fz["n"], f["n"])
+
+
+def test_gradients_match_torch_autograd(rng):
+    torch = pytest.importorskip("torch")
+    T, H, V = 5, 12, 30
+    h, W, temp = _problem(rng, T, H, V, scale=2)
+    meta = dict(top_k=np.array([0, 4, 0, 0, 7]), top_p=np.array([1.0, 1.0, 0.7, 1.0, 0.95], np.float32),
+                min_p=np.array([0.0, 0.0, 0.0, 0.2, 0.0], np.float32))
+    f0 = oracle.forward(h, W, np.zeros(T, np.int64), temp, **meta)
+    y = np.array([oracle.order_row(f0["keys"][t])[0] for t in range(T)])
+    f = oracle.forward(h, W, y, temp, **meta)
+    g = rng.standard_normal(T)
+    dH, dW = oracle.backward(h, W, y, f, g, temp)
+    th = torch.tensor(h, dtype=torch.float64, requires_grad=True)
+    tW = torch.tensor(W, dtype=torch.float64, requires_grad=True)
+    u = (th @ tW.T) / torch.tensor(temp, dtype=torch.float64)[:, None]
+    L = 0
+    for t in range(T):
+        S = torch.tensor(oracle.order_row(f["keys"][t])[: f["n"][t]])
+        L = L + float(g[t]) * (u[t, int(y[t])] - torch.logsumexp(u[t, S], 0))
+    L.backward()
+    np.testing.assert_allclose(dH, th.grad.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dW, tW.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_loss_sign_convention(rng):
+    """The descent direction of the NLL is (q - onehot)/T = -d logprob/dz."""
+    torch = pytest.importorskip("torch")
+    h, W, temp = _problem(rng, 1, 6, 11)
+    y = np.array([3])
+    f = oracle.forward(h, W, y, temp)
+    dz = oracle.dlogits(h, W, y, f, np.array([1.0]), temp)
+    z = torch.tensor(h.astype(np.float64) @ W.astype(np.float64).T, requires_grad=True)
+    nll = -torch.log_softmax(z / float(temp[0]), 1)[0, 3]
+    nll.backward()
+    np.testing.assert_allclose(-dz, z.grad.numpy(), atol=1e-15)
+
+
+def test_weight_gradient_columns_sum_to_zero(rng):
+    h, W, temp = _problem(rng, T=6, V=25, scale=2)
+    f = oracle.forward(h, W, np.zeros(6, np.int64), temp, top_p=np.full(6, 0.9, np.float32))
+    dH, dW = oracle.backward(h, W, np.zeros(6, np.int64), f, rng.standard_normal(6), temp)
+    assert np.abs(dW.sum(axis=0)).max() < 1e-12 * max(1.0, np.abs(dW).max())
+
+
+def test_sampled_targets_lie_in_support(rng):
+    h, W, temp = _problem(rng, T=30, V=64, scale=3)
+    meta = dict(top_k=rng.choice([0, 5], 30), top_p=rng.choice([1.0, 0.7], 30).astype(np.float32),
+                min_p=rng.choice([0.0, 0.1], 30).astype(np.float32))
+    y = oracle.sample_targets(h, W, temp, meta["top_k"], meta["top_p"], meta["min_p"], rng.random(30))
+    f = oracle.forward(h, W, y, temp, **meta)
+    assert f["in_support"].all()
+
+
+def test_bad_metadata_is_rejected():
+    s = np.zeros(4, np.float32)
+    for args in ((-1, 1.0, 0.0), (0, 0.0, 0.0), (0, 1.5, 0.0), (0, 1.0, -0.1), (0, 1.0, 1.5)):
+        with pytest.raises(ValueError):
+            oracle.support_row(s, *args)
+    with pytest.raises(ValueError):
+        oracle.forward(np.ones((1, 2), np.float32), np.ones((3, 2), np.float32), np.array([0]),
+                       np.array([0.0], np.float32))
