@@ -1,0 +1,192 @@
+/*
+ * stce.h -- C ABI of the sampling-transform scoring core for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The library scores replayed rollout tokens: for every row t (one scored
+ * token) it computes the log-probability of the token that was sampled,
+ * target[t], under the sampling program that produced it, and the gradient
+ * of that log-probability with respect to the hidden state and the LM-head
+ * weight.  The method is the one of togethercomputer/xorl pull request 74,
+ * "Consolidate sampling-transform scoring on one shared chunked core;
+ * implement top-k/top-p/min-p replay for generic ce_modes":
+ *
+ *   - "What this PR does" item 2: chunked projection, then temperature, then
+ *     the pinned support program, then the selected logprob; a recompute
+ *     closed-form VJP that keeps only per-row scalars between forward and
+ *     backward, never a [tokens, vocab] activation.
+ *   - item 1: the support program.  Temperature first; keys ordered by value,
+ *     lower token id first among equal values; top-k keeps the first k;
+ *     top-p keeps the shortest prefix whose probability mass reaches top_p,
+ *     the crossing token included; min-p keeps tokens with probability at
+ *     least min_p times that of the row maximum taken before any filter;
+ *     top_p == 1 is the exact identity.  The filters act jointly on the one
+ *     temperature-scaled, unfiltered distribution: each is a prefix of the
+ *     same order and the support is the shortest of the three.
+ *   - item 4: a target outside its row's support scores -inf with an exactly
+ *     zero gradient; one actionable error for an unsupported operand dtype.
+ *   - self-review pass: per-row temperature applied after the projection
+ *     (s = fl32(z / T), correctly rounded); logprob clamped to <= 0;
+ *     over-length metadata rejected, never truncated; weight gradients
+ *     written once per vocabulary slice.
+ *
+ * Logits are computed in fp32 from bf16 (or fp32) operands and are never
+ * rounded to bf16 (align "architecture v2: proposal", section 5.4 A: an fp32
+ * head needs fp32 output, not fp32 compute).  The backward forms
+ * dz = g * (1[j == y] - q) / T with q the softmax on the support, rounds dz
+ * to the operand dtype and runs the two gradient products on it (same
+ * section: bf16 dlogits are what lets the dh product run on the matrix
+ * cores).
+ *
+ * Conventions for every entry point
+ *   - All array pointers are DEVICE pointers on the current HIP device,
+ *     row-major and contiguous, owned by the caller.  The library allocates
+ *     no device memory and keeps none between calls; scratch space is the
+ *     caller's workspace (sizes from stce_workspace_bytes).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  All work is
+ *     enqueued on it; no call synchronizes it, so calls can be captured in
+ *     a HIP graph.
+ *   - Host-detectable errors (NULL required pointers, bad shapes,
+ *     misaligned pointers, a workspace that is too small, an unsupported
+ *     dtype) return a non-zero stce_status BEFORE anything is enqueued and
+ *     write nothing.  stce_last_error() then holds a thread-local message.
+ *   - Per-row value errors (temperature not finite or <= 0, top_k < 0,
+ *     top_p outside (0, 1] or NaN, min_p outside [0, 1] or NaN, target
+ *     outside [0, V)) are found on the device.  Such a row gets a NaN
+ *     logprob and a zero gradient, and *dev_status (if not NULL) receives
+ *     the first bad row: see STCE_STATUS_NONE.
+ *   - Thread-safe: the only global mutable state is the thread-local error
+ *     string.  Calls that share a workspace must be ordered by the caller.
+ */
+#ifndef STCE_H
+#define STCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  STCE_DT_BF16 = 1, /* hidden and weight are bf16 (the fast path) */
+  STCE_DT_F32 = 2   /* hidden and weight are fp32 */
+} stce_dtype;
+
+typedef enum {
+  STCE_OK = 0,
+  STCE_E_ARG = 1,         /* NULL pointer, bad shape, misalignment */
+  STCE_E_UNSUPPORTED = 2, /* operand dtype or shape the library does not run */
+  STCE_E_WORKSPACE = 3,   /* workspace smaller than stce_workspace_bytes */
+  STCE_E_HIP = 4          /* a HIP runtime call failed (kernel launch) */
+} stce_status;
+
+/* dev_status value meaning "no bad row".  Otherwise the value is
+ * (row << 8) | field, field being one of STCE_FIELD_*, for the smallest bad
+ * row (and the smallest field code on that row). */
+#define STCE_STATUS_NONE INT64_MAX
+#define STCE_FIELD_TEMPERATURE 1
+#define STCE_FIELD_TOP_K 2
+#define STCE_FIELD_TOP_P 3
+#define STCE_FIELD_MIN_P 4
+#define STCE_FIELD_TARGET 5
+
+/* Bytes of per-row state stce_forward writes and stce_backward reads. */
+#define STCE_STATE_BYTES_PER_ROW 32
+
+typedef struct stce_problem {
+  int64_t T;             /* rows (scored tokens), >= 1 */
+  int64_t H;             /* hidden size, >= 8, multiple of 8 */
+  int64_t V;             /* vocabulary size, 1 <= V < 2^31 - 256 */
+  int32_t dtype;         /* stce_dtype of hidden and weight */
+  int32_t reserved;      /* must be 0 */
+  const void *hidden;    /* [T, H], dtype; 16-byte aligned */
+  const void *weight;    /* [V, H] (lm_head.weight layout), dtype; 16-byte aligned */
+  const int64_t *target; /* [T] sampled token ids in [0, V) */
+  const float *temperature; /* [T] finite > 0, or NULL = 1.0 for every row */
+  const int32_t *top_k;  /* [T] >= 0; 0 or >= V = off; or NULL = off */
+  const float *top_p;    /* [T] in (0, 1]; 1 = off; or NULL = off */
+  const float *min_p;    /* [T] in [0, 1]; 0 = off; or NULL = off */
+  int64_t chunk_rows;    /* forward rows per chunk; 0 = library default */
+  int64_t vocab_slice;   /* backward vocabulary columns per slice; 0 = default */
+} stce_problem;
+
+/* Per-row state size in bytes for T rows (STCE_STATE_BYTES_PER_ROW * T). */
+size_t stce_state_bytes(int64_t T);
+
+/* Workspace bytes needed by stce_forward (*fwd) and stce_backward (*bwd)
+ * for this problem's shapes, dtype and chunking (pointers are not read).
+ * Either output pointer may be NULL. */
+stce_status stce_workspace_bytes(const stce_problem *prob, size_t *fwd, size_t *bwd);
+
+/* Forward: logprob[t] = min(s[t, y_t] - logsumexp_{j in S_t} s[t, j], 0) if
+ * y_t is in the support S_t, else -inf, with s = fl32(h W^T) / T per row.
+ * Writes logprob [T] fp32 and state [T * 32 bytes] (support boundary,
+ * filtered log-sum-exp, flags) for stce_backward.  dev_status: one int64
+ * (may be NULL).  ws: at least the forward workspace size, 256-byte
+ * aligned. */
+stce_status stce_forward(const stce_problem *prob, float *logprob, void *state,
+                         int64_t *dev_status, void *ws, size_t ws_bytes, void *stream);
+
+/* Backward of sum_t grad_logprob[t] * logprob[t].  Recomputes the logits of
+ * every vocabulary slice bit-for-bit as the forward did, reads the support
+ * from `state`, forms dz = g (1[j == y] - q) / T (zero on rows whose target
+ * is out of support or whose metadata is invalid) and writes
+ *   grad_hidden [T, H] in the hidden dtype (overwritten; NULL = skip) and
+ *   grad_weight [V, H] fp32 (overwritten, or added to when
+ *                accumulate_grad_weight != 0; NULL = skip).
+ * `prob` must describe the same inputs as the forward that wrote `state`
+ * (not checked).  ws: at least the backward workspace size. */
+stce_status stce_backward(const stce_problem *prob, const float *grad_logprob, const void *state,
+                          void *grad_hidden, float *grad_weight, int32_t accumulate_grad_weight,
+                          int64_t *dev_status, void *ws, size_t ws_bytes, void *stream);
+
+/* Parity entry: the fp32 keys s = fl32(h W^T) / T of rows [row0, row0 +
+ * nrows), written to s_out [nrows, V], produced by the same projection
+ * kernel and temperature step as stce_forward (same bits).  Needs the
+ * forward workspace of the problem. */
+stce_status stce_scaled_logits(const stce_problem *prob, int64_t row0, int64_t nrows, float *s_out,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/* Parity entry: the support program and selected logprob applied to given
+ * fp32 keys s [R, V] (row-major, 16-byte aligned, V a multiple of 4), with
+ * the same selection kernel as
+ * stce_forward.  Metadata pointers as in stce_problem (NULL = off), target
+ * [R] required.  Writes logprob [R] (= min(s_y - lse_S, 0) or -inf) and
+ * state [R * 32 bytes].  ws: at least stce_support_workspace_bytes(R, V). */
+stce_status stce_support_from_logits(const float *s, int64_t R, int64_t V, const int32_t *top_k,
+                                     const float *top_p, const float *min_p, const int64_t *target,
+                                     float *logprob, void *state, int64_t *dev_status, void *ws,
+                                     size_t ws_bytes, void *stream);
+
+/* Workspace bytes for stce_support_from_logits. */
+size_t stce_support_workspace_bytes(int64_t R, int64_t V);
+
+/* Decoding of the 32-byte per-row state (for tests and diagnostics).  The
+ * state holds, per row: the boundary key (order-preserving uint32 image of
+ * the last support token's fp32 key), the boundary token id, the support
+ * size n (V for an unfiltered row, whose boundary is then 0 / V - 1), the
+ * filtered and full log-sum-exp, the row maximum, the target's key and
+ * flags.  Reads `nrows` entries of a HOST copy of the state. */
+typedef struct stce_row_info {
+  uint32_t key_thr;
+  int32_t id_thr;
+  int32_t n;
+  uint32_t flags; /* bit 0 valid metadata, bit 1 filtered row, bit 2 target in support */
+  float lse_support;
+  float lse_full;
+  float row_max;
+  float target_key;
+} stce_row_info;
+stce_status stce_decode_state(const void *host_state, int64_t nrows, stce_row_info *out);
+
+/* Human-readable name of a status code (static string). */
+const char *stce_status_string(stce_status status);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char *stce_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STCE_H */

@@ -295,26 +295,28 @@ def backward(h, W, target, fwd: dict, grad_logprob, temperature=None):
     return dz @ W64, dz.T @ h64
 
 
-def sample_targets(h, W, temperature, top_k, top_p, min_p, u) -> np.ndarray:
+def sample_targets(h, W, temperature, top_k, top_p, min_p, u, rows=None) -> np.ndarray:
     """Draw one target per row from its filtered distribution.
 
     Inverse CDF along the order pi over ``q`` (softmax of z/T on the
-    support), with the caller's uniforms ``u`` in [0, 1).
+    support), with the caller's uniforms ``u`` in [0, 1).  ``rows`` limits
+    the draw to a subset of rows (returned in that order).
     """
     T = np.asarray(h).shape[0]
+    rows = np.arange(T) if rows is None else np.asarray(rows)
     temp = np.ones(T, np.float32) if temperature is None else np.asarray(temperature, np.float32)
     tk, tp, mp = _meta(T, top_k, top_p, min_p)
-    z = chunk_logits(h, W)
-    s32 = scale_logits(z, temp)
-    uu = z / temp.astype(np.float64)[:, None]
-    out = np.empty(T, np.int64)
-    for t in range(T):
-        d = support_row(s32[t], tk[t], tp[t], mp[t])
+    z = chunk_logits(np.asarray(h)[rows], W)
+    s32 = scale_logits(z, temp[rows])
+    uu = z / temp[rows].astype(np.float64)[:, None]
+    out = np.empty(len(rows), np.int64)
+    for i, t in enumerate(rows):
+        d = support_row(s32[i], tk[t], tp[t], mp[t])
         S = d["pi"][: d["n"]]
-        w = np.exp(uu[t, S] - uu[t, S].max())
+        w = np.exp(uu[i, S] - uu[i, S].max())
         cdf = np.cumsum(w)
-        i = int(np.searchsorted(cdf, float(u[t]) * cdf[-1], side="right"))
-        out[t] = S[min(i, len(S) - 1)]
+        j = int(np.searchsorted(cdf, float(u[t]) * cdf[-1], side="right"))
+        out[i] = S[min(j, len(S) - 1)]
     return out
 
 

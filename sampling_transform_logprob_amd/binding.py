@@ -1,0 +1,278 @@
+"""ctypes binding of ``libstce.so`` (argument marshalling only).
+
+Every step of the scoring path runs in the HIP library; this module checks
+tensor shapes/dtypes/devices, allocates outputs and workspaces with torch and
+passes raw device pointers plus the current HIP stream to the C ABI declared
+in ``include/stce.h``.  There is no fallback: without the built library every
+entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libstce.so")
+
+STATUS_NONE = (1 << 63) - 1
+FIELDS = {1: "temperature", 2: "top_k", 3: "top_p", 4: "min_p", 5: "target"}
+FLAG_VALID, FLAG_FILTERED, FLAG_IN_SUPPORT = 1, 2, 4
+STATE_BYTES_PER_ROW = 32
+DT_BF16, DT_F32 = 1, 2
+
+SYMBOLS = (
+    "stce_state_bytes", "stce_workspace_bytes", "stce_forward", "stce_backward",
+    "stce_scaled_logits", "stce_support_from_logits", "stce_support_workspace_bytes",
+    "stce_decode_state", "stce_status_string", "stce_last_error",
+)
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64), ("H", ctypes.c_int64), ("V", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("hidden", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("target", ctypes.c_void_p),
+        ("temperature", ctypes.c_void_p), ("top_k", ctypes.c_void_p), ("top_p", ctypes.c_void_p),
+        ("min_p", ctypes.c_void_p), ("chunk_rows", ctypes.c_int64), ("vocab_slice", ctypes.c_int64),
+    ]
+
+
+class RowInfo(ctypes.Structure):
+    _fields_ = [
+        ("key_thr", ctypes.c_uint32), ("id_thr", ctypes.c_int32), ("n", ctypes.c_int32),
+        ("flags", ctypes.c_uint32), ("lse_support", ctypes.c_float), ("lse_full", ctypes.c_float),
+        ("row_max", ctypes.c_float), ("target_key", ctypes.c_float),
+    ]
+
+
+class StceError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise StceError(f"{path} is not built: run sampling_transform_logprob_amd/build.py")
+    L = ctypes.CDLL(path)
+    P, vp, i64, i32, sz = ctypes.POINTER(Problem), ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "stce_state_bytes": (sz, [i64]),
+        "stce_workspace_bytes": (ctypes.c_int, [P, ctypes.POINTER(sz), ctypes.POINTER(sz)]),
+        "stce_forward": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
+        "stce_backward": (ctypes.c_int, [P, vp, vp, vp, vp, i32, vp, vp, sz, vp]),
+        "stce_scaled_logits": (ctypes.c_int, [P, i64, i64, vp, vp, sz, vp]),
+        "stce_support_from_logits": (ctypes.c_int, [vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "stce_support_workspace_bytes": (sz, [i64, i64]),
+        "stce_decode_state": (ctypes.c_int, [vp, i64, ctypes.POINTER(RowInfo)]),
+        "stce_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "stce_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        L = load()
+        raise StceError(f"{L.stce_status_string(status).decode()}: {L.stce_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _meta(name, t, T, dtype, device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor or None")
+    if t.dim() != 1 or t.shape[0] != T:
+        # over-length (or short) per-row metadata is an error, never truncated
+        raise ValueError(f"{name} must have shape [{T}], got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t.contiguous()
+
+
+def make_problem(hidden, weight, target, temperature=None, top_k=None, top_p=None, min_p=None,
+                 chunk_rows: int = 0, vocab_slice: int = 0):
+    """Checked ``stce_problem`` plus the tensors it points into (kept alive)."""
+    if hidden.dim() != 2 or weight.dim() != 2 or hidden.shape[1] != weight.shape[1]:
+        raise ValueError(f"hidden [T, H] and weight [V, H] expected, got {tuple(hidden.shape)}, {tuple(weight.shape)}")
+    if hidden.dtype != weight.dtype:
+        raise TypeError(f"hidden ({hidden.dtype}) and weight ({weight.dtype}) must share a dtype")
+    dt = {torch.bfloat16: DT_BF16, torch.float32: DT_F32}.get(hidden.dtype)
+    if dt is None:
+        raise TypeError(
+            f"unsupported LM-head dtype {hidden.dtype}: scoring takes bf16 or fp32 hidden/weight "
+            "(keep a bf16/fp32 copy of a quantized lm_head.weight for scoring)")
+    if hidden.device.type != "cuda" or weight.device != hidden.device:
+        raise ValueError("hidden and weight must be on the same GPU")
+    T, H = hidden.shape
+    V = weight.shape[0]
+    dev = hidden.device
+    hidden, weight = hidden.contiguous(), weight.contiguous()
+    target = _meta("target", target, T, torch.int64, dev)
+    if target is None:
+        raise ValueError("target is required")
+    keep = [hidden, weight, target,
+            _meta("temperature", temperature, T, torch.float32, dev),
+            _meta("top_k", top_k, T, torch.int32, dev),
+            _meta("top_p", top_p, T, torch.float32, dev),
+            _meta("min_p", min_p, T, torch.float32, dev)]
+    prob = Problem(T, H, V, dt, 0, *[t.data_ptr() if t is not None else None for t in keep],
+                   chunk_rows, vocab_slice)
+    return prob, keep
+
+
+def workspace_bytes(prob: Problem):
+    f, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().stce_workspace_bytes(ctypes.byref(prob), ctypes.byref(f), ctypes.byref(b)))
+    return f.value, b.value
+
+
+def _raise_rows(status: torch.Tensor, what: str, tensors: dict) -> None:
+    v = int(status.item())
+    if v == STATUS_NONE:
+        return
+    row, field = v >> 8, v & 0xFF
+    name = FIELDS.get(field, f"field {field}")
+    t = tensors.get(name)
+    val = "" if t is None else f"={t[row].item()!r}"
+    raise ValueError(f"{what}: invalid {name}[{row}]{val}")
+
+
+def forward(hidden, weight, target, temperature=None, top_k=None, top_p=None, min_p=None, *,
+            chunk_rows: int = 0, check: bool = True, workspace: Optional[torch.Tensor] = None):
+    """Selected logprob per row and the 32-byte-per-row state for backward."""
+    prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, chunk_rows)
+    T = prob.T
+    fwd_b, _ = workspace_bytes(prob)
+    dev = hidden.device
+    ws = workspace if workspace is not None else torch.empty(max(fwd_b, 1), dtype=torch.uint8, device=dev)
+    logprob = torch.empty(T, dtype=torch.float32, device=dev)
+    state = torch.empty(T * STATE_BYTES_PER_ROW, dtype=torch.uint8, device=dev)
+    status = torch.empty(1, dtype=torch.int64, device=dev)
+    _check(load().stce_forward(ctypes.byref(prob), _ptr(logprob), _ptr(state), _ptr(status), _ptr(ws),
+                               ws.numel(), _stream()))
+    if check:
+        _raise_rows(status, "stce_forward", dict(temperature=keep[3], top_k=keep[4], top_p=keep[5],
+                                                 min_p=keep[6], target=keep[2]))
+    return logprob, state
+
+
+def backward(hidden, weight, target, state, grad_logprob, temperature=None, top_k=None, top_p=None,
+             min_p=None, *, need_hidden: bool = True, need_weight: bool = True,
+             grad_weight: Optional[torch.Tensor] = None, accumulate_grad_weight: bool = False,
+             vocab_slice: int = 0, workspace: Optional[torch.Tensor] = None):
+    """(grad_hidden [T, H] in hidden's dtype, grad_weight [V, H] fp32)."""
+    prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, 0, vocab_slice)
+    T, H, V = prob.T, prob.H, prob.V
+    dev = hidden.device
+    if grad_logprob.shape != (T,) or grad_logprob.dtype != torch.float32 or grad_logprob.device != dev:
+        raise ValueError("grad_logprob must be fp32 [T] on the hidden's device")
+    if state.numel() != T * STATE_BYTES_PER_ROW or state.dtype != torch.uint8:
+        raise ValueError("state must be the uint8 [T*32] tensor written by forward")
+    g = grad_logprob.contiguous()
+    _, bwd_b = workspace_bytes(prob)
+    ws = workspace if workspace is not None else torch.empty(max(bwd_b, 1), dtype=torch.uint8, device=dev)
+    gh = torch.empty(T, H, dtype=hidden.dtype, device=dev) if need_hidden else None
+    if need_weight:
+        if grad_weight is None:
+            grad_weight = torch.empty(V, H, dtype=torch.float32, device=dev)
+            accumulate_grad_weight = False
+        elif grad_weight.shape != (V, H) or grad_weight.dtype != torch.float32 or not grad_weight.is_contiguous():
+            raise ValueError("grad_weight must be a contiguous fp32 [V, H] tensor")
+    else:
+        grad_weight = None
+    _check(load().stce_backward(ctypes.byref(prob), _ptr(g), _ptr(state), _ptr(gh), _ptr(grad_weight),
+                                1 if accumulate_grad_weight else 0, None, _ptr(ws), ws.numel(), _stream()))
+    return gh, grad_weight
+
+
+def scaled_logits(hidden, weight, temperature=None, row0: int = 0, nrows: Optional[int] = None):
+    """fp32 keys s = fl32(h W^T) / T of rows [row0, row0 + nrows) from the forward's kernel."""
+    T = hidden.shape[0]
+    nrows = T - row0 if nrows is None else nrows
+    target = torch.zeros(T, dtype=torch.int64, device=hidden.device)
+    prob, keep = make_problem(hidden, weight, target, temperature)
+    fwd_b, _ = workspace_bytes(prob)
+    ws = torch.empty(max(fwd_b, 1), dtype=torch.uint8, device=hidden.device)
+    out = torch.empty(nrows, prob.V, dtype=torch.float32, device=hidden.device)
+    _check(load().stce_scaled_logits(ctypes.byref(prob), row0, nrows, _ptr(out), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def support_from_logits(s, target, top_k=None, top_p=None, min_p=None, *, check: bool = True):
+    """Support program + selected logprob on given fp32 keys s [R, V]."""
+    if s.dim() != 2 or s.dtype != torch.float32 or s.device.type != "cuda":
+        raise ValueError("s must be a fp32 [R, V] GPU tensor")
+    s = s.contiguous()
+    R, V = s.shape
+    dev = s.device
+    target = _meta("target", target, R, torch.int64, dev)
+    tk = _meta("top_k", top_k, R, torch.int32, dev)
+    tp = _meta("top_p", top_p, R, torch.float32, dev)
+    mp = _meta("min_p", min_p, R, torch.float32, dev)
+    L = load()
+    nb = L.stce_support_workspace_bytes(R, V)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    logprob = torch.empty(R, dtype=torch.float32, device=dev)
+    state = torch.empty(R * STATE_BYTES_PER_ROW, dtype=torch.uint8, device=dev)
+    status = torch.empty(1, dtype=torch.int64, device=dev)
+    _check(L.stce_support_from_logits(_ptr(s), R, V, _ptr(tk), _ptr(tp), _ptr(mp), _ptr(target), _ptr(logprob),
+                                      _ptr(state), _ptr(status), _ptr(ws), ws.numel(), _stream()))
+    if check:
+        _raise_rows(status, "stce_support_from_logits", dict(top_k=tk, top_p=tp, min_p=mp, target=target))
+    return logprob, state
+
+
+def decode_state(state: torch.Tensor) -> dict:
+    """Per-row state fields as numpy arrays (copies the state to the host)."""
+    import numpy as np
+    host = state.detach().cpu().contiguous()
+    n = host.numel() // STATE_BYTES_PER_ROW
+    out = (RowInfo * n)()
+    _check(load().stce_decode_state(ctypes.c_void_p(host.data_ptr()), n, out))
+    arr = np.frombuffer(bytes(out), dtype=np.dtype([
+        ("key_thr", "<u4"), ("id_thr", "<i4"), ("n", "<i4"), ("flags", "<u4"),
+        ("lse_support", "<f4"), ("lse_full", "<f4"), ("row_max", "<f4"), ("target_key", "<f4")]))
+    return {k: arr[k].copy() for k in arr.dtype.names}
+
+
+class ScoreFunction(torch.autograd.Function):
+    """Autograd wrapper: logprob = ScoreFunction.apply(hidden, weight, target, T, top_k, top_p, min_p)."""
+
+    @staticmethod
+    def forward(ctx, hidden, weight, target, temperature=None, top_k=None, top_p=None, min_p=None):
+        logprob, state = forward(hidden, weight, target, temperature, top_k, top_p, min_p)
+        ctx.save_for_backward(hidden, weight, target, state)
+        ctx.meta = (temperature, top_k, top_p, min_p)
+        return logprob
+
+    @staticmethod
+    def backward(ctx, g):
+        hidden, weight, target, state = ctx.saved_tensors
+        gh, gw = backward(hidden, weight, target, state, g.float().contiguous(), *ctx.meta,
+                          need_hidden=ctx.needs_input_grad[0], need_weight=ctx.needs_input_grad[1])
+        if gw is not None:
+            gw = gw.to(weight.dtype)
+        return gh, gw, None, None, None, None, None

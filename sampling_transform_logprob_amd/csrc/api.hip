@@ -1,0 +1,349 @@
+// Host side of the C ABI declared in include/stce.h: argument checks,
+// workspace layout, chunk / slice schedule and kernel launches.  No call
+// allocates device memory or synchronizes the stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/stce.h"
+#include "kernels.hpp"
+
+using namespace stce;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+stce_status fail(stce_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+stce_status hip_fail(hipError_t e, const char* what) {
+  return fail(STCE_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kDefaultChunk = 4096;   // forward rows per chunk
+constexpr int64_t kDefaultSlice = 16384;  // backward vocabulary columns per slice
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  int64_t C, ldt, ntv;                                     // forward
+  size_t f_flags, f_tile, f_part, f_sy, fwd;
+  int64_t Vs, Vsp, Tp;                                      // backward
+  size_t b_flags, b_hT, b_WT, b_d, b_dT, b_dh, bwd;
+};
+
+size_t elt_size(int dtype) { return dtype == STCE_DT_BF16 ? 2 : 4; }
+
+stce_status check_shapes(const stce_problem* p) {
+  if (!p) return fail(STCE_E_ARG, "problem is NULL");
+  if (p->reserved != 0) return fail(STCE_E_ARG, "problem.reserved must be 0");
+  if (p->dtype != STCE_DT_BF16 && p->dtype != STCE_DT_F32)
+    return fail(STCE_E_UNSUPPORTED,
+                "unsupported operand dtype %d: hidden and weight must both be bf16 (STCE_DT_BF16) or fp32 "
+                "(STCE_DT_F32); quantized (e.g. fp8) LM heads are not scored -- keep an fp32/bf16 copy of "
+                "lm_head.weight for scoring",
+                (int)p->dtype);
+  if (p->T < 1 || p->T > INT32_MAX - 512) return fail(STCE_E_ARG, "T=%lld out of range [1, 2^31-513]", (long long)p->T);
+  if (p->H < 8 || p->H % 8 != 0 || p->H > (1 << 20))
+    return fail(STCE_E_ARG, "H=%lld must be a positive multiple of 8 (<= 2^20)", (long long)p->H);
+  if (p->V < 1 || p->V > INT32_MAX - 512) return fail(STCE_E_ARG, "V=%lld out of range [1, 2^31-513]", (long long)p->V);
+  if (p->chunk_rows < 0 || p->vocab_slice < 0) return fail(STCE_E_ARG, "chunk_rows / vocab_slice must be >= 0");
+  return STCE_OK;
+}
+
+Layout plan(const stce_problem* p) {
+  Layout L{};
+  const int64_t T = p->T, V = p->V, H = p->H;
+  const size_t es = elt_size(p->dtype);
+  L.C = p->chunk_rows > 0 ? p->chunk_rows : kDefaultChunk;
+  if (L.C > T) L.C = T;
+  L.ldt = round_up(V, 4);
+  L.ntv = ceil_div(V, VTILE);
+  size_t o = 0;
+  L.f_flags = o; o = align_up(o + 4 * (size_t)T);
+  L.f_tile = o;  o = align_up(o + 4 * (size_t)L.C * L.ldt);
+  L.f_part = o;  o = align_up(o + sizeof(TilePart) * (size_t)L.C * L.ntv);
+  L.f_sy = o;    o = align_up(o + 4 * (size_t)L.C);
+  L.fwd = o;
+
+  L.Vs = p->vocab_slice > 0 ? p->vocab_slice : kDefaultSlice;
+  if (L.Vs > V) L.Vs = V;
+  L.Vsp = round_up(L.Vs, 64);
+  L.Tp = round_up(T, 64);
+  o = 0;
+  L.b_flags = o; o = align_up(o + 4 * (size_t)T);
+  L.b_hT = o;    o = align_up(o + es * (size_t)H * L.Tp);
+  L.b_WT = o;    o = align_up(o + es * (size_t)H * L.Vsp);
+  L.b_d = o;     o = align_up(o + es * (size_t)L.Tp * L.Vsp);
+  L.b_dT = o;    o = align_up(o + es * (size_t)L.Vsp * L.Tp);
+  L.b_dh = o;    o = align_up(o + (p->dtype == STCE_DT_BF16 ? 4 * (size_t)T * H : 0));
+  L.bwd = o;
+  return L;
+}
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+stce_status check_inputs(const stce_problem* p) {
+  if (!p->hidden || !p->weight || !p->target) return fail(STCE_E_ARG, "hidden, weight and target are required");
+  if (!aligned(p->hidden, 16) || !aligned(p->weight, 16))
+    return fail(STCE_E_ARG, "hidden and weight must be 16-byte aligned");
+  if (!aligned(p->target, 8)) return fail(STCE_E_ARG, "target must be 8-byte aligned");
+  if ((p->temperature && !aligned(p->temperature, 4)) || (p->top_k && !aligned(p->top_k, 4)) ||
+      (p->top_p && !aligned(p->top_p, 4)) || (p->min_p && !aligned(p->min_p, 4)))
+    return fail(STCE_E_ARG, "metadata arrays must be 4-byte aligned");
+  return STCE_OK;
+}
+
+stce_status check_ws(void* ws, size_t have, size_t need) {
+  if (need && !ws) return fail(STCE_E_WORKSPACE, "workspace is NULL (needs %zu bytes)", need);
+  if (have < need) return fail(STCE_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", have, need);
+  if (ws && !aligned(ws, kAlign)) return fail(STCE_E_ARG, "workspace must be 256-byte aligned");
+  return STCE_OK;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t stce_state_bytes(int64_t T) { return T > 0 ? (size_t)T * STCE_STATE_BYTES_PER_ROW : 0; }
+
+stce_status stce_workspace_bytes(const stce_problem* prob, size_t* fwd, size_t* bwd) {
+  stce_status s = check_shapes(prob);
+  if (s) return s;
+  const Layout L = plan(prob);
+  if (fwd) *fwd = L.fwd;
+  if (bwd) *bwd = L.bwd;
+  return STCE_OK;
+}
+
+stce_status stce_forward(const stce_problem* p, float* logprob, void* state, int64_t* dev_status, void* ws,
+                         size_t ws_bytes, void* stream) {
+  stce_status s = check_shapes(p);
+  if (s) return s;
+  if ((s = check_inputs(p))) return s;
+  if (!logprob || !state) return fail(STCE_E_ARG, "logprob and state are required");
+  const Layout L = plan(p);
+  if ((s = check_ws(ws, ws_bytes, L.fwd))) return s;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  uint32_t* flags = at<uint32_t>(ws, L.f_flags);
+  if (dev_status && (e = launch_fill_i64(dev_status, STCE_STATUS_NONE, st))) return hip_fail(e, "status fill");
+  if ((e = launch_validate(p->T, p->V, p->temperature, p->top_k, p->top_p, p->min_p, p->target, flags, dev_status,
+                           st)))
+    return hip_fail(e, "validate");
+  const size_t es = elt_size(p->dtype);
+  for (int64_t c0 = 0; c0 < p->T; c0 += L.C) {
+    const int64_t nc = p->T - c0 < L.C ? p->T - c0 : L.C;
+    FwdArgs a{};
+    a.dtype = p->dtype;
+    a.W = p->weight;
+    a.h = (const char*)p->hidden + es * (size_t)c0 * p->H;
+    a.H = p->H;
+    a.V = p->V;
+    a.rows = nc;
+    a.tile = at<float>(ws, L.f_tile);
+    a.ld = L.ldt;
+    a.temp = p->temperature ? p->temperature + c0 : nullptr;
+    a.target = p->target + c0;
+    a.flags = flags + c0;
+    a.store_all = 0;
+    a.part = at<TilePart>(ws, L.f_part);
+    a.ntv = (int)L.ntv;
+    a.s_y = at<float>(ws, L.f_sy);
+    if ((e = launch_fwd_projection(a, st))) return hip_fail(e, "projection");
+    SelParams sp{};
+    sp.tile = a.tile;
+    sp.ld = L.ldt;
+    sp.part = a.part;
+    sp.ntv = (int)L.ntv;
+    sp.s_y = a.s_y;
+    sp.flags = flags + c0;
+    sp.target = p->target + c0;
+    sp.top_k = p->top_k ? p->top_k + c0 : nullptr;
+    sp.top_p = p->top_p ? p->top_p + c0 : nullptr;
+    sp.min_p = p->min_p ? p->min_p + c0 : nullptr;
+    sp.logprob = logprob + c0;
+    sp.state = (RowState*)state + c0;
+    sp.V = (int)p->V;
+    launch_select(sp, (int)nc, st);
+    if ((e = hipGetLastError())) return hip_fail(e, "select");
+  }
+  return STCE_OK;
+}
+
+stce_status stce_backward(const stce_problem* p, const float* grad_logprob, const void* state, void* grad_hidden,
+                          float* grad_weight, int32_t accumulate_grad_weight, int64_t* dev_status, void* ws,
+                          size_t ws_bytes, void* stream) {
+  stce_status s = check_shapes(p);
+  if (s) return s;
+  if ((s = check_inputs(p))) return s;
+  if (!grad_logprob || !state) return fail(STCE_E_ARG, "grad_logprob and state are required");
+  if ((grad_hidden && !aligned(grad_hidden, 16)) || (grad_weight && !aligned(grad_weight, 16)))
+    return fail(STCE_E_ARG, "gradient outputs must be 16-byte aligned");
+  const Layout L = plan(p);
+  if ((s = check_ws(ws, ws_bytes, L.bwd))) return s;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (dev_status) {
+    if ((e = launch_fill_i64(dev_status, STCE_STATUS_NONE, st))) return hip_fail(e, "status fill");
+    if ((e = launch_validate(p->T, p->V, p->temperature, p->top_k, p->top_p, p->min_p, p->target,
+                             at<uint32_t>(ws, L.b_flags), dev_status, st)))
+      return hip_fail(e, "validate");
+  }
+  if (!grad_hidden && !grad_weight) return STCE_OK;
+  if (grad_weight) {
+    if (p->dtype == STCE_DT_BF16)
+      e = launch_transpose_bf16((const bf16*)p->hidden, p->H, p->T, p->H, at<bf16>(ws, L.b_hT), L.Tp, L.Tp, st);
+    else
+      e = launch_transpose_f32((const float*)p->hidden, p->H, p->T, p->H, at<float>(ws, L.b_hT), L.Tp, L.Tp, st);
+    if (e) return hip_fail(e, "transpose hidden");
+  }
+  const int64_t nsl = ceil_div(p->V, L.Vs);
+  for (int64_t si = 0; si < nsl; ++si) {
+    BwdSliceArgs a{};
+    a.dtype = p->dtype;
+    a.W = p->weight;
+    a.h = p->hidden;
+    a.hT = at<char>(ws, L.b_hT);
+    a.WT = at<char>(ws, L.b_WT);
+    a.d = at<char>(ws, L.b_d);
+    a.dT = at<char>(ws, L.b_dT);
+    a.dh_sum = p->dtype == STCE_DT_BF16 ? at<float>(ws, L.b_dh) : (float*)grad_hidden;
+    a.grad_hidden = grad_hidden;
+    a.grad_weight = grad_weight;
+    a.accumulate_w = accumulate_grad_weight ? 1 : 0;
+    a.temp = p->temperature;
+    a.target = p->target;
+    a.st = (const RowState*)state;
+    a.g = grad_logprob;
+    a.T = p->T;
+    a.Tp = L.Tp;
+    a.H = p->H;
+    a.V = p->V;
+    a.v0 = si * L.Vs;
+    a.vs = p->V - a.v0 < L.Vs ? p->V - a.v0 : L.Vs;
+    a.vsp = round_up(a.vs, 64);
+    a.ld_d = L.Vsp;
+    a.first = si == 0;
+    a.last = si == nsl - 1;
+    if ((e = launch_bwd_slice(a, st))) return hip_fail(e, "backward slice");
+  }
+  return STCE_OK;
+}
+
+stce_status stce_scaled_logits(const stce_problem* p, int64_t row0, int64_t nrows, float* s_out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  stce_status s = check_shapes(p);
+  if (s) return s;
+  if ((s = check_inputs(p))) return s;
+  if (!s_out) return fail(STCE_E_ARG, "s_out is required");
+  if (row0 < 0 || nrows < 0 || row0 + nrows > p->T) return fail(STCE_E_ARG, "rows [%lld, %lld) outside [0, T)",
+                                                                 (long long)row0, (long long)(row0 + nrows));
+  const Layout L = plan(p);
+  if ((s = check_ws(ws, ws_bytes, L.fwd))) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t es = elt_size(p->dtype);
+  for (int64_t c0 = row0; c0 < row0 + nrows; c0 += L.C) {
+    const int64_t nc = row0 + nrows - c0 < L.C ? row0 + nrows - c0 : L.C;
+    FwdArgs a{};
+    a.dtype = p->dtype;
+    a.W = p->weight;
+    a.h = (const char*)p->hidden + es * (size_t)c0 * p->H;
+    a.H = p->H;
+    a.V = p->V;
+    a.rows = nc;
+    a.tile = s_out + (c0 - row0) * p->V;
+    a.ld = p->V;
+    a.temp = p->temperature ? p->temperature + c0 : nullptr;
+    a.target = nullptr;
+    a.flags = nullptr;
+    a.store_all = 1;
+    a.part = at<TilePart>(ws, L.f_part);
+    a.ntv = (int)L.ntv;
+    a.s_y = nullptr;
+    hipError_t e = launch_fwd_projection(a, st);
+    if (e) return hip_fail(e, "projection");
+  }
+  return STCE_OK;
+}
+
+size_t stce_support_workspace_bytes(int64_t R, int64_t V) {
+  if (R < 1 || V < 1) return 0;
+  const int64_t ntv = ceil_div(V, VTILE);
+  return align_up(4 * (size_t)R) + align_up(sizeof(TilePart) * (size_t)R * ntv) + align_up(4 * (size_t)R);
+}
+
+stce_status stce_support_from_logits(const float* sk, int64_t R, int64_t V, const int32_t* top_k, const float* top_p,
+                                     const float* min_p, const int64_t* target, float* logprob, void* state,
+                                     int64_t* dev_status, void* ws, size_t ws_bytes, void* stream) {
+  if (!sk || !target || !logprob || !state) return fail(STCE_E_ARG, "s, target, logprob and state are required");
+  if (R < 1 || R > INT32_MAX - 512 || V < 1 || V > INT32_MAX - 512)
+    return fail(STCE_E_ARG, "R=%lld, V=%lld out of range", (long long)R, (long long)V);
+  if (!aligned(sk, 16) || V % 4 != 0) return fail(STCE_E_ARG, "s must be 16-byte aligned with V a multiple of 4");
+  stce_status s = check_ws(ws, ws_bytes, stce_support_workspace_bytes(R, V));
+  if (s) return s;
+  const int64_t ntv = ceil_div(V, VTILE);
+  size_t o = 0;
+  uint32_t* flags = at<uint32_t>(ws, o);
+  o = align_up(o + 4 * (size_t)R);
+  TilePart* part = at<TilePart>(ws, o);
+  o = align_up(o + sizeof(TilePart) * (size_t)R * ntv);
+  float* s_y = at<float>(ws, o);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (dev_status && (e = launch_fill_i64(dev_status, STCE_STATUS_NONE, st))) return hip_fail(e, "status fill");
+  if ((e = launch_validate(R, V, nullptr, top_k, top_p, min_p, target, flags, dev_status, st)))
+    return hip_fail(e, "validate");
+  if ((e = launch_tile_partials(sk, V, R, V, (int)ntv, target, part, s_y, st))) return hip_fail(e, "partials");
+  SelParams sp{};
+  sp.tile = sk;
+  sp.ld = V;
+  sp.part = part;
+  sp.ntv = (int)ntv;
+  sp.s_y = s_y;
+  sp.flags = flags;
+  sp.target = target;
+  sp.top_k = top_k;
+  sp.top_p = top_p;
+  sp.min_p = min_p;
+  sp.logprob = logprob;
+  sp.state = (RowState*)state;
+  sp.V = (int)V;
+  launch_select(sp, (int)R, st);
+  if ((e = hipGetLastError())) return hip_fail(e, "select");
+  return STCE_OK;
+}
+
+stce_status stce_decode_state(const void* host_state, int64_t nrows, stce_row_info* out) {
+  if (!host_state || !out || nrows < 0) return fail(STCE_E_ARG, "bad arguments");
+  static_assert(sizeof(stce_row_info) == sizeof(RowState), "state layout");
+  memcpy(out, host_state, (size_t)nrows * sizeof(RowState));
+  return STCE_OK;
+}
+
+const char* stce_status_string(stce_status status) {
+  switch (status) {
+    case STCE_OK: return "STCE_OK";
+    case STCE_E_ARG: return "STCE_E_ARG: invalid argument";
+    case STCE_E_UNSUPPORTED: return "STCE_E_UNSUPPORTED: unsupported dtype or shape";
+    case STCE_E_WORKSPACE: return "STCE_E_WORKSPACE: workspace too small";
+    case STCE_E_HIP: return "STCE_E_HIP: HIP runtime error";
+  }
+  return "unknown stce_status";
+}
+
+const char* stce_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,295 @@
+// Epilogues of the block-tiled product (accumulator layout in gemm.hpp).
+#pragma once
+
+#include "gemm.hpp"
+
+namespace stce {
+
+#define STCE_INF __builtin_huge_valf()
+
+// Index helpers for the accumulator layout.
+__device__ inline int acc_row(int wm, int i, int r, int half) { return wm * 128 + i * 32 + (r >> 2) * 8 + half * 4 + (r & 3); }
+__device__ inline int acc_col(int wn, int j, int col) { return wn * 128 + j * 32 + col; }
+
+// (max, sum of exp(x - max)) merge; max = -inf means "empty".
+__device__ inline void lse_merge(float& mx, float& sm, float omx, float osm) {
+  const float M = fmaxf(mx, omx);
+  if (M == -STCE_INF) {
+    sm = 0.f;
+  } else {
+    sm = sm * __expf(mx - M) + osm * __expf(omx - M);
+  }
+  mx = M;
+}
+
+// Per-row temperature: s = fl32(z / T).  IEEE division (correctly rounded);
+// the same expression is used by the forward and the backward epilogue, so
+// the backward's keys are the forward's keys bit for bit.
+__device__ inline float scale_key(float z, float t) { return z / t; }
+
+// ---------------------------------------------------------------------------
+// Forward projection epilogue.  M = vocabulary, N = tokens of the chunk.
+// For each (token, 256-wide vocabulary tile): applies the temperature,
+// optionally stores the fp32 keys (rows flagged ROW_FILTERED, or all rows),
+// writes the tile's (max, sum exp(s - max), min) and captures the target key.
+// ---------------------------------------------------------------------------
+struct EpiLogits {
+  float* tile;             // [N][ld] keys, row = token
+  int64_t ld;
+  const float* temp;       // [N] or null (= 1)
+  const int64_t* target;   // [N] or null
+  const uint32_t* flags;   // [N] or null (with store_all)
+  int store_all;
+  int vec;                 // ld and the tile base allow 16-byte stores
+  TilePart* part;          // [N][ntv]
+  int ntv;
+  float* s_y;              // [N] or null
+  int V;                   // valid vocabulary rows
+  int N;                   // valid tokens
+
+  __device__ inline void operator()(f32x16 (&acc)[4][4], int m0, int n0, char* smem) const {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1, half = lane >> 5, col = lane & 31;
+    const int mb = m0 + wm * 128;
+    float pmx[4], psm[4], pmn[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + acc_col(wn, j, col);
+      const bool nv = n < N;
+      const float t = (nv && temp) ? temp[n] : 1.0f;
+      float mx = -STCE_INF, mn = STCE_INF;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float s = scale_key(acc[i][j][r], t);
+          acc[i][j][r] = s;
+          if (m0 + acc_row(wm, i, r, half) < V) {
+            mx = fmaxf(mx, s);
+            mn = fminf(mn, s);
+          }
+        }
+      const bool st = nv && (store_all || (flags[n] & ROW_FILTERED));
+      if (st) {
+        float* rowp = tile + (int64_t)n * ld;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int mm = mb + i * 32 + g * 8 + half * 4;
+            if (vec && mm + 3 < V) {
+              *(f32x4*)(rowp + mm) = f32x4{acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (mm + e < V) rowp[mm + e] = acc[i][j][g * 4 + e];
+            }
+          }
+      }
+      if (nv && target && s_y) {
+        const int64_t off = target[n] - mb;
+        if (off >= 0 && off < 128) {
+          const int oi = (int)off >> 5, ow = (int)off & 31;
+          if (((ow >> 2) & 1) == half) {
+            const int orr = (ow >> 3) * 4 + (ow & 3);
+            float v = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                if (i == oi && r == orr) v = acc[i][j][r];
+            s_y[n] = v;
+          }
+        }
+      }
+      float sm = 0.f;
+      if (mx != -STCE_INF) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (m0 + acc_row(wm, i, r, half) < V) sm += __expf(acc[i][j][r] - mx);
+      }
+      const float omx = __shfl_xor(mx, 32), osm = __shfl_xor(sm, 32), omn = __shfl_xor(mn, 32);
+      lse_merge(mx, sm, omx, osm);
+      pmx[j] = mx;
+      psm[j] = sm;
+      pmn[j] = fminf(mn, omn);
+    }
+    // merge the two waves that share these tokens (wm = 0 and 1)
+    __syncthreads();
+    float* red = (float*)smem;  // [2][256][3]
+    if (half == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tok = acc_col(wn, j, col);
+        red[(wm * 256 + tok) * 3 + 0] = pmx[j];
+        red[(wm * 256 + tok) * 3 + 1] = psm[j];
+        red[(wm * 256 + tok) * 3 + 2] = pmn[j];
+      }
+    }
+    __syncthreads();
+    if (wm == 0 && half == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tok = acc_col(wn, j, col);
+        const int n = n0 + tok;
+        if (n < N) {
+          float mx = red[tok * 3 + 0], sm = red[tok * 3 + 1];
+          lse_merge(mx, sm, red[(256 + tok) * 3 + 0], red[(256 + tok) * 3 + 1]);
+          TilePart tp;
+          tp.mx = mx;
+          tp.sum = sm;
+          tp.mn = fminf(red[tok * 3 + 2], red[(256 + tok) * 3 + 2]);
+          tp.pad = 0.f;
+          part[(int64_t)n * ntv + m0 / VTILE] = tp;
+        }
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Backward recompute epilogue.  M = vocabulary rows of one slice (local index
+// m, global v0 + m), N = tokens.  Recomputes the keys exactly as EpiLogits
+// does, re-derives support membership from the saved boundary, and writes
+//   dz[t, v] = c_t * (1[v == y_t] - exp(s - lse_S) * 1[v in S_t]),
+//   c_t = g_t / T_t on rows whose target is in support, else 0,
+// rounded to the operand type, both token-major (d) and vocab-major (dT).
+// Padding rows/columns (m >= Vs, n >= N, up to the padded sizes) get zeros.
+// ---------------------------------------------------------------------------
+template <class OutT>
+struct EpiDlogits {
+  const float* temp;       // [N] or null
+  const int64_t* target;   // [N]
+  const RowState* st;      // [N]
+  const float* g;          // [N]
+  OutT* d;                 // [N_pad][ld_d]
+  int64_t ld_d;
+  OutT* dT;                // [Vs_pad][ld_dT]
+  int64_t ld_dT;
+  int v0, Vs, Vs_pad, N, N_pad;
+
+  __device__ inline void operator()(f32x16 (&acc)[4][4], int m0, int n0, char* smem) const {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1, half = lane >> 5, col = lane & 31;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + acc_col(wn, j, col);
+      const bool nv = n < N;
+      const float t = (nv && temp) ? temp[n] : 1.0f;
+      RowState rs{};
+      float c = 0.f;
+      int64_t y = -1;
+      if (nv) {
+        rs = st[n];
+        y = target[n];
+        if ((rs.flags & (ROW_VALID | ROW_IN_SUPPORT)) == (ROW_VALID | ROW_IN_SUPPORT)) c = g[n] / t;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + acc_row(wm, i, r, half);
+          const int vg = v0 + m;
+          const float s = scale_key(acc[i][j][r], t);
+          const uint32_t key = order_key(s);
+          const bool in = key > rs.key_thr || (key == rs.key_thr && vg <= rs.id_thr);
+          const float q = in ? __expf(s - rs.lse_s) : 0.f;
+          // rows with c == 0 (out of support, invalid, padding) give exact
+          // zeros, whatever q is
+          acc[i][j][r] = (c != 0.f && m < Vs) ? c * ((vg == y ? 1.f : 0.f) - q) : 0.f;
+        }
+      if (n < N_pad) {
+        OutT* dr = d + (int64_t)n * ld_d;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int mm = m0 + wm * 128 + i * 32 + gq * 8 + half * 4;
+            if (mm < Vs_pad) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) dr[mm + e] = (OutT)acc[i][j][gq * 4 + e];
+            }
+          }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + acc_row(wm, i, r, half);
+            if (m < Vs_pad) dT[(int64_t)m * ld_dT + n] = (OutT)acc[i][j][r];
+          }
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Plain fp32 store (weight gradient slice): out[m, n] (+)= acc.
+// ---------------------------------------------------------------------------
+struct EpiStore {
+  float* out;
+  int64_t ld;
+  int M, N;
+  int accumulate;
+
+  __device__ inline void operator()(f32x16 (&acc)[4][4], int m0, int n0, char*) const {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1, half = lane >> 5, col = lane & 31;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + acc_col(wn, j, col);
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + acc_row(wm, i, r, half);
+          if (m < M) {
+            float* p = out + (int64_t)m * ld + n;
+            *p = accumulate ? *p + acc[i][j][r] : acc[i][j][r];
+          }
+        }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Hidden-gradient accumulation over vocabulary slices: sum[m, n] = (first ? 0 :
+// sum[m, n]) + acc; on the last slice the result goes to `out` (OutT) instead.
+// The slices are visited in a fixed order, so the sum is deterministic.
+// ---------------------------------------------------------------------------
+template <class OutT>
+struct EpiAccum {
+  float* sum;  // [M][ld] fp32 running sum (may alias out when OutT is float)
+  int64_t ld;
+  OutT* out;   // [M][ld]
+  int M, N;
+  int first, last;
+
+  __device__ inline void operator()(f32x16 (&acc)[4][4], int m0, int n0, char*) const {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1, half = lane >> 5, col = lane & 31;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + acc_col(wn, j, col);
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + acc_row(wm, i, r, half);
+          if (m < M) {
+            const int64_t o = (int64_t)m * ld + n;
+            const float v = first ? acc[i][j][r] : sum[o] + acc[i][j][r];
+            if (last)
+              out[o] = (OutT)v;
+            else
+              sum[o] = v;
+          }
+        }
+    }
+  }
+};
+
+}  // namespace stce

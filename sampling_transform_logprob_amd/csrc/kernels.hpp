@@ -1,0 +1,67 @@
+// Launchers of the library's kernels (host side).
+#pragma once
+
+#include "common.hpp"
+#include "select.hpp"
+
+namespace stce {
+
+// Per-row metadata validation: flags[t] = ROW_VALID | ROW_FILTERED or 0, and
+// the first bad (row << 8 | field) into *status with an atomic min.
+hipError_t launch_validate(int64_t T, int64_t V, const float* temp, const int32_t* top_k, const float* top_p,
+                           const float* min_p, const int64_t* target, uint32_t* flags, int64_t* status,
+                           hipStream_t s);
+hipError_t launch_fill_i64(int64_t* p, int64_t v, hipStream_t s);
+
+// out[c][r] = in[r][c] for r < R, c < Cc; zeros for R <= r < R_pad.
+hipError_t launch_transpose_bf16(const bf16* in, int64_t ld_in, int64_t R, int64_t Cc, bf16* out,
+                                 int64_t ld_out, int64_t R_pad, hipStream_t s);
+hipError_t launch_transpose_f32(const float* in, int64_t ld_in, int64_t R, int64_t Cc, float* out,
+                                int64_t ld_out, int64_t R_pad, hipStream_t s);
+
+// (max, sum exp, min) of every (row, 256-wide tile) of given keys, and the
+// target key of every row.
+hipError_t launch_tile_partials(const float* s, int64_t ld, int64_t R, int64_t V, int ntv,
+                                const int64_t* target, TilePart* part, float* s_y, hipStream_t st);
+
+// Forward projection of one chunk of rows with the keys epilogue.
+struct FwdArgs {
+  int dtype;  // 1 bf16, 2 fp32
+  const void* W;
+  const void* h;  // first row of the chunk
+  int64_t H, V, rows;
+  float* tile;
+  int64_t ld;
+  const float* temp;
+  const int64_t* target;
+  const uint32_t* flags;
+  int store_all;
+  TilePart* part;
+  int ntv;
+  float* s_y;
+};
+hipError_t launch_fwd_projection(const FwdArgs& a, hipStream_t s);
+
+// One vocabulary slice of the backward.
+struct BwdSliceArgs {
+  int dtype;
+  const void* W;       // full weight [V][H]
+  const void* h;       // [T][H]
+  const void* hT;      // [H][Tp]
+  void* WT;            // [H][ld_WT] scratch
+  void* d;             // [Tp][ld_d] scratch
+  void* dT;            // [ld_d rows][Tp] scratch
+  float* dh_sum;       // [T][H] fp32 running sum (bf16 path) or the fp32 output
+  void* grad_hidden;   // [T][H] or null
+  float* grad_weight;  // [V][H] or null
+  int accumulate_w;
+  const float* temp;
+  const int64_t* target;
+  const RowState* st;
+  const float* g;
+  int64_t T, Tp, H, V, v0, vs, vsp, ld_d;
+  int first, last;
+};
+hipError_t launch_bwd_slice(const BwdSliceArgs& a, hipStream_t s);
+
+}  // namespace stce

@@ -1,0 +1,451 @@
+// Support program + selected logprob, one workgroup of 256 threads per row.
+// The algorithm is described in select.hpp.
+#include "select.hpp"
+
+namespace stce {
+namespace {
+
+#define F_INF __builtin_huge_valf()
+#define D_INF __builtin_huge_val()
+
+struct MaxF { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct MinF { __device__ float operator()(float a, float b) const { return fminf(a, b); } };
+struct AddD { __device__ double operator()(double a, double b) const { return a + b; } };
+struct MinI { __device__ int operator()(int a, int b) const { return min(a, b); } };
+struct MaxI { __device__ int operator()(int a, int b) const { return max(a, b); } };
+
+// Deterministic block reduction: xor butterfly inside each wave (every lane
+// ends with the same value since each step combines a commutative pair),
+// then waves 0..3 in order.  All threads must call it.
+template <class T, class Op>
+__device__ inline T block_reduce(T v, Op op, T* scratch) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = op(v, __shfl_xor(v, o));
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  T r = scratch[0];
+#pragma unroll
+  for (int i = 1; i < ST / 64; ++i) r = op(r, scratch[i]);
+  return r;
+}
+
+// Exclusive prefix sum of one double per thread (thread order).
+__device__ inline double block_excl_scan(double v, double* scratch) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  double x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  double ex = __shfl_up(x, 1);
+  if (lane == 0) ex = 0.0;
+  __syncthreads();
+  if (lane == 63) scratch[w] = x;
+  __syncthreads();
+  double off = 0.0;
+  for (int i = 0; i < w; ++i) off += scratch[i];
+  return off + ex;
+}
+
+__device__ inline int next_pow2(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+// Bitonic sort, descending, of x[0, n) with n a power of two.
+template <class T>
+__device__ inline void bitonic_desc(T* x, int n) {
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < (n >> 1); i += ST) {
+        const int lo = 2 * stride * (i / stride) + (i % stride);
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const T a = x[lo], b = x[hi];
+        if ((a < b) == desc) {
+          x[lo] = b;
+          x[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+struct Shared {
+  union {
+    uint64_t cand[CAP];
+    uint32_t k32[2 * CAP];
+    struct {
+      uint32_t cnt[ST / 64][NB];
+      double mass[ST / 64][NB];
+    } h;
+  } u;
+  double sd[ST / 64];
+  float sf[ST / 64];
+  int si[ST / 64];
+  int cnt;
+  int c;             // chosen bin
+  int c_p;           // bin where top-p crosses (NB if not found)
+  uint32_t nbin;     // tokens in the chosen bin
+  uint32_t above;    // tokens ahead of the window
+  double mabove;     // their mass
+  double Z;          // full-row mass
+  double mass_s;     // mass of the support
+};
+
+__global__ __launch_bounds__(ST) void select_kernel(SelParams P) {
+  __shared__ Shared S;
+  const int row = blockIdx.x, tid = threadIdx.x, w = tid >> 6;
+  const int V = P.V;
+  const uint32_t fl = P.flags[row];
+  if (!(fl & ROW_VALID)) {
+    if (tid == 0) {
+      P.logprob[row] = __builtin_nanf("");
+      RowState rs{};
+      P.state[row] = rs;
+    }
+    return;
+  }
+
+  // ---- row maximum, minimum and full log-sum-exp from the tile partials
+  const TilePart* pp = P.part + (int64_t)row * P.ntv;
+  float mx = -F_INF, mn = F_INF;
+  for (int t = tid; t < P.ntv; t += ST) {
+    mx = fmaxf(mx, pp[t].mx);
+    mn = fminf(mn, pp[t].mn);
+  }
+  const float m = block_reduce(mx, MaxF{}, S.sf);
+  const float smin = block_reduce(mn, MinF{}, S.sf);
+  const double m64 = (double)m;
+  double zs = 0.0;
+  for (int t = tid; t < P.ntv; t += ST) zs += (double)pp[t].sum * exp((double)pp[t].mx - m64);
+  const double lse_full = m64 + log(block_reduce(zs, AddD{}, S.sd));
+
+  const float sy = P.s_y[row];
+  const int64_t y = P.target[row];
+  RowState rs;
+  rs.m = m;
+  rs.lse_full = (float)lse_full;
+  rs.s_y = sy;
+
+  if (!(fl & ROW_FILTERED)) {  // identity program: the support is the whole row
+    if (tid == 0) {
+      rs.key_thr = 0u;
+      rs.id_thr = V - 1;
+      rs.n = V;
+      rs.flags = ROW_VALID | ROW_IN_SUPPORT;
+      rs.lse_s = rs.lse_full;
+      P.logprob[row] = (float)fmin((double)sy - lse_full, 0.0);
+      P.state[row] = rs;
+    }
+    return;
+  }
+
+  const int k = P.top_k ? P.top_k[row] : 0;
+  const float p = P.top_p ? P.top_p[row] : 1.0f;
+  const float mp = P.min_p ? P.min_p[row] : 0.0f;
+  const bool k_on = k > 0 && k < V, p_on = p < 1.0f, m_on = mp > 0.0f;
+  const double thr = m_on ? log((double)mp) : -D_INF;
+  const float* rp = P.tile + (int64_t)row * P.ld;
+  const int nv4 = (V + 3) >> 2;
+
+  // One pass over the row: gathers the tokens `pred` accepts into the window
+  // (up to CAP) and, if want_z, sums the fp64 masses of the whole row.
+  auto collect = [&](auto pred, bool want_z, double& Z) -> int {
+    if (tid == 0) S.cnt = 0;
+    __syncthreads();
+    double zl = 0.0;
+    for (int q = tid; q < nv4; q += ST) {
+      const f32x4 x = *(const f32x4*)(rp + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * q + e;
+        if (v < V) {
+          const float s = x[e];
+          if (want_z) zl += exp((double)s - m64);
+          const uint32_t key = order_key(s);
+          if (pred(s, key, v)) {
+            const int i = atomicAdd(&S.cnt, 1);
+            if (i < CAP) S.u.cand[i] = composite(key, (uint32_t)v);
+          }
+        }
+      }
+    }
+    Z = want_z ? block_reduce(zl, AddD{}, S.sd) : 0.0;
+    __syncthreads();
+    return S.cnt;
+  };
+
+  int nw = -1;              // window size; -1 until a window is found
+  uint32_t above = 0;       // tokens ahead of the window in the order
+  double mabove = 0.0;      // their fp64 mass
+  double Z = 0.0;           // full-row fp64 mass (top-p only)
+  bool p_here = false;      // top-p is known to cross inside the window
+
+  if (V <= CAP) {
+    nw = collect([](float, uint32_t, int) { return true; }, p_on, Z);
+    p_here = p_on;
+  } else {
+    // lower bound of the k-th largest key: the k-th largest tile maximum
+    bool kb = false;
+    uint32_t bkey = 0u;
+    if (k_on && k <= P.ntv && P.ntv <= 2 * CAP) {
+      const int n2 = next_pow2(P.ntv);
+      for (int t = tid; t < n2; t += ST) S.u.k32[t] = t < P.ntv ? order_key(pp[t].mx) : 0u;
+      __syncthreads();
+      bitonic_desc(S.u.k32, n2);
+      bkey = S.u.k32[k - 1];
+      kb = true;
+      __syncthreads();
+    }
+    if (kb || m_on) {
+      const int n = collect(
+          [&](float s, uint32_t key, int) { return (!kb || key >= bkey) && (!m_on || (double)s - m64 >= thr); },
+          p_on, Z);
+      if (n <= CAP) nw = n;
+    }
+  }
+
+  if (nw < 0) {
+    // ---- value histogram of (m - s): counts and fp64 masses per bin
+    const float range = m - smin;
+    const float scale = (range > 1e-30f && range < 3.0e38f) ? (float)NB / range : 0.0f;
+    auto vbin = [&](float s) -> int {
+      const float d = (m - s) * scale;
+      return d >= (float)(NB - 1) ? NB - 1 : (d > 0.0f ? (int)d : 0);
+    };
+    for (int b = tid; b < (ST / 64) * NB; b += ST) {
+      S.u.h.cnt[b / NB][b % NB] = 0u;
+      S.u.h.mass[b / NB][b % NB] = 0.0;
+    }
+    __syncthreads();
+    int cm_loc = -1;
+    for (int q = tid; q < nv4; q += ST) {
+      const f32x4 x = *(const f32x4*)(rp + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * q + e;
+        if (v < V) {
+          const float s = x[e];
+          const int b = vbin(s);
+          const double dm = (double)s - m64;
+          atomicAdd(&S.u.h.cnt[w][b], 1u);
+          atomicAdd(&S.u.h.mass[w][b], exp(dm));
+          if (m_on && dm >= thr) cm_loc = max(cm_loc, b);
+        }
+      }
+    }
+    const int cm = m_on ? block_reduce(cm_loc, MaxI{}, S.si) : NB;
+    __syncthreads();
+    for (int b = tid; b < NB; b += ST) {
+      uint32_t c = S.u.h.cnt[0][b];
+      double ms = S.u.h.mass[0][b];
+      for (int i = 1; i < ST / 64; ++i) {
+        c += S.u.h.cnt[i][b];
+        ms += S.u.h.mass[i][b];
+      }
+      S.u.h.cnt[0][b] = c;
+      S.u.h.mass[0][b] = ms;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double Zt = 0.0;
+      for (int b = 0; b < NB; ++b) Zt += S.u.h.mass[0][b];
+      const double pz = (double)p * Zt;
+      uint32_t cc = 0;
+      double cms = 0.0;
+      int ck = NB, cp = NB;
+      for (int b = 0; b < NB; ++b) {
+        cc += S.u.h.cnt[0][b];
+        cms += S.u.h.mass[0][b];
+        if (k_on && ck == NB && cc >= (uint32_t)k) ck = b;
+        if (p_on && cp == NB && cms >= pz) cp = b;
+      }
+      const int c = min(min(ck, cp), cm);
+      uint32_t ab = 0;
+      double mab = 0.0;
+      for (int b = 0; b < c; ++b) {
+        ab += S.u.h.cnt[0][b];
+        mab += S.u.h.mass[0][b];
+      }
+      S.c = c;
+      S.c_p = cp;
+      S.nbin = S.u.h.cnt[0][c];
+      S.above = ab;
+      S.mabove = mab;
+      S.Z = Zt;
+    }
+    __syncthreads();
+    const int c = S.c;
+    above = S.above;
+    mabove = S.mabove;
+    Z = S.Z;
+    p_here = p_on && S.c_p == c;
+    const uint32_t nbin = S.nbin;
+    __syncthreads();
+
+    if (nbin <= (uint32_t)CAP) {
+      double dummy;
+      nw = collect([&](float s, uint32_t, int) { return vbin(s) == c; }, false, dummy);
+    } else {
+      // ---- radix refinement of bin c on the composite (key, ~id)
+      uint64_t prefix = 0, pmask = 0;
+      for (int shift = 56;; shift -= 8) {
+        for (int b = tid; b < (ST / 64) * RB; b += ST) {
+          S.u.h.cnt[b / RB][b % RB] = 0u;
+          S.u.h.mass[b / RB][b % RB] = 0.0;
+        }
+        __syncthreads();
+        int cml = -1;
+        for (int q = tid; q < nv4; q += ST) {
+          const f32x4 x = *(const f32x4*)(rp + 4 * q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = 4 * q + e;
+            if (v < V) {
+              const float s = x[e];
+              if (vbin(s) != c) continue;
+              const uint64_t comp = composite(order_key(s), (uint32_t)v);
+              if ((comp & pmask) != prefix) continue;
+              const int b = 255 - (int)((comp >> shift) & 255u);
+              const double dm = (double)s - m64;
+              atomicAdd(&S.u.h.cnt[w][b], 1u);
+              atomicAdd(&S.u.h.mass[w][b], exp(dm));
+              if (m_on && dm >= thr) cml = max(cml, b);
+            }
+          }
+        }
+        const int cm2 = m_on ? block_reduce(cml, MaxI{}, S.si) : RB;
+        __syncthreads();
+        for (int b = tid; b < RB; b += ST) {
+          uint32_t cc = S.u.h.cnt[0][b];
+          double ms = S.u.h.mass[0][b];
+          for (int i = 1; i < ST / 64; ++i) {
+            cc += S.u.h.cnt[i][b];
+            ms += S.u.h.mass[i][b];
+          }
+          S.u.h.cnt[0][b] = cc;
+          S.u.h.mass[0][b] = ms;
+        }
+        __syncthreads();
+        if (tid == 0) {
+          const double pz = (double)p * Z;
+          uint32_t cc = above;
+          double cms = mabove;
+          int ck = RB, cp = RB, last = 0;
+          for (int b = 0; b < RB; ++b) {
+            cc += S.u.h.cnt[0][b];
+            cms += S.u.h.mass[0][b];
+            if (S.u.h.cnt[0][b]) last = b;
+            if (k_on && ck == RB && cc >= (uint32_t)k) ck = b;
+            if (p_on && cp == RB && cms >= pz) cp = b;
+          }
+          // rounding may leave top-p just short inside the bin it crossed in
+          if (p_here && cp == RB) cp = last;
+          const int c2 = min(min(ck, cp), cm2);
+          uint32_t ab = above;
+          double mab = mabove;
+          for (int b = 0; b < c2; ++b) {
+            ab += S.u.h.cnt[0][b];
+            mab += S.u.h.mass[0][b];
+          }
+          S.c = c2;
+          S.c_p = cp;
+          S.nbin = S.u.h.cnt[0][c2];
+          S.above = ab;
+          S.mabove = mab;
+        }
+        __syncthreads();
+        const int c2 = S.c;
+        p_here = p_here && S.c_p == c2;
+        above = S.above;
+        mabove = S.mabove;
+        prefix |= (uint64_t)(255 - c2) << shift;
+        pmask |= (uint64_t)0xff << shift;
+        const uint32_t nsub = S.nbin;
+        __syncthreads();
+        if (nsub <= (uint32_t)CAP || shift == 0) break;
+      }
+      double dummy;
+      nw = collect(
+          [&](float s, uint32_t key, int v) {
+            return vbin(s) == c && (composite(key, (uint32_t)v) & pmask) == prefix;
+          },
+          false, dummy);
+    }
+  }
+
+  // ---- resolve the boundary inside the window
+  const int n2 = next_pow2(max(nw, 1));
+  for (int i = nw + tid; i < n2; i += ST) S.u.cand[i] = 0ull;
+  __syncthreads();
+  bitonic_desc(S.u.cand, n2);
+  const int E = (n2 + ST - 1) / ST;
+  const int lo = tid * E, hi = min(lo + E, nw);
+  double seg = 0.0;
+  for (int i = lo; i < hi; ++i) seg += exp((double)key_value(comp_key(S.u.cand[i])) - m64);
+  const double base = mabove + block_excl_scan(seg, S.sd);
+  const double pz = (double)p * Z;
+  int np_loc = INT32_MAX, nm_loc = INT32_MAX;
+  {
+    double run = base;
+    for (int i = lo; i < hi; ++i) {
+      const double dm = (double)key_value(comp_key(S.u.cand[i])) - m64;
+      run += exp(dm);
+      if (p_on && np_loc == INT32_MAX && run >= pz) np_loc = i;
+      if (m_on && nm_loc == INT32_MAX && dm < thr) nm_loc = i;
+    }
+  }
+  const int np_idx = block_reduce(np_loc, MinI{}, S.si);
+  const int nm_idx = block_reduce(nm_loc, MinI{}, S.si);
+  int n_loc = nw;
+  if (k_on) {
+    const int64_t nk = (int64_t)k - (int64_t)above;
+    if (nk >= 1 && nk < n_loc) n_loc = (int)nk;
+  }
+  if (p_on) {
+    const int np = np_idx != INT32_MAX ? np_idx + 1 : (p_here ? nw : INT32_MAX);
+    if (np < n_loc) n_loc = np;
+  }
+  if (m_on) {
+    const int nm = nm_idx != INT32_MAX ? nm_idx : nw;
+    if (nm < n_loc) n_loc = nm;
+  }
+  if (n_loc < 1) n_loc = 1;
+  {
+    const int b = n_loc - 1;
+    if (b >= lo && b < hi) {
+      double run = base;
+      for (int i = lo; i <= b; ++i) run += exp((double)key_value(comp_key(S.u.cand[i])) - m64);
+      S.mass_s = run;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const uint64_t bc = S.u.cand[n_loc - 1];
+    rs.key_thr = comp_key(bc);
+    rs.id_thr = (int32_t)comp_id(bc);
+    rs.n = (int32_t)(above + (uint32_t)n_loc);
+    const double lse_s = m64 + log(S.mass_s);
+    rs.lse_s = (float)lse_s;
+    const uint32_t ky = order_key(sy);
+    const bool in = ky > rs.key_thr || (ky == rs.key_thr && y <= (int64_t)rs.id_thr);
+    rs.flags = ROW_VALID | ROW_FILTERED | (in ? ROW_IN_SUPPORT : 0u);
+    P.logprob[row] = in ? (float)fmin((double)sy - lse_s, 0.0) : -F_INF;
+    P.state[row] = rs;
+  }
+}
+
+}  // namespace
+
+void launch_select(const SelParams& p, int rows, hipStream_t stream) {
+  if (rows <= 0) return;
+  hipLaunchKernelGGL(select_kernel, dim3(rows), dim3(ST), 0, stream, p);
+}
+
+}  // namespace stce

@@ -1,0 +1,53 @@
+// Support program and selected logprob, one workgroup per row.
+//
+// Inputs per row: the fp32 keys s[0, V) of the row (stored by the projection
+// epilogue), the (max, sum exp, min) partials of its 256-wide vocabulary
+// tiles, the target key, and the metadata.  Decisions are exact functions of
+// the fp32 keys: counts are integers, masses exp(s - m) are fp64, min-p is the
+// fp64 comparison s - m >= ln(min_p) with m the unfiltered row maximum.
+//
+// Every filter keeps a prefix of one order (key descending, lower token id
+// first among equal keys).  The row's support is the shortest prefix; its
+// last token is found inside a "window" of at most CAP consecutive tokens of
+// that order, which is gathered into LDS, sorted by composite (key, ~id) and
+// scanned, with the count and the mass of everything ahead of the window
+// known.  The window is found by one of:
+//   * whole row, when V <= CAP;
+//   * bounded candidates: tokens >= the k-th largest tile maximum (a lower
+//     bound of the k-th largest key, since the tile maxima are distinct
+//     tokens) and passing min-p -- a prefix that contains the support;
+//   * value histogram: NB bins of (m - s) over the row with per-bin counts and
+//     fp64 masses; the first bin where a filter crosses is the window;
+//   * radix refinement of that bin on the 64-bit composite (key, ~id), 8 bits
+//     per pass, when the bin holds more than CAP tokens (ties or very peaked
+//     rows).
+#pragma once
+
+#include "common.hpp"
+
+namespace stce {
+
+constexpr int ST = 256;     // threads per row
+constexpr int CAP = 4096;   // window capacity (composites in LDS)
+constexpr int NB = 512;     // value-histogram bins
+constexpr int RB = 256;     // radix bins (8-bit digits)
+
+struct SelParams {
+  const float* tile;        // [R][ld] keys
+  int64_t ld;
+  const TilePart* part;     // [R][ntv]
+  int ntv;
+  const float* s_y;         // [R] target keys
+  const uint32_t* flags;    // [R] ROW_VALID / ROW_FILTERED
+  const int64_t* target;    // [R]
+  const int32_t* top_k;     // [R] or null
+  const float* top_p;       // [R] or null
+  const float* min_p;       // [R] or null
+  float* logprob;           // [R]
+  RowState* state;          // [R]
+  int V;
+};
+
+void launch_select(const SelParams& p, int rows, hipStream_t stream);
+
+}  // namespace stce

@@ -38,10 +38,11 @@ CONFIGS = {
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bf16 (ties to even), as float32."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    b = x.view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
-    return b.astype(np.uint32).view(np.float32)
+    x = np.array(x, dtype=np.float32, copy=True)
+    b = x.view(np.uint32)              # finite values: the sum cannot wrap
+    b += np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))
+    b &= np.uint32(0xFFFF0000)
+    return x
 
 
 def _children(seed: int, n: int = 6):

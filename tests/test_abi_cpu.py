@@ -1,0 +1,106 @@
+"""Host-side checks of the C ABI: the library loads without a GPU, exports
+every function include/stce.h declares, and rejects bad arguments before
+anything is launched (no device call is made by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sampling_transform_logprob_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "stce.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(stce_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libstce.so not built")
+    return binding.load()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = _declared()
+    assert "stce_forward" in names and "stce_backward" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(binding.SYMBOLS)
+
+
+def test_struct_layouts_match_header():
+    assert ctypes.sizeof(binding.Problem) == 104
+    assert ctypes.sizeof(binding.RowInfo) == binding.STATE_BYTES_PER_ROW
+
+
+def _prob(**kw):
+    d = dict(T=8, H=64, V=100, dtype=binding.DT_BF16)
+    d.update(kw)
+    p = binding.Problem()
+    for k, v in d.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_workspace_sizes_are_host_computable(lib):
+    f, b = binding.workspace_bytes(_prob())
+    assert f > 8 * 100 * 4 and b > 0
+    f2, _ = binding.workspace_bytes(_prob(T=100000, chunk_rows=512))
+    assert f2 < 512 * 101 * 4 + 100000 * 4 + 4 * 512 * 16 + 4096
+    assert lib.stce_state_bytes(10) == 320
+
+
+def test_unsupported_dtype_is_one_actionable_error(lib):
+    with pytest.raises(binding.StceError, match="UNSUPPORTED.*fp8"):
+        binding.workspace_bytes(_prob(dtype=7))
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(T=0), "T=0"), (dict(H=12), "H=12"), (dict(V=0), "V=0"), (dict(reserved=1), "reserved"),
+    (dict(chunk_rows=-1), "chunk_rows"),
+])
+def test_bad_shapes_are_rejected(lib, kw, msg):
+    with pytest.raises(binding.StceError, match=msg):
+        binding.workspace_bytes(_prob(**kw))
+
+
+def test_forward_rejects_null_and_small_workspace_before_launch(lib):
+    p = _prob()
+    st = lib.stce_forward(ctypes.byref(p), None, None, None, None, 0, None)
+    assert st == 1 and b"required" in lib.stce_last_error()
+    p.hidden, p.weight, p.target = 16, 16, 16          # fake, never dereferenced: checks stop first
+    st = lib.stce_forward(ctypes.byref(p), ctypes.c_void_p(16), ctypes.c_void_p(16), None, None, 0, None)
+    assert st == 3 and b"workspace" in lib.stce_last_error()
+    p.hidden = 18
+    st = lib.stce_forward(ctypes.byref(p), ctypes.c_void_p(16), ctypes.c_void_p(16), None, None, 0, None)
+    assert st == 1 and b"aligned" in lib.stce_last_error()
+
+
+def test_support_entry_rejects_bad_layout(lib):
+    st = lib.stce_support_from_logits(ctypes.c_void_p(16), 2, 10, None, None, None, ctypes.c_void_p(16),
+                                      ctypes.c_void_p(16), ctypes.c_void_p(16), None, None, 0, None)
+    assert st == 1 and b"multiple of 4" in lib.stce_last_error()
+
+
+def test_binding_rejects_over_length_metadata():
+    torch = pytest.importorskip("torch")
+    t = torch.zeros(5)
+    with pytest.raises(ValueError, match=r"shape \[4\]"):
+        binding._meta("top_p", t, 4, torch.float32, t.device)
+
+
+def test_decode_state_roundtrip(lib):
+    import numpy as np
+    raw = np.zeros(3, dtype=np.dtype([("key_thr", "<u4"), ("id_thr", "<i4"), ("n", "<i4"), ("flags", "<u4"),
+                                      ("lse", "<f4"), ("lsef", "<f4"), ("m", "<f4"), ("sy", "<f4")]))
+    raw["id_thr"] = [5, 6, 7]
+    raw["n"] = [1, 2, 3]
+    torch = pytest.importorskip("torch")
+    d = binding.decode_state(torch.from_numpy(raw.view(np.uint8).copy()))
+    assert list(d["id_thr"]) == [5, 6, 7] and list(d["n"]) == [1, 2, 3]

@@ -1,0 +1,195 @@
+"""GPU parity of the HIP scoring core against the fp64 oracle.
+
+Every test drives the library through its C ABI (``binding`` only marshals
+arguments) and compares with ``oracle`` on the same seeded inputs:
+  * the support bit for bit, the oracle being fed the GPU's own fp32 keys
+    (exported by the forward's projection kernel);
+  * logprob within 2e-3 absolute, -inf exactly where the oracle has it;
+  * grad_hidden and grad_weight within 1e-2 relative Frobenius error.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (GRAD_RTOL, check_logprob, check_support, dev, meta_of, rel_fro, say, targets, to_gpu)
+from sampling_transform_logprob_amd import binding, workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load()
+
+
+def _run(w, y, g=None, **kw):
+    G = to_gpu(w, y)
+    lp, st = binding.forward(G["h"], G["W"], G["target"], **meta_of(G), chunk_rows=kw.get("chunk_rows", 0))
+    gg = torch.from_numpy(g.astype(np.float32)).to(dev()) if g is not None else None
+    gh = gw = None
+    if gg is not None:
+        gh, gw = binding.backward(G["h"], G["W"], G["target"], st, gg, **meta_of(G),
+                                  vocab_slice=kw.get("vocab_slice", 0))
+    keys = binding.scaled_logits(G["h"], G["W"], G["temperature"])
+    torch.cuda.synchronize()
+    return G, lp, st, gh, gw, keys
+
+
+# ---------------------------------------------------------------- projection + temperature
+def test_projection_accuracy_and_temperature_bitwise():
+    w = workloads.make("top_p", T=96)
+    w["W"] = w["W"][:8192]
+    G = to_gpu(w, np.zeros(96, np.int64))
+    say("projection: T=96 H=4096 V=8192")
+    z = binding.scaled_logits(G["h"], G["W"], None).cpu().numpy()
+    z64 = oracle.chunk_logits(w["h"], w["W"])
+    scale = np.abs(w["h"]).astype(np.float64) @ np.abs(w["W"]).astype(np.float64).T
+    assert (np.abs(z - z64) / scale).max() < 1e-5          # fp32 accumulation of exact products
+    t = torch.from_numpy(np.concatenate([w["temperature"][:90], np.float32([1.0, 0.7, 1e-3, 3.0, 0.3, 1.5])]))
+    s = binding.scaled_logits(G["h"], G["W"], t.to(dev())).cpu()
+    ref = (torch.from_numpy(z).double() / t.double()[:, None]).float()   # correctly rounded fp32 quotient
+    assert torch.equal(s.view(torch.int32), ref.view(torch.int32))
+
+
+# ---------------------------------------------------------------- five workloads, reduced T
+CASES = [("tiny", 64), ("identity", 300), ("top_p", 300), ("headline", 300), ("ties", 300)]
+
+
+@pytest.mark.parametrize("name,T", CASES)
+def test_workload_parity(name, T):
+    w = workloads.make(name, T=T)
+    say(f"parity {name}: T={T} H={w['H']} V={w['V']}")
+    y = targets(w)
+    g = np.full(T, -1.0 / T)                                # mean NLL
+    G, lp, st, gh, gw, keys = _run(w, y, g)
+    kc = keys.cpu().numpy()
+    ref = oracle.forward(w["h"], w["W"], y, w["temperature"], w["top_k"], w["top_p"], w["min_p"], keys=kc)
+    info = binding.decode_state(st)
+    near = check_support(info, ref, name)
+    err = check_logprob(lp.cpu().numpy(), ref)
+    dH, dW = oracle.backward(w["h"], w["W"], y, ref, g, w["temperature"])
+    rh, rw = rel_fro(gh.float().cpu().numpy(), dH), rel_fro(gw.cpu().numpy(), dW)
+    say(f"  near={near} logprob err={err:.2e} dH rel={rh:.2e} dW rel={rw:.2e} "
+        f"supports: min {info['n'].min()} max {info['n'].max()}")
+    assert near == 0
+    assert rh < GRAD_RTOL and rw < GRAD_RTOL
+    # the independent run (oracle's own fp64 keys): boundary flips are rare
+    own = oracle.forward(w["h"], w["W"], y, w["temperature"], w["top_k"], w["top_p"], w["min_p"])
+    flips = int((own["n"] != ref["n"]).sum())
+    say(f"  rows whose support differs on the oracle's own keys: {flips}")
+    assert flips <= max(1, T // 100)
+
+
+def test_gradients_with_random_upstream():
+    w = workloads.make("ties", T=280)
+    w["W"] = w["W"][:20000]
+    say("random upstream gradient: ties T=280 V=20000")
+    y = targets(w)
+    g = np.random.Generator(np.random.PCG64(11)).standard_normal(280)
+    G, lp, st, gh, gw, keys = _run(w, y, g, vocab_slice=3000)
+    ref = oracle.forward(w["h"], w["W"], y, w["temperature"], w["top_k"], w["top_p"], w["min_p"],
+                         keys=keys.cpu().numpy())
+    dH, dW = oracle.backward(w["h"], w["W"], y, ref, g, w["temperature"])
+    assert rel_fro(gh.float().cpu().numpy(), dH) < GRAD_RTOL
+    assert rel_fro(gw.cpu().numpy(), dW) < GRAD_RTOL
+    # dz sums to zero over each row, so the columns of dW sum to zero
+    colsum = gw.double().sum(0).abs().max().item()
+    assert colsum < 1e-3 * gw.abs().max().item() * np.sqrt(280)
+
+
+# ---------------------------------------------------------------- invariances
+def test_chunking_and_repetition_are_bitwise_invariant():
+    w = workloads.make("headline", T=300)
+    w["W"] = w["W"][:30000]
+    y = targets(w)
+    G = to_gpu(w, y)
+    say("invariance: headline T=300 V=30000")
+    outs = []
+    for chunk in (0, 64, 300, 0):
+        lp, st = binding.forward(G["h"], G["W"], G["target"], **meta_of(G), chunk_rows=chunk)
+        outs.append((lp.cpu(), st.cpu()))
+    for lp, st in outs[1:]:
+        assert torch.equal(lp.view(torch.int32), outs[0][0].view(torch.int32))
+        assert torch.equal(st, outs[0][1])
+    g = torch.full((300,), -1.0 / 300, device=dev())
+    gh1, gw1 = binding.backward(G["h"], G["W"], G["target"], outs[0][1].to(dev()), g, **meta_of(G))
+    gh2, gw2 = binding.backward(G["h"], G["W"], G["target"], outs[0][1].to(dev()), g, **meta_of(G))
+    gh3, gw3 = binding.backward(G["h"], G["W"], G["target"], outs[0][1].to(dev()), g, **meta_of(G),
+                                vocab_slice=7000)
+    assert torch.equal(gh1, gh2) and torch.equal(gw1, gw2)          # run to run
+    assert torch.equal(gw1, gw3)                                     # dW rows do not depend on the slicing
+    assert rel_fro(gh1.float().cpu().numpy(), gh3.float().cpu().numpy()) < 1e-2
+
+
+def test_null_metadata_equals_explicit_identity_metadata():
+    w = workloads.make("identity", T=260)
+    w["W"] = w["W"][:9000]
+    w["target_uniform"] = w["target_uniform"] % 9000
+    G = to_gpu(w, w["target_uniform"])
+    say("identity metadata: T=260 V=9000")
+    lp1, st1 = binding.forward(G["h"], G["W"], G["target"])
+    lp2, st2 = binding.forward(G["h"], G["W"], G["target"], **meta_of(G))
+    assert torch.equal(lp1.view(torch.int32), lp2.view(torch.int32)) and torch.equal(st1, st2)
+    g = torch.randn(260, device=dev())
+    a = binding.backward(G["h"], G["W"], G["target"], st1, g)
+    b = binding.backward(G["h"], G["W"], G["target"], st2, g, **meta_of(G))
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_per_row_temperature_matches_scaled_cross_entropy():
+    w = workloads.make("tiny", T=64)
+    w["top_k"][:] = 0
+    w["top_p"][:] = 1
+    w["min_p"][:] = 0
+    y = w["target_uniform"]
+    G, lp, st, gh, gw, keys = _run(w, y)
+    from scipy.special import log_softmax
+    z = oracle.chunk_logits(w["h"], w["W"]) / w["temperature"].astype(np.float64)[:, None]
+    ref = log_softmax(z, axis=1)[np.arange(64), y]
+    assert np.abs(lp.cpu().numpy() - ref).max() < 1e-4
+
+
+# ---------------------------------------------------------------- errors and out-of-support
+def test_invalid_rows_are_reported_and_inert():
+    w = workloads.make("headline", T=40)
+    w["W"] = w["W"][:5000]
+    y = w["target_uniform"] % 5000
+    G = to_gpu(w, y)
+    G["top_p"][7] = 1.5
+    G["temperature"][3] = 0.0
+    with pytest.raises(ValueError, match=r"temperature\[3\]"):
+        binding.forward(G["h"], G["W"], G["target"], **meta_of(G))
+    lp, st = binding.forward(G["h"], G["W"], G["target"], **meta_of(G), check=False)
+    lpc = lp.cpu().numpy()
+    assert np.isnan(lpc[3]) and np.isnan(lpc[7]) and not np.isnan(np.delete(lpc, [3, 7])).any()
+    g = torch.ones(40, device=dev())
+    gh, gw = binding.backward(G["h"], G["W"], G["target"], st, g, **meta_of(G))
+    assert not gh[3].any() and not gh[7].any()
+    G["target"][5] = 5000
+    with pytest.raises(ValueError, match=r"temperature\[3\]"):
+        binding.forward(G["h"], G["W"], G["target"], **meta_of(G))
+    G["temperature"][3] = 1.0
+    G["top_p"][7] = 0.5
+    with pytest.raises(ValueError, match=r"target\[5\]"):
+        binding.forward(G["h"], G["W"], G["target"], **meta_of(G))
+
+
+def test_out_of_support_targets_score_minus_inf_with_zero_gradient():
+    w = workloads.make("headline", T=64)
+    w["W"] = w["W"][:6000]
+    G0 = to_gpu(w, np.zeros(64, np.int64))
+    keys = binding.scaled_logits(G0["h"], G0["W"], G0["temperature"]).cpu().numpy()
+    y = np.array([oracle.order_row(keys[t])[-1] if t % 2 else oracle.order_row(keys[t])[0] for t in range(64)])
+    G = to_gpu(w, y)
+    lp, st = binding.forward(G["h"], G["W"], G["target"], **meta_of(G))
+    lpc = lp.cpu().numpy()
+    assert np.all(lpc[1::2] == -np.inf) and np.all(np.isfinite(lpc[0::2]))
+    g = torch.ones(64, device=dev())
+    gh, gw = binding.backward(G["h"], G["W"], G["target"], st, g, **meta_of(G))
+    assert not gh[1::2].any()
+    ref = oracle.forward(w["h"], w["W"], y, w["temperature"], w["top_k"], w["top_p"], w["min_p"], keys=keys)
+    dH, dW = oracle.backward(w["h"], w["W"], y, ref, np.ones(64), w["temperature"])
+    assert rel_fro(gw.cpu().numpy(), dW) < GRAD_RTOL

@@ -1,0 +1,134 @@
+"""Bit-exact support of the GPU selection kernel on adversarial fp32 key rows.
+
+``stce_support_from_logits`` runs the forward's selection kernel on given
+keys; the oracle computes the support of the very same keys.  The rows cover
+every path of the kernel: whole-row windows (V <= 4096), bounded candidates
+(top-k from tile maxima, min-p), the value histogram, and the radix
+refinement used when a histogram bin holds more tokens than the window
+(long tie groups, very peaked rows), plus the identities of the program."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import dev, say
+from sampling_transform_logprob_amd import binding
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load()
+
+
+def _check(keys, k, p, mp, y=None, label=""):
+    keys = np.ascontiguousarray(keys, np.float32)
+    R, V = keys.shape
+    k = np.asarray(k, np.int32)
+    p = np.asarray(p, np.float32)
+    mp = np.asarray(mp, np.float32)
+    y = np.zeros(R, np.int64) if y is None else np.asarray(y, np.int64)
+    say(f"support {label}: R={R} V={V}")
+    lp, st = binding.support_from_logits(torch.from_numpy(keys).to(dev()), torch.from_numpy(y).to(dev()),
+                                         torch.from_numpy(k).to(dev()), torch.from_numpy(p).to(dev()),
+                                         torch.from_numpy(mp).to(dev()))
+    info = binding.decode_state(st)
+    lpc = lp.cpu().numpy()
+    ref = oracle.support(keys, k, p, mp)
+    ok = ~ref["near"]
+    assert ref["near"].sum() == 0, f"{label}: {ref['near'].sum()} rows within rounding"
+    bad = np.nonzero(info["n"] != ref["n"])[0]
+    assert bad.size == 0, f"{label}: n differs at rows {bad[:8]}: gpu {info['n'][bad[:8]]} oracle {ref['n'][bad[:8]]}"
+    filt = (info["flags"] & binding.FLAG_FILTERED) != 0
+    bad = np.nonzero(filt & ((info["key_thr"] != ref["key_thr"]) | (info["id_thr"] != ref["id_thr"])))[0]
+    assert bad.size == 0, f"{label}: boundary differs at rows {bad[:8]}"
+    # selected logprob on the support, from the same keys
+    for r in range(R):
+        mask = oracle.in_support(keys[r], int(ref["key_thr"][r]), int(ref["id_thr"][r])) if filt[r] else \
+            np.ones(V, bool)
+        s64 = keys[r].astype(np.float64)
+        mx = s64[mask].max()
+        lse = mx + math.log(np.exp(s64[mask] - mx).sum())
+        want = min(s64[y[r]] - lse, 0.0) if mask[y[r]] else -math.inf
+        if math.isinf(want):
+            assert lpc[r] == -np.inf, (label, r)
+        else:
+            assert abs(lpc[r] - want) < 1e-4, (label, r, lpc[r], want)
+    return info
+
+
+def _grid(rng, V, R, ties):
+    keys = (rng.standard_normal((R, V)) * rng.uniform(0.3, 4, (R, 1))).astype(np.float32)
+    if ties:
+        keys = (np.round(keys * 4) / 4).astype(np.float32)
+    return keys
+
+
+@pytest.mark.parametrize("V", [4, 8, 300, 1000, 4096, 5000, 40000])
+def test_random_rows_all_filter_mixes(V):
+    rng = np.random.Generator(np.random.PCG64(V))
+    R = 96
+    keys = _grid(rng, V, R, ties=(V % 2 == 0))
+    ks = np.array([0, 1, 2, 20, 64, V - 1, V, V + 5, 4095, 4097])
+    ps = np.array([1.0, 0.9, 0.5, 1e-6, np.nextafter(np.float32(1), np.float32(0)), 0.99])
+    mps = np.array([0.0, 0.0, 0.1, 1.0, 1e-3])
+    k = np.maximum(ks[rng.integers(0, len(ks), R)], 0)
+    p = ps[rng.integers(0, len(ps), R)]
+    mp = mps[rng.integers(0, len(mps), R)]
+    y = rng.integers(0, V, R)
+    _check(keys, k, p, mp, y, f"random V={V}")
+
+
+def test_identities():
+    rng = np.random.Generator(np.random.PCG64(3))
+    V = 7000
+    keys = _grid(rng, V, 8, ties=True)
+    info = _check(keys, [0, V, V + 3, 0, 0, 0, 0, 0], [1.0] * 8, [0.0] * 8, label="identity rows")
+    assert np.all(info["n"] == V)
+
+
+def test_top_p_one_despite_fp32_overshoot():
+    V = 6000
+    keys = np.zeros((2, V), np.float32)      # equal keys: fp32 running sums of 1/V drift past 1
+    info = _check(keys, [0, 0], [1.0, 1.0], [0.0, 0.0], label="overshoot")
+    assert np.all(info["n"] == V)
+
+
+def test_tie_groups_longer_than_the_window():
+    V = 20000
+    keys = np.zeros((6, V), np.float32)
+    keys[1, :] = 1.5
+    keys[2, ::2] = 2.0                         # two long tie groups
+    keys[3, 5000:15000] = 3.0
+    keys[4] = np.where(np.arange(V) % 3 == 0, -0.0, 0.0)   # signed zeros are one key
+    keys[5, 17] = 5.0
+    k = [10000, 1, 9999, 7000, 4500, 12000]
+    _check(keys, k, [1.0, 1.0, 1.0, 0.3, 1.0, 1.0], [0.0] * 6, np.arange(6) * 997, "long ties")
+
+
+def test_peaked_rows_need_radix_refinement():
+    rng = np.random.Generator(np.random.PCG64(5))
+    V = 60000
+    keys = (rng.random((4, V)) * 1e-3).astype(np.float32)   # a narrow cluster...
+    keys[:, 123] = 40.0                                      # ...and one far outlier
+    k = [30000, 0, 25000, 0]
+    p = [1.0, 1.0, 0.9, 1.0]
+    mp = [0.0, 1e-30, 0.0, 0.0]
+    keys[3, :] = np.float32(7.0)
+    keys[3, ::7] = np.nextafter(np.float32(7.0), np.float32(8.0))
+    _check(keys, k, p, mp, [123, 5, 77, 14], "peaked")
+
+
+def test_min_p_keeps_whole_tie_groups_and_uses_unfiltered_max():
+    V = 9000
+    keys = np.full((3, V), -5.0, np.float32)
+    keys[:, :100] = 0.0
+    keys[:, 100:2000] = np.float32(math.log(0.1))           # exactly at the min-p threshold in fp32
+    keys[1, 7] = 3.0
+    info = _check(keys, [0, 0, 50], [1.0, 1.0, 1.0], [0.1, 0.1, 0.1], label="min-p groups")
+    assert info["n"][0] in (100, 2000)
