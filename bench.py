@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Throughput of the sampling-transform scoring core on one MI355X.
+
+One step = stce_forward + stce_backward (grad_hidden and grad_weight) over one
+batch of synthetic rows at the headline shape: T = 16,384 scored tokens,
+H = 5,120, V = 151,936, bf16 operands, fp32 logits, temperature 0.7,
+top-k 20, top-p 0.8, targets drawn from each row's filtered distribution.
+
+Prints one JSON line with scored tokens/s, the fraction of bf16 MFMA peak of
+the whole step (8 T H V flop: forward projection, backward recompute,
+hidden gradient, weight gradient), the roofline of the dominant kernel timed
+with HIP events around its launches inside the timed steps, and the fp64 CPU
+oracle timed on a bounded sample of the same rows.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def sample_targets_gpu(h, W, meta, u, chunk=1024):
+    """Targets drawn from each row's filtered distribution, with plain torch
+    ops on the GPU (input preparation, outside the timed region)."""
+    import torch
+    T = h.shape[0]
+    Wf = W.float()
+    out = torch.empty(T, dtype=torch.int64, device=h.device)
+    uu = torch.from_numpy(u).to(h.device)
+    for c0 in range(0, T, chunk):
+        c1 = min(T, c0 + chunk)
+        z = (h[c0:c1].float() @ Wf.T) / meta["temperature"][c0:c1, None]
+        s, idx = torch.sort(z, dim=1, descending=True, stable=True)
+        prob = torch.softmax(s, dim=1)
+        before = torch.cumsum(prob, dim=1) - prob
+        keep = before < meta["top_p"][c0:c1, None]
+        keep |= (meta["top_p"][c0:c1, None] >= 1.0)
+        k = meta["top_k"][c0:c1, None].long()
+        ar = torch.arange(s.shape[1], device=h.device)[None, :]
+        keep &= (k <= 0) | (ar < k)
+        mp = meta["min_p"][c0:c1, None]
+        keep &= (mp <= 0) | ((s - s[:, :1]) >= torch.log(mp.clamp_min(1e-30)))
+        q = prob * keep
+        cdf = torch.cumsum(q, dim=1)
+        pick = torch.searchsorted(cdf, (uu[c0:c1] * cdf[:, -1]).float()[:, None].contiguous())
+        pick = torch.minimum(pick, keep.sum(1, keepdim=True) - 1)
+        out[c0:c1] = idx.gather(1, pick)[:, 0]
+        del z, s, idx, prob, before, keep, q, cdf
+    del Wf
+    return out
+
+
+class HipEvents:
+    """Raw hipEvent_t handles for the library's per-launch timing hook."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.start = (ctypes.c_void_p * n)()
+        self.stop = (ctypes.c_void_p * n)()
+        for arr in (self.start, self.stop):
+            for i in range(n):
+                ev = ctypes.c_void_p()
+                assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+                arr[i] = ev
+        self.kind = (ctypes.c_int32 * n)()
+        self.n = n
+
+    def elapsed_ms(self, i):
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.start[i]),
+                                            ctypes.c_void_p(self.stop[i])) == 0
+        return ms.value
+
+
+def cpu_baseline(w, y, rows):
+    """fp64 oracle (as it stands) on a bounded sample of the same rows."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count()
+    sel = np.arange(rows)
+    g = np.full(w["T"], -1.0 / w["T"])
+    t0 = time.perf_counter()
+    f = oracle.forward(w["h"], w["W"], y, w["temperature"], w["top_k"], w["top_p"], w["min_p"], rows=sel)
+    oracle.backward(w["h"], w["W"], y, f, g, w["temperature"])
+    dt = time.perf_counter() - t0
+    return dict(value=rows / dt, unit="scored tokens/s", cores=int(cores), kind="oracle",
+                sample=f"first {rows} rows of the same workload, forward + backward (their grad_hidden rows "
+                       f"and their whole grad_weight contribution), fp64 numpy, {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="headline")
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chunk-rows", type=int, default=0)
+    ap.add_argument("--vocab-slice", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sampling_transform_logprob_amd import binding, workloads
+    L = binding.load()
+    dev = torch.device("cuda:0")
+
+    log(f"[bench] generating {args.config} inputs")
+    w = workloads.make(args.config)
+    T, H, V = w["T"], w["H"], w["V"]
+    dt = torch.float32 if w["dtype"] == "f32" else torch.bfloat16
+    h = torch.from_numpy(w["h"]).to(dev).to(dt)
+    W = torch.from_numpy(w["W"]).to(dev).to(dt)
+    meta = dict(temperature=torch.from_numpy(w["temperature"]).to(dev), top_k=torch.from_numpy(w["top_k"]).to(dev),
+                top_p=torch.from_numpy(w["top_p"]).to(dev), min_p=torch.from_numpy(w["min_p"]).to(dev))
+    log("[bench] drawing targets from the filtered distributions")
+    if w["filtered"]:
+        target = sample_targets_gpu(h, W, meta, w["u"])
+    else:
+        target = torch.from_numpy(w["target_uniform"]).to(dev)
+    torch.cuda.synchronize()
+
+    prob, keep = binding.make_problem(h, W, target, meta["temperature"], meta["top_k"], meta["top_p"],
+                                      meta["min_p"], args.chunk_rows, args.vocab_slice)
+    fwd_b, bwd_b = binding.workspace_bytes(prob)
+    ws_f = torch.empty(fwd_b, dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(bwd_b, dtype=torch.uint8, device=dev)
+    logprob = torch.empty(T, dtype=torch.float32, device=dev)
+    state = torch.empty(T * binding.STATE_BYTES_PER_ROW, dtype=torch.uint8, device=dev)
+    gh = torch.empty(T, H, dtype=dt, device=dev)
+    gw = torch.empty(V, H, dtype=torch.float32, device=dev)
+    g = torch.full((T,), -1.0 / T, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = ctypes.byref(prob)
+
+    def step():
+        binding._check(L.stce_forward(P, ctypes.c_void_p(logprob.data_ptr()), ctypes.c_void_p(state.data_ptr()),
+                                      None, ctypes.c_void_p(ws_f.data_ptr()), fwd_b, stream))
+        binding._check(L.stce_backward(P, ctypes.c_void_p(g.data_ptr()), ctypes.c_void_p(state.data_ptr()),
+                                       ctypes.c_void_p(gh.data_ptr()), ctypes.c_void_p(gw.data_ptr()), 0, None,
+                                       ctypes.c_void_p(ws_b.data_ptr()), bwd_b, stream))
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    in_support = float((logprob > -float("inf")).float().mean().item())
+
+    ev = HipEvents(256 * max(args.steps, 1))
+    prof = binding.Profile(ev.n, 0, ctypes.cast(ev.start, ctypes.POINTER(ctypes.c_void_p)),
+                           ctypes.cast(ev.stop, ctypes.POINTER(ctypes.c_void_p)),
+                           ctypes.cast(ev.kind, ctypes.POINTER(ctypes.c_int32)))
+    log(f"[bench] timing {args.steps} steps")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    L.stce_profile_attach(ctypes.byref(prof))
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        step()
+    t_end.record()
+    torch.cuda.synchronize()
+    L.stce_profile_attach(None)
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+
+    # per-kind launch statistics from the events recorded around each launch
+    kinds = {}
+    for i in range(prof.count):
+        k = binding.KERNEL_KINDS.get(ev.kind[i], str(ev.kind[i]))
+        kinds.setdefault(k, []).append(ev.elapsed_ms(i))
+    # algorithmic flop per launch of each product
+    C = min(T, args.chunk_rows or 4096)
+    Vs = min(V, args.vocab_slice or 16384)
+    nsl = -(-V // Vs)
+    per_launch = {
+        "projection": 2.0 * H * V * T / -(-T // C),
+        "dlogits": 2.0 * T * H * V / nsl,
+        "grad_weight": 2.0 * T * H * V / nsl,
+        "grad_hidden": 2.0 * T * H * V / nsl,
+    }
+    stats = {}
+    for k, v in kinds.items():
+        a = np.array(v)
+        stats[k] = dict(launches=int(len(a) / args.steps), avg_ms=float(a.mean()), total_ms_per_step=float(a.sum() / args.steps))
+        if k in per_launch:
+            stats[k]["tflops"] = per_launch[k] / (a.mean() * 1e-3) / 1e12
+    dom = max((k for k in stats if k in per_launch), key=lambda k: stats[k]["total_ms_per_step"])
+    achieved = stats[dom]["tflops"]
+
+    flop_step = 8.0 * T * H * V
+    value = T / (ms_step * 1e-3)
+    out = {
+        "metric": "scored tokens/s fwd+bwd at V=151936,H=5120; % of bf16 MFMA peak",
+        "value": value,
+        "unit": "scored tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded PCG64; h ~ N(0,1), W ~ N(0,0.02^2), bf16; targets drawn from the filtered "
+                "distributions)",
+        "config": {"workload": f"{args.config}: T={T} scored tokens, H={H}, V={V}, temperature "
+                               f"{'per-row' if args.config != 'headline' else 0.7}, top_k "
+                               f"{int(w['top_k'].max())}, top_p {float(w['top_p'].min())}, min_p "
+                               f"{float(w['min_p'].max())}; forward + backward (grad_hidden, grad_weight)",
+                   "T": T, "H": H, "V": V, "chunk_rows": C, "vocab_slice": Vs},
+        "mfma_peak_frac": flop_step / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "tflops_8thv": flop_step / (ms_step * 1e-3) / 1e12,
+        "tflops_6thv": 6.0 * T * H * V / (ms_step * 1e-3) / 1e12,
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "kernels": stats,
+        "targets_in_support": in_support,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows")
+        w_np = dict(w)
+        out["cpu_baseline"] = cpu_baseline(w_np, target.cpu().numpy(), args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -179,6 +179,30 @@ typedef struct stce_row_info {
 } stce_row_info;
 stce_status stce_decode_state(const void *host_state, int64_t nrows, stce_row_info *out);
 
+/* Diagnostics: per-launch HIP event timing.  While a profile is attached to
+ * the calling thread, each kernel launch the library makes from that thread
+ * records start[i] before and stop[i] after the launch on the call's stream
+ * and stores the launch's kind (STCE_KERNEL_*) in kind[i], for
+ * i = count++ while count < capacity (later launches are not recorded).
+ * start/stop hold hipEvent_t handles created by the caller, who also reads
+ * the elapsed times.  Pass NULL to detach.  Thread-local; never fails. */
+#define STCE_KERNEL_VALIDATE 1
+#define STCE_KERNEL_PROJECTION 2  /* forward logits product + keys epilogue */
+#define STCE_KERNEL_SELECT 3      /* support program + selected logprob */
+#define STCE_KERNEL_DLOGITS 4     /* backward recompute product + dlogits epilogue */
+#define STCE_KERNEL_GRAD_WEIGHT 5 /* weight-gradient product of one slice */
+#define STCE_KERNEL_GRAD_HIDDEN 6 /* hidden-gradient product of one slice */
+#define STCE_KERNEL_TRANSPOSE 7
+#define STCE_KERNEL_PARTIALS 8
+typedef struct stce_profile {
+  int32_t capacity;
+  int32_t count;
+  void **start;
+  void **stop;
+  int32_t *kind;
+} stce_profile;
+stce_status stce_profile_attach(stce_profile *prof);
+
 /* Human-readable name of a status code (static string). */
 const char *stce_status_string(stce_status status);
 

@@ -26,8 +26,10 @@ DT_BF16, DT_F32 = 1, 2
 SYMBOLS = (
     "stce_state_bytes", "stce_workspace_bytes", "stce_forward", "stce_backward",
     "stce_scaled_logits", "stce_support_from_logits", "stce_support_workspace_bytes",
-    "stce_decode_state", "stce_status_string", "stce_last_error",
+    "stce_decode_state", "stce_status_string", "stce_last_error", "stce_profile_attach",
 )
+KERNEL_KINDS = {1: "validate", 2: "projection", 3: "select", 4: "dlogits", 5: "grad_weight",
+                6: "grad_hidden", 7: "transpose", 8: "partials"}
 
 
 class Problem(ctypes.Structure):
@@ -46,6 +48,12 @@ class RowInfo(ctypes.Structure):
         ("flags", ctypes.c_uint32), ("lse_support", ctypes.c_float), ("lse_full", ctypes.c_float),
         ("row_max", ctypes.c_float), ("target_key", ctypes.c_float),
     ]
+
+
+class Profile(ctypes.Structure):
+    _fields_ = [("capacity", ctypes.c_int32), ("count", ctypes.c_int32),
+                ("start", ctypes.POINTER(ctypes.c_void_p)), ("stop", ctypes.POINTER(ctypes.c_void_p)),
+                ("kind", ctypes.POINTER(ctypes.c_int32))]
 
 
 class StceError(RuntimeError):
@@ -75,6 +83,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "stce_decode_state": (ctypes.c_int, [vp, i64, ctypes.POINTER(RowInfo)]),
         "stce_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "stce_last_error": (ctypes.c_char_p, []),
+        "stce_profile_attach": (ctypes.c_int, [ctypes.POINTER(Profile)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

@@ -13,6 +13,8 @@ using namespace stce;
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local stce_profile* g_prof = nullptr;
+thread_local int g_prof_open = -1;
 
 stce_status fail(stce_status s, const char* fmt, ...) {
   va_list ap;
@@ -115,7 +117,31 @@ T* at(void* ws, size_t off) {
 
 }  // namespace
 
+namespace stce {
+void prof_begin(int kind, hipStream_t s) {
+  stce_profile* p = g_prof;
+  if (!p || p->count >= p->capacity) {
+    g_prof_open = -1;
+    return;
+  }
+  g_prof_open = p->count++;
+  p->kind[g_prof_open] = kind;
+  hipEventRecord((hipEvent_t)p->start[g_prof_open], s);
+}
+void prof_end(hipStream_t s) {
+  if (g_prof && g_prof_open >= 0) hipEventRecord((hipEvent_t)g_prof->stop[g_prof_open], s);
+  g_prof_open = -1;
+}
+}  // namespace stce
+
 extern "C" {
+
+stce_status stce_profile_attach(stce_profile* prof) {
+  g_prof = prof;
+  g_prof_open = -1;
+  return STCE_OK;
+}
+
 
 size_t stce_state_bytes(int64_t T) { return T > 0 ? (size_t)T * STCE_STATE_BYTES_PER_ROW : 0; }
 

@@ -109,6 +109,7 @@ hipError_t launch_gemm(const Main& mn, const Epi& ep, int64_t tiles_m, int64_t t
 hipError_t launch_validate(int64_t T, int64_t V, const float* temp, const int32_t* top_k, const float* top_p,
                            const float* min_p, const int64_t* target, uint32_t* flags, int64_t* status,
                            hipStream_t s) {
+  ProfScope ps(1, s);
   hipLaunchKernelGGL(validate_kernel, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, s, T, V, temp, top_k,
                      top_p, min_p, target, flags, status);
   return hipGetLastError();
@@ -121,6 +122,7 @@ hipError_t launch_fill_i64(int64_t* p, int64_t v, hipStream_t s) {
 
 hipError_t launch_transpose_bf16(const bf16* in, int64_t ld_in, int64_t R, int64_t Cc, bf16* out,
                                  int64_t ld_out, int64_t R_pad, hipStream_t s) {
+  ProfScope ps(7, s);
   hipLaunchKernelGGL(transpose_kernel<bf16>, dim3((unsigned)ceil_div(R_pad, 64), (unsigned)ceil_div(Cc, 64)),
                      dim3(256), 0, s, in, ld_in, R, Cc, out, ld_out, R_pad);
   return hipGetLastError();
@@ -128,6 +130,7 @@ hipError_t launch_transpose_bf16(const bf16* in, int64_t ld_in, int64_t R, int64
 
 hipError_t launch_transpose_f32(const float* in, int64_t ld_in, int64_t R, int64_t Cc, float* out,
                                 int64_t ld_out, int64_t R_pad, hipStream_t s) {
+  ProfScope ps(7, s);
   hipLaunchKernelGGL(transpose_kernel<float>, dim3((unsigned)ceil_div(R_pad, 64), (unsigned)ceil_div(Cc, 64)),
                      dim3(256), 0, s, in, ld_in, R, Cc, out, ld_out, R_pad);
   return hipGetLastError();
@@ -135,6 +138,7 @@ hipError_t launch_transpose_f32(const float* in, int64_t ld_in, int64_t R, int64
 
 hipError_t launch_tile_partials(const float* sk, int64_t ld, int64_t R, int64_t V, int ntv,
                                 const int64_t* target, TilePart* part, float* s_y, hipStream_t st) {
+  ProfScope ps(8, st);
   hipLaunchKernelGGL(tile_partials_kernel, dim3((unsigned)R, (unsigned)ceil_div(ntv, 4)), dim3(256), 0, st, sk,
                      ld, R, V, ntv, target, part, s_y);
   return hipGetLastError();
@@ -155,6 +159,7 @@ hipError_t launch_fwd_projection(const FwdArgs& a, hipStream_t s) {
   ep.V = (int)a.V;
   ep.N = (int)a.rows;
   const int64_t tm = ceil_div(a.V, GM), tn = ceil_div(a.rows, GN);
+  ProfScope ps(2, s);
   if (a.dtype == 1) {
     MainBf16 mn{(const bf16*)a.W, a.H, (int)a.V, (const bf16*)a.h, a.H, (int)a.rows, (int)a.H};
     return launch_gemm(mn, ep, tm, tn, s);
@@ -173,6 +178,7 @@ hipError_t bwd_slice_impl(const BwdSliceArgs& a, hipStream_t s) {
     EpiDlogits<E> ep{a.temp, a.target, a.st, a.g, (E*)a.d, a.ld_d, (E*)a.dT, a.Tp,
                      (int)a.v0, (int)a.vs, (int)a.vsp, (int)a.T, (int)a.Tp};
     Main mn{W + a.v0 * a.H, a.H, (int)a.vs, (const E*)a.h, a.H, (int)a.T, (int)a.H};
+    ProfScope ps(4, s);
     e = launch_gemm(mn, ep, ceil_div(a.vsp, GM), ceil_div(a.Tp, GN), s);
     if (e != hipSuccess) return e;
   }
@@ -180,6 +186,7 @@ hipError_t bwd_slice_impl(const BwdSliceArgs& a, hipStream_t s) {
   if (a.grad_weight) {
     EpiStore ep{a.grad_weight + a.v0 * a.H, a.H, (int)a.vs, (int)a.H, a.accumulate_w};
     Main mn{(const E*)a.dT, a.Tp, (int)a.vsp, (const E*)a.hT, a.Tp, (int)a.H, (int)a.Tp};
+    ProfScope ps(5, s);
     e = launch_gemm(mn, ep, ceil_div(a.vsp, GM), ceil_div(a.H, GN), s);
     if (e != hipSuccess) return e;
   }
@@ -192,6 +199,7 @@ hipError_t bwd_slice_impl(const BwdSliceArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     EpiAccum<E> ep{a.dh_sum, a.H, (E*)a.grad_hidden, (int)a.T, (int)a.H, a.first, a.last};
     Main mn{(const E*)a.d, a.ld_d, (int)a.T, (const E*)a.WT, a.ld_d, (int)a.H, (int)a.vsp};
+    ProfScope ps(6, s);
     e = launch_gemm(mn, ep, ceil_div(a.T, GM), ceil_div(a.H, GN), s);
     if (e != hipSuccess) return e;
   }

@@ -6,6 +6,15 @@
 
 namespace stce {
 
+// Launch-timing hook (no-op unless a profile is attached to this thread).
+void prof_begin(int kind, hipStream_t s);
+void prof_end(hipStream_t s);
+struct ProfScope {
+  hipStream_t s;
+  ProfScope(int kind, hipStream_t st) : s(st) { prof_begin(kind, st); }
+  ~ProfScope() { prof_end(s); }
+};
+
 // Per-row metadata validation: flags[t] = ROW_VALID | ROW_FILTERED or 0, and
 // the first bad (row << 8 | field) into *status with an atomic min.
 hipError_t launch_validate(int64_t T, int64_t V, const float* temp, const int32_t* top_k, const float* top_p,

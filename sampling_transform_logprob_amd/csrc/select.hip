@@ -1,5 +1,6 @@
 // Support program + selected logprob, one workgroup of 256 threads per row.
 // The algorithm is described in select.hpp.
+#include "kernels.hpp"
 #include "select.hpp"
 
 namespace stce {
@@ -445,6 +446,7 @@ __global__ __launch_bounds__(ST) void select_kernel(SelParams P) {
 
 void launch_select(const SelParams& p, int rows, hipStream_t stream) {
   if (rows <= 0) return;
+  ProfScope ps(3, stream);
   hipLaunchKernelGGL(select_kernel, dim3(rows), dim3(ST), 0, stream, p);
 }
 
