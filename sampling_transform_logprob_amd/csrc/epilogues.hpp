@@ -7,10 +7,6 @@ namespace stce {
 
 #define STCE_INF __builtin_huge_valf()
 
-// Index helpers for the accumulator layout.
-__device__ inline int acc_row(int wm, int i, int r, int half) { return wm * 128 + i * 32 + (r >> 2) * 8 + half * 4 + (r & 3); }
-__device__ inline int acc_col(int wn, int j, int col) { return wn * 128 + j * 32 + col; }
-
 // (max, sum of exp(x - max)) merge; max = -inf means "empty".
 __device__ inline void lse_merge(float& mx, float& sm, float omx, float osm) {
   const float M = fmaxf(mx, omx);
@@ -47,13 +43,13 @@ struct EpiLogits {
   int V;                   // valid vocabulary rows
   int N;                   // valid tokens
 
-  __device__ inline void operator()(f32x16 (&acc)[4][4], int m0, int n0, char* smem) const {
+  __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1, half = lane >> 5, col = lane & 31;
+    const int wm = w >> 2, wn = w & 3, half = lane >> 5, col = lane & 31;
     const int mb = m0 + wm * 128;
-    float pmx[4], psm[4], pmn[4];
+    float pmx[ACC_J], psm[ACC_J], pmn[ACC_J];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < ACC_J; ++j) {
       const int n = n0 + acc_col(wn, j, col);
       const bool nv = n < N;
       const float t = (nv && temp) ? temp[n] : 1.0f;
@@ -121,7 +117,7 @@ struct EpiLogits {
     float* red = (float*)smem;  // [2][256][3]
     if (half == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < ACC_J; ++j) {
         const int tok = acc_col(wn, j, col);
         red[(wm * 256 + tok) * 3 + 0] = pmx[j];
         red[(wm * 256 + tok) * 3 + 1] = psm[j];
@@ -131,7 +127,7 @@ struct EpiLogits {
     __syncthreads();
     if (wm == 0 && half == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < ACC_J; ++j) {
         const int tok = acc_col(wn, j, col);
         const int n = n0 + tok;
         if (n < N) {
@@ -170,11 +166,11 @@ struct EpiDlogits {
   int64_t ld_dT;
   int v0, Vs, Vs_pad, N, N_pad;
 
-  __device__ inline void operator()(f32x16 (&acc)[4][4], int m0, int n0, char* smem) const {
+  __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1, half = lane >> 5, col = lane & 31;
+    const int wm = w >> 2, wn = w & 3, half = lane >> 5, col = lane & 31;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < ACC_J; ++j) {
       const int n = n0 + acc_col(wn, j, col);
       const bool nv = n < N;
       const float t = (nv && temp) ? temp[n] : 1.0f;
@@ -186,40 +182,31 @@ struct EpiDlogits {
         y = target[n];
         if ((rs.flags & (ROW_VALID | ROW_IN_SUPPORT)) == (ROW_VALID | ROW_IN_SUPPORT)) c = g[n] / t;
       }
+      if (n >= N_pad) continue;
+      OutT* dr = d + (int64_t)n * ld_d;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + acc_row(wm, i, r, half);
-          const int vg = v0 + m;
-          const float s = scale_key(acc[i][j][r], t);
-          const uint32_t key = order_key(s);
-          const bool in = key > rs.key_thr || (key == rs.key_thr && vg <= rs.id_thr);
-          const float q = in ? __expf(s - rs.lse_s) : 0.f;
-          // rows with c == 0 (out of support, invalid, padding) give exact
-          // zeros, whatever q is
-          acc[i][j][r] = (c != 0.f && m < Vs) ? c * ((vg == y ? 1.f : 0.f) - q) : 0.f;
+        for (int gq = 0; gq < 4; ++gq) {
+          const int mm = m0 + wm * 128 + i * 32 + gq * 8 + half * 4;  // 4 consecutive rows
+          if (mm >= Vs_pad) continue;
+          OutT v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = mm + e;
+            const int vg = v0 + m;
+            const float s = scale_key(acc[i][j][gq * 4 + e], t);
+            const uint32_t key = order_key(s);
+            const bool in = key > rs.key_thr || (key == rs.key_thr && vg <= rs.id_thr);
+            const float q = in ? __expf(s - rs.lse_s) : 0.f;
+            // rows with c == 0 (out of support, invalid, padding) give exact
+            // zeros, whatever q is
+            v[e] = (OutT)((c != 0.f && m < Vs) ? c * ((vg == y ? 1.f : 0.f) - q) : 0.f);
+            dT[(int64_t)m * ld_dT + n] = v[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dr[mm + e] = v[e];
         }
-      if (n < N_pad) {
-        OutT* dr = d + (int64_t)n * ld_d;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int mm = m0 + wm * 128 + i * 32 + gq * 8 + half * 4;
-            if (mm < Vs_pad) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) dr[mm + e] = (OutT)acc[i][j][gq * 4 + e];
-            }
-          }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = m0 + acc_row(wm, i, r, half);
-            if (m < Vs_pad) dT[(int64_t)m * ld_dT + n] = (OutT)acc[i][j][r];
-          }
-      }
     }
   }
 };
@@ -233,11 +220,11 @@ struct EpiStore {
   int M, N;
   int accumulate;
 
-  __device__ inline void operator()(f32x16 (&acc)[4][4], int m0, int n0, char*) const {
+  __device__ inline void operator()(AccTile& acc, int m0, int n0, char*) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1, half = lane >> 5, col = lane & 31;
+    const int wm = w >> 2, wn = w & 3, half = lane >> 5, col = lane & 31;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < ACC_J; ++j) {
       const int n = n0 + acc_col(wn, j, col);
       if (n >= N) continue;
 #pragma unroll
@@ -267,11 +254,11 @@ struct EpiAccum {
   int M, N;
   int first, last;
 
-  __device__ inline void operator()(f32x16 (&acc)[4][4], int m0, int n0, char*) const {
+  __device__ inline void operator()(AccTile& acc, int m0, int n0, char*) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1, half = lane >> 5, col = lane & 31;
+    const int wm = w >> 2, wn = w & 3, half = lane >> 5, col = lane & 31;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < ACC_J; ++j) {
       const int n = n0 + acc_col(wn, j, col);
       if (n >= N) continue;
 #pragma unroll

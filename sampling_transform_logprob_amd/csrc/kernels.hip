@@ -99,7 +99,7 @@ hipError_t launch_gemm(const Main& mn, const Epi& ep, int64_t tiles_m, int64_t t
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Main::LDS_BYTES);
   if (attr != hipSuccess) return attr;
-  TileMap map{(int)tiles_m, (int)tiles_n, 8};
+  TileMap map{(int)tiles_m, (int)tiles_n, 4};
   hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(GTHREADS), Main::LDS_BYTES, s, mn, ep, map);
   return hipGetLastError();
 }
