@@ -193,3 +193,31 @@ def test_out_of_support_targets_score_minus_inf_with_zero_gradient():
     ref = oracle.forward(w["h"], w["W"], y, w["temperature"], w["top_k"], w["top_p"], w["min_p"], keys=keys)
     dH, dW = oracle.backward(w["h"], w["W"], y, ref, np.ones(64), w["temperature"])
     assert rel_fro(gw.cpu().numpy(), dW) < GRAD_RTOL
+
+
+# ---------------------------------------------------------------- ragged and tiny shapes
+@pytest.mark.parametrize("T,H,V,dtype", [(300, 72, 1000, "bf16"), (7, 8, 1, "bf16"), (33, 136, 3, "bf16"),
+                                         (257, 200, 257, "bf16"), (130, 24, 4500, "f32"), (5, 64, 9000, "bf16")])
+def test_ragged_shapes(T, H, V, dtype):
+    rng = np.random.Generator(np.random.PCG64(T * 1000 + V))
+    from sampling_transform_logprob_amd.workloads import round_bf16
+    h = rng.standard_normal((T, H)).astype(np.float32)
+    W = (rng.standard_normal((V, H)) * 0.3).astype(np.float32)
+    if dtype == "bf16":
+        h, W = round_bf16(h), round_bf16(W)
+    temp = rng.uniform(0.5, 1.5, T).astype(np.float32)
+    k = rng.choice([0, 1, 2, 5, V], T).astype(np.int32)
+    p = rng.choice([1.0, 0.9, 0.5], T).astype(np.float32)
+    mp = rng.choice([0.0, 0.1], T).astype(np.float32)
+    w = dict(h=h, W=W, temperature=temp, top_k=k, top_p=p, min_p=mp, dtype=dtype, u=rng.random(T), filtered=True)
+    say(f"ragged: T={T} H={H} V={V} {dtype}")
+    y = targets(w)
+    g = rng.standard_normal(T)
+    G, lp, st, gh, gw, keys = _run(w, y, g, chunk_rows=128, vocab_slice=max(1, V // 3))
+    ref = oracle.forward(h, W, y, temp, k, p, mp, keys=keys.cpu().numpy())
+    info = binding.decode_state(st)
+    assert check_support(info, ref, "ragged") == 0
+    check_logprob(lp.cpu().numpy(), ref)
+    dH, dW = oracle.backward(h, W, y, ref, g, temp)
+    assert rel_fro(gh.float().cpu().numpy(), dH) < GRAD_RTOL
+    assert rel_fro(gw.cpu().numpy(), dW) < GRAD_RTOL
