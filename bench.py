@@ -192,8 +192,7 @@ def main():
         k = binding.KERNEL_KINDS.get(ev.kind[i], str(ev.kind[i]))
         kinds.setdefault(k, []).append(ev.elapsed_ms(i))
     # algorithmic flop per launch of each product
-    C = min(T, args.chunk_rows or 4096)
-    Vs = min(V, args.vocab_slice or 16384)
+    C, Vs = binding.schedule(prob)
     nsl = -(-V // Vs)
     per_launch = {
         "projection": 2.0 * H * V * T / -(-T // C),

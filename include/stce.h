@@ -118,6 +118,11 @@ size_t stce_state_bytes(int64_t T);
  * Either output pointer may be NULL. */
 stce_status stce_workspace_bytes(const stce_problem *prob, size_t *fwd, size_t *bwd);
 
+/* The chunk and slice sizes the library will use for this problem: forward
+ * rows per chunk and backward vocabulary columns per slice (the problem's
+ * own values when non-zero, else the defaults).  Either pointer may be NULL. */
+stce_status stce_schedule(const stce_problem *prob, int64_t *chunk_rows, int64_t *vocab_slice);
+
 /* Forward: logprob[t] = min(s[t, y_t] - logsumexp_{j in S_t} s[t, j], 0) if
  * y_t is in the support S_t, else -inf, with s = fl32(h W^T) / T per row.
  * Writes logprob [T] fp32 and state [T * 32 bytes] (support boundary,

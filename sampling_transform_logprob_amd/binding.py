@@ -26,7 +26,7 @@ DT_BF16, DT_F32 = 1, 2
 SYMBOLS = (
     "stce_state_bytes", "stce_workspace_bytes", "stce_forward", "stce_backward",
     "stce_scaled_logits", "stce_support_from_logits", "stce_support_workspace_bytes",
-    "stce_decode_state", "stce_status_string", "stce_last_error", "stce_profile_attach",
+    "stce_decode_state", "stce_status_string", "stce_last_error", "stce_profile_attach", "stce_schedule",
 )
 KERNEL_KINDS = {1: "validate", 2: "projection", 3: "select", 4: "dlogits", 5: "grad_weight",
                 6: "grad_hidden", 7: "transpose", 8: "partials"}
@@ -84,6 +84,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "stce_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "stce_last_error": (ctypes.c_char_p, []),
         "stce_profile_attach": (ctypes.c_int, [ctypes.POINTER(Profile)]),
+        "stce_schedule": (ctypes.c_int, [P, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -156,6 +157,13 @@ def workspace_bytes(prob: Problem):
     f, b = ctypes.c_size_t(), ctypes.c_size_t()
     _check(load().stce_workspace_bytes(ctypes.byref(prob), ctypes.byref(f), ctypes.byref(b)))
     return f.value, b.value
+
+
+def schedule(prob: Problem):
+    """(forward rows per chunk, backward vocabulary columns per slice)."""
+    c, v = ctypes.c_int64(), ctypes.c_int64()
+    _check(load().stce_schedule(ctypes.byref(prob), ctypes.byref(c), ctypes.byref(v)))
+    return c.value, v.value
 
 
 def _raise_rows(status: torch.Tensor, what: str, tensors: dict) -> None:

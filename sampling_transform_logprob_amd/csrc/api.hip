@@ -29,7 +29,10 @@ stce_status hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kDefaultChunk = 4096;   // forward rows per chunk
-constexpr int64_t kDefaultSlice = 16384;  // backward vocabulary columns per slice
+// Default backward slice: the widest (multiple of 256) whose dz copies (token-
+// and vocab-major, 2 x T x V_s elements) fit in this many bytes.  Wider
+// slices mean fewer read-modify-write passes over the fp32 dH sum.
+constexpr double kSliceBudgetBytes = 8e9;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -75,7 +78,16 @@ Layout plan(const stce_problem* p) {
   L.f_sy = o;    o = align_up(o + 4 * (size_t)L.C);
   L.fwd = o;
 
-  L.Vs = p->vocab_slice > 0 ? p->vocab_slice : kDefaultSlice;
+  if (p->vocab_slice > 0) {
+    L.Vs = p->vocab_slice;
+  } else {
+    const double per_col = 2.0 * (double)round_up(T, 64) * (double)es;
+    int64_t fit = (int64_t)(kSliceBudgetBytes / per_col) / 256 * 256;
+    if (fit < 4096) fit = 4096;
+    // equal slices: ceil(V / fit) of them
+    const int64_t n = ceil_div(V, fit);
+    L.Vs = round_up(ceil_div(V, n), 256);
+  }
   if (L.Vs > V) L.Vs = V;
   L.Vsp = round_up(L.Vs, 64);
   L.Tp = round_up(T, 64);
@@ -151,6 +163,15 @@ stce_status stce_workspace_bytes(const stce_problem* prob, size_t* fwd, size_t* 
   const Layout L = plan(prob);
   if (fwd) *fwd = L.fwd;
   if (bwd) *bwd = L.bwd;
+  return STCE_OK;
+}
+
+stce_status stce_schedule(const stce_problem* prob, int64_t* chunk_rows, int64_t* vocab_slice) {
+  stce_status s = check_shapes(prob);
+  if (s) return s;
+  const Layout L = plan(prob);
+  if (chunk_rows) *chunk_rows = L.C;
+  if (vocab_slice) *vocab_slice = L.Vs;
   return STCE_OK;
 }
 

@@ -18,10 +18,23 @@ __device__ inline void lse_merge(float& mx, float& sm, float omx, float osm) {
   mx = M;
 }
 
-// Per-row temperature: s = fl32(z / T).  IEEE division (correctly rounded);
-// the same expression is used by the forward and the backward epilogue, so
-// the backward's keys are the forward's keys bit for bit.
-__device__ inline float scale_key(float z, float t) { return z / t; }
+// Per-row temperature: s = fl32(z / T), correctly rounded, from the row's
+// correctly rounded reciprocal r = fl32(1 / T): q0 = fl32(z r) is within one
+// ulp of z / T, the fma gives the remainder z - q0 T exactly, and one more
+// fma rounds q0 + (z - q0 T) r to the correctly rounded quotient (Markstein's
+// correction step, as used for IA-64 division).  The remainder is about
+// |z| 2^-24, so it stays a normal number only when |z| and |q0| are at least
+// 2^-100; tiny, zero, huge or infinite operands take the plain IEEE division
+// (logits that small are zeros in practice).  Forward and backward
+// epilogues use this one function, so the backward's keys are the forward's
+// keys bit for bit.
+__device__ inline float scale_key(float z, float t, float r) {
+  const float q0 = z * r;
+  const float a = __builtin_fabsf(q0);
+  if (!(a >= 0x1p-100f && __builtin_fabsf(z) >= 0x1p-100f && a <= 0x1p+126f)) return z / t;
+  const float e = __builtin_fmaf(-q0, t, z);
+  return __builtin_fmaf(e, r, q0);
+}
 
 // ---------------------------------------------------------------------------
 // Forward projection epilogue.  M = vocabulary, N = tokens of the chunk.
@@ -53,12 +66,13 @@ struct EpiLogits {
       const int n = n0 + acc_col(wn, j, col);
       const bool nv = n < N;
       const float t = (nv && temp) ? temp[n] : 1.0f;
+      const float rt = 1.0f / t;
       float mx = -STCE_INF, mn = STCE_INF;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float s = scale_key(acc[i][j][r], t);
+          const float s = scale_key(acc[i][j][r], t, rt);
           acc[i][j][r] = s;
           if (m0 + acc_row(wm, i, r, half) < V) {
             mx = fmaxf(mx, s);
@@ -174,6 +188,7 @@ struct EpiDlogits {
       const int n = n0 + acc_col(wn, j, col);
       const bool nv = n < N;
       const float t = (nv && temp) ? temp[n] : 1.0f;
+      const float rt = 1.0f / t;
       RowState rs{};
       float c = 0.f;
       int64_t y = -1;
@@ -195,7 +210,7 @@ struct EpiDlogits {
           for (int e = 0; e < 4; ++e) {
             const int m = mm + e;
             const int vg = v0 + m;
-            const float s = scale_key(acc[i][j][gq * 4 + e], t);
+            const float s = scale_key(acc[i][j][gq * 4 + e], t, rt);
             const uint32_t key = order_key(s);
             const bool in = key > rs.key_thr || (key == rs.key_thr && vg <= rs.id_thr);
             const float q = in ? __expf(s - rs.lse_s) : 0.f;

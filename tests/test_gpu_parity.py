@@ -221,3 +221,33 @@ def test_ragged_shapes(T, H, V, dtype):
     dH, dW = oracle.backward(h, W, y, ref, g, temp)
     assert rel_fro(gh.float().cpu().numpy(), dH) < GRAD_RTOL
     assert rel_fro(gw.cpu().numpy(), dW) < GRAD_RTOL
+
+
+def test_temperature_division_bitwise_on_many_pairs():
+    """s = fl32(z / T) must be the correctly rounded quotient for every pair.
+
+    fp32 operands with one-hot hidden rows make z = W[:, 0] exactly, so the
+    keys exported by the projection kernel are the division results alone.
+    Reference: fp64 quotient of the two fp32 values rounded to fp32 (exact,
+    since 53 >= 2*24 + 2)."""
+    rng = np.random.Generator(np.random.PCG64(99))
+    V, T, H = 1 << 20, 64, 8
+    z = np.concatenate([
+        (rng.standard_normal(V // 2) * 10).astype(np.float32),
+        (np.exp(rng.uniform(-80, 80, V // 2 - 16)) * rng.choice([-1, 1], V // 2 - 16)).astype(np.float32),
+        np.float32([0.0, -0.0, 1e-38, -1e-38, 3e38, -3e38, 1.0, -1.0, 1e-45, 2e-45, 1.5, 7.0, 1e-30, 1e30, 2.0, 0.5]),
+    ]).astype(np.float32)
+    t = np.concatenate([rng.uniform(0.05, 3.0, T - 8),
+                        [1.0, 0.7, 1e-3, 3.0, 0.3, 1.5, 1e-20, 1e20]]).astype(np.float32)
+    W = np.zeros((V, H), np.float32)
+    W[:, 0] = z
+    h = np.zeros((T, H), np.float32)
+    h[:, 0] = 1.0
+    d = dev()
+    hd, Wd = torch.from_numpy(h).to(d), torch.from_numpy(W).to(d)
+    s = binding.scaled_logits(hd, Wd, torch.from_numpy(t).to(d)).cpu()
+    zg = binding.scaled_logits(hd, Wd, None)[0].cpu()         # the projection's own z (an accumulated -0 is +0)
+    assert torch.equal(zg.abs(), torch.from_numpy(z).abs())
+    ref = (zg.double()[None, :] / torch.from_numpy(t).double()[:, None]).float()
+    bad = (s.view(torch.int32) != ref.view(torch.int32))
+    assert int(bad.sum()) == 0, f"{int(bad.sum())} quotients differ, e.g. z={z[bad.any(0).numpy()][:3]}"
