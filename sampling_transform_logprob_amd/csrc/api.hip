@@ -5,6 +5,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <unordered_map>
+#include <vector>
+
 #include "../../include/stce.h"
 #include "kernels.hpp"
 
@@ -38,8 +41,9 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  int64_t C, ldt, ntv;                                     // forward
+  int64_t C, ldt, ntv, nbuf;                               // forward
   size_t f_flags, f_tile, f_part, f_sy, fwd;
+  size_t buf_tile, buf_part, buf_sy;                       // bytes per chunk buffer
   int64_t Vs, Vsp, Tp;                                      // backward
   size_t b_flags, b_hT, b_WT, b_d, b_dT, b_dh, bwd;
 };
@@ -71,11 +75,18 @@ Layout plan(const stce_problem* p) {
   if (L.C > T) L.C = T;
   L.ldt = round_up(V, 4);
   L.ntv = ceil_div(V, VTILE);
+  // two chunk buffers when there is more than one chunk: the selection of
+  // chunk c (side stream) reads one while the projection of chunk c + 1
+  // writes the other
+  L.nbuf = T > L.C ? 2 : 1;
+  L.buf_tile = align_up(4 * (size_t)L.C * L.ldt);
+  L.buf_part = align_up(sizeof(TilePart) * (size_t)L.C * L.ntv);
+  L.buf_sy = align_up(4 * (size_t)L.C);
   size_t o = 0;
   L.f_flags = o; o = align_up(o + 4 * (size_t)T);
-  L.f_tile = o;  o = align_up(o + 4 * (size_t)L.C * L.ldt);
-  L.f_part = o;  o = align_up(o + sizeof(TilePart) * (size_t)L.C * L.ntv);
-  L.f_sy = o;    o = align_up(o + 4 * (size_t)L.C);
+  L.f_tile = o;  o += L.nbuf * L.buf_tile;
+  L.f_part = o;  o += L.nbuf * L.buf_part;
+  L.f_sy = o;    o += L.nbuf * L.buf_sy;
   L.fwd = o;
 
   if (p->vocab_slice > 0) {
@@ -125,6 +136,33 @@ stce_status check_ws(void* ws, size_t have, size_t need) {
 template <class T>
 T* at(void* ws, size_t off) {
   return (T*)((char*)ws + off);
+}
+
+// Per-thread, per-device side stream (default priority) and a pool of
+// timing-free events, created on first use and kept for the thread's life.
+// The forward runs each chunk's selection on the side stream, ordered
+// against the projections on the caller's stream by event waits only, so
+// the pattern is a plain fork/join that stream capture records as graph
+// dependencies.
+struct SideCtx {
+  hipStream_t stream = nullptr;
+  std::vector<hipEvent_t> ev;
+};
+thread_local std::unordered_map<int, SideCtx> g_side;
+
+hipError_t side_ctx(SideCtx** out, size_t nevents) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  SideCtx& c = g_side[dev];
+  if (!c.stream && (e = hipStreamCreateWithFlags(&c.stream, hipStreamNonBlocking)) != hipSuccess) return e;
+  while (c.ev.size() < nevents) {
+    hipEvent_t ev;
+    if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return e;
+    c.ev.push_back(ev);
+  }
+  *out = &c;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -191,8 +229,15 @@ stce_status stce_forward(const stce_problem* p, float* logprob, void* state, int
                            st)))
     return hip_fail(e, "validate");
   const size_t es = elt_size(p->dtype);
-  for (int64_t c0 = 0; c0 < p->T; c0 += L.C) {
+  const int64_t nch = ceil_div(p->T, L.C);
+  SideCtx* side = nullptr;
+  if (L.nbuf == 2 && (e = side_ctx(&side, 2 * (size_t)nch))) return hip_fail(e, "side stream");
+  for (int64_t c = 0; c < nch; ++c) {
+    const int64_t c0 = c * L.C;
     const int64_t nc = p->T - c0 < L.C ? p->T - c0 : L.C;
+    const int64_t b = c % L.nbuf;
+    if (side && c >= 2 && (e = hipStreamWaitEvent(st, side->ev[2 * (c - 2) + 1], 0)))
+      return hip_fail(e, "wait for selection");  // chunk c - 2 released this buffer
     FwdArgs a{};
     a.dtype = p->dtype;
     a.W = p->weight;
@@ -200,16 +245,22 @@ stce_status stce_forward(const stce_problem* p, float* logprob, void* state, int
     a.H = p->H;
     a.V = p->V;
     a.rows = nc;
-    a.tile = at<float>(ws, L.f_tile);
+    a.tile = at<float>(ws, L.f_tile + b * L.buf_tile);
     a.ld = L.ldt;
     a.temp = p->temperature ? p->temperature + c0 : nullptr;
     a.target = p->target + c0;
     a.flags = flags + c0;
     a.store_all = 0;
-    a.part = at<TilePart>(ws, L.f_part);
+    a.part = at<TilePart>(ws, L.f_part + b * L.buf_part);
     a.ntv = (int)L.ntv;
-    a.s_y = at<float>(ws, L.f_sy);
+    a.s_y = at<float>(ws, L.f_sy + b * L.buf_sy);
     if ((e = launch_fwd_projection(a, st))) return hip_fail(e, "projection");
+    hipStream_t ss = st;
+    if (side) {
+      ss = side->stream;
+      if ((e = hipEventRecord(side->ev[2 * c], st)) || (e = hipStreamWaitEvent(ss, side->ev[2 * c], 0)))
+        return hip_fail(e, "fork to the side stream");
+    }
     SelParams sp{};
     sp.tile = a.tile;
     sp.ld = L.ldt;
@@ -224,9 +275,13 @@ stce_status stce_forward(const stce_problem* p, float* logprob, void* state, int
     sp.logprob = logprob + c0;
     sp.state = (RowState*)state + c0;
     sp.V = (int)p->V;
-    launch_select(sp, (int)nc, st);
+    launch_select(sp, (int)nc, ss);
     if ((e = hipGetLastError())) return hip_fail(e, "select");
+    if (side && (e = hipEventRecord(side->ev[2 * c + 1], ss))) return hip_fail(e, "selection event");
   }
+  // join: the caller's stream waits for the last selection (the side stream
+  // runs them in order)
+  if (side && (e = hipStreamWaitEvent(st, side->ev[2 * (nch - 1) + 1], 0))) return hip_fail(e, "join");
   return STCE_OK;
 }
 

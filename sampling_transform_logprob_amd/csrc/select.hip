@@ -51,31 +51,47 @@ __device__ inline double block_excl_scan(double v, double* scratch) {
   return off + ex;
 }
 
-__device__ inline int next_pow2(int n) {
-  int p = 1;
-  while (p < n) p <<= 1;
-  return p;
-}
-
-// Bitonic sort, descending, of x[0, n) with n a power of two.
+// Bitonic sort, descending, of x[0, n) for any n: the network of the next
+// power of two in the form where every compare-exchange puts the larger value
+// at the lower index (each merge starts with a mirrored half-cleaner).
+// Positions >= n stand for minimum values that never move, so they are
+// neither read nor written.
 template <class T>
 __device__ inline void bitonic_desc(T* x, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < (n >> 1); i += ST) {
-        const int lo = 2 * stride * (i / stride) + (i % stride);
-        const int hi = lo + stride;
-        const bool desc = (lo & size) == 0;
+  int n2 = 1;
+  while (n2 < n) n2 <<= 1;
+  for (int size = 2; size <= n2; size <<= 1) {
+    const int half = size >> 1;
+    for (int i = threadIdx.x; i < (n2 >> 1); i += ST) {
+      const int base = (i / half) * size, off = i % half;
+      const int lo = base + off, hi = base + size - 1 - off;
+      if (hi < n) {
         const T a = x[lo], b = x[hi];
-        if ((a < b) == desc) {
+        if (a < b) {
           x[lo] = b;
           x[hi] = a;
+        }
+      }
+    }
+    __syncthreads();
+    for (int stride = half >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < (n2 >> 1); i += ST) {
+        const int lo = 2 * stride * (i / stride) + (i % stride);
+        const int hi = lo + stride;
+        if (hi < n) {
+          const T a = x[lo], b = x[hi];
+          if (a < b) {
+            x[lo] = b;
+            x[hi] = a;
+          }
         }
       }
       __syncthreads();
     }
   }
 }
+
+constexpr int TLIST = 512;  // candidate-tile list capacity
 
 struct Shared {
   union {
@@ -89,6 +105,10 @@ struct Shared {
   double sd[ST / 64];
   float sf[ST / 64];
   int si[ST / 64];
+  uint16_t tiles[TLIST];   // vocabulary tiles that can hold window tokens
+  int ntiles;
+  uint32_t bkey;
+  double mass_o;           // mass of the first n_other window tokens
   int cnt;
   int c;             // chosen bin
   int c_p;           // bin where top-p crosses (NB if not found)
@@ -99,7 +119,9 @@ struct Shared {
   double mass_s;     // mass of the support
 };
 
-__global__ __launch_bounds__(ST) void select_kernel(SelParams P) {
+// At most 96 VGPRs (5 waves per SIMD): one of these waves fits beside the
+// two projection waves of a SIMD.
+__global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
   __shared__ Shared S;
   const int row = blockIdx.x, tid = threadIdx.x, w = tid >> 6;
   const int V = P.V;
@@ -182,33 +204,94 @@ __global__ __launch_bounds__(ST) void select_kernel(SelParams P) {
     return S.cnt;
   };
 
+  // Full-row mass relative to m from the fp32 tile partials: within 1e-4
+  // relative of the exact value (each exp carries ~|x| 2^-24 relative error,
+  // each 256-term fp32 sum at most 256 ulps), used only to certify that
+  // top-p cannot bind before another filter does.
+  const double z32 = exp(lse_full - m64);
+
   int nw = -1;              // window size; -1 until a window is found
   uint32_t above = 0;       // tokens ahead of the window in the order
   double mabove = 0.0;      // their fp64 mass
   double Z = 0.0;           // full-row fp64 mass (top-p only)
+  int zmode = 0;            // 0: Z exact; 1: Z = window total; 2: only z32 known
   bool p_here = false;      // top-p is known to cross inside the window
 
   if (V <= CAP) {
-    nw = collect([](float, uint32_t, int) { return true; }, p_on, Z);
+    double dummy;
+    nw = collect([](float, uint32_t, int) { return true; }, false, dummy);
+    zmode = 1;
     p_here = p_on;
   } else {
     // lower bound of the k-th largest key: the k-th largest tile maximum
+    // (the tile maxima are distinct tokens), found bit by bit by wave 0
     bool kb = false;
-    uint32_t bkey = 0u;
     if (k_on && k <= P.ntv && P.ntv <= 2 * CAP) {
-      const int n2 = next_pow2(P.ntv);
-      for (int t = tid; t < n2; t += ST) S.u.k32[t] = t < P.ntv ? order_key(pp[t].mx) : 0u;
+      for (int t = tid; t < P.ntv; t += ST) S.u.k32[t] = order_key(pp[t].mx);
       __syncthreads();
-      bitonic_desc(S.u.k32, n2);
-      bkey = S.u.k32[k - 1];
+      if (w == 0) {
+        const int lane = tid & 63;
+        uint32_t tau = 0u;
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t c = tau | (1u << bit);
+          int cnt = 0;
+          for (int t = lane; t < P.ntv; t += 64) cnt += S.u.k32[t] >= c ? 1 : 0;
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+          if (cnt >= k) tau = c;
+        }
+        if (lane == 0) S.bkey = tau;
+      }
       kb = true;
       __syncthreads();
     }
+    const uint32_t bkey = kb ? S.bkey : 0u;
     if (kb || m_on) {
-      const int n = collect(
-          [&](float s, uint32_t key, int) { return (!kb || key >= bkey) && (!m_on || (double)s - m64 >= thr); },
-          p_on, Z);
-      if (n <= CAP) nw = n;
+      // tiles whose maximum passes the bound can hold window tokens
+      if (tid == 0) S.ntiles = 0;
+      __syncthreads();
+      for (int t = tid; t < P.ntv; t += ST) {
+        const float tm = pp[t].mx;
+        if ((!kb || order_key(tm) >= bkey) && (!m_on || (double)tm - m64 >= thr)) {
+          const int i = atomicAdd(&S.ntiles, 1);
+          if (i < TLIST) S.tiles[i] = (uint16_t)t;
+        }
+      }
+      __syncthreads();
+      const int nt = S.ntiles;
+      auto pred = [&](float s, uint32_t key, int) { return (!kb || key >= bkey) && (!m_on || (double)s - m64 >= thr); };
+      int n;
+      if (nt <= TLIST) {
+        if (tid == 0) S.cnt = 0;
+        __syncthreads();
+        for (int q = tid; q < nt * (VTILE / 4); q += ST) {
+          const int v0 = (int)S.tiles[q / (VTILE / 4)] * VTILE + (q % (VTILE / 4)) * 4;
+          if (v0 >= V) continue;
+          const f32x4 x = *(const f32x4*)(rp + v0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = v0 + e;
+            if (v < V) {
+              const float sv = x[e];
+              const uint32_t key = order_key(sv);
+              if (pred(sv, key, v)) {
+                const int i = atomicAdd(&S.cnt, 1);
+                if (i < CAP) S.u.cand[i] = composite(key, (uint32_t)v);
+              }
+            }
+          }
+        }
+        __syncthreads();
+        n = S.cnt;
+        __syncthreads();
+      } else {
+        double dummy;
+        n = collect(pred, false, dummy);
+      }
+      if (n <= CAP) {
+        nw = n;
+        zmode = 2;
+      }
     }
   }
 
@@ -382,51 +465,79 @@ __global__ __launch_bounds__(ST) void select_kernel(SelParams P) {
   }
 
   // ---- resolve the boundary inside the window
-  const int n2 = next_pow2(max(nw, 1));
-  for (int i = nw + tid; i < n2; i += ST) S.u.cand[i] = 0ull;
   __syncthreads();
-  bitonic_desc(S.u.cand, n2);
-  const int E = (n2 + ST - 1) / ST;
+  bitonic_desc(S.u.cand, nw);
+  const int E = (nw + ST - 1) / ST;
   const int lo = tid * E, hi = min(lo + E, nw);
   double seg = 0.0;
   for (int i = lo; i < hi; ++i) seg += exp((double)key_value(comp_key(S.u.cand[i])) - m64);
+  if (zmode == 1) Z = block_reduce(seg, AddD{}, S.sd);   // the window is the whole row
   const double base = mabove + block_excl_scan(seg, S.sd);
-  const double pz = (double)p * Z;
-  int np_loc = INT32_MAX, nm_loc = INT32_MAX;
-  {
-    double run = base;
-    for (int i = lo; i < hi; ++i) {
-      const double dm = (double)key_value(comp_key(S.u.cand[i])) - m64;
-      run += exp(dm);
-      if (p_on && np_loc == INT32_MAX && run >= pz) np_loc = i;
-      if (m_on && nm_loc == INT32_MAX && dm < thr) nm_loc = i;
-    }
-  }
-  const int np_idx = block_reduce(np_loc, MinI{}, S.si);
+  // min-p: the passing tokens are a prefix of the window
+  int nm_loc = INT32_MAX;
+  if (m_on)
+    for (int i = lo; i < hi; ++i)
+      if ((double)key_value(comp_key(S.u.cand[i])) - m64 < thr) {
+        nm_loc = i;
+        break;
+      }
   const int nm_idx = block_reduce(nm_loc, MinI{}, S.si);
   int n_loc = nw;
   if (k_on) {
     const int64_t nk = (int64_t)k - (int64_t)above;
     if (nk >= 1 && nk < n_loc) n_loc = (int)nk;
   }
-  if (p_on) {
-    const int np = np_idx != INT32_MAX ? np_idx + 1 : (p_here ? nw : INT32_MAX);
-    if (np < n_loc) n_loc = np;
-  }
   if (m_on) {
     const int nm = nm_idx != INT32_MAX ? nm_idx : nw;
     if (nm < n_loc) n_loc = nm;
   }
   if (n_loc < 1) n_loc = 1;
-  {
-    const int b = n_loc - 1;
+  // mass of the first `upto` window tokens, summed in the same order as the
+  // top-p scan below
+  auto mass_upto = [&](int upto, double* dst) {
+    const int b = upto - 1;
     if (b >= lo && b < hi) {
       double run = base;
       for (int i = lo; i <= b; ++i) run += exp((double)key_value(comp_key(S.u.cand[i])) - m64);
-      S.mass_s = run;
+      *dst = run;
+    }
+    __syncthreads();
+  };
+  bool need_p = p_on;
+  if (p_on && zmode == 2) {
+    // top-p cannot bind before n_loc if even the first n_loc tokens hold
+    // clearly less than p of the row mass; otherwise take the exact fp64
+    // full-row mass (one more pass) and decide exactly
+    mass_upto(n_loc, &S.mass_o);
+    if (S.mass_o < (double)p * z32 * (1.0 - 1e-3)) {
+      need_p = false;
+    } else {
+      double zl = 0.0;
+      for (int q = tid; q < nv4; q += ST) {
+        const f32x4 x = *(const f32x4*)(rp + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * q + e < V) zl += exp((double)x[e] - m64);
+      }
+      Z = block_reduce(zl, AddD{}, S.sd);
     }
   }
-  __syncthreads();
+  if (need_p) {
+    const double pz = (double)p * Z;
+    int np_loc = INT32_MAX;
+    double run = base;
+    for (int i = lo; i < hi; ++i) {
+      run += exp((double)key_value(comp_key(S.u.cand[i])) - m64);
+      if (run >= pz) {
+        np_loc = i;
+        break;
+      }
+    }
+    const int np_idx = block_reduce(np_loc, MinI{}, S.si);
+    const int np = np_idx != INT32_MAX ? np_idx + 1 : (p_here ? nw : INT32_MAX);
+    if (np < n_loc) n_loc = np;
+  }
+  mass_upto(n_loc, &S.mass_s);
   if (tid == 0) {
     const uint64_t bc = S.u.cand[n_loc - 1];
     rs.key_thr = comp_key(bc);

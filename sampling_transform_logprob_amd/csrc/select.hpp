@@ -28,7 +28,9 @@
 namespace stce {
 
 constexpr int ST = 256;     // threads per row
-constexpr int CAP = 4096;   // window capacity (composites in LDS)
+constexpr int CAP = 3840;   // window capacity (composites in LDS); with the
+                            // rest of the shared state the kernel stays under
+                            // 32 KB, so it fits beside a projection workgroup
 constexpr int NB = 512;     // value-histogram bins
 constexpr int RB = 256;     // radix bins (8-bit digits)
 

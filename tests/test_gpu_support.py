@@ -2,7 +2,7 @@
 
 ``stce_support_from_logits`` runs the forward's selection kernel on given
 keys; the oracle computes the support of the very same keys.  The rows cover
-every path of the kernel: whole-row windows (V <= 4096), bounded candidates
+every path of the kernel: whole-row windows (V <= 3840), bounded candidates
 (top-k from tile maxima, min-p), the value histogram, and the radix
 refinement used when a histogram bin holds more tokens than the window
 (long tie groups, very peaked rows), plus the identities of the program."""
@@ -69,12 +69,12 @@ def _grid(rng, V, R, ties):
     return keys
 
 
-@pytest.mark.parametrize("V", [4, 8, 300, 1000, 4096, 5000, 40000])
+@pytest.mark.parametrize("V", [4, 8, 300, 1000, 3840, 3844, 4096, 5000, 40000])
 def test_random_rows_all_filter_mixes(V):
     rng = np.random.Generator(np.random.PCG64(V))
     R = 96
     keys = _grid(rng, V, R, ties=(V % 2 == 0))
-    ks = np.array([0, 1, 2, 20, 64, V - 1, V, V + 5, 4095, 4097])
+    ks = np.array([0, 1, 2, 20, 64, V - 1, V, V + 5, 3839, 3841, 4097])
     ps = np.array([1.0, 0.9, 0.5, 1e-6, np.nextafter(np.float32(1), np.float32(0)), 0.99])
     mps = np.array([0.0, 0.0, 0.1, 1.0, 1e-3])
     k = np.maximum(ks[rng.integers(0, len(ks), R)], 0)
@@ -132,3 +132,36 @@ def test_min_p_keeps_whole_tie_groups_and_uses_unfiltered_max():
     keys[1, 7] = 3.0
     info = _check(keys, [0, 0, 50], [1.0, 1.0, 1.0], [0.1, 0.1, 0.1], label="min-p groups")
     assert info["n"][0] in (100, 2000)
+
+
+def test_top_p_near_the_top_k_mass_takes_the_exact_path():
+    """Rows whose top-k mass lies within 1e-3 of p of the row mass cannot be
+    certified from the fp32 partials; the kernel must then take the exact
+    fp64 full-row mass, on both sides of the crossing."""
+    rng = np.random.Generator(np.random.PCG64(17))
+    V, R = 20000, 24
+    keys = rng.standard_normal((R, V)).astype(np.float32)
+    keys[:, :2] = 10.0
+    s64 = keys.astype(np.float64)
+    frac = np.exp(s64[:, :2] - 10.0).sum(1) / np.exp(s64 - 10.0).sum(1)   # mass of the top two
+    rel = np.tile([-3e-4, -1e-5, -1e-7, 1e-7, 1e-5, 3e-4, -5e-3, 5e-3], R // 8)
+    p = (frac * (1 + rel)).astype(np.float32)
+    info = _check(keys, np.full(R, 2), p, np.zeros(R), np.zeros(R, np.int64), "top-p band")
+    # p slightly below the top-two mass: top-p crosses at the second token (a
+    # tie with the first: n = 2 either way); p above it: top-k 2 binds
+    assert np.all(info["n"] <= 2)
+
+
+def test_k_bounded_rows_read_only_candidate_tiles():
+    """Top-k rows whose candidates sit in a few tiles, next to rows whose
+    tile list overflows (min-p keeping most of the row)."""
+    rng = np.random.Generator(np.random.PCG64(23))
+    V, R = 150000, 16
+    keys = (rng.standard_normal((R, V)) * 0.01).astype(np.float32)
+    hot = rng.integers(0, V, (R, 30))
+    for r in range(R):
+        keys[r, hot[r]] = rng.uniform(5, 6, 30).astype(np.float32)
+    k = np.array([20, 1, 30, 31] * 4)
+    p = np.array([1.0, 0.8, 0.999, 1.0] * 4, np.float32)
+    mp = np.array([0.0, 0.0, 0.0, 1e-9] * 4, np.float32)
+    _check(keys, k, p, mp, hot[:, 0], "candidate tiles")
