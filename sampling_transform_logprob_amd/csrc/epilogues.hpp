@@ -18,23 +18,46 @@ __device__ inline void lse_merge(float& mx, float& sm, float omx, float osm) {
   mx = M;
 }
 
-// Per-row temperature: s = fl32(z / T), correctly rounded, from the row's
-// correctly rounded reciprocal r = fl32(1 / T): q0 = fl32(z r) is within one
-// ulp of z / T, the fma gives the remainder z - q0 T exactly, and one more
-// fma rounds q0 + (z - q0 T) r to the correctly rounded quotient (Markstein's
-// correction step, as used for IA-64 division).  The remainder is about
-// |z| 2^-24, so it stays a normal number only when |z| and |q0| are at least
-// 2^-100; tiny, zero, huge or infinite operands take the plain IEEE division
-// (logits that small are zeros in practice).  Forward and backward
-// epilogues use this one function, so the backward's keys are the forward's
-// keys bit for bit.
-__device__ inline float scale_key(float z, float t, float r) {
+// Per-row temperature: s = fl32(z / T), correctly rounded.  With the row's
+// correctly rounded reciprocal r = fl32(1 / T), q0 = fl32(z r) is within one
+// ulp of z / T, an fma gives the remainder z - q0 T exactly, and one more fma
+// rounds q0 + (z - q0 T) r to the correctly rounded quotient (Markstein's
+// correction step, as used for IA-64 division).  That needs the remainder and
+// the quotient to stay normal numbers, which holds when 2^-90 <= |z| <= 2^90
+// and 2^-30 <= T <= 2^30; a lane column with any value outside that range
+// (zeros included) takes the IEEE division instead.  Both give the same bits,
+// so the choice cannot make the forward and the backward disagree.
+__device__ inline float quot_fast(float z, float t, float r) {
   const float q0 = z * r;
-  const float a = __builtin_fabsf(q0);
-  if (!(a >= 0x1p-100f && __builtin_fabsf(z) >= 0x1p-100f && a <= 0x1p+126f)) return z / t;
-  const float e = __builtin_fmaf(-q0, t, z);
-  return __builtin_fmaf(e, r, q0);
+  return __builtin_fmaf(__builtin_fmaf(-q0, t, z), r, q0);
 }
+
+// Scales the lane's accumulators of column j (one token) by 1 / t in place.
+__device__ inline void scale_column(AccTile& acc, int j, float t) {
+  if (t == 1.0f) return;  // exact
+  float lo = STCE_INF, hi = 0.f;
+#pragma unroll
+  for (int i = 0; i < ACC_I; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      lo = fminf(lo, __builtin_fabsf(acc[i][j][r]));
+      hi = fmaxf(hi, __builtin_fabsf(acc[i][j][r]));
+    }
+  if (lo >= 0x1p-90f && hi <= 0x1p+90f && t >= 0x1p-30f && t <= 0x1p+30f) {
+    const float r = 1.0f / t;
+#pragma unroll
+    for (int i = 0; i < ACC_I; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = quot_fast(acc[i][j][q], t, r);
+  } else {
+#pragma unroll
+    for (int i = 0; i < ACC_I; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = acc[i][j][q] / t;
+  }
+}
+
+constexpr float LOG2E = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
 // Forward projection epilogue.  M = vocabulary, N = tokens of the chunk.
@@ -66,28 +89,37 @@ struct EpiLogits {
       const int n = n0 + acc_col(wn, j, col);
       const bool nv = n < N;
       const float t = (nv && temp) ? temp[n] : 1.0f;
-      const float rt = 1.0f / t;
+      scale_column(acc, j, t);
       float mx = -STCE_INF, mn = STCE_INF;
+      if (m0 + GM <= V) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float s = scale_key(acc[i][j][r], t, rt);
-          acc[i][j][r] = s;
-          if (m0 + acc_row(wm, i, r, half) < V) {
-            mx = fmaxf(mx, s);
-            mn = fminf(mn, s);
+          for (int r = 0; r < 16; ++r) {
+            mx = fmaxf(mx, acc[i][j][r]);
+            mn = fminf(mn, acc[i][j][r]);
           }
-        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < ACC_I; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (m0 + acc_row(wm, i, r, half) < V) {
+              mx = fmaxf(mx, acc[i][j][r]);
+              mn = fminf(mn, acc[i][j][r]);
+            }
+      }
       const bool st = nv && (store_all || (flags[n] & ROW_FILTERED));
       if (st) {
         float* rowp = tile + (int64_t)n * ld;
+        const int mbu = __builtin_amdgcn_readfirstlane(mb);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int mm = mb + i * 32 + g * 8 + half * 4;
-            if (vec && mm + 3 < V) {
+            const int base = mbu + i * 32 + g * 8;   // the wave's 8 rows (uniform)
+            const int mm = base + half * 4;
+            if (vec && base + 8 <= V) {
               *(f32x4*)(rowp + mm) = f32x4{acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]};
             } else {
 #pragma unroll
@@ -104,7 +136,7 @@ struct EpiLogits {
             const int orr = (ow >> 3) * 4 + (ow & 3);
             float v = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
               for (int r = 0; r < 16; ++r)
                 if (i == oi && r == orr) v = acc[i][j][r];
@@ -114,11 +146,20 @@ struct EpiLogits {
       }
       float sm = 0.f;
       if (mx != -STCE_INF) {
+        const float nmx = -mx * LOG2E;
+        if (m0 + GM <= V) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (m0 + acc_row(wm, i, r, half) < V) sm += __expf(acc[i][j][r] - mx);
+            for (int r = 0; r < 16; ++r) sm += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][r], LOG2E, nmx));
+        } else {
+#pragma unroll
+          for (int i = 0; i < ACC_I; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (m0 + acc_row(wm, i, r, half) < V)
+                sm += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][r], LOG2E, nmx));
+        }
       }
       const float omx = __shfl_xor(mx, 32), osm = __shfl_xor(sm, 32), omn = __shfl_xor(mn, 32);
       lse_merge(mx, sm, omx, osm);
@@ -188,40 +229,66 @@ struct EpiDlogits {
       const int n = n0 + acc_col(wn, j, col);
       const bool nv = n < N;
       const float t = (nv && temp) ? temp[n] : 1.0f;
-      const float rt = 1.0f / t;
       RowState rs{};
       float c = 0.f;
-      int64_t y = -1;
+      int yy = -1;
       if (nv) {
         rs = st[n];
-        y = target[n];
+        yy = (int)target[n];
         if ((rs.flags & (ROW_VALID | ROW_IN_SUPPORT)) == (ROW_VALID | ROW_IN_SUPPORT)) c = g[n] / t;
       }
       if (n >= N_pad) continue;
+      scale_column(acc, j, t);
+      // support membership as a float compare against the boundary key's
+      // value (-0 == +0 like the canonical keys); unfiltered rows keep all
+      const float sthr = (rs.flags & ROW_FILTERED) ? key_value(rs.key_thr) : -STCE_INF;
+      const int idt = rs.id_thr;
+      const float nl = -rs.lse_s * LOG2E;
+      const bool live = c != 0.f;  // rows with c == 0 give exact zeros
       OutT* dr = d + (int64_t)n * ld_d;
+      const int wmu = __builtin_amdgcn_readfirstlane(wm);
 #pragma unroll
       for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int mm = m0 + wm * 128 + i * 32 + gq * 8 + half * 4;  // 4 consecutive rows
-          if (mm >= Vs_pad) continue;
+          // the wave's 8 rows base .. base + 7 (Vs_pad is a multiple of 64,
+          // so they are all in or all out): a uniform test
+          const int base = m0 + wmu * 128 + i * 32 + gq * 8;
+          if (base >= Vs_pad) continue;
+          const int mm = base + half * 4;  // this lane's 4 consecutive rows
           OutT v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int m = mm + e;
             const int vg = v0 + m;
-            const float s = scale_key(acc[i][j][gq * 4 + e], t, rt);
-            const uint32_t key = order_key(s);
-            const bool in = key > rs.key_thr || (key == rs.key_thr && vg <= rs.id_thr);
-            const float q = in ? __expf(s - rs.lse_s) : 0.f;
-            // rows with c == 0 (out of support, invalid, padding) give exact
-            // zeros, whatever q is
-            v[e] = (OutT)((c != 0.f && m < Vs) ? c * ((vg == y ? 1.f : 0.f) - q) : 0.f);
-            dT[(int64_t)m * ld_dT + n] = v[e];
+            const float s = acc[i][j][gq * 4 + e];
+            const bool in = (s > sthr) | ((s == sthr) & (vg <= idt));
+            const float q = in ? __builtin_amdgcn_exp2f(__builtin_fmaf(s, LOG2E, nl)) : 0.f;
+            const float dv = c * ((vg == yy ? 1.f : 0.f) - q);
+            v[e] = (OutT)((live && m < Vs) ? dv : 0.f);
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e) dr[mm + e] = v[e];
+          if constexpr (sizeof(OutT) == 2) {
+            // stage the vocab-major copy in LDS: [m - m0][n - n0], 512-byte rows
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ((OutT*)smem)[(mm + e - m0) * GN + (n - n0)] = v[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dT[(int64_t)(mm + e) * ld_dT + n] = v[e];
+          }
         }
+    }
+    if constexpr (sizeof(OutT) == 2) {
+      // every row/column of the staged tile that was not written above
+      // (m >= Vs_pad or n >= N_pad) is never copied out below
+      __syncthreads();
+      const int rows = min(GM, Vs_pad - m0), cols = min(GN, N_pad - n0);
+      for (int c16 = tid; c16 < GM * (GN / 8); c16 += GTHREADS) {
+        const int r = c16 / (GN / 8), cc = (c16 % (GN / 8)) * 8;
+        if (r < rows && cc < cols)
+          *(u32x4*)(dT + (int64_t)(m0 + r) * ld_dT + n0 + cc) = *(const u32x4*)((const OutT*)smem + r * GN + cc);
+      }
     }
   }
 };
