@@ -39,7 +39,7 @@ __device__ inline void scale_column(AccTile& acc, int j, float t) {
 #pragma unroll
   for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < ACC_R; ++r) {
       lo = fminf(lo, __builtin_fabsf(acc[i][j][r]));
       hi = fmaxf(hi, __builtin_fabsf(acc[i][j][r]));
     }
@@ -48,12 +48,12 @@ __device__ inline void scale_column(AccTile& acc, int j, float t) {
 #pragma unroll
     for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = quot_fast(acc[i][j][q], t, r);
+      for (int q = 0; q < ACC_R; ++q) acc[i][j][q] = quot_fast(acc[i][j][q], t, r);
   } else {
 #pragma unroll
     for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = acc[i][j][q] / t;
+      for (int q = 0; q < ACC_R; ++q) acc[i][j][q] = acc[i][j][q] / t;
   }
 }
 
@@ -81,8 +81,9 @@ struct EpiLogits {
 
   __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 2, wn = w & 3, half = lane >> 5, col = lane & 31;
+    const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
     const int mb = m0 + wm * 128;
+    const bool full = m0 + GM <= V;
     float pmx[ACC_J], psm[ACC_J], pmn[ACC_J];
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) {
@@ -91,11 +92,11 @@ struct EpiLogits {
       const float t = (nv && temp) ? temp[n] : 1.0f;
       scale_column(acc, j, t);
       float mx = -STCE_INF, mn = STCE_INF;
-      if (m0 + GM <= V) {
+      if (full) {
 #pragma unroll
         for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
+          for (int r = 0; r < ACC_R; ++r) {
             mx = fmaxf(mx, acc[i][j][r]);
             mn = fminf(mn, acc[i][j][r]);
           }
@@ -103,8 +104,8 @@ struct EpiLogits {
 #pragma unroll
         for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (m0 + acc_row(wm, i, r, half) < V) {
+          for (int r = 0; r < ACC_R; ++r)
+            if (m0 + acc_row(wm, i, r, quad) < V) {
               mx = fmaxf(mx, acc[i][j][r]);
               mn = fminf(mn, acc[i][j][r]);
             }
@@ -114,31 +115,29 @@ struct EpiLogits {
         float* rowp = tile + (int64_t)n * ld;
         const int mbu = __builtin_amdgcn_readfirstlane(mb);
 #pragma unroll
-        for (int i = 0; i < ACC_I; ++i)
+        for (int i = 0; i < ACC_I; ++i) {
+          const int base = mbu + i * 16;  // the wave's 16 rows (uniform)
+          const int mm = base + quad * 4;
+          if (vec && base + 16 <= V) {
+            *(f32x4*)(rowp + mm) = acc[i][j];
+          } else {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int base = mbu + i * 32 + g * 8;   // the wave's 8 rows (uniform)
-            const int mm = base + half * 4;
-            if (vec && base + 8 <= V) {
-              *(f32x4*)(rowp + mm) = f32x4{acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]};
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (mm + e < V) rowp[mm + e] = acc[i][j][g * 4 + e];
-            }
+            for (int e = 0; e < ACC_R; ++e)
+              if (mm + e < V) rowp[mm + e] = acc[i][j][e];
           }
+        }
       }
       if (nv && target && s_y) {
         const int64_t off = target[n] - mb;
         if (off >= 0 && off < 128) {
-          const int oi = (int)off >> 5, ow = (int)off & 31;
-          if (((ow >> 2) & 1) == half) {
-            const int orr = (ow >> 3) * 4 + (ow & 3);
+          const int oi = (int)off >> 4, ow = (int)off & 15;
+          if ((ow >> 2) == quad) {
+            const int orr = ow & 3;
             float v = 0.f;
 #pragma unroll
             for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-              for (int r = 0; r < 16; ++r)
+              for (int r = 0; r < ACC_R; ++r)
                 if (i == oi && r == orr) v = acc[i][j][r];
             s_y[n] = v;
           }
@@ -147,30 +146,35 @@ struct EpiLogits {
       float sm = 0.f;
       if (mx != -STCE_INF) {
         const float nmx = -mx * LOG2E;
-        if (m0 + GM <= V) {
+        if (full) {
 #pragma unroll
           for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sm += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][r], LOG2E, nmx));
+            for (int r = 0; r < ACC_R; ++r) sm += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][r], LOG2E, nmx));
         } else {
 #pragma unroll
           for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (m0 + acc_row(wm, i, r, half) < V)
+            for (int r = 0; r < ACC_R; ++r)
+              if (m0 + acc_row(wm, i, r, quad) < V)
                 sm += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][r], LOG2E, nmx));
         }
       }
-      const float omx = __shfl_xor(mx, 32), osm = __shfl_xor(sm, 32), omn = __shfl_xor(mn, 32);
-      lse_merge(mx, sm, omx, osm);
+      // merge the four lanes that hold this column (quads 0..3)
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        const float omx = __shfl_xor(mx, o), osm = __shfl_xor(sm, o), omn = __shfl_xor(mn, o);
+        lse_merge(mx, sm, omx, osm);
+        mn = fminf(mn, omn);
+      }
       pmx[j] = mx;
       psm[j] = sm;
-      pmn[j] = fminf(mn, omn);
+      pmn[j] = mn;
     }
     // merge the two waves that share these tokens (wm = 0 and 1)
     __syncthreads();
     float* red = (float*)smem;  // [2][256][3]
-    if (half == 0) {
+    if (quad == 0) {
 #pragma unroll
       for (int j = 0; j < ACC_J; ++j) {
         const int tok = acc_col(wn, j, col);
@@ -180,7 +184,7 @@ struct EpiLogits {
       }
     }
     __syncthreads();
-    if (wm == 0 && half == 0) {
+    if (wm == 0 && quad == 0) {
 #pragma unroll
       for (int j = 0; j < ACC_J; ++j) {
         const int tok = acc_col(wn, j, col);
@@ -223,7 +227,8 @@ struct EpiDlogits {
 
   __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 2, wn = w & 3, half = lane >> 5, col = lane & 31;
+    const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
+    const int wmu = __builtin_amdgcn_readfirstlane(wm);
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) {
       const int n = n0 + acc_col(wn, j, col);
@@ -246,38 +251,40 @@ struct EpiDlogits {
       const float nl = -rs.lse_s * LOG2E;
       const bool live = c != 0.f;  // rows with c == 0 give exact zeros
       OutT* dr = d + (int64_t)n * ld_d;
-      const int wmu = __builtin_amdgcn_readfirstlane(wm);
 #pragma unroll
-      for (int i = 0; i < ACC_I; ++i)
+      for (int i = 0; i < ACC_I; ++i) {
+        // the wave's 16 rows base .. base + 15 (Vs_pad is a multiple of 64,
+        // so they are all in or all out): a uniform test
+        const int base = m0 + wmu * 128 + i * 16;
+        if (base >= Vs_pad) continue;
+        const int mm = base + quad * 4;  // this lane's 4 consecutive rows
+        OutT v[ACC_R];
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          // the wave's 8 rows base .. base + 7 (Vs_pad is a multiple of 64,
-          // so they are all in or all out): a uniform test
-          const int base = m0 + wmu * 128 + i * 32 + gq * 8;
-          if (base >= Vs_pad) continue;
-          const int mm = base + half * 4;  // this lane's 4 consecutive rows
-          OutT v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int m = mm + e;
-            const int vg = v0 + m;
-            const float s = acc[i][j][gq * 4 + e];
-            const bool in = (s > sthr) | ((s == sthr) & (vg <= idt));
-            const float q = in ? __builtin_amdgcn_exp2f(__builtin_fmaf(s, LOG2E, nl)) : 0.f;
-            const float dv = c * ((vg == yy ? 1.f : 0.f) - q);
-            v[e] = (OutT)((live && m < Vs) ? dv : 0.f);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dr[mm + e] = v[e];
-          if constexpr (sizeof(OutT) == 2) {
-            // stage the vocab-major copy in LDS: [m - m0][n - n0], 512-byte rows
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ((OutT*)smem)[(mm + e - m0) * GN + (n - n0)] = v[e];
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dT[(int64_t)(mm + e) * ld_dT + n] = v[e];
-          }
+        for (int e = 0; e < ACC_R; ++e) {
+          const int m = mm + e;
+          const int vg = v0 + m;
+          const float s = acc[i][j][e];
+          const bool in = (s > sthr) | ((s == sthr) & (vg <= idt));
+          const float q = in ? __builtin_amdgcn_exp2f(__builtin_fmaf(s, LOG2E, nl)) : 0.f;
+          const float dv = c * ((vg == yy ? 1.f : 0.f) - q);
+          v[e] = (OutT)((live && m < Vs) ? dv : 0.f);
         }
+        if constexpr (sizeof(OutT) == 2) {
+          // 8-byte store of the 4 rows (ld_d and mm are multiples of 4)
+          uint32_t p0 = (uint32_t)__builtin_bit_cast(uint16_t, v[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[1]) << 16);
+          uint32_t p1 = (uint32_t)__builtin_bit_cast(uint16_t, v[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[3]) << 16);
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          *(u32x2*)(dr + mm) = u32x2{p0, p1};
+          // stage the vocab-major copy in LDS: [m - m0][n - n0], 512-byte rows
+#pragma unroll
+          for (int e = 0; e < ACC_R; ++e) ((OutT*)smem)[(mm + e - m0) * GN + (n - n0)] = v[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < ACC_R; ++e) dr[mm + e] = v[e];
+#pragma unroll
+          for (int e = 0; e < ACC_R; ++e) dT[(int64_t)(mm + e) * ld_dT + n] = v[e];
+        }
+      }
     }
     if constexpr (sizeof(OutT) == 2) {
       // every row/column of the staged tile that was not written above
@@ -304,16 +311,16 @@ struct EpiStore {
 
   __device__ inline void operator()(AccTile& acc, int m0, int n0, char*) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 2, wn = w & 3, half = lane >> 5, col = lane & 31;
+    const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) {
       const int n = n0 + acc_col(wn, j, col);
       if (n >= N) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + acc_row(wm, i, r, half);
+        for (int r = 0; r < ACC_R; ++r) {
+          const int m = m0 + acc_row(wm, i, r, quad);
           if (m < M) {
             float* p = out + (int64_t)m * ld + n;
             *p = accumulate ? *p + acc[i][j][r] : acc[i][j][r];
@@ -338,16 +345,16 @@ struct EpiAccum {
 
   __device__ inline void operator()(AccTile& acc, int m0, int n0, char*) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 2, wn = w & 3, half = lane >> 5, col = lane & 31;
+    const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) {
       const int n = n0 + acc_col(wn, j, col);
       if (n >= N) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + acc_row(wm, i, r, half);
+        for (int r = 0; r < ACC_R; ++r) {
+          const int m = m0 + acc_row(wm, i, r, quad);
           if (m < M) {
             const int64_t o = (int64_t)m * ld + n;
             const float v = first ? acc[i][j][r] : sum[o] + acc[i][j][r];

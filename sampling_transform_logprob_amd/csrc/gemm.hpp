@@ -6,30 +6,37 @@
 //   weight grad  dW[v, :] = dz^T[v, :] . h^T[:, :]   (M = vocab, N = H,      K = tokens)
 //   hidden grad  dH[t, :] = dz[t, :] . W^T[:, :]     (M = tokens, N = H,     K = vocab)
 //
-// Block tile 256 x 256, k-step 64, 512 threads = 8 waves (2 per SIMD) in a
-// 2 (m) x 4 (n) grid, each wave owning a 128 x 64 sub-tile = 4 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16.  Operand tiles go straight from global memory to
-// LDS with buffer loads (buffer_load_dwordx4 ... lds): each instruction fills
-// 1 KB of LDS, lane l writing bytes [16 l, 16 l + 16) of it, so the lane ->
-// global address mapping realizes the LDS layout.  Rows are 128 bytes; the
-// 16-byte chunks of a row are XOR-permuted by (row >> 1) & 7, which makes
-// the fragment reads (16 lanes = 16 consecutive rows at one k offset per
-// LDS cycle on the 64-bank LDS) conflict-free.  Two LDS stages: the loads of
-// k-tile t + 2 are issued right after the barrier that frees stage t % 2,
-// which sits before the last k-step of tile t, so they, and the first
-// fragment reads of tile t + 1, overlap that k-step's MFMAs.  Fragment reads
-// of k-step s + 1 are interleaved one per MFMA with the MFMAs of k-step s.
-// Out-of-range rows and k-columns read as zeros (buffer range checking).
-// An output element's k order is the same in every launch (no split-k), so
-// the projection is bitwise identical wherever a row or vocabulary slice
-// falls; the backward relies on it.
+// Block tile 256 x 256, k-tile 64, 512 threads = 8 waves (2 per SIMD) in a
+// 2 (m) x 4 (n) grid, each wave owning a 128 x 64 sub-tile = 8 x 4 blocks of
+// v_mfma_f32_16x16x32_bf16.  (On this part the 16x16x32 form sustains a
+// higher clock under full load than the 32x32x16 form, for the same work per
+// cycle.)  Operand tiles go straight from global memory to LDS with buffer
+// loads (buffer_load_dwordx4 ... lds): each instruction fills 1 KB of LDS,
+// lane l writing bytes [16 l, 16 l + 16) of it, so the lane -> global address
+// mapping realizes the LDS layout.  Rows are 128 bytes; the 16-byte chunks of
+// a row are XOR-permuted by (row >> 1) & 7, which makes the fragment reads
+// (16 lanes = 16 consecutive rows at one k offset per LDS cycle on the
+// 64-bank LDS) conflict-free.  Two LDS stages.  A k-tile is two k-steps of
+// 32; the fragments of k-step s + 1 are read (one LDS read per two MFMAs)
+// while the MFMAs of k-step s run.  Halfway through the last k-step of tile t
+// sits the one barrier of the tile: it waits for tile t + 1 to land and frees
+// stage t % 2; right after it the first fragments of tile t + 1 are read and
+// the loads of tile t + 2 are issued, interleaved with the remaining MFMAs,
+// so the matrix pipe keeps work queued across the barrier.  The steady-state
+// tile is one basic block (no branches), which keeps that interleaving
+// intact.  Out-of-range rows and k-columns read as zeros (buffer range
+// checking).  An output element's k order is the same in every launch (no
+// split-k), so the projection is bitwise identical wherever a row or
+// vocabulary slice falls; the backward relies on it.
 //
 // Accumulator layout, shared by both main loops and read by the epilogues:
-// acc[i][j][r] (i < 4, j < 2, r < 16) of lane l in wave w (wm = w / 4,
+// acc[i][j][r] (i < 8, j < 4, r < 4) of lane l in wave w (wm = w / 4,
 // wn = w % 4) holds
-//   m = m0 + wm*128 + i*32 + (r/4)*8 + (l/32)*4 + (r%4)
-//   n = n0 + wn*64 + j*32 + (l%32).
+//   m = m0 + wm*128 + i*16 + (l/16)*4 + r
+//   n = n0 + wn*64 + j*16 + (l%16).
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -37,12 +44,13 @@ namespace stce {
 
 constexpr int GM = 256, GN = 256, GK = 64;
 constexpr int GTHREADS = 512;
-constexpr int ACC_I = 4, ACC_J = 2;
+constexpr int ACC_I = 8, ACC_J = 4, ACC_R = 4;
 
-typedef f32x16 AccTile[ACC_I][ACC_J];
+typedef f32x4 AccTile[ACC_I][ACC_J];
 
-__device__ inline int acc_row(int wm, int i, int r, int half) { return wm * 128 + i * 32 + (r >> 2) * 8 + half * 4 + (r & 3); }
-__device__ inline int acc_col(int wn, int j, int col) { return wn * 64 + j * 32 + col; }
+// quad = lane / 16, col = lane % 16
+__device__ inline int acc_row(int wm, int i, int r, int quad) { return wm * 128 + i * 16 + quad * 4 + r; }
+__device__ inline int acc_col(int wn, int j, int col) { return wn * 64 + j * 16 + col; }
 
 // Linear workgroup id -> output tile.  Workgroups are dispatched round-robin
 // over the 8 XCDs (id % 8); the remap gives each XCD a contiguous range of
@@ -96,7 +104,8 @@ struct MainBf16 {
   int K;  // multiple of 8
 
   __device__ inline void run(AccTile& acc, int m0, int n0, char* smem) const {
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases stay scalar
     const int wm = w >> 2, wn = w & 3;
     // each resource spans only this tile's (at most 256) rows, so offsets
     // stay far below 2^31 and the tail sentinel below is always out of range
@@ -106,94 +115,97 @@ struct MainBf16 {
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)(B + (int64_t)n0 * ldb), (short)0,
                                                                         rowsB * (int)ldb * 2, RSRC_WORD3);
     // load instruction i of wave w fills rows (w*LPW + i)*8 .. +8 of a tile;
-    // lane l covers row + l/8, physical chunk l%8
+    // lane l covers row + l/8 and physical chunk l%8, i.e. logical chunk
+    // (l%8) ^ swz(row); the swizzle uses row bits 1..3, bit 3 being the
+    // parity of i
     const int lrow = lane >> 3, lpc = lane & 7;
-    int voffA[LPW], voffB[LPW], lchunk[LPW];
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int row = (w * LPW + i) * 8 + lrow;
-      lchunk[i] = lpc ^ lds_swz(row);
-      voffA[i] = row * (int)lda * 2 + lchunk[i] * 16;
-      voffB[i] = row * (int)ldb * 2 + lchunk[i] * 16;
-    }
+    const int ce = lpc ^ lds_swz(lrow), co = lpc ^ lds_swz(lrow + 8);
+    const int rA = (w * LPW * 8 + lrow) * (int)lda * 2, rB = (w * LPW * 8 + lrow) * (int)ldb * 2;
+    const int stepA = 8 * (int)lda * 2, stepB = 8 * (int)ldb * 2;
     const int nk = (K + GK - 1) / GK;
-    auto issue = [&](int kt) {
-      char* st = smem + (kt & 1) * STAGEB;
-      const int k0 = kt * GK;
-      const int so = k0 * 2;
-      if (k0 + GK <= K) {
+    // loads of k-tile kt into stage kt % 2; 16-byte chunks at or past K get
+    // an offset beyond the buffer's range, which the hardware turns into zeros
+    auto issue = [&](int kt) __attribute__((always_inline)) {
+      char* st = smem + (kt & 1) * STAGEB + w * LPW * 1024;
+      const int k0 = kt * GK, so = k0 * 2;
+      const bool ine = k0 + ce * 8 < K, ino = k0 + co * 8 < K;
 #pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, STCE_LDS(st + (w * LPW + i) * 1024), 16, voffA[i], so, 0, 0);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, STCE_LDS(st + TILEB + (w * LPW + i) * 1024), 16, voffB[i], so,
-                                                   0, 0);
-        }
-      } else {
-        // k tail: chunks at or past K get an offset beyond the buffer's
-        // range, which the hardware turns into zeros
-#pragma unroll
-        for (int i = 0; i < LPW; ++i) {
-          const bool in = k0 + lchunk[i] * 8 < K;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, STCE_LDS(st + (w * LPW + i) * 1024), 16,
-                                                   in ? voffA[i] : 0x7ffffff0, so, 0, 0);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, STCE_LDS(st + TILEB + (w * LPW + i) * 1024), 16,
-                                                   in ? voffB[i] : 0x7ffffff0, so, 0, 0);
-        }
+      for (int i = 0; i < LPW; ++i) {
+        const bool in = (i & 1) ? ino : ine;
+        const int c16 = ((i & 1) ? co : ce) * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, STCE_LDS(st + i * 1024), 16, in ? rA + i * stepA + c16 : 0x7ffffff0,
+                                                 so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, STCE_LDS(st + TILEB + i * 1024), 16,
+                                                 in ? rB + i * stepB + c16 : 0x7ffffff0, so, 0, 0);
       }
     };
-    const int frow = lane & 31, fhalf = lane >> 5, sw = lds_swz(frow);
-    int offA[4], offB[2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) offA[i] = (wm * 128 + i * 32 + frow) * ROWB;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) offB[j] = TILEB + (wn * 64 + j * 32 + frow) * ROWB;
-    auto rd = [&](bf16x8 (&a)[4], bf16x8 (&b)[2], int kt, int kk) {
+    // fragment of a 16 x 32 (rows x k) block: lane l reads row l % 16, the
+    // 16-byte chunk l / 16 of the k-step's 32 columns
+    const int frow = lane & 15, fq = lane >> 4, sw = lds_swz(frow);
+    const int offA = (wm * 128 + frow) * ROWB, offB = TILEB + (wn * 64 + frow) * ROWB;
+    bf16x8 fa[2][ACC_I], fb[2][ACC_J];
+    auto rd = [&](bf16x8 (&a)[ACC_I], bf16x8 (&b)[ACC_J], int kt, int kk) __attribute__((always_inline)) {
       const char* st = smem + (kt & 1) * STAGEB;
-      const int ch = ((kk * 2 + fhalf) ^ sw) * 16;
+      const int ch = ((kk * 4 + fq) ^ sw) * 16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(st + offA[i] + ch);
+      for (int i = 0; i < ACC_I; ++i) a[i] = *(const bf16x8*)(st + offA + i * 16 * ROWB + ch);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = *(const bf16x8*)(st + offB[j] + ch);
+      for (int j = 0; j < ACC_J; ++j) b[j] = *(const bf16x8*)(st + offB + j * 16 * ROWB + ch);
+    };
+    auto mma = [&](int cur, int i0, int i1) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = i0; i < i1; ++i)
+#pragma unroll
+        for (int j = 0; j < ACC_J; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+    };
+    // one k-tile; NEXT: a tile follows (barrier + its first fragments),
+    // ISSUE: the tile after that is loaded into the stage this one frees
+    auto tile = [&](int kt, auto next_c, auto issue_c) __attribute__((always_inline)) {
+      constexpr bool NEXT = decltype(next_c)::value, ISSUE = decltype(issue_c)::value;
+      rd(fa[1], fb[1], kt, 1);
+      mma(0, 0, ACC_I);
+#pragma unroll
+      for (int q = 0; q < ACC_I + ACC_J; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, ACC_I * ACC_J - 2 * (ACC_I + ACC_J), 0);
+      mma(1, 0, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (NEXT) {
+        // tile kt + 1 has landed (every wave waits for its own loads) and
+        // every wave is done reading stage kt % 2 before it is refilled
+        __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        rd(fa[0], fb[0], kt + 1, 0);
+        if (ISSUE) issue(kt + 2);
+      }
+      mma(1, 2, ACC_I);
+      if (NEXT) {
+#pragma unroll
+        for (int q = 0; q < ACC_I + ACC_J; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (ISSUE && q < 2 * LPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     };
 
     issue(0);
     __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
     __syncthreads();
-    bf16x8 fa[2][4], fb[2][2];
     rd(fa[0], fb[0], 0, 0);
     if (1 < nk) issue(1);
-    for (int kt = 0; kt < nk; ++kt) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int cur = kk & 1, nxt = cur ^ 1;
-        if (kk < 3) {
-          rd(fa[nxt], fb[nxt], kt, kk + 1);
-        } else if (kt + 1 < nk) {
-          // tile kt + 1 has landed (every wave waits for its own loads) and
-          // every wave is done reading stage kt & 1 before it is refilled
-          __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
-          __syncthreads();
-          rd(fa[nxt], fb[nxt], kt + 1, 0);
-          if (kt + 2 < nk) issue(kt + 2);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
-        // one LDS read (or operand load) issued after each MFMA
-#pragma unroll
-        for (int q = 0; q < 6; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, LPW, 0);
-        }
-      }
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) tile(kt, std::true_type{}, std::true_type{});
+    if (kt + 1 < nk) {
+      tile(kt, std::true_type{}, std::false_type{});
+      ++kt;
     }
+    tile(kt, std::false_type{}, std::false_type{});
     __syncthreads();  // the epilogue may reuse the LDS
   }
 };
@@ -240,12 +252,12 @@ struct MainF32 {
       for (int kk = 0; kk < BK; ++kk) {
         float bv[ACC_J];
 #pragma unroll
-        for (int j = 0; j < ACC_J; ++j) bv[j] = sb[acc_col(wn, j, lane & 31) * (BK + 1) + kk];
+        for (int j = 0; j < ACC_J; ++j) bv[j] = sb[acc_col(wn, j, lane & 15) * (BK + 1) + kk];
 #pragma unroll
         for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float av = sa[acc_row(wm, i, r, lane >> 5) * (BK + 1) + kk];
+          for (int r = 0; r < ACC_R; ++r) {
+            const float av = sa[acc_row(wm, i, r, lane >> 4) * (BK + 1) + kk];
 #pragma unroll
             for (int j = 0; j < ACC_J; ++j) acc[i][j][r] = __builtin_fmaf(av, bv[j], acc[i][j][r]);
           }
@@ -264,7 +276,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(Main mainloop, Epi ep
 #pragma unroll
   for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-    for (int j = 0; j < ACC_J; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < ACC_J; ++j) acc[i][j] = f32x4{};
   mainloop.run(acc, tm * GM, tn * GN, smem);
   epi(acc, tm * GM, tn * GN, smem);
 }

@@ -52,7 +52,10 @@ def test_workspace_sizes_are_host_computable(lib):
     f, b = binding.workspace_bytes(_prob())
     assert f > 8 * 100 * 4 and b > 0
     f2, _ = binding.workspace_bytes(_prob(T=100000, chunk_rows=512))
-    assert f2 < 512 * 101 * 4 + 100000 * 4 + 4 * 512 * 16 + 4096
+    # bounded by two chunk buffers (keys, tile partials, target keys; the
+    # selection of one chunk overlaps the projection of the next) plus the
+    # per-row flags: nothing scales with T x V
+    assert f2 < 2 * (512 * 101 * 4 + 512 * 16 + 512 * 4) + 100000 * 4 + 4096
     assert lib.stce_state_bytes(10) == 320
 
 
