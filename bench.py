@@ -106,6 +106,120 @@ def cpu_baseline(w, y, rows):
                        f"and their whole grad_weight contribution), fp64 numpy, {dt:.1f} s")
 
 
+KERNEL_SYMBOLS = {
+    # kernel kind -> substring of its symbol in counter output
+    "projection": "gemm_kernelINS_8MainBf16ENS_9EpiLogits",
+    "dlogits": "gemm_kernelINS_8MainBf16ENS_10EpiDlogits",
+    "grad_weight": "gemm_kernelINS_8MainBf16ENS_8EpiStore",
+    "grad_hidden": "gemm_kernelINS_8MainBf16ENS_8EpiAccum",
+}
+
+
+def source_digest():
+    """sha256 over the kernel sources; a traffic figure is valid only for the
+    sources it was measured on."""
+    import hashlib
+    d = os.path.join(ROOT, "sampling_transform_logprob_amd", "csrc")
+    hsh = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            hsh.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                hsh.update(f.read())
+    return hsh.hexdigest()
+
+
+def traffic_file(kernel, config):
+    return os.path.join(ROOT, "profiles", f"{kernel}_{config}_hbm_traffic.txt")
+
+
+def read_traffic(kernel, config):
+    """HBM bytes per launch of `kernel` from its committed counter summary, or
+    None when there is none or the kernel sources changed since."""
+    try:
+        with open(traffic_file(kernel, config)) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(" "))
+    except OSError:
+        return None
+    if kv.get("source_sha256", "").strip() != source_digest():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def _counter_rows(path, name_part):
+    import csv
+    import glob
+    out = []
+    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if name_part in r["Kernel_Name"]:
+                out.append(float(r["Counter_Value"]))
+    return out
+
+
+def traffic_summary(args):
+    """Writes the per-launch HBM traffic of the dominant kernel from four
+    rocprofv3 --pmc runs: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) over
+    this bench, each scaled by what the same counter reads for a plain device
+    copy of known size (--copy-calibration)."""
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic_summary
+    kernel, config = args.traffic_kernel, args.config
+    sym = KERNEL_SYMBOLS[kernel]
+    copy_sym = "copyBuffer"
+    n_copy = float(1 << 30)
+    cf = _counter_rows(cfetch_dir, copy_sym)
+    cw = _counter_rows(cwrite_dir, copy_sym)
+    kf = _counter_rows(fetch_dir, sym)
+    kw = _counter_rows(write_dir, sym)
+    assert cf and cw and kf and kw, "missing dispatches in the counter output"
+    # the calibration makes three copies; a copy may be split over dispatches
+    cf_copy, cw_copy = sum(cf) / 3.0, sum(cw) / 3.0
+    f_fac = n_copy / (cf_copy * 1024.0)     # bytes per counted KiB, reads
+    w_fac = n_copy / (cw_copy * 1024.0)     # writes
+    fetch_b = float(np.mean(kf)) * 1024.0 * f_fac
+    write_b = float(np.mean(kw)) * 1024.0 * w_fac
+    lines = [
+        f"kernel: {kernel} ({sym})",
+        f"workload: {config}",
+        f"source_sha256: {source_digest()}",
+        "commands (from the repository root, one rocprofv3 run each):",
+        f"  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <F> -- python3 bench.py --steps 1 --warmup 0 "
+        f"--no-cpu-baseline --config {config}",
+        f"  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <W> -- python3 bench.py --steps 1 --warmup 0 "
+        f"--no-cpu-baseline --config {config}",
+        "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <CF> -- python3 bench.py --copy-calibration",
+        "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <CW> -- python3 bench.py --copy-calibration",
+        f"  python3 bench.py --traffic-summary <F> <W> <CF> <CW> --traffic-kernel {kernel} --config {config}",
+        f"copy calibration: a 1 GiB device copy counts FETCH_SIZE {cf_copy:.0f} KiB (factor {f_fac:.4f}), "
+        f"WRITE_SIZE {cw_copy:.0f} KiB (factor {w_fac:.4f})",
+        f"dispatches: {len(kf)} (FETCH run), {len(kw)} (WRITE run)",
+        f"FETCH_SIZE per dispatch: mean {np.mean(kf):.0f} KiB, min {min(kf):.0f}, max {max(kf):.0f}",
+        f"WRITE_SIZE per dispatch: mean {np.mean(kw):.0f} KiB, min {min(kw):.0f}, max {max(kw):.0f}",
+        f"fetch_bytes_per_launch: {fetch_b:.6e}",
+        f"write_bytes_per_launch: {write_b:.6e}",
+        f"traffic_bytes_per_launch: {fetch_b + write_b:.6e}",
+        "note: FETCH_SIZE and WRITE_SIZE count L2 <-> fabric traffic, so reads served by the",
+        "  Infinity Cache are included; the figure is an upper bound on HBM bytes",
+    ]
+    os.makedirs(os.path.dirname(traffic_file(kernel, config)), exist_ok=True)
+    with open(traffic_file(kernel, config), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB, three times (counter scale)."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,11 +230,23 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--chunk-rows", type=int, default=0)
     ap.add_argument("--vocab-slice", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy (scale of the HBM byte counters) and exit")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write the HBM traffic summary of --traffic-kernel from rocprofv3 --pmc outputs and exit")
+    ap.add_argument("--traffic-kernel", default="dlogits")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
 
@@ -234,7 +360,8 @@ def main():
         "tflops_8thv": flop_step / (ms_step * 1e-3) / 1e12,
         "tflops_6thv": 6.0 * T * H * V / (ms_step * 1e-3) / 1e12,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": read_traffic(dom, args.config)},
         "kernels": stats,
         "targets_in_support": in_support,
     }

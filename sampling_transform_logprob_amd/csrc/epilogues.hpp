@@ -78,6 +78,7 @@ struct EpiLogits {
   float* s_y;              // [N] or null
   int V;                   // valid vocabulary rows
   int N;                   // valid tokens
+  static constexpr int LDS_BYTES = 2 * GN * 3 * 4;  // cross-wave merge
 
   __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -224,6 +225,11 @@ struct EpiDlogits {
   OutT* dT;                // [Vs_pad][ld_dT]
   int64_t ld_dT;
   int v0, Vs, Vs_pad, N, N_pad;
+  // bf16: the vocab-major copy is staged in LDS with rows padded to SROW
+  // elements (528 bytes), so the four quads of a wave, 4 rows apart, write
+  // distinct banks
+  static constexpr int SROW = GN + 8;
+  static constexpr int LDS_BYTES = sizeof(OutT) == 2 ? GM * SROW * 2 : 0;
 
   __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -275,9 +281,9 @@ struct EpiDlogits {
           uint32_t p1 = (uint32_t)__builtin_bit_cast(uint16_t, v[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[3]) << 16);
           typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
           *(u32x2*)(dr + mm) = u32x2{p0, p1};
-          // stage the vocab-major copy in LDS: [m - m0][n - n0], 512-byte rows
+          // stage the vocab-major copy in LDS: [m - m0][n - n0]
 #pragma unroll
-          for (int e = 0; e < ACC_R; ++e) ((OutT*)smem)[(mm + e - m0) * GN + (n - n0)] = v[e];
+          for (int e = 0; e < ACC_R; ++e) ((OutT*)smem)[(mm + e - m0) * SROW + (n - n0)] = v[e];
         } else {
 #pragma unroll
           for (int e = 0; e < ACC_R; ++e) dr[mm + e] = v[e];
@@ -294,7 +300,7 @@ struct EpiDlogits {
       for (int c16 = tid; c16 < GM * (GN / 8); c16 += GTHREADS) {
         const int r = c16 / (GN / 8), cc = (c16 % (GN / 8)) * 8;
         if (r < rows && cc < cols)
-          *(u32x4*)(dT + (int64_t)(m0 + r) * ld_dT + n0 + cc) = *(const u32x4*)((const OutT*)smem + r * GN + cc);
+          *(u32x4*)(dT + (int64_t)(m0 + r) * ld_dT + n0 + cc) = *(const u32x4*)((const OutT*)smem + r * SROW + cc);
       }
     }
   }
@@ -308,6 +314,7 @@ struct EpiStore {
   int64_t ld;
   int M, N;
   int accumulate;
+  static constexpr int LDS_BYTES = 0;
 
   __device__ inline void operator()(AccTile& acc, int m0, int n0, char*) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -342,6 +349,7 @@ struct EpiAccum {
   OutT* out;   // [M][ld]
   int M, N;
   int first, last;
+  static constexpr int LDS_BYTES = 0;
 
   __device__ inline void operator()(AccTile& acc, int m0, int n0, char*) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;

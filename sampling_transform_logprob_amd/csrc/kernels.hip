@@ -96,11 +96,12 @@ template <class Main, class Epi>
 hipError_t launch_gemm(const Main& mn, const Epi& ep, int64_t tiles_m, int64_t tiles_n, hipStream_t s) {
   if (tiles_m <= 0 || tiles_n <= 0) return hipSuccess;
   auto kern = gemm_kernel<Main, Epi>;
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Main::LDS_BYTES);
+  constexpr int lds = Main::LDS_BYTES > Epi::LDS_BYTES ? Main::LDS_BYTES : Epi::LDS_BYTES;
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  static const hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   TileMap map{(int)tiles_m, (int)tiles_n, 4};
-  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(GTHREADS), Main::LDS_BYTES, s, mn, ep, map);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(GTHREADS), lds, s, mn, ep, map);
   return hipGetLastError();
 }
 
