@@ -5,5 +5,5 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 """
 from .stce_oracle import (  # noqa: F401
     MARGIN, backward, canonical_f32, chunk_logits, dlogits, forward, in_support,
-    order_keys, order_row, sample_targets, scale_logits, support, support_row,
+    OBJECTIVES, order_keys, order_row, policy_loss, sample_targets, scale_logits, support, support_row,
 )

@@ -47,6 +47,18 @@ The pipeline per scored row t (a token of a replayed rollout):
    softmax of ``z / T`` restricted to the support, then ``dH = dz W`` and
    ``dW = dz^T h``.
 
+A policy-gradient token loss on top of the selected logprob ([align-v2]
+5.4 A, "Why the in-chunk form works for this loss"): with the ratio
+``r = exp(logprob - logprob_old)`` and advantage ``A``, the loss sign (the
+quantity an optimizer minimises) has ``d loss / d z = c (q - onehot) / T``,
+i.e. ``d loss / d logprob = -c``, where
+  CISPO:              c = A * sg(min(r, 1 + eps_high))   (no lower bound)
+  clipped surrogate:  c = A * r * 1[the unclipped term is the minimum]
+so the per-token losses are ``-A sg(min(r, 1+eps_high)) logprob`` and
+``-min(r A, clip(r, 1-eps_low, 1+eps_high) A)``, each times a caller scale
+(the reciprocal of a constant denominator).  The gradient then flows
+through the same VJP as the logprob with ``g = d loss / d logprob``.
+
 Values (logprob, gradients) use the unrounded fp64 logits ``u = z / T``.
 Support decisions use only the fp32 keys, so a caller may pass the keys of
 another implementation (``keys=``) to compare supports bit for bit.
@@ -293,6 +305,62 @@ def backward(h, W, target, fwd: dict, grad_logprob, temperature=None):
     h64 = np.asarray(h, dtype=np.float64)[fwd["rows"]]
     W64 = np.asarray(W, dtype=np.float64)
     return dz @ W64, dz.T @ h64
+
+
+OBJECTIVES = ("cispo", "clip")
+
+
+def policy_loss(logprob, advantages, old_logprob, objective="cispo", eps_low=0.2, eps_high=0.28,
+                scale=1.0) -> dict:
+    """Per-token policy-gradient loss and ``g = d loss / d logprob``.
+
+    [align-v2] 5.4 A: the token coefficient ``c`` of ``d loss / d z =
+    c (softmax - onehot)`` is ``A sg(clip(r, ., 1 + eps_high))`` for CISPO
+    (the importance weight is a stop-gradient constant, with no lower clip)
+    and ``A r 1[not clipped]`` for the clipped surrogate (clip-higher
+    PPO/DAPO), both in the loss sign; ``d logprob / d z = onehot - softmax``,
+    so ``g = -c``.  The losses are the functions with those derivatives:
+    ``-A sg(w) logprob`` and ``-min(r A, clip(r, 1 - eps_low, 1 + eps_high) A)``.
+
+    A row whose logprob is -inf (target outside the support) has no
+    defined ratio; it contributes zero loss and zero gradient, like the
+    logprob's own gradient on such rows.  A NaN logprob (invalid row)
+    gives a NaN loss and zero gradient.  Everything is multiplied by
+    ``scale``.  Returns ``loss``, ``g`` and ``ratio`` (fp64 arrays).
+    """
+    if objective not in OBJECTIVES:
+        raise ValueError(f"objective must be one of {OBJECTIVES}")
+    lp = np.asarray(logprob, np.float64)
+    A = np.asarray(advantages, np.float32).astype(np.float64)
+    old = np.asarray(old_logprob, np.float32).astype(np.float64)
+    eh = float(np.float32(eps_high))
+    el = float(np.float32(eps_low))
+    sc = float(np.float32(scale))
+    loss = np.zeros_like(lp)
+    g = np.zeros_like(lp)
+    ratio = np.zeros_like(lp)
+    for t in range(lp.shape[0]):
+        if math.isnan(lp[t]):
+            loss[t] = math.nan
+            continue
+        if lp[t] == -math.inf:
+            continue
+        r = math.exp(lp[t] - old[t])
+        ratio[t] = r
+        if objective == "cispo":
+            wgt = min(r, 1.0 + eh)
+            loss[t] = -A[t] * wgt * lp[t]
+            g[t] = -A[t] * wgt
+        else:
+            unclipped = r * A[t]
+            clipped = min(max(r, 1.0 - el), 1.0 + eh) * A[t]
+            if unclipped <= clipped:
+                loss[t] = -unclipped
+                g[t] = -A[t] * r
+            else:
+                loss[t] = -clipped
+                g[t] = 0.0
+    return dict(loss=loss * sc, g=g * sc, ratio=ratio)
 
 
 def sample_targets(h, W, temperature, top_k, top_p, min_p, u, rows=None) -> np.ndarray:

@@ -42,6 +42,16 @@ MUTANTS = {
                                               "test_min_p_closed_form_matches_probability_space"]),
     "dW uses the wrong operand": ("return dz @ W64, dz.T @ h64", "return dz @ W64, dz.T @ (h64 * 0.5)",
                                   ["test_gradients_match_central_differences"]),
+    "CISPO weight not a stop-gradient": ("            g[t] = -A[t] * wgt\n",
+                                         "            g[t] = -A[t] * wgt - (A[t] * r * lp[t] if r < 1.0 + eh else 0.0)\n",
+                                         ["test_policy_gradient_matches_autograd_of_objective"]),
+    "clipped surrogate takes the max": ("            if unclipped <= clipped:", "            if unclipped >= clipped:",
+                                        ["test_policy_loss_special_cases",
+                                         "test_clipped_policy_gradient_matches_central_differences"]),
+    "policy gradient in the objective's sign": ("    return dict(loss=loss * sc, g=g * sc, ratio=ratio)",
+                                                "    return dict(loss=loss * sc, g=-g * sc, ratio=ratio)",
+                                                ["test_policy_gradient_matches_autograd_of_objective",
+                                                 "test_clipped_policy_gradient_matches_central_differences"]),
 }
 
 
@@ -63,7 +73,12 @@ def test_pins_catch_mutant(name, monkeypatch):
         rng = np.random.Generator(np.random.PCG64(20261203))
         fn = getattr(pins, t)
         try:
-            fn(rng) if fn.__code__.co_argcount else fn()
+            args = fn.__code__.co_varnames[: fn.__code__.co_argcount]
+            if "objective" in args:
+                for obj in ("cispo", "clip"):
+                    fn(np.random.Generator(np.random.PCG64(20261203)), obj)
+            else:
+                fn(rng) if args else fn()
         except Exception:  # noqa: BLE001 -- any failure of the pin counts
             caught.append(t)
     assert caught, f"mutant '{name}' survived {tests}"

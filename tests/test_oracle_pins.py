@@ -413,3 +413,107 @@ def test_bad_metadata_is_rejected():
     with pytest.raises(ValueError):
         oracle.forward(np.ones((1, 2), np.float32), np.ones((3, 2), np.float32), np.array([0]),
                        np.array([0.0], np.float32))
+
+
+# ---------------------------------------------------------------- policy-gradient loss
+def _pg_problem(rng, T=6, H=10, V=24):
+    h, W, temp = _problem(rng, T, H, V, scale=2)
+    meta = dict(top_k=np.array([0, 5, 0, 8, 0, 3][:T]), top_p=np.array([1.0, 1.0, 0.9, 1.0, 0.8, 1.0][:T], np.float32),
+                min_p=np.zeros(T, np.float32))
+    f0 = oracle.forward(h, W, np.zeros(T, np.int64), temp, **meta)
+    y = np.array([oracle.order_row(f0["keys"][t])[t % 2] for t in range(T)])
+    f = oracle.forward(h, W, y, temp, **meta)
+    assert f["in_support"].all()
+    # old logprobs put the ratios on both sides of both clip bounds
+    offs = np.array([-1.0, -0.1, 0.05, 0.4, 1.3, -0.6][:T])
+    old = (f["logprob"] + offs).astype(np.float32)
+    A = np.array([1.5, -0.7, 2.0, -1.2, 0.8, -2.5][:T], np.float32)
+    return h, W, temp, meta, y, f, old, A
+
+
+@pytest.mark.parametrize("objective", ["cispo", "clip"])
+def test_policy_gradient_matches_autograd_of_objective(rng, objective):
+    """d loss / d(h, W) through the selected logprob, against fp64 autograd of
+    the objective written on the logits (CISPO's weight detached)."""
+    torch = pytest.importorskip("torch")
+    h, W, temp, meta, y, f, old, A = _pg_problem(rng)
+    el, eh, sc = (float(np.float32(x)) for x in (0.2, 0.28, 0.125))   # parameters are fp32 values
+    pg = oracle.policy_loss(f["logprob"], A, old, objective, el, eh, sc)
+    dH, dW = oracle.backward(h, W, y, f, pg["g"], temp)
+    th = torch.tensor(h, dtype=torch.float64, requires_grad=True)
+    tW = torch.tensor(W, dtype=torch.float64, requires_grad=True)
+    u = (th @ tW.T) / torch.tensor(temp, dtype=torch.float64)[:, None]
+    L = 0
+    for t in range(len(y)):
+        S = torch.tensor(oracle.order_row(f["keys"][t])[: f["n"][t]])
+        lp = torch.clamp(u[t, int(y[t])] - torch.logsumexp(u[t, S], 0), max=0.0)
+        r = torch.exp(lp - float(old[t]))
+        a = float(A[t])
+        if objective == "cispo":
+            L = L - a * torch.clamp(r, max=1 + eh).detach() * lp
+        else:
+            L = L - torch.minimum(r * a, torch.clamp(r, 1 - el, 1 + eh) * a)
+    L = L * sc
+    L.backward()
+    assert abs(float(L) - pg["loss"].sum()) < 1e-12 * max(1.0, abs(float(L)))
+    np.testing.assert_allclose(dH, th.grad.numpy(), rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(dW, tW.grad.numpy(), rtol=1e-11, atol=1e-14)
+
+
+def test_policy_loss_special_cases():
+    """Hand-worked values: ratio 1, zero advantage, each clip branch, -inf and NaN rows."""
+    e = math.e
+    lp = np.array([-0.5, -0.5, -1.0, -1.0, -2.0, -1.0, -3.0, -math.inf, math.nan])
+    # ratio:        1     1     e     e^-1  e     e^-1   1     -       -
+    old = np.array([-0.5, -0.5, -2.0, 0.0, -3.0, 0.0, -3.0, -1.0, -1.0], np.float32)
+    A = np.array([2.0, 0.0, 2.0, -2.0, -2.0, 2.0, -1.0, 3.0, 3.0], np.float32)
+    c = oracle.policy_loss(lp, A, old, "clip", eps_low=0.25, eps_high=0.5)
+    want_loss = [2.0 * -1, 0.0, -1.5 * 2.0, 0.75 * 2.0, 2.0 * e, -2.0 / e, 1.0, 0.0, math.nan]
+    want_g = [-2.0, 0.0, 0.0, 0.0, 2.0 * e, -2.0 / e, 1.0, 0.0, 0.0]
+    np.testing.assert_allclose(c["loss"], want_loss, rtol=1e-6)
+    np.testing.assert_allclose(c["g"], want_g, rtol=1e-6, atol=1e-12)
+    k = oracle.policy_loss(lp, A, old, "cispo", eps_high=0.5)
+    # weight min(r, 1.5): 1, 1, 1.5, e^-1, 1.5, e^-1, 1
+    w = [1.0, 1.0, 1.5, 1 / e, 1.5, 1 / e, 1.0]
+    want_g = [-A[i] * w[i] for i in range(7)] + [0.0, 0.0]
+    want_loss = [-A[i] * w[i] * lp[i] for i in range(7)] + [0.0, math.nan]
+    np.testing.assert_allclose(k["loss"], want_loss, rtol=1e-6, atol=1e-12)
+    np.testing.assert_allclose(k["g"], want_g, rtol=1e-6, atol=1e-12)
+    s = oracle.policy_loss(lp[:1], A[:1], old[:1], "cispo", scale=0.25)
+    assert s["loss"][0] == 0.25 * -2.0 * -0.5 * 1.0 and s["g"][0] == 0.25 * -2.0
+    with pytest.raises(ValueError):
+        oracle.policy_loss(lp, A, old, "ppo")
+
+
+def test_clipped_policy_gradient_matches_central_differences(rng):
+    """The clipped surrogate has a true gradient away from its kinks."""
+    h, W, temp, meta, y, f, old, A = _pg_problem(rng, T=4, H=6, V=10)
+    S = [oracle.order_row(f["keys"][t])[: f["n"][t]] for t in range(4)]
+    el, eh = float(np.float32(0.2)), float(np.float32(0.28))
+    pg = oracle.policy_loss(f["logprob"], A, old, "clip", el, eh)
+    dH, dW = oracle.backward(h, W, y, f, pg["g"], temp)
+    h64, W64, t64 = h.astype(np.float64), W.astype(np.float64), temp.astype(np.float64)
+
+    def total(hh, WW):
+        u = (hh @ WW.T) / t64[:, None]
+        tot = 0.0
+        for t in range(4):
+            mx = u[t, S[t]].max()
+            lp = min(u[t, y[t]] - (mx + math.log(np.exp(u[t, S[t]] - mx).sum())), 0.0)
+            r = math.exp(lp - float(old[t]))
+            tot += -min(r * float(A[t]), min(max(r, 1 - el), 1 + eh) * float(A[t]))
+        return tot
+
+    eps = 1e-6
+    for arr, grad in ((h64, dH), (W64, dW)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            o = arr[idx]
+            arr[idx] = o + eps
+            fp = total(h64, W64)
+            arr[idx] = o - eps
+            fm = total(h64, W64)
+            arr[idx] = o
+            num[idx] = (fp - fm) / (2 * eps)
+        rel = np.linalg.norm(num - grad) / np.linalg.norm(grad)
+        assert rel < 1e-6, rel
