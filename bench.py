@@ -235,6 +235,9 @@ def main():
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write the HBM traffic summary of --traffic-kernel from rocprofv3 --pmc outputs and exit")
     ap.add_argument("--traffic-kernel", default="dlogits")
+    ap.add_argument("--policy-loss", choices=["none", "cispo", "clip"], default="none",
+                    help="time the fused policy-gradient step instead: forward, per-token loss (advantages "
+                         "and behaviour logprobs synthetic), backward of the summed loss")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(args)
@@ -281,10 +284,23 @@ def main():
     g = torch.full((T,), -1.0 / T, dtype=torch.float32, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     P = ctypes.byref(prob)
+    pg = None
+    if args.policy_loss != "none":
+        # synthetic advantages and behaviour logprobs (seeded), fp32 on the device
+        rng = np.random.Generator(np.random.PCG64(17))
+        adv = torch.from_numpy(rng.standard_normal(T).astype(np.float32)).to(dev)
+        old_lp = torch.from_numpy((-rng.exponential(1.0, T)).astype(np.float32)).to(dev)
+        loss_t = torch.empty(T, dtype=torch.float32, device=dev)
+        pg = binding.PgParams(binding.PG_OBJECTIVES[args.policy_loss], 0.2, 0.28, 1.0 / T, adv.data_ptr(),
+                              old_lp.data_ptr())
 
     def step():
         binding._check(L.stce_forward(P, ctypes.c_void_p(logprob.data_ptr()), ctypes.c_void_p(state.data_ptr()),
                                       None, ctypes.c_void_p(ws_f.data_ptr()), fwd_b, stream))
+        if pg is not None:
+            binding._check(L.stce_policy_loss(ctypes.byref(pg), T, ctypes.c_void_p(logprob.data_ptr()),
+                                              ctypes.c_void_p(loss_t.data_ptr()), ctypes.c_void_p(g.data_ptr()),
+                                              None, stream))
         binding._check(L.stce_backward(P, ctypes.c_void_p(g.data_ptr()), ctypes.c_void_p(state.data_ptr()),
                                        ctypes.c_void_p(gh.data_ptr()), ctypes.c_void_p(gw.data_ptr()), 0, None,
                                        ctypes.c_void_p(ws_b.data_ptr()), bwd_b, stream))
@@ -354,7 +370,9 @@ def main():
         "config": {"workload": f"{args.config}: T={T} scored tokens, H={H}, V={V}, temperature "
                                f"{'per-row' if args.config != 'headline' else 0.7}, top_k "
                                f"{int(w['top_k'].max())}, top_p {float(w['top_p'].min())}, min_p "
-                               f"{float(w['min_p'].max())}; forward + backward (grad_hidden, grad_weight)",
+                               f"{float(w['min_p'].max())}; forward + backward (grad_hidden, grad_weight)"
+                               + ("" if args.policy_loss == "none" else
+                                  f" of the {args.policy_loss} policy-gradient token loss"),
                    "T": T, "H": H, "V": V, "chunk_rows": C, "vocab_slice": Vs},
         "mfma_peak_frac": flop_step / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "tflops_8thv": flop_step / (ms_step * 1e-3) / 1e12,

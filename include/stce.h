@@ -199,6 +199,7 @@ stce_status stce_decode_state(const void *host_state, int64_t nrows, stce_row_in
 #define STCE_KERNEL_GRAD_HIDDEN 6 /* hidden-gradient product of one slice */
 #define STCE_KERNEL_TRANSPOSE 7
 #define STCE_KERNEL_PARTIALS 8
+#define STCE_KERNEL_POLICY_LOSS 9  /* per-row policy-gradient loss */
 typedef struct stce_profile {
   int32_t capacity;
   int32_t count;
@@ -207,6 +208,42 @@ typedef struct stce_profile {
   int32_t *kind;
 } stce_profile;
 stce_status stce_profile_attach(stce_profile *prof);
+
+/* Policy-gradient token loss on the selected logprob (align "architecture
+ * v2: proposal", section 5.4 A, "Why the in-chunk form works for this
+ * loss").  With the ratio r = exp(logprob - old_logprob) and the advantage
+ * A of each row, the loss-sign token coefficient c of
+ * d loss / d z = c (softmax - onehot) is
+ *   STCE_PG_CISPO: c = A * sg(min(r, 1 + eps_high))  (stop-gradient weight,
+ *                  no lower bound; CISPO);
+ *   STCE_PG_CLIP:  c = A * r * 1[not clipped]          (clipped surrogate,
+ *                  clip-higher PPO / DAPO, ratio bounds 1 - eps_low and
+ *                  1 + eps_high);
+ * and the per-token losses are -A sg(min(r, 1 + eps_high)) logprob and
+ * -min(r A, clip(r, 1 - eps_low, 1 + eps_high) A).  Writes, for t < T,
+ *   loss[t]         = scale * loss_t,
+ *   grad_logprob[t] = scale * d loss_t / d logprob_t  (= -scale * c), the
+ *                     upstream gradient to pass to stce_backward, which
+ *                     then yields the gradient of sum_t loss[t],
+ *   ratio[t]        = r (NULL = skip).
+ * A row whose logprob is -inf (target outside its support) gets loss 0,
+ * gradient 0 and ratio 0; a NaN logprob (invalid row) gets a NaN loss and a
+ * zero gradient.  Arithmetic is fp32.  All arrays are device pointers,
+ * 4-byte aligned; `logprob` is typically stce_forward's output.  Host
+ * errors: NULL pointers, an unknown objective, eps_low outside [0, 1),
+ * eps_high negative or not finite, scale not finite. */
+#define STCE_PG_CISPO 1
+#define STCE_PG_CLIP 2
+typedef struct stce_pg_params {
+  int32_t objective;        /* STCE_PG_CISPO or STCE_PG_CLIP */
+  float eps_low;            /* lower ratio bound 1 - eps_low (STCE_PG_CLIP only) */
+  float eps_high;           /* upper ratio bound 1 + eps_high */
+  float scale;              /* multiplies losses and gradients, e.g. 1 / a constant denominator */
+  const float *advantages;  /* [T] */
+  const float *old_logprob; /* [T] logprob of the target under the behaviour policy */
+} stce_pg_params;
+stce_status stce_policy_loss(const stce_pg_params *pg, int64_t T, const float *logprob, float *loss,
+                             float *grad_logprob, float *ratio, void *stream);
 
 /* Human-readable name of a status code (static string). */
 const char *stce_status_string(stce_status status);

@@ -27,9 +27,11 @@ SYMBOLS = (
     "stce_state_bytes", "stce_workspace_bytes", "stce_forward", "stce_backward",
     "stce_scaled_logits", "stce_support_from_logits", "stce_support_workspace_bytes",
     "stce_decode_state", "stce_status_string", "stce_last_error", "stce_profile_attach", "stce_schedule",
+    "stce_policy_loss",
 )
 KERNEL_KINDS = {1: "validate", 2: "projection", 3: "select", 4: "dlogits", 5: "grad_weight",
-                6: "grad_hidden", 7: "transpose", 8: "partials"}
+                6: "grad_hidden", 7: "transpose", 8: "partials", 9: "policy_loss"}
+PG_OBJECTIVES = {"cispo": 1, "clip": 2}
 
 
 class Problem(ctypes.Structure):
@@ -54,6 +56,13 @@ class Profile(ctypes.Structure):
     _fields_ = [("capacity", ctypes.c_int32), ("count", ctypes.c_int32),
                 ("start", ctypes.POINTER(ctypes.c_void_p)), ("stop", ctypes.POINTER(ctypes.c_void_p)),
                 ("kind", ctypes.POINTER(ctypes.c_int32))]
+
+
+class PgParams(ctypes.Structure):
+    _fields_ = [
+        ("objective", ctypes.c_int32), ("eps_low", ctypes.c_float), ("eps_high", ctypes.c_float),
+        ("scale", ctypes.c_float), ("advantages", ctypes.c_void_p), ("old_logprob", ctypes.c_void_p),
+    ]
 
 
 class StceError(RuntimeError):
@@ -85,6 +94,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "stce_last_error": (ctypes.c_char_p, []),
         "stce_profile_attach": (ctypes.c_int, [ctypes.POINTER(Profile)]),
         "stce_schedule": (ctypes.c_int, [P, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
+        "stce_policy_loss": (ctypes.c_int, [ctypes.POINTER(PgParams), i64, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -260,6 +270,45 @@ def support_from_logits(s, target, top_k=None, top_p=None, min_p=None, *, check:
     if check:
         _raise_rows(status, "stce_support_from_logits", dict(top_k=tk, top_p=tp, min_p=mp, target=target))
     return logprob, state
+
+
+def policy_loss(logprob, advantages, old_logprob, objective: str = "cispo", eps_low: float = 0.2,
+                eps_high: float = 0.28, scale: float = 1.0):
+    """Per-token policy-gradient loss on the selected logprob.
+
+    Returns (loss [T], grad_logprob [T], ratio [T]); grad_logprob is the
+    upstream gradient to pass to ``backward`` for d(sum loss)/d(h, W).
+    """
+    if objective not in PG_OBJECTIVES:
+        raise ValueError(f"objective must be one of {tuple(PG_OBJECTIVES)}")
+    if logprob.dim() != 1 or logprob.dtype != torch.float32:
+        raise ValueError("logprob must be fp32 [T]")
+    T = logprob.shape[0]
+    dev = logprob.device
+    adv = _meta("advantages", advantages, T, torch.float32, dev)
+    old = _meta("old_logprob", old_logprob, T, torch.float32, dev)
+    if adv is None or old is None:
+        raise ValueError("advantages and old_logprob are required")
+    lp = logprob.contiguous()
+    loss = torch.empty(T, dtype=torch.float32, device=dev)
+    grad = torch.empty(T, dtype=torch.float32, device=dev)
+    ratio = torch.empty(T, dtype=torch.float32, device=dev)
+    pg = PgParams(PG_OBJECTIVES[objective], eps_low, eps_high, scale, adv.data_ptr(), old.data_ptr())
+    _check(load().stce_policy_loss(ctypes.byref(pg), T, _ptr(lp), _ptr(loss), _ptr(grad), _ptr(ratio), _stream()))
+    return loss, grad, ratio
+
+
+def policy_loss_step(hidden, weight, target, advantages, old_logprob, temperature=None, top_k=None, top_p=None,
+                     min_p=None, *, objective: str = "cispo", eps_low: float = 0.2, eps_high: float = 0.28,
+                     scale: float = 1.0, need_hidden: bool = True, need_weight: bool = True):
+    """Fused head + policy-gradient token loss: forward, per-token loss and
+    the gradients of ``sum(loss)``.  Returns (loss [T], logprob [T], ratio [T],
+    grad_hidden, grad_weight)."""
+    logprob, state = forward(hidden, weight, target, temperature, top_k, top_p, min_p)
+    loss, g, ratio = policy_loss(logprob, advantages, old_logprob, objective, eps_low, eps_high, scale)
+    gh, gw = backward(hidden, weight, target, state, g, temperature, top_k, top_p, min_p,
+                      need_hidden=need_hidden, need_weight=need_weight)
+    return loss, logprob, ratio, gh, gw
 
 
 def decode_state(state: torch.Tensor) -> dict:

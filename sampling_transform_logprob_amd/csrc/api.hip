@@ -435,6 +435,28 @@ stce_status stce_decode_state(const void* host_state, int64_t nrows, stce_row_in
   return STCE_OK;
 }
 
+stce_status stce_policy_loss(const stce_pg_params* pg, int64_t T, const float* logprob, float* loss,
+                             float* grad_logprob, float* ratio, void* stream) {
+  if (!pg) return fail(STCE_E_ARG, "pg parameters are NULL");
+  if (pg->objective != STCE_PG_CISPO && pg->objective != STCE_PG_CLIP)
+    return fail(STCE_E_ARG, "objective=%d: expected STCE_PG_CISPO (1) or STCE_PG_CLIP (2)", (int)pg->objective);
+  if (!(pg->eps_low >= 0.0f && pg->eps_low < 1.0f))
+    return fail(STCE_E_ARG, "eps_low=%g outside [0, 1)", (double)pg->eps_low);
+  if (!(pg->eps_high >= 0.0f && __builtin_isfinite(pg->eps_high)))
+    return fail(STCE_E_ARG, "eps_high=%g must be finite and >= 0", (double)pg->eps_high);
+  if (!__builtin_isfinite(pg->scale)) return fail(STCE_E_ARG, "scale must be finite");
+  if (T < 1 || T > INT32_MAX - 512) return fail(STCE_E_ARG, "T=%lld out of range", (long long)T);
+  if (!pg->advantages || !pg->old_logprob || !logprob || !loss || !grad_logprob)
+    return fail(STCE_E_ARG, "advantages, old_logprob, logprob, loss and grad_logprob are required");
+  if (!aligned(pg->advantages, 4) || !aligned(pg->old_logprob, 4) || !aligned(logprob, 4) || !aligned(loss, 4) ||
+      !aligned(grad_logprob, 4) || (ratio && !aligned(ratio, 4)))
+    return fail(STCE_E_ARG, "arrays must be 4-byte aligned");
+  hipError_t e = launch_policy_loss(pg->objective, pg->eps_low, pg->eps_high, pg->scale, pg->advantages,
+                                    pg->old_logprob, T, logprob, loss, grad_logprob, ratio, (hipStream_t)stream);
+  if (e) return hip_fail(e, "policy loss");
+  return STCE_OK;
+}
+
 const char* stce_status_string(stce_status status) {
   switch (status) {
     case STCE_OK: return "STCE_OK";

@@ -30,6 +30,41 @@ __global__ void validate_kernel(int64_t T, int64_t V, const float* temp, const i
 
 __global__ void fill_i64_kernel(int64_t* p, int64_t v) { *p = v; }
 
+// One thread per row.  The loss sign: CISPO's token loss is
+// -A sg(min(r, 1 + eh)) lp, the clipped surrogate's -min(r A, clip(r) A);
+// grad is d loss / d lp with the CISPO weight held constant.
+__global__ void policy_loss_kernel(int objective, float el, float eh, float scale, const float* adv,
+                                   const float* old_lp, int64_t T, const float* lp, float* loss,
+                                   float* grad, float* ratio) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const float x = lp[t];
+  float l = 0.f, g = 0.f, r = 0.f;
+  if (x != x) {
+    l = x;  // invalid row: NaN loss, no gradient
+  } else if (x != -__builtin_huge_valf()) {
+    const float a = adv[t];
+    r = expf(x - old_lp[t]);
+    if (objective == 1) {
+      const float w = fminf(r, 1.0f + eh);
+      l = -a * w * x;
+      g = -a * w;
+    } else {
+      const float unclipped = r * a;
+      const float clipped = fminf(fmaxf(r, 1.0f - el), 1.0f + eh) * a;
+      if (unclipped <= clipped) {
+        l = -unclipped;
+        g = -a * r;
+      } else {
+        l = -clipped;
+      }
+    }
+  }
+  loss[t] = l * scale;
+  grad[t] = g * scale;
+  if (ratio) ratio[t] = r;
+}
+
 template <class T>
 __global__ void transpose_kernel(const T* in, int64_t ld_in, int64_t R, int64_t Cc, T* out, int64_t ld_out,
                                  int64_t R_pad) {
@@ -113,6 +148,15 @@ hipError_t launch_validate(int64_t T, int64_t V, const float* temp, const int32_
   ProfScope ps(1, s);
   hipLaunchKernelGGL(validate_kernel, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, s, T, V, temp, top_k,
                      top_p, min_p, target, flags, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_policy_loss(int objective, float eps_low, float eps_high, float scale, const float* adv,
+                              const float* old_lp, int64_t T, const float* lp, float* loss, float* grad,
+                              float* ratio, hipStream_t s) {
+  ProfScope ps(9, s);
+  hipLaunchKernelGGL(policy_loss_kernel, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, s, objective, eps_low,
+                     eps_high, scale, adv, old_lp, T, lp, loss, grad, ratio);
   return hipGetLastError();
 }
 

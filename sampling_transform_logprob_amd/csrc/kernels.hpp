@@ -51,6 +51,11 @@ struct FwdArgs {
 };
 hipError_t launch_fwd_projection(const FwdArgs& a, hipStream_t s);
 
+// Per-row policy-gradient loss: objective 1 = CISPO, 2 = clipped surrogate.
+hipError_t launch_policy_loss(int objective, float eps_low, float eps_high, float scale, const float* adv,
+                              const float* old_lp, int64_t T, const float* lp, float* loss, float* grad,
+                              float* ratio, hipStream_t s);
+
 // One vocabulary slice of the backward.
 struct BwdSliceArgs {
   int dtype;

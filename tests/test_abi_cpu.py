@@ -107,3 +107,24 @@ def test_decode_state_roundtrip(lib):
     torch = pytest.importorskip("torch")
     d = binding.decode_state(torch.from_numpy(raw.view(np.uint8).copy()))
     assert list(d["id_thr"]) == [5, 6, 7] and list(d["n"]) == [1, 2, 3]
+
+
+def test_policy_loss_rejects_bad_parameters_before_launch(lib):
+    fake = ctypes.c_void_p(16)
+    good = dict(objective=1, eps_low=0.2, eps_high=0.28, scale=1.0, advantages=16, old_logprob=16)
+
+    def call(T=4, **kw):
+        d = dict(good)
+        d.update(kw)
+        pg = binding.PgParams(**d)
+        return lib.stce_policy_loss(ctypes.byref(pg), T, fake, fake, fake, None, None)
+
+    for kw, msg in ((dict(objective=3), b"objective"), (dict(eps_low=1.0), b"eps_low"),
+                    (dict(eps_low=-0.1), b"eps_low"), (dict(eps_high=-1.0), b"eps_high"),
+                    (dict(eps_high=float("inf")), b"eps_high"), (dict(scale=float("nan")), b"scale"),
+                    (dict(advantages=None), b"required"), (dict(old_logprob=18), b"aligned")):
+        assert call(**kw) == 1, kw
+        assert msg in lib.stce_last_error(), (kw, lib.stce_last_error())
+    assert call(T=0) == 1 and b"T=0" in lib.stce_last_error()
+    assert lib.stce_policy_loss(None, 4, fake, fake, fake, None, None) == 1
+    assert ctypes.sizeof(binding.PgParams) == 32
