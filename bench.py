@@ -318,15 +318,19 @@ def main():
     log(f"[bench] timing {args.steps} steps")
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     L.stce_profile_attach(ctypes.byref(prof))
     torch.cuda.synchronize()
     t_start.record()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        marks[i].record()
         step()
+    marks[args.steps].record()
     t_end.record()
     torch.cuda.synchronize()
     L.stce_profile_attach(None)
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
 
     # per-kind launch statistics from the events recorded around each launch
     kinds = {}
@@ -361,6 +365,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_median": float(np.median(per_step)),
+        "ms_per_step_min": float(per_step.min()),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
