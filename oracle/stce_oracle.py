@@ -234,7 +234,12 @@ def forward(h, W, target, temperature=None, top_k=None, top_p=None, min_p=None,
 
     Returns per selected row: ``logprob`` (fp64, -inf out of support),
     ``lse`` (log-sum-exp of z/T over the support), ``n``, ``key_thr``,
-    ``id_thr``, ``in_support``, ``near``, and the keys used.
+    ``id_thr``, ``in_support``, ``near``, and the keys used; and the side
+    outputs of one sweep ([align-v2] 5.4 A: "entropy from the same sweep"):
+    ``lse_full`` (log-sum-exp of z/T over the whole row), ``entropy_full``
+    (Shannon entropy, in nats, of softmax(z/T) over the whole row) and
+    ``entropy_support`` (entropy of the filtered distribution q on the
+    support), each ``-sum p log p`` written out term by term.
     """
     h = np.asarray(h)
     T = h.shape[0]
@@ -251,7 +256,7 @@ def forward(h, W, target, temperature=None, top_k=None, top_p=None, min_p=None,
     out = dict(logprob=np.empty(R), lse=np.empty(R), n=np.empty(R, np.int64),
                key_thr=np.empty(R, np.uint32), id_thr=np.empty(R, np.int64),
                in_support=np.empty(R, bool), near=np.empty(R, bool), keys=s32,
-               rows=rows)
+               rows=rows, lse_full=np.empty(R), entropy_full=np.empty(R), entropy_support=np.empty(R))
     for i, t in enumerate(rows):
         d = support_row(s32[i], tk[t], tp[t], mp[t])
         S = d["pi"][: d["n"]]
@@ -266,7 +271,17 @@ def forward(h, W, target, temperature=None, top_k=None, top_p=None, min_p=None,
         out["id_thr"][i] = d["id_thr"]
         out["in_support"][i] = inside
         out["near"][i] = d["near"]
+        out["lse_full"][i], out["entropy_full"][i] = _entropy(u[i])
+        out["entropy_support"][i] = _entropy(u[i, S])[1]
     return out
+
+
+def _entropy(x) -> tuple:
+    """(log-sum-exp, -sum_j p_j log p_j) of the distribution softmax(x)."""
+    mx = x.max()
+    lse = mx + math.log(np.exp(x - mx).sum())
+    logp = x - lse
+    return lse, float(-(np.exp(logp) * logp).sum())
 
 
 def dlogits(h, W, target, fwd: dict, grad_logprob, temperature=None) -> np.ndarray:

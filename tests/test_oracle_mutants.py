@@ -48,6 +48,12 @@ MUTANTS = {
     "clipped surrogate takes the max": ("            if unclipped <= clipped:", "            if unclipped >= clipped:",
                                         ["test_policy_loss_special_cases",
                                          "test_clipped_policy_gradient_matches_central_differences"]),
+    "support entropy over the full row": ('        out["entropy_support"][i] = _entropy(u[i, S])[1]',
+                                          '        out["entropy_support"][i] = _entropy(u[i])[1]',
+                                          ["test_entropy_closed_forms", "test_entropy_matches_scipy_and_bounds"]),
+    "entropy with a plus sign": ("    return lse, float(-(np.exp(logp) * logp).sum())",
+                                 "    return lse, float((np.exp(logp) * logp).sum())",
+                                 ["test_entropy_closed_forms", "test_entropy_matches_scipy_and_bounds"]),
     "policy gradient in the objective's sign": ("    return dict(loss=loss * sc, g=g * sc, ratio=ratio)",
                                                 "    return dict(loss=loss * sc, g=-g * sc, ratio=ratio)",
                                                 ["test_policy_gradient_matches_autograd_of_objective",

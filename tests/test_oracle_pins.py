@@ -517,3 +517,41 @@ def test_clipped_policy_gradient_matches_central_differences(rng):
             num[idx] = (fp - fm) / (2 * eps)
         rel = np.linalg.norm(num - grad) / np.linalg.norm(grad)
         assert rel < 1e-6, rel
+
+
+# ---------------------------------------------------------------- side outputs: entropies, full LSE
+def test_entropy_closed_forms():
+    # all-equal logits: log V over the row; top-k 7 keeps 7 tokens (ties split by id): log 7
+    V = 50
+    h = np.ones((1, 1), np.float32)
+    W = np.zeros((V, 1), np.float32)
+    f = oracle.forward(h, W, np.array([0]), top_k=np.array([7]))
+    assert abs(f["entropy_full"][0] - math.log(V)) < 1e-13
+    assert abs(f["entropy_support"][0] - math.log(7)) < 1e-13
+    assert abs(f["lse_full"][0] - math.log(V)) < 1e-13
+    # top-k 1: a one-token support has zero entropy
+    W = np.arange(V, dtype=np.float32)[:, None] * 0.1
+    f = oracle.forward(h, W, np.array([V - 1]), top_k=np.array([1]))
+    assert f["entropy_support"][0] == 0.0
+    # two tokens a bit apart, temperature 0.5: binary entropy of sigmoid(2 d)
+    W = np.array([[1.0], [0.25], [-3.0]], np.float32)
+    f = oracle.forward(h, W, np.array([0]), np.array([0.5], np.float32), top_k=np.array([2]))
+    q = 1.0 / (1.0 + math.exp(-2 * 0.75))
+    assert abs(f["entropy_support"][0] - (-q * math.log(q) - (1 - q) * math.log(1 - q))) < 1e-13
+
+
+def test_entropy_matches_scipy_and_bounds(rng):
+    from scipy.special import softmax
+    from scipy.stats import entropy
+    h, W, temp = _problem(rng, T=8, V=60, scale=3)
+    meta = dict(top_k=rng.choice([0, 5, 20], 8), top_p=rng.choice([1.0, 0.6], 8).astype(np.float32),
+                min_p=rng.choice([0.0, 0.1], 8).astype(np.float32))
+    f = oracle.forward(h, W, np.zeros(8, np.int64), temp, **meta)
+    u = (h.astype(np.float64) @ W.astype(np.float64).T) / temp.astype(np.float64)[:, None]
+    for t in range(8):
+        S = oracle.order_row(f["keys"][t])[: f["n"][t]]
+        assert abs(f["entropy_full"][t] - entropy(softmax(u[t]))) < 1e-12
+        assert abs(f["entropy_support"][t] - entropy(softmax(u[t, S]))) < 1e-12
+        assert -1e-15 <= f["entropy_support"][t] <= math.log(f["n"][t]) + 1e-12
+        assert f["entropy_full"][t] <= math.log(60) + 1e-12
+        assert abs(f["lse_full"][t] - (u[t].max() + math.log(np.exp(u[t] - u[t].max()).sum()))) < 1e-12
