@@ -235,6 +235,8 @@ def main():
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write the HBM traffic summary of --traffic-kernel from rocprofv3 --pmc outputs and exit")
     ap.add_argument("--traffic-kernel", default="dlogits")
+    ap.add_argument("--side-outputs", action="store_true",
+                    help="forward with the sweep's side outputs (full LSE, full and support entropy)")
     ap.add_argument("--policy-loss", choices=["none", "cispo", "clip"], default="none",
                     help="time the fused policy-gradient step instead: forward, per-token loss (advantages "
                          "and behaviour logprobs synthetic), backward of the summed loss")
@@ -294,9 +296,19 @@ def main():
         pg = binding.PgParams(binding.PG_OBJECTIVES[args.policy_loss], 0.2, 0.28, 1.0 / T, adv.data_ptr(),
                               old_lp.data_ptr())
 
+    side = None
+    if args.side_outputs:
+        side_t = [torch.empty(T, dtype=torch.float32, device=dev) for _ in range(3)]
+        side = binding.SideOutputs(*(t.data_ptr() for t in side_t))
+
     def step():
-        binding._check(L.stce_forward(P, ctypes.c_void_p(logprob.data_ptr()), ctypes.c_void_p(state.data_ptr()),
-                                      None, ctypes.c_void_p(ws_f.data_ptr()), fwd_b, stream))
+        if side is not None:
+            binding._check(L.stce_forward_with_side(P, ctypes.c_void_p(logprob.data_ptr()),
+                                                    ctypes.c_void_p(state.data_ptr()), ctypes.byref(side), None,
+                                                    ctypes.c_void_p(ws_f.data_ptr()), fwd_b, stream))
+        else:
+            binding._check(L.stce_forward(P, ctypes.c_void_p(logprob.data_ptr()), ctypes.c_void_p(state.data_ptr()),
+                                          None, ctypes.c_void_p(ws_f.data_ptr()), fwd_b, stream))
         if pg is not None:
             binding._check(L.stce_policy_loss(ctypes.byref(pg), T, ctypes.c_void_p(logprob.data_ptr()),
                                               ctypes.c_void_p(loss_t.data_ptr()), ctypes.c_void_p(g.data_ptr()),
@@ -378,7 +390,8 @@ def main():
                                f"{int(w['top_k'].max())}, top_p {float(w['top_p'].min())}, min_p "
                                f"{float(w['min_p'].max())}; forward + backward (grad_hidden, grad_weight)"
                                + ("" if args.policy_loss == "none" else
-                                  f" of the {args.policy_loss} policy-gradient token loss"),
+                                  f" of the {args.policy_loss} policy-gradient token loss")
+                               + ("; forward side outputs (full LSE, entropies)" if args.side_outputs else ""),
                    "T": T, "H": H, "V": V, "chunk_rows": C, "vocab_slice": Vs},
         "mfma_peak_frac": flop_step / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "tflops_8thv": flop_step / (ms_step * 1e-3) / 1e12,

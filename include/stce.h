@@ -132,6 +132,29 @@ stce_status stce_schedule(const stce_problem *prob, int64_t *chunk_rows, int64_t
 stce_status stce_forward(const stce_problem *prob, float *logprob, void *state,
                          int64_t *dev_status, void *ws, size_t ws_bytes, void *stream);
 
+/* Forward with side outputs of the same sweep (align "architecture v2:
+ * proposal", section 5.4 A: the entropy comes from the forward's sweep, no
+ * extra product).  Each pointer of `side` is a device array [T] fp32, or
+ * NULL to skip it (`side` itself may be NULL: then this is stce_forward):
+ *   lse_full[t]        = logsumexp_j s[t, j] over the whole row,
+ *   entropy_full[t]    = -sum_j p_j log p_j, p = softmax(s[t, :]),
+ *   entropy_support[t] = -sum_{j in S_t} q_j log q_j, q the filtered
+ *                        distribution (softmax of s on the support),
+ * in nats, on the fp32 keys s; rows with invalid metadata get NaN.  The
+ * full-row entropy comes from per-tile sums of e^(s - max) (s - max) that
+ * the projection epilogue forms only when an entropy is requested (fp32
+ * sums, fp64 combination); the support entropy is summed over the sorted
+ * selection window when the support starts at the top of the order, else
+ * in one more pass over the row.  Same workspace as stce_forward. */
+typedef struct stce_side_outputs {
+  float *lse_full;
+  float *entropy_full;
+  float *entropy_support;
+} stce_side_outputs;
+stce_status stce_forward_with_side(const stce_problem *prob, float *logprob, void *state,
+                                   const stce_side_outputs *side, int64_t *dev_status, void *ws,
+                                   size_t ws_bytes, void *stream);
+
 /* Backward of sum_t grad_logprob[t] * logprob[t].  Recomputes the logits of
  * every vocabulary slice bit-for-bit as the forward did, reads the support
  * from `state`, forms dz = g (1[j == y] - q) / T (zero on rows whose target

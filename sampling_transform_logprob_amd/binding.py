@@ -27,7 +27,7 @@ SYMBOLS = (
     "stce_state_bytes", "stce_workspace_bytes", "stce_forward", "stce_backward",
     "stce_scaled_logits", "stce_support_from_logits", "stce_support_workspace_bytes",
     "stce_decode_state", "stce_status_string", "stce_last_error", "stce_profile_attach", "stce_schedule",
-    "stce_policy_loss",
+    "stce_policy_loss", "stce_forward_with_side",
 )
 KERNEL_KINDS = {1: "validate", 2: "projection", 3: "select", 4: "dlogits", 5: "grad_weight",
                 6: "grad_hidden", 7: "transpose", 8: "partials", 9: "policy_loss"}
@@ -65,6 +65,11 @@ class PgParams(ctypes.Structure):
     ]
 
 
+class SideOutputs(ctypes.Structure):
+    _fields_ = [("lse_full", ctypes.c_void_p), ("entropy_full", ctypes.c_void_p),
+                ("entropy_support", ctypes.c_void_p)]
+
+
 class StceError(RuntimeError):
     pass
 
@@ -95,6 +100,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "stce_profile_attach": (ctypes.c_int, [ctypes.POINTER(Profile)]),
         "stce_schedule": (ctypes.c_int, [P, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
         "stce_policy_loss": (ctypes.c_int, [ctypes.POINTER(PgParams), i64, vp, vp, vp, vp, vp]),
+        "stce_forward_with_side": (ctypes.c_int, [P, vp, vp, ctypes.POINTER(SideOutputs), vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -188,8 +194,13 @@ def _raise_rows(status: torch.Tensor, what: str, tensors: dict) -> None:
 
 
 def forward(hidden, weight, target, temperature=None, top_k=None, top_p=None, min_p=None, *,
-            chunk_rows: int = 0, check: bool = True, workspace: Optional[torch.Tensor] = None):
-    """Selected logprob per row and the 32-byte-per-row state for backward."""
+            chunk_rows: int = 0, check: bool = True, workspace: Optional[torch.Tensor] = None,
+            side: bool = False):
+    """Selected logprob per row and the 32-byte-per-row state for backward.
+
+    With ``side=True`` also returns a dict of the sweep's side outputs
+    (``lse_full``, ``entropy_full``, ``entropy_support``, fp32 [T]).
+    """
     prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, chunk_rows)
     T = prob.T
     fwd_b, _ = workspace_bytes(prob)
@@ -198,12 +209,20 @@ def forward(hidden, weight, target, temperature=None, top_k=None, top_p=None, mi
     logprob = torch.empty(T, dtype=torch.float32, device=dev)
     state = torch.empty(T * STATE_BYTES_PER_ROW, dtype=torch.uint8, device=dev)
     status = torch.empty(1, dtype=torch.int64, device=dev)
-    _check(load().stce_forward(ctypes.byref(prob), _ptr(logprob), _ptr(state), _ptr(status), _ptr(ws),
-                               ws.numel(), _stream()))
+    outs = None
+    if side:
+        outs = {k: torch.empty(T, dtype=torch.float32, device=dev)
+                for k in ("lse_full", "entropy_full", "entropy_support")}
+        so = SideOutputs(*(outs[k].data_ptr() for k in ("lse_full", "entropy_full", "entropy_support")))
+        _check(load().stce_forward_with_side(ctypes.byref(prob), _ptr(logprob), _ptr(state), ctypes.byref(so),
+                                             _ptr(status), _ptr(ws), ws.numel(), _stream()))
+    else:
+        _check(load().stce_forward(ctypes.byref(prob), _ptr(logprob), _ptr(state), _ptr(status), _ptr(ws),
+                                   ws.numel(), _stream()))
     if check:
         _raise_rows(status, "stce_forward", dict(temperature=keep[3], top_k=keep[4], top_p=keep[5],
                                                  min_p=keep[6], target=keep[2]))
-    return logprob, state
+    return (logprob, state, outs) if side else (logprob, state)
 
 
 def backward(hidden, weight, target, state, grad_logprob, temperature=None, top_k=None, top_p=None,

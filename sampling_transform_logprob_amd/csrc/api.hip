@@ -215,10 +215,22 @@ stce_status stce_schedule(const stce_problem* prob, int64_t* chunk_rows, int64_t
 
 stce_status stce_forward(const stce_problem* p, float* logprob, void* state, int64_t* dev_status, void* ws,
                          size_t ws_bytes, void* stream) {
+  return stce_forward_with_side(p, logprob, state, nullptr, dev_status, ws, ws_bytes, stream);
+}
+
+stce_status stce_forward_with_side(const stce_problem* p, float* logprob, void* state,
+                                   const stce_side_outputs* side_out, int64_t* dev_status, void* ws,
+                                   size_t ws_bytes, void* stream) {
   stce_status s = check_shapes(p);
   if (s) return s;
   if ((s = check_inputs(p))) return s;
   if (!logprob || !state) return fail(STCE_E_ARG, "logprob and state are required");
+  float* so_lse = side_out ? side_out->lse_full : nullptr;
+  float* so_hf = side_out ? side_out->entropy_full : nullptr;
+  float* so_hs = side_out ? side_out->entropy_support : nullptr;
+  if ((so_lse && !aligned(so_lse, 4)) || (so_hf && !aligned(so_hf, 4)) || (so_hs && !aligned(so_hs, 4)))
+    return fail(STCE_E_ARG, "side outputs must be 4-byte aligned");
+  const int want_ent = (so_hf || so_hs) ? 1 : 0;
   const Layout L = plan(p);
   if ((s = check_ws(ws, ws_bytes, L.fwd))) return s;
   hipStream_t st = (hipStream_t)stream;
@@ -254,6 +266,7 @@ stce_status stce_forward(const stce_problem* p, float* logprob, void* state, int
     a.part = at<TilePart>(ws, L.f_part + b * L.buf_part);
     a.ntv = (int)L.ntv;
     a.s_y = at<float>(ws, L.f_sy + b * L.buf_sy);
+    a.want_ent = want_ent;
     if ((e = launch_fwd_projection(a, st))) return hip_fail(e, "projection");
     hipStream_t ss = st;
     if (side) {
@@ -275,6 +288,9 @@ stce_status stce_forward(const stce_problem* p, float* logprob, void* state, int
     sp.logprob = logprob + c0;
     sp.state = (RowState*)state + c0;
     sp.V = (int)p->V;
+    sp.lse_full = so_lse ? so_lse + c0 : nullptr;
+    sp.ent_full = so_hf ? so_hf + c0 : nullptr;
+    sp.ent_supp = so_hs ? so_hs + c0 : nullptr;
     launch_select(sp, (int)nc, ss);
     if ((e = hipGetLastError())) return hip_fail(e, "select");
     if (side && (e = hipEventRecord(side->ev[2 * c + 1], ss))) return hip_fail(e, "selection event");

@@ -34,12 +34,14 @@ struct RowState {
 static_assert(sizeof(RowState) == 32, "row state must be 32 bytes");
 
 // Partial statistics of one (row, 256-wide vocabulary tile) block, written by
-// the projection epilogue: tile maximum, sum of exp(s - tile max), tile minimum.
+// the projection epilogue: tile maximum, sum of exp(s - tile max), tile
+// minimum, and (when entropies are requested, else 0) the sum of
+// exp(s - tile max) * (s - tile max).
 struct TilePart {
   float mx;
   float sum;
   float mn;
-  float pad;
+  float ent;
 };
 
 constexpr int VTILE = 256;  // vocabulary columns per partial

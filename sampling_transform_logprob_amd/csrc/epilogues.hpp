@@ -7,12 +7,20 @@ namespace stce {
 
 #define STCE_INF __builtin_huge_valf()
 
-// (max, sum of exp(x - max)) merge; max = -inf means "empty".
-__device__ inline void lse_merge(float& mx, float& sm, float omx, float osm) {
+// Merge of two (max, sum of exp(x - max), sum of exp(x - max) (x - max))
+// partials; max = -inf means "empty".  Re-based on the new maximum M, a
+// part's entropy sum gains (max - M) times its mass; an empty part adds
+// nothing.
+__device__ inline void lse_ent_merge(float& mx, float& sm, float& en, float omx, float osm, float oen) {
   const float M = fmaxf(mx, omx);
   if (M == -STCE_INF) {
     sm = 0.f;
+    en = 0.f;
   } else {
+    float e = 0.f;
+    if (mx != -STCE_INF) e += (en + (mx - M) * sm) * __expf(mx - M);
+    if (omx != -STCE_INF) e += (oen + (omx - M) * osm) * __expf(omx - M);
+    en = e;
     sm = sm * __expf(mx - M) + osm * __expf(omx - M);
   }
   mx = M;
@@ -78,14 +86,15 @@ struct EpiLogits {
   float* s_y;              // [N] or null
   int V;                   // valid vocabulary rows
   int N;                   // valid tokens
-  static constexpr int LDS_BYTES = 2 * GN * 3 * 4;  // cross-wave merge
+  int want_ent;            // store the per-tile sum of exp(s - max) (s - max)
+  static constexpr int LDS_BYTES = 2 * GN * 4 * 4;  // cross-wave merge
 
   __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
     const int mb = m0 + wm * 128;
     const bool full = m0 + GM <= V;
-    float pmx[ACC_J], psm[ACC_J], pmn[ACC_J];
+    float pmx[ACC_J], psm[ACC_J], pmn[ACC_J], pen[ACC_J];
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) {
       const int n = n0 + acc_col(wn, j, col);
@@ -144,44 +153,45 @@ struct EpiLogits {
           }
         }
       }
-      float sm = 0.f;
+      // the tile's mass and its entropy sum, formed the same way whether or
+      // not the entropy is stored, so the mass (and every decision and
+      // logprob that uses it) does not depend on the request
+      float sm = 0.f, en = 0.f;
       if (mx != -STCE_INF) {
         const float nmx = -mx * LOG2E;
-        if (full) {
 #pragma unroll
-          for (int i = 0; i < ACC_I; ++i)
+        for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-            for (int r = 0; r < ACC_R; ++r) sm += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][r], LOG2E, nmx));
-        } else {
-#pragma unroll
-          for (int i = 0; i < ACC_I; ++i)
-#pragma unroll
-            for (int r = 0; r < ACC_R; ++r)
-              if (m0 + acc_row(wm, i, r, quad) < V)
-                sm += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][r], LOG2E, nmx));
-        }
+          for (int r = 0; r < ACC_R; ++r)
+            if (full || m0 + acc_row(wm, i, r, quad) < V) {
+              const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][r], LOG2E, nmx));
+              sm += e;
+              en = __builtin_fmaf(e, acc[i][j][r] - mx, en);
+            }
       }
       // merge the four lanes that hold this column (quads 0..3)
 #pragma unroll
       for (int o = 16; o <= 32; o <<= 1) {
-        const float omx = __shfl_xor(mx, o), osm = __shfl_xor(sm, o), omn = __shfl_xor(mn, o);
-        lse_merge(mx, sm, omx, osm);
+        const float omx = __shfl_xor(mx, o), osm = __shfl_xor(sm, o), omn = __shfl_xor(mn, o), oen = __shfl_xor(en, o);
+        lse_ent_merge(mx, sm, en, omx, osm, oen);
         mn = fminf(mn, omn);
       }
       pmx[j] = mx;
       psm[j] = sm;
       pmn[j] = mn;
+      pen[j] = en;
     }
     // merge the two waves that share these tokens (wm = 0 and 1)
     __syncthreads();
-    float* red = (float*)smem;  // [2][256][3]
+    float* red = (float*)smem;  // [2][256][4]
     if (quad == 0) {
 #pragma unroll
       for (int j = 0; j < ACC_J; ++j) {
         const int tok = acc_col(wn, j, col);
-        red[(wm * 256 + tok) * 3 + 0] = pmx[j];
-        red[(wm * 256 + tok) * 3 + 1] = psm[j];
-        red[(wm * 256 + tok) * 3 + 2] = pmn[j];
+        red[(wm * 256 + tok) * 4 + 0] = pmx[j];
+        red[(wm * 256 + tok) * 4 + 1] = psm[j];
+        red[(wm * 256 + tok) * 4 + 2] = pmn[j];
+        red[(wm * 256 + tok) * 4 + 3] = pen[j];
       }
     }
     __syncthreads();
@@ -191,13 +201,13 @@ struct EpiLogits {
         const int tok = acc_col(wn, j, col);
         const int n = n0 + tok;
         if (n < N) {
-          float mx = red[tok * 3 + 0], sm = red[tok * 3 + 1];
-          lse_merge(mx, sm, red[(256 + tok) * 3 + 0], red[(256 + tok) * 3 + 1]);
+          float mx = red[tok * 4 + 0], sm = red[tok * 4 + 1], en = red[tok * 4 + 3];
+          lse_ent_merge(mx, sm, en, red[(256 + tok) * 4 + 0], red[(256 + tok) * 4 + 1], red[(256 + tok) * 4 + 3]);
           TilePart tp;
           tp.mx = mx;
           tp.sum = sm;
-          tp.mn = fminf(red[tok * 3 + 2], red[(256 + tok) * 3 + 2]);
-          tp.pad = 0.f;
+          tp.mn = fminf(red[tok * 4 + 2], red[(256 + tok) * 4 + 2]);
+          tp.ent = want_ent ? en : 0.f;
           part[(int64_t)n * ntv + m0 / VTILE] = tp;
         }
       }

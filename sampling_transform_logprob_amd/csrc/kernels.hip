@@ -110,18 +110,25 @@ __global__ void tile_partials_kernel(const float* s, int64_t ld, int64_t R, int6
     mx = fmaxf(mx, __shfl_xor(mx, o));
     mn = fminf(mn, __shfl_xor(mn, o));
   }
-  float sm = 0.f;
+  float sm = 0.f, en = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    if ((int64_t)t * VTILE + lane + 64 * e < V) sm += __expf(v[e] - mx);
+    if ((int64_t)t * VTILE + lane + 64 * e < V) {
+      const float x = __expf(v[e] - mx);
+      sm += x;
+      en = __builtin_fmaf(x, v[e] - mx, en);
+    }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) sm += __shfl_xor(sm, o);
+  for (int o = 32; o > 0; o >>= 1) {
+    sm += __shfl_xor(sm, o);
+    en += __shfl_xor(en, o);
+  }
   if (lane == 0) {
     TilePart tp;
     tp.mx = mx;
     tp.sum = sm;
     tp.mn = mn;
-    tp.pad = 0.f;
+    tp.ent = en;
     part[row * ntv + t] = tp;
   }
 }
@@ -201,6 +208,7 @@ hipError_t launch_fwd_projection(const FwdArgs& a, hipStream_t s) {
   ep.part = a.part;
   ep.ntv = a.ntv;
   ep.s_y = a.s_y;
+  ep.want_ent = a.want_ent;
   ep.V = (int)a.V;
   ep.N = (int)a.rows;
   const int64_t tm = ceil_div(a.V, GM), tn = ceil_div(a.rows, GN);

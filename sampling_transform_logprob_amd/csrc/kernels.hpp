@@ -48,6 +48,7 @@ struct FwdArgs {
   TilePart* part;
   int ntv;
   float* s_y;
+  int want_ent;  // tile partials carry the entropy sums
 };
 hipError_t launch_fwd_projection(const FwdArgs& a, hipStream_t s);
 

@@ -128,9 +128,13 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
   const uint32_t fl = P.flags[row];
   if (!(fl & ROW_VALID)) {
     if (tid == 0) {
-      P.logprob[row] = __builtin_nanf("");
+      const float nan = __builtin_nanf("");
+      P.logprob[row] = nan;
       RowState rs{};
       P.state[row] = rs;
+      if (P.lse_full) P.lse_full[row] = nan;
+      if (P.ent_full) P.ent_full[row] = nan;
+      if (P.ent_supp) P.ent_supp[row] = nan;
     }
     return;
   }
@@ -147,7 +151,22 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
   const double m64 = (double)m;
   double zs = 0.0;
   for (int t = tid; t < P.ntv; t += ST) zs += (double)pp[t].sum * exp((double)pp[t].mx - m64);
-  const double lse_full = m64 + log(block_reduce(zs, AddD{}, S.sd));
+  const double zfull = block_reduce(zs, AddD{}, S.sd);
+  const double lse_full = m64 + log(zfull);
+  // entropy of softmax(s) over the row from the tiles' sums of
+  // e^(s - mx) (s - mx): sum_j e^(s_j - m) (s_j - m) re-bases each tile on m
+  const bool want_ent = P.ent_full || P.ent_supp;
+  double h_full = 0.0;
+  if (want_ent) {
+    double es = 0.0;
+    for (int t = tid; t < P.ntv; t += ST) {
+      const double d = (double)pp[t].mx - m64;
+      if (pp[t].mx != -F_INF) es += exp(d) * ((double)pp[t].ent + d * (double)pp[t].sum);
+    }
+    h_full = log(zfull) - block_reduce(es, AddD{}, S.sd) / zfull;
+    if (tid == 0 && P.ent_full) P.ent_full[row] = (float)h_full;
+  }
+  if (tid == 0 && P.lse_full) P.lse_full[row] = (float)lse_full;
 
   const float sy = P.s_y[row];
   const int64_t y = P.target[row];
@@ -165,6 +184,7 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
       rs.lse_s = rs.lse_full;
       P.logprob[row] = (float)fmin((double)sy - lse_full, 0.0);
       P.state[row] = rs;
+      if (P.ent_supp) P.ent_supp[row] = (float)h_full;
     }
     return;
   }
@@ -538,6 +558,36 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
     if (np < n_loc) n_loc = np;
   }
   mass_upto(n_loc, &S.mass_s);
+  if (P.ent_supp) {
+    // sum over the support of e^(s - m) (s - m): from the window when the
+    // support starts at the top of the order, else one membership pass
+    double es = 0.0;
+    if (above == 0) {
+      for (int i = lo; i < min(hi, n_loc); ++i) {
+        const double d = (double)key_value(comp_key(S.u.cand[i])) - m64;
+        es += exp(d) * d;
+      }
+    } else {
+      const uint64_t bc = S.u.cand[n_loc - 1];
+      const uint32_t kt = comp_key(bc), it = comp_id(bc);
+      for (int q = tid; q < nv4; q += ST) {
+        const f32x4 x = *(const f32x4*)(rp + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = 4 * q + e;
+          if (v < V) {
+            const uint32_t key = order_key(x[e]);
+            if (key > kt || (key == kt && (uint32_t)v <= it)) {
+              const double d = (double)x[e] - m64;
+              es += exp(d) * d;
+            }
+          }
+        }
+      }
+    }
+    const double E = block_reduce(es, AddD{}, S.sd);
+    if (tid == 0) P.ent_supp[row] = (float)(log(S.mass_s) - E / S.mass_s);
+  }
   if (tid == 0) {
     const uint64_t bc = S.u.cand[n_loc - 1];
     rs.key_thr = comp_key(bc);

@@ -48,6 +48,10 @@ struct SelParams {
   float* logprob;           // [R]
   RowState* state;          // [R]
   int V;
+  // side outputs, each [R] or null; the entropies need the partials' sums
+  float* lse_full;          // log-sum-exp of the keys over the row
+  float* ent_full;          // entropy of softmax(s) over the row
+  float* ent_supp;          // entropy of the filtered distribution on the support
 };
 
 void launch_select(const SelParams& p, int rows, hipStream_t stream);
