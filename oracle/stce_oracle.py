@@ -223,14 +223,18 @@ def _meta(R, top_k, top_p, min_p):
 # forward and backward
 # --------------------------------------------------------------------------
 def forward(h, W, target, temperature=None, top_k=None, top_p=None, min_p=None,
-            keys=None, rows=None) -> dict:
+            keys=None, rows=None, ignore_index=None) -> dict:
     """Selected logprob on the filtered support, per row.
 
     ``h`` [T, H] and ``W`` [V, H] hold the operand values (bf16 or fp32 values,
     any float dtype); ``target`` [T] token ids; metadata per row or None.
     ``keys`` optionally supplies the fp32 keys [len(rows), V] the supports are
     decided on (default: this oracle's own keys).  ``rows`` restricts the
-    computation to a subset of rows (all by default).
+    computation to a subset of rows (all by default).  ``ignore_index``: rows
+    whose target equals it are inactive ([nested-learning]
+    ``compute_teach_signal``: such rows are masked out of the residual):
+    logprob 0 and an exactly zero gradient; their support and side outputs
+    are still computed.
 
     Returns per selected row: ``logprob`` (fp64, -inf out of support),
     ``lse`` (log-sum-exp of z/T over the support), ``n``, ``key_thr``,
@@ -252,18 +256,21 @@ def forward(h, W, target, temperature=None, top_k=None, top_p=None, min_p=None,
     u = z / temp[rows].astype(np.float64)[:, None]            # values: fp64
     R, V = z.shape
     tgt = np.asarray(target, np.int64)[rows]
-    assert np.all((tgt >= 0) & (tgt < V)), "targets must lie in [0, V)"
+    ignored = np.zeros(R, bool) if ignore_index is None else tgt == int(ignore_index)
+    assert ignore_index is None or not (0 <= int(ignore_index) < V), "ignore_index must not be a token id"
+    assert np.all(((tgt >= 0) & (tgt < V)) | ignored), "targets must lie in [0, V)"
     out = dict(logprob=np.empty(R), lse=np.empty(R), n=np.empty(R, np.int64),
                key_thr=np.empty(R, np.uint32), id_thr=np.empty(R, np.int64),
                in_support=np.empty(R, bool), near=np.empty(R, bool), keys=s32,
-               rows=rows, lse_full=np.empty(R), entropy_full=np.empty(R), entropy_support=np.empty(R))
+               rows=rows, lse_full=np.empty(R), entropy_full=np.empty(R), entropy_support=np.empty(R),
+               ignored=ignored)
     for i, t in enumerate(rows):
         d = support_row(s32[i], tk[t], tp[t], mp[t])
         S = d["pi"][: d["n"]]
         mx = u[i, S].max()
         lse = mx + math.log(np.exp(u[i, S] - mx).sum())
-        inside = bool(np.isin(tgt[i], S))
-        lp = min(u[i, tgt[i]] - lse, 0.0) if inside else -math.inf
+        inside = bool(np.isin(tgt[i], S)) and not ignored[i]
+        lp = 0.0 if ignored[i] else (min(u[i, tgt[i]] - lse, 0.0) if inside else -math.inf)
         out["logprob"][i] = lp
         out["lse"][i] = lse
         out["n"][i] = d["n"]

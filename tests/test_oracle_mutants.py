@@ -54,6 +54,8 @@ MUTANTS = {
     "entropy with a plus sign": ("    return lse, float(-(np.exp(logp) * logp).sum())",
                                  "    return lse, float((np.exp(logp) * logp).sum())",
                                  ["test_entropy_closed_forms", "test_entropy_matches_scipy_and_bounds"]),
+    "ignored rows score -inf": ("        lp = 0.0 if ignored[i] else", "        lp = -math.inf if ignored[i] else",
+                                ["test_ignored_rows_score_zero_and_get_no_gradient"]),
     "policy gradient in the objective's sign": ("    return dict(loss=loss * sc, g=g * sc, ratio=ratio)",
                                                 "    return dict(loss=loss * sc, g=-g * sc, ratio=ratio)",
                                                 ["test_policy_gradient_matches_autograd_of_objective",

@@ -555,3 +555,25 @@ def test_entropy_matches_scipy_and_bounds(rng):
         assert -1e-15 <= f["entropy_support"][t] <= math.log(f["n"][t]) + 1e-12
         assert f["entropy_full"][t] <= math.log(60) + 1e-12
         assert abs(f["lse_full"][t] - (u[t].max() + math.log(np.exp(u[t] - u[t].max()).sum()))) < 1e-12
+
+
+# ---------------------------------------------------------------- ignore_index rows
+def test_ignored_rows_score_zero_and_get_no_gradient(rng):
+    h, W, temp = _problem(rng, T=6, V=30, scale=2)
+    y = np.array([3, -100, 7, -100, 0, 11])
+    meta = dict(top_k=np.array([0, 4, 0, 0, 5, 0]), top_p=np.full(6, 0.9, np.float32))
+    f = oracle.forward(h, W, y, temp, **meta, ignore_index=-100)
+    assert list(f["ignored"]) == [False, True, False, True, False, False]
+    assert f["logprob"][1] == 0.0 and f["logprob"][3] == 0.0
+    # the active rows are scored exactly as without the ignored ones
+    act = np.array([0, 2, 4, 5])
+    g = oracle.forward(h, W, y, temp, **meta, rows=act)
+    assert np.array_equal(f["logprob"][act], g["logprob"])
+    # ignored rows still have a support and side outputs
+    assert f["n"][1] == 4 and np.isfinite(f["entropy_support"][[1, 3]]).all()
+    dH, dW = oracle.backward(h, W, y, f, np.ones(6), temp)
+    assert not dH[[1, 3]].any()
+    dH2, dW2 = oracle.backward(h, W, y, g, np.ones(6), temp)
+    np.testing.assert_allclose(dW, dW2, rtol=0, atol=0)          # ignored rows add nothing to dW
+    with pytest.raises(AssertionError):
+        oracle.forward(h, W, y, temp, ignore_index=None)         # -100 is not a token without ignore_index
