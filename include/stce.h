@@ -90,6 +90,9 @@ typedef enum {
 #define STCE_FIELD_MIN_P 4
 #define STCE_FIELD_TARGET 5
 
+/* stce_problem.flags */
+#define STCE_PROBLEM_IGNORE_INDEX 1 /* targets equal to ignore_index mark inactive rows */
+
 /* Bytes of per-row state stce_forward writes and stce_backward reads. */
 #define STCE_STATE_BYTES_PER_ROW 32
 
@@ -98,7 +101,7 @@ typedef struct stce_problem {
   int64_t H;             /* hidden size, >= 8, multiple of 8 */
   int64_t V;             /* vocabulary size, 1 <= V < 2^31 - 256 */
   int32_t dtype;         /* stce_dtype of hidden and weight */
-  int32_t reserved;      /* must be 0 */
+  int32_t flags;         /* 0 or STCE_PROBLEM_IGNORE_INDEX */
   const void *hidden;    /* [T, H], dtype; 16-byte aligned */
   const void *weight;    /* [V, H] (lm_head.weight layout), dtype; 16-byte aligned */
   const int64_t *target; /* [T] sampled token ids in [0, V) */
@@ -108,6 +111,12 @@ typedef struct stce_problem {
   const float *min_p;    /* [T] in [0, 1]; 0 = off; or NULL = off */
   int64_t chunk_rows;    /* forward rows per chunk; 0 = library default */
   int64_t vocab_slice;   /* backward vocabulary columns per slice; 0 = default */
+  int64_t ignore_index;  /* with STCE_PROBLEM_IGNORE_INDEX: a target equal to it
+                            (a value outside [0, V), e.g. -100) marks an inactive
+                            row (nested-learning compute_teach_signal masks such
+                            rows out): logprob 0, exactly zero gradient, no
+                            error; its support and side outputs are still
+                            computed.  Ignored otherwise. */
 } stce_problem;
 
 /* Per-row state size in bytes for T rows (STCE_STATE_BYTES_PER_ROW * T). */
@@ -199,7 +208,8 @@ typedef struct stce_row_info {
   uint32_t key_thr;
   int32_t id_thr;
   int32_t n;
-  uint32_t flags; /* bit 0 valid metadata, bit 1 filtered row, bit 2 target in support */
+  uint32_t flags; /* bit 0 valid metadata, bit 1 filtered row, bit 2 target in support,
+                     bit 3 inactive (ignore_index) row */
   float lse_support;
   float lse_full;
   float row_max;
@@ -264,6 +274,8 @@ typedef struct stce_pg_params {
   float scale;              /* multiplies losses and gradients, e.g. 1 / a constant denominator */
   const float *advantages;  /* [T] */
   const float *old_logprob; /* [T] logprob of the target under the behaviour policy */
+  const void *state;        /* [T * 32] from the forward, or NULL: rows it marks inactive
+                               (ignore_index) get loss 0, gradient 0 and ratio 0 */
 } stce_pg_params;
 stce_status stce_policy_loss(const stce_pg_params *pg, int64_t T, const float *logprob, float *loss,
                              float *grad_logprob, float *ratio, void *stream);

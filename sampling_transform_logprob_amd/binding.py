@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libstce.so")
 
 STATUS_NONE = (1 << 63) - 1
 FIELDS = {1: "temperature", 2: "top_k", 3: "top_p", 4: "min_p", 5: "target"}
-FLAG_VALID, FLAG_FILTERED, FLAG_IN_SUPPORT = 1, 2, 4
+FLAG_VALID, FLAG_FILTERED, FLAG_IN_SUPPORT, FLAG_IGNORED = 1, 2, 4, 8
+PROBLEM_IGNORE_INDEX = 1
 STATE_BYTES_PER_ROW = 32
 DT_BF16, DT_F32 = 1, 2
 
@@ -37,10 +38,11 @@ PG_OBJECTIVES = {"cispo": 1, "clip": 2}
 class Problem(ctypes.Structure):
     _fields_ = [
         ("T", ctypes.c_int64), ("H", ctypes.c_int64), ("V", ctypes.c_int64),
-        ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
         ("hidden", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("target", ctypes.c_void_p),
         ("temperature", ctypes.c_void_p), ("top_k", ctypes.c_void_p), ("top_p", ctypes.c_void_p),
         ("min_p", ctypes.c_void_p), ("chunk_rows", ctypes.c_int64), ("vocab_slice", ctypes.c_int64),
+        ("ignore_index", ctypes.c_int64),
     ]
 
 
@@ -62,6 +64,7 @@ class PgParams(ctypes.Structure):
     _fields_ = [
         ("objective", ctypes.c_int32), ("eps_low", ctypes.c_float), ("eps_high", ctypes.c_float),
         ("scale", ctypes.c_float), ("advantages", ctypes.c_void_p), ("old_logprob", ctypes.c_void_p),
+        ("state", ctypes.c_void_p),
     ]
 
 
@@ -139,7 +142,7 @@ def _meta(name, t, T, dtype, device):
 
 
 def make_problem(hidden, weight, target, temperature=None, top_k=None, top_p=None, min_p=None,
-                 chunk_rows: int = 0, vocab_slice: int = 0):
+                 chunk_rows: int = 0, vocab_slice: int = 0, ignore_index: Optional[int] = None):
     """Checked ``stce_problem`` plus the tensors it points into (kept alive)."""
     if hidden.dim() != 2 or weight.dim() != 2 or hidden.shape[1] != weight.shape[1]:
         raise ValueError(f"hidden [T, H] and weight [V, H] expected, got {tuple(hidden.shape)}, {tuple(weight.shape)}")
@@ -164,8 +167,9 @@ def make_problem(hidden, weight, target, temperature=None, top_k=None, top_p=Non
             _meta("top_k", top_k, T, torch.int32, dev),
             _meta("top_p", top_p, T, torch.float32, dev),
             _meta("min_p", min_p, T, torch.float32, dev)]
-    prob = Problem(T, H, V, dt, 0, *[t.data_ptr() if t is not None else None for t in keep],
-                   chunk_rows, vocab_slice)
+    prob = Problem(T, H, V, dt, 0 if ignore_index is None else PROBLEM_IGNORE_INDEX,
+                   *[t.data_ptr() if t is not None else None for t in keep], chunk_rows, vocab_slice,
+                   0 if ignore_index is None else int(ignore_index))
     return prob, keep
 
 
@@ -195,13 +199,14 @@ def _raise_rows(status: torch.Tensor, what: str, tensors: dict) -> None:
 
 def forward(hidden, weight, target, temperature=None, top_k=None, top_p=None, min_p=None, *,
             chunk_rows: int = 0, check: bool = True, workspace: Optional[torch.Tensor] = None,
-            side: bool = False):
+            side: bool = False, ignore_index: Optional[int] = None):
     """Selected logprob per row and the 32-byte-per-row state for backward.
 
     With ``side=True`` also returns a dict of the sweep's side outputs
     (``lse_full``, ``entropy_full``, ``entropy_support``, fp32 [T]).
     """
-    prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, chunk_rows)
+    prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, chunk_rows,
+                              ignore_index=ignore_index)
     T = prob.T
     fwd_b, _ = workspace_bytes(prob)
     dev = hidden.device
@@ -228,9 +233,10 @@ def forward(hidden, weight, target, temperature=None, top_k=None, top_p=None, mi
 def backward(hidden, weight, target, state, grad_logprob, temperature=None, top_k=None, top_p=None,
              min_p=None, *, need_hidden: bool = True, need_weight: bool = True,
              grad_weight: Optional[torch.Tensor] = None, accumulate_grad_weight: bool = False,
-             vocab_slice: int = 0, workspace: Optional[torch.Tensor] = None):
+             vocab_slice: int = 0, workspace: Optional[torch.Tensor] = None, ignore_index: Optional[int] = None):
     """(grad_hidden [T, H] in hidden's dtype, grad_weight [V, H] fp32)."""
-    prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, 0, vocab_slice)
+    prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, 0, vocab_slice,
+                              ignore_index=ignore_index)
     T, H, V = prob.T, prob.H, prob.V
     dev = hidden.device
     if grad_logprob.shape != (T,) or grad_logprob.dtype != torch.float32 or grad_logprob.device != dev:
@@ -292,7 +298,7 @@ def support_from_logits(s, target, top_k=None, top_p=None, min_p=None, *, check:
 
 
 def policy_loss(logprob, advantages, old_logprob, objective: str = "cispo", eps_low: float = 0.2,
-                eps_high: float = 0.28, scale: float = 1.0):
+                eps_high: float = 0.28, scale: float = 1.0, state: Optional[torch.Tensor] = None):
     """Per-token policy-gradient loss on the selected logprob.
 
     Returns (loss [T], grad_logprob [T], ratio [T]); grad_logprob is the
@@ -312,21 +318,23 @@ def policy_loss(logprob, advantages, old_logprob, objective: str = "cispo", eps_
     loss = torch.empty(T, dtype=torch.float32, device=dev)
     grad = torch.empty(T, dtype=torch.float32, device=dev)
     ratio = torch.empty(T, dtype=torch.float32, device=dev)
-    pg = PgParams(PG_OBJECTIVES[objective], eps_low, eps_high, scale, adv.data_ptr(), old.data_ptr())
+    pg = PgParams(PG_OBJECTIVES[objective], eps_low, eps_high, scale, adv.data_ptr(), old.data_ptr(),
+                  None if state is None else state.data_ptr())
     _check(load().stce_policy_loss(ctypes.byref(pg), T, _ptr(lp), _ptr(loss), _ptr(grad), _ptr(ratio), _stream()))
     return loss, grad, ratio
 
 
 def policy_loss_step(hidden, weight, target, advantages, old_logprob, temperature=None, top_k=None, top_p=None,
                      min_p=None, *, objective: str = "cispo", eps_low: float = 0.2, eps_high: float = 0.28,
-                     scale: float = 1.0, need_hidden: bool = True, need_weight: bool = True):
+                     scale: float = 1.0, need_hidden: bool = True, need_weight: bool = True,
+                     ignore_index: Optional[int] = None):
     """Fused head + policy-gradient token loss: forward, per-token loss and
     the gradients of ``sum(loss)``.  Returns (loss [T], logprob [T], ratio [T],
     grad_hidden, grad_weight)."""
-    logprob, state = forward(hidden, weight, target, temperature, top_k, top_p, min_p)
-    loss, g, ratio = policy_loss(logprob, advantages, old_logprob, objective, eps_low, eps_high, scale)
+    logprob, state = forward(hidden, weight, target, temperature, top_k, top_p, min_p, ignore_index=ignore_index)
+    loss, g, ratio = policy_loss(logprob, advantages, old_logprob, objective, eps_low, eps_high, scale, state)
     gh, gw = backward(hidden, weight, target, state, g, temperature, top_k, top_p, min_p,
-                      need_hidden=need_hidden, need_weight=need_weight)
+                      need_hidden=need_hidden, need_weight=need_weight, ignore_index=ignore_index)
     return loss, logprob, ratio, gh, gw
 
 

@@ -52,7 +52,9 @@ size_t elt_size(int dtype) { return dtype == STCE_DT_BF16 ? 2 : 4; }
 
 stce_status check_shapes(const stce_problem* p) {
   if (!p) return fail(STCE_E_ARG, "problem is NULL");
-  if (p->reserved != 0) return fail(STCE_E_ARG, "problem.reserved must be 0");
+  if (p->flags & ~STCE_PROBLEM_IGNORE_INDEX) return fail(STCE_E_ARG, "problem.flags=%d has unknown bits", (int)p->flags);
+  if ((p->flags & STCE_PROBLEM_IGNORE_INDEX) && p->ignore_index >= 0 && p->ignore_index < p->V)
+    return fail(STCE_E_ARG, "ignore_index=%lld is a token id of [0, V)", (long long)p->ignore_index);
   if (p->dtype != STCE_DT_BF16 && p->dtype != STCE_DT_F32)
     return fail(STCE_E_UNSUPPORTED,
                 "unsupported operand dtype %d: hidden and weight must both be bf16 (STCE_DT_BF16) or fp32 "
@@ -237,7 +239,8 @@ stce_status stce_forward_with_side(const stce_problem* p, float* logprob, void* 
   hipError_t e;
   uint32_t* flags = at<uint32_t>(ws, L.f_flags);
   if (dev_status && (e = launch_fill_i64(dev_status, STCE_STATUS_NONE, st))) return hip_fail(e, "status fill");
-  if ((e = launch_validate(p->T, p->V, p->temperature, p->top_k, p->top_p, p->min_p, p->target, flags, dev_status,
+  if ((e = launch_validate(p->T, p->V, p->flags & STCE_PROBLEM_IGNORE_INDEX, p->ignore_index, p->temperature,
+                           p->top_k, p->top_p, p->min_p, p->target, flags, dev_status,
                            st)))
     return hip_fail(e, "validate");
   const size_t es = elt_size(p->dtype);
@@ -316,7 +319,8 @@ stce_status stce_backward(const stce_problem* p, const float* grad_logprob, cons
   hipError_t e;
   if (dev_status) {
     if ((e = launch_fill_i64(dev_status, STCE_STATUS_NONE, st))) return hip_fail(e, "status fill");
-    if ((e = launch_validate(p->T, p->V, p->temperature, p->top_k, p->top_p, p->min_p, p->target,
+    if ((e = launch_validate(p->T, p->V, p->flags & STCE_PROBLEM_IGNORE_INDEX, p->ignore_index, p->temperature,
+                             p->top_k, p->top_p, p->min_p, p->target,
                              at<uint32_t>(ws, L.b_flags), dev_status, st)))
       return hip_fail(e, "validate");
   }
@@ -422,7 +426,7 @@ stce_status stce_support_from_logits(const float* sk, int64_t R, int64_t V, cons
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
   if (dev_status && (e = launch_fill_i64(dev_status, STCE_STATUS_NONE, st))) return hip_fail(e, "status fill");
-  if ((e = launch_validate(R, V, nullptr, top_k, top_p, min_p, target, flags, dev_status, st)))
+  if ((e = launch_validate(R, V, 0, 0, nullptr, top_k, top_p, min_p, target, flags, dev_status, st)))
     return hip_fail(e, "validate");
   if ((e = launch_tile_partials(sk, V, R, V, (int)ntv, target, part, s_y, st))) return hip_fail(e, "partials");
   SelParams sp{};
@@ -465,10 +469,11 @@ stce_status stce_policy_loss(const stce_pg_params* pg, int64_t T, const float* l
   if (!pg->advantages || !pg->old_logprob || !logprob || !loss || !grad_logprob)
     return fail(STCE_E_ARG, "advantages, old_logprob, logprob, loss and grad_logprob are required");
   if (!aligned(pg->advantages, 4) || !aligned(pg->old_logprob, 4) || !aligned(logprob, 4) || !aligned(loss, 4) ||
-      !aligned(grad_logprob, 4) || (ratio && !aligned(ratio, 4)))
-    return fail(STCE_E_ARG, "arrays must be 4-byte aligned");
+      !aligned(grad_logprob, 4) || (ratio && !aligned(ratio, 4)) || (pg->state && !aligned(pg->state, 16)))
+    return fail(STCE_E_ARG, "arrays must be 4-byte aligned (state 16-byte)");
   hipError_t e = launch_policy_loss(pg->objective, pg->eps_low, pg->eps_high, pg->scale, pg->advantages,
-                                    pg->old_logprob, T, logprob, loss, grad_logprob, ratio, (hipStream_t)stream);
+                                    pg->old_logprob, (const RowState*)pg->state, T, logprob, loss, grad_logprob,
+                                    ratio, (hipStream_t)stream);
   if (e) return hip_fail(e, "policy loss");
   return STCE_OK;
 }

@@ -16,7 +16,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 enum : uint32_t {
   ROW_VALID = 1u,      // metadata passed validation
   ROW_FILTERED = 2u,   // at least one of top-k / top-p / min-p is active
-  ROW_IN_SUPPORT = 4u  // the target lies in the row's support
+  ROW_IN_SUPPORT = 4u, // the target lies in the row's support
+  ROW_IGNORED = 8u     // inactive row (target equals the problem's ignore_index)
 };
 
 // Per-row state written by the forward, read by the backward (32 bytes).

@@ -7,9 +7,9 @@ namespace stce {
 namespace {
 
 // ---------------------------------------------------------------------------
-__global__ void validate_kernel(int64_t T, int64_t V, const float* temp, const int32_t* top_k,
-                                const float* top_p, const float* min_p, const int64_t* target,
-                                uint32_t* flags, int64_t* status) {
+__global__ void validate_kernel(int64_t T, int64_t V, int ignore, int64_t ignore_index, const float* temp,
+                                const int32_t* top_k, const float* top_p, const float* min_p,
+                                const int64_t* target, uint32_t* flags, int64_t* status) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
   const float tt = temp ? temp[t] : 1.0f;
@@ -17,14 +17,15 @@ __global__ void validate_kernel(int64_t T, int64_t V, const float* temp, const i
   const float p = top_p ? top_p[t] : 1.0f;
   const float mp = min_p ? min_p[t] : 0.0f;
   const int64_t y = target[t];
+  const bool ign = ignore && y == ignore_index;
   int field = 0;
   if (!(__builtin_isfinite(tt) && tt > 0.0f)) field = 1;
   else if (k < 0) field = 2;
   else if (!(p > 0.0f && p <= 1.0f)) field = 3;
   else if (!(mp >= 0.0f && mp <= 1.0f)) field = 4;
-  else if (y < 0 || y >= V) field = 5;
+  else if (!ign && (y < 0 || y >= V)) field = 5;
   const bool filtered = (k > 0 && (int64_t)k < V) || p < 1.0f || mp > 0.0f;
-  flags[t] = field ? 0u : (ROW_VALID | (filtered ? ROW_FILTERED : 0u));
+  flags[t] = field ? 0u : (ROW_VALID | (filtered ? ROW_FILTERED : 0u) | (ign ? ROW_IGNORED : 0u));
   if (field && status) atomicMin((unsigned long long*)status, (unsigned long long)((t << 8) | field));
 }
 
@@ -34,13 +35,15 @@ __global__ void fill_i64_kernel(int64_t* p, int64_t v) { *p = v; }
 // -A sg(min(r, 1 + eh)) lp, the clipped surrogate's -min(r A, clip(r) A);
 // grad is d loss / d lp with the CISPO weight held constant.
 __global__ void policy_loss_kernel(int objective, float el, float eh, float scale, const float* adv,
-                                   const float* old_lp, int64_t T, const float* lp, float* loss,
-                                   float* grad, float* ratio) {
+                                   const float* old_lp, const RowState* st, int64_t T, const float* lp,
+                                   float* loss, float* grad, float* ratio) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
   const float x = lp[t];
   float l = 0.f, g = 0.f, r = 0.f;
-  if (x != x) {
+  if (st && (st[t].flags & ROW_IGNORED)) {
+    // inactive row: nothing
+  } else if (x != x) {
     l = x;  // invalid row: NaN loss, no gradient
   } else if (x != -__builtin_huge_valf()) {
     const float a = adv[t];
@@ -149,21 +152,22 @@ hipError_t launch_gemm(const Main& mn, const Epi& ep, int64_t tiles_m, int64_t t
 
 }  // namespace
 
-hipError_t launch_validate(int64_t T, int64_t V, const float* temp, const int32_t* top_k, const float* top_p,
+hipError_t launch_validate(int64_t T, int64_t V, int ignore, int64_t ignore_index, const float* temp,
+                           const int32_t* top_k, const float* top_p,
                            const float* min_p, const int64_t* target, uint32_t* flags, int64_t* status,
                            hipStream_t s) {
   ProfScope ps(1, s);
-  hipLaunchKernelGGL(validate_kernel, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, s, T, V, temp, top_k,
-                     top_p, min_p, target, flags, status);
+  hipLaunchKernelGGL(validate_kernel, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, s, T, V, ignore,
+                     ignore_index, temp, top_k, top_p, min_p, target, flags, status);
   return hipGetLastError();
 }
 
 hipError_t launch_policy_loss(int objective, float eps_low, float eps_high, float scale, const float* adv,
-                              const float* old_lp, int64_t T, const float* lp, float* loss, float* grad,
-                              float* ratio, hipStream_t s) {
+                              const float* old_lp, const RowState* st, int64_t T, const float* lp, float* loss,
+                              float* grad, float* ratio, hipStream_t s) {
   ProfScope ps(9, s);
   hipLaunchKernelGGL(policy_loss_kernel, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, s, objective, eps_low,
-                     eps_high, scale, adv, old_lp, T, lp, loss, grad, ratio);
+                     eps_high, scale, adv, old_lp, st, T, lp, loss, grad, ratio);
   return hipGetLastError();
 }
 

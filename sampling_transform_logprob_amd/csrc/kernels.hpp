@@ -17,7 +17,8 @@ struct ProfScope {
 
 // Per-row metadata validation: flags[t] = ROW_VALID | ROW_FILTERED or 0, and
 // the first bad (row << 8 | field) into *status with an atomic min.
-hipError_t launch_validate(int64_t T, int64_t V, const float* temp, const int32_t* top_k, const float* top_p,
+hipError_t launch_validate(int64_t T, int64_t V, int ignore, int64_t ignore_index, const float* temp,
+                           const int32_t* top_k, const float* top_p,
                            const float* min_p, const int64_t* target, uint32_t* flags, int64_t* status,
                            hipStream_t s);
 hipError_t launch_fill_i64(int64_t* p, int64_t v, hipStream_t s);
@@ -54,8 +55,8 @@ hipError_t launch_fwd_projection(const FwdArgs& a, hipStream_t s);
 
 // Per-row policy-gradient loss: objective 1 = CISPO, 2 = clipped surrogate.
 hipError_t launch_policy_loss(int objective, float eps_low, float eps_high, float scale, const float* adv,
-                              const float* old_lp, int64_t T, const float* lp, float* loss, float* grad,
-                              float* ratio, hipStream_t s);
+                              const float* old_lp, const RowState* st, int64_t T, const float* lp, float* loss,
+                              float* grad, float* ratio, hipStream_t s);
 
 // One vocabulary slice of the backward.
 struct BwdSliceArgs {

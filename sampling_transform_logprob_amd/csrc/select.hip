@@ -182,7 +182,8 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
       rs.n = V;
       rs.flags = ROW_VALID | ROW_IN_SUPPORT;
       rs.lse_s = rs.lse_full;
-      P.logprob[row] = (float)fmin((double)sy - lse_full, 0.0);
+      if (fl & ROW_IGNORED) rs.flags = ROW_VALID | ROW_IGNORED;
+      P.logprob[row] = (fl & ROW_IGNORED) ? 0.0f : (float)fmin((double)sy - lse_full, 0.0);
       P.state[row] = rs;
       if (P.ent_supp) P.ent_supp[row] = (float)h_full;
     }
@@ -596,9 +597,10 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
     const double lse_s = m64 + log(S.mass_s);
     rs.lse_s = (float)lse_s;
     const uint32_t ky = order_key(sy);
-    const bool in = ky > rs.key_thr || (ky == rs.key_thr && y <= (int64_t)rs.id_thr);
-    rs.flags = ROW_VALID | ROW_FILTERED | (in ? ROW_IN_SUPPORT : 0u);
-    P.logprob[row] = in ? (float)fmin((double)sy - lse_s, 0.0) : -F_INF;
+    const bool ign = (fl & ROW_IGNORED) != 0;
+    const bool in = !ign && (ky > rs.key_thr || (ky == rs.key_thr && y <= (int64_t)rs.id_thr));
+    rs.flags = ROW_VALID | ROW_FILTERED | (in ? ROW_IN_SUPPORT : 0u) | (ign ? ROW_IGNORED : 0u);
+    P.logprob[row] = ign ? 0.0f : (in ? (float)fmin((double)sy - lse_s, 0.0) : -F_INF);
     P.state[row] = rs;
   }
 }

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_struct_layouts_match_header():
-    assert ctypes.sizeof(binding.Problem) == 104
+    assert ctypes.sizeof(binding.Problem) == 112
     assert ctypes.sizeof(binding.RowInfo) == binding.STATE_BYTES_PER_ROW
 
 
@@ -65,7 +65,8 @@ def test_unsupported_dtype_is_one_actionable_error(lib):
 
 
 @pytest.mark.parametrize("kw,msg", [
-    (dict(T=0), "T=0"), (dict(H=12), "H=12"), (dict(V=0), "V=0"), (dict(reserved=1), "reserved"),
+    (dict(T=0), "T=0"), (dict(H=12), "H=12"), (dict(V=0), "V=0"), (dict(flags=2), "flags"),
+    (dict(flags=1, ignore_index=5), "ignore_index=5"),
     (dict(chunk_rows=-1), "chunk_rows"),
 ])
 def test_bad_shapes_are_rejected(lib, kw, msg):
@@ -127,4 +128,4 @@ def test_policy_loss_rejects_bad_parameters_before_launch(lib):
         assert msg in lib.stce_last_error(), (kw, lib.stce_last_error())
     assert call(T=0) == 1 and b"T=0" in lib.stce_last_error()
     assert lib.stce_policy_loss(None, 4, fake, fake, fake, None, None) == 1
-    assert ctypes.sizeof(binding.PgParams) == 32
+    assert ctypes.sizeof(binding.PgParams) == 40
