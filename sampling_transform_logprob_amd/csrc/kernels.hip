@@ -85,6 +85,41 @@ __global__ void transpose_kernel(const T* in, int64_t ld_in, int64_t R, int64_t 
   }
 }
 
+// bf16 transpose with 16-byte accesses only: each wave moves one 64 x 64
+// tile; lane (rb, cb) = (lane / 8, lane % 8) loads rows rb*8 .. +8 at columns
+// cb*8 .. +8 (8 lanes cover 128 contiguous bytes of a row), transposes the
+// 8 x 8 block in registers and stores output rows cb*8 + e at columns
+// rb*8 .. +8 (again 128 contiguous bytes per 8 lanes).  Needs Cc, ld_in,
+// ld_out and R_pad multiples of 8, 8, 8 and 64 and 16-byte aligned bases;
+// rows R .. R_pad - 1 of the output columns are zero-filled.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* in, int64_t ld_in, int64_t R, int64_t Cc,
+                                                             bf16* out, int64_t ld_out) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = ((int64_t)blockIdx.y * 4 + w) * 64;
+  if (c0 >= Cc) return;
+  const int rb = lane >> 3, cb = lane & 7;
+  const int64_t c = c0 + cb * 8;
+  if (c >= Cc) return;  // whole 8-column block out of range (Cc % 8 == 0)
+  u32x4 v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t r = r0 + rb * 8 + j;
+    v[j] = r < R ? *(const u32x4*)(in + r * ld_in + c) : u32x4{0u, 0u, 0u, 0u};
+  }
+  // element e of row j is the 16-bit half (e & 1) of word e >> 1 of v[j]
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = (v[2 * k][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+      const uint32_t hi = (v[2 * k + 1][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+      o[k] = lo | (hi << 16);
+    }
+    *(u32x4*)(out + (c + e) * ld_out + r0 + rb * 8) = o;
+  }
+}
+
 // One wave per (row, 256-wide tile).
 __global__ void tile_partials_kernel(const float* s, int64_t ld, int64_t R, int64_t V, int ntv,
                                      const int64_t* target, TilePart* part, float* s_y) {
@@ -179,8 +214,14 @@ hipError_t launch_fill_i64(int64_t* p, int64_t v, hipStream_t s) {
 hipError_t launch_transpose_bf16(const bf16* in, int64_t ld_in, int64_t R, int64_t Cc, bf16* out,
                                  int64_t ld_out, int64_t R_pad, hipStream_t s) {
   ProfScope ps(7, s);
-  hipLaunchKernelGGL(transpose_kernel<bf16>, dim3((unsigned)ceil_div(R_pad, 64), (unsigned)ceil_div(Cc, 64)),
-                     dim3(256), 0, s, in, ld_in, R, Cc, out, ld_out, R_pad);
+  if (Cc % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0 && R_pad % 64 == 0 && (uintptr_t)in % 16 == 0 &&
+      (uintptr_t)out % 16 == 0) {
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(R_pad / 64), (unsigned)ceil_div(Cc, 256)), dim3(256), 0,
+                       s, in, ld_in, R, Cc, out, ld_out);
+  } else {
+    hipLaunchKernelGGL(transpose_kernel<bf16>, dim3((unsigned)ceil_div(R_pad, 64), (unsigned)ceil_div(Cc, 64)),
+                       dim3(256), 0, s, in, ld_in, R, Cc, out, ld_out, R_pad);
+  }
   return hipGetLastError();
 }
 
