@@ -165,3 +165,19 @@ def test_k_bounded_rows_read_only_candidate_tiles():
     p = np.array([1.0, 0.8, 0.999, 1.0] * 4, np.float32)
     mp = np.array([0.0, 0.0, 0.0, 1e-9] * 4, np.float32)
     _check(keys, k, p, mp, hot[:, 0], "candidate tiles")
+
+
+def test_vocabularies_beyond_the_tile_bound_search():
+    """V > 2 * CAP * 256: more tile maxima than the bitwise k-th-largest search
+    handles (its list lives in the window's LDS), so top-k rows fall back to
+    the value histogram (and radix refinement on ties).  Also a vocabulary
+    just below that limit, where the search still runs."""
+    rng = np.random.Generator(np.random.PCG64(29))
+    for V, R in ((2 * 3840 * 256 + 256, 6), (2 * 3840 * 256 - 256, 6)):
+        keys = (rng.standard_normal((R, V)) * rng.uniform(0.5, 3, (R, 1))).astype(np.float32)
+        keys[1] = np.round(keys[1] * 2) / 2                     # heavy ties
+        k = np.array([20, 1000, 64, 0, 5, 3000], np.int32)
+        p = np.array([1.0, 0.9, 1.0, 0.5, 0.99, 1.0], np.float32)
+        mp = np.array([0.0, 0.0, 0.05, 0.0, 0.0, 1e-4], np.float32)
+        y = np.array([int(np.argmax(keys[r])) for r in range(R)])
+        _check(keys, k, p, mp, y, f"V={V}")
