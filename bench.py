@@ -107,11 +107,11 @@ def cpu_baseline(w, y, rows):
 
 
 KERNEL_SYMBOLS = {
-    # kernel kind -> substring of its symbol in counter output
-    "projection": "gemm_kernelINS_8MainBf16ENS_9EpiLogits",
-    "dlogits": "gemm_kernelINS_8MainBf16ENS_10EpiDlogits",
-    "grad_weight": "gemm_kernelINS_8MainBf16ENS_8EpiStore",
-    "grad_hidden": "gemm_kernelINS_8MainBf16ENS_8EpiAccum",
+    # kernel kind -> epilogue name in its (mangled or demangled) symbol; the bf16 main loop
+    "projection": "EpiLogits",
+    "dlogits": "EpiDlogits",
+    "grad_weight": "EpiStore",
+    "grad_hidden": "EpiAccum",
 }
 
 
@@ -147,12 +147,21 @@ def read_traffic(kernel, config):
 
 
 def _counter_rows(path, name_part):
+    """Counter values of the dispatches of one kernel (name_part), or of the
+    plain copies (name_part None), in one rocprofv3 output directory."""
     import csv
     import glob
     out = []
-    for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    assert len(files) == 1, f"expected the output of one run in {path}, found {files}"
+    for f in files:
         for r in csv.DictReader(open(f)):
-            if name_part in r["Kernel_Name"]:
+            if name_part is None:
+                if "copyBuffer" in r["Kernel_Name"]:
+                    out.append(float(r["Counter_Value"]))
+                continue
+            kn = r["Kernel_Name"]
+            if name_part in kn and "gemm_kernel" in kn and "MainBf16" in kn:
                 out.append(float(r["Counter_Value"]))
     return out
 
@@ -165,7 +174,7 @@ def traffic_summary(args):
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic_summary
     kernel, config = args.traffic_kernel, args.config
     sym = KERNEL_SYMBOLS[kernel]
-    copy_sym = "copyBuffer"
+    copy_sym = None
     n_copy = float(1 << 30)
     cf = _counter_rows(cfetch_dir, copy_sym)
     cw = _counter_rows(cwrite_dir, copy_sym)
