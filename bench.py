@@ -249,7 +249,13 @@ def main():
     ap.add_argument("--policy-loss", choices=["none", "cispo", "clip"], default="none",
                     help="time the fused policy-gradient step instead: forward, per-token loss (advantages "
                          "and behaviour logprobs synthetic), backward of the summed loss")
+    ap.add_argument("--fused", action="store_true",
+                    help="with --policy-loss: the fused step (dlogits formed in the forward's sweep from the "
+                         "chunk's keys, 3 products instead of 4)")
     args = ap.parse_args()
+    if args.fused and args.policy_loss == "none":
+        print("--fused needs --policy-loss cispo|clip", file=sys.stderr)
+        sys.exit(2)
     if args.traffic_summary:
         traffic_summary(args)
         return
@@ -309,8 +315,22 @@ def main():
     if args.side_outputs:
         side_t = [torch.empty(T, dtype=torch.float32, device=dev) for _ in range(3)]
         side = binding.SideOutputs(*(t.data_ptr() for t in side_t))
+    if args.fused:
+        del ws_f, ws_b
+        fus_b, _ = binding.fused_workspace_bytes(prob)
+        ws_u = torch.empty(fus_b, dtype=torch.uint8, device=dev)
+
+    def fused_step():
+        binding._check(L.stce_fused_policy_step(
+            P, ctypes.byref(pg), ctypes.c_void_p(logprob.data_ptr()), ctypes.c_void_p(state.data_ptr()),
+            ctypes.c_void_p(loss_t.data_ptr()), None, None if side is None else ctypes.byref(side),
+            ctypes.c_void_p(gh.data_ptr()), ctypes.c_void_p(gw.data_ptr()), 0, None,
+            ctypes.c_void_p(ws_u.data_ptr()), fus_b, stream))
 
     def step():
+        if args.fused:
+            fused_step()
+            return
         if side is not None:
             binding._check(L.stce_forward_with_side(P, ctypes.c_void_p(logprob.data_ptr()),
                                                     ctypes.c_void_p(state.data_ptr()), ctypes.byref(side), None,
@@ -358,25 +378,27 @@ def main():
     for i in range(prof.count):
         k = binding.KERNEL_KINDS.get(ev.kind[i], str(ev.kind[i]))
         kinds.setdefault(k, []).append(ev.elapsed_ms(i))
-    # algorithmic flop per launch of each product
+    # algorithmic flop per launch of each product: each kind of product does
+    # 2 T H V per step (the fused step has no dlogits product), spread over
+    # the launches observed
     C, Vs = binding.schedule(prob)
-    nsl = -(-V // Vs)
-    per_launch = {
-        "projection": 2.0 * H * V * T / -(-T // C),
-        "dlogits": 2.0 * T * H * V / nsl,
-        "grad_weight": 2.0 * T * H * V / nsl,
-        "grad_hidden": 2.0 * T * H * V / nsl,
-    }
+    if args.fused:
+        C = min(-(-(args.chunk_rows or 4096) // 64) * 64, -(-T // 64) * 64)
+        Vs = None
+    per_step_flop = {k: 2.0 * T * H * V for k in ("projection", "dlogits", "grad_weight", "grad_hidden")}
     stats = {}
+    per_launch = {}
     for k, v in kinds.items():
         a = np.array(v)
-        stats[k] = dict(launches=int(len(a) / args.steps), avg_ms=float(a.mean()), total_ms_per_step=float(a.sum() / args.steps))
-        if k in per_launch:
+        n_launch = len(a) / args.steps
+        stats[k] = dict(launches=int(n_launch), avg_ms=float(a.mean()), total_ms_per_step=float(a.sum() / args.steps))
+        if k in per_step_flop:
+            per_launch[k] = per_step_flop[k] / n_launch
             stats[k]["tflops"] = per_launch[k] / (a.mean() * 1e-3) / 1e12
     dom = max((k for k in stats if k in per_launch), key=lambda k: stats[k]["total_ms_per_step"])
     achieved = stats[dom]["tflops"]
 
-    flop_step = 8.0 * T * H * V
+    flop_step = (6.0 if args.fused else 8.0) * T * H * V
     value = T / (ms_step * 1e-3)
     out = {
         "metric": "scored tokens/s fwd+bwd at V=151936,H=5120; % of bf16 MFMA peak",
@@ -400,10 +422,13 @@ def main():
                                f"{float(w['min_p'].max())}; forward + backward (grad_hidden, grad_weight)"
                                + ("" if args.policy_loss == "none" else
                                   f" of the {args.policy_loss} policy-gradient token loss")
+                               + ("; fused step: dlogits formed in the forward's sweep, no recompute product"
+                                  if args.fused else "")
                                + ("; forward side outputs (full LSE, entropies)" if args.side_outputs else ""),
                    "T": T, "H": H, "V": V, "chunk_rows": C, "vocab_slice": Vs},
         "mfma_peak_frac": flop_step / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
-        "tflops_8thv": flop_step / (ms_step * 1e-3) / 1e12,
+        "tflops_8thv": 8.0 * T * H * V / (ms_step * 1e-3) / 1e12,
+        "tflops_performed": flop_step / (ms_step * 1e-3) / 1e12,
         "tflops_6thv": 6.0 * T * H * V / (ms_step * 1e-3) / 1e12,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,

@@ -202,8 +202,8 @@ size_t stce_support_workspace_bytes(int64_t R, int64_t V);
  * state holds, per row: the boundary key (order-preserving uint32 image of
  * the last support token's fp32 key), the boundary token id, the support
  * size n (V for an unfiltered row, whose boundary is then 0 / V - 1), the
- * filtered and full log-sum-exp, the row maximum, the target's key and
- * flags.  Reads `nrows` entries of a HOST copy of the state. */
+ * filtered and full log-sum-exp, the row maximum, the target's key (0 on
+ * inactive ignore_index rows) and flags.  Reads `nrows` entries of a HOST copy of the state. */
 typedef struct stce_row_info {
   uint32_t key_thr;
   int32_t id_thr;
@@ -233,6 +233,8 @@ stce_status stce_decode_state(const void *host_state, int64_t nrows, stce_row_in
 #define STCE_KERNEL_TRANSPOSE 7
 #define STCE_KERNEL_PARTIALS 8
 #define STCE_KERNEL_POLICY_LOSS 9  /* per-row policy-gradient loss */
+#define STCE_KERNEL_DZ_KEYS 10     /* fused step: dlogits from a chunk's stored keys */
+#define STCE_KERNEL_SPLIT_SUM 11   /* fused step: sum of the hidden-gradient split partials */
 typedef struct stce_profile {
   int32_t capacity;
   int32_t count;
@@ -279,6 +281,47 @@ typedef struct stce_pg_params {
 } stce_pg_params;
 stce_status stce_policy_loss(const stce_pg_params *pg, int64_t T, const float *logprob, float *loss,
                              float *grad_logprob, float *ratio, void *stream);
+
+/* Fused head + policy-gradient step (align "architecture v2: proposal",
+ * section 5.4 A: the "Fused" row of its GEMM-count table and "Why the
+ * in-chunk form works for this loss").  The token coefficient needs only the
+ * new logprob, which a chunk has just computed, so dlogits is formed inside
+ * the forward's sweep and no product is recomputed: 2 products for a frozen
+ * head (logits, dH), 3 for a trainable one (plus dW), against 3 and 4 for
+ * stce_forward + stce_policy_loss + stce_backward.  Per chunk of rows, on
+ * `stream`:
+ *   1. the projection keeps the fp32 keys of every row of the chunk;
+ *   2. the support program and selected logprob as in stce_forward (side
+ *      outputs as in stce_forward_with_side, `side` may be NULL);
+ *   3. the token loss, its gradient and the ratio as in stce_policy_loss;
+ *   4. dz = g (1[j == y] - q) / T from the stored keys, with the arithmetic
+ *      of stce_backward's recompute, so dz equals that path's bit for bit;
+ *   5. grad_hidden rows of the chunk = dz . W (split over the vocabulary,
+ *      fp32 partials summed in split order); the vocab-major dz of a group of
+ *      consecutive chunks is kept (as many as 8 GB hold: all of them at the
+ *      sizes below), and at a group's end grad_weight (+)= dz^T . h with the
+ *      group's rows as the reduction.
+ * Outputs: logprob, state (as stce_forward), loss and ratio (as
+ * stce_policy_loss; ratio may be NULL), and the gradients of sum_t loss[t]:
+ * grad_hidden [T][H] in the operand dtype and grad_weight [V][H] fp32
+ * (overwritten, or added to when accumulate_grad_weight is nonzero); either
+ * may be NULL, both NULL = forward and loss only.  logprob, state and loss are
+ * bitwise those of the unfused sequence on the same inputs; the gradients
+ * differ from its only by fp32 summation order.  pg->state is not read (the
+ * step's own state marks inactive rows).  The chunk size is
+ * prob->chunk_rows rounded up to a multiple of 64 (default 4096); the
+ * workspace (256-byte aligned device memory, stce_fused_workspace_bytes;
+ * about 10.8 GB at T = 16384, H = 5120, V = 151936) holds one chunk's fp32
+ * keys and token-major dz, the group's vocab-major dz, the transposed weight
+ * and hidden, and the split partials.  A workspace between *min_bytes (one
+ * chunk per group) and *bytes keeps as many chunks per group as it holds;
+ * the grouping changes only the order of dW's fp32 sums.  Host errors as stce_forward, stce_backward and
+ * stce_policy_loss. */
+stce_status stce_fused_workspace_bytes(const stce_problem *prob, size_t *bytes, size_t *min_bytes);
+stce_status stce_fused_policy_step(const stce_problem *prob, const stce_pg_params *pg, float *logprob,
+                                   void *state, float *loss, float *ratio, const stce_side_outputs *side,
+                                   void *grad_hidden, float *grad_weight, int32_t accumulate_grad_weight,
+                                   int64_t *dev_status, void *ws, size_t ws_bytes, void *stream);
 
 /* Human-readable name of a status code (static string). */
 const char *stce_status_string(stce_status status);

@@ -28,10 +28,11 @@ SYMBOLS = (
     "stce_state_bytes", "stce_workspace_bytes", "stce_forward", "stce_backward",
     "stce_scaled_logits", "stce_support_from_logits", "stce_support_workspace_bytes",
     "stce_decode_state", "stce_status_string", "stce_last_error", "stce_profile_attach", "stce_schedule",
-    "stce_policy_loss", "stce_forward_with_side",
+    "stce_policy_loss", "stce_forward_with_side", "stce_fused_workspace_bytes", "stce_fused_policy_step",
 )
 KERNEL_KINDS = {1: "validate", 2: "projection", 3: "select", 4: "dlogits", 5: "grad_weight",
-                6: "grad_hidden", 7: "transpose", 8: "partials", 9: "policy_loss"}
+                6: "grad_hidden", 7: "transpose", 8: "partials", 9: "policy_loss", 10: "dz_keys",
+                11: "split_sum"}
 PG_OBJECTIVES = {"cispo": 1, "clip": 2}
 
 
@@ -104,6 +105,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "stce_schedule": (ctypes.c_int, [P, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
         "stce_policy_loss": (ctypes.c_int, [ctypes.POINTER(PgParams), i64, vp, vp, vp, vp, vp]),
         "stce_forward_with_side": (ctypes.c_int, [P, vp, vp, ctypes.POINTER(SideOutputs), vp, vp, sz, vp]),
+        "stce_fused_workspace_bytes": (ctypes.c_int, [P, ctypes.POINTER(sz), ctypes.POINTER(sz)]),
+        "stce_fused_policy_step": (ctypes.c_int, [P, ctypes.POINTER(PgParams), vp, vp, vp, vp,
+                                                  ctypes.POINTER(SideOutputs), vp, vp, i32, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -336,6 +340,68 @@ def policy_loss_step(hidden, weight, target, advantages, old_logprob, temperatur
     gh, gw = backward(hidden, weight, target, state, g, temperature, top_k, top_p, min_p,
                       need_hidden=need_hidden, need_weight=need_weight, ignore_index=ignore_index)
     return loss, logprob, ratio, gh, gw
+
+
+def fused_workspace_bytes(prob: Problem):
+    """(default, minimum) workspace bytes of the fused step; a size between
+    them keeps fewer chunks per weight-gradient group."""
+    n, m = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().stce_fused_workspace_bytes(ctypes.byref(prob), ctypes.byref(n), ctypes.byref(m)))
+    return n.value, m.value
+
+
+def fused_policy_step(hidden, weight, target, advantages, old_logprob, temperature=None, top_k=None, top_p=None,
+                      min_p=None, *, objective: str = "cispo", eps_low: float = 0.2, eps_high: float = 0.28,
+                      scale: float = 1.0, need_hidden: bool = True, need_weight: bool = True,
+                      grad_weight: Optional[torch.Tensor] = None, accumulate_grad_weight: bool = False,
+                      side: bool = False, chunk_rows: int = 0, ignore_index: Optional[int] = None,
+                      check: bool = True, workspace: Optional[torch.Tensor] = None):
+    """The fused head + policy-gradient step (dlogits formed in the forward's
+    sweep, no recompute).  Returns a dict with ``loss``, ``logprob``,
+    ``ratio`` (fp32 [T]), ``state``, ``grad_hidden`` ([T, H], hidden's dtype,
+    or None), ``grad_weight`` (fp32 [V, H] or None) and, with ``side=True``,
+    ``lse_full``, ``entropy_full``, ``entropy_support``."""
+    if objective not in PG_OBJECTIVES:
+        raise ValueError(f"objective must be one of {tuple(PG_OBJECTIVES)}")
+    prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, chunk_rows,
+                              ignore_index=ignore_index)
+    T, H, V = prob.T, prob.H, prob.V
+    dev = hidden.device
+    adv = _meta("advantages", advantages, T, torch.float32, dev)
+    old = _meta("old_logprob", old_logprob, T, torch.float32, dev)
+    if adv is None or old is None:
+        raise ValueError("advantages and old_logprob are required")
+    keep += [adv, old]
+    nb, _ = fused_workspace_bytes(prob)
+    ws = workspace if workspace is not None else torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    out = {k: torch.empty(T, dtype=torch.float32, device=dev) for k in ("loss", "logprob", "ratio")}
+    out["state"] = torch.empty(T * STATE_BYTES_PER_ROW, dtype=torch.uint8, device=dev)
+    out["grad_hidden"] = torch.empty(T, H, dtype=hidden.dtype, device=dev) if need_hidden else None
+    if need_weight:
+        if grad_weight is None:
+            grad_weight = torch.empty(V, H, dtype=torch.float32, device=dev)
+            accumulate_grad_weight = False
+        elif grad_weight.shape != (V, H) or grad_weight.dtype != torch.float32 or not grad_weight.is_contiguous():
+            raise ValueError("grad_weight must be a contiguous fp32 [V, H] tensor")
+    else:
+        grad_weight = None
+    out["grad_weight"] = grad_weight
+    so = None
+    if side:
+        for k in ("lse_full", "entropy_full", "entropy_support"):
+            out[k] = torch.empty(T, dtype=torch.float32, device=dev)
+        so = SideOutputs(*(out[k].data_ptr() for k in ("lse_full", "entropy_full", "entropy_support")))
+    pg = PgParams(PG_OBJECTIVES[objective], eps_low, eps_high, scale, adv.data_ptr(), old.data_ptr(), None)
+    status = torch.empty(1, dtype=torch.int64, device=dev)
+    _check(load().stce_fused_policy_step(ctypes.byref(prob), ctypes.byref(pg), _ptr(out["logprob"]),
+                                         _ptr(out["state"]), _ptr(out["loss"]), _ptr(out["ratio"]),
+                                         None if so is None else ctypes.byref(so), _ptr(out["grad_hidden"]),
+                                         _ptr(grad_weight), 1 if accumulate_grad_weight else 0, _ptr(status),
+                                         _ptr(ws), ws.numel(), _stream()))
+    if check:
+        _raise_rows(status, "stce_fused_policy_step", dict(temperature=keep[3], top_k=keep[4], top_p=keep[5],
+                                                            min_p=keep[6], target=keep[2]))
+    return out
 
 
 def decode_state(state: torch.Tensor) -> dict:

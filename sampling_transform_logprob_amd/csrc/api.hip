@@ -117,6 +117,71 @@ Layout plan(const stce_problem* p) {
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
+// Scalar parameters of the policy-gradient loss.
+stce_status check_pg(const stce_pg_params* pg) {
+  if (!pg) return fail(STCE_E_ARG, "pg parameters are NULL");
+  if (pg->objective != STCE_PG_CISPO && pg->objective != STCE_PG_CLIP)
+    return fail(STCE_E_ARG, "objective=%d: expected STCE_PG_CISPO (1) or STCE_PG_CLIP (2)", (int)pg->objective);
+  if (!(pg->eps_low >= 0.0f && pg->eps_low < 1.0f))
+    return fail(STCE_E_ARG, "eps_low=%g outside [0, 1)", (double)pg->eps_low);
+  if (!(pg->eps_high >= 0.0f && __builtin_isfinite(pg->eps_high)))
+    return fail(STCE_E_ARG, "eps_high=%g must be finite and >= 0", (double)pg->eps_high);
+  if (!__builtin_isfinite(pg->scale)) return fail(STCE_E_ARG, "scale must be finite");
+  return STCE_OK;
+}
+
+// Workspace of the fused policy step: one set of chunk buffers (a chunk's
+// gradients follow its selection on the same stream), the transposed weight
+// and hidden, and the fp32 split partials of the chunk's hidden gradient.
+struct FusedLayout {
+  int64_t C, ldt, ntv, Vp, Tp, S, ks, G;
+  size_t flags, tile, part, sy, g, d, dT, WT, hT, dhp, total;
+};
+
+FusedLayout plan_fused(const stce_problem* p, int64_t gmax = INT64_MAX) {
+  FusedLayout L{};
+  const int64_t T = p->T, V = p->V, H = p->H;
+  const size_t es = elt_size(p->dtype);
+  L.Tp = round_up(T, 64);
+  L.C = round_up(p->chunk_rows > 0 ? p->chunk_rows : kDefaultChunk, 64);
+  if (L.C > L.Tp) L.C = L.Tp;
+  L.ldt = round_up(V, 4);
+  L.ntv = ceil_div(V, VTILE);
+  L.Vp = round_up(V, 64);
+  // split-K of the chunk's hidden-gradient product (a chunk has few output
+  // tiles): about four workgroups per compute unit, splits at least 512
+  // vocabulary columns wide
+  const int64_t tiles = ceil_div(L.C, 256) * ceil_div(H, 256);
+  int64_t S = ceil_div(4 * 256, tiles);
+  if (S > 16) S = 16;
+  int64_t ks = round_up(ceil_div(L.Vp, S), 64);
+  if (ks < 512) ks = 512;
+  if (ks > L.Vp) ks = L.Vp;
+  L.ks = ks;
+  L.S = ceil_div(L.Vp, ks);
+  // the vocab-major dz of G consecutive chunks is kept, so dW is one product
+  // per group with the group's rows as its reduction: as many chunks as the
+  // slice budget holds (fewer fp32 read-modify-write passes over dW)
+  const int64_t nch = ceil_div(T, L.C);
+  L.G = (int64_t)(kSliceBudgetBytes / ((double)es * (double)L.Vp * (double)L.C));
+  if (L.G > nch) L.G = nch;
+  if (L.G > gmax) L.G = gmax;
+  if (L.G < 1) L.G = 1;
+  size_t o = 0;
+  L.flags = o; o = align_up(o + 4 * (size_t)T);
+  L.tile = o;  o = align_up(o + 4 * (size_t)L.C * L.ldt);
+  L.part = o;  o = align_up(o + sizeof(TilePart) * (size_t)L.C * L.ntv);
+  L.sy = o;    o = align_up(o + 4 * (size_t)L.C);
+  L.g = o;     o = align_up(o + 4 * (size_t)L.C);
+  L.d = o;     o = align_up(o + es * (size_t)L.C * L.Vp);
+  L.dT = o;    o = align_up(o + es * (size_t)L.Vp * L.C * L.G);
+  L.WT = o;    o = align_up(o + es * (size_t)H * L.Vp);
+  L.hT = o;    o = align_up(o + es * (size_t)H * L.Tp);
+  L.dhp = o;   o = align_up(o + 4 * (size_t)L.S * L.C * H);
+  L.total = o;
+  return L;
+}
+
 stce_status check_inputs(const stce_problem* p) {
   if (!p->hidden || !p->weight || !p->target) return fail(STCE_E_ARG, "hidden, weight and target are required");
   if (!aligned(p->hidden, 16) || !aligned(p->weight, 16))
@@ -455,16 +520,152 @@ stce_status stce_decode_state(const void* host_state, int64_t nrows, stce_row_in
   return STCE_OK;
 }
 
+stce_status stce_fused_workspace_bytes(const stce_problem* p, size_t* bytes, size_t* min_bytes) {
+  stce_status s = check_shapes(p);
+  if (s) return s;
+  if (!bytes) return fail(STCE_E_ARG, "bytes is NULL");
+  *bytes = plan_fused(p).total;
+  if (min_bytes) *min_bytes = plan_fused(p, 1).total;
+  return STCE_OK;
+}
+
+stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* pg, float* logprob, void* state,
+                                   float* loss, float* ratio, const stce_side_outputs* side_out, void* grad_hidden,
+                                   float* grad_weight, int32_t accumulate_grad_weight, int64_t* dev_status, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  stce_status s = check_shapes(p);
+  if (s) return s;
+  if ((s = check_inputs(p))) return s;
+  if ((s = check_pg(pg))) return s;
+  if (!pg->advantages || !pg->old_logprob || !logprob || !state || !loss)
+    return fail(STCE_E_ARG, "advantages, old_logprob, logprob, state and loss are required");
+  if (!aligned(pg->advantages, 4) || !aligned(pg->old_logprob, 4) || !aligned(logprob, 4) || !aligned(loss, 4) ||
+      (ratio && !aligned(ratio, 4)) || !aligned(state, 16))
+    return fail(STCE_E_ARG, "arrays must be 4-byte aligned (state 16-byte)");
+  if ((grad_hidden && !aligned(grad_hidden, 16)) || (grad_weight && !aligned(grad_weight, 16)))
+    return fail(STCE_E_ARG, "gradient outputs must be 16-byte aligned");
+  float* so_lse = side_out ? side_out->lse_full : nullptr;
+  float* so_hf = side_out ? side_out->entropy_full : nullptr;
+  float* so_hs = side_out ? side_out->entropy_support : nullptr;
+  if ((so_lse && !aligned(so_lse, 4)) || (so_hf && !aligned(so_hf, 4)) || (so_hs && !aligned(so_hs, 4)))
+    return fail(STCE_E_ARG, "side outputs must be 4-byte aligned");
+  // a workspace below the default keeps fewer chunks per weight-gradient
+  // group: each further chunk of a group adds exactly G1.Vp * G1.C elements
+  const FusedLayout G1 = plan_fused(p, 1);
+  if ((s = check_ws(ws, ws_bytes, G1.total))) return s;
+  const size_t per_chunk = elt_size(p->dtype) * (size_t)G1.Vp * (size_t)G1.C;
+  const FusedLayout L = plan_fused(p, 1 + (int64_t)((ws_bytes - G1.total) / per_chunk));
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  uint32_t* flags = at<uint32_t>(ws, L.flags);
+  if (dev_status && (e = launch_fill_i64(dev_status, STCE_STATUS_NONE, st))) return hip_fail(e, "status fill");
+  if ((e = launch_validate(p->T, p->V, p->flags & STCE_PROBLEM_IGNORE_INDEX, p->ignore_index, p->temperature,
+                           p->top_k, p->top_p, p->min_p, p->target, flags, dev_status, st)))
+    return hip_fail(e, "validate");
+  const size_t es = elt_size(p->dtype);
+  if (grad_hidden) {
+    if (p->dtype == STCE_DT_BF16)
+      e = launch_transpose_bf16((const bf16*)p->weight, p->H, p->V, p->H, at<bf16>(ws, L.WT), L.Vp, L.Vp, st);
+    else
+      e = launch_transpose_f32((const float*)p->weight, p->H, p->V, p->H, at<float>(ws, L.WT), L.Vp, L.Vp, st);
+    if (e) return hip_fail(e, "transpose weight");
+  }
+  if (grad_weight) {
+    if (p->dtype == STCE_DT_BF16)
+      e = launch_transpose_bf16((const bf16*)p->hidden, p->H, p->T, p->H, at<bf16>(ws, L.hT), L.Tp, L.Tp, st);
+    else
+      e = launch_transpose_f32((const float*)p->hidden, p->H, p->T, p->H, at<float>(ws, L.hT), L.Tp, L.Tp, st);
+    if (e) return hip_fail(e, "transpose hidden");
+  }
+  const int64_t nch = ceil_div(p->T, L.C);
+  for (int64_t c = 0; c < nch; ++c) {
+    const int64_t c0 = c * L.C;
+    const int64_t nc = p->T - c0 < L.C ? p->T - c0 : L.C;
+    // the chunk's keys (every row: the gradient needs them all), selection,
+    // selected logprob and token loss
+    FwdArgs a{};
+    a.dtype = p->dtype;
+    a.W = p->weight;
+    a.h = (const char*)p->hidden + es * (size_t)c0 * p->H;
+    a.H = p->H;
+    a.V = p->V;
+    a.rows = nc;
+    a.tile = at<float>(ws, L.tile);
+    a.ld = L.ldt;
+    a.temp = p->temperature ? p->temperature + c0 : nullptr;
+    a.target = p->target + c0;
+    a.flags = flags + c0;
+    a.store_all = 1;
+    a.part = at<TilePart>(ws, L.part);
+    a.ntv = (int)L.ntv;
+    a.s_y = at<float>(ws, L.sy);
+    a.want_ent = (so_hf || so_hs) ? 1 : 0;
+    if ((e = launch_fwd_projection(a, st))) return hip_fail(e, "projection");
+    SelParams sp{};
+    sp.tile = a.tile;
+    sp.ld = L.ldt;
+    sp.part = a.part;
+    sp.ntv = (int)L.ntv;
+    sp.s_y = a.s_y;
+    sp.flags = flags + c0;
+    sp.target = p->target + c0;
+    sp.top_k = p->top_k ? p->top_k + c0 : nullptr;
+    sp.top_p = p->top_p ? p->top_p + c0 : nullptr;
+    sp.min_p = p->min_p ? p->min_p + c0 : nullptr;
+    sp.logprob = logprob + c0;
+    sp.state = (RowState*)state + c0;
+    sp.V = (int)p->V;
+    sp.lse_full = so_lse ? so_lse + c0 : nullptr;
+    sp.ent_full = so_hf ? so_hf + c0 : nullptr;
+    sp.ent_supp = so_hs ? so_hs + c0 : nullptr;
+    launch_select(sp, (int)nc, st);
+    if ((e = hipGetLastError())) return hip_fail(e, "select");
+    float* g = at<float>(ws, L.g);
+    if ((e = launch_policy_loss(pg->objective, pg->eps_low, pg->eps_high, pg->scale, pg->advantages + c0,
+                                pg->old_logprob + c0, sp.state, nc, sp.logprob, loss + c0, g,
+                                ratio ? ratio + c0 : nullptr, st)))
+      return hip_fail(e, "policy loss");
+    if (!grad_hidden && !grad_weight) continue;
+    // dlogits formed from the chunk's keys, then its dH rows and its share
+    // of dW
+    FusedGradArgs ga{};
+    ga.dtype = p->dtype;
+    ga.keys = a.tile;
+    ga.ld_keys = L.ldt;
+    ga.temp = a.temp;
+    ga.target = a.target;
+    ga.st = sp.state;
+    ga.g = g;
+    ga.d = at<char>(ws, L.d);
+    ga.dT = at<char>(ws, L.dT);
+    ga.ld_dT = L.G * L.C;
+    ga.dT_col = (c % L.G) * L.C;
+    ga.WT = at<char>(ws, L.WT);
+    ga.hT = at<char>(ws, L.hT);
+    ga.dh_part = at<float>(ws, L.dhp);
+    ga.splits = (int)L.S;
+    ga.ks = L.ks;
+    ga.grad_hidden = grad_hidden ? (char*)grad_hidden + es * (size_t)c0 * p->H : nullptr;
+    ga.grad_weight = grad_weight;
+    ga.accumulate_w = (c >= L.G || accumulate_grad_weight) ? 1 : 0;
+    ga.rows = nc;
+    ga.rows_pad = round_up(nc, 64);
+    ga.dw = (c % L.G == L.G - 1 || c == nch - 1) ? 1 : 0;
+    ga.dw_c0 = (c / L.G) * L.G * L.C;
+    ga.dw_k = c0 - ga.dw_c0 + ga.rows_pad;
+    ga.Tp = L.Tp;
+    ga.H = p->H;
+    ga.V = p->V;
+    ga.V_pad = L.Vp;
+    if ((e = launch_fused_chunk_grads(ga, st))) return hip_fail(e, "fused gradients");
+  }
+  return STCE_OK;
+}
+
 stce_status stce_policy_loss(const stce_pg_params* pg, int64_t T, const float* logprob, float* loss,
                              float* grad_logprob, float* ratio, void* stream) {
-  if (!pg) return fail(STCE_E_ARG, "pg parameters are NULL");
-  if (pg->objective != STCE_PG_CISPO && pg->objective != STCE_PG_CLIP)
-    return fail(STCE_E_ARG, "objective=%d: expected STCE_PG_CISPO (1) or STCE_PG_CLIP (2)", (int)pg->objective);
-  if (!(pg->eps_low >= 0.0f && pg->eps_low < 1.0f))
-    return fail(STCE_E_ARG, "eps_low=%g outside [0, 1)", (double)pg->eps_low);
-  if (!(pg->eps_high >= 0.0f && __builtin_isfinite(pg->eps_high)))
-    return fail(STCE_E_ARG, "eps_high=%g must be finite and >= 0", (double)pg->eps_high);
-  if (!__builtin_isfinite(pg->scale)) return fail(STCE_E_ARG, "scale must be finite");
+  stce_status s = check_pg(pg);
+  if (s) return s;
   if (T < 1 || T > INT32_MAX - 512) return fail(STCE_E_ARG, "T=%lld out of range", (long long)T);
   if (!pg->advantages || !pg->old_logprob || !logprob || !loss || !grad_logprob)
     return fail(STCE_E_ARG, "advantages, old_logprob, logprob, loss and grad_logprob are required");

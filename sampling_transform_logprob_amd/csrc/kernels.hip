@@ -171,6 +171,156 @@ __global__ void tile_partials_kernel(const float* s, int64_t ld, int64_t R, int6
   }
 }
 
+// dz of one chunk from its stored fp32 keys, with the arithmetic of the
+// recompute epilogue (the same membership test against the boundary key's
+// value, exp2 argument, coefficient and rounding), so every value is the one
+// the recompute backward forms from the same keys.  Block: TT rows x 256
+// columns; lane l of a wave takes columns 4l .. 4l+3 of 8 rows at a time,
+// writes them token-major and stages them in LDS, from where the
+// vocab-major copy leaves as 16-byte row segments.  Rows rows .. rows_pad
+// and columns V .. V_pad get zeros.
+template <class OutT>
+__global__ __launch_bounds__(256) void dz_keys_kernel(const float* keys, int64_t ld, const float* temp,
+                                                      const int64_t* target, const RowState* st, const float* g,
+                                                      int rows, int rows_pad, int V, int V_pad, OutT* d,
+                                                      int64_t ld_d, OutT* dT, int64_t ld_dT) {
+  constexpr int TT = sizeof(OutT) == 2 ? 64 : 32, TV = 256, SP = TT + 16 / (int)sizeof(OutT);
+  __shared__ __attribute__((aligned(16))) OutT stage[TV * SP];
+  __shared__ float r_c[TT], r_thr[TT], r_nl[TT];
+  __shared__ int r_idt[TT], r_y[TT];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int t0 = blockIdx.y * TT, v0 = blockIdx.x * TV;
+  if (tid < TT) {
+    const int t = t0 + tid;
+    float c = 0.f, thr = -__builtin_huge_valf(), nl = 0.f;
+    int idt = 0, y = -1;
+    if (t < rows) {
+      const RowState rs = st[t];
+      const float tt = temp ? temp[t] : 1.0f;
+      if ((rs.flags & (ROW_VALID | ROW_IN_SUPPORT)) == (ROW_VALID | ROW_IN_SUPPORT)) c = g[t] / tt;
+      thr = (rs.flags & ROW_FILTERED) ? key_value(rs.key_thr) : -__builtin_huge_valf();
+      idt = rs.id_thr;
+      nl = -rs.lse_s * LOG2E;
+      y = (int)target[t];
+    }
+    r_c[tid] = c;
+    r_thr[tid] = thr;
+    r_nl[tid] = nl;
+    r_idt[tid] = idt;
+    r_y[tid] = y;
+  }
+  __syncthreads();
+  const int v = v0 + 4 * lane;
+  for (int grp = w; grp < TT / 8; grp += 4) {
+    OutT o[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int tl = grp * 8 + i, t = t0 + tl;
+      const float c = r_c[tl], thr = r_thr[tl], nl = r_nl[tl];
+      const int idt = r_idt[tl], y = r_y[tl];
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if (c != 0.f) {  // live row (t < rows)
+        const float* kp = keys + (int64_t)t * ld;
+        if (v + 4 <= V) {
+          x = *(const f32x4*)(kp + v);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (v + e < V) x[e] = kp[v + e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int vg = v + e;
+        const float sv = x[e];
+        const bool in = (sv > thr) | ((sv == thr) & (vg <= idt));
+        const float q = in ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv, LOG2E, nl)) : 0.f;
+        const float dv = c * ((vg == y ? 1.f : 0.f) - q);
+        o[i][e] = (OutT)((c != 0.f && vg < V) ? dv : 0.f);
+      }
+      if (t < rows_pad && v < V_pad) {
+        OutT* dp = d + (int64_t)t * ld_d + v;
+        if constexpr (sizeof(OutT) == 2) {
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          const uint32_t p0 = (uint32_t)__builtin_bit_cast(uint16_t, o[i][0]) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, o[i][1]) << 16);
+          const uint32_t p1 = (uint32_t)__builtin_bit_cast(uint16_t, o[i][2]) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, o[i][3]) << 16);
+          *(u32x2*)dp = u32x2{p0, p1};
+        } else {
+          *(f32x4*)dp = f32x4{(float)o[i][0], (float)o[i][1], (float)o[i][2], (float)o[i][3]};
+        }
+      }
+    }
+    // staged as [column][row]: 8 consecutive rows of each of the 4 columns
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      OutT* sp = stage + (4 * lane + e) * SP + grp * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sp[i] = o[i][e];
+    }
+  }
+  __syncthreads();
+  constexpr int EPC = 16 / (int)sizeof(OutT);  // elements per 16-byte chunk
+  constexpr int CPR = TT / EPC;                // chunks per staged row
+  for (int q = tid; q < TV * CPR; q += 256) {
+    const int r = q / CPR, cc = (q % CPR) * EPC;
+    const int vv = v0 + r, tt = t0 + cc;
+    if (vv < V_pad && tt < rows_pad)
+      *(u32x4*)(dT + (int64_t)vv * ld_dT + tt) = *(const u32x4*)(stage + r * SP + cc);
+  }
+}
+
+// Split-K product: workgroup b computes tile b % tiles over the reduction
+// range [split * ks, min(K, (split + 1) * ks)), split = b / tiles, and
+// stores it (fp32) into partial buffer `split`.
+template <class Main>
+__global__ __launch_bounds__(GTHREADS, 1) void gemm_splitk_kernel(Main mainloop, EpiStore epi, TileMap map, int tiles,
+                                                                 int64_t ks, int64_t pstride) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int split = blockIdx.x / tiles;
+  int tm, tn;
+  map.get(blockIdx.x - split * tiles, tm, tn);
+  Main mn = mainloop;
+  mn.A += split * ks;
+  mn.B += split * ks;
+  mn.K = (int)min((int64_t)mainloop.K - split * ks, ks);
+  EpiStore ep = epi;
+  ep.out += split * pstride;
+  AccTile acc;
+#pragma unroll
+  for (int i = 0; i < ACC_I; ++i)
+#pragma unroll
+    for (int j = 0; j < ACC_J; ++j) acc[i][j] = f32x4{};
+  mn.run(acc, tm * GM, tn * GN, smem);
+  ep(acc, tm * GM, tn * GN, smem);
+}
+
+// out[i] = part[0][i] + part[1][i] + ... in split order, 4 elements a thread.
+template <class OutT>
+__global__ void sum_splits_kernel(const float* part, int splits, int64_t pstride, int64_t n4, OutT* out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  f32x4 v = ((const f32x4*)part)[i];
+  for (int s = 1; s < splits; ++s) {
+    const f32x4 x = ((const f32x4*)(part + s * pstride))[i];
+    v[0] += x[0];
+    v[1] += x[1];
+    v[2] += x[2];
+    v[3] += x[3];
+  }
+  if constexpr (sizeof(OutT) == 2) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const uint32_t p0 = (uint32_t)__builtin_bit_cast(uint16_t, (OutT)v[0]) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (OutT)v[1]) << 16);
+    const uint32_t p1 = (uint32_t)__builtin_bit_cast(uint16_t, (OutT)v[2]) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (OutT)v[3]) << 16);
+    ((u32x2*)out)[i] = u32x2{p0, p1};
+  } else {
+    ((f32x4*)out)[i] = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 template <class Main, class Epi>
 hipError_t launch_gemm(const Main& mn, const Epi& ep, int64_t tiles_m, int64_t tiles_n, hipStream_t s) {
@@ -182,6 +332,21 @@ hipError_t launch_gemm(const Main& mn, const Epi& ep, int64_t tiles_m, int64_t t
   if (attr != hipSuccess) return attr;
   TileMap map{(int)tiles_m, (int)tiles_n, 4};
   hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(GTHREADS), lds, s, mn, ep, map);
+  return hipGetLastError();
+}
+
+template <class Main>
+hipError_t launch_gemm_splitk(const Main& mn, const EpiStore& ep, int64_t tiles_m, int64_t tiles_n, int splits,
+                              int64_t ks, int64_t pstride, hipStream_t s) {
+  if (tiles_m <= 0 || tiles_n <= 0 || splits <= 0) return hipSuccess;
+  auto kern = gemm_splitk_kernel<Main>;
+  constexpr int lds = Main::LDS_BYTES;
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  static const hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  TileMap map{(int)tiles_m, (int)tiles_n, 4};
+  const int tiles = (int)(tiles_m * tiles_n);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * splits)), dim3(GTHREADS), lds, s, mn, ep, map, tiles, ks, pstride);
   return hipGetLastError();
 }
 
@@ -308,6 +473,54 @@ hipError_t bwd_slice_impl(const BwdSliceArgs& a, hipStream_t s) {
 hipError_t launch_bwd_slice(const BwdSliceArgs& a, hipStream_t s) {
   if (a.dtype == 1) return bwd_slice_impl<bf16, MainBf16>(a, s);
   return bwd_slice_impl<float, MainF32>(a, s);
+}
+
+namespace {
+template <class E, class Main>
+hipError_t fused_grads_impl(const FusedGradArgs& a, hipStream_t s) {
+  hipError_t e;
+  // 1. dz of the chunk, token-major d [rows_pad][V_pad] and vocab-major dT
+  //    [V_pad][rows_pad]
+  {
+    constexpr int TT = sizeof(E) == 2 ? 64 : 32;
+    ProfScope ps(10, s);
+    hipLaunchKernelGGL(dz_keys_kernel<E>, dim3((unsigned)ceil_div(a.V_pad, 256), (unsigned)ceil_div(a.rows_pad, TT)),
+                       dim3(256), 0, s, a.keys, a.ld_keys, a.temp, a.target, a.st, a.g, (int)a.rows, (int)a.rows_pad,
+                       (int)a.V, (int)a.V_pad, (E*)a.d, a.V_pad, (E*)a.dT + a.dT_col, a.ld_dT);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // 2. the chunk's hidden-gradient rows: dH = dz . W over vocabulary splits,
+  //    fp32 partials, then their sum in split order
+  if (a.grad_hidden) {
+    Main mn{(const E*)a.d, a.V_pad, (int)a.rows, (const E*)a.WT, a.V_pad, (int)a.H, (int)a.V_pad};
+    EpiStore ep{a.dh_part, a.H, (int)a.rows, (int)a.H, 0};
+    {
+      ProfScope ps(6, s);
+      e = launch_gemm_splitk(mn, ep, ceil_div(a.rows, GM), ceil_div(a.H, GN), a.splits, a.ks, a.rows * a.H, s);
+    }
+    if (e != hipSuccess) return e;
+    const int64_t n4 = a.rows * a.H / 4;
+    ProfScope ps(11, s);
+    hipLaunchKernelGGL(sum_splits_kernel<E>, dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0, s, a.dh_part, a.splits,
+                       a.rows * a.H, n4, (E*)a.grad_hidden);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // 3. weight gradient of a finished group: dW (+)= dz^T . h over the
+  //    group's rows (zero dT columns for the padding rows)
+  if (a.grad_weight && a.dw) {
+    Main mn{(const E*)a.dT, a.ld_dT, (int)a.V, (const E*)a.hT + a.dw_c0, a.Tp, (int)a.H, (int)a.dw_k};
+    EpiStore ep{a.grad_weight, a.H, (int)a.V, (int)a.H, a.accumulate_w};
+    ProfScope ps(5, s);
+    e = launch_gemm(mn, ep, ceil_div(a.V, GM), ceil_div(a.H, GN), s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_fused_chunk_grads(const FusedGradArgs& a, hipStream_t s) {
+  if (a.dtype == 1) return fused_grads_impl<bf16, MainBf16>(a, s);
+  return fused_grads_impl<float, MainF32>(a, s);
 }
 
 }  // namespace stce

@@ -80,4 +80,37 @@ struct BwdSliceArgs {
 };
 hipError_t launch_bwd_slice(const BwdSliceArgs& a, hipStream_t s);
 
+// Gradients of one chunk of the fused policy step, from the chunk's stored
+// keys (no recompute product): dz token-major and vocab-major, the chunk's
+// hidden-gradient rows as a split-K product over the vocabulary (fp32
+// partials summed in split order), and, at the end of a group of chunks whose
+// vocab-major dz is kept, the weight gradient with the group's rows as the
+// reduction.
+struct FusedGradArgs {
+  int dtype;
+  const float* keys;    // [rows][ld_keys] fp32 keys of the chunk
+  int64_t ld_keys;
+  const float* temp;    // chunk rows, or null
+  const int64_t* target;
+  const RowState* st;
+  const float* g;       // [rows] d loss / d logprob
+  void* d;              // [rows_pad][V_pad] scratch
+  void* dT;             // [V_pad][ld_dT] scratch: the group's vocab-major dz; this chunk's at column dT_col
+  int64_t ld_dT, dT_col;
+  const void* WT;       // [H][V_pad] transposed weight (zero columns V .. V_pad)
+  const void* hT;       // [H][Tp] transposed hidden
+  float* dh_part;       // [splits][rows][H] scratch
+  int splits;
+  int64_t ks;           // vocabulary columns per split (multiple of 64)
+  void* grad_hidden;    // chunk rows [rows][H] or null
+  float* grad_weight;   // [V][H] or null
+  int accumulate_w;
+  // the weight-gradient product of the group ends with this chunk: rows
+  // dw_c0 .. dw_c0 + dw_k of hT against dT columns 0 .. dw_k
+  int dw;
+  int64_t dw_c0, dw_k;
+  int64_t rows, rows_pad, Tp, H, V, V_pad;
+};
+hipError_t launch_fused_chunk_grads(const FusedGradArgs& a, hipStream_t s);
+
 }  // namespace stce

@@ -168,7 +168,9 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
   }
   if (tid == 0 && P.lse_full) P.lse_full[row] = (float)lse_full;
 
-  const float sy = P.s_y[row];
+  // an inactive row's target is no token, so the projection left no key
+  // for it: its state records 0
+  const float sy = (fl & ROW_IGNORED) ? 0.0f : P.s_y[row];
   const int64_t y = P.target[row];
   RowState rs;
   rs.m = m;

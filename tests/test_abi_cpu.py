@@ -129,3 +129,47 @@ def test_policy_loss_rejects_bad_parameters_before_launch(lib):
     assert call(T=0) == 1 and b"T=0" in lib.stce_last_error()
     assert lib.stce_policy_loss(None, 4, fake, fake, fake, None, None) == 1
     assert ctypes.sizeof(binding.PgParams) == 40
+
+
+def test_fused_workspace_is_host_computable_and_chunk_bounded(lib):
+    n, nmin = binding.fused_workspace_bytes(_prob(T=100000, chunk_rows=512))
+    V, Vp, H = 100, 128, 64
+    # one chunk's keys, partials, target keys, row gradients and token-major
+    # dz; the vocab-major dz of a group of chunks (at most the 8 GB slice
+    # budget, here all rows); the transposed weight and hidden, the split
+    # partials and the row flags
+    per_chunk = 512 * (104 * 4 + 16 + 4 + 4) + 2 * 512 * Vp
+    groups = 2 * Vp * 100352
+    assert n < per_chunk + groups + 2 * H * Vp + 2 * H * 100032 + 16 * 4 * 512 * H + 100000 * 4 + 16 * 4096
+    big = _prob(T=16384, H=5120, V=151936)
+    nb, _ = binding.fused_workspace_bytes(big)
+    assert 10e9 < nb < 11.5e9      # keys 2.5 GB, dz 1.25 + 5 GB, transposed weight 1.6 GB, ...
+    # the minimum keeps one chunk per weight-gradient group
+    assert nmin == n - 2 * Vp * 512 * (-(-100000 // 512) - 1)
+    n2 = binding.fused_workspace_bytes(_prob(T=100000, chunk_rows=100))[1]   # rounded up to 128 rows
+    assert n2 > binding.fused_workspace_bytes(_prob(T=100000, chunk_rows=64))[1]
+
+
+def test_fused_step_rejects_bad_arguments_before_launch(lib):
+    fake = ctypes.c_void_p(16)
+    p = _prob()
+    p.hidden, p.weight, p.target = 16, 16, 16       # fake, never dereferenced: checks stop first
+    good = dict(objective=1, eps_low=0.2, eps_high=0.28, scale=1.0, advantages=16, old_logprob=16)
+
+    def call(pg_kw=None, state=fake, loss=fake, ws=None, nbytes=0):
+        d = dict(good)
+        d.update(pg_kw or {})
+        pg = binding.PgParams(**d)
+        return lib.stce_fused_policy_step(ctypes.byref(p), ctypes.byref(pg), fake, state, loss, None, None, None,
+                                          None, 0, None, ws, nbytes, None)
+
+    for kw, msg in ((dict(objective=0), b"objective"), (dict(eps_low=1.5), b"eps_low"),
+                    (dict(scale=float("inf")), b"scale"), (dict(advantages=None), b"required")):
+        assert call(kw) == 1 and msg in lib.stce_last_error(), kw
+    assert call(state=None) == 1 and b"required" in lib.stce_last_error()
+    assert call(state=ctypes.c_void_p(20)) == 1 and b"aligned" in lib.stce_last_error()
+    assert call() == 3 and b"workspace" in lib.stce_last_error()
+    assert lib.stce_fused_policy_step(ctypes.byref(p), None, fake, fake, fake, None, None, None, None, 0, None,
+                                      None, 0, None) == 1
+    n = ctypes.c_size_t()
+    assert lib.stce_fused_workspace_bytes(ctypes.byref(_prob(T=0)), ctypes.byref(n), None) == 1
