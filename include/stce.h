@@ -311,12 +311,15 @@ stce_status stce_policy_loss(const stce_pg_params *pg, int64_t T, const float *l
  * step's own state marks inactive rows).  The chunk size is
  * prob->chunk_rows rounded up to a multiple of 64 (default 4096); the
  * workspace (256-byte aligned device memory, stce_fused_workspace_bytes;
- * about 10.8 GB at T = 16384, H = 5120, V = 151936) holds one chunk's fp32
- * keys and token-major dz, the group's vocab-major dz, the transposed weight
- * and hidden, and the split partials.  A workspace between *min_bytes (one
+ * 13.3 GB at T = 16384, H = 5120, V = 151936, 9.6 GB at its minimum) holds
+ * the fp32 keys of two chunks (a chunk's selection runs on a side stream of
+ * the library's while the next chunk is projected, joined by event waits as
+ * in stce_forward), a chunk's token-major dz, the group's vocab-major dz, the
+ * transposed weight and hidden, and the split partials.  A workspace between *min_bytes (one
  * chunk per group) and *bytes keeps as many chunks per group as it holds;
  * the grouping changes only the order of dW's fp32 sums.  Host errors as stce_forward, stce_backward and
- * stce_policy_loss. */
+ * stce_policy_loss, and V must be below 2^29 (the chunk's key rows are read
+ * through 32-bit buffer offsets). */
 stce_status stce_fused_workspace_bytes(const stce_problem *prob, size_t *bytes, size_t *min_bytes);
 stce_status stce_fused_policy_step(const stce_problem *prob, const stce_pg_params *pg, float *logprob,
                                    void *state, float *loss, float *ratio, const stce_side_outputs *side,

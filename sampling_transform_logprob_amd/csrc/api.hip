@@ -130,12 +130,15 @@ stce_status check_pg(const stce_pg_params* pg) {
   return STCE_OK;
 }
 
-// Workspace of the fused policy step: one set of chunk buffers (a chunk's
-// gradients follow its selection on the same stream), the transposed weight
-// and hidden, and the fp32 split partials of the chunk's hidden gradient.
+// Workspace of the fused policy step: two sets of chunk key buffers when
+// there is more than one chunk (chunk c's selection, on the side stream,
+// overlaps chunk c + 1's projection), the chunk's token-major dz, the
+// group's vocab-major dz, the transposed weight and hidden, and the fp32
+// split partials of the chunk's hidden gradient.
 struct FusedLayout {
-  int64_t C, ldt, ntv, Vp, Tp, S, ks, G;
+  int64_t C, ldt, ntv, Vp, Tp, S, ks, G, nbuf;
   size_t flags, tile, part, sy, g, d, dT, WT, hT, dhp, total;
+  size_t buf_tile, buf_part, buf_sy;
 };
 
 FusedLayout plan_fused(const stce_problem* p, int64_t gmax = INT64_MAX) {
@@ -169,9 +172,13 @@ FusedLayout plan_fused(const stce_problem* p, int64_t gmax = INT64_MAX) {
   if (L.G < 1) L.G = 1;
   size_t o = 0;
   L.flags = o; o = align_up(o + 4 * (size_t)T);
-  L.tile = o;  o = align_up(o + 4 * (size_t)L.C * L.ldt);
-  L.part = o;  o = align_up(o + sizeof(TilePart) * (size_t)L.C * L.ntv);
-  L.sy = o;    o = align_up(o + 4 * (size_t)L.C);
+  L.nbuf = nch > 1 ? 2 : 1;
+  L.buf_tile = align_up(4 * (size_t)L.C * L.ldt);
+  L.buf_part = align_up(sizeof(TilePart) * (size_t)L.C * L.ntv);
+  L.buf_sy = align_up(4 * (size_t)L.C);
+  L.tile = o;  o += L.nbuf * L.buf_tile;
+  L.part = o;  o += L.nbuf * L.buf_part;
+  L.sy = o;    o += L.nbuf * L.buf_sy;
   L.g = o;     o = align_up(o + 4 * (size_t)L.C);
   L.d = o;     o = align_up(o + es * (size_t)L.C * L.Vp);
   L.dT = o;    o = align_up(o + es * (size_t)L.Vp * L.C * L.G);
@@ -551,6 +558,8 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
     return fail(STCE_E_ARG, "side outputs must be 4-byte aligned");
   // a workspace below the default keeps fewer chunks per weight-gradient
   // group: each further chunk of a group adds exactly G1.Vp * G1.C elements
+  if (4 * round_up(p->V, 4) >= (int64_t)INT32_MAX)
+    return fail(STCE_E_ARG, "V=%lld: the fused step takes V < 2^29", (long long)p->V);
   const FusedLayout G1 = plan_fused(p, 1);
   if ((s = check_ws(ws, ws_bytes, G1.total))) return s;
   const size_t per_chunk = elt_size(p->dtype) * (size_t)G1.Vp * (size_t)G1.C;
@@ -578,11 +587,13 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
     if (e) return hip_fail(e, "transpose hidden");
   }
   const int64_t nch = ceil_div(p->T, L.C);
-  for (int64_t c = 0; c < nch; ++c) {
-    const int64_t c0 = c * L.C;
-    const int64_t nc = p->T - c0 < L.C ? p->T - c0 : L.C;
-    // the chunk's keys (every row: the gradient needs them all), selection,
-    // selected logprob and token loss
+  SideCtx* side = nullptr;
+  if (L.nbuf == 2 && (e = side_ctx(&side, 2 * (size_t)nch))) return hip_fail(e, "side stream");
+  auto rows_of = [&](int64_t c) { return p->T - c * L.C < L.C ? p->T - c * L.C : L.C; };
+  // the chunk's keys (every row: the gradient needs them all), then its
+  // selection and selected logprob, on the side stream when there is one
+  auto project_select = [&](int64_t c) -> stce_status {
+    const int64_t c0 = c * L.C, nc = rows_of(c), b = c % L.nbuf;
     FwdArgs a{};
     a.dtype = p->dtype;
     a.W = p->weight;
@@ -590,17 +601,24 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
     a.H = p->H;
     a.V = p->V;
     a.rows = nc;
-    a.tile = at<float>(ws, L.tile);
+    a.tile = at<float>(ws, L.tile + b * L.buf_tile);
     a.ld = L.ldt;
     a.temp = p->temperature ? p->temperature + c0 : nullptr;
     a.target = p->target + c0;
     a.flags = flags + c0;
     a.store_all = 1;
-    a.part = at<TilePart>(ws, L.part);
+    a.part = at<TilePart>(ws, L.part + b * L.buf_part);
     a.ntv = (int)L.ntv;
-    a.s_y = at<float>(ws, L.sy);
+    a.s_y = at<float>(ws, L.sy + b * L.buf_sy);
     a.want_ent = (so_hf || so_hs) ? 1 : 0;
-    if ((e = launch_fwd_projection(a, st))) return hip_fail(e, "projection");
+    hipError_t e2;
+    if ((e2 = launch_fwd_projection(a, st))) return hip_fail(e2, "projection");
+    hipStream_t ss = st;
+    if (side) {
+      ss = side->stream;
+      if ((e2 = hipEventRecord(side->ev[2 * c], st)) || (e2 = hipStreamWaitEvent(ss, side->ev[2 * c], 0)))
+        return hip_fail(e2, "fork to the side stream");
+    }
     SelParams sp{};
     sp.tile = a.tile;
     sp.ld = L.ldt;
@@ -618,11 +636,24 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
     sp.lse_full = so_lse ? so_lse + c0 : nullptr;
     sp.ent_full = so_hf ? so_hf + c0 : nullptr;
     sp.ent_supp = so_hs ? so_hs + c0 : nullptr;
-    launch_select(sp, (int)nc, st);
-    if ((e = hipGetLastError())) return hip_fail(e, "select");
+    launch_select(sp, (int)nc, ss);
+    if ((e2 = hipGetLastError())) return hip_fail(e2, "select");
+    if (side && (e2 = hipEventRecord(side->ev[2 * c + 1], ss))) return hip_fail(e2, "selection event");
+    return STCE_OK;
+  };
+  if ((s = project_select(0))) return s;
+  for (int64_t c = 0; c < nch; ++c) {
+    const int64_t c0 = c * L.C, nc = rows_of(c), b = c % L.nbuf;
+    // the next chunk's projection overlaps this chunk's selection; it writes
+    // the other buffer, whose readers (chunk c - 1's selection and dz) are
+    // done: the first is waited for below, the second is earlier on `st`
+    if (c + 1 < nch && (s = project_select(c + 1))) return s;
+    if (side && (e = hipStreamWaitEvent(st, side->ev[2 * c + 1], 0))) return hip_fail(e, "join");
+    // the token loss of the chunk's rows
+    RowState* stc = (RowState*)state + c0;
     float* g = at<float>(ws, L.g);
     if ((e = launch_policy_loss(pg->objective, pg->eps_low, pg->eps_high, pg->scale, pg->advantages + c0,
-                                pg->old_logprob + c0, sp.state, nc, sp.logprob, loss + c0, g,
+                                pg->old_logprob + c0, stc, nc, logprob + c0, loss + c0, g,
                                 ratio ? ratio + c0 : nullptr, st)))
       return hip_fail(e, "policy loss");
     if (!grad_hidden && !grad_weight) continue;
@@ -630,11 +661,11 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
     // of dW
     FusedGradArgs ga{};
     ga.dtype = p->dtype;
-    ga.keys = a.tile;
+    ga.keys = at<float>(ws, L.tile + b * L.buf_tile);
     ga.ld_keys = L.ldt;
-    ga.temp = a.temp;
-    ga.target = a.target;
-    ga.st = sp.state;
+    ga.temp = p->temperature ? p->temperature + c0 : nullptr;
+    ga.target = p->target + c0;
+    ga.st = stc;
     ga.g = g;
     ga.d = at<char>(ws, L.d);
     ga.dT = at<char>(ws, L.dT);

@@ -188,7 +188,8 @@ __global__ __launch_bounds__(256) void dz_keys_kernel(const float* keys, int64_t
   __shared__ __attribute__((aligned(16))) OutT stage[TV * SP];
   __shared__ float r_c[TT], r_thr[TT], r_nl[TT];
   __shared__ int r_idt[TT], r_y[TT];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: the row resources stay scalar
   const int t0 = blockIdx.y * TT, v0 = blockIdx.x * TV;
   if (tid < TT) {
     const int t = t0 + tid;
@@ -212,23 +213,25 @@ __global__ __launch_bounds__(256) void dz_keys_kernel(const float* keys, int64_t
   __syncthreads();
   const int v = v0 + 4 * lane;
   for (int grp = w; grp < TT / 8; grp += 4) {
+    // the 8 rows' keys, all loaded before any store: one range-checked
+    // resource per row spanning its ld keys (a dead row's range is empty, so
+    // its loads return zeros; columns V .. ld are masked below)
+    f32x4 xs[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int tl = grp * 8 + i;
+      const int nrec = __builtin_amdgcn_readfirstlane(r_c[tl] != 0.f ? (int)(ld * 4) : 0);
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(keys + (int64_t)(t0 + tl) * ld), (short)0, nrec, RSRC_WORD3);
+      xs[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, v * 4, 0, 0));
+    }
     OutT o[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int tl = grp * 8 + i, t = t0 + tl;
       const float c = r_c[tl], thr = r_thr[tl], nl = r_nl[tl];
       const int idt = r_idt[tl], y = r_y[tl];
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (c != 0.f) {  // live row (t < rows)
-        const float* kp = keys + (int64_t)t * ld;
-        if (v + 4 <= V) {
-          x = *(const f32x4*)(kp + v);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (v + e < V) x[e] = kp[v + e];
-        }
-      }
+      const f32x4 x = xs[i];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int vg = v + e;
