@@ -32,10 +32,12 @@ stce_status hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kDefaultChunk = 4096;   // forward rows per chunk
-// Default backward slice: the widest (multiple of 256) whose dz copies (token-
-// and vocab-major, 2 x T x V_s elements) fit in this many bytes.  Wider
-// slices mean fewer read-modify-write passes over the fp32 dH sum.
+// Default backward slice: the widest (multiple of 256) whose dz (T x V_s
+// elements for bf16 operands; twice that for fp32, which also keeps it
+// vocab-major) fits in this many bytes.  Wider slices mean fewer
+// read-modify-write passes over the fp32 dH sum.
 constexpr double kSliceBudgetBytes = 8e9;
+constexpr int64_t kMaxSlice = (1 << 22) - 256;  // vocabulary columns of a slice
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -91,10 +93,13 @@ Layout plan(const stce_problem* p) {
   L.f_sy = o;    o += L.nbuf * L.buf_sy;
   L.fwd = o;
 
+  // bf16 keeps dz vocab-major only (the hidden gradient reads it MN-major);
+  // fp32, whose products take K-major operands only, keeps it both ways
+  const bool bf = p->dtype == STCE_DT_BF16;
   if (p->vocab_slice > 0) {
     L.Vs = p->vocab_slice;
   } else {
-    const double per_col = 2.0 * (double)round_up(T, 64) * (double)es;
+    const double per_col = (bf ? 1.0 : 2.0) * (double)round_up(T, 64) * (double)es;
     int64_t fit = (int64_t)(kSliceBudgetBytes / per_col) / 256 * 256;
     if (fit < 4096) fit = 4096;
     // equal slices: ceil(V / fit) of them
@@ -102,13 +107,15 @@ Layout plan(const stce_problem* p) {
     L.Vs = round_up(ceil_div(V, n), 256);
   }
   if (L.Vs > V) L.Vs = V;
+  // a product's operand resource spans 256 rows of dz: keep them below 2^31 bytes
+  if (L.Vs > kMaxSlice) L.Vs = kMaxSlice;
   L.Vsp = round_up(L.Vs, 64);
   L.Tp = round_up(T, 64);
   o = 0;
   L.b_flags = o; o = align_up(o + 4 * (size_t)T);
   L.b_hT = o;    o = align_up(o + es * (size_t)H * L.Tp);
   L.b_WT = o;    o = align_up(o + es * (size_t)H * L.Vsp);
-  L.b_d = o;     o = align_up(o + es * (size_t)L.Tp * L.Vsp);
+  L.b_d = o;     o = align_up(o + (bf ? 0 : es * (size_t)L.Tp * L.Vsp));
   L.b_dT = o;    o = align_up(o + es * (size_t)L.Vsp * L.Tp);
   L.b_dh = o;    o = align_up(o + (p->dtype == STCE_DT_BF16 ? 4 * (size_t)T * H : 0));
   L.bwd = o;
@@ -180,7 +187,7 @@ FusedLayout plan_fused(const stce_problem* p, int64_t gmax = INT64_MAX) {
   L.part = o;  o += L.nbuf * L.buf_part;
   L.sy = o;    o += L.nbuf * L.buf_sy;
   L.g = o;     o = align_up(o + 4 * (size_t)L.C);
-  L.d = o;     o = align_up(o + es * (size_t)L.C * L.Vp);
+  L.d = o;     o = align_up(o + (p->dtype == STCE_DT_BF16 ? 0 : es * (size_t)L.C * L.Vp));
   L.dT = o;    o = align_up(o + es * (size_t)L.Vp * L.C * L.G);
   L.WT = o;    o = align_up(o + es * (size_t)H * L.Vp);
   L.hT = o;    o = align_up(o + es * (size_t)H * L.Tp);

@@ -221,7 +221,9 @@ struct EpiLogits {
 // does, re-derives support membership from the saved boundary, and writes
 //   dz[t, v] = c_t * (1[v == y_t] - exp(s - lse_S) * 1[v in S_t]),
 //   c_t = g_t / T_t on rows whose target is in support, else 0,
-// rounded to the operand type, both token-major (d) and vocab-major (dT).
+// rounded to the operand type, vocab-major (dT [v][t]: the weight gradient
+// reads it K-major, the hidden gradient MN-major).  The fp32 path, whose
+// products take K-major operands only, also writes it token-major (d).
 // Padding rows/columns (m >= Vs, n >= N, up to the padded sizes) get zeros.
 // ---------------------------------------------------------------------------
 template <class OutT>
@@ -230,21 +232,18 @@ struct EpiDlogits {
   const int64_t* target;   // [N]
   const RowState* st;      // [N]
   const float* g;          // [N]
-  OutT* d;                 // [N_pad][ld_d]
+  OutT* d;                 // [N_pad][ld_d] (fp32 only)
   int64_t ld_d;
   OutT* dT;                // [Vs_pad][ld_dT]
   int64_t ld_dT;
   int v0, Vs, Vs_pad, N, N_pad;
-  // bf16: the vocab-major copy is staged in LDS with rows padded to SROW
-  // elements (528 bytes), so the four quads of a wave, 4 rows apart, write
-  // distinct banks
-  static constexpr int SROW = GN + 8;
-  static constexpr int LDS_BYTES = sizeof(OutT) == 2 ? GM * SROW * 2 : 0;
+  // bf16: the vocab-major tile leaves through LDS in two passes of 128 rows
+  static constexpr int LDS_BYTES = sizeof(OutT) == 2 ? 128 * GN * 2 : 0;
 
-  __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem) const {
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
-    const int wmu = __builtin_amdgcn_readfirstlane(wm);
+  // fn(i, j, n, mm, v): the dz values v[0..3] of rows mm .. mm + 3 (block i)
+  // of column n (j), for the lane's columns below N_pad and rows below Vs_pad
+  template <class Fn>
+  __device__ inline void each(AccTile& acc, int m0, int n0, int wmu, int wn, int quad, int col, Fn&& fn) const {
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) {
       const int n = n0 + acc_col(wn, j, col);
@@ -266,7 +265,6 @@ struct EpiDlogits {
       const int idt = rs.id_thr;
       const float nl = -rs.lse_s * LOG2E;
       const bool live = c != 0.f;  // rows with c == 0 give exact zeros
-      OutT* dr = d + (int64_t)n * ld_d;
 #pragma unroll
       for (int i = 0; i < ACC_I; ++i) {
         // the wave's 16 rows base .. base + 15 (Vs_pad is a multiple of 64,
@@ -285,33 +283,49 @@ struct EpiDlogits {
           const float dv = c * ((vg == yy ? 1.f : 0.f) - q);
           v[e] = (OutT)((live && m < Vs) ? dv : 0.f);
         }
-        if constexpr (sizeof(OutT) == 2) {
-          // 8-byte store of the 4 rows (ld_d and mm are multiples of 4)
-          uint32_t p0 = (uint32_t)__builtin_bit_cast(uint16_t, v[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[1]) << 16);
-          uint32_t p1 = (uint32_t)__builtin_bit_cast(uint16_t, v[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, v[3]) << 16);
-          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-          *(u32x2*)(dr + mm) = u32x2{p0, p1};
-          // stage the vocab-major copy in LDS: [m - m0][n - n0]
-#pragma unroll
-          for (int e = 0; e < ACC_R; ++e) ((OutT*)smem)[(mm + e - m0) * SROW + (n - n0)] = v[e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < ACC_R; ++e) dr[mm + e] = v[e];
-#pragma unroll
-          for (int e = 0; e < ACC_R; ++e) dT[(int64_t)(mm + e) * ld_dT + n] = v[e];
-        }
+        fn(i, j, n, mm, v);
       }
     }
+  }
+
+  __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem) const {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
+    const int wmu = __builtin_amdgcn_readfirstlane(wm);
     if constexpr (sizeof(OutT) == 2) {
-      // every row/column of the staged tile that was not written above
-      // (m >= Vs_pad or n >= N_pad) is never copied out below
-      __syncthreads();
-      const int rows = min(GM, Vs_pad - m0), cols = min(GN, N_pad - n0);
-      for (int c16 = tid; c16 < GM * (GN / 8); c16 += GTHREADS) {
-        const int r = c16 / (GN / 8), cc = (c16 % (GN / 8)) * 8;
-        if (r < rows && cc < cols)
-          *(u32x4*)(dT + (int64_t)(m0 + r) * ld_dT + n0 + cc) = *(const u32x4*)((const OutT*)smem + r * SROW + cc);
+      // pass p stages rows p*128 .. +128 (the waves with wm == p) as 512-byte
+      // rows whose 16-byte chunk c sits at c ^ 2 ((r >> 2) & 3): the four
+      // quads of a wave's store (rows 4 apart) then hit distinct banks; then
+      // every thread copies out 16-byte row segments
+      OutT* stg = (OutT*)smem;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        if (wmu == p) {
+          each(acc, m0, n0, wmu, wn, quad, col, [&](int, int, int n, int mm, OutT(&v)[ACC_R]) {
+            const int nl = n - n0, r0 = mm - m0 - p * 128;  // r0 = i*16 + quad*4
+            const int pc = (nl >> 3) ^ (2 * quad);
+#pragma unroll
+            for (int e = 0; e < ACC_R; ++e) stg[(r0 + e) * GN + pc * 8 + (nl & 7)] = v[e];
+          });
+        }
+        __syncthreads();
+        const int rows = min(128, Vs_pad - m0 - p * 128), cols = min(GN, N_pad - n0);
+        for (int q = tid; q < 128 * (GN / 8); q += GTHREADS) {
+          const int r = q / (GN / 8), cc = q % (GN / 8);
+          if (r < rows && cc * 8 < cols)
+            *(u32x4*)(dT + (int64_t)(m0 + p * 128 + r) * ld_dT + n0 + cc * 8) =
+                *(const u32x4*)(stg + r * GN + ((cc ^ (2 * ((r >> 2) & 3))) * 8));
+        }
+        __syncthreads();
       }
+    } else {
+      each(acc, m0, n0, wmu, wn, quad, col, [&](int, int, int n, int mm, OutT(&v)[ACC_R]) {
+        OutT* dr = d + (int64_t)n * ld_d;
+#pragma unroll
+        for (int e = 0; e < ACC_R; ++e) dr[mm + e] = v[e];
+#pragma unroll
+        for (int e = 0; e < ACC_R; ++e) dT[(int64_t)(mm + e) * ld_dT + n] = v[e];
+      });
     }
   }
 };
@@ -382,6 +396,84 @@ struct EpiAccum {
               sum[o] = v;
           }
         }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Transposed forms, for products computed as C^T: C[m, n] goes to
+// out[n * ld + m].  The lane's 4 consecutive m of one n are contiguous there,
+// so every store is 16 bytes (8 for bf16).  M is a multiple of 4.
+// ---------------------------------------------------------------------------
+// Hidden-gradient accumulation (dH^T = W^T dz^T): sum[n, m] = (first ? 0 :
+// sum[n, m]) + acc; on the last slice the result goes to `out` (OutT).
+template <class OutT>
+struct EpiAccumT {
+  float* sum;  // [N][ld] fp32 running sum (may alias out when OutT is float)
+  int64_t ld;
+  OutT* out;   // [N][ld]
+  int M, N;
+  int first, last;
+  static constexpr int LDS_BYTES = 0;
+
+  __device__ inline void operator()(AccTile& acc, int m0, int n0, char*) const {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
+#pragma unroll
+    for (int j = 0; j < ACC_J; ++j) {
+      const int n = n0 + acc_col(wn, j, col);
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < ACC_I; ++i) {
+        const int m = m0 + acc_row(wm, i, 0, quad);
+        if (m >= M) continue;
+        const int64_t o = (int64_t)n * ld + m;
+        f32x4 v = acc[i][j];
+        if (!first) {
+          const f32x4 s0 = *(const f32x4*)(sum + o);
+          v[0] += s0[0];
+          v[1] += s0[1];
+          v[2] += s0[2];
+          v[3] += s0[3];
+        }
+        if (last) {
+          if constexpr (sizeof(OutT) == 2) {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const uint32_t p0 = (uint32_t)__builtin_bit_cast(uint16_t, (OutT)v[0]) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, (OutT)v[1]) << 16);
+            const uint32_t p1 = (uint32_t)__builtin_bit_cast(uint16_t, (OutT)v[2]) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, (OutT)v[3]) << 16);
+            *(u32x2*)(out + o) = u32x2{p0, p1};
+          } else {
+            *(f32x4*)(out + o) = v;
+          }
+        } else {
+          *(f32x4*)(sum + o) = v;
+        }
+      }
+    }
+  }
+};
+
+// Plain fp32 transposed store: out[n, m] = acc (split-K partials of dH^T).
+struct EpiStoreT {
+  float* out;
+  int64_t ld;
+  int M, N;
+  static constexpr int LDS_BYTES = 0;
+
+  __device__ inline void operator()(AccTile& acc, int m0, int n0, char*) const {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
+#pragma unroll
+    for (int j = 0; j < ACC_J; ++j) {
+      const int n = n0 + acc_col(wn, j, col);
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < ACC_I; ++i) {
+        const int m = m0 + acc_row(wm, i, 0, quad);
+        if (m < M) *(f32x4*)(out + (int64_t)n * ld + m) = acc[i][j];
+      }
     }
   }
 };

@@ -87,70 +87,184 @@ __device__ inline int lds_swz(int row) { return (row >> 1) & 7; }
 constexpr int WAIT_VM0_LGKM0 = 0x0070;
 
 // ---------------------------------------------------------------------------
-// bf16 main loop (MFMA)
+// bf16 main loop (MFMA).  Each operand is stored either K-major (X[r * ld + k],
+// the form above) or MN-major (X[k * ld + r]: rows of the tile along k).  An
+// MN-major operand spares the products of the backward a transposed copy:
+// the weight gradient reads dz and h as they are, the hidden gradient reads W.
+//
+// MN-major tile in LDS: 64 k-rows of 512 bytes (256 rows of the operand).
+// Its 32-byte chunks are XOR-permuted by f(k) = (k & 3) | ((k >> 3) & 1) << 2,
+// applied on the global side of the LDS loads (lane l of a load writes bytes
+// [16 l, 16 l + 16) of two consecutive k-rows).  Fragments come from the
+// transposing LDS read ds_read_b64_tr_b16: within a 16-lane group, lane L
+// receives element L % 4 of the 8-byte chunks addressed by lanes L / 4 + 4 j,
+// j < 4.  Lane c of group g addresses k-row kk*32 + g*8 + 4 r + c / 4 at
+// operand rows 4 (c % 4) .. +4 of the 16-row block, so lane L gets
+// rows L, k-rows kk*32 + g*8 + 4 r .. +4; the reads r = 0, 1 make the 8
+// k values of the MFMA operand.  Every 32 lanes of a read cover the 8 bank
+// groups of 32 bytes once (no conflicts).  Each k-tile builds a fresh buffer
+// resource at its first k-row, so offsets stay below 64 rows and rows past
+// the operand's k extent read as zeros; rows past M (N) read values whose
+// products land only in output rows the epilogues drop.
 // ---------------------------------------------------------------------------
-struct MainBf16 {
+__device__ inline int mn_swz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <bool A_MN, bool B_MN>
+struct MainBf16T {
   static constexpr int LDS_BYTES = 2 * 2 * GM * GK * 2;  // 2 stages x (A, B) x 32 KB
-  static constexpr int ROWB = GK * 2;                     // 128-byte tile rows
+  static constexpr int ROWB = GK * 2;                     // 128-byte K-major tile rows
+  static constexpr int MNROWB = GM * 2;                   // 512-byte MN-major tile rows
   static constexpr int TILEB = GM * ROWB;                 // one operand tile
   static constexpr int STAGEB = 2 * TILEB;
   static constexpr int LPW = 4;                           // 1 KB loads per wave per operand per k-tile
+  // LDS reads per k-step of 32: a K-major fragment is one 16-byte read, an
+  // MN-major one two transposing 8-byte reads
+  static constexpr int NRD = (A_MN ? 2 : 1) * ACC_I + (B_MN ? 2 : 1) * ACC_J;
   const bf16* A;
   int64_t lda;
   int M;  // rows of A that exist
   const bf16* B;
   int64_t ldb;
   int N;
-  int K;  // multiple of 8
+  int K;  // K-major operands: multiple of 8
+  int ka = 0, kb = 0;  // MN-major operands: k-rows that exist (0: K); lda, ldb < 2^24
 
-  __device__ inline void run(AccTile& acc, int m0, int n0, char* smem) const {
+  // the same product over k-columns dk .. K of this one (split-K)
+  __device__ inline void shift_k(int64_t dk) {
+    A += A_MN ? dk * lda : dk;
+    B += B_MN ? dk * ldb : dk;
+    const int ka0 = ka ? ka : K, kb0 = kb ? kb : K;
+    ka = max(ka0 - (int)dk, 0);
+    kb = max(kb0 - (int)dk, 0);
+    K -= (int)dk;
+    if (ka == 0) ka = -1;  // nothing left (0 would mean "K")
+    if (kb == 0) kb = -1;
+  }
+
+  // The two stages are distinct __shared__ objects (see the loop at the end
+  // of run for why).  Stage 0 doubles as the epilogue's LDS (at most 64 KB),
+  // so the product launches with no dynamic LDS.
+  static constexpr int DYN_LDS = 0;
+  static constexpr int EPI_LDS_MAX = STAGEB;
+  __device__ static char* stage0() {
+    __shared__ __attribute__((aligned(16))) char s0[STAGEB];
+    return s0;
+  }
+  __device__ static char* stage1() {
+    __shared__ __attribute__((aligned(16))) char s1[STAGEB];
+    return s1;
+  }
+  __device__ static char* epilogue_lds(char*) { return stage0(); }
+
+  __device__ inline void run(AccTile& acc, int m0, int n0, char*) const {
+    char* const S0 = stage0();
+    char* const S1 = stage1();
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases stay scalar
     const int wm = w >> 2, wn = w & 3;
-    // each resource spans only this tile's (at most 256) rows, so offsets
-    // stay far below 2^31 and the tail sentinel below is always out of range
+    const int kxa = ka ? ka : K, kxb = kb ? kb : K;
+    // K-major: each resource spans only this tile's (at most 256) rows, so
+    // offsets stay far below 2^31 and the tail sentinel below is always out
+    // of range
     const int rowsA = min(M - m0, GM), rowsB = min(N - n0, GN);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)m0 * lda), (short)0,
-                                                                        rowsA * (int)lda * 2, RSRC_WORD3);
+                                                                        A_MN ? 0 : rowsA * (int)lda * 2, RSRC_WORD3);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)(B + (int64_t)n0 * ldb), (short)0,
-                                                                        rowsB * (int)ldb * 2, RSRC_WORD3);
-    // load instruction i of wave w fills rows (w*LPW + i)*8 .. +8 of a tile;
-    // lane l covers row + l/8 and physical chunk l%8, i.e. logical chunk
-    // (l%8) ^ swz(row); the swizzle uses row bits 1..3, bit 3 being the
-    // parity of i
+                                                                        B_MN ? 0 : rowsB * (int)ldb * 2, RSRC_WORD3);
+    // K-major loads: instruction i of wave w fills rows (w*LPW + i)*8 .. +8
+    // of a tile; lane l covers row + l/8 and physical chunk l%8, i.e.
+    // logical chunk (l%8) ^ swz(row); the swizzle uses row bits 1..3, bit 3
+    // being the parity of i
     const int lrow = lane >> 3, lpc = lane & 7;
     const int ce = lpc ^ lds_swz(lrow), co = lpc ^ lds_swz(lrow + 8);
     const int rA = (w * LPW * 8 + lrow) * (int)lda * 2, rB = (w * LPW * 8 + lrow) * (int)ldb * 2;
     const int stepA = 8 * (int)lda * 2, stepB = 8 * (int)ldb * 2;
+    // MN-major loads: instruction i of wave w fills k-rows (w*LPW + i)*2 .. +2;
+    // lane l covers k-row + l/32, physical 32-byte chunk (l%32)/2, half l%2.
+    // The swizzle of those rows depends on i only through its parity, so
+    // instruction i takes the even or odd lane offset plus the scalar offset
+    // of rows (i & ~1) * 2
+    int mnoA[2], mnoB[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int kr = (w * LPW + i) * 2 + (lane >> 5);
+      const int col = ((((lane & 31) >> 1) ^ mn_swz(kr)) * 16 + (lane & 1) * 8) * 2;
+      mnoA[i] = kr * (int)lda * 2 + col;
+      mnoB[i] = kr * (int)ldb * 2 + col;
+    }
     const int nk = (K + GK - 1) / GK;
-    // loads of k-tile kt into stage kt % 2; 16-byte chunks at or past K get
-    // an offset beyond the buffer's range, which the hardware turns into zeros
-    auto issue = [&](int kt) __attribute__((always_inline)) {
-      char* st = smem + (kt & 1) * STAGEB + w * LPW * 1024;
+    // loads of k-tile kt into stage kt % 2; K-major 16-byte chunks at or past
+    // K get an offset beyond the buffer's range, which the hardware turns
+    // into zeros
+    auto issue = [&](int sg, int kt) __attribute__((always_inline)) {
+      char* st = (sg ? S1 : S0) + w * LPW * 1024;
       const int k0 = kt * GK, so = k0 * 2;
       const bool ine = k0 + ce * 8 < K, ino = k0 + co * 8 < K;
+      __amdgpu_buffer_rsrc_t rak = ra, rbk = rb;
+      // (the record counts are wave-uniform; readfirstlane keeps the
+      // resources in scalar registers)
+      if constexpr (A_MN)
+        rak = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(A + (int64_t)k0 * lda + m0), (short)0,
+            __builtin_amdgcn_readfirstlane(max(min(GK, kxa - k0), 0) * (int)lda * 2), RSRC_WORD3);
+      if constexpr (B_MN)
+        rbk = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(B + (int64_t)k0 * ldb + n0), (short)0,
+            __builtin_amdgcn_readfirstlane(max(min(GK, kxb - k0), 0) * (int)ldb * 2), RSRC_WORD3);
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const bool in = (i & 1) ? ino : ine;
         const int c16 = ((i & 1) ? co : ce) * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, STCE_LDS(st + i * 1024), 16, in ? rA + i * stepA + c16 : 0x7ffffff0,
-                                                 so, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, STCE_LDS(st + TILEB + i * 1024), 16,
-                                                 in ? rB + i * stepB + c16 : 0x7ffffff0, so, 0, 0);
+        if constexpr (A_MN)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rak, STCE_LDS(st + i * 1024), 16, mnoA[i & 1],
+                                                   (i & ~1) * 4 * (int)lda, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, STCE_LDS(st + i * 1024), 16,
+                                                   in ? rA + i * stepA + c16 : 0x7ffffff0, so, 0, 0);
+        if constexpr (B_MN)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rbk, STCE_LDS(st + TILEB + i * 1024), 16, mnoB[i & 1],
+                                                   (i & ~1) * 4 * (int)ldb, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, STCE_LDS(st + TILEB + i * 1024), 16,
+                                                   in ? rB + i * stepB + c16 : 0x7ffffff0, so, 0, 0);
       }
     };
-    // fragment of a 16 x 32 (rows x k) block: lane l reads row l % 16, the
-    // 16-byte chunk l / 16 of the k-step's 32 columns
+    // K-major fragment of a 16 x 32 (rows x k) block: lane l reads row
+    // l % 16, the 16-byte chunk l / 16 of the k-step's 32 columns
     const int frow = lane & 15, fq = lane >> 4, sw = lds_swz(frow);
     const int offA = (wm * 128 + frow) * ROWB, offB = TILEB + (wn * 64 + frow) * ROWB;
+    // MN-major fragment: lane (g, c) = (lane / 16, lane % 16) reads k-row
+    // g*8 + c/4 (+ 32 kk + 4 r) at chunk (block ^ f), byte 8 (c % 4)
+    const int fz = (frow >> 2) | ((fq & 1) << 2);
+    const int mnrow = (fq * 8 + (frow >> 2)) * MNROWB + (frow & 3) * 8;
+    const int xbA = wm * 8, xbB = wn * 4;  // first 32-byte chunk of the wave's rows
+    auto rd_mn = [&](const char* base, int x, int kk) __attribute__((always_inline)) {
+      const char* p = base + mnrow + kk * 32 * MNROWB + ((x ^ fz) * 32);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)STCE_LDS(p));
+      const s16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)STCE_LDS(p + 4 * MNROWB));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
     bf16x8 fa[2][ACC_I], fb[2][ACC_J];
-    auto rd = [&](bf16x8 (&a)[ACC_I], bf16x8 (&b)[ACC_J], int kt, int kk) __attribute__((always_inline)) {
-      const char* st = smem + (kt & 1) * STAGEB;
+    auto rd = [&](int sg, bf16x8 (&a)[ACC_I], bf16x8 (&b)[ACC_J], int kk) __attribute__((always_inline)) {
+      const char* st = sg ? S1 : S0;
       const int ch = ((kk * 4 + fq) ^ sw) * 16;
 #pragma unroll
-      for (int i = 0; i < ACC_I; ++i) a[i] = *(const bf16x8*)(st + offA + i * 16 * ROWB + ch);
+      for (int i = 0; i < ACC_I; ++i) {
+        if constexpr (A_MN)
+          a[i] = rd_mn(st, xbA + i, kk);
+        else
+          a[i] = *(const bf16x8*)(st + offA + i * 16 * ROWB + ch);
+      }
 #pragma unroll
-      for (int j = 0; j < ACC_J; ++j) b[j] = *(const bf16x8*)(st + offB + j * 16 * ROWB + ch);
+      for (int j = 0; j < ACC_J; ++j) {
+        if constexpr (B_MN)
+          b[j] = rd_mn(st + TILEB, xbB + j, kk);
+        else
+          b[j] = *(const bf16x8*)(st + offB + j * 16 * ROWB + ch);
+      }
     };
     auto mma = [&](int cur, int i0, int i1) __attribute__((always_inline)) {
 #pragma unroll
@@ -159,18 +273,23 @@ struct MainBf16 {
         for (int j = 0; j < ACC_J; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
     };
-    // one k-tile; NEXT: a tile follows (barrier + its first fragments),
-    // ISSUE: the tile after that is loaded into the stage this one frees
-    auto tile = [&](int kt, auto next_c, auto issue_c) __attribute__((always_inline)) {
+    // MFMAs per LDS read in the two interleaved stretches (24 MFMAs each,
+    // then 8 more in the first), and the number of reads they interleave
+    constexpr int P = NRD <= 12 ? 2 : 1;
+    constexpr int Q = NRD < 24 / P ? NRD : 24 / P;
+    // one k-tile, held in stage sg; NEXT: a tile follows (barrier + its
+    // first fragments, from the other stage), ISSUE: the tile after that is
+    // loaded into the stage this one frees
+    auto tile = [&](int sg, int kt, auto next_c, auto issue_c) __attribute__((always_inline)) {
       constexpr bool NEXT = decltype(next_c)::value, ISSUE = decltype(issue_c)::value;
-      rd(fa[1], fb[1], kt, 1);
+      rd(sg, fa[1], fb[1], 1);
       mma(0, 0, ACC_I);
 #pragma unroll
-      for (int q = 0; q < ACC_I + ACC_J; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMA
+      for (int q = 0; q < Q; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, P, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, ACC_I * ACC_J - 2 * (ACC_I + ACC_J), 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, ACC_I * ACC_J - P * Q, 0);
       mma(1, 0, 2);
       __builtin_amdgcn_sched_barrier(0);
       if (NEXT) {
@@ -179,36 +298,59 @@ struct MainBf16 {
         __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        rd(fa[0], fb[0], kt + 1, 0);
-        if (ISSUE) issue(kt + 2);
+        rd(1 - sg, fa[0], fb[0], 0);
+        if (ISSUE) issue(sg, kt + 2);
       }
       mma(1, 2, ACC_I);
       if (NEXT) {
 #pragma unroll
-        for (int q = 0; q < ACC_I + ACC_J; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        for (int q = 0; q < Q; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, P, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           if (ISSUE && q < 2 * LPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
+        if constexpr ((ACC_I - 2) * ACC_J > P * Q)
+          __builtin_amdgcn_sched_group_barrier(0x008, (ACC_I - 2) * ACC_J - P * Q, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    issue(0);
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    issue(0, 0);
     __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
     __syncthreads();
-    rd(fa[0], fb[0], 0, 0);
-    if (1 < nk) issue(1);
-    int kt = 0;
-    for (; kt + 2 < nk; ++kt) tile(kt, std::true_type{}, std::true_type{});
-    if (kt + 1 < nk) {
-      tile(kt, std::true_type{}, std::false_type{});
-      ++kt;
+    rd(0, fa[0], fb[0], 0);
+    if constexpr (A_MN || B_MN) {
+      // an even number of k-tiles (an odd count gets one more, all zeros: its
+      // loads fall past K), so that tile kt's stage kt % 2 is a constant at
+      // every read and load: the compiler then sees that the transposing
+      // reads of one stage do not alias the loads in flight into the other
+      // and adds no wait for them.  Pairs while a tile two ahead exists, then
+      // the last two.
+      const int nk2 = (nk + 1) & ~1;
+      issue(1, 1);
+      int kt = 0;
+      for (; kt + 2 < nk2; kt += 2) {
+        tile(0, kt, T_{}, T_{});
+        tile(1, kt + 1, T_{}, T_{});
+      }
+      tile(0, kt, T_{}, F_{});
+      tile(1, kt + 1, F_{}, F_{});
+    } else {
+      if (1 < nk) issue(1, 1);
+      int kt = 0;
+      for (; kt + 2 < nk; ++kt) tile(kt & 1, kt, T_{}, T_{});
+      if (kt + 1 < nk) {
+        tile(kt & 1, kt, T_{}, F_{});
+        ++kt;
+      }
+      tile(kt & 1, kt, F_{}, F_{});
     }
-    tile(kt, std::false_type{}, std::false_type{});
     __syncthreads();  // the epilogue may reuse the LDS
   }
 };
+using MainBf16 = MainBf16T<false, false>;
 
 // ---------------------------------------------------------------------------
 // fp32 main loop (plain fused multiply-adds, same accumulator layout).  Used
@@ -218,6 +360,9 @@ struct MainBf16 {
 struct MainF32 {
   static constexpr int BK = 16;
   static constexpr int LDS_BYTES = 2 * GM * (BK + 1) * 4;
+  static constexpr int DYN_LDS = LDS_BYTES;  // dynamic LDS, shared with the epilogue
+  static constexpr int EPI_LDS_MAX = 160 * 1024;
+  __device__ static char* epilogue_lds(char* dyn) { return dyn; }
   const float* A;
   int64_t lda;
   int M;
@@ -225,6 +370,13 @@ struct MainF32 {
   int64_t ldb;
   int N;
   int K;  // multiple of 4
+
+  // the same product over k-columns dk .. K of this one (split-K)
+  __device__ inline void shift_k(int64_t dk) {
+    A += dk;
+    B += dk;
+    K -= (int)dk;
+  }
 
   __device__ inline void run(AccTile& acc, int m0, int n0, char* smem) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -267,6 +419,14 @@ struct MainF32 {
   }
 };
 
+// Dynamic LDS of a product: the main loop's when it takes dynamic LDS (the
+// epilogue then shares it), else the epilogue reuses the main loop's stage 0.
+template <class Main, class Epi>
+constexpr int gemm_dyn_lds() {
+  static_assert(Epi::LDS_BYTES <= Main::EPI_LDS_MAX, "epilogue LDS exceeds what the main loop leaves it");
+  return Main::DYN_LDS ? (Main::DYN_LDS > Epi::LDS_BYTES ? Main::DYN_LDS : Epi::LDS_BYTES) : 0;
+}
+
 template <class Main, class Epi>
 __global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(Main mainloop, Epi epi, TileMap map) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -278,7 +438,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(Main mainloop, Epi ep
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) acc[i][j] = f32x4{};
   mainloop.run(acc, tm * GM, tn * GN, smem);
-  epi(acc, tm * GM, tn * GN, smem);
+  epi(acc, tm * GM, tn * GN, Main::epilogue_lds(smem));
 }
 
 }  // namespace stce

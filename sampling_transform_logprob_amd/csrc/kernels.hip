@@ -176,9 +176,9 @@ __global__ void tile_partials_kernel(const float* s, int64_t ld, int64_t R, int6
 // value, exp2 argument, coefficient and rounding), so every value is the one
 // the recompute backward forms from the same keys.  Block: TT rows x 256
 // columns; lane l of a wave takes columns 4l .. 4l+3 of 8 rows at a time,
-// writes them token-major and stages them in LDS, from where the
-// vocab-major copy leaves as 16-byte row segments.  Rows rows .. rows_pad
-// and columns V .. V_pad get zeros.
+// writes them token-major when d is not null (the fp32 path) and stages
+// them in LDS, from where the vocab-major copy leaves as 16-byte row
+// segments.  Rows rows .. rows_pad and columns V .. V_pad get zeros.
 template <class OutT>
 __global__ __launch_bounds__(256) void dz_keys_kernel(const float* keys, int64_t ld, const float* temp,
                                                       const int64_t* target, const RowState* st, const float* g,
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256) void dz_keys_kernel(const float* keys, int64_t
         const float dv = c * ((vg == y ? 1.f : 0.f) - q);
         o[i][e] = (OutT)((c != 0.f && vg < V) ? dv : 0.f);
       }
-      if (t < rows_pad && v < V_pad) {
+      if (d && t < rows_pad && v < V_pad) {
         OutT* dp = d + (int64_t)t * ld_d + v;
         if constexpr (sizeof(OutT) == 2) {
           typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -276,19 +276,18 @@ __global__ __launch_bounds__(256) void dz_keys_kernel(const float* keys, int64_t
 
 // Split-K product: workgroup b computes tile b % tiles over the reduction
 // range [split * ks, min(K, (split + 1) * ks)), split = b / tiles, and
-// stores it (fp32) into partial buffer `split`.
-template <class Main>
-__global__ __launch_bounds__(GTHREADS, 1) void gemm_splitk_kernel(Main mainloop, EpiStore epi, TileMap map, int tiles,
+// stores it (fp32, through the epilogue) into partial buffer `split`.
+template <class Main, class Epi>
+__global__ __launch_bounds__(GTHREADS, 1) void gemm_splitk_kernel(Main mainloop, Epi epi, TileMap map, int tiles,
                                                                  int64_t ks, int64_t pstride) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int split = blockIdx.x / tiles;
   int tm, tn;
   map.get(blockIdx.x - split * tiles, tm, tn);
   Main mn = mainloop;
-  mn.A += split * ks;
-  mn.B += split * ks;
-  mn.K = (int)min((int64_t)mainloop.K - split * ks, ks);
-  EpiStore ep = epi;
+  mn.shift_k(split * ks);
+  if (mn.K > ks) mn.K = (int)ks;
+  Epi ep = epi;
   ep.out += split * pstride;
   AccTile acc;
 #pragma unroll
@@ -296,7 +295,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_splitk_kernel(Main mainloop,
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) acc[i][j] = f32x4{};
   mn.run(acc, tm * GM, tn * GN, smem);
-  ep(acc, tm * GM, tn * GN, smem);
+  ep(acc, tm * GM, tn * GN, Main::epilogue_lds(smem));
 }
 
 // out[i] = part[0][i] + part[1][i] + ... in split order, 4 elements a thread.
@@ -329,7 +328,7 @@ template <class Main, class Epi>
 hipError_t launch_gemm(const Main& mn, const Epi& ep, int64_t tiles_m, int64_t tiles_n, hipStream_t s) {
   if (tiles_m <= 0 || tiles_n <= 0) return hipSuccess;
   auto kern = gemm_kernel<Main, Epi>;
-  constexpr int lds = Main::LDS_BYTES > Epi::LDS_BYTES ? Main::LDS_BYTES : Epi::LDS_BYTES;
+  constexpr int lds = gemm_dyn_lds<Main, Epi>();
   static_assert(lds <= 160 * 1024, "LDS budget");
   static const hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
@@ -338,12 +337,12 @@ hipError_t launch_gemm(const Main& mn, const Epi& ep, int64_t tiles_m, int64_t t
   return hipGetLastError();
 }
 
-template <class Main>
-hipError_t launch_gemm_splitk(const Main& mn, const EpiStore& ep, int64_t tiles_m, int64_t tiles_n, int splits,
+template <class Main, class Epi>
+hipError_t launch_gemm_splitk(const Main& mn, const Epi& ep, int64_t tiles_m, int64_t tiles_n, int splits,
                               int64_t ks, int64_t pstride, hipStream_t s) {
   if (tiles_m <= 0 || tiles_n <= 0 || splits <= 0) return hipSuccess;
-  auto kern = gemm_splitk_kernel<Main>;
-  constexpr int lds = Main::LDS_BYTES;
+  auto kern = gemm_splitk_kernel<Main, Epi>;
+  constexpr int lds = gemm_dyn_lds<Main, Epi>();
   static_assert(lds <= 160 * 1024, "LDS budget");
   static const hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
@@ -473,8 +472,46 @@ hipError_t bwd_slice_impl(const BwdSliceArgs& a, hipStream_t s) {
 }
 }  // namespace
 
+// bf16 slice: dz is kept vocab-major only; the weight gradient reads it
+// K-major, the hidden gradient is formed transposed (dH^T = W^T dz^T) and
+// reads it MN-major, so no token-major copy is written.
+hipError_t bwd_slice_bf16(const BwdSliceArgs& a, hipStream_t s) {
+  hipError_t e;
+  const bf16* W = (const bf16*)a.W;
+  const bf16* dT = (const bf16*)a.dT;
+  // 1. recompute the slice's keys and form dz^T [vsp][Tp]
+  {
+    EpiDlogits<bf16> ep{a.temp, a.target, a.st, a.g, nullptr, 0, (bf16*)a.dT, a.Tp,
+                        (int)a.v0, (int)a.vs, (int)a.vsp, (int)a.T, (int)a.Tp};
+    MainBf16 mn{W + a.v0 * a.H, a.H, (int)a.vs, (const bf16*)a.h, a.H, (int)a.T, (int)a.H};
+    ProfScope ps(4, s);
+    e = launch_gemm(mn, ep, ceil_div(a.vsp, GM), ceil_div(a.Tp, GN), s);
+    if (e != hipSuccess) return e;
+  }
+  // 2. weight gradient of the slice: dW[v0 + m, :] = dz^T[m, :] . h^T
+  if (a.grad_weight) {
+    EpiStore ep{a.grad_weight + a.v0 * a.H, a.H, (int)a.vs, (int)a.H, a.accumulate_w};
+    MainBf16 mn{dT, a.Tp, (int)a.vsp, (const bf16*)a.hT, a.Tp, (int)a.H, (int)a.Tp};
+    ProfScope ps(5, s);
+    e = launch_gemm(mn, ep, ceil_div(a.vsp, GM), ceil_div(a.H, GN), s);
+    if (e != hipSuccess) return e;
+  }
+  // 3. hidden gradient, summed over slices in order: dH^T += W_slice^T . dz_slice^T,
+  //    with dz^T as an MN-major operand (k = vocabulary rows of the slice)
+  if (a.grad_hidden) {
+    e = launch_transpose_bf16(W + a.v0 * a.H, a.H, a.vs, a.H, (bf16*)a.WT, a.ld_d, a.vsp, s);
+    if (e != hipSuccess) return e;
+    EpiAccumT<bf16> ep{a.dh_sum, a.H, (bf16*)a.grad_hidden, (int)a.H, (int)a.T, a.first, a.last};
+    MainBf16T<false, true> mn{(const bf16*)a.WT, a.ld_d, (int)a.H, dT, a.Tp, (int)a.T, (int)a.vsp, 0, (int)a.vs};
+    ProfScope ps(6, s);
+    e = launch_gemm(mn, ep, ceil_div(a.H, GM), ceil_div(a.T, GN), s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_bwd_slice(const BwdSliceArgs& a, hipStream_t s) {
-  if (a.dtype == 1) return bwd_slice_impl<bf16, MainBf16>(a, s);
+  if (a.dtype == 1) return bwd_slice_bf16(a, s);
   return bwd_slice_impl<float, MainF32>(a, s);
 }
 
@@ -482,22 +519,30 @@ namespace {
 template <class E, class Main>
 hipError_t fused_grads_impl(const FusedGradArgs& a, hipStream_t s) {
   hipError_t e;
-  // 1. dz of the chunk, token-major d [rows_pad][V_pad] and vocab-major dT
-  //    [V_pad][rows_pad]
+  // 1. dz of the chunk, vocab-major into the group's dT [V_pad][ld_dT] and
+  //    (fp32 only) token-major d [rows_pad][V_pad]
   {
     constexpr int TT = sizeof(E) == 2 ? 64 : 32;
     ProfScope ps(10, s);
     hipLaunchKernelGGL(dz_keys_kernel<E>, dim3((unsigned)ceil_div(a.V_pad, 256), (unsigned)ceil_div(a.rows_pad, TT)),
                        dim3(256), 0, s, a.keys, a.ld_keys, a.temp, a.target, a.st, a.g, (int)a.rows, (int)a.rows_pad,
-                       (int)a.V, (int)a.V_pad, (E*)a.d, a.V_pad, (E*)a.dT + a.dT_col, a.ld_dT);
+                       (int)a.V, (int)a.V_pad, sizeof(E) == 2 ? nullptr : (E*)a.d, a.V_pad, (E*)a.dT + a.dT_col,
+                       a.ld_dT);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // 2. the chunk's hidden-gradient rows: dH = dz . W over vocabulary splits,
-  //    fp32 partials, then their sum in split order
+  // 2. the chunk's hidden-gradient rows over vocabulary splits, fp32
+  //    partials, then their sum in split order; bf16 forms them transposed,
+  //    dH^T = W^T . dz^T, reading the chunk's columns of dT MN-major
   if (a.grad_hidden) {
-    Main mn{(const E*)a.d, a.V_pad, (int)a.rows, (const E*)a.WT, a.V_pad, (int)a.H, (int)a.V_pad};
-    EpiStore ep{a.dh_part, a.H, (int)a.rows, (int)a.H, 0};
-    {
+    if constexpr (sizeof(E) == 2) {
+      MainBf16T<false, true> mn{(const bf16*)a.WT, a.V_pad, (int)a.H, (const bf16*)a.dT + a.dT_col, a.ld_dT,
+                                (int)a.rows, (int)a.V_pad, 0, (int)a.V_pad};
+      EpiStoreT ep{a.dh_part, a.H, (int)a.H, (int)a.rows};
+      ProfScope ps(6, s);
+      e = launch_gemm_splitk(mn, ep, ceil_div(a.H, GM), ceil_div(a.rows, GN), a.splits, a.ks, a.rows * a.H, s);
+    } else {
+      Main mn{(const E*)a.d, a.V_pad, (int)a.rows, (const E*)a.WT, a.V_pad, (int)a.H, (int)a.V_pad};
+      EpiStore ep{a.dh_part, a.H, (int)a.rows, (int)a.H, 0};
       ProfScope ps(6, s);
       e = launch_gemm_splitk(mn, ep, ceil_div(a.rows, GM), ceil_div(a.H, GN), a.splits, a.ks, a.rows * a.H, s);
     }
