@@ -311,13 +311,13 @@ stce_status stce_policy_loss(const stce_pg_params *pg, int64_t T, const float *l
  * step's own state marks inactive rows).  The chunk size is
  * prob->chunk_rows rounded up to a multiple of 64 (default 4096); the
  * workspace (256-byte aligned device memory, stce_fused_workspace_bytes;
- * 12.1 GB at T = 16384, H = 5120, V = 151936, 8.4 GB at its minimum) holds
+ * 11.9 GB at T = 16384, H = 5120, V = 151936, 8.2 GB at its minimum) holds
  * the fp32 keys of two chunks (a chunk's selection runs on a side stream of
  * the library's while the next chunk is projected, joined by event waits as
  * in stce_forward), the group's vocab-major dz (with bf16 operands the only
  * copy: the hidden gradient is formed transposed and reads it as it is; fp32
- * also keeps a chunk's token-major copy), the transposed weight and hidden,
- * and the split partials.  A workspace between *min_bytes (one
+ * also keeps a chunk's token-major copy), the transposed weight (and for
+ * fp32 the transposed hidden), and the split partials.  A workspace between *min_bytes (one
  * chunk per group) and *bytes keeps as many chunks per group as it holds;
  * the grouping changes only the order of dW's fp32 sums.  Host errors as stce_forward, stce_backward and
  * stce_policy_loss, and V must be below 2^29 (the chunk's key rows are read

@@ -113,7 +113,7 @@ Layout plan(const stce_problem* p) {
   L.Tp = round_up(T, 64);
   o = 0;
   L.b_flags = o; o = align_up(o + 4 * (size_t)T);
-  L.b_hT = o;    o = align_up(o + es * (size_t)H * L.Tp);
+  L.b_hT = o;    o = align_up(o + (bf ? 0 : es * (size_t)H * L.Tp));
   L.b_WT = o;    o = align_up(o + es * (size_t)H * L.Vsp);
   L.b_d = o;     o = align_up(o + (bf ? 0 : es * (size_t)L.Tp * L.Vsp));
   L.b_dT = o;    o = align_up(o + es * (size_t)L.Vsp * L.Tp);
@@ -190,7 +190,7 @@ FusedLayout plan_fused(const stce_problem* p, int64_t gmax = INT64_MAX) {
   L.d = o;     o = align_up(o + (p->dtype == STCE_DT_BF16 ? 0 : es * (size_t)L.C * L.Vp));
   L.dT = o;    o = align_up(o + es * (size_t)L.Vp * L.C * L.G);
   L.WT = o;    o = align_up(o + es * (size_t)H * L.Vp);
-  L.hT = o;    o = align_up(o + es * (size_t)H * L.Tp);
+  L.hT = o;    o = align_up(o + (p->dtype == STCE_DT_BF16 ? 0 : es * (size_t)H * L.Tp));
   L.dhp = o;   o = align_up(o + 4 * (size_t)L.S * L.C * H);
   L.total = o;
   return L;
@@ -404,12 +404,10 @@ stce_status stce_backward(const stce_problem* p, const float* grad_logprob, cons
       return hip_fail(e, "validate");
   }
   if (!grad_hidden && !grad_weight) return STCE_OK;
-  if (grad_weight) {
-    if (p->dtype == STCE_DT_BF16)
-      e = launch_transpose_bf16((const bf16*)p->hidden, p->H, p->T, p->H, at<bf16>(ws, L.b_hT), L.Tp, L.Tp, st);
-    else
-      e = launch_transpose_f32((const float*)p->hidden, p->H, p->T, p->H, at<float>(ws, L.b_hT), L.Tp, L.Tp, st);
-    if (e) return hip_fail(e, "transpose hidden");
+  if (grad_weight && p->dtype != STCE_DT_BF16) {
+    // the fp32 products take K-major operands only (bf16 reads h as it is)
+    if ((e = launch_transpose_f32((const float*)p->hidden, p->H, p->T, p->H, at<float>(ws, L.b_hT), L.Tp, L.Tp, st)))
+      return hip_fail(e, "transpose hidden");
   }
   const int64_t nsl = ceil_div(p->V, L.Vs);
   for (int64_t si = 0; si < nsl; ++si) {
@@ -586,12 +584,10 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
       e = launch_transpose_f32((const float*)p->weight, p->H, p->V, p->H, at<float>(ws, L.WT), L.Vp, L.Vp, st);
     if (e) return hip_fail(e, "transpose weight");
   }
-  if (grad_weight) {
-    if (p->dtype == STCE_DT_BF16)
-      e = launch_transpose_bf16((const bf16*)p->hidden, p->H, p->T, p->H, at<bf16>(ws, L.hT), L.Tp, L.Tp, st);
-    else
-      e = launch_transpose_f32((const float*)p->hidden, p->H, p->T, p->H, at<float>(ws, L.hT), L.Tp, L.Tp, st);
-    if (e) return hip_fail(e, "transpose hidden");
+  if (grad_weight && p->dtype != STCE_DT_BF16) {
+    // fp32 products take K-major operands only (bf16 reads h as it is)
+    if ((e = launch_transpose_f32((const float*)p->hidden, p->H, p->T, p->H, at<float>(ws, L.hT), L.Tp, L.Tp, st)))
+      return hip_fail(e, "transpose hidden");
   }
   const int64_t nch = ceil_div(p->T, L.C);
   SideCtx* side = nullptr;
@@ -680,6 +676,8 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
     ga.dT_col = (c % L.G) * L.C;
     ga.WT = at<char>(ws, L.WT);
     ga.hT = at<char>(ws, L.hT);
+    ga.h = p->hidden;
+    ga.T = p->T;
     ga.dh_part = at<float>(ws, L.dhp);
     ga.splits = (int)L.S;
     ga.ks = L.ks;

@@ -473,8 +473,9 @@ hipError_t bwd_slice_impl(const BwdSliceArgs& a, hipStream_t s) {
 }  // namespace
 
 // bf16 slice: dz is kept vocab-major only; the weight gradient reads it
-// K-major, the hidden gradient is formed transposed (dH^T = W^T dz^T) and
-// reads it MN-major, so no token-major copy is written.
+// K-major (and h MN-major), the hidden gradient is formed transposed
+// (dH^T = W^T dz^T) and reads it MN-major, so neither a token-major copy of
+// dz nor a transposed h is written.
 hipError_t bwd_slice_bf16(const BwdSliceArgs& a, hipStream_t s) {
   hipError_t e;
   const bf16* W = (const bf16*)a.W;
@@ -488,10 +489,11 @@ hipError_t bwd_slice_bf16(const BwdSliceArgs& a, hipStream_t s) {
     e = launch_gemm(mn, ep, ceil_div(a.vsp, GM), ceil_div(a.Tp, GN), s);
     if (e != hipSuccess) return e;
   }
-  // 2. weight gradient of the slice: dW[v0 + m, :] = dz^T[m, :] . h^T
+  // 2. weight gradient of the slice: dW[v0 + m, :] = sum_t dz^T[m, t] h[t, :],
+  //    h read as it is (MN-major, k = token; rows past T read 0)
   if (a.grad_weight) {
     EpiStore ep{a.grad_weight + a.v0 * a.H, a.H, (int)a.vs, (int)a.H, a.accumulate_w};
-    MainBf16 mn{dT, a.Tp, (int)a.vsp, (const bf16*)a.hT, a.Tp, (int)a.H, (int)a.Tp};
+    MainBf16T<false, true> mn{dT, a.Tp, (int)a.vsp, (const bf16*)a.h, a.H, (int)a.H, (int)a.Tp, 0, (int)a.T};
     ProfScope ps(5, s);
     e = launch_gemm(mn, ep, ceil_div(a.vsp, GM), ceil_div(a.H, GN), s);
     if (e != hipSuccess) return e;
@@ -556,10 +558,17 @@ hipError_t fused_grads_impl(const FusedGradArgs& a, hipStream_t s) {
   // 3. weight gradient of a finished group: dW (+)= dz^T . h over the
   //    group's rows (zero dT columns for the padding rows)
   if (a.grad_weight && a.dw) {
-    Main mn{(const E*)a.dT, a.ld_dT, (int)a.V, (const E*)a.hT + a.dw_c0, a.Tp, (int)a.H, (int)a.dw_k};
     EpiStore ep{a.grad_weight, a.H, (int)a.V, (int)a.H, a.accumulate_w};
     ProfScope ps(5, s);
-    e = launch_gemm(mn, ep, ceil_div(a.V, GM), ceil_div(a.H, GN), s);
+    if constexpr (sizeof(E) == 2) {
+      // h read as it is (MN-major): rows dw_c0 .. of the T that exist
+      MainBf16T<false, true> mn{(const bf16*)a.dT, a.ld_dT, (int)a.V, (const bf16*)a.h + a.dw_c0 * a.H, a.H,
+                                (int)a.H, (int)a.dw_k, 0, (int)(a.T - a.dw_c0)};
+      e = launch_gemm(mn, ep, ceil_div(a.V, GM), ceil_div(a.H, GN), s);
+    } else {
+      Main mn{(const E*)a.dT, a.ld_dT, (int)a.V, (const E*)a.hT + a.dw_c0, a.Tp, (int)a.H, (int)a.dw_k};
+      e = launch_gemm(mn, ep, ceil_div(a.V, GM), ceil_div(a.H, GN), s);
+    }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

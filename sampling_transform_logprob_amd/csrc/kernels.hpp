@@ -98,7 +98,9 @@ struct FusedGradArgs {
   void* dT;             // [V_pad][ld_dT] scratch: the group's vocab-major dz; this chunk's at column dT_col
   int64_t ld_dT, dT_col;
   const void* WT;       // [H][V_pad] transposed weight (zero columns V .. V_pad)
-  const void* hT;       // [H][Tp] transposed hidden
+  const void* h;        // [T][H] hidden (bf16: read MN-major)
+  const void* hT;       // [H][Tp] transposed hidden (fp32)
+  int64_t T;
   float* dh_part;       // [splits][rows][H] scratch
   int splits;
   int64_t ks;           // vocabulary columns per split (multiple of 64)

@@ -143,7 +143,7 @@ def test_fused_workspace_is_host_computable_and_chunk_bounded(lib):
     assert n < per_chunk + groups + 2 * H * Vp + 2 * H * 100032 + 16 * 4 * 512 * H + 100000 * 4 + 16 * 4096
     big = _prob(T=16384, H=5120, V=151936)
     nb, _ = binding.fused_workspace_bytes(big)
-    assert 12e9 < nb < 12.2e9      # keys 2 x 2.5 GB, vocab-major dz 5 GB, transposed weight 1.6 GB, ...
+    assert 11.8e9 < nb < 12.1e9    # keys 2 x 2.5 GB, vocab-major dz 5 GB, transposed weight 1.6 GB, ...
     # the minimum keeps one chunk per weight-gradient group
     assert nmin == n - 2 * Vp * 512 * (-(-100000 // 512) - 1)
     n2 = binding.fused_workspace_bytes(_prob(T=100000, chunk_rows=100))[1]   # rounded up to 128 rows
