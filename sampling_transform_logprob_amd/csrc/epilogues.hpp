@@ -89,7 +89,7 @@ struct EpiLogits {
   int want_ent;            // store the per-tile sum of exp(s - max) (s - max)
   static constexpr int LDS_BYTES = 2 * GN * 4 * 4;  // cross-wave merge
 
-  __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem) const {
+  __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem, char*) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
     const int mb = m0 + wm * 128;
@@ -237,7 +237,8 @@ struct EpiDlogits {
   OutT* dT;                // [Vs_pad][ld_dT]
   int64_t ld_dT;
   int v0, Vs, Vs_pad, N, N_pad;
-  // bf16: the vocab-major tile leaves through LDS in two passes of 128 rows
+  // bf16: the vocab-major tile leaves through LDS, 128 rows in each of the
+  // two epilogue buffers
   static constexpr int LDS_BYTES = sizeof(OutT) == 2 ? 128 * GN * 2 : 0;
 
   // fn(i, j, n, mm, v): the dz values v[0..3] of rows mm .. mm + 3 (block i)
@@ -288,35 +289,31 @@ struct EpiDlogits {
     }
   }
 
-  __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem) const {
+  __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem, char* smem1) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
     const int wmu = __builtin_amdgcn_readfirstlane(wm);
     if constexpr (sizeof(OutT) == 2) {
-      // pass p stages rows p*128 .. +128 (the waves with wm == p) as 512-byte
-      // rows whose 16-byte chunk c sits at c ^ 2 ((r >> 2) & 3): the four
-      // quads of a wave's store (rows 4 apart) then hit distinct banks; then
-      // every thread copies out 16-byte row segments
-      OutT* stg = (OutT*)smem;
+      // rows 0 .. 127 of the tile (the waves with wm == 0) are staged in the
+      // first buffer, rows 128 .. 255 in the second, as 512-byte rows whose
+      // 16-byte chunk c sits at c ^ 2 ((r >> 2) & 3): the four quads of a
+      // wave's store (rows 4 apart) then hit distinct banks; then every
+      // thread copies out 16-byte row segments
+      OutT* stg = (OutT*)(wmu ? smem1 : smem);
+      each(acc, m0, n0, wmu, wn, quad, col, [&](int, int, int n, int mm, OutT(&v)[ACC_R]) {
+        const int nl = n - n0, r0 = mm - m0 - wmu * 128;  // r0 = i*16 + quad*4
+        const int pc = (nl >> 3) ^ (2 * quad);
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        if (wmu == p) {
-          each(acc, m0, n0, wmu, wn, quad, col, [&](int, int, int n, int mm, OutT(&v)[ACC_R]) {
-            const int nl = n - n0, r0 = mm - m0 - p * 128;  // r0 = i*16 + quad*4
-            const int pc = (nl >> 3) ^ (2 * quad);
-#pragma unroll
-            for (int e = 0; e < ACC_R; ++e) stg[(r0 + e) * GN + pc * 8 + (nl & 7)] = v[e];
-          });
-        }
-        __syncthreads();
-        const int rows = min(128, Vs_pad - m0 - p * 128), cols = min(GN, N_pad - n0);
-        for (int q = tid; q < 128 * (GN / 8); q += GTHREADS) {
-          const int r = q / (GN / 8), cc = q % (GN / 8);
-          if (r < rows && cc * 8 < cols)
-            *(u32x4*)(dT + (int64_t)(m0 + p * 128 + r) * ld_dT + n0 + cc * 8) =
-                *(const u32x4*)(stg + r * GN + ((cc ^ (2 * ((r >> 2) & 3))) * 8));
-        }
-        __syncthreads();
+        for (int e = 0; e < ACC_R; ++e) stg[(r0 + e) * GN + pc * 8 + (nl & 7)] = v[e];
+      });
+      __syncthreads();
+      const int rows = min(GM, Vs_pad - m0), cols = min(GN, N_pad - n0);
+      for (int q = tid; q < GM * (GN / 8); q += GTHREADS) {
+        const int r = q / (GN / 8), cc = q % (GN / 8);
+        const OutT* src = (const OutT*)(r < 128 ? smem : smem1) + (r & 127) * GN;
+        if (r < rows && cc * 8 < cols)
+          *(u32x4*)(dT + (int64_t)(m0 + r) * ld_dT + n0 + cc * 8) =
+              *(const u32x4*)(src + ((cc ^ (2 * ((r >> 2) & 3))) * 8));
       }
     } else {
       each(acc, m0, n0, wmu, wn, quad, col, [&](int, int, int n, int mm, OutT(&v)[ACC_R]) {
@@ -340,7 +337,7 @@ struct EpiStore {
   int accumulate;
   static constexpr int LDS_BYTES = 0;
 
-  __device__ inline void operator()(AccTile& acc, int m0, int n0, char*) const {
+  __device__ inline void operator()(AccTile& acc, int m0, int n0, char*, char*) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
 #pragma unroll
@@ -375,7 +372,7 @@ struct EpiAccum {
   int first, last;
   static constexpr int LDS_BYTES = 0;
 
-  __device__ inline void operator()(AccTile& acc, int m0, int n0, char*) const {
+  __device__ inline void operator()(AccTile& acc, int m0, int n0, char*, char*) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
 #pragma unroll
@@ -416,7 +413,7 @@ struct EpiAccumT {
   int first, last;
   static constexpr int LDS_BYTES = 0;
 
-  __device__ inline void operator()(AccTile& acc, int m0, int n0, char*) const {
+  __device__ inline void operator()(AccTile& acc, int m0, int n0, char*, char*) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
 #pragma unroll
@@ -462,7 +459,7 @@ struct EpiStoreT {
   int M, N;
   static constexpr int LDS_BYTES = 0;
 
-  __device__ inline void operator()(AccTile& acc, int m0, int n0, char*) const {
+  __device__ inline void operator()(AccTile& acc, int m0, int n0, char*, char*) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
 #pragma unroll

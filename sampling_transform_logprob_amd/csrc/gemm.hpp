@@ -156,7 +156,9 @@ struct MainBf16T {
     __shared__ __attribute__((aligned(16))) char s1[STAGEB];
     return s1;
   }
+  // the epilogue's two LDS buffers (up to EPI_LDS_MAX bytes each): the stages
   __device__ static char* epilogue_lds(char*) { return stage0(); }
+  __device__ static char* epilogue_lds1(char*) { return stage1(); }
 
   __device__ inline void run(AccTile& acc, int m0, int n0, char*) const {
     char* const S0 = stage0();
@@ -362,7 +364,9 @@ struct MainF32 {
   static constexpr int LDS_BYTES = 2 * GM * (BK + 1) * 4;
   static constexpr int DYN_LDS = LDS_BYTES;  // dynamic LDS, shared with the epilogue
   static constexpr int EPI_LDS_MAX = 160 * 1024;
+  // one epilogue LDS buffer, shared with the main loop (no second one)
   __device__ static char* epilogue_lds(char* dyn) { return dyn; }
+  __device__ static char* epilogue_lds1(char*) { return nullptr; }
   const float* A;
   int64_t lda;
   int M;
@@ -438,7 +442,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(Main mainloop, Epi ep
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) acc[i][j] = f32x4{};
   mainloop.run(acc, tm * GM, tn * GN, smem);
-  epi(acc, tm * GM, tn * GN, Main::epilogue_lds(smem));
+  epi(acc, tm * GM, tn * GN, Main::epilogue_lds(smem), Main::epilogue_lds1(smem));
 }
 
 }  // namespace stce

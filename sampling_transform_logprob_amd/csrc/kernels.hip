@@ -295,7 +295,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_splitk_kernel(Main mainloop,
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) acc[i][j] = f32x4{};
   mn.run(acc, tm * GM, tn * GN, smem);
-  ep(acc, tm * GM, tn * GN, Main::epilogue_lds(smem));
+  ep(acc, tm * GM, tn * GN, Main::epilogue_lds(smem), Main::epilogue_lds1(smem));
 }
 
 // out[i] = part[0][i] + part[1][i] + ... in split order, 4 elements a thread.
