@@ -403,7 +403,9 @@ struct EpiAccum {
 // so every store is 16 bytes (8 for bf16).  M is a multiple of 4.
 // ---------------------------------------------------------------------------
 // Hidden-gradient accumulation (dH^T = W^T dz^T): sum[n, m] = (first ? 0 :
-// sum[n, m]) + acc; on the last slice the result goes to `out` (OutT).
+// sum[n, m]) + acc; on the last slice the result goes to `out` (OutT).  With
+// first = last = 1 and OutT = float it is a plain transposed fp32 store (the
+// split-K partials of the fused step).
 template <class OutT>
 struct EpiAccumT {
   float* sum;  // [N][ld] fp32 running sum (may alias out when OutT is float)
@@ -447,29 +449,6 @@ struct EpiAccumT {
         } else {
           *(f32x4*)(sum + o) = v;
         }
-      }
-    }
-  }
-};
-
-// Plain fp32 transposed store: out[n, m] = acc (split-K partials of dH^T).
-struct EpiStoreT {
-  float* out;
-  int64_t ld;
-  int M, N;
-  static constexpr int LDS_BYTES = 0;
-
-  __device__ inline void operator()(AccTile& acc, int m0, int n0, char*, char*) const {
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
-#pragma unroll
-    for (int j = 0; j < ACC_J; ++j) {
-      const int n = n0 + acc_col(wn, j, col);
-      if (n >= N) continue;
-#pragma unroll
-      for (int i = 0; i < ACC_I; ++i) {
-        const int m = m0 + acc_row(wm, i, 0, quad);
-        if (m < M) *(f32x4*)(out + (int64_t)n * ld + m) = acc[i][j];
       }
     }
   }

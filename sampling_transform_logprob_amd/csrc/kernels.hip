@@ -274,16 +274,16 @@ __global__ __launch_bounds__(256) void dz_keys_kernel(const float* keys, int64_t
   }
 }
 
-// Split-K product: workgroup b computes tile b % tiles over the reduction
-// range [split * ks, min(K, (split + 1) * ks)), split = b / tiles, and
-// stores it (fp32, through the epilogue) into partial buffer `split`.
+// Split-K product: workgroup (b, split) computes tile b over the reduction
+// range [split * ks, min(K, (split + 1) * ks)) and stores it (fp32, through
+// the epilogue) into partial buffer `split`.
 template <class Main, class Epi>
 __global__ __launch_bounds__(GTHREADS, 1) void gemm_splitk_kernel(Main mainloop, Epi epi, TileMap map, int tiles,
                                                                  int64_t ks, int64_t pstride) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int split = blockIdx.x / tiles;
+  const int split = blockIdx.y;
   int tm, tn;
-  map.get(blockIdx.x - split * tiles, tm, tn);
+  map.get(blockIdx.x, tm, tn);
   Main mn = mainloop;
   mn.shift_k(split * ks);
   if (mn.K > ks) mn.K = (int)ks;
@@ -348,7 +348,8 @@ hipError_t launch_gemm_splitk(const Main& mn, const Epi& ep, int64_t tiles_m, in
   if (attr != hipSuccess) return attr;
   TileMap map{(int)tiles_m, (int)tiles_n, 4};
   const int tiles = (int)(tiles_m * tiles_n);
-  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * splits)), dim3(GTHREADS), lds, s, mn, ep, map, tiles, ks, pstride);
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles, (unsigned)splits), dim3(GTHREADS), lds, s, mn, ep, map, tiles, ks,
+                     pstride);
   return hipGetLastError();
 }
 
@@ -539,7 +540,7 @@ hipError_t fused_grads_impl(const FusedGradArgs& a, hipStream_t s) {
     if constexpr (sizeof(E) == 2) {
       MainBf16T<false, true> mn{(const bf16*)a.WT, a.V_pad, (int)a.H, (const bf16*)a.dT + a.dT_col, a.ld_dT,
                                 (int)a.rows, (int)a.V_pad, 0, (int)a.V_pad};
-      EpiStoreT ep{a.dh_part, a.H, (int)a.H, (int)a.rows};
+      EpiAccumT<float> ep{a.dh_part, a.H, a.dh_part, (int)a.H, (int)a.rows, 1, 1};
       ProfScope ps(6, s);
       e = launch_gemm_splitk(mn, ep, ceil_div(a.H, GM), ceil_div(a.rows, GN), a.splits, a.ks, a.rows * a.H, s);
     } else {
