@@ -251,3 +251,29 @@ def test_temperature_division_bitwise_on_many_pairs():
     ref = (zg.double()[None, :] / torch.from_numpy(t).double()[:, None]).float()
     bad = (s.view(torch.int32) != ref.view(torch.int32))
     assert int(bad.sum()) == 0, f"{int(bad.sum())} quotients differ, e.g. z={z[bad.any(0).numpy()][:3]}"
+
+
+# ---------------------------------------------------------------- odd k-tile counts and a K tail
+def test_hidden_size_with_odd_k_tiles_and_a_tail():
+    """H = 1064 = 16 x 64 + 40: the products run 17 k-tiles (an odd count,
+    padded with one all-zero tile) and a partial last one, in the forward's
+    projection and the backward's recompute; T = 300 gives the weight
+    gradient 5 k-tiles (odd) and the hidden gradient an odd count over a
+    V = 5000 slice.  Several chunks and vocabulary slices."""
+    w = workloads.make("headline", T=300)
+    H = 1064
+    w["h"] = np.ascontiguousarray(w["h"][:, :H])
+    w["W"] = np.ascontiguousarray(w["W"][:5000, :H])
+    w["H"], w["V"] = H, 5000
+    y = targets(w)
+    say(f"odd k-tiles: T=300 H={H} V=5000")
+    g = np.random.Generator(np.random.PCG64(21)).standard_normal(300) / 300
+    G, lp, st, gh, gw, keys = _run(w, y, g, chunk_rows=128, vocab_slice=2048)
+    ref = oracle.forward(w["h"], w["W"], y, w["temperature"], w["top_k"], w["top_p"], w["min_p"],
+                         keys=keys.cpu().numpy())
+    check_support(binding.decode_state(st), ref, "odd k-tiles")
+    err = check_logprob(lp.cpu().numpy(), ref)
+    dH, dW = oracle.backward(w["h"], w["W"], y, ref, g, w["temperature"])
+    rh, rw = rel_fro(gh.float().cpu().numpy(), dH), rel_fro(gw.cpu().numpy(), dW)
+    say(f"  logprob err {err:.2e}  dH rel {rh:.2e}  dW rel {rw:.2e}")
+    assert rh < GRAD_RTOL and rw < GRAD_RTOL
