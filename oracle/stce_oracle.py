@@ -59,6 +59,18 @@ so the per-token losses are ``-A sg(min(r, 1+eps_high)) logprob`` and
 (the reciprocal of a constant denominator).  The gradient then flows
 through the same VJP as the logprob with ``g = d loss / d logprob``.
 
+A second temperature convention ([xorl#74] self-review pass: "the scalar
+(pre-GEMM) vs per-row-tensor (post-GEMM) temperature convention split is now
+documented"; "What this PR does" 1: temperature first, at the lane's dtype
+boundary).  The pages name it without its formula; read plainly: one scalar
+T divides the hidden state before the projection, in fp32, and the quotient
+is rounded to the operand dtype, ``h' = round(fl32(h) / T)``; the keys are
+then ``s = fl32(h' W^T)`` (no per-row division) and the VJP carries the 1/T
+to the hidden state, ``dH = (dz W) / T`` with ``dz = g (onehot - q)``, and
+``dW = dz^T h'`` (the rounding of ``h'`` passes gradients unchanged).
+``pre_gemm_hidden`` and ``backward_pre_gemm`` below; ``forward`` takes ``h'``
+with no per-row temperature.
+
 Values (logprob, gradients) use the unrounded fp64 logits ``u = z / T``.
 Support decisions use only the fp32 keys, so a caller may pass the keys of
 another implementation (``keys=``) to compare supports bit for bit.
@@ -327,6 +339,34 @@ def backward(h, W, target, fwd: dict, grad_logprob, temperature=None):
     h64 = np.asarray(h, dtype=np.float64)[fwd["rows"]]
     W64 = np.asarray(W, dtype=np.float64)
     return dz @ W64, dz.T @ h64
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """fp32 values rounded to the nearest bf16 (ties to even), as fp32: the
+    upper 16 bits of the fp32 pattern after adding 0x7fff plus the lowest
+    kept bit (finite inputs)."""
+    b = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32)
+
+
+def pre_gemm_hidden(h, temperature, operand="bf16") -> np.ndarray:
+    """Scalar pre-GEMM temperature: ``h' = round(fl32(h) / T)`` with the
+    quotient correctly rounded to fp32 (an fp64 quotient of fp32 values
+    rounded once, as in ``scale_logits``) and then rounded to the operand
+    dtype (``"bf16"``, ties to even, or ``"f32"``)."""
+    t = np.float32(temperature)
+    assert np.isfinite(t) and t > 0, "the scalar temperature must be finite and > 0"
+    q = (np.asarray(h, np.float32).astype(np.float64) / np.float64(t)).astype(np.float32)
+    return round_to_bf16(q) if operand == "bf16" else q
+
+
+def backward_pre_gemm(h_scaled, W, target, fwd: dict, grad_logprob, temperature):
+    """VJP of ``sum_r g_r * logprob_r`` under the scalar pre-GEMM convention,
+    ``fwd`` being ``forward(h_scaled, W, ...)`` with no per-row temperature:
+    ``dH = (dz W) / T`` and ``dW = dz^T h_scaled``, ``dz = g (onehot - q)``."""
+    dH, dW = backward(h_scaled, W, target, fwd, grad_logprob)
+    return dH / float(np.float32(temperature)), dW
 
 
 OBJECTIVES = ("cispo", "clip")

@@ -60,6 +60,16 @@ MUTANTS = {
                                                 "    return dict(loss=loss * sc, g=-g * sc, ratio=ratio)",
                                                 ["test_policy_gradient_matches_autograd_of_objective",
                                                  "test_clipped_policy_gradient_matches_central_differences"]),
+    "pre-GEMM gradient misses the 1/T": ("    return dH / float(np.float32(temperature)), dW",
+                                         "    return dH, dW",
+                                         ["test_pre_gemm_temperature_equals_post_gemm_for_a_power_of_two",
+                                          "test_pre_gemm_gradient_matches_autograd"]),
+    "pre-GEMM hidden not rounded to the operand": ('    return round_to_bf16(q) if operand == "bf16" else q',
+                                                   "    return q",
+                                                   ["test_pre_gemm_hidden_matches_torch_division_and_rounding"]),
+    "bf16 rounding half up": ("    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000",
+                              "    b = (b + 0x8000) & 0xFFFF0000",
+                              ["test_round_to_bf16_matches_torch_and_ties_to_even"]),
 }
 
 

@@ -577,3 +577,83 @@ def test_ignored_rows_score_zero_and_get_no_gradient(rng):
     np.testing.assert_allclose(dW, dW2, rtol=0, atol=0)          # ignored rows add nothing to dW
     with pytest.raises(AssertionError):
         oracle.forward(h, W, y, temp, ignore_index=None)         # -100 is not a token without ignore_index
+
+
+# ---------------------------------------------------------------- scalar pre-GEMM temperature
+def test_round_to_bf16_matches_torch_and_ties_to_even(rng):
+    torch = pytest.importorskip("torch")
+    mag = np.float32(10.0) ** rng.integers(-30, 30, 20000).astype(np.float32)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * mag,
+                        np.float32([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 1 + 2 ** -8 + 2 ** -20, 0.0, -0.0])])
+    x = x[np.isfinite(x)]
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(oracle.round_to_bf16(x).view(np.uint32), ref.view(np.uint32))
+    assert oracle.round_to_bf16(np.float32([1 + 2 ** -8]))[0] == 1.0              # tie, down to even
+    assert oracle.round_to_bf16(np.float32([1 + 3 * 2 ** -8]))[0] == 1 + 2 ** -6   # tie, up to even
+
+
+def test_pre_gemm_hidden_matches_torch_division_and_rounding(rng):
+    torch = pytest.importorskip("torch")
+    h = rng.standard_normal((7, 33)).astype(np.float32) * 3
+    for t in (0.7, 1.3, 0.05):
+        ref = (torch.from_numpy(h) / torch.tensor(t, dtype=torch.float32)).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(oracle.pre_gemm_hidden(h, t, "bf16").view(np.uint32), ref.view(np.uint32))
+        ref32 = (torch.from_numpy(h) / torch.tensor(t, dtype=torch.float32)).numpy()
+        assert np.array_equal(oracle.pre_gemm_hidden(h, t, "f32").view(np.uint32), ref32.view(np.uint32))
+    assert np.array_equal(oracle.pre_gemm_hidden(h, 1.0, "f32"), h)
+
+
+def _pre_gemm_case(rng, Tn=12, H=16, V=40):
+    h = oracle.round_to_bf16(rng.standard_normal((Tn, H)).astype(np.float32))
+    W = oracle.round_to_bf16((rng.standard_normal((V, H)) * 0.3).astype(np.float32))
+    z = h.astype(np.float64) @ W.astype(np.float64).T
+    y = np.where(np.arange(Tn) % 3 == 0, rng.integers(0, V, Tn), z.argmax(1)).astype(np.int64)
+    tk = np.where(np.arange(Tn) % 2 == 0, 8, 0).astype(np.int32)
+    tp = np.where(np.arange(Tn) % 4 == 1, 0.9, 1.0).astype(np.float32)
+    mp = np.where(np.arange(Tn) % 5 == 2, 0.05, 0.0).astype(np.float32)
+    return h, W, y, tk, tp, mp
+
+
+def test_pre_gemm_temperature_equals_post_gemm_for_a_power_of_two(rng):
+    """T = 0.5 divides exactly (h / T = 2h in bf16, fl32(z) / T = 2 fl32(z)),
+    so the scalar pre-GEMM convention gives the post-GEMM convention's keys,
+    logprobs and gradients, row by row."""
+    h, W, y, tk, tp, mp = _pre_gemm_case(rng)
+    Tn = h.shape[0]
+    hs = oracle.pre_gemm_hidden(h, 0.5, "bf16")
+    assert np.array_equal(hs, 2 * h)
+    t = np.full(Tn, 0.5, np.float32)
+    post = oracle.forward(h, W, y, t, tk, tp, mp)
+    pre = oracle.forward(hs, W, y, None, tk, tp, mp)
+    assert np.array_equal(pre["keys"].view(np.uint32), post["keys"].view(np.uint32))
+    assert np.array_equal(pre["logprob"], post["logprob"]) and pre["in_support"].any()
+    g = rng.standard_normal(Tn)
+    dh1, dw1 = oracle.backward(h, W, y, post, g, t)
+    dh2, dw2 = oracle.backward_pre_gemm(hs, W, y, pre, g, 0.5)
+    np.testing.assert_allclose(dh2, dh1, rtol=1e-13, atol=1e-300)
+    np.testing.assert_allclose(dw2, dw1, rtol=1e-13, atol=1e-300)
+
+
+def test_pre_gemm_gradient_matches_autograd(rng):
+    """fp64 autograd of sum_r g_r (u[r, y_r] - logsumexp of u[r] over the
+    support), u = (h / T) W^T, for T = 0.7 (the pre-GEMM quotient unrounded
+    here: the oracle's fp32 rounding of h / T accounts for ~1e-7)."""
+    torch = pytest.importorskip("torch")
+    h, W, y, tk, _, _ = _pre_gemm_case(rng, Tn=6, H=10, V=30)
+    y = (h.astype(np.float64) @ W.astype(np.float64).T).argmax(1)   # all targets in support
+    t = 0.7
+    hs = oracle.pre_gemm_hidden(h, t, "f32")
+    fwd = oracle.forward(hs, W, y, None, tk, None, None)
+    assert fwd["in_support"].all()
+    g = rng.standard_normal(h.shape[0])
+    dH, dW = oracle.backward_pre_gemm(hs, W, y, fwd, g, t)
+    H64 = torch.tensor(h.astype(np.float64), requires_grad=True)
+    W64 = torch.tensor(W.astype(np.float64), requires_grad=True)
+    u = (H64 / t) @ W64.T
+    total = 0
+    for r in range(h.shape[0]):
+        mask = torch.tensor(oracle.in_support(fwd["keys"][r], int(fwd["key_thr"][r]), int(fwd["id_thr"][r])))
+        total = total + float(g[r]) * (u[r, int(y[r])] - torch.logsumexp(u[r][mask], 0))
+    total.backward()
+    for a, b in ((dH, H64.grad.numpy()), (dW, W64.grad.numpy())):
+        assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-6
