@@ -92,6 +92,9 @@ typedef enum {
 
 /* stce_problem.flags */
 #define STCE_PROBLEM_IGNORE_INDEX 1 /* targets equal to ignore_index mark inactive rows */
+#define STCE_PROBLEM_PRE_GEMM_TEMPERATURE 2 /* one scalar temperature applied to the hidden
+                                              states before the projection: see
+                                              stce_problem.pre_gemm_temperature */
 
 /* Bytes of per-row state stce_forward writes and stce_backward reads. */
 #define STCE_STATE_BYTES_PER_ROW 32
@@ -101,7 +104,7 @@ typedef struct stce_problem {
   int64_t H;             /* hidden size, >= 8, multiple of 8 */
   int64_t V;             /* vocabulary size, 1 <= V < 2^31 - 256 */
   int32_t dtype;         /* stce_dtype of hidden and weight */
-  int32_t flags;         /* 0 or STCE_PROBLEM_IGNORE_INDEX */
+  int32_t flags;         /* 0 or a combination of STCE_PROBLEM_* */
   const void *hidden;    /* [T, H], dtype; 16-byte aligned */
   const void *weight;    /* [V, H] (lm_head.weight layout), dtype; 16-byte aligned */
   const int64_t *target; /* [T] sampled token ids in [0, V) */
@@ -117,6 +120,22 @@ typedef struct stce_problem {
                             rows out): logprob 0, exactly zero gradient, no
                             error; its support and side outputs are still
                             computed.  Ignored otherwise. */
+  float pre_gemm_temperature; /* with STCE_PROBLEM_PRE_GEMM_TEMPERATURE: the lane's
+                            one scalar temperature Ts (finite, > 0), applied
+                            before the product -- the scalar convention the
+                            xorl pull request's self-review pass sets beside the
+                            per-row post-GEMM one.  The library forms h', the
+                            correctly rounded fp32 quotient h / Ts rounded to
+                            the operand dtype (nearest, ties to even), and
+                            scores s = fl32(h' W^T);
+                            the gradients are those of that s with respect to h
+                            and W (dz = g (1[j == y] - q), dW = dz^T h',
+                            dH = (dz W) / Ts).  `temperature` must then be NULL
+                            (the two conventions do not combine).  A power of
+                            two such as Ts = 0.5 divides exactly, so it gives
+                            the bits of the per-row convention with every row
+                            at Ts (barring overflow and subnormals).  Ignored
+                            without the flag. */
 } stce_problem;
 
 /* Per-row state size in bytes for T rows (STCE_STATE_BYTES_PER_ROW * T). */
@@ -235,6 +254,7 @@ stce_status stce_decode_state(const void *host_state, int64_t nrows, stce_row_in
 #define STCE_KERNEL_POLICY_LOSS 9  /* per-row policy-gradient loss */
 #define STCE_KERNEL_DZ_KEYS 10     /* fused step: dlogits from a chunk's stored keys */
 #define STCE_KERNEL_SPLIT_SUM 11   /* fused step: sum of the hidden-gradient split partials */
+#define STCE_KERNEL_PRESCALE 12    /* hidden states divided by the scalar pre-GEMM temperature */
 typedef struct stce_profile {
   int32_t capacity;
   int32_t count;

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libstce.so")
 STATUS_NONE = (1 << 63) - 1
 FIELDS = {1: "temperature", 2: "top_k", 3: "top_p", 4: "min_p", 5: "target"}
 FLAG_VALID, FLAG_FILTERED, FLAG_IN_SUPPORT, FLAG_IGNORED = 1, 2, 4, 8
-PROBLEM_IGNORE_INDEX = 1
+PROBLEM_IGNORE_INDEX, PROBLEM_PRE_GEMM_TEMPERATURE = 1, 2
 STATE_BYTES_PER_ROW = 32
 DT_BF16, DT_F32 = 1, 2
 
@@ -32,7 +32,7 @@ SYMBOLS = (
 )
 KERNEL_KINDS = {1: "validate", 2: "projection", 3: "select", 4: "dlogits", 5: "grad_weight",
                 6: "grad_hidden", 7: "transpose", 8: "partials", 9: "policy_loss", 10: "dz_keys",
-                11: "split_sum"}
+                11: "split_sum", 12: "prescale"}
 PG_OBJECTIVES = {"cispo": 1, "clip": 2}
 
 
@@ -43,7 +43,7 @@ class Problem(ctypes.Structure):
         ("hidden", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("target", ctypes.c_void_p),
         ("temperature", ctypes.c_void_p), ("top_k", ctypes.c_void_p), ("top_p", ctypes.c_void_p),
         ("min_p", ctypes.c_void_p), ("chunk_rows", ctypes.c_int64), ("vocab_slice", ctypes.c_int64),
-        ("ignore_index", ctypes.c_int64),
+        ("ignore_index", ctypes.c_int64), ("pre_gemm_temperature", ctypes.c_float),
     ]
 
 
@@ -146,8 +146,15 @@ def _meta(name, t, T, dtype, device):
 
 
 def make_problem(hidden, weight, target, temperature=None, top_k=None, top_p=None, min_p=None,
-                 chunk_rows: int = 0, vocab_slice: int = 0, ignore_index: Optional[int] = None):
-    """Checked ``stce_problem`` plus the tensors it points into (kept alive)."""
+                 chunk_rows: int = 0, vocab_slice: int = 0, ignore_index: Optional[int] = None,
+                 pre_gemm_temperature: Optional[float] = None):
+    """Checked ``stce_problem`` plus the tensors it points into (kept alive).
+
+    ``temperature`` is the per-row tensor applied to the logits after the
+    product; ``pre_gemm_temperature`` is instead one scalar applied to the
+    hidden states before it (the two do not combine)."""
+    if pre_gemm_temperature is not None and temperature is not None:
+        raise ValueError("pass either a per-row temperature tensor or pre_gemm_temperature, not both")
     if hidden.dim() != 2 or weight.dim() != 2 or hidden.shape[1] != weight.shape[1]:
         raise ValueError(f"hidden [T, H] and weight [V, H] expected, got {tuple(hidden.shape)}, {tuple(weight.shape)}")
     if hidden.dtype != weight.dtype:
@@ -171,9 +178,12 @@ def make_problem(hidden, weight, target, temperature=None, top_k=None, top_p=Non
             _meta("top_k", top_k, T, torch.int32, dev),
             _meta("top_p", top_p, T, torch.float32, dev),
             _meta("min_p", min_p, T, torch.float32, dev)]
-    prob = Problem(T, H, V, dt, 0 if ignore_index is None else PROBLEM_IGNORE_INDEX,
-                   *[t.data_ptr() if t is not None else None for t in keep], chunk_rows, vocab_slice,
-                   0 if ignore_index is None else int(ignore_index))
+    flags = 0 if ignore_index is None else PROBLEM_IGNORE_INDEX
+    if pre_gemm_temperature is not None:
+        flags |= PROBLEM_PRE_GEMM_TEMPERATURE
+    prob = Problem(T, H, V, dt, flags, *[t.data_ptr() if t is not None else None for t in keep], chunk_rows,
+                   vocab_slice, 0 if ignore_index is None else int(ignore_index),
+                   0.0 if pre_gemm_temperature is None else float(pre_gemm_temperature))
     return prob, keep
 
 
@@ -203,14 +213,14 @@ def _raise_rows(status: torch.Tensor, what: str, tensors: dict) -> None:
 
 def forward(hidden, weight, target, temperature=None, top_k=None, top_p=None, min_p=None, *,
             chunk_rows: int = 0, check: bool = True, workspace: Optional[torch.Tensor] = None,
-            side: bool = False, ignore_index: Optional[int] = None):
+            side: bool = False, ignore_index: Optional[int] = None, pre_gemm_temperature: Optional[float] = None):
     """Selected logprob per row and the 32-byte-per-row state for backward.
 
     With ``side=True`` also returns a dict of the sweep's side outputs
     (``lse_full``, ``entropy_full``, ``entropy_support``, fp32 [T]).
     """
     prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, chunk_rows,
-                              ignore_index=ignore_index)
+                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature)
     T = prob.T
     fwd_b, _ = workspace_bytes(prob)
     dev = hidden.device
@@ -237,10 +247,11 @@ def forward(hidden, weight, target, temperature=None, top_k=None, top_p=None, mi
 def backward(hidden, weight, target, state, grad_logprob, temperature=None, top_k=None, top_p=None,
              min_p=None, *, need_hidden: bool = True, need_weight: bool = True,
              grad_weight: Optional[torch.Tensor] = None, accumulate_grad_weight: bool = False,
-             vocab_slice: int = 0, workspace: Optional[torch.Tensor] = None, ignore_index: Optional[int] = None):
+             vocab_slice: int = 0, workspace: Optional[torch.Tensor] = None, ignore_index: Optional[int] = None,
+             pre_gemm_temperature: Optional[float] = None):
     """(grad_hidden [T, H] in hidden's dtype, grad_weight [V, H] fp32)."""
     prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, 0, vocab_slice,
-                              ignore_index=ignore_index)
+                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature)
     T, H, V = prob.T, prob.H, prob.V
     dev = hidden.device
     if grad_logprob.shape != (T,) or grad_logprob.dtype != torch.float32 or grad_logprob.device != dev:
@@ -264,12 +275,15 @@ def backward(hidden, weight, target, state, grad_logprob, temperature=None, top_
     return gh, grad_weight
 
 
-def scaled_logits(hidden, weight, temperature=None, row0: int = 0, nrows: Optional[int] = None):
-    """fp32 keys s = fl32(h W^T) / T of rows [row0, row0 + nrows) from the forward's kernel."""
+def scaled_logits(hidden, weight, temperature=None, row0: int = 0, nrows: Optional[int] = None, *,
+                  pre_gemm_temperature: Optional[float] = None):
+    """fp32 keys of rows [row0, row0 + nrows) from the forward's kernel:
+    s = fl32(h W^T) / T per row, or fl32((h / Ts) W^T) with the scalar
+    pre-GEMM temperature Ts."""
     T = hidden.shape[0]
     nrows = T - row0 if nrows is None else nrows
     target = torch.zeros(T, dtype=torch.int64, device=hidden.device)
-    prob, keep = make_problem(hidden, weight, target, temperature)
+    prob, keep = make_problem(hidden, weight, target, temperature, pre_gemm_temperature=pre_gemm_temperature)
     fwd_b, _ = workspace_bytes(prob)
     ws = torch.empty(max(fwd_b, 1), dtype=torch.uint8, device=hidden.device)
     out = torch.empty(nrows, prob.V, dtype=torch.float32, device=hidden.device)
@@ -331,14 +345,16 @@ def policy_loss(logprob, advantages, old_logprob, objective: str = "cispo", eps_
 def policy_loss_step(hidden, weight, target, advantages, old_logprob, temperature=None, top_k=None, top_p=None,
                      min_p=None, *, objective: str = "cispo", eps_low: float = 0.2, eps_high: float = 0.28,
                      scale: float = 1.0, need_hidden: bool = True, need_weight: bool = True,
-                     ignore_index: Optional[int] = None):
+                     ignore_index: Optional[int] = None, pre_gemm_temperature: Optional[float] = None):
     """Fused head + policy-gradient token loss: forward, per-token loss and
     the gradients of ``sum(loss)``.  Returns (loss [T], logprob [T], ratio [T],
     grad_hidden, grad_weight)."""
-    logprob, state = forward(hidden, weight, target, temperature, top_k, top_p, min_p, ignore_index=ignore_index)
+    logprob, state = forward(hidden, weight, target, temperature, top_k, top_p, min_p, ignore_index=ignore_index,
+                             pre_gemm_temperature=pre_gemm_temperature)
     loss, g, ratio = policy_loss(logprob, advantages, old_logprob, objective, eps_low, eps_high, scale, state)
     gh, gw = backward(hidden, weight, target, state, g, temperature, top_k, top_p, min_p,
-                      need_hidden=need_hidden, need_weight=need_weight, ignore_index=ignore_index)
+                      need_hidden=need_hidden, need_weight=need_weight, ignore_index=ignore_index,
+                      pre_gemm_temperature=pre_gemm_temperature)
     return loss, logprob, ratio, gh, gw
 
 
@@ -355,7 +371,8 @@ def fused_policy_step(hidden, weight, target, advantages, old_logprob, temperatu
                       scale: float = 1.0, need_hidden: bool = True, need_weight: bool = True,
                       grad_weight: Optional[torch.Tensor] = None, accumulate_grad_weight: bool = False,
                       side: bool = False, chunk_rows: int = 0, ignore_index: Optional[int] = None,
-                      check: bool = True, workspace: Optional[torch.Tensor] = None):
+                      check: bool = True, workspace: Optional[torch.Tensor] = None,
+                      pre_gemm_temperature: Optional[float] = None):
     """The fused head + policy-gradient step (dlogits formed in the forward's
     sweep, no recompute).  Returns a dict with ``loss``, ``logprob``,
     ``ratio`` (fp32 [T]), ``state``, ``grad_hidden`` ([T, H], hidden's dtype,
@@ -364,7 +381,7 @@ def fused_policy_step(hidden, weight, target, advantages, old_logprob, temperatu
     if objective not in PG_OBJECTIVES:
         raise ValueError(f"objective must be one of {tuple(PG_OBJECTIVES)}")
     prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, chunk_rows,
-                              ignore_index=ignore_index)
+                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature)
     T, H, V = prob.T, prob.H, prob.V
     dev = hidden.device
     adv = _meta("advantages", advantages, T, torch.float32, dev)

@@ -44,17 +44,27 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
   int64_t C, ldt, ntv, nbuf;                               // forward
-  size_t f_flags, f_tile, f_part, f_sy, fwd;
+  size_t f_flags, f_tile, f_part, f_sy, f_hs, fwd;
   size_t buf_tile, buf_part, buf_sy;                       // bytes per chunk buffer
   int64_t Vs, Vsp, Tp;                                      // backward
-  size_t b_flags, b_hT, b_WT, b_d, b_dT, b_dh, bwd;
+  size_t b_flags, b_hT, b_WT, b_d, b_dT, b_dh, b_hs, bwd;
 };
 
+// The scalar pre-GEMM temperature: the problem's hidden states are replaced
+// by h' = h / Ts (rounded to the operand type), written to the workspace.
+bool pre_gemm(const stce_problem* p) { return (p->flags & STCE_PROBLEM_PRE_GEMM_TEMPERATURE) != 0; }
+
 size_t elt_size(int dtype) { return dtype == STCE_DT_BF16 ? 2 : 4; }
+size_t hs_bytes(const stce_problem* p) {
+  return pre_gemm(p) ? align_up(elt_size(p->dtype) * (size_t)p->T * (size_t)p->H) : 0;
+}
 
 stce_status check_shapes(const stce_problem* p) {
   if (!p) return fail(STCE_E_ARG, "problem is NULL");
-  if (p->flags & ~STCE_PROBLEM_IGNORE_INDEX) return fail(STCE_E_ARG, "problem.flags=%d has unknown bits", (int)p->flags);
+  if (p->flags & ~(STCE_PROBLEM_IGNORE_INDEX | STCE_PROBLEM_PRE_GEMM_TEMPERATURE))
+    return fail(STCE_E_ARG, "problem.flags=%d has unknown bits", (int)p->flags);
+  if (pre_gemm(p) && !(__builtin_isfinite(p->pre_gemm_temperature) && p->pre_gemm_temperature > 0.0f))
+    return fail(STCE_E_ARG, "pre_gemm_temperature=%g must be finite and > 0", (double)p->pre_gemm_temperature);
   if ((p->flags & STCE_PROBLEM_IGNORE_INDEX) && p->ignore_index >= 0 && p->ignore_index < p->V)
     return fail(STCE_E_ARG, "ignore_index=%lld is a token id of [0, V)", (long long)p->ignore_index);
   if (p->dtype != STCE_DT_BF16 && p->dtype != STCE_DT_F32)
@@ -91,6 +101,7 @@ Layout plan(const stce_problem* p) {
   L.f_tile = o;  o += L.nbuf * L.buf_tile;
   L.f_part = o;  o += L.nbuf * L.buf_part;
   L.f_sy = o;    o += L.nbuf * L.buf_sy;
+  L.f_hs = o;    o += hs_bytes(p);
   L.fwd = o;
 
   // bf16 keeps dz vocab-major only (the hidden gradient reads it MN-major);
@@ -118,6 +129,7 @@ Layout plan(const stce_problem* p) {
   L.b_d = o;     o = align_up(o + (bf ? 0 : es * (size_t)L.Tp * L.Vsp));
   L.b_dT = o;    o = align_up(o + es * (size_t)L.Vsp * L.Tp);
   L.b_dh = o;    o = align_up(o + (p->dtype == STCE_DT_BF16 ? 4 * (size_t)T * H : 0));
+  L.b_hs = o;    o += hs_bytes(p);
   L.bwd = o;
   return L;
 }
@@ -144,7 +156,7 @@ stce_status check_pg(const stce_pg_params* pg) {
 // split partials of the chunk's hidden gradient.
 struct FusedLayout {
   int64_t C, ldt, ntv, Vp, Tp, S, ks, G, nbuf;
-  size_t flags, tile, part, sy, g, d, dT, WT, hT, dhp, total;
+  size_t flags, tile, part, sy, g, d, dT, WT, hT, dhp, hs, total;
   size_t buf_tile, buf_part, buf_sy;
 };
 
@@ -192,6 +204,7 @@ FusedLayout plan_fused(const stce_problem* p, int64_t gmax = INT64_MAX) {
   L.WT = o;    o = align_up(o + es * (size_t)H * L.Vp);
   L.hT = o;    o = align_up(o + (p->dtype == STCE_DT_BF16 ? 0 : es * (size_t)H * L.Tp));
   L.dhp = o;   o = align_up(o + 4 * (size_t)L.S * L.C * H);
+  L.hs = o;    o += hs_bytes(p);
   L.total = o;
   return L;
 }
@@ -204,7 +217,26 @@ stce_status check_inputs(const stce_problem* p) {
   if ((p->temperature && !aligned(p->temperature, 4)) || (p->top_k && !aligned(p->top_k, 4)) ||
       (p->top_p && !aligned(p->top_p, 4)) || (p->min_p && !aligned(p->min_p, 4)))
     return fail(STCE_E_ARG, "metadata arrays must be 4-byte aligned");
+  if (pre_gemm(p) && p->temperature)
+    return fail(STCE_E_ARG,
+                "a per-row temperature array and the scalar pre-GEMM temperature do not combine: pass one of them");
   return STCE_OK;
+}
+
+// The hidden states the products read: the caller's, or h' = h / Ts written
+// into the workspace at `off` (rows row0 .. row0 + nrows; the rows keep their
+// offsets).  *dh_div receives the divisor of the hidden gradient.
+hipError_t hidden_for_products(const stce_problem* p, void* ws, size_t off, int64_t row0, int64_t nrows,
+                               const void** h, float* dh_div, hipStream_t st) {
+  *h = p->hidden;
+  if (dh_div) *dh_div = 1.0f;
+  if (!pre_gemm(p)) return hipSuccess;
+  if (dh_div) *dh_div = p->pre_gemm_temperature;
+  const size_t es = elt_size(p->dtype);
+  char* hs = (char*)ws + off;
+  *h = hs;
+  return launch_prescale(p->dtype, (const char*)p->hidden + es * (size_t)row0 * p->H, nrows * p->H,
+                         p->pre_gemm_temperature, hs + es * (size_t)row0 * p->H, st);
 }
 
 stce_status check_ws(void* ws, size_t have, size_t need) {
@@ -323,6 +355,8 @@ stce_status stce_forward_with_side(const stce_problem* p, float* logprob, void* 
                            st)))
     return hip_fail(e, "validate");
   const size_t es = elt_size(p->dtype);
+  const void* hid = nullptr;
+  if ((e = hidden_for_products(p, ws, L.f_hs, 0, p->T, &hid, nullptr, st))) return hip_fail(e, "prescale hidden");
   const int64_t nch = ceil_div(p->T, L.C);
   SideCtx* side = nullptr;
   if (L.nbuf == 2 && (e = side_ctx(&side, 2 * (size_t)nch))) return hip_fail(e, "side stream");
@@ -335,7 +369,7 @@ stce_status stce_forward_with_side(const stce_problem* p, float* logprob, void* 
     FwdArgs a{};
     a.dtype = p->dtype;
     a.W = p->weight;
-    a.h = (const char*)p->hidden + es * (size_t)c0 * p->H;
+    a.h = (const char*)hid + es * (size_t)c0 * p->H;
     a.H = p->H;
     a.V = p->V;
     a.rows = nc;
@@ -404,9 +438,12 @@ stce_status stce_backward(const stce_problem* p, const float* grad_logprob, cons
       return hip_fail(e, "validate");
   }
   if (!grad_hidden && !grad_weight) return STCE_OK;
+  const void* hid = nullptr;
+  float dh_div = 1.0f;
+  if ((e = hidden_for_products(p, ws, L.b_hs, 0, p->T, &hid, &dh_div, st))) return hip_fail(e, "prescale hidden");
   if (grad_weight && p->dtype != STCE_DT_BF16) {
     // the fp32 products take K-major operands only (bf16 reads h as it is)
-    if ((e = launch_transpose_f32((const float*)p->hidden, p->H, p->T, p->H, at<float>(ws, L.b_hT), L.Tp, L.Tp, st)))
+    if ((e = launch_transpose_f32((const float*)hid, p->H, p->T, p->H, at<float>(ws, L.b_hT), L.Tp, L.Tp, st)))
       return hip_fail(e, "transpose hidden");
   }
   const int64_t nsl = ceil_div(p->V, L.Vs);
@@ -414,7 +451,7 @@ stce_status stce_backward(const stce_problem* p, const float* grad_logprob, cons
     BwdSliceArgs a{};
     a.dtype = p->dtype;
     a.W = p->weight;
-    a.h = p->hidden;
+    a.h = hid;
     a.hT = at<char>(ws, L.b_hT);
     a.WT = at<char>(ws, L.b_WT);
     a.d = at<char>(ws, L.b_d);
@@ -437,6 +474,7 @@ stce_status stce_backward(const stce_problem* p, const float* grad_logprob, cons
     a.ld_d = L.Vsp;
     a.first = si == 0;
     a.last = si == nsl - 1;
+    a.dh_div = dh_div;
     if ((e = launch_bwd_slice(a, st))) return hip_fail(e, "backward slice");
   }
   return STCE_OK;
@@ -454,12 +492,15 @@ stce_status stce_scaled_logits(const stce_problem* p, int64_t row0, int64_t nrow
   if ((s = check_ws(ws, ws_bytes, L.fwd))) return s;
   hipStream_t st = (hipStream_t)stream;
   const size_t es = elt_size(p->dtype);
+  const void* hid = nullptr;
+  hipError_t e0 = hidden_for_products(p, ws, L.f_hs, row0, nrows, &hid, nullptr, st);
+  if (e0) return hip_fail(e0, "prescale hidden");
   for (int64_t c0 = row0; c0 < row0 + nrows; c0 += L.C) {
     const int64_t nc = row0 + nrows - c0 < L.C ? row0 + nrows - c0 : L.C;
     FwdArgs a{};
     a.dtype = p->dtype;
     a.W = p->weight;
-    a.h = (const char*)p->hidden + es * (size_t)c0 * p->H;
+    a.h = (const char*)hid + es * (size_t)c0 * p->H;
     a.H = p->H;
     a.V = p->V;
     a.rows = nc;
@@ -577,6 +618,9 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
                            p->top_k, p->top_p, p->min_p, p->target, flags, dev_status, st)))
     return hip_fail(e, "validate");
   const size_t es = elt_size(p->dtype);
+  const void* hid = nullptr;
+  float dh_div = 1.0f;
+  if ((e = hidden_for_products(p, ws, L.hs, 0, p->T, &hid, &dh_div, st))) return hip_fail(e, "prescale hidden");
   if (grad_hidden) {
     if (p->dtype == STCE_DT_BF16)
       e = launch_transpose_bf16((const bf16*)p->weight, p->H, p->V, p->H, at<bf16>(ws, L.WT), L.Vp, L.Vp, st);
@@ -586,7 +630,7 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
   }
   if (grad_weight && p->dtype != STCE_DT_BF16) {
     // fp32 products take K-major operands only (bf16 reads h as it is)
-    if ((e = launch_transpose_f32((const float*)p->hidden, p->H, p->T, p->H, at<float>(ws, L.hT), L.Tp, L.Tp, st)))
+    if ((e = launch_transpose_f32((const float*)hid, p->H, p->T, p->H, at<float>(ws, L.hT), L.Tp, L.Tp, st)))
       return hip_fail(e, "transpose hidden");
   }
   const int64_t nch = ceil_div(p->T, L.C);
@@ -600,7 +644,7 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
     FwdArgs a{};
     a.dtype = p->dtype;
     a.W = p->weight;
-    a.h = (const char*)p->hidden + es * (size_t)c0 * p->H;
+    a.h = (const char*)hid + es * (size_t)c0 * p->H;
     a.H = p->H;
     a.V = p->V;
     a.rows = nc;
@@ -676,7 +720,7 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
     ga.dT_col = (c % L.G) * L.C;
     ga.WT = at<char>(ws, L.WT);
     ga.hT = at<char>(ws, L.hT);
-    ga.h = p->hidden;
+    ga.h = hid;
     ga.T = p->T;
     ga.dh_part = at<float>(ws, L.dhp);
     ga.splits = (int)L.S;
@@ -693,6 +737,7 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
     ga.H = p->H;
     ga.V = p->V;
     ga.V_pad = L.Vp;
+    ga.dh_div = dh_div;
     if ((e = launch_fused_chunk_grads(ga, st))) return hip_fail(e, "fused gradients");
   }
   return STCE_OK;

@@ -370,11 +370,13 @@ struct EpiAccum {
   OutT* out;   // [M][ld]
   int M, N;
   int first, last;
+  float div = 1.f;  // the last slice writes (sum + acc) / div
   static constexpr int LDS_BYTES = 0;
 
   __device__ inline void operator()(AccTile& acc, int m0, int n0, char*, char*) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
+    const bool scaled = last && div != 1.f;
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) {
       const int n = n0 + acc_col(wn, j, col);
@@ -386,7 +388,8 @@ struct EpiAccum {
           const int m = m0 + acc_row(wm, i, r, quad);
           if (m < M) {
             const int64_t o = (int64_t)m * ld + n;
-            const float v = first ? acc[i][j][r] : sum[o] + acc[i][j][r];
+            float v = first ? acc[i][j][r] : sum[o] + acc[i][j][r];
+            if (scaled) v = v / div;
             if (last)
               out[o] = (OutT)v;
             else
@@ -413,11 +416,13 @@ struct EpiAccumT {
   OutT* out;   // [N][ld]
   int M, N;
   int first, last;
+  float div = 1.f;  // the last slice writes (sum + acc) / div
   static constexpr int LDS_BYTES = 0;
 
   __device__ inline void operator()(AccTile& acc, int m0, int n0, char*, char*) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
+    const bool scaled = last && div != 1.f;
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) {
       const int n = n0 + acc_col(wn, j, col);
@@ -434,6 +439,12 @@ struct EpiAccumT {
           v[1] += s0[1];
           v[2] += s0[2];
           v[3] += s0[3];
+        }
+        if (scaled) {
+          v[0] = v[0] / div;
+          v[1] = v[1] / div;
+          v[2] = v[2] / div;
+          v[3] = v[3] / div;
         }
         if (last) {
           if constexpr (sizeof(OutT) == 2) {

@@ -120,6 +120,33 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* in, int
   }
 }
 
+// out = in / t element by element: the fp32 quotient (IEEE division,
+// correctly rounded) rounded to the operand type, nearest with ties to even.
+// n8 groups of 8 elements, 16-byte aligned; a grid-stride loop.
+template <class E>
+__global__ __launch_bounds__(256) void prescale_kernel(const E* in, int64_t n8, float t, E* out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+    if constexpr (sizeof(E) == 2) {
+      const bf16x8 v = ((const bf16x8*)in)[i];
+      bf16x8 o;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = (bf16)((float)v[k] / t);
+      ((bf16x8*)out)[i] = o;
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 v = ((const f32x4*)in)[2 * i + h];
+        v[0] = v[0] / t;
+        v[1] = v[1] / t;
+        v[2] = v[2] / t;
+        v[3] = v[3] / t;
+        ((f32x4*)out)[2 * i + h] = v;
+      }
+    }
+  }
+}
+
 // One wave per (row, 256-wide tile).
 __global__ void tile_partials_kernel(const float* s, int64_t ld, int64_t R, int64_t V, int ntv,
                                      const int64_t* target, TilePart* part, float* s_y) {
@@ -298,9 +325,10 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_splitk_kernel(Main mainloop,
   ep(acc, tm * GM, tn * GN, Main::epilogue_lds(smem), Main::epilogue_lds1(smem));
 }
 
-// out[i] = part[0][i] + part[1][i] + ... in split order, 4 elements a thread.
+// out[i] = (part[0][i] + part[1][i] + ...) / div, summed in split order, 4
+// elements a thread.
 template <class OutT>
-__global__ void sum_splits_kernel(const float* part, int splits, int64_t pstride, int64_t n4, OutT* out) {
+__global__ void sum_splits_kernel(const float* part, int splits, int64_t pstride, int64_t n4, float div, OutT* out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n4) return;
   f32x4 v = ((const f32x4*)part)[i];
@@ -310,6 +338,12 @@ __global__ void sum_splits_kernel(const float* part, int splits, int64_t pstride
     v[1] += x[1];
     v[2] += x[2];
     v[3] += x[3];
+  }
+  if (div != 1.f) {
+    v[0] = v[0] / div;
+    v[1] = v[1] / div;
+    v[2] = v[2] / div;
+    v[3] = v[3] / div;
   }
   if constexpr (sizeof(OutT) == 2) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -393,6 +427,18 @@ hipError_t launch_transpose_bf16(const bf16* in, int64_t ld_in, int64_t R, int64
   return hipGetLastError();
 }
 
+hipError_t launch_prescale(int dtype, const void* in, int64_t n, float t, void* out, hipStream_t s) {
+  const int64_t n8 = n / 8;
+  if (n8 <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)(ceil_div(n8, 256) < 16384 ? ceil_div(n8, 256) : 16384);
+  ProfScope ps(12, s);
+  if (dtype == 1)
+    hipLaunchKernelGGL(prescale_kernel<bf16>, dim3(blocks), dim3(256), 0, s, (const bf16*)in, n8, t, (bf16*)out);
+  else
+    hipLaunchKernelGGL(prescale_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)in, n8, t, (float*)out);
+  return hipGetLastError();
+}
+
 hipError_t launch_transpose_f32(const float* in, int64_t ld_in, int64_t R, int64_t Cc, float* out,
                                 int64_t ld_out, int64_t R_pad, hipStream_t s) {
   ProfScope ps(7, s);
@@ -463,7 +509,7 @@ hipError_t bwd_slice_impl(const BwdSliceArgs& a, hipStream_t s) {
     else
       e = launch_transpose_f32((const float*)(W + a.v0 * a.H), a.H, a.vs, a.H, (float*)a.WT, a.ld_d, a.vsp, s);
     if (e != hipSuccess) return e;
-    EpiAccum<E> ep{a.dh_sum, a.H, (E*)a.grad_hidden, (int)a.T, (int)a.H, a.first, a.last};
+    EpiAccum<E> ep{a.dh_sum, a.H, (E*)a.grad_hidden, (int)a.T, (int)a.H, a.first, a.last, a.dh_div};
     Main mn{(const E*)a.d, a.ld_d, (int)a.T, (const E*)a.WT, a.ld_d, (int)a.H, (int)a.vsp};
     ProfScope ps(6, s);
     e = launch_gemm(mn, ep, ceil_div(a.T, GM), ceil_div(a.H, GN), s);
@@ -504,7 +550,7 @@ hipError_t bwd_slice_bf16(const BwdSliceArgs& a, hipStream_t s) {
   if (a.grad_hidden) {
     e = launch_transpose_bf16(W + a.v0 * a.H, a.H, a.vs, a.H, (bf16*)a.WT, a.ld_d, a.vsp, s);
     if (e != hipSuccess) return e;
-    EpiAccumT<bf16> ep{a.dh_sum, a.H, (bf16*)a.grad_hidden, (int)a.H, (int)a.T, a.first, a.last};
+    EpiAccumT<bf16> ep{a.dh_sum, a.H, (bf16*)a.grad_hidden, (int)a.H, (int)a.T, a.first, a.last, a.dh_div};
     MainBf16T<false, true> mn{(const bf16*)a.WT, a.ld_d, (int)a.H, dT, a.Tp, (int)a.T, (int)a.vsp, 0, (int)a.vs};
     ProfScope ps(6, s);
     e = launch_gemm(mn, ep, ceil_div(a.H, GM), ceil_div(a.T, GN), s);
@@ -553,7 +599,7 @@ hipError_t fused_grads_impl(const FusedGradArgs& a, hipStream_t s) {
     const int64_t n4 = a.rows * a.H / 4;
     ProfScope ps(11, s);
     hipLaunchKernelGGL(sum_splits_kernel<E>, dim3((unsigned)ceil_div(n4, 256)), dim3(256), 0, s, a.dh_part, a.splits,
-                       a.rows * a.H, n4, (E*)a.grad_hidden);
+                       a.rows * a.H, n4, a.dh_div, (E*)a.grad_hidden);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // 3. weight gradient of a finished group: dW (+)= dz^T . h over the

@@ -29,6 +29,10 @@ hipError_t launch_transpose_bf16(const bf16* in, int64_t ld_in, int64_t R, int64
 hipError_t launch_transpose_f32(const float* in, int64_t ld_in, int64_t R, int64_t Cc, float* out,
                                 int64_t ld_out, int64_t R_pad, hipStream_t s);
 
+// out = in / t for n elements (n a multiple of 8, 16-byte aligned buffers):
+// the fp32 quotient rounded to the operand type (dtype 1 bf16, 2 fp32).
+hipError_t launch_prescale(int dtype, const void* in, int64_t n, float t, void* out, hipStream_t s);
+
 // (max, sum exp, min) of every (row, 256-wide tile) of given keys, and the
 // target key of every row.
 hipError_t launch_tile_partials(const float* s, int64_t ld, int64_t R, int64_t V, int ntv,
@@ -77,6 +81,7 @@ struct BwdSliceArgs {
   const float* g;
   int64_t T, Tp, H, V, v0, vs, vsp, ld_d;
   int first, last;
+  float dh_div;        // the hidden gradient's final value is divided by it (1 = none)
 };
 hipError_t launch_bwd_slice(const BwdSliceArgs& a, hipStream_t s);
 
@@ -112,6 +117,7 @@ struct FusedGradArgs {
   int dw;
   int64_t dw_c0, dw_k;
   int64_t rows, rows_pad, Tp, H, V, V_pad;
+  float dh_div;         // the hidden-gradient rows are divided by it (1 = none)
 };
 hipError_t launch_fused_chunk_grads(const FusedGradArgs& a, hipStream_t s);
 

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_struct_layouts_match_header():
-    assert ctypes.sizeof(binding.Problem) == 112
+    assert ctypes.sizeof(binding.Problem) == 120
     assert ctypes.sizeof(binding.RowInfo) == binding.STATE_BYTES_PER_ROW
 
 
@@ -65,13 +65,45 @@ def test_unsupported_dtype_is_one_actionable_error(lib):
 
 
 @pytest.mark.parametrize("kw,msg", [
-    (dict(T=0), "T=0"), (dict(H=12), "H=12"), (dict(V=0), "V=0"), (dict(flags=2), "flags"),
+    (dict(T=0), "T=0"), (dict(H=12), "H=12"), (dict(V=0), "V=0"), (dict(flags=4), "flags"),
     (dict(flags=1, ignore_index=5), "ignore_index=5"),
     (dict(chunk_rows=-1), "chunk_rows"),
 ])
 def test_bad_shapes_are_rejected(lib, kw, msg):
     with pytest.raises(binding.StceError, match=msg):
         binding.workspace_bytes(_prob(**kw))
+
+
+@pytest.mark.parametrize("ts", [0.0, -0.5, float("nan"), float("inf")])
+def test_bad_pre_gemm_temperature_is_rejected(lib, ts):
+    with pytest.raises(binding.StceError, match="pre_gemm_temperature"):
+        binding.workspace_bytes(_prob(flags=binding.PROBLEM_PRE_GEMM_TEMPERATURE, pre_gemm_temperature=ts))
+
+
+def test_pre_gemm_temperature_workspaces_hold_the_scaled_hidden(lib):
+    """The scalar pre-GEMM convention keeps h / Ts (operand dtype, T x H) in
+    every workspace; nothing else changes."""
+    for dt, es in ((binding.DT_BF16, 2), (binding.DT_F32, 4)):
+        base = _prob(T=1000, H=136, V=5000, dtype=dt)
+        pre = _prob(T=1000, H=136, V=5000, dtype=dt, flags=binding.PROBLEM_PRE_GEMM_TEMPERATURE,
+                    pre_gemm_temperature=0.7)
+        hs = -(-1000 * 136 * es // 256) * 256
+        f0, b0 = binding.workspace_bytes(base)
+        f1, b1 = binding.workspace_bytes(pre)
+        assert (f1 - f0, b1 - b0) == (hs, hs)
+        assert binding.fused_workspace_bytes(pre)[0] - binding.fused_workspace_bytes(base)[0] == hs
+        assert binding.schedule(pre) == binding.schedule(base)
+
+
+def test_pre_gemm_temperature_excludes_the_per_row_array(lib):
+    p = _prob(flags=binding.PROBLEM_PRE_GEMM_TEMPERATURE, pre_gemm_temperature=0.7)
+    p.hidden, p.weight, p.target, p.temperature = 16, 16, 16, 16    # fake, never dereferenced
+    st = lib.stce_forward(ctypes.byref(p), ctypes.c_void_p(16), ctypes.c_void_p(16), None, None, 0, None)
+    assert st == 1 and b"do not combine" in lib.stce_last_error()
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError, match="not both"):
+        binding.make_problem(torch.zeros(2, 8), torch.zeros(3, 8), torch.zeros(2, dtype=torch.int64),
+                             torch.ones(2), pre_gemm_temperature=0.7)
 
 
 def test_forward_rejects_null_and_small_workspace_before_launch(lib):
