@@ -4,7 +4,7 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may use this package; the HIP library never does.
 """
 from .stce_oracle import (  # noqa: F401
-    MARGIN, backward, backward_pre_gemm, canonical_f32, chunk_logits, dlogits, forward, in_support,
+    MARGIN, backward, backward_pre_gemm, bf16_lane_keys, canonical_f32, chunk_logits, dlogits, forward, in_support,
     OBJECTIVES, order_keys, order_row, policy_loss, pre_gemm_hidden, round_to_bf16, sample_targets,
     scale_logits, support, support_row,
 )

@@ -59,17 +59,32 @@ so the per-token losses are ``-A sg(min(r, 1+eps_high)) logprob`` and
 (the reciprocal of a constant denominator).  The gradient then flows
 through the same VJP as the logprob with ``g = d loss / d logprob``.
 
-A second temperature convention ([xorl#74] self-review pass: "the scalar
-(pre-GEMM) vs per-row-tensor (post-GEMM) temperature convention split is now
-documented"; "What this PR does" 1: temperature first, at the lane's dtype
-boundary).  The pages name it without its formula; read plainly: one scalar
-T divides the hidden state before the projection, in fp32, and the quotient
-is rounded to the operand dtype, ``h' = round(fl32(h) / T)``; the keys are
-then ``s = fl32(h' W^T)`` (no per-row division) and the VJP carries the 1/T
-to the hidden state, ``dH = (dz W) / T`` with ``dz = g (onehot - q)``, and
+A second temperature convention ([xorl#74] self-review pass, which records
+that a scalar temperature applied before the projection and a per-row one
+applied after it are two documented conventions; "What this PR does" 1:
+temperature is applied first, at the dtype boundary of the lane).  The pages
+name it without its formula; read plainly: one scalar T divides the hidden
+state before the projection, in fp32, and the quotient is rounded to the
+operand dtype, ``h' = round(fl32(h) / T)``; the keys are then
+``s = fl32(h' W^T)`` (no per-row division) and the VJP carries the 1/T to the
+hidden state, ``dH = (dz W) / T`` with ``dz = g (onehot - q)``, and
 ``dW = dz^T h'`` (the rounding of ``h'`` passes gradients unchanged).
 ``pre_gemm_hidden`` and ``backward_pre_gemm`` below; ``forward`` takes ``h'``
 with no per-row temperature.
+
+A bf16 value lane ([xorl#74] deduplication and review passes: one model
+family's exact head runs its value program in bf16 from end to end, with a
+bf16 base projection, its own temperature dtype boundary and a bf16 selected
+logprob, the expected logprob dtype being part of the family's contract).
+The pages give no formula; read plainly, every value the program hands on
+is a bf16 tensor: the projection's fp32 result is rounded to bf16,
+``z_b = bf16(fl32(h W^T))``; the temperature divides that value in fp32 and
+the quotient is rounded to bf16 again, ``s = bf16(fl32(z_b / T))``; the
+support and the log-sum-exp are taken on these keys (accumulated at higher
+precision, as a bf16 log-softmax does), and the selected logprob is rounded
+to bf16 at the end.  The VJP is the one of ``s_y - lse_S(s)`` with the two
+roundings passing gradients unchanged, so ``q`` comes from the bf16 keys.
+``bf16_lane_keys`` and ``forward(lane="bf16")`` / ``backward(lane="bf16")``.
 
 Values (logprob, gradients) use the unrounded fp64 logits ``u = z / T``.
 Support decisions use only the fp32 keys, so a caller may pass the keys of
@@ -235,7 +250,7 @@ def _meta(R, top_k, top_p, min_p):
 # forward and backward
 # --------------------------------------------------------------------------
 def forward(h, W, target, temperature=None, top_k=None, top_p=None, min_p=None,
-            keys=None, rows=None, ignore_index=None) -> dict:
+            keys=None, rows=None, ignore_index=None, lane="fp32") -> dict:
     """Selected logprob on the filtered support, per row.
 
     ``h`` [T, H] and ``W`` [V, H] hold the operand values (bf16 or fp32 values,
@@ -246,12 +261,15 @@ def forward(h, W, target, temperature=None, top_k=None, top_p=None, min_p=None,
     whose target equals it are inactive ([nested-learning]
     ``compute_teach_signal``: such rows are masked out of the residual):
     logprob 0 and an exactly zero gradient; their support and side outputs
-    are still computed.
+    are still computed.  ``lane="bf16"``: the bf16 value program (keys from
+    ``bf16_lane_keys``, values taken from those keys, logprob rounded to
+    bf16); the default is the fp32 program.
 
     Returns per selected row: ``logprob`` (fp64, -inf out of support),
     ``lse`` (log-sum-exp of z/T over the support), ``n``, ``key_thr``,
     ``id_thr``, ``in_support``, ``near``, and the keys used; and the side
-    outputs of one sweep ([align-v2] 5.4 A: "entropy from the same sweep"):
+    outputs of one sweep ([align-v2] 5.4 A: the entropy comes out of the
+    same pass over the logits):
     ``lse_full`` (log-sum-exp of z/T over the whole row), ``entropy_full``
     (Shannon entropy, in nats, of softmax(z/T) over the whole row) and
     ``entropy_support`` (entropy of the filtered distribution q on the
@@ -263,9 +281,16 @@ def forward(h, W, target, temperature=None, top_k=None, top_p=None, min_p=None,
     temp = np.ones(T, np.float32) if temperature is None else np.asarray(temperature, np.float32)
     tk, tp, mp = _meta(T, top_k, top_p, min_p)
     _check_temperature(temp[rows])
+    assert lane in ("fp32", "bf16"), lane
     z = chunk_logits(h[rows], W)                              # fp64 [R, V]
-    s32 = scale_logits(z, temp[rows]) if keys is None else canonical_f32(keys)
-    u = z / temp[rows].astype(np.float64)[:, None]            # values: fp64
+    if keys is not None:
+        s32 = canonical_f32(keys)
+    elif lane == "bf16":
+        s32 = bf16_lane_keys(z, temp[rows])
+    else:
+        s32 = scale_logits(z, temp[rows])
+    # values: fp64 z / T, or in the bf16 lane the bf16 keys themselves
+    u = z / temp[rows].astype(np.float64)[:, None] if lane == "fp32" else s32.astype(np.float64)
     R, V = z.shape
     tgt = np.asarray(target, np.int64)[rows]
     ignored = np.zeros(R, bool) if ignore_index is None else tgt == int(ignore_index)
@@ -275,7 +300,7 @@ def forward(h, W, target, temperature=None, top_k=None, top_p=None, min_p=None,
                key_thr=np.empty(R, np.uint32), id_thr=np.empty(R, np.int64),
                in_support=np.empty(R, bool), near=np.empty(R, bool), keys=s32,
                rows=rows, lse_full=np.empty(R), entropy_full=np.empty(R), entropy_support=np.empty(R),
-               ignored=ignored)
+               ignored=ignored, lane=lane)
     for i, t in enumerate(rows):
         d = support_row(s32[i], tk[t], tp[t], mp[t])
         S = d["pi"][: d["n"]]
@@ -283,6 +308,8 @@ def forward(h, W, target, temperature=None, top_k=None, top_p=None, min_p=None,
         lse = mx + math.log(np.exp(u[i, S] - mx).sum())
         inside = bool(np.isin(tgt[i], S)) and not ignored[i]
         lp = 0.0 if ignored[i] else (min(u[i, tgt[i]] - lse, 0.0) if inside else -math.inf)
+        if lane == "bf16":
+            lp = float(round_to_bf16(np.float32(lp)))             # the lane's logprob dtype
         out["logprob"][i] = lp
         out["lse"][i] = lse
         out["n"][i] = d["n"]
@@ -306,15 +333,16 @@ def _entropy(x) -> tuple:
 def dlogits(h, W, target, fwd: dict, grad_logprob, temperature=None) -> np.ndarray:
     """``dz[r, j] = g_r (1[j = y_r] - q_rj) / T_r`` on the rows of ``fwd``.
 
-    ``q`` is the softmax of ``z / T`` restricted to the support.  Rows whose
-    target is out of support get an exactly zero row whatever ``g`` is.
+    ``q`` is the softmax of ``z / T`` restricted to the support (in the bf16
+    lane of ``fwd``, the softmax of its bf16 keys).  Rows whose target is out
+    of support get an exactly zero row whatever ``g`` is.
     """
     rows = fwd["rows"]
     T = np.asarray(h).shape[0]
     temp = np.ones(T, np.float32) if temperature is None else np.asarray(temperature, np.float32)
     z = chunk_logits(np.asarray(h)[rows], W)
     t64 = temp[rows].astype(np.float64)
-    u = z / t64[:, None]
+    u = z / t64[:, None] if fwd.get("lane", "fp32") == "fp32" else fwd["keys"].astype(np.float64)
     g = np.asarray(grad_logprob, np.float64)[rows]
     tgt = np.asarray(target, np.int64)[rows]
     dz = np.zeros_like(z)
@@ -348,6 +376,14 @@ def round_to_bf16(x) -> np.ndarray:
     b = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
     b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
     return b.astype(np.uint32).view(np.float32)
+
+
+def bf16_lane_keys(z, temperature) -> np.ndarray:
+    """Keys of the bf16 value lane from the logits ``z`` [R, V] (fp64): the
+    projection's fp32 value rounded to bf16, divided by the row's temperature
+    in fp32 (correctly rounded), and rounded to bf16 again."""
+    zb = round_to_bf16(np.asarray(z, np.float64).astype(np.float32))
+    return canonical_f32(round_to_bf16(scale_logits(zb, temperature)))
 
 
 def pre_gemm_hidden(h, temperature, operand="bf16") -> np.ndarray:

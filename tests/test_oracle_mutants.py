@@ -70,6 +70,18 @@ MUTANTS = {
     "bf16 rounding half up": ("    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000",
                               "    b = (b + 0x8000) & 0xFFFF0000",
                               ["test_round_to_bf16_matches_torch_and_ties_to_even"]),
+    "bf16 lane skips the projection's rounding": (
+        "    zb = round_to_bf16(np.asarray(z, np.float64).astype(np.float32))",
+        "    zb = np.asarray(z, np.float64).astype(np.float32)",
+        ["test_bf16_lane_keys_follow_the_value_program_exactly"]),
+    "bf16 lane logprob not rounded": (
+        "            lp = float(round_to_bf16(np.float32(lp)))             # the lane's logprob dtype",
+        "            lp = float(lp)",
+        ["test_bf16_lane_logprob_is_the_bf16_log_softmax_of_the_keys"]),
+    "bf16 lane gradient from the fp64 logits": (
+        '    u = z / t64[:, None] if fwd.get("lane", "fp32") == "fp32" else fwd["keys"].astype(np.float64)',
+        "    u = z / t64[:, None]",
+        ["test_bf16_lane_gradient_is_the_straight_through_vjp"]),
 }
 
 

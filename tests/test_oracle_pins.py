@@ -657,3 +657,93 @@ def test_pre_gemm_gradient_matches_autograd(rng):
     total.backward()
     for a, b in ((dH, H64.grad.numpy()), (dW, W64.grad.numpy())):
         assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-6
+
+
+# ---------------------------------------------------------------- bf16 value lane
+def _bf16_round_exact(q: Fraction) -> Fraction:
+    """An exact rational rounded to 8 significant bits, nearest with ties to
+    even (normal range), in exact arithmetic."""
+    if q == 0:
+        return Fraction(0)
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    ulp = Fraction(2) ** (e - 7)
+    m = a / ulp                                   # in [128, 256)
+    n = m.numerator // m.denominator
+    r = m - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return (n * ulp) if q > 0 else -(n * ulp)
+
+
+def _lane_problem(rng, T=6, H=16, V=40):
+    h = oracle.round_to_bf16(rng.standard_normal((T, H)).astype(np.float32) * 2)
+    W = oracle.round_to_bf16(rng.standard_normal((V, H)).astype(np.float32))
+    temp = rng.uniform(0.1, 3.0, T).astype(np.float32)
+    return h, W, temp
+
+
+def test_bf16_lane_keys_follow_the_value_program_exactly(rng):
+    """Each key is bf16(fl32(bf16(fl32(z)) / T)), every step an exact
+    rational rounding; keys are bf16 values."""
+    h, W, temp = _lane_problem(rng)
+    z64 = h.astype(np.float64) @ W.astype(np.float64).T
+    s = oracle.bf16_lane_keys(z64, temp)
+    assert np.all((s.view(np.uint32) & 0xFFFF) == 0)
+    for t in range(h.shape[0]):
+        for j in range(W.shape[0]):
+            z = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(h[t], W[j]))
+            zb = _bf16_round_exact(Fraction(float(_f32_round_exact(z))))
+            q = _f32_round_exact(zb / Fraction(float(temp[t])))
+            want = _bf16_round_exact(Fraction(float(q)))
+            assert Fraction(float(s[t, j])) == want, (t, j)
+    # small integer logits at T = 1 are bf16 values: the keys are the logits
+    hi = np.float32(rng.integers(-3, 4, (4, 8)))
+    Wi = np.float32(rng.integers(-3, 4, (10, 8)))
+    zi = hi.astype(np.float64) @ Wi.astype(np.float64).T
+    assert np.array_equal(oracle.bf16_lane_keys(zi, np.ones(4, np.float32)), zi.astype(np.float32) + 0)
+
+
+def test_bf16_lane_logprob_is_the_bf16_log_softmax_of_the_keys(rng):
+    torch = pytest.importorskip("torch")
+    from scipy.special import log_softmax
+    h, W, temp = _lane_problem(rng, T=8, V=50)
+    y = rng.integers(0, 50, 8)
+    f = oracle.forward(h, W, y, temp, lane="bf16")
+    ref = np.minimum(log_softmax(f["keys"].astype(np.float64), axis=1)[np.arange(8), y], 0)
+    want = torch.from_numpy(ref).float().bfloat16().double().numpy()
+    assert np.array_equal(f["logprob"], want)
+    # top-k 1 keeps the lowest-id maximum only: logprob exactly 0
+    yk = np.array([oracle.order_row(f["keys"][t])[0] for t in range(8)])
+    fk = oracle.forward(h, W, yk, temp, top_k=np.ones(8, np.int32), lane="bf16")
+    assert np.all(fk["logprob"] == 0.0)
+
+
+def test_bf16_lane_gradient_is_the_straight_through_vjp(rng):
+    """fp64 autograd of sum_r g_r (u[r, y_r] - logsumexp of u[r] over the
+    support), u = z / T carrying the bf16 keys' values (the roundings pass
+    gradients unchanged)."""
+    torch = pytest.importorskip("torch")
+    T, V = 5, 30
+    h, W, temp = _lane_problem(rng, T=T, V=V)
+    meta = dict(top_k=np.array([0, 4, 0, 0, 7]), top_p=np.array([1.0, 1.0, 0.7, 1.0, 0.95], np.float32),
+                min_p=np.array([0.0, 0.0, 0.0, 0.2, 0.0], np.float32))
+    f0 = oracle.forward(h, W, np.zeros(T, np.int64), temp, **meta, lane="bf16")
+    y = np.array([oracle.order_row(f0["keys"][t])[0] for t in range(T)])
+    f = oracle.forward(h, W, y, temp, **meta, lane="bf16")
+    assert f["in_support"].all()
+    g = rng.standard_normal(T)
+    dH, dW = oracle.backward(h, W, y, f, g, temp)
+    th = torch.tensor(h, dtype=torch.float64, requires_grad=True)
+    tW = torch.tensor(W, dtype=torch.float64, requires_grad=True)
+    zt = (th @ tW.T) / torch.tensor(temp, dtype=torch.float64)[:, None]
+    u = zt + (torch.tensor(f["keys"], dtype=torch.float64) - zt).detach()
+    L = 0
+    for t in range(T):
+        S = torch.tensor(oracle.order_row(f["keys"][t])[: f["n"][t]])
+        L = L + float(g[t]) * (u[t, int(y[t])] - torch.logsumexp(u[t, S], 0))
+    L.backward()
+    np.testing.assert_allclose(dH, th.grad.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dW, tW.grad.numpy(), rtol=1e-12, atol=1e-14)
