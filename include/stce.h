@@ -95,6 +95,20 @@ typedef enum {
 #define STCE_PROBLEM_PRE_GEMM_TEMPERATURE 2 /* one scalar temperature applied to the hidden
                                               states before the projection: see
                                               stce_problem.pre_gemm_temperature */
+#define STCE_PROBLEM_BF16_LANE 4 /* the bf16 value lane (bf16 operands only), read from
+                                    the xorl pull request's deduplication and review
+                                    passes, where one model family runs its value
+                                    program in bf16 from end to end and its logprob
+                                    dtype is part of the family's contract: the
+                                    projection's fp32 result is rounded to bf16,
+                                    divided by the row's temperature in fp32 and
+                                    rounded to bf16 again, s = bf16(fl32(bf16(z) / T));
+                                    the support and log-sum-exps are taken on these
+                                    keys, and the selected logprob is rounded to bf16
+                                    (still written as fp32, so every value is exact in
+                                    a bf16 tensor).  Gradients treat both roundings as
+                                    identity: q comes from the bf16 keys.  Without a
+                                    bf16 hidden/weight: STCE_E_UNSUPPORTED. */
 
 /* Bytes of per-row state stce_forward writes and stce_backward reads. */
 #define STCE_STATE_BYTES_PER_ROW 32

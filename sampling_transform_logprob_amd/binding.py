@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libstce.so")
 STATUS_NONE = (1 << 63) - 1
 FIELDS = {1: "temperature", 2: "top_k", 3: "top_p", 4: "min_p", 5: "target"}
 FLAG_VALID, FLAG_FILTERED, FLAG_IN_SUPPORT, FLAG_IGNORED = 1, 2, 4, 8
-PROBLEM_IGNORE_INDEX, PROBLEM_PRE_GEMM_TEMPERATURE = 1, 2
+PROBLEM_IGNORE_INDEX, PROBLEM_PRE_GEMM_TEMPERATURE, PROBLEM_BF16_LANE = 1, 2, 4
+LANES = {"fp32": 0, "bf16": PROBLEM_BF16_LANE}
 STATE_BYTES_PER_ROW = 32
 DT_BF16, DT_F32 = 1, 2
 
@@ -147,12 +148,16 @@ def _meta(name, t, T, dtype, device):
 
 def make_problem(hidden, weight, target, temperature=None, top_k=None, top_p=None, min_p=None,
                  chunk_rows: int = 0, vocab_slice: int = 0, ignore_index: Optional[int] = None,
-                 pre_gemm_temperature: Optional[float] = None):
+                 pre_gemm_temperature: Optional[float] = None, lane: str = "fp32"):
     """Checked ``stce_problem`` plus the tensors it points into (kept alive).
 
     ``temperature`` is the per-row tensor applied to the logits after the
     product; ``pre_gemm_temperature`` is instead one scalar applied to the
-    hidden states before it (the two do not combine)."""
+    hidden states before it (the two do not combine).  ``lane="bf16"`` runs
+    the bf16 value program (bf16 keys; the logprob, still an fp32 tensor,
+    holds bf16 values, so ``.bfloat16()`` is exact)."""
+    if lane not in LANES:
+        raise ValueError(f"lane must be one of {tuple(LANES)}")
     if pre_gemm_temperature is not None and temperature is not None:
         raise ValueError("pass either a per-row temperature tensor or pre_gemm_temperature, not both")
     if hidden.dim() != 2 or weight.dim() != 2 or hidden.shape[1] != weight.shape[1]:
@@ -178,7 +183,7 @@ def make_problem(hidden, weight, target, temperature=None, top_k=None, top_p=Non
             _meta("top_k", top_k, T, torch.int32, dev),
             _meta("top_p", top_p, T, torch.float32, dev),
             _meta("min_p", min_p, T, torch.float32, dev)]
-    flags = 0 if ignore_index is None else PROBLEM_IGNORE_INDEX
+    flags = (0 if ignore_index is None else PROBLEM_IGNORE_INDEX) | LANES[lane]
     if pre_gemm_temperature is not None:
         flags |= PROBLEM_PRE_GEMM_TEMPERATURE
     prob = Problem(T, H, V, dt, flags, *[t.data_ptr() if t is not None else None for t in keep], chunk_rows,
@@ -213,14 +218,15 @@ def _raise_rows(status: torch.Tensor, what: str, tensors: dict) -> None:
 
 def forward(hidden, weight, target, temperature=None, top_k=None, top_p=None, min_p=None, *,
             chunk_rows: int = 0, check: bool = True, workspace: Optional[torch.Tensor] = None,
-            side: bool = False, ignore_index: Optional[int] = None, pre_gemm_temperature: Optional[float] = None):
+            side: bool = False, ignore_index: Optional[int] = None, pre_gemm_temperature: Optional[float] = None,
+            lane: str = "fp32"):
     """Selected logprob per row and the 32-byte-per-row state for backward.
 
     With ``side=True`` also returns a dict of the sweep's side outputs
     (``lse_full``, ``entropy_full``, ``entropy_support``, fp32 [T]).
     """
     prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, chunk_rows,
-                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature)
+                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane)
     T = prob.T
     fwd_b, _ = workspace_bytes(prob)
     dev = hidden.device
@@ -248,10 +254,10 @@ def backward(hidden, weight, target, state, grad_logprob, temperature=None, top_
              min_p=None, *, need_hidden: bool = True, need_weight: bool = True,
              grad_weight: Optional[torch.Tensor] = None, accumulate_grad_weight: bool = False,
              vocab_slice: int = 0, workspace: Optional[torch.Tensor] = None, ignore_index: Optional[int] = None,
-             pre_gemm_temperature: Optional[float] = None):
+             pre_gemm_temperature: Optional[float] = None, lane: str = "fp32"):
     """(grad_hidden [T, H] in hidden's dtype, grad_weight [V, H] fp32)."""
     prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, 0, vocab_slice,
-                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature)
+                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane)
     T, H, V = prob.T, prob.H, prob.V
     dev = hidden.device
     if grad_logprob.shape != (T,) or grad_logprob.dtype != torch.float32 or grad_logprob.device != dev:
@@ -276,14 +282,15 @@ def backward(hidden, weight, target, state, grad_logprob, temperature=None, top_
 
 
 def scaled_logits(hidden, weight, temperature=None, row0: int = 0, nrows: Optional[int] = None, *,
-                  pre_gemm_temperature: Optional[float] = None):
+                  pre_gemm_temperature: Optional[float] = None, lane: str = "fp32"):
     """fp32 keys of rows [row0, row0 + nrows) from the forward's kernel:
     s = fl32(h W^T) / T per row, or fl32((h / Ts) W^T) with the scalar
-    pre-GEMM temperature Ts."""
+    pre-GEMM temperature Ts; in the bf16 lane the bf16 keys."""
     T = hidden.shape[0]
     nrows = T - row0 if nrows is None else nrows
     target = torch.zeros(T, dtype=torch.int64, device=hidden.device)
-    prob, keep = make_problem(hidden, weight, target, temperature, pre_gemm_temperature=pre_gemm_temperature)
+    prob, keep = make_problem(hidden, weight, target, temperature, pre_gemm_temperature=pre_gemm_temperature,
+                              lane=lane)
     fwd_b, _ = workspace_bytes(prob)
     ws = torch.empty(max(fwd_b, 1), dtype=torch.uint8, device=hidden.device)
     out = torch.empty(nrows, prob.V, dtype=torch.float32, device=hidden.device)
@@ -345,16 +352,17 @@ def policy_loss(logprob, advantages, old_logprob, objective: str = "cispo", eps_
 def policy_loss_step(hidden, weight, target, advantages, old_logprob, temperature=None, top_k=None, top_p=None,
                      min_p=None, *, objective: str = "cispo", eps_low: float = 0.2, eps_high: float = 0.28,
                      scale: float = 1.0, need_hidden: bool = True, need_weight: bool = True,
-                     ignore_index: Optional[int] = None, pre_gemm_temperature: Optional[float] = None):
+                     ignore_index: Optional[int] = None, pre_gemm_temperature: Optional[float] = None,
+                     lane: str = "fp32"):
     """Fused head + policy-gradient token loss: forward, per-token loss and
     the gradients of ``sum(loss)``.  Returns (loss [T], logprob [T], ratio [T],
     grad_hidden, grad_weight)."""
     logprob, state = forward(hidden, weight, target, temperature, top_k, top_p, min_p, ignore_index=ignore_index,
-                             pre_gemm_temperature=pre_gemm_temperature)
+                             pre_gemm_temperature=pre_gemm_temperature, lane=lane)
     loss, g, ratio = policy_loss(logprob, advantages, old_logprob, objective, eps_low, eps_high, scale, state)
     gh, gw = backward(hidden, weight, target, state, g, temperature, top_k, top_p, min_p,
                       need_hidden=need_hidden, need_weight=need_weight, ignore_index=ignore_index,
-                      pre_gemm_temperature=pre_gemm_temperature)
+                      pre_gemm_temperature=pre_gemm_temperature, lane=lane)
     return loss, logprob, ratio, gh, gw
 
 
@@ -372,7 +380,7 @@ def fused_policy_step(hidden, weight, target, advantages, old_logprob, temperatu
                       grad_weight: Optional[torch.Tensor] = None, accumulate_grad_weight: bool = False,
                       side: bool = False, chunk_rows: int = 0, ignore_index: Optional[int] = None,
                       check: bool = True, workspace: Optional[torch.Tensor] = None,
-                      pre_gemm_temperature: Optional[float] = None):
+                      pre_gemm_temperature: Optional[float] = None, lane: str = "fp32"):
     """The fused head + policy-gradient step (dlogits formed in the forward's
     sweep, no recompute).  Returns a dict with ``loss``, ``logprob``,
     ``ratio`` (fp32 [T]), ``state``, ``grad_hidden`` ([T, H], hidden's dtype,
@@ -381,7 +389,7 @@ def fused_policy_step(hidden, weight, target, advantages, old_logprob, temperatu
     if objective not in PG_OBJECTIVES:
         raise ValueError(f"objective must be one of {tuple(PG_OBJECTIVES)}")
     prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, chunk_rows,
-                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature)
+                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane)
     T, H, V = prob.T, prob.H, prob.V
     dev = hidden.device
     adv = _meta("advantages", advantages, T, torch.float32, dev)

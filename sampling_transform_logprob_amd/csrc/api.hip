@@ -53,6 +53,8 @@ struct Layout {
 // The scalar pre-GEMM temperature: the problem's hidden states are replaced
 // by h' = h / Ts (rounded to the operand type), written to the workspace.
 bool pre_gemm(const stce_problem* p) { return (p->flags & STCE_PROBLEM_PRE_GEMM_TEMPERATURE) != 0; }
+// The bf16 value lane: bf16 keys and a bf16 logprob.
+int bf16_lane(const stce_problem* p) { return (p->flags & STCE_PROBLEM_BF16_LANE) ? 1 : 0; }
 
 size_t elt_size(int dtype) { return dtype == STCE_DT_BF16 ? 2 : 4; }
 size_t hs_bytes(const stce_problem* p) {
@@ -61,7 +63,7 @@ size_t hs_bytes(const stce_problem* p) {
 
 stce_status check_shapes(const stce_problem* p) {
   if (!p) return fail(STCE_E_ARG, "problem is NULL");
-  if (p->flags & ~(STCE_PROBLEM_IGNORE_INDEX | STCE_PROBLEM_PRE_GEMM_TEMPERATURE))
+  if (p->flags & ~(STCE_PROBLEM_IGNORE_INDEX | STCE_PROBLEM_PRE_GEMM_TEMPERATURE | STCE_PROBLEM_BF16_LANE))
     return fail(STCE_E_ARG, "problem.flags=%d has unknown bits", (int)p->flags);
   if (pre_gemm(p) && !(__builtin_isfinite(p->pre_gemm_temperature) && p->pre_gemm_temperature > 0.0f))
     return fail(STCE_E_ARG, "pre_gemm_temperature=%g must be finite and > 0", (double)p->pre_gemm_temperature);
@@ -73,6 +75,8 @@ stce_status check_shapes(const stce_problem* p) {
                 "(STCE_DT_F32); quantized (e.g. fp8) LM heads are not scored -- keep an fp32/bf16 copy of "
                 "lm_head.weight for scoring",
                 (int)p->dtype);
+  if (bf16_lane(p) && p->dtype != STCE_DT_BF16)
+    return fail(STCE_E_UNSUPPORTED, "the bf16 value lane (STCE_PROBLEM_BF16_LANE) takes bf16 hidden and weight");
   if (p->T < 1 || p->T > INT32_MAX - 512) return fail(STCE_E_ARG, "T=%lld out of range [1, 2^31-513]", (long long)p->T);
   if (p->H < 8 || p->H % 8 != 0 || p->H > (1 << 20))
     return fail(STCE_E_ARG, "H=%lld must be a positive multiple of 8 (<= 2^20)", (long long)p->H);
@@ -383,6 +387,7 @@ stce_status stce_forward_with_side(const stce_problem* p, float* logprob, void* 
     a.ntv = (int)L.ntv;
     a.s_y = at<float>(ws, L.f_sy + b * L.buf_sy);
     a.want_ent = want_ent;
+    a.bf16_lane = bf16_lane(p);
     if ((e = launch_fwd_projection(a, st))) return hip_fail(e, "projection");
     hipStream_t ss = st;
     if (side) {
@@ -407,6 +412,7 @@ stce_status stce_forward_with_side(const stce_problem* p, float* logprob, void* 
     sp.lse_full = so_lse ? so_lse + c0 : nullptr;
     sp.ent_full = so_hf ? so_hf + c0 : nullptr;
     sp.ent_supp = so_hs ? so_hs + c0 : nullptr;
+    sp.round_lp_bf16 = bf16_lane(p);
     launch_select(sp, (int)nc, ss);
     if ((e = hipGetLastError())) return hip_fail(e, "select");
     if (side && (e = hipEventRecord(side->ev[2 * c + 1], ss))) return hip_fail(e, "selection event");
@@ -475,6 +481,7 @@ stce_status stce_backward(const stce_problem* p, const float* grad_logprob, cons
     a.first = si == 0;
     a.last = si == nsl - 1;
     a.dh_div = dh_div;
+    a.bf16_lane = bf16_lane(p);
     if ((e = launch_bwd_slice(a, st))) return hip_fail(e, "backward slice");
   }
   return STCE_OK;
@@ -513,6 +520,7 @@ stce_status stce_scaled_logits(const stce_problem* p, int64_t row0, int64_t nrow
     a.part = at<TilePart>(ws, L.f_part);
     a.ntv = (int)L.ntv;
     a.s_y = nullptr;
+    a.bf16_lane = bf16_lane(p);
     hipError_t e = launch_fwd_projection(a, st);
     if (e) return hip_fail(e, "projection");
   }
@@ -658,6 +666,7 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
     a.ntv = (int)L.ntv;
     a.s_y = at<float>(ws, L.sy + b * L.buf_sy);
     a.want_ent = (so_hf || so_hs) ? 1 : 0;
+    a.bf16_lane = bf16_lane(p);
     hipError_t e2;
     if ((e2 = launch_fwd_projection(a, st))) return hip_fail(e2, "projection");
     hipStream_t ss = st;
@@ -683,6 +692,7 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
     sp.lse_full = so_lse ? so_lse + c0 : nullptr;
     sp.ent_full = so_hf ? so_hf + c0 : nullptr;
     sp.ent_supp = so_hs ? so_hs + c0 : nullptr;
+    sp.round_lp_bf16 = bf16_lane(p);
     launch_select(sp, (int)nc, ss);
     if ((e2 = hipGetLastError())) return hip_fail(e2, "select");
     if (side && (e2 = hipEventRecord(side->ev[2 * c + 1], ss))) return hip_fail(e2, "selection event");

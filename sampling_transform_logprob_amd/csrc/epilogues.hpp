@@ -65,6 +65,21 @@ __device__ inline void scale_column(AccTile& acc, int j, float t) {
   }
 }
 
+// The keys of column j from its fp32 products: s = fl32(z / t), or in the
+// bf16 value lane s = bf16(fl32(bf16(z) / t)) (both roundings to nearest,
+// ties to even).
+__device__ inline void round_column_bf16(AccTile& acc, int j) {
+#pragma unroll
+  for (int i = 0; i < ACC_I; ++i)
+#pragma unroll
+    for (int r = 0; r < ACC_R; ++r) acc[i][j][r] = (float)(bf16)acc[i][j][r];
+}
+__device__ inline void keys_column(AccTile& acc, int j, float t, bool bf16_lane) {
+  if (bf16_lane) round_column_bf16(acc, j);
+  scale_column(acc, j, t);
+  if (bf16_lane && t != 1.0f) round_column_bf16(acc, j);
+}
+
 constexpr float LOG2E = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
@@ -87,6 +102,7 @@ struct EpiLogits {
   int V;                   // valid vocabulary rows
   int N;                   // valid tokens
   int want_ent;            // store the per-tile sum of exp(s - max) (s - max)
+  int bf16_lane;           // keys of the bf16 value lane
   static constexpr int LDS_BYTES = 2 * GN * 4 * 4;  // cross-wave merge
 
   __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem, char*) const {
@@ -100,7 +116,7 @@ struct EpiLogits {
       const int n = n0 + acc_col(wn, j, col);
       const bool nv = n < N;
       const float t = (nv && temp) ? temp[n] : 1.0f;
-      scale_column(acc, j, t);
+      keys_column(acc, j, t, bf16_lane);
       float mx = -STCE_INF, mn = STCE_INF;
       if (full) {
 #pragma unroll
@@ -237,6 +253,7 @@ struct EpiDlogits {
   OutT* dT;                // [Vs_pad][ld_dT]
   int64_t ld_dT;
   int v0, Vs, Vs_pad, N, N_pad;
+  int bf16_lane = 0;       // keys of the bf16 value lane
   // bf16: the vocab-major tile leaves through LDS, 128 rows in each of the
   // two epilogue buffers
   static constexpr int LDS_BYTES = sizeof(OutT) == 2 ? 128 * GN * 2 : 0;
@@ -259,7 +276,7 @@ struct EpiDlogits {
         if ((rs.flags & (ROW_VALID | ROW_IN_SUPPORT)) == (ROW_VALID | ROW_IN_SUPPORT)) c = g[n] / t;
       }
       if (n >= N_pad) continue;
-      scale_column(acc, j, t);
+      keys_column(acc, j, t, bf16_lane);
       // support membership as a float compare against the boundary key's
       // value (-0 == +0 like the canonical keys); unfiltered rows keep all
       const float sthr = (rs.flags & ROW_FILTERED) ? key_value(rs.key_thr) : -STCE_INF;

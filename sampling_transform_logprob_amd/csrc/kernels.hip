@@ -468,6 +468,7 @@ hipError_t launch_fwd_projection(const FwdArgs& a, hipStream_t s) {
   ep.ntv = a.ntv;
   ep.s_y = a.s_y;
   ep.want_ent = a.want_ent;
+  ep.bf16_lane = a.bf16_lane;
   ep.V = (int)a.V;
   ep.N = (int)a.rows;
   const int64_t tm = ceil_div(a.V, GM), tn = ceil_div(a.rows, GN);
@@ -489,6 +490,7 @@ hipError_t bwd_slice_impl(const BwdSliceArgs& a, hipStream_t s) {
   {
     EpiDlogits<E> ep{a.temp, a.target, a.st, a.g, (E*)a.d, a.ld_d, (E*)a.dT, a.Tp,
                      (int)a.v0, (int)a.vs, (int)a.vsp, (int)a.T, (int)a.Tp};
+    ep.bf16_lane = a.bf16_lane;
     Main mn{W + a.v0 * a.H, a.H, (int)a.vs, (const E*)a.h, a.H, (int)a.T, (int)a.H};
     ProfScope ps(4, s);
     e = launch_gemm(mn, ep, ceil_div(a.vsp, GM), ceil_div(a.Tp, GN), s);
@@ -531,6 +533,7 @@ hipError_t bwd_slice_bf16(const BwdSliceArgs& a, hipStream_t s) {
   {
     EpiDlogits<bf16> ep{a.temp, a.target, a.st, a.g, nullptr, 0, (bf16*)a.dT, a.Tp,
                         (int)a.v0, (int)a.vs, (int)a.vsp, (int)a.T, (int)a.Tp};
+    ep.bf16_lane = a.bf16_lane;
     MainBf16 mn{W + a.v0 * a.H, a.H, (int)a.vs, (const bf16*)a.h, a.H, (int)a.T, (int)a.H};
     ProfScope ps(4, s);
     e = launch_gemm(mn, ep, ceil_div(a.vsp, GM), ceil_div(a.Tp, GN), s);

@@ -54,6 +54,7 @@ struct FwdArgs {
   int ntv;
   float* s_y;
   int want_ent;  // tile partials carry the entropy sums
+  int bf16_lane; // keys of the bf16 value lane
 };
 hipError_t launch_fwd_projection(const FwdArgs& a, hipStream_t s);
 
@@ -82,6 +83,7 @@ struct BwdSliceArgs {
   int64_t T, Tp, H, V, v0, vs, vsp, ld_d;
   int first, last;
   float dh_div;        // the hidden gradient's final value is divided by it (1 = none)
+  int bf16_lane;       // keys of the bf16 value lane
 };
 hipError_t launch_bwd_slice(const BwdSliceArgs& a, hipStream_t s);
 

@@ -6,6 +6,13 @@
 namespace stce {
 namespace {
 
+// The selected logprob in the lane's dtype: the fp32 value, or its bf16
+// rounding (nearest, ties to even) in the bf16 value lane.
+__device__ inline float lane_logprob(const SelParams& P, float lp) {
+  return P.round_lp_bf16 ? (float)(bf16)lp : lp;
+}
+
+
 #define F_INF __builtin_huge_valf()
 #define D_INF __builtin_huge_val()
 
@@ -185,7 +192,7 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
       rs.flags = ROW_VALID | ROW_IN_SUPPORT;
       rs.lse_s = rs.lse_full;
       if (fl & ROW_IGNORED) rs.flags = ROW_VALID | ROW_IGNORED;
-      P.logprob[row] = (fl & ROW_IGNORED) ? 0.0f : (float)fmin((double)sy - lse_full, 0.0);
+      P.logprob[row] = lane_logprob(P, (fl & ROW_IGNORED) ? 0.0f : (float)fmin((double)sy - lse_full, 0.0));
       P.state[row] = rs;
       if (P.ent_supp) P.ent_supp[row] = (float)h_full;
     }
@@ -602,7 +609,7 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
     const bool ign = (fl & ROW_IGNORED) != 0;
     const bool in = !ign && (ky > rs.key_thr || (ky == rs.key_thr && y <= (int64_t)rs.id_thr));
     rs.flags = ROW_VALID | ROW_FILTERED | (in ? ROW_IN_SUPPORT : 0u) | (ign ? ROW_IGNORED : 0u);
-    P.logprob[row] = ign ? 0.0f : (in ? (float)fmin((double)sy - lse_s, 0.0) : -F_INF);
+    P.logprob[row] = lane_logprob(P, ign ? 0.0f : (in ? (float)fmin((double)sy - lse_s, 0.0) : -F_INF));
     P.state[row] = rs;
   }
 }

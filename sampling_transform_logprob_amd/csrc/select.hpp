@@ -52,6 +52,7 @@ struct SelParams {
   float* lse_full;          // log-sum-exp of the keys over the row
   float* ent_full;          // entropy of softmax(s) over the row
   float* ent_supp;          // entropy of the filtered distribution on the support
+  int round_lp_bf16;        // the bf16 value lane: logprob rounded to bf16
 };
 
 void launch_select(const SelParams& p, int rows, hipStream_t stream);

@@ -65,7 +65,7 @@ def test_unsupported_dtype_is_one_actionable_error(lib):
 
 
 @pytest.mark.parametrize("kw,msg", [
-    (dict(T=0), "T=0"), (dict(H=12), "H=12"), (dict(V=0), "V=0"), (dict(flags=4), "flags"),
+    (dict(T=0), "T=0"), (dict(H=12), "H=12"), (dict(V=0), "V=0"), (dict(flags=8), "flags"),
     (dict(flags=1, ignore_index=5), "ignore_index=5"),
     (dict(chunk_rows=-1), "chunk_rows"),
 ])
@@ -93,6 +93,15 @@ def test_pre_gemm_temperature_workspaces_hold_the_scaled_hidden(lib):
         assert (f1 - f0, b1 - b0) == (hs, hs)
         assert binding.fused_workspace_bytes(pre)[0] - binding.fused_workspace_bytes(base)[0] == hs
         assert binding.schedule(pre) == binding.schedule(base)
+
+
+def test_bf16_lane_takes_bf16_operands_only(lib):
+    with pytest.raises(binding.StceError, match="UNSUPPORTED.*bf16 value lane"):
+        binding.workspace_bytes(_prob(dtype=binding.DT_F32, flags=binding.PROBLEM_BF16_LANE))
+    lane = _prob(flags=binding.PROBLEM_BF16_LANE | binding.PROBLEM_PRE_GEMM_TEMPERATURE, pre_gemm_temperature=0.5)
+    assert binding.workspace_bytes(lane)[0] > 0
+    with pytest.raises(ValueError, match="lane"):
+        binding.make_problem(None, None, None, lane="fp16")
 
 
 def test_pre_gemm_temperature_excludes_the_per_row_array(lib):
