@@ -252,6 +252,11 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="with --policy-loss: the fused step (dlogits formed in the forward's sweep from the "
                          "chunk's keys, 3 products instead of 4)")
+    ap.add_argument("--lane", choices=["fp32", "bf16"], default="fp32",
+                    help="bf16: the bf16 value lane (bf16 keys, bf16 logprob)")
+    ap.add_argument("--pre-gemm-temperature", type=float, default=None,
+                    help="one scalar temperature applied to the hidden states before the projection, in place "
+                         "of the workload's per-row temperature applied after it")
     args = ap.parse_args()
     if args.fused and args.policy_loss == "none":
         print("--fused needs --policy-loss cispo|clip", file=sys.stderr)
@@ -289,8 +294,10 @@ def main():
         target = torch.from_numpy(w["target_uniform"]).to(dev)
     torch.cuda.synchronize()
 
-    prob, keep = binding.make_problem(h, W, target, meta["temperature"], meta["top_k"], meta["top_p"],
-                                      meta["min_p"], args.chunk_rows, args.vocab_slice)
+    ts = args.pre_gemm_temperature
+    prob, keep = binding.make_problem(h, W, target, None if ts is not None else meta["temperature"], meta["top_k"],
+                                      meta["top_p"], meta["min_p"], args.chunk_rows, args.vocab_slice,
+                                      pre_gemm_temperature=ts, lane=args.lane)
     fwd_b, bwd_b = binding.workspace_bytes(prob)
     ws_f = torch.empty(fwd_b, dtype=torch.uint8, device=dev)
     ws_b = torch.empty(bwd_b, dtype=torch.uint8, device=dev)
@@ -424,7 +431,10 @@ def main():
                                   f" of the {args.policy_loss} policy-gradient token loss")
                                + ("; fused step: dlogits formed in the forward's sweep, no recompute product"
                                   if args.fused else "")
-                               + ("; forward side outputs (full LSE, entropies)" if args.side_outputs else ""),
+                               + ("; forward side outputs (full LSE, entropies)" if args.side_outputs else "")
+                               + ("; bf16 value lane" if args.lane == "bf16" else "")
+                               + (f"; scalar pre-GEMM temperature {ts} in place of the per-row one"
+                                  if ts is not None else ""),
                    "T": T, "H": H, "V": V, "chunk_rows": C, "vocab_slice": Vs},
         "mfma_peak_frac": flop_step / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "tflops_8thv": 8.0 * T * H * V / (ms_step * 1e-3) / 1e12,
