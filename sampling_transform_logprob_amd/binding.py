@@ -443,20 +443,29 @@ def decode_state(state: torch.Tensor) -> dict:
 
 
 class ScoreFunction(torch.autograd.Function):
-    """Autograd wrapper: logprob = ScoreFunction.apply(hidden, weight, target, T, top_k, top_p, min_p)."""
+    """Autograd wrapper of the scoring core:
+
+    ``logprob = ScoreFunction.apply(hidden, weight, target, temperature, top_k, top_p, min_p,
+    ignore_index, pre_gemm_temperature, lane)`` (arguments after ``target`` optional, as in
+    ``forward``).  The backward recomputes through ``backward`` with the
+    incoming gradient as ``grad_logprob``; the weight gradient is returned in
+    the weight's dtype."""
 
     @staticmethod
-    def forward(ctx, hidden, weight, target, temperature=None, top_k=None, top_p=None, min_p=None):
-        logprob, state = forward(hidden, weight, target, temperature, top_k, top_p, min_p)
+    def forward(ctx, hidden, weight, target, temperature=None, top_k=None, top_p=None, min_p=None,
+                ignore_index=None, pre_gemm_temperature=None, lane="fp32"):
+        opts = dict(ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane)
+        logprob, state = forward(hidden, weight, target, temperature, top_k, top_p, min_p, **opts)
         ctx.save_for_backward(hidden, weight, target, state)
         ctx.meta = (temperature, top_k, top_p, min_p)
+        ctx.opts = opts
         return logprob
 
     @staticmethod
     def backward(ctx, g):
         hidden, weight, target, state = ctx.saved_tensors
         gh, gw = backward(hidden, weight, target, state, g.float().contiguous(), *ctx.meta,
-                          need_hidden=ctx.needs_input_grad[0], need_weight=ctx.needs_input_grad[1])
+                          need_hidden=ctx.needs_input_grad[0], need_weight=ctx.needs_input_grad[1], **ctx.opts)
         if gw is not None:
             gw = gw.to(weight.dtype)
-        return gh, gw, None, None, None, None, None
+        return (gh, gw) + (None,) * 8
