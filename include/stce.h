@@ -166,7 +166,9 @@ stce_status stce_workspace_bytes(const stce_problem *prob, size_t *fwd, size_t *
 stce_status stce_schedule(const stce_problem *prob, int64_t *chunk_rows, int64_t *vocab_slice);
 
 /* Forward: logprob[t] = min(s[t, y_t] - logsumexp_{j in S_t} s[t, j], 0) if
- * y_t is in the support S_t, else -inf, with s = fl32(h W^T) / T per row.
+ * y_t is in the support S_t, else -inf, with s = fl32(h W^T) / T per row
+ * (or the keys of the convention prob->flags selects: scalar pre-GEMM
+ * temperature, bf16 value lane, which also rounds logprob to bf16).
  * Writes logprob [T] fp32 and state [T * 32 bytes] (support boundary,
  * filtered log-sum-exp, flags) for stce_backward.  dev_status: one int64
  * (may be NULL).  ws: at least the forward workspace size, 256-byte
@@ -184,8 +186,9 @@ stce_status stce_forward(const stce_problem *prob, float *logprob, void *state,
  *                        distribution (softmax of s on the support),
  * in nats, on the fp32 keys s; rows with invalid metadata get NaN.  The
  * full-row entropy comes from per-tile sums of e^(s - max) (s - max) that
- * the projection epilogue forms only when an entropy is requested (fp32
- * sums, fp64 combination); the support entropy is summed over the sorted
+ * the projection epilogue always forms (so that no other bit depends on the
+ * request) and stores only when an entropy is requested (fp32 sums, fp64
+ * combination); the support entropy is summed over the sorted
  * selection window when the support starts at the top of the order, else
  * in one more pass over the row.  Same workspace as stce_forward. */
 typedef struct stce_side_outputs {
@@ -200,7 +203,9 @@ stce_status stce_forward_with_side(const stce_problem *prob, float *logprob, voi
 /* Backward of sum_t grad_logprob[t] * logprob[t].  Recomputes the logits of
  * every vocabulary slice bit-for-bit as the forward did, reads the support
  * from `state`, forms dz = g (1[j == y] - q) / T (zero on rows whose target
- * is out of support or whose metadata is invalid) and writes
+ * is out of support or whose metadata is invalid; with the scalar pre-GEMM
+ * temperature dz = g (1[j == y] - q) and the hidden gradient is divided by
+ * Ts) and writes
  *   grad_hidden [T, H] in the hidden dtype (overwritten; NULL = skip) and
  *   grad_weight [V, H] fp32 (overwritten, or added to when
  *                accumulate_grad_weight != 0; NULL = skip).
@@ -211,8 +216,9 @@ stce_status stce_backward(const stce_problem *prob, const float *grad_logprob, c
                           int64_t *dev_status, void *ws, size_t ws_bytes, void *stream);
 
 /* Parity entry: the fp32 keys s = fl32(h W^T) / T of rows [row0, row0 +
- * nrows), written to s_out [nrows, V], produced by the same projection
- * kernel and temperature step as stce_forward (same bits).  Needs the
+ * nrows) (or those of the convention prob->flags selects), written to
+ * s_out [nrows, V], produced by the same projection kernel and temperature
+ * step as stce_forward (same bits).  Needs the
  * forward workspace of the problem. */
 stce_status stce_scaled_logits(const stce_problem *prob, int64_t row0, int64_t nrows, float *s_out,
                                void *ws, size_t ws_bytes, void *stream);
@@ -351,7 +357,8 @@ stce_status stce_policy_loss(const stce_pg_params *pg, int64_t T, const float *l
  * in stce_forward), the group's vocab-major dz (with bf16 operands the only
  * copy: the hidden gradient is formed transposed and reads it as it is; fp32
  * also keeps a chunk's token-major copy), the transposed weight (and for
- * fp32 the transposed hidden), and the split partials.  A workspace between *min_bytes (one
+ * fp32 the transposed hidden), the split partials, and with the scalar
+ * pre-GEMM temperature h / Ts.  A workspace between *min_bytes (one
  * chunk per group) and *bytes keeps as many chunks per group as it holds;
  * the grouping changes only the order of dW's fp32 sums.  Host errors as stce_forward, stce_backward and
  * stce_policy_loss, and V must be below 2^29 (the chunk's key rows are read

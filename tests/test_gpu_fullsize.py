@@ -34,7 +34,7 @@ def _gpu():
     binding.load()
 
 
-@pytest.mark.parametrize("name", ["headline", "top_p", "ties"])
+@pytest.mark.parametrize("name", ["identity", "headline", "top_p", "ties"])
 def test_full_size_sampled_rows(name):
     w = workloads.make(name)
     T, H, V = w["T"], w["H"], w["V"]
