@@ -6,7 +6,6 @@
 #include <string.h>
 
 #include <unordered_map>
-#include <vector>
 
 #include "../../include/stce.h"
 #include "kernels.hpp"
@@ -255,29 +254,31 @@ T* at(void* ws, size_t off) {
   return (T*)((char*)ws + off);
 }
 
-// Per-thread, per-device side stream (default priority) and a pool of
+// Per-thread, per-device side stream (default priority) and four
 // timing-free events, created on first use and kept for the thread's life.
 // The forward runs each chunk's selection on the side stream, ordered
 // against the projections on the caller's stream by event waits only, so
 // the pattern is a plain fork/join that stream capture records as graph
-// dependencies.
+// dependencies.  Chunk c uses the fork and done events of its buffer c % 2;
+// a wait takes the event's record current at the time of the call, and every
+// wait on chunk c's records is enqueued before chunk c + 2 records them
+// again, so the four events serve any number of chunks.
 struct SideCtx {
   hipStream_t stream = nullptr;
-  std::vector<hipEvent_t> ev;
+  hipEvent_t ev[4] = {};
+  hipEvent_t fork(int64_t c) const { return ev[2 * (c & 1)]; }
+  hipEvent_t done(int64_t c) const { return ev[2 * (c & 1) + 1]; }
 };
 thread_local std::unordered_map<int, SideCtx> g_side;
 
-hipError_t side_ctx(SideCtx** out, size_t nevents) {
+hipError_t side_ctx(SideCtx** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   SideCtx& c = g_side[dev];
   if (!c.stream && (e = hipStreamCreateWithFlags(&c.stream, hipStreamNonBlocking)) != hipSuccess) return e;
-  while (c.ev.size() < nevents) {
-    hipEvent_t ev;
-    if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return e;
-    c.ev.push_back(ev);
-  }
+  for (hipEvent_t& ev : c.ev)
+    if (!ev && (e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return e;
   *out = &c;
   return hipSuccess;
 }
@@ -363,12 +364,12 @@ stce_status stce_forward_with_side(const stce_problem* p, float* logprob, void* 
   if ((e = hidden_for_products(p, ws, L.f_hs, 0, p->T, &hid, nullptr, st))) return hip_fail(e, "prescale hidden");
   const int64_t nch = ceil_div(p->T, L.C);
   SideCtx* side = nullptr;
-  if (L.nbuf == 2 && (e = side_ctx(&side, 2 * (size_t)nch))) return hip_fail(e, "side stream");
+  if (L.nbuf == 2 && (e = side_ctx(&side))) return hip_fail(e, "side stream");
   for (int64_t c = 0; c < nch; ++c) {
     const int64_t c0 = c * L.C;
     const int64_t nc = p->T - c0 < L.C ? p->T - c0 : L.C;
     const int64_t b = c % L.nbuf;
-    if (side && c >= 2 && (e = hipStreamWaitEvent(st, side->ev[2 * (c - 2) + 1], 0)))
+    if (side && c >= 2 && (e = hipStreamWaitEvent(st, side->done(c - 2), 0)))
       return hip_fail(e, "wait for selection");  // chunk c - 2 released this buffer
     FwdArgs a{};
     a.dtype = p->dtype;
@@ -392,7 +393,7 @@ stce_status stce_forward_with_side(const stce_problem* p, float* logprob, void* 
     hipStream_t ss = st;
     if (side) {
       ss = side->stream;
-      if ((e = hipEventRecord(side->ev[2 * c], st)) || (e = hipStreamWaitEvent(ss, side->ev[2 * c], 0)))
+      if ((e = hipEventRecord(side->fork(c), st)) || (e = hipStreamWaitEvent(ss, side->fork(c), 0)))
         return hip_fail(e, "fork to the side stream");
     }
     SelParams sp{};
@@ -415,11 +416,11 @@ stce_status stce_forward_with_side(const stce_problem* p, float* logprob, void* 
     sp.round_lp_bf16 = bf16_lane(p);
     launch_select(sp, (int)nc, ss);
     if ((e = hipGetLastError())) return hip_fail(e, "select");
-    if (side && (e = hipEventRecord(side->ev[2 * c + 1], ss))) return hip_fail(e, "selection event");
+    if (side && (e = hipEventRecord(side->done(c), ss))) return hip_fail(e, "selection event");
   }
   // join: the caller's stream waits for the last selection (the side stream
   // runs them in order)
-  if (side && (e = hipStreamWaitEvent(st, side->ev[2 * (nch - 1) + 1], 0))) return hip_fail(e, "join");
+  if (side && (e = hipStreamWaitEvent(st, side->done(nch - 1), 0))) return hip_fail(e, "join");
   return STCE_OK;
 }
 
@@ -643,7 +644,7 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
   }
   const int64_t nch = ceil_div(p->T, L.C);
   SideCtx* side = nullptr;
-  if (L.nbuf == 2 && (e = side_ctx(&side, 2 * (size_t)nch))) return hip_fail(e, "side stream");
+  if (L.nbuf == 2 && (e = side_ctx(&side))) return hip_fail(e, "side stream");
   auto rows_of = [&](int64_t c) { return p->T - c * L.C < L.C ? p->T - c * L.C : L.C; };
   // the chunk's keys (every row: the gradient needs them all), then its
   // selection and selected logprob, on the side stream when there is one
@@ -672,7 +673,7 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
     hipStream_t ss = st;
     if (side) {
       ss = side->stream;
-      if ((e2 = hipEventRecord(side->ev[2 * c], st)) || (e2 = hipStreamWaitEvent(ss, side->ev[2 * c], 0)))
+      if ((e2 = hipEventRecord(side->fork(c), st)) || (e2 = hipStreamWaitEvent(ss, side->fork(c), 0)))
         return hip_fail(e2, "fork to the side stream");
     }
     SelParams sp{};
@@ -695,7 +696,7 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
     sp.round_lp_bf16 = bf16_lane(p);
     launch_select(sp, (int)nc, ss);
     if ((e2 = hipGetLastError())) return hip_fail(e2, "select");
-    if (side && (e2 = hipEventRecord(side->ev[2 * c + 1], ss))) return hip_fail(e2, "selection event");
+    if (side && (e2 = hipEventRecord(side->done(c), ss))) return hip_fail(e2, "selection event");
     return STCE_OK;
   };
   if ((s = project_select(0))) return s;
@@ -705,7 +706,7 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
     // the other buffer, whose readers (chunk c - 1's selection and dz) are
     // done: the first is waited for below, the second is earlier on `st`
     if (c + 1 < nch && (s = project_select(c + 1))) return s;
-    if (side && (e = hipStreamWaitEvent(st, side->ev[2 * c + 1], 0))) return hip_fail(e, "join");
+    if (side && (e = hipStreamWaitEvent(st, side->done(c), 0))) return hip_fail(e, "join");
     // the token loss of the chunk's rows
     RowState* stc = (RowState*)state + c0;
     float* g = at<float>(ws, L.g);

@@ -200,3 +200,23 @@ def test_full_size_headline_fused_equals_unfused():
     say(f"  bitwise logprob/state/loss/ratio; dH rel {rh:.2e}  dW rel {rw:.2e}  "
         f"-inf rows {int(torch.isinf(f['logprob']).sum())}")
     assert rh < 1e-3 and rw < 1e-4
+
+
+def test_many_chunks_equal_the_unfused_sequence():
+    """18 chunks of 64 rows: the selection of every chunk overlaps the next
+    projection on the side stream, whose events are reused chunk after
+    chunk; logprob, state and loss stay bitwise those of the unfused path."""
+    w, y, G = _setup("top_p", 1100, 3000)
+    lp0, _ = binding.forward(G["h"], G["W"], G["target"], **meta_of(G), check=False)
+    A, old = _pg_inputs(lp0.cpu().numpy(), 19)
+    A, old = torch.from_numpy(A).to(dev()), torch.from_numpy(old).to(dev())
+    say("fused vs unfused: top_p T=1100 V=3000, 18 chunks")
+    u = _unfused(G, A, old, "clip", 1.0 / 1100)
+    f = binding.fused_policy_step(G["h"], G["W"], G["target"], A, old, **meta_of(G), objective="clip",
+                                  eps_low=EL, eps_high=EH, scale=1.0 / 1100, chunk_rows=64, check=False)
+    for k in ("logprob", "state", "loss", "ratio"):
+        assert _same(f[k], u[k]), k
+    rh = rel_fro(f["grad_hidden"].float().cpu().numpy(), u["grad_hidden"].float().cpu().numpy())
+    rw = rel_fro(f["grad_weight"].cpu().numpy(), u["grad_weight"].cpu().numpy())
+    say(f"  bitwise logprob/state/loss/ratio; dH rel {rh:.2e}  dW rel {rw:.2e}")
+    assert rh < 1e-3 and rw < 1e-5
