@@ -229,6 +229,43 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
+def library_reference(reps=5):
+    """The four products of the step at the headline shape, each as one
+    torch.mm call (the vendor library, hipBLASLt on ROCm) on synthetic bf16
+    operands of the same layouts, with bf16 and with fp32 output: a reference
+    rate for the matrix products alone, without the path's epilogues
+    (temperature, tile partials, keys, dz).  Not part of the scoring path."""
+    import torch
+    T, H, V, C = 16384, 5120, 151936, 4096
+    g = torch.Generator(device="cuda").manual_seed(0)
+    W = (torch.randn(V, H, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    h = torch.randn(T, H, device="cuda", generator=g).to(torch.bfloat16)
+    dT = (torch.randn(V, T, device="cuda", generator=g) * 1e-6).to(torch.bfloat16)
+    products = [
+        ("projection z^T = W h_chunk^T (K = H)", lambda dt: torch.mm(W, h[:C].t(), out_dtype=dt), V * C * H),
+        ("recompute z^T = W h^T (K = H)", lambda dt: torch.mm(W, h.t(), out_dtype=dt), V * T * H),
+        ("grad_weight dW = dz^T h (K = T)", lambda dt: torch.mm(dT, h, out_dtype=dt), V * H * T),
+        ("grad_hidden dH^T = W^T dz^T (K = V)", lambda dt: torch.mm(W.t(), dT, out_dtype=dt), H * T * V),
+    ]
+    out = []
+    for name, f, mnk in products:
+        for dt in (torch.bfloat16, torch.float32):
+            f(dt)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                r = f(dt)
+            e1.record()
+            torch.cuda.synchronize()
+            del r
+            ms = e0.elapsed_time(e1) / reps
+            tf = 2.0 * mnk / (ms * 1e-3) / 1e12
+            out.append(dict(product=name, out_dtype=str(dt).replace("torch.", ""), ms=ms, tflops=tf))
+            log(f"[library] {name:40s} out {out[-1]['out_dtype']:8s} {ms:8.3f} ms {tf:7.1f} TFLOP/s")
+    print(json.dumps({"library_reference": out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +281,8 @@ def main():
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write the HBM traffic summary of --traffic-kernel from rocprofv3 --pmc outputs and exit")
     ap.add_argument("--traffic-kernel", default="dlogits")
+    ap.add_argument("--library-reference", action="store_true",
+                    help="time the step's four products as plain torch.mm calls (vendor library) and exit")
     ap.add_argument("--side-outputs", action="store_true",
                     help="forward with the sweep's side outputs (full LSE, full and support entropy)")
     ap.add_argument("--policy-loss", choices=["none", "cispo", "clip"], default="none",
@@ -271,6 +310,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.library_reference:
+        library_reference()
         return
 
     import torch
