@@ -214,3 +214,40 @@ def test_fused_step_rejects_bad_arguments_before_launch(lib):
                                       None, 0, None) == 1
     n = ctypes.c_size_t()
     assert lib.stce_fused_workspace_bytes(ctypes.byref(_prob(T=0)), ctypes.byref(n), None) == 1
+
+
+def test_plain_c_program_links_and_sizes_a_problem(lib, tmp_path):
+    """The header is C99 and the library links into a plain C program: the
+    program sizes the headline problem's workspaces and reads a host error
+    (no device call)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "abi.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <string.h>
+#include "stce.h"
+int main(void) {
+  stce_problem p;
+  memset(&p, 0, sizeof p);
+  p.T = 16384; p.H = 5120; p.V = 151936; p.dtype = STCE_DT_BF16;
+  size_t f = 0, b = 0, fu = 0, fm = 0;
+  if (stce_workspace_bytes(&p, &f, &b) != STCE_OK) return 1;
+  if (stce_fused_workspace_bytes(&p, &fu, &fm) != STCE_OK) return 2;
+  p.H = 12;
+  stce_status s = stce_workspace_bytes(&p, &f, &b);
+  printf("%zu %zu %zu %zu %d %s\n", f, b, fu, fm, (int)s, stce_last_error());
+  return s == STCE_E_ARG ? 0 : 3;
+}
+''')
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(binding.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                    binding.LIB_PATH, "-Wl,-rpath," + libdir], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    f, b, fu, fm = (int(x) for x in out[:4])
+    pf, pb = binding.workspace_bytes(_prob(T=16384, H=5120, V=151936))
+    assert (f, b) == (pf, pb) and fu > fm > 0
+    assert out[4] == "1" and "H=12" in " ".join(out[5:])
