@@ -21,8 +21,15 @@ __device__ inline void lse_ent_merge(float& mx, float& sm, float& en, float omx,
     if (mx != -STCE_INF) e += (en + (mx - M) * sm) * __expf(mx - M);
     if (omx != -STCE_INF) e += (oen + (omx - M) * osm) * __expf(omx - M);
     en = e;
-    sm = sm * __expf(mx - M) + osm * __expf(omx - M);
+    sm = __builtin_fmaf(sm, __expf(mx - M), osm * __expf(omx - M));
   }
+  mx = M;
+}
+
+// The same merge of (max, mass) alone; its mass arithmetic is lse_ent_merge's.
+__device__ inline void lse_merge(float& mx, float& sm, float omx, float osm) {
+  const float M = fmaxf(mx, omx);
+  sm = M == -STCE_INF ? 0.f : __builtin_fmaf(sm, __expf(mx - M), osm * __expf(omx - M));
   mx = M;
 }
 
@@ -88,6 +95,7 @@ constexpr float LOG2E = 1.4426950408889634f;
 // optionally stores the fp32 keys (rows flagged ROW_FILTERED, or all rows),
 // writes the tile's (max, sum exp(s - max), min) and captures the target key.
 // ---------------------------------------------------------------------------
+template <bool Ent>
 struct EpiLogits {
   float* tile;             // [N][ld] keys, row = token
   int64_t ld;
@@ -101,7 +109,6 @@ struct EpiLogits {
   float* s_y;              // [N] or null
   int V;                   // valid vocabulary rows
   int N;                   // valid tokens
-  int want_ent;            // store the per-tile sum of exp(s - max) (s - max)
   int bf16_lane;           // keys of the bf16 value lane
   static constexpr int LDS_BYTES = 2 * GN * 4 * 4;  // cross-wave merge
 
@@ -169,9 +176,10 @@ struct EpiLogits {
           }
         }
       }
-      // the tile's mass and its entropy sum, formed the same way whether or
-      // not the entropy is stored, so the mass (and every decision and
-      // logprob that uses it) does not depend on the request
+      // the tile's mass and, with Ent, its entropy sum, in a separate
+      // accumulator: the mass arithmetic is the same in both instances, so
+      // the mass (and every decision and logprob that uses it) does not
+      // depend on whether the entropy is requested
       float sm = 0.f, en = 0.f;
       if (mx != -STCE_INF) {
         const float nmx = -mx * LOG2E;
@@ -182,14 +190,18 @@ struct EpiLogits {
             if (full || m0 + acc_row(wm, i, r, quad) < V) {
               const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i][j][r], LOG2E, nmx));
               sm += e;
-              en = __builtin_fmaf(e, acc[i][j][r] - mx, en);
+              if (Ent) en = __builtin_fmaf(e, acc[i][j][r] - mx, en);
             }
       }
       // merge the four lanes that hold this column (quads 0..3)
 #pragma unroll
       for (int o = 16; o <= 32; o <<= 1) {
-        const float omx = __shfl_xor(mx, o), osm = __shfl_xor(sm, o), omn = __shfl_xor(mn, o), oen = __shfl_xor(en, o);
-        lse_ent_merge(mx, sm, en, omx, osm, oen);
+        const float omx = __shfl_xor(mx, o), osm = __shfl_xor(sm, o), omn = __shfl_xor(mn, o);
+        if (Ent) {
+          lse_ent_merge(mx, sm, en, omx, osm, __shfl_xor(en, o));
+        } else {
+          lse_merge(mx, sm, omx, osm);
+        }
         mn = fminf(mn, omn);
       }
       pmx[j] = mx;
@@ -207,7 +219,7 @@ struct EpiLogits {
         red[(wm * 256 + tok) * 4 + 0] = pmx[j];
         red[(wm * 256 + tok) * 4 + 1] = psm[j];
         red[(wm * 256 + tok) * 4 + 2] = pmn[j];
-        red[(wm * 256 + tok) * 4 + 3] = pen[j];
+        if (Ent) red[(wm * 256 + tok) * 4 + 3] = pen[j];
       }
     }
     __syncthreads();
@@ -217,13 +229,18 @@ struct EpiLogits {
         const int tok = acc_col(wn, j, col);
         const int n = n0 + tok;
         if (n < N) {
-          float mx = red[tok * 4 + 0], sm = red[tok * 4 + 1], en = red[tok * 4 + 3];
-          lse_ent_merge(mx, sm, en, red[(256 + tok) * 4 + 0], red[(256 + tok) * 4 + 1], red[(256 + tok) * 4 + 3]);
+          float mx = red[tok * 4 + 0], sm = red[tok * 4 + 1], en = 0.f;
+          if (Ent) {
+            en = red[tok * 4 + 3];
+            lse_ent_merge(mx, sm, en, red[(256 + tok) * 4 + 0], red[(256 + tok) * 4 + 1], red[(256 + tok) * 4 + 3]);
+          } else {
+            lse_merge(mx, sm, red[(256 + tok) * 4 + 0], red[(256 + tok) * 4 + 1]);
+          }
           TilePart tp;
           tp.mx = mx;
           tp.sum = sm;
           tp.mn = fminf(red[tok * 4 + 2], red[(256 + tok) * 4 + 2]);
-          tp.ent = want_ent ? en : 0.f;
+          tp.ent = en;
           part[(int64_t)n * ntv + m0 / VTILE] = tp;
         }
       }

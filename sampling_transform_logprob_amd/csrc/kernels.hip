@@ -455,8 +455,10 @@ hipError_t launch_tile_partials(const float* sk, int64_t ld, int64_t R, int64_t 
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_projection(const FwdArgs& a, hipStream_t s) {
-  EpiLogits ep{};
+namespace {
+template <bool Ent>
+hipError_t fwd_projection_impl(const FwdArgs& a, hipStream_t s) {
+  EpiLogits<Ent> ep{};
   ep.tile = a.tile;
   ep.ld = a.ld;
   ep.temp = a.temp;
@@ -467,7 +469,6 @@ hipError_t launch_fwd_projection(const FwdArgs& a, hipStream_t s) {
   ep.part = a.part;
   ep.ntv = a.ntv;
   ep.s_y = a.s_y;
-  ep.want_ent = a.want_ent;
   ep.bf16_lane = a.bf16_lane;
   ep.V = (int)a.V;
   ep.N = (int)a.rows;
@@ -479,6 +480,12 @@ hipError_t launch_fwd_projection(const FwdArgs& a, hipStream_t s) {
   }
   MainF32 mn{(const float*)a.W, a.H, (int)a.V, (const float*)a.h, a.H, (int)a.rows, (int)a.H};
   return launch_gemm(mn, ep, tm, tn, s);
+}
+}  // namespace
+
+// the entropy sums are formed only when requested (a separate instance)
+hipError_t launch_fwd_projection(const FwdArgs& a, hipStream_t s) {
+  return a.want_ent ? fwd_projection_impl<true>(a, s) : fwd_projection_impl<false>(a, s);
 }
 
 namespace {
