@@ -118,12 +118,24 @@ struct EpiLogits {
     const int mb = m0 + wm * 128;
     const bool full = m0 + GM <= V;
     float pmx[ACC_J], psm[ACC_J], pmn[ACC_J], pen[ACC_J];
+    // Every per-token load comes first: loads and stores share one in-order
+    // counter, so a load issued after a column's key stores would make the
+    // wave wait for all of them to complete before the next column.
+    float tv[ACC_J];
+    bool stv[ACC_J];
+    int64_t tgv[ACC_J];
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) {
       const int n = n0 + acc_col(wn, j, col);
       const bool nv = n < N;
-      const float t = (nv && temp) ? temp[n] : 1.0f;
-      keys_column(acc, j, t, bf16_lane);
+      tv[j] = (nv && temp) ? temp[n] : 1.0f;
+      stv[j] = nv && (store_all || (flags[n] & ROW_FILTERED));
+      tgv[j] = (nv && target && s_y) ? target[n] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < ACC_J; ++j) {
+      const int n = n0 + acc_col(wn, j, col);
+      keys_column(acc, j, tv[j], bf16_lane);
       float mx = -STCE_INF, mn = STCE_INF;
       if (full) {
 #pragma unroll
@@ -143,8 +155,7 @@ struct EpiLogits {
               mn = fminf(mn, acc[i][j][r]);
             }
       }
-      const bool st = nv && (store_all || (flags[n] & ROW_FILTERED));
-      if (st) {
+      if (stv[j]) {
         float* rowp = tile + (int64_t)n * ld;
         const int mbu = __builtin_amdgcn_readfirstlane(mb);
 #pragma unroll
@@ -160,8 +171,8 @@ struct EpiLogits {
           }
         }
       }
-      if (nv && target && s_y) {
-        const int64_t off = target[n] - mb;
+      if (tgv[j] >= 0) {
+        const int64_t off = tgv[j] - mb;
         if (off >= 0 && off < 128) {
           const int oi = (int)off >> 4, ow = (int)off & 15;
           if ((ow >> 2) == quad) {
