@@ -54,8 +54,13 @@
  *     outside [0, V)) are found on the device.  Such a row gets a NaN
  *     logprob and a zero gradient, and *dev_status (if not NULL) receives
  *     the first bad row: see STCE_STATUS_NONE.
- *   - Thread-safe: the only global mutable state is the thread-local error
- *     string.  Calls that share a workspace must be ordered by the caller.
+ *   - Thread-safe.  Mutable state kept between calls, all of it per thread:
+ *     the error string, the attached profile (stce_profile_attach), and, per
+ *     device, one side stream of default priority and four timing-free events
+ *     that the chunked forward and the fused step fork to and join from.  The
+ *     stream and events are created on a thread's first multi-chunk call and
+ *     kept for the life of the process (they are released when the process
+ *     ends).  Calls that share a workspace must be ordered by the caller.
  */
 #ifndef STCE_H
 #define STCE_H
@@ -114,7 +119,9 @@ typedef enum {
 #define STCE_STATE_BYTES_PER_ROW 32
 
 typedef struct stce_problem {
-  int64_t T;             /* rows (scored tokens), >= 1 */
+  int64_t T;             /* rows (scored tokens), 1 <= T <= 2^22 - 64 (the products
+                            address a [vocabulary, T] dz through 32-bit buffer
+                            offsets) */
   int64_t H;             /* hidden size, >= 8, multiple of 8 */
   int64_t V;             /* vocabulary size, 1 <= V < 2^31 - 256 */
   int32_t dtype;         /* stce_dtype of hidden and weight */
@@ -165,7 +172,10 @@ stce_status stce_workspace_bytes(const stce_problem *prob, size_t *fwd, size_t *
  * own values when non-zero, else the defaults).  Either pointer may be NULL. */
 stce_status stce_schedule(const stce_problem *prob, int64_t *chunk_rows, int64_t *vocab_slice);
 
-/* Forward: logprob[t] = min(s[t, y_t] - logsumexp_{j in S_t} s[t, j], 0) if
+/* Forward (xorl pull request 74, "What this PR does" items 1, 2 and 4 and the
+ * self-review pass: temperature first, the joint top-k / top-p / min-p
+ * support, the selected logprob clamped to <= 0, -inf out of support):
+ * logprob[t] = min(s[t, y_t] - logsumexp_{j in S_t} s[t, j], 0) if
  * y_t is in the support S_t, else -inf, with s = fl32(h W^T) / T per row
  * (or the keys of the convention prob->flags selects: scalar pre-GEMM
  * temperature, bf16 value lane, which also rounds logprob to bf16).
@@ -185,10 +195,11 @@ stce_status stce_forward(const stce_problem *prob, float *logprob, void *state,
  *   entropy_support[t] = -sum_{j in S_t} q_j log q_j, q the filtered
  *                        distribution (softmax of s on the support),
  * in nats, on the fp32 keys s; rows with invalid metadata get NaN.  The
- * full-row entropy comes from per-tile sums of e^(s - max) (s - max) that
- * the projection epilogue always forms (so that no other bit depends on the
- * request) and stores only when an entropy is requested (fp32 sums, fp64
- * combination); the support entropy is summed over the sorted
+ * full-row entropy comes from per-tile sums of e^(s - max) (s - max) that the
+ * projection epilogue forms only when an entropy is requested (a separate
+ * instance of the epilogue whose mass arithmetic is the plain forward's, so
+ * logprob and state are bitwise the same with and without the request; fp32
+ * sums, fp64 combination); the support entropy is summed over the sorted
  * selection window when the support starts at the top of the order, else
  * in one more pass over the row.  Same workspace as stce_forward. */
 typedef struct stce_side_outputs {
@@ -200,7 +211,11 @@ stce_status stce_forward_with_side(const stce_problem *prob, float *logprob, voi
                                    const stce_side_outputs *side, int64_t *dev_status, void *ws,
                                    size_t ws_bytes, void *stream);
 
-/* Backward of sum_t grad_logprob[t] * logprob[t].  Recomputes the logits of
+/* Backward of sum_t grad_logprob[t] * logprob[t]: the recompute closed-form
+ * VJP of xorl pull request 74, "What this PR does" item 2 (nothing of size
+ * [T, V] kept from the forward; exactly zero gradient for out-of-support
+ * rows, item 4; weight gradients written once per vocabulary slice,
+ * self-review pass).  Recomputes the logits of
  * every vocabulary slice bit-for-bit as the forward did, reads the support
  * from `state`, forms dz = g (1[j == y] - q) / T (zero on rows whose target
  * is out of support or whose metadata is invalid; with the scalar pre-GEMM
@@ -222,6 +237,17 @@ stce_status stce_backward(const stce_problem *prob, const float *grad_logprob, c
  * forward workspace of the problem. */
 stce_status stce_scaled_logits(const stce_problem *prob, int64_t row0, int64_t nrows, float *s_out,
                                void *ws, size_t ws_bytes, void *stream);
+
+/* Parity entry: the recompute product of stce_backward, launched as
+ * stce_backward launches it (same kernel, same vocabulary slices and
+ * arguments), which in this call also writes the fp32 keys it recomputes,
+ * keys_out [T, V] row-major; no gradient product runs.  The keys must equal
+ * the forward's bit for bit (the recompute closed-form VJP of xorl pull
+ * request 74, "What this PR does" item 2, takes its support from the state
+ * and re-derives membership from these keys).  Arguments and workspace as
+ * stce_backward; keys_out is required. */
+stce_status stce_recompute_keys(const stce_problem *prob, const float *grad_logprob, const void *state,
+                                float *keys_out, void *ws, size_t ws_bytes, void *stream);
 
 /* Parity entry: the support program and selected logprob applied to given
  * fp32 keys s [R, V] (row-major, 16-byte aligned, V a multiple of 4), with

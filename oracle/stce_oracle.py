@@ -216,7 +216,9 @@ def support(keys: np.ndarray, top_k, top_p, min_p) -> dict:
     """Row-wise support of a [R, V] fp32 key matrix.
 
     ``top_k``/``top_p``/``min_p`` are per-row arrays (or None for "off").
-    Returns arrays ``n``, ``key_thr``, ``id_thr`` (uint32/int64), ``near``.
+    Returns arrays ``n``, ``key_thr``, ``id_thr`` (uint32/int64), ``near``,
+    and the per-filter prefix lengths ``n_k``, ``n_p``, ``n_m`` (V when the
+    filter is off), so a caller can tell which filter binds.
     """
     keys = np.asarray(keys, dtype=np.float32)
     R = keys.shape[0]
@@ -225,10 +227,23 @@ def support(keys: np.ndarray, top_k, top_p, min_p) -> dict:
     kt = np.zeros(R, np.uint32)
     it = np.zeros(R, np.int64)
     near = np.zeros(R, bool)
+    nk, np_, nm = (np.zeros(R, np.int64) for _ in range(3))
     for r in range(R):
         d = support_row(keys[r], tk[r], tp[r], mp[r])
         n[r], kt[r], it[r], near[r] = d["n"], d["key_thr"], d["id_thr"], d["near"]
-    return dict(n=n, key_thr=kt, id_thr=it, near=near)
+        nk[r], np_[r], nm[r] = d["n_k"], d["n_p"], d["n_m"]
+    return dict(n=n, key_thr=kt, id_thr=it, near=near, n_k=nk, n_p=np_, n_m=nm)
+
+
+def binding_filters(sup: dict, V: int) -> dict:
+    """Rows on which each filter binds (its prefix is the support; a row may
+    count for several filters when their prefixes coincide), and unfiltered
+    rows, from the output of ``support``."""
+    n = sup["n"]
+    out = {"unfiltered": int((n == V).sum())}
+    for f, key in (("top_k", "n_k"), ("top_p", "n_p"), ("min_p", "n_m")):
+        out[f] = int(((sup[key] == n) & (n < V)).sum())
+    return out
 
 
 def in_support(keys_row: np.ndarray, key_thr: int, id_thr: int) -> np.ndarray:
@@ -364,9 +379,18 @@ def backward(h, W, target, fwd: dict, grad_logprob, temperature=None):
     ``dW`` [V, H] summed over those rows.
     """
     dz = dlogits(h, W, target, fwd, grad_logprob, temperature)
-    h64 = np.asarray(h, dtype=np.float64)[fwd["rows"]]
+    return gradient_products(dz, np.asarray(h)[fwd["rows"]], W)
+
+
+def gradient_products(dz, h, W):
+    """``(dH, dW) = (dz W, dz^T h)`` in fp64 for ``dz`` [R, V] and the rows
+    ``h`` [R, H] it belongs to.  ``dz`` may be a dense array or a
+    ``scipy.sparse`` matrix holding the same values (dz is nonzero only on the
+    support, so a top-k row has at most k nonzeros): the products are the
+    same sums either way."""
+    h64 = np.asarray(h, dtype=np.float64)
     W64 = np.asarray(W, dtype=np.float64)
-    return dz @ W64, dz.T @ h64
+    return np.asarray(dz @ W64), np.asarray(dz.T @ h64)
 
 
 def round_to_bf16(x) -> np.ndarray:

@@ -30,6 +30,7 @@ SYMBOLS = (
     "stce_scaled_logits", "stce_support_from_logits", "stce_support_workspace_bytes",
     "stce_decode_state", "stce_status_string", "stce_last_error", "stce_profile_attach", "stce_schedule",
     "stce_policy_loss", "stce_forward_with_side", "stce_fused_workspace_bytes", "stce_fused_policy_step",
+    "stce_recompute_keys",
 )
 KERNEL_KINDS = {1: "validate", 2: "projection", 3: "select", 4: "dlogits", 5: "grad_weight",
                 6: "grad_hidden", 7: "transpose", 8: "partials", 9: "policy_loss", 10: "dz_keys",
@@ -96,6 +97,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "stce_workspace_bytes": (ctypes.c_int, [P, ctypes.POINTER(sz), ctypes.POINTER(sz)]),
         "stce_forward": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
         "stce_backward": (ctypes.c_int, [P, vp, vp, vp, vp, i32, vp, vp, sz, vp]),
+        "stce_recompute_keys": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
         "stce_scaled_logits": (ctypes.c_int, [P, i64, i64, vp, vp, sz, vp]),
         "stce_support_from_logits": (ctypes.c_int, [vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "stce_support_workspace_bytes": (sz, [i64, i64]),
@@ -279,6 +281,25 @@ def backward(hidden, weight, target, state, grad_logprob, temperature=None, top_
     _check(load().stce_backward(ctypes.byref(prob), _ptr(g), _ptr(state), _ptr(gh), _ptr(grad_weight),
                                 1 if accumulate_grad_weight else 0, None, _ptr(ws), ws.numel(), _stream()))
     return gh, grad_weight
+
+
+def recompute_keys(hidden, weight, target, state, grad_logprob, temperature=None, top_k=None, top_p=None,
+                   min_p=None, *, vocab_slice: int = 0, ignore_index: Optional[int] = None,
+                   pre_gemm_temperature: Optional[float] = None, lane: str = "fp32"):
+    """fp32 keys [T, V] recomputed by the backward's product, exported by that
+    launch itself (parity: they must equal the forward's bit for bit)."""
+    prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, 0, vocab_slice,
+                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane)
+    dev = hidden.device
+    if state.numel() != prob.T * STATE_BYTES_PER_ROW or state.dtype != torch.uint8:
+        raise ValueError("state must be the uint8 [T*32] tensor written by forward")
+    _, bwd_b = workspace_bytes(prob)
+    ws = torch.empty(max(bwd_b, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty(prob.T, prob.V, dtype=torch.float32, device=dev)
+    g = grad_logprob.contiguous()
+    _check(load().stce_recompute_keys(ctypes.byref(prob), _ptr(g), _ptr(state), _ptr(out), _ptr(ws), ws.numel(),
+                                      _stream()))
+    return out
 
 
 def scaled_logits(hidden, weight, temperature=None, row0: int = 0, nrows: Optional[int] = None, *,

@@ -38,6 +38,7 @@ constexpr int64_t kDefaultChunk = 4096;   // forward rows per chunk
 constexpr double kSliceBudgetBytes = 8e9;
 constexpr int64_t kMaxSlice = (1 << 22) - 256;  // vocabulary columns of a slice
 constexpr size_t kAlign = 256;
+constexpr int64_t kMaxRows = (1 << 22) - 64;    // scored rows per call
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -76,7 +77,11 @@ stce_status check_shapes(const stce_problem* p) {
                 (int)p->dtype);
   if (bf16_lane(p) && p->dtype != STCE_DT_BF16)
     return fail(STCE_E_UNSUPPORTED, "the bf16 value lane (STCE_PROBLEM_BF16_LANE) takes bf16 hidden and weight");
-  if (p->T < 1 || p->T > INT32_MAX - 512) return fail(STCE_E_ARG, "T=%lld out of range [1, 2^31-513]", (long long)p->T);
+  // the weight-gradient product reads dz^T K-major with a row length of T
+  // padded to 64, through a buffer resource of 256 such rows whose byte
+  // count is 32-bit: 512 * round_up(T, 64) must stay below 2^31
+  if (p->T < 1 || p->T > kMaxRows)
+    return fail(STCE_E_ARG, "T=%lld out of range [1, %lld]", (long long)p->T, (long long)kMaxRows);
   if (p->H < 8 || p->H % 8 != 0 || p->H > (1 << 20))
     return fail(STCE_E_ARG, "H=%lld must be a positive multiple of 8 (<= 2^20)", (long long)p->H);
   if (p->V < 1 || p->V > INT32_MAX - 512) return fail(STCE_E_ARG, "V=%lld out of range [1, 2^31-513]", (long long)p->V);
@@ -424,9 +429,16 @@ stce_status stce_forward_with_side(const stce_problem* p, float* logprob, void* 
   return STCE_OK;
 }
 
-stce_status stce_backward(const stce_problem* p, const float* grad_logprob, const void* state, void* grad_hidden,
+}  // extern "C"
+
+namespace {
+
+// stce_backward, and with keys_out the parity export of its recompute
+// product (stce_recompute_keys): the same launches up to the recompute, which
+// then also writes its keys, and no gradient product.
+stce_status backward_impl(const stce_problem* p, const float* grad_logprob, const void* state, void* grad_hidden,
                           float* grad_weight, int32_t accumulate_grad_weight, int64_t* dev_status, void* ws,
-                          size_t ws_bytes, void* stream) {
+                          size_t ws_bytes, void* stream, float* keys_out) {
   stce_status s = check_shapes(p);
   if (s) return s;
   if ((s = check_inputs(p))) return s;
@@ -444,11 +456,11 @@ stce_status stce_backward(const stce_problem* p, const float* grad_logprob, cons
                              at<uint32_t>(ws, L.b_flags), dev_status, st)))
       return hip_fail(e, "validate");
   }
-  if (!grad_hidden && !grad_weight) return STCE_OK;
+  if (!grad_hidden && !grad_weight && !keys_out) return STCE_OK;
   const void* hid = nullptr;
   float dh_div = 1.0f;
   if ((e = hidden_for_products(p, ws, L.b_hs, 0, p->T, &hid, &dh_div, st))) return hip_fail(e, "prescale hidden");
-  if (grad_weight && p->dtype != STCE_DT_BF16) {
+  if (grad_weight && !keys_out && p->dtype != STCE_DT_BF16) {
     // the fp32 products take K-major operands only (bf16 reads h as it is)
     if ((e = launch_transpose_f32((const float*)hid, p->H, p->T, p->H, at<float>(ws, L.b_hT), L.Tp, L.Tp, st)))
       return hip_fail(e, "transpose hidden");
@@ -483,9 +495,28 @@ stce_status stce_backward(const stce_problem* p, const float* grad_logprob, cons
     a.last = si == nsl - 1;
     a.dh_div = dh_div;
     a.bf16_lane = bf16_lane(p);
+    a.keys_out = keys_out;
+    a.ld_keys = p->V;
     if ((e = launch_bwd_slice(a, st))) return hip_fail(e, "backward slice");
   }
   return STCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+stce_status stce_backward(const stce_problem* p, const float* grad_logprob, const void* state, void* grad_hidden,
+                          float* grad_weight, int32_t accumulate_grad_weight, int64_t* dev_status, void* ws,
+                          size_t ws_bytes, void* stream) {
+  return backward_impl(p, grad_logprob, state, grad_hidden, grad_weight, accumulate_grad_weight, dev_status, ws,
+                       ws_bytes, stream, nullptr);
+}
+
+stce_status stce_recompute_keys(const stce_problem* p, const float* grad_logprob, const void* state,
+                                float* keys_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!keys_out) return fail(STCE_E_ARG, "keys_out is required");
+  return backward_impl(p, grad_logprob, state, nullptr, nullptr, 0, nullptr, ws, ws_bytes, stream, keys_out);
 }
 
 stce_status stce_scaled_logits(const stce_problem* p, int64_t row0, int64_t nrows, float* s_out, void* ws,

@@ -282,6 +282,10 @@ struct EpiDlogits {
   int64_t ld_dT;
   int v0, Vs, Vs_pad, N, N_pad;
   int bf16_lane = 0;       // keys of the bf16 value lane
+  // parity export (null in every production launch): the recomputed keys of
+  // the tile, keys_out[n * ld_keys + v0 + m], for n < N and m < Vs
+  float* keys_out = nullptr;
+  int64_t ld_keys = 0;
   // bf16: the vocab-major tile leaves through LDS, 128 rows in each of the
   // two epilogue buffers
   static constexpr int LDS_BYTES = sizeof(OutT) == 2 ? 128 * GN * 2 : 0;
@@ -305,6 +309,15 @@ struct EpiDlogits {
       }
       if (n >= N_pad) continue;
       keys_column(acc, j, t, bf16_lane);
+      if (keys_out && nv) {
+#pragma unroll
+        for (int i = 0; i < ACC_I; ++i)
+#pragma unroll
+          for (int e = 0; e < ACC_R; ++e) {
+            const int m = m0 + wmu * 128 + i * 16 + quad * 4 + e;
+            if (m < Vs) keys_out[(int64_t)n * ld_keys + v0 + m] = acc[i][j][e];
+          }
+      }
       // support membership as a float compare against the boundary key's
       // value (-0 == +0 like the canonical keys); unfiltered rows keep all
       const float sthr = (rs.flags & ROW_FILTERED) ? key_value(rs.key_thr) : -STCE_INF;

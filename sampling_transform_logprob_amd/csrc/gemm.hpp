@@ -1,10 +1,13 @@
-// Block-tiled "NT" matrix product for gfx950: C[m, n] = sum_k A[m, k] * B[n, k]
-// with both operands row-major and contiguous along k.  Every product of the
-// scoring core has this form once the backward keeps transposed copies of its
-// operands (h^T, a W^T slice, dz^T):
-//   projection   z^T[v, t] = W[v, :] . h[t, :]       (M = vocab, N = tokens, K = H)
-//   weight grad  dW[v, :] = dz^T[v, :] . h^T[:, :]   (M = vocab, N = H,      K = tokens)
-//   hidden grad  dH[t, :] = dz[t, :] . W^T[:, :]     (M = tokens, N = H,     K = vocab)
+// Block-tiled matrix product for gfx950: C[m, n] = sum_k A[m, k] * B[n, k].
+// Each operand is read either K-major (row-major along k) or MN-major
+// (row-major along m or n, through transposing LDS reads; see the bf16 main
+// loop below), so the products of the scoring core read their operands as
+// they lie in memory:
+//   projection   z^T[v, t] = W[v, :] . h[t, :]       (M = vocab, N = tokens, K = H; both K-major)
+//   weight grad  dW[v, :] = dz^T[v, :] . h[:, :]     (M = vocab, N = H, K = tokens; h MN-major)
+//   hidden grad  dH^T[:, t] = W^T[:, :] . dz^T[:, t] (M = H, N = tokens, K = vocab; dz^T MN-major,
+//                                                     W^T a transposed copy)
+// The fp32 main loop (plain fmas, small shapes) takes K-major operands only.
 //
 // Block tile 256 x 256, k-tile 64, 512 threads = 8 waves (2 per SIMD) in a
 // 2 (m) x 4 (n) grid, each wave owning a 128 x 64 sub-tile = 8 x 4 blocks of

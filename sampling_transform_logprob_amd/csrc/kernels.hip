@@ -498,11 +498,14 @@ hipError_t bwd_slice_impl(const BwdSliceArgs& a, hipStream_t s) {
     EpiDlogits<E> ep{a.temp, a.target, a.st, a.g, (E*)a.d, a.ld_d, (E*)a.dT, a.Tp,
                      (int)a.v0, (int)a.vs, (int)a.vsp, (int)a.T, (int)a.Tp};
     ep.bf16_lane = a.bf16_lane;
+    ep.keys_out = a.keys_out;
+    ep.ld_keys = a.ld_keys;
     Main mn{W + a.v0 * a.H, a.H, (int)a.vs, (const E*)a.h, a.H, (int)a.T, (int)a.H};
     ProfScope ps(4, s);
     e = launch_gemm(mn, ep, ceil_div(a.vsp, GM), ceil_div(a.Tp, GN), s);
     if (e != hipSuccess) return e;
   }
+  if (a.keys_out) return hipSuccess;
   // 2. weight gradient of the slice: dW[v0 + m, :] = dz^T[m, :] . h^T
   if (a.grad_weight) {
     EpiStore ep{a.grad_weight + a.v0 * a.H, a.H, (int)a.vs, (int)a.H, a.accumulate_w};
@@ -541,11 +544,14 @@ hipError_t bwd_slice_bf16(const BwdSliceArgs& a, hipStream_t s) {
     EpiDlogits<bf16> ep{a.temp, a.target, a.st, a.g, nullptr, 0, (bf16*)a.dT, a.Tp,
                         (int)a.v0, (int)a.vs, (int)a.vsp, (int)a.T, (int)a.Tp};
     ep.bf16_lane = a.bf16_lane;
+    ep.keys_out = a.keys_out;
+    ep.ld_keys = a.ld_keys;
     MainBf16 mn{W + a.v0 * a.H, a.H, (int)a.vs, (const bf16*)a.h, a.H, (int)a.T, (int)a.H};
     ProfScope ps(4, s);
     e = launch_gemm(mn, ep, ceil_div(a.vsp, GM), ceil_div(a.Tp, GN), s);
     if (e != hipSuccess) return e;
   }
+  if (a.keys_out) return hipSuccess;
   // 2. weight gradient of the slice: dW[v0 + m, :] = sum_t dz^T[m, t] h[t, :],
   //    h read as it is (MN-major, k = token; rows past T read 0)
   if (a.grad_weight) {

@@ -84,6 +84,10 @@ struct BwdSliceArgs {
   int first, last;
   float dh_div;        // the hidden gradient's final value is divided by it (1 = none)
   int bf16_lane;       // keys of the bf16 value lane
+  // parity export: when set, only the recompute product runs, and it also
+  // writes the keys it recomputes to keys_out [T][ld_keys] (columns v0 ..)
+  float* keys_out;
+  int64_t ld_keys;
 };
 hipError_t launch_bwd_slice(const BwdSliceArgs& a, hipStream_t s);
 

@@ -112,7 +112,7 @@ struct Shared {
   double sd[ST / 64];
   float sf[ST / 64];
   int si[ST / 64];
-  uint16_t tiles[TLIST];   // vocabulary tiles that can hold window tokens
+  uint32_t tiles[TLIST];   // vocabulary tiles that can hold window tokens (V < 2^31: up to 2^23 tiles)
   int ntiles;
   uint32_t bkey;
   double mass_o;           // mass of the first n_other window tokens
@@ -125,6 +125,10 @@ struct Shared {
   double Z;          // full-row mass
   double mass_s;     // mass of the support
 };
+
+// The projection's two LDS stages take 128 KB of a compute unit's 160 KB, so
+// a selection workgroup fits beside a projection workgroup only within 32 KB.
+static_assert(sizeof(Shared) <= 32 * 1024, "selection LDS must fit beside a projection workgroup");
 
 // At most 96 VGPRs (5 waves per SIMD): one of these waves fits beside the
 // two projection waves of a SIMD.
@@ -284,7 +288,7 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
         const float tm = pp[t].mx;
         if ((!kb || order_key(tm) >= bkey) && (!m_on || (double)tm - m64 >= thr)) {
           const int i = atomicAdd(&S.ntiles, 1);
-          if (i < TLIST) S.tiles[i] = (uint16_t)t;
+          if (i < TLIST) S.tiles[i] = (uint32_t)t;
         }
       }
       __syncthreads();

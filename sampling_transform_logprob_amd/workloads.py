@@ -31,6 +31,9 @@ CONFIGS = {
     "top_p": dict(T=8192, H=4096, V=128256, dtype="bf16", seed=3),
     # the headline shape: temperature 0.7, top-k 20, top-p 0.8
     "headline": dict(T=16384, H=5120, V=151936, dtype="bf16", seed=4),
+    # the headline program on a sharper head (W std x3): logits/T std about 6,
+    # so top-p 0.8 binds inside top-k 20 on most rows (a parity variant)
+    "headline_sharp": dict(T=16384, H=5120, V=151936, dtype="bf16", seed=6, w_std=0.06),
     # 4-bit weight levels with duplicated rows: many bitwise-equal logits
     "ties": dict(T=32768, H=7168, V=129280, dtype="bf16", seed=5),
 }
@@ -73,7 +76,7 @@ def make(name: str, T: int | None = None, seed: int | None = None) -> dict:
         pool = np.clip(np.rint(pool * 64.0), -8, 7).astype(np.float32) / np.float32(64.0)
         W = pool[rp.integers(0, V // 6, size=V)]
     else:
-        W = rw.standard_normal((V, H), dtype=np.float32) * np.float32(0.02)
+        W = rw.standard_normal((V, H), dtype=np.float32) * np.float32(cfg.get("w_std", 0.02))
     h = rh.standard_normal((T, H), dtype=np.float32)
     if bf16:
         W, h = round_bf16(W), round_bf16(h)
@@ -89,7 +92,7 @@ def make(name: str, T: int | None = None, seed: int | None = None) -> dict:
     elif name == "top_p":
         temp = rm.uniform(0.6, 1.2, T).astype(np.float32)
         top_k, top_p, min_p = np.zeros(T, np.int32), np.full(T, 0.95, np.float32), np.zeros(T, np.float32)
-    elif name == "headline":
+    elif name in ("headline", "headline_sharp"):
         temp = np.full(T, 0.7, np.float32)
         top_k, top_p, min_p = np.full(T, 20, np.int32), np.full(T, 0.8, np.float32), np.zeros(T, np.float32)
     elif name == "ties":

@@ -68,10 +68,17 @@ def test_unsupported_dtype_is_one_actionable_error(lib):
     (dict(T=0), "T=0"), (dict(H=12), "H=12"), (dict(V=0), "V=0"), (dict(flags=8), "flags"),
     (dict(flags=1, ignore_index=5), "ignore_index=5"),
     (dict(chunk_rows=-1), "chunk_rows"),
+    # 512 * round_up(T, 64) bytes must fit a 32-bit buffer record count
+    (dict(T=(1 << 22) - 63), "T=4194241"),
 ])
 def test_bad_shapes_are_rejected(lib, kw, msg):
     with pytest.raises(binding.StceError, match=msg):
         binding.workspace_bytes(_prob(**kw))
+
+
+def test_largest_row_count_is_accepted(lib):
+    f, b = binding.workspace_bytes(_prob(T=(1 << 22) - 64))
+    assert f > 0 and b > 0
 
 
 @pytest.mark.parametrize("ts", [0.0, -0.5, float("nan"), float("inf")])

@@ -55,7 +55,8 @@ def test_projection_accuracy_and_temperature_bitwise():
 
 
 # ---------------------------------------------------------------- five workloads, reduced T
-CASES = [("tiny", 64), ("identity", 300), ("top_p", 300), ("headline", 300), ("ties", 300)]
+CASES = [("tiny", 64), ("identity", 300), ("top_p", 300), ("headline", 300), ("ties", 300),
+         ("headline_sharp", 300)]
 
 
 @pytest.mark.parametrize("name,T", CASES)
@@ -72,9 +73,12 @@ def test_workload_parity(name, T):
     err = check_logprob(lp.cpu().numpy(), ref)
     dH, dW = oracle.backward(w["h"], w["W"], y, ref, g, w["temperature"])
     rh, rw = rel_fro(gh.float().cpu().numpy(), dH), rel_fro(gw.cpu().numpy(), dW)
+    binds = oracle.binding_filters(oracle.support(kc, w["top_k"], w["top_p"], w["min_p"]), w["V"])
     say(f"  near={near} logprob err={err:.2e} dH rel={rh:.2e} dW rel={rw:.2e} "
-        f"supports: min {info['n'].min()} max {info['n'].max()}")
+        f"supports: min {info['n'].min()} max {info['n'].max()}; binding filter rows {binds}")
     assert near == 0
+    if name == "headline_sharp":      # top-p binds inside top-k on most rows: its path is exercised
+        assert binds["top_p"] > T // 2 and binds["top_p"] > binds["top_k"]
     assert rh < GRAD_RTOL and rw < GRAD_RTOL
     # the independent run (oracle's own fp64 keys): boundary flips are rare
     own = oracle.forward(w["h"], w["W"], y, w["temperature"], w["top_k"], w["top_p"], w["min_p"])
@@ -231,14 +235,23 @@ def test_temperature_division_bitwise_on_many_pairs():
     Reference: fp64 quotient of the two fp32 values rounded to fp32 (exact,
     since 53 >= 2*24 + 2)."""
     rng = np.random.Generator(np.random.PCG64(99))
-    V, T, H = 1 << 20, 64, 8
+    V, T, H = 1 << 21, 64, 8                                  # 2^27 > 1e8 (z, T) pairs
+    ones = lambda e: (np.asarray(e, np.uint32) << 23 | 0x7FFFFF).view(np.float32)   # all-ones significands
+    nz1 = 4096
     z = np.concatenate([
         (rng.standard_normal(V // 2) * 10).astype(np.float32),
-        (np.exp(rng.uniform(-80, 80, V // 2 - 16)) * rng.choice([-1, 1], V // 2 - 16)).astype(np.float32),
+        (np.exp(rng.uniform(-80, 80, V // 2 - 16 - 2 * nz1)) * rng.choice([-1, 1], V // 2 - 16 - 2 * nz1)
+         ).astype(np.float32),
+        ones(rng.integers(1, 254, nz1)) * rng.choice([-1, 1], nz1).astype(np.float32),
+        (rng.integers(1, 1 << 23, nz1, dtype=np.uint32) | np.uint32(127 << 23)).view(np.float32),
         np.float32([0.0, -0.0, 1e-38, -1e-38, 3e38, -3e38, 1.0, -1.0, 1e-45, 2e-45, 1.5, 7.0, 1e-30, 1e30, 2.0, 0.5]),
     ]).astype(np.float32)
-    t = np.concatenate([rng.uniform(0.05, 3.0, T - 8),
+    # divisors with an all-ones significand (the largest significand below a
+    # power of two: the reciprocal's correction step works hardest there)
+    t_ones = ones([126, 127, 125, 128, 124, 129, 120, 133, 100, 150, 97, 156])
+    t = np.concatenate([rng.uniform(0.05, 3.0, T - 8 - len(t_ones)), t_ones,
                         [1.0, 0.7, 1e-3, 3.0, 0.3, 1.5, 1e-20, 1e20]]).astype(np.float32)
+    assert len(t) == T and z.shape == (V,)
     W = np.zeros((V, H), np.float32)
     W[:, 0] = z
     h = np.zeros((T, H), np.float32)

@@ -2,7 +2,7 @@
 
 ``stce_support_from_logits`` runs the forward's selection kernel on given
 keys; the oracle computes the support of the very same keys.  The rows cover
-every path of the kernel: whole-row windows (V <= 3840), bounded candidates
+every path of the kernel: whole-row windows (V <= CAP), bounded candidates
 (top-k from tile maxima, min-p), the value histogram, and the radix
 refinement used when a histogram bin holds more tokens than the window
 (long tie groups, very peaked rows), plus the identities of the program."""
@@ -17,6 +17,8 @@ from gpu_helpers import dev, say
 from sampling_transform_logprob_amd import binding
 
 pytestmark = pytest.mark.gpu
+
+CAP = 3712   # the selection kernel's window capacity (tokens gathered into LDS)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -69,12 +71,12 @@ def _grid(rng, V, R, ties):
     return keys
 
 
-@pytest.mark.parametrize("V", [4, 8, 300, 1000, 3840, 3844, 4096, 5000, 40000])
+@pytest.mark.parametrize("V", [4, 8, 300, 1000, CAP, CAP + 4, 4096, 5000, 40000])
 def test_random_rows_all_filter_mixes(V):
     rng = np.random.Generator(np.random.PCG64(V))
     R = 96
     keys = _grid(rng, V, R, ties=(V % 2 == 0))
-    ks = np.array([0, 1, 2, 20, 64, V - 1, V, V + 5, 3839, 3841, 4097])
+    ks = np.array([0, 1, 2, 20, 64, V - 1, V, V + 5, CAP - 1, CAP + 1, 4097])
     ps = np.array([1.0, 0.9, 0.5, 1e-6, np.nextafter(np.float32(1), np.float32(0)), 0.99])
     mps = np.array([0.0, 0.0, 0.1, 1.0, 1e-3])
     k = np.maximum(ks[rng.integers(0, len(ks), R)], 0)
@@ -173,7 +175,7 @@ def test_vocabularies_beyond_the_tile_bound_search():
     the value histogram (and radix refinement on ties).  Also a vocabulary
     just below that limit, where the search still runs."""
     rng = np.random.Generator(np.random.PCG64(29))
-    for V, R in ((2 * 3840 * 256 + 256, 6), (2 * 3840 * 256 - 256, 6)):
+    for V, R in ((2 * CAP * 256 + 256, 6), (2 * CAP * 256 - 256, 6)):
         keys = (rng.standard_normal((R, V)) * rng.uniform(0.5, 3, (R, 1))).astype(np.float32)
         keys[1] = np.round(keys[1] * 2) / 2                     # heavy ties
         k = np.array([20, 1000, 64, 0, 5, 3000], np.int32)
@@ -181,3 +183,27 @@ def test_vocabularies_beyond_the_tile_bound_search():
         mp = np.array([0.0, 0.0, 0.05, 0.0, 0.0, 1e-4], np.float32)
         y = np.array([int(np.argmax(keys[r])) for r in range(R)])
         _check(keys, k, p, mp, y, f"V={V}")
+
+
+def test_min_p_tiles_above_index_65535():
+    """V = 2^24 + 1024 has 65,540 vocabulary tiles.  A min-p row whose
+    passing tokens sit only in tiles 65,536 .. 65,539 takes the candidate-tile
+    list; the list must keep those indices whole (a 16-bit index would wrap
+    them to tiles 0 .. 3 and read the wrong keys).  A top-k row at this V
+    takes the value histogram (too many tile maxima for the bound search)."""
+    V = (1 << 24) + 1024
+    rng = np.random.Generator(np.random.PCG64(41))
+    keys = rng.uniform(-10.0, -9.0, (3, V)).astype(np.float32)
+    hi = 1 << 24                                    # first token of tile 65,536
+    for r in range(3):
+        keys[r, hi + 10] = 5.0                      # tile 65,536: the row maximum
+        keys[r, hi + 300] = 4.8                     # tile 65,537
+        keys[r, hi + 900] = 4.5                     # tile 65,539
+        keys[r, 77] = 4.0                           # tile 0: below the min-p bar of rows 0 and 1
+    k = np.array([0, 0, 2], np.int32)
+    p = np.array([1.0, 0.9, 1.0], np.float32)
+    mp = np.array([0.5, 0.5, 0.0], np.float32)      # ln 0.5 = -0.69: keys >= 4.31 pass
+    y = np.array([hi + 900, hi + 10, hi + 300])
+    info = _check(keys, k, p, mp, y, "tiles above 65535")
+    assert info["n"][0] == 3 and info["id_thr"][0] == hi + 900
+    assert info["n"][2] == 2 and info["id_thr"][2] == hi + 300

@@ -40,7 +40,8 @@ MUTANTS = {
     "min-p against the second-largest key": ("gap = s64[pi] - m ", "gap = s64[pi] - s64[pi[min(1, V - 1)]] ",
                                              ["test_min_p_one_keeps_the_whole_max_tie_group",
                                               "test_min_p_closed_form_matches_probability_space"]),
-    "dW uses the wrong operand": ("return dz @ W64, dz.T @ h64", "return dz @ W64, dz.T @ (h64 * 0.5)",
+    "dW uses the wrong operand": ("return np.asarray(dz @ W64), np.asarray(dz.T @ h64)",
+                                  "return np.asarray(dz @ W64), np.asarray(dz.T @ (h64 * 0.5))",
                                   ["test_gradients_match_central_differences"]),
     "CISPO weight not a stop-gradient": ("            g[t] = -A[t] * wgt\n",
                                          "            g[t] = -A[t] * wgt - (A[t] * r * lp[t] if r < 1.0 + eh else 0.0)\n",

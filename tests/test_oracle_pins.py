@@ -396,6 +396,31 @@ def test_weight_gradient_columns_sum_to_zero(rng):
     assert np.abs(dW.sum(axis=0)).max() < 1e-12 * max(1.0, np.abs(dW).max())
 
 
+def test_gradient_products_take_sparse_dz_with_the_same_sums():
+    """dz is nonzero only on the support; the products dz W and dz^T h of a
+    scipy.sparse copy equal the dense ones (pins the sparse form a full-size
+    test uses), and equal a hand loop over the nonzeros.  (Its own generator:
+    the session one feeds the pins that follow.)"""
+    sp = pytest.importorskip("scipy.sparse")
+    rng = np.random.Generator(np.random.PCG64(515))
+    h, W, temp = _problem(rng, T=7, V=40, scale=2)
+    meta = dict(top_k=np.array([3, 0, 5, 1, 0, 2, 4]), top_p=np.array([1, .8, 1, 1, .6, 1, 1], np.float32))
+    y = np.array([oracle.order_row(oracle.forward(h, W, np.zeros(7, np.int64), temp, **meta)["keys"][t])[0]
+                  for t in range(7)])
+    f = oracle.forward(h, W, y, temp, **meta)
+    g = rng.standard_normal(7)
+    dz = oracle.dlogits(h, W, y, f, g, temp)
+    dH, dW = oracle.backward(h, W, y, f, g, temp)
+    sH, sW = oracle.gradient_products(sp.csr_matrix(dz), h, W)
+    np.testing.assert_allclose(sH, dH, rtol=1e-14, atol=1e-16)
+    np.testing.assert_allclose(sW, dW, rtol=1e-14, atol=1e-16)
+    loopW = np.zeros_like(dW)
+    for t, j in zip(*np.nonzero(dz)):
+        loopW[j] += dz[t, j] * h[t].astype(np.float64)
+    np.testing.assert_allclose(loopW, dW, rtol=1e-13, atol=1e-16)
+    assert (np.count_nonzero(dz, axis=1) <= np.where(meta["top_k"] > 0, meta["top_k"], 40)).all()
+
+
 def test_sampled_targets_lie_in_support(rng):
     h, W, temp = _problem(rng, T=30, V=64, scale=3)
     meta = dict(top_k=rng.choice([0, 5], 30), top_p=rng.choice([1.0, 0.7], 30).astype(np.float32),
