@@ -125,6 +125,17 @@ def filter_binding(info, w):
     return out
 
 
+def row_classes(info, g, nsp=128):
+    """Rows of each backward class, by the library's rule: a row with a
+    gradient (target in its support, valid metadata, nonzero upstream
+    gradient) is sparse when its support holds at most nsp tokens, dense
+    otherwise (unfiltered rows included); the others are empty."""
+    fl = info["flags"]
+    active = ((fl & 1) != 0) & ((fl & 4) != 0) & (g != 0)
+    dense = active & (((fl & 2) == 0) | (info["n"] > nsp))
+    return {"dense": int(dense.sum()), "sparse": int((active & ~dense).sum()), "empty": int((~active).sum())}
+
+
 KERNEL_SYMBOLS = {
     # kernel kind -> epilogue name in its (mangled or demangled) symbol; the bf16 main loop
     "projection": "EpiLogits",
@@ -472,20 +483,32 @@ def main():
     if args.fused:
         C = min(-(-(args.chunk_rows or 4096) // 64) * 64, -(-T // 64) * 64)
         Vs = None
-    per_step_flop = {k: 2.0 * T * H * V for k in ("projection", "dlogits", "grad_weight", "grad_hidden")}
+    # the backward's row classes (bf16 unfused step): the recompute product
+    # runs over the rows with a gradient, the two gradient products over the
+    # dense rows; sparse rows' gradients are sums over their dz entries
+    classes = row_classes(binding.decode_state(state), g.cpu().numpy())
+    classed = dt == torch.bfloat16 and not args.fused
+    t_act = classes["dense"] + classes["sparse"] if classed else T
+    t_dense = classes["dense"] if classed else T
+    per_step_flop = {"projection": 2.0 * T * H * V, "dlogits": 2.0 * t_act * H * V,
+                     "grad_weight": 2.0 * t_dense * H * V, "grad_hidden": 2.0 * t_dense * H * V}
+    if args.fused:
+        per_step_flop = {k: 2.0 * T * H * V for k in ("projection", "grad_weight", "grad_hidden")}
     stats = {}
     per_launch = {}
     for k, v in kinds.items():
         a = np.array(v)
         n_launch = len(a) / prof_steps
         stats[k] = dict(launches=int(n_launch), avg_ms=float(a.mean()), total_ms_per_step=float(a.sum() / prof_steps))
-        if k in per_step_flop:
+        if per_step_flop.get(k):
             per_launch[k] = per_step_flop[k] / n_launch
             stats[k]["tflops"] = per_launch[k] / (a.mean() * 1e-3) / 1e12
     dom = max((k for k in stats if k in per_launch), key=lambda k: stats[k]["total_ms_per_step"])
     achieved = stats[dom]["tflops"]
 
-    flop_step = (6.0 if args.fused else 8.0) * T * H * V
+    # matrix-core flop the step performs (the dense formulation would perform
+    # 8 T H V: forward, recompute, dH, dW over every row)
+    flop_step = sum(per_step_flop.values())
     value = T / (ms_step * 1e-3)
     out = {
         "metric": "scored tokens/s fwd+bwd at V=151936,H=5120; % of bf16 MFMA peak",
@@ -518,9 +541,12 @@ def main():
                                   if ts is not None else ""),
                    "T": T, "H": H, "V": V, "chunk_rows": C, "vocab_slice": Vs},
         "mfma_peak_frac": flop_step / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
-        "tflops_8thv": 8.0 * T * H * V / (ms_step * 1e-3) / 1e12,
+        "mfma_flop_per_step": flop_step,
         "tflops_performed": flop_step / (ms_step * 1e-3) / 1e12,
+        "tflops_8thv": 8.0 * T * H * V / (ms_step * 1e-3) / 1e12,
+        "dense_equivalent_frac_8thv": 8.0 * T * H * V / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "tflops_6thv": 6.0 * T * H * V / (ms_step * 1e-3) / 1e12,
+        "row_classes": classes if classed else None,
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                      "traffic": read_traffic(dom, args.config)},

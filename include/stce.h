@@ -301,6 +301,9 @@ stce_status stce_decode_state(const void *host_state, int64_t nrows, stce_row_in
 #define STCE_KERNEL_DZ_KEYS 10     /* fused step: dlogits from a chunk's stored keys */
 #define STCE_KERNEL_SPLIT_SUM 11   /* fused step: sum of the hidden-gradient split partials */
 #define STCE_KERNEL_PRESCALE 12    /* hidden states divided by the scalar pre-GEMM temperature */
+#define STCE_KERNEL_CLASSIFY 13    /* backward: row classes (dense, sparse, empty) and their order */
+#define STCE_KERNEL_SPARSE_DW 14   /* backward: weight-gradient rows from the sparse rows' dz entries */
+#define STCE_KERNEL_SPARSE_DH 15   /* backward: hidden-gradient rows of the sparse and empty rows */
 typedef struct stce_profile {
   int32_t capacity;
   int32_t count;

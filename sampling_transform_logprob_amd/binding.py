@@ -34,7 +34,8 @@ SYMBOLS = (
 )
 KERNEL_KINDS = {1: "validate", 2: "projection", 3: "select", 4: "dlogits", 5: "grad_weight",
                 6: "grad_hidden", 7: "transpose", 8: "partials", 9: "policy_loss", 10: "dz_keys",
-                11: "split_sum", 12: "prescale"}
+                11: "split_sum", 12: "prescale", 13: "classify", 14: "sparse_grad_weight",
+                15: "sparse_grad_hidden"}
 PG_OBJECTIVES = {"cispo": 1, "clip": 2}
 
 

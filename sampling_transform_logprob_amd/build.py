@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libstce.so")
-SOURCES = ["kernels.hip", "select.hip", "api.hip"]
+SOURCES = ["kernels.hip", "select.hip", "sparse.hip", "api.hip"]
 
 FLAGS = [
     "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",

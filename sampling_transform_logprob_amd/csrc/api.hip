@@ -48,6 +48,10 @@ struct Layout {
   size_t buf_tile, buf_part, buf_sy;                       // bytes per chunk buffer
   int64_t Vs, Vsp, Tp;                                      // backward
   size_t b_flags, b_hT, b_WT, b_d, b_dT, b_dh, b_hs, bwd;
+  // backward with row classes (bf16): counts, permutation, per-position
+  // entry counters, classification scratch, permuted hidden rows, entry
+  // lists, per-vocabulary-row counts and bucket offsets, scan scratch, buckets
+  size_t b_cnt, b_perm, b_rowcnt, b_blk, b_hperm, b_list, b_cntj, b_offj, b_sums, b_bucket;
 };
 
 // The scalar pre-GEMM temperature: the problem's hidden states are replaced
@@ -137,7 +141,19 @@ Layout plan(const stce_problem* p) {
   L.b_d = o;     o = align_up(o + (bf ? 0 : es * (size_t)L.Tp * L.Vsp));
   L.b_dT = o;    o = align_up(o + es * (size_t)L.Vsp * L.Tp);
   L.b_dh = o;    o = align_up(o + (p->dtype == STCE_DT_BF16 ? 4 * (size_t)T * H : 0));
-  L.b_hs = o;    o += hs_bytes(p);
+  L.b_hs = o;    o = align_up(o + hs_bytes(p));
+  if (bf) {
+    L.b_cnt = o;    o = align_up(o + sizeof(GradCounts));
+    L.b_perm = o;   o = align_up(o + 4 * (size_t)T);
+    L.b_rowcnt = o; o = align_up(o + 4 * (size_t)T);
+    L.b_blk = o;    o = align_up(o + 4 * grad_class_blk_ints(T));
+    L.b_hperm = o;  o = align_up(o + es * (size_t)T * H);
+    L.b_list = o;   o = align_up(o + sizeof(SpEntry) * (size_t)T * NSP);
+    L.b_cntj = o;   o = align_up(o + 4 * (size_t)V);
+    L.b_offj = o;   o = align_up(o + 4 * ((size_t)V + 1));
+    L.b_sums = o;   o = align_up(o + 4 * scan_sums_ints(V));
+    L.b_bucket = o; o = align_up(o + sizeof(SpEntry) * (size_t)T * NSP);
+  }
   L.bwd = o;
   return L;
 }
@@ -433,6 +449,86 @@ stce_status stce_forward_with_side(const stce_problem* p, float* logprob, void* 
 
 namespace {
 
+// The bf16 backward with row classes: classification of the rows (dense,
+// sparse, empty) and their permutation, the hidden rows gathered into that
+// order, per vocabulary slice the recompute product and the dense rows' two
+// products, then the sparse rows' products over their dz entries.
+stce_status backward_classed(const stce_problem* p, const Layout& L, const float* grad_logprob, const void* state,
+                             const void* hid, float dh_div, void* grad_hidden, float* grad_weight,
+                             int32_t accumulate_grad_weight, void* ws, hipStream_t st, float* keys_out) {
+  hipError_t e;
+  GradCounts* cnt = at<GradCounts>(ws, L.b_cnt);
+  int* perm = at<int>(ws, L.b_perm);
+  int* rowcnt = at<int>(ws, L.b_rowcnt);
+  int* cntj = at<int>(ws, L.b_cntj);
+  bf16* h_perm = at<bf16>(ws, L.b_hperm);
+  SpEntry* list = at<SpEntry>(ws, L.b_list);
+  const bool want_w = grad_weight && !keys_out;
+  if ((e = launch_grad_classes((const RowState*)state, grad_logprob, p->T, at<int>(ws, L.b_blk), cnt, perm, rowcnt,
+                               st)))
+    return hip_fail(e, "row classes");
+  if ((e = launch_gather_rows(1, hid, perm, p->T, p->H, h_perm, st))) return hip_fail(e, "gather hidden rows");
+  if (want_w && (e = launch_fill_i32(cntj, p->V, 0, st))) return hip_fail(e, "clear counts");
+  const int64_t nsl = ceil_div(p->V, L.Vs);
+  for (int64_t si = 0; si < nsl; ++si) {
+    ClassSliceArgs a{};
+    a.W = (const bf16*)p->weight;
+    a.h_perm = h_perm;
+    a.perm = perm;
+    a.cnt = cnt;
+    a.WT = at<bf16>(ws, L.b_WT);
+    a.dT = at<bf16>(ws, L.b_dT);
+    a.dh_sum = at<float>(ws, L.b_dh);
+    a.grad_hidden = keys_out ? nullptr : grad_hidden;
+    a.grad_weight = keys_out ? nullptr : grad_weight;
+    a.accumulate_w = accumulate_grad_weight ? 1 : 0;
+    a.temp = p->temperature;
+    a.target = p->target;
+    a.st = (const RowState*)state;
+    a.g = grad_logprob;
+    a.rowcnt = rowcnt;
+    a.list = list;
+    a.cntj = want_w ? cntj : nullptr;
+    a.T = p->T;
+    a.Tp = L.Tp;
+    a.H = p->H;
+    a.V = p->V;
+    a.v0 = si * L.Vs;
+    a.vs = p->V - a.v0 < L.Vs ? p->V - a.v0 : L.Vs;
+    a.vsp = round_up(a.vs, 64);
+    a.ld_d = L.Vsp;
+    a.first = si == 0;
+    a.last = si == nsl - 1;
+    a.dh_div = dh_div;
+    a.bf16_lane = bf16_lane(p);
+    a.keys_out = keys_out;
+    a.ld_keys = p->V;
+    if ((e = launch_class_slice(a, st))) return hip_fail(e, "backward slice");
+  }
+  if (keys_out) return STCE_OK;
+  SparseGradArgs sa{};
+  sa.dtype = 1;
+  sa.W = p->weight;
+  sa.h_perm = h_perm;
+  sa.perm = perm;
+  sa.cnt = cnt;
+  sa.rowcnt = rowcnt;
+  sa.list = list;
+  sa.cntj = cntj;
+  sa.offj = at<int>(ws, L.b_offj);
+  sa.scan_sums = at<int>(ws, L.b_sums);
+  sa.bucket = at<SpEntry>(ws, L.b_bucket);
+  sa.grad_hidden = grad_hidden;
+  sa.grad_weight = grad_weight;
+  sa.accumulate_w = accumulate_grad_weight ? 1 : 0;
+  sa.T = p->T;
+  sa.H = p->H;
+  sa.V = p->V;
+  sa.dh_div = dh_div;
+  if ((e = launch_sparse_grads(sa, st))) return hip_fail(e, "sparse gradients");
+  return STCE_OK;
+}
+
 // stce_backward, and with keys_out the parity export of its recompute
 // product (stce_recompute_keys): the same launches up to the recompute, which
 // then also writes its keys, and no gradient product.
@@ -460,7 +556,10 @@ stce_status backward_impl(const stce_problem* p, const float* grad_logprob, cons
   const void* hid = nullptr;
   float dh_div = 1.0f;
   if ((e = hidden_for_products(p, ws, L.b_hs, 0, p->T, &hid, &dh_div, st))) return hip_fail(e, "prescale hidden");
-  if (grad_weight && !keys_out && p->dtype != STCE_DT_BF16) {
+  if (p->dtype == STCE_DT_BF16)
+    return backward_classed(p, L, grad_logprob, state, hid, dh_div, grad_hidden, grad_weight, accumulate_grad_weight,
+                            ws, st, keys_out);
+  if (grad_weight && !keys_out) {
     // the fp32 products take K-major operands only (bf16 reads h as it is)
     if ((e = launch_transpose_f32((const float*)hid, p->H, p->T, p->H, at<float>(ws, L.b_hT), L.Tp, L.Tp, st)))
       return hip_fail(e, "transpose hidden");

@@ -47,6 +47,31 @@ struct TilePart {
 
 constexpr int VTILE = 256;  // vocabulary columns per partial
 
+// The backward's row classes.  dz = c (1[j == y] - q) is nonzero only on the
+// row's support, so a row whose support holds at most NSP tokens ("sparse")
+// has at most NSP nonzero dz entries: the recompute emits them as
+// (vocabulary row, value) entries and the two gradient products take them
+// one by one.  Rows with a larger support ("dense") go through the matrix-core
+// products; rows with no gradient (target out of support, invalid or ignored
+// metadata, zero upstream gradient) are "empty".
+constexpr int NSP = 128;
+enum : int { GRAD_DENSE = 0, GRAD_SPARSE = 1, GRAD_EMPTY = 2 };
+
+// Row counts of the classes, written on the device by the classification:
+// rows are placed in the order dense, sparse, empty, each in row order, so
+// dense rows take permuted positions [0, dense) and sparse ones
+// [dense, active).
+struct GradCounts {
+  int dense, sparse, active, pad;
+};
+
+// One nonzero dz entry: a vocabulary row (or, in a weight-gradient bucket,
+// a permuted token position) and its fp32 value.
+struct SpEntry {
+  int32_t idx;
+  float v;
+};
+
 // Order-preserving map of an fp32 key to uint32: a larger float gives a
 // larger unsigned integer; -0 and +0 map to the same value.
 __device__ __host__ inline uint32_t order_key(float s) {

@@ -386,6 +386,142 @@ struct EpiDlogits {
 };
 
 // ---------------------------------------------------------------------------
+// Backward recompute epilogue with row classes (bf16 operands).  M =
+// vocabulary rows of one slice (local m, global v0 + m), N = permuted token
+// positions: position n holds row perm[n]; positions [0, dense) are dense
+// rows, [dense, active) sparse rows, the rest empty (GradCounts).  Recomputes
+// the keys exactly as EpiLogits does and re-derives support membership from
+// the saved boundary, as EpiDlogits does, with the same dz arithmetic
+//   dz[t, v] = c_t (1[v == y_t] - exp(s - lse_S) 1[v in S_t]),  c_t = g_t / T_t.
+// Dense rows: dz rounded to bf16, vocab-major into dT [v][n] (a tile holding
+// any dense position writes all its columns, zeros past the dense ones, so
+// the products reading dT over k = n < dense see zeros in the padding).
+// Sparse rows: every dz of a support token (the only nonzero ones), rounded
+// to bf16 as the dense rows' are, is appended to the position's entry list
+// (list[n * NSP + slot], slot from rowcnt[n]), and counted per vocabulary row
+// in cntj for the weight gradient's buckets.
+// ---------------------------------------------------------------------------
+struct EpiGrad {
+  const int* perm;          // [N] permuted position -> row
+  const GradCounts* cnt;
+  const float* temp;        // [rows] or null
+  const int64_t* target;
+  const RowState* st;
+  const float* g;
+  bf16* dT;                 // [Vs_pad][ld_dT]
+  int64_t ld_dT;
+  int v0, Vs, Vs_pad, N, N_pad;
+  int bf16_lane;
+  int* rowcnt;              // [N]
+  SpEntry* list;            // [N][NSP]
+  int* cntj;                // [V] or null (no weight gradient)
+  float* keys_out = nullptr;  // parity export of the keys, [rows][ld_keys] (null in production)
+  int64_t ld_keys = 0;
+  static constexpr int LDS_BYTES = 128 * GN * 2;
+
+  __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem, char* smem1) const {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
+    const int wmu = __builtin_amdgcn_readfirstlane(wm);
+    const int nd = cnt->dense, na = cnt->active;
+    const bool any_dense = n0 < nd;  // uniform over the workgroup
+    bf16* stg = (bf16*)(wmu ? smem1 : smem);
+    // every per-token load first (loads and stores share one in-order counter)
+    float tv[ACC_J], cv[ACC_J], thr[ACC_J], nlv[ACC_J];
+    int idt[ACC_J], yv[ACC_J], rowv[ACC_J];
+#pragma unroll
+    for (int j = 0; j < ACC_J; ++j) {
+      const int n = n0 + acc_col(wn, j, col);
+      const int t = n < N ? perm[n] : -1;  // the row at this position
+      RowState rs{};
+      float tt = 1.0f, c = 0.f;
+      int y = -1;
+      if (t >= 0 && temp) tt = temp[t];
+      if (n < na) {  // a row with a gradient (dense or sparse)
+        rs = st[t];
+        y = (int)target[t];
+        if ((rs.flags & (ROW_VALID | ROW_IN_SUPPORT)) == (ROW_VALID | ROW_IN_SUPPORT)) c = g[t] / tt;
+      }
+      rowv[j] = t;
+      tv[j] = tt;
+      cv[j] = c;
+      thr[j] = (rs.flags & ROW_FILTERED) ? key_value(rs.key_thr) : -STCE_INF;
+      idt[j] = rs.id_thr;
+      nlv[j] = -rs.lse_s * LOG2E;
+      yv[j] = y;
+    }
+#pragma unroll
+    for (int j = 0; j < ACC_J; ++j) {
+      const int n = n0 + acc_col(wn, j, col);
+      keys_column(acc, j, tv[j], bf16_lane);
+      if (keys_out && rowv[j] >= 0) {
+#pragma unroll
+        for (int i = 0; i < ACC_I; ++i)
+#pragma unroll
+          for (int e = 0; e < ACC_R; ++e) {
+            const int m = m0 + wmu * 128 + i * 16 + quad * 4 + e;
+            if (m < Vs) keys_out[(int64_t)rowv[j] * ld_keys + v0 + m] = acc[i][j][e];
+          }
+      }
+      const float c = cv[j], sthr = thr[j], nl = nlv[j];
+      const int it = idt[j], y = yv[j];
+      const bool live = c != 0.f;
+      const bool dense = n < nd, sparse = live && !dense && n < na;
+      const int nl_ = n - n0;
+#pragma unroll
+      for (int i = 0; i < ACC_I; ++i) {
+        const int base = m0 + wmu * 128 + i * 16;  // the wave's 16 rows (uniform)
+        if (base >= Vs_pad) continue;
+        const int mm = base + quad * 4;
+        float dv[ACC_R];
+        bool in[ACC_R];
+#pragma unroll
+        for (int e = 0; e < ACC_R; ++e) {
+          const int m = mm + e;
+          const int vg = v0 + m;
+          const float s = acc[i][j][e];
+          in[e] = ((s > sthr) | ((s == sthr) & (vg <= it))) && m < Vs;
+          const float q = in[e] ? __builtin_amdgcn_exp2f(__builtin_fmaf(s, LOG2E, nl)) : 0.f;
+          dv[e] = c * ((vg == y ? 1.f : 0.f) - q);
+        }
+        if (any_dense) {
+          const int r0 = mm - m0 - wmu * 128;  // i*16 + quad*4
+          const int pc = (nl_ >> 3) ^ (2 * quad);
+#pragma unroll
+          for (int e = 0; e < ACC_R; ++e)
+            stg[(r0 + e) * GN + pc * 8 + (nl_ & 7)] = (bf16)((dense && live && mm + e < Vs) ? dv[e] : 0.f);
+        }
+        if (sparse) {
+#pragma unroll
+          for (int e = 0; e < ACC_R; ++e) {
+            if (in[e]) {
+              const int slot = atomicAdd(rowcnt + n, 1);
+              if (slot < NSP) {
+                // rounded to bf16 like the dense rows' dz: a row's gradient
+                // does not depend on its class beyond fp32 summation order
+                list[(int64_t)n * NSP + slot] = SpEntry{v0 + mm + e, (float)(bf16)dv[e]};
+                if (cntj) atomicAdd(cntj + v0 + mm + e, 1);
+              }
+            }
+          }
+        }
+      }
+    }
+    if (any_dense) {
+      __syncthreads();
+      const int rows = min(GM, Vs_pad - m0), cols = min(GN, N_pad - n0);
+      for (int q = tid; q < GM * (GN / 8); q += GTHREADS) {
+        const int r = q / (GN / 8), cc = q % (GN / 8);
+        const bf16* src = (const bf16*)(r < 128 ? smem : smem1) + (r & 127) * GN;
+        if (r < rows && cc * 8 < cols)
+          *(u32x4*)(dT + (int64_t)(m0 + r) * ld_dT + n0 + cc * 8) =
+              *(const u32x4*)(src + ((cc ^ (2 * ((r >> 2) & 3))) * 8));
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Plain fp32 store (weight gradient slice): out[m, n] (+)= acc.
 // ---------------------------------------------------------------------------
 struct EpiStore {
@@ -475,21 +611,28 @@ struct EpiAccumT {
   int M, N;
   int first, last;
   float div = 1.f;  // the last slice writes (sum + acc) / div
+  // columns n are permuted token positions: the result of column n goes to
+  // out row rowmap[n] (the running sum keeps position n), and only columns
+  // below *n_dev exist (null: identity, N)
+  const int* rowmap = nullptr;
+  const int* n_dev = nullptr;
   static constexpr int LDS_BYTES = 0;
 
   __device__ inline void operator()(AccTile& acc, int m0, int n0, char*, char*) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
     const bool scaled = last && div != 1.f;
+    const int Nn = n_dev ? min(N, *n_dev) : N;
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) {
       const int n = n0 + acc_col(wn, j, col);
-      if (n >= N) continue;
+      if (n >= Nn) continue;
+      const int64_t orow = rowmap ? rowmap[n] : n;
 #pragma unroll
       for (int i = 0; i < ACC_I; ++i) {
         const int m = m0 + acc_row(wm, i, 0, quad);
         if (m >= M) continue;
-        const int64_t o = (int64_t)n * ld + m;
+        const int64_t o = (int64_t)n * ld + m, oo = orow * ld + m;
         f32x4 v = acc[i][j];
         if (!first) {
           const f32x4 s0 = *(const f32x4*)(sum + o);
@@ -511,9 +654,9 @@ struct EpiAccumT {
                                 ((uint32_t)__builtin_bit_cast(uint16_t, (OutT)v[1]) << 16);
             const uint32_t p1 = (uint32_t)__builtin_bit_cast(uint16_t, (OutT)v[2]) |
                                 ((uint32_t)__builtin_bit_cast(uint16_t, (OutT)v[3]) << 16);
-            *(u32x2*)(out + o) = u32x2{p0, p1};
+            *(u32x2*)(out + oo) = u32x2{p0, p1};
           } else {
-            *(f32x4*)(out + o) = v;
+            *(f32x4*)(out + oo) = v;
           }
         } else {
           *(f32x4*)(sum + o) = v;

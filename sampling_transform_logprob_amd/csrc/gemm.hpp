@@ -146,6 +146,14 @@ struct MainBf16T {
     if (kb == 0) kb = -1;
   }
 
+  // the same product over k-columns 0 .. k only (k > 0; a reduction length
+  // known on the device)
+  __device__ inline void limit_k(int k) {
+    if (ka > 0) ka = min(ka, k);
+    if (kb > 0) kb = min(kb, k);
+    K = min(K, k);
+  }
+
   // The two stages are distinct __shared__ objects (see the loop at the end
   // of run for why).  Stage 0 doubles as the epilogue's LDS (at most 64 KB),
   // so the product launches with no dynamic LDS.
@@ -374,6 +382,7 @@ struct MainF32 {
     B += dk;
     K -= (int)dk;
   }
+  __device__ inline void limit_k(int k) { K = min(K, k); }
 
   __device__ inline void run(AccTile& acc, int m0, int n0, char* smem) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -424,11 +433,26 @@ constexpr int gemm_dyn_lds() {
   return Main::DYN_LDS ? (Main::DYN_LDS > Epi::LDS_BYTES ? Main::DYN_LDS : Epi::LDS_BYTES) : 0;
 }
 
+// Extents of a product known only on the device (counts a previous kernel
+// wrote): output tiles whose first column reaches *n_lim do nothing, and the
+// reduction runs over k-columns 0 .. *k_lim (no tile does anything when it
+// is 0).  Null pointers: the launch's own extents.
+struct DynLimits {
+  const int* n_lim = nullptr;
+  const int* k_lim = nullptr;
+};
+
 template <class Main, class Epi>
-__global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(Main mainloop, Epi epi, TileMap map) {
+__global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(Main mainloop, Epi epi, TileMap map, DynLimits dyn) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   int tm, tn;
   map.get(blockIdx.x, tm, tn);
+  if (dyn.n_lim && tn * GN >= *dyn.n_lim) return;
+  if (dyn.k_lim) {
+    const int k = *dyn.k_lim;
+    if (k <= 0) return;
+    mainloop.limit_k(k);
+  }
   AccTile acc;
 #pragma unroll
   for (int i = 0; i < ACC_I; ++i)

@@ -70,7 +70,8 @@ __global__ void policy_loss_kernel(int objective, float el, float eh, float scal
 
 template <class T>
 __global__ void transpose_kernel(const T* in, int64_t ld_in, int64_t R, int64_t Cc, T* out, int64_t ld_out,
-                                 int64_t R_pad) {
+                                 int64_t R_pad, const int* skip) {
+  if (skip && *skip == 0) return;
   __shared__ T tile[64][65];
   const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 64 x 4
@@ -93,7 +94,8 @@ __global__ void transpose_kernel(const T* in, int64_t ld_in, int64_t R, int64_t 
 // ld_out and R_pad multiples of 8, 8, 8 and 64 and 16-byte aligned bases;
 // rows R .. R_pad - 1 of the output columns are zero-filled.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* in, int64_t ld_in, int64_t R, int64_t Cc,
-                                                             bf16* out, int64_t ld_out) {
+                                                             bf16* out, int64_t ld_out, const int* skip) {
+  if (skip && *skip == 0) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = ((int64_t)blockIdx.y * 4 + w) * 64;
   if (c0 >= Cc) return;
@@ -359,7 +361,8 @@ __global__ void sum_splits_kernel(const float* part, int splits, int64_t pstride
 
 // ---------------------------------------------------------------------------
 template <class Main, class Epi>
-hipError_t launch_gemm(const Main& mn, const Epi& ep, int64_t tiles_m, int64_t tiles_n, hipStream_t s) {
+hipError_t launch_gemm(const Main& mn, const Epi& ep, int64_t tiles_m, int64_t tiles_n, hipStream_t s,
+                       DynLimits dyn = {}) {
   if (tiles_m <= 0 || tiles_n <= 0) return hipSuccess;
   auto kern = gemm_kernel<Main, Epi>;
   constexpr int lds = gemm_dyn_lds<Main, Epi>();
@@ -367,7 +370,7 @@ hipError_t launch_gemm(const Main& mn, const Epi& ep, int64_t tiles_m, int64_t t
   static const hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   TileMap map{(int)tiles_m, (int)tiles_n, 4};
-  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(GTHREADS), lds, s, mn, ep, map);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(GTHREADS), lds, s, mn, ep, map, dyn);
   return hipGetLastError();
 }
 
@@ -414,15 +417,15 @@ hipError_t launch_fill_i64(int64_t* p, int64_t v, hipStream_t s) {
 }
 
 hipError_t launch_transpose_bf16(const bf16* in, int64_t ld_in, int64_t R, int64_t Cc, bf16* out,
-                                 int64_t ld_out, int64_t R_pad, hipStream_t s) {
+                                 int64_t ld_out, int64_t R_pad, hipStream_t s, const int* skip) {
   ProfScope ps(7, s);
   if (Cc % 8 == 0 && ld_in % 8 == 0 && ld_out % 8 == 0 && R_pad % 64 == 0 && (uintptr_t)in % 16 == 0 &&
       (uintptr_t)out % 16 == 0) {
     hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)(R_pad / 64), (unsigned)ceil_div(Cc, 256)), dim3(256), 0,
-                       s, in, ld_in, R, Cc, out, ld_out);
+                       s, in, ld_in, R, Cc, out, ld_out, skip);
   } else {
     hipLaunchKernelGGL(transpose_kernel<bf16>, dim3((unsigned)ceil_div(R_pad, 64), (unsigned)ceil_div(Cc, 64)),
-                       dim3(256), 0, s, in, ld_in, R, Cc, out, ld_out, R_pad);
+                       dim3(256), 0, s, in, ld_in, R, Cc, out, ld_out, R_pad, skip);
   }
   return hipGetLastError();
 }
@@ -443,7 +446,7 @@ hipError_t launch_transpose_f32(const float* in, int64_t ld_in, int64_t R, int64
                                 int64_t ld_out, int64_t R_pad, hipStream_t s) {
   ProfScope ps(7, s);
   hipLaunchKernelGGL(transpose_kernel<float>, dim3((unsigned)ceil_div(R_pad, 64), (unsigned)ceil_div(Cc, 64)),
-                     dim3(256), 0, s, in, ld_in, R, Cc, out, ld_out, R_pad);
+                     dim3(256), 0, s, in, ld_in, R, Cc, out, ld_out, R_pad, (const int*)nullptr);
   return hipGetLastError();
 }
 
@@ -578,6 +581,70 @@ hipError_t bwd_slice_bf16(const BwdSliceArgs& a, hipStream_t s) {
 hipError_t launch_bwd_slice(const BwdSliceArgs& a, hipStream_t s) {
   if (a.dtype == 1) return bwd_slice_bf16(a, s);
   return bwd_slice_impl<float, MainF32>(a, s);
+}
+
+// One slice of the classed backward (bf16).  Columns of every product are
+// permuted token positions; the products of the dense rows run over the
+// dense prefix only (its length is a device count).
+hipError_t launch_class_slice(const ClassSliceArgs& a, hipStream_t s) {
+  hipError_t e;
+  // 1. recompute the slice's keys: dense rows' dz^T, sparse rows' entries
+  {
+    EpiGrad ep{};
+    ep.perm = a.perm;
+    ep.cnt = a.cnt;
+    ep.temp = a.temp;
+    ep.target = a.target;
+    ep.st = a.st;
+    ep.g = a.g;
+    ep.dT = a.dT;
+    ep.ld_dT = a.Tp;
+    ep.v0 = (int)a.v0;
+    ep.Vs = (int)a.vs;
+    ep.Vs_pad = (int)a.vsp;
+    ep.N = (int)a.T;
+    ep.N_pad = (int)a.Tp;
+    ep.bf16_lane = a.bf16_lane;
+    ep.rowcnt = a.rowcnt;
+    ep.list = a.list;
+    ep.cntj = a.keys_out ? nullptr : a.cntj;
+    ep.keys_out = a.keys_out;
+    ep.ld_keys = a.ld_keys;
+    MainBf16 mn{a.W + a.v0 * a.H, a.H, (int)a.vs, a.h_perm, a.H, (int)a.T, (int)a.H};
+    DynLimits dyn{};
+    dyn.n_lim = a.keys_out ? nullptr : &a.cnt->active;
+    ProfScope ps(KIND_DLOGITS, s);
+    e = launch_gemm(mn, ep, ceil_div(a.vsp, GM), ceil_div(a.Tp, GN), s, dyn);
+    if (e != hipSuccess) return e;
+  }
+  if (a.keys_out) return hipSuccess;
+  // 2. dense rows' weight gradient of the slice: dW[v0 + m, :] (+)= sum over
+  //    dense positions n of dz^T[m, n] h_perm[n, :] (no tile runs without dense rows)
+  if (a.grad_weight) {
+    EpiStore ep{a.grad_weight + a.v0 * a.H, a.H, (int)a.vs, (int)a.H, a.accumulate_w};
+    MainBf16T<false, true> mn{a.dT, a.Tp, (int)a.vsp, a.h_perm, a.H, (int)a.H, (int)a.Tp, 0, (int)a.T};
+    DynLimits dyn{};
+    dyn.k_lim = &a.cnt->dense;
+    ProfScope ps(KIND_GRAD_WEIGHT, s);
+    e = launch_gemm(mn, ep, ceil_div(a.vsp, GM), ceil_div(a.H, GN), s, dyn);
+    if (e != hipSuccess) return e;
+  }
+  // 3. dense rows' hidden gradient, summed over slices in order:
+  //    dH^T[:, n] += W_slice^T . dz^T[:, n] for dense positions n, written to row perm[n]
+  if (a.grad_hidden) {
+    e = launch_transpose_bf16(a.W + a.v0 * a.H, a.H, a.vs, a.H, a.WT, a.ld_d, a.vsp, s, &a.cnt->dense);
+    if (e != hipSuccess) return e;
+    EpiAccumT<bf16> ep{a.dh_sum, a.H, (bf16*)a.grad_hidden, (int)a.H, (int)a.T, a.first, a.last, a.dh_div};
+    ep.rowmap = a.perm;
+    ep.n_dev = &a.cnt->dense;
+    MainBf16T<false, true> mn{a.WT, a.ld_d, (int)a.H, a.dT, a.Tp, (int)a.T, (int)a.vsp, 0, (int)a.vs};
+    DynLimits dyn{};
+    dyn.n_lim = &a.cnt->dense;
+    ProfScope ps(KIND_GRAD_HIDDEN, s);
+    e = launch_gemm(mn, ep, ceil_div(a.H, GM), ceil_div(a.T, GN), s, dyn);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 namespace {

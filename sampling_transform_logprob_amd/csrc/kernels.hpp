@@ -6,6 +6,13 @@
 
 namespace stce {
 
+// Launch kinds of the timing hook (the STCE_KERNEL_* values of stce.h).
+enum : int {
+  KIND_VALIDATE = 1, KIND_PROJECTION = 2, KIND_SELECT = 3, KIND_DLOGITS = 4, KIND_GRAD_WEIGHT = 5,
+  KIND_GRAD_HIDDEN = 6, KIND_TRANSPOSE = 7, KIND_PARTIALS = 8, KIND_POLICY_LOSS = 9, KIND_DZ_KEYS = 10,
+  KIND_SPLIT_SUM = 11, KIND_PRESCALE = 12, KIND_CLASSIFY = 13, KIND_SPARSE_DW = 14, KIND_SPARSE_DH = 15
+};
+
 // Launch-timing hook (no-op unless a profile is attached to this thread).
 void prof_begin(int kind, hipStream_t s);
 void prof_end(hipStream_t s);
@@ -24,8 +31,9 @@ hipError_t launch_validate(int64_t T, int64_t V, int ignore, int64_t ignore_inde
 hipError_t launch_fill_i64(int64_t* p, int64_t v, hipStream_t s);
 
 // out[c][r] = in[r][c] for r < R, c < Cc; zeros for R <= r < R_pad.
+// skip: when not null and *skip == 0 on the device, nothing is written.
 hipError_t launch_transpose_bf16(const bf16* in, int64_t ld_in, int64_t R, int64_t Cc, bf16* out,
-                                 int64_t ld_out, int64_t R_pad, hipStream_t s);
+                                 int64_t ld_out, int64_t R_pad, hipStream_t s, const int* skip = nullptr);
 hipError_t launch_transpose_f32(const float* in, int64_t ld_in, int64_t R, int64_t Cc, float* out,
                                 int64_t ld_out, int64_t R_pad, hipStream_t s);
 
@@ -90,6 +98,75 @@ struct BwdSliceArgs {
   int64_t ld_keys;
 };
 hipError_t launch_bwd_slice(const BwdSliceArgs& a, hipStream_t s);
+
+// ---- the backward with row classes (bf16 operands; sparse.hip) ----------
+// Classification: counts of the classes into *cnt, the permutation perm
+// (permuted position -> row: dense rows, then sparse, then empty, each in row
+// order) and a cleared entry counter per position.  blk: scratch of
+// grad_class_blk_ints(T) ints.
+size_t grad_class_blk_ints(int64_t T);
+hipError_t launch_grad_classes(const RowState* st, const float* g, int64_t T, int* blk, GradCounts* cnt, int* perm,
+                               int* rowcnt, hipStream_t s);
+// out[n] = in[perm[n]] for rows of H elements of the dtype (1 bf16, 2 fp32).
+hipError_t launch_gather_rows(int dtype, const void* in, const int* perm, int64_t T, int64_t H, void* out,
+                              hipStream_t s);
+hipError_t launch_fill_i32(int* p, int64_t n, int v, hipStream_t s);
+// Exclusive scan of x[0, n) into y[0, n] (y[n] = the total); sums: scratch
+// of scan_sums_ints(n) ints.
+size_t scan_sums_ints(int64_t n);
+hipError_t launch_exclusive_scan(const int* x, int64_t n, int* sums, int* y, hipStream_t s);
+
+// One vocabulary slice of the classed backward: the recompute product (dense
+// rows' dz^T, sparse rows' entries) and the dense rows' two products.
+struct ClassSliceArgs {
+  const bf16* W;        // full weight [V][H]
+  const bf16* h_perm;   // [T][H] hidden rows in permuted order
+  const int* perm;
+  const GradCounts* cnt;
+  bf16* WT;             // [H][ld_d] scratch
+  bf16* dT;             // [ld_d rows][Tp] scratch: dense rows' dz^T, columns = permuted positions
+  float* dh_sum;        // [T][H] fp32 running sum of the dense rows (permuted positions)
+  void* grad_hidden;    // [T][H] or null
+  float* grad_weight;   // [V][H] or null
+  int accumulate_w;
+  const float* temp;
+  const int64_t* target;
+  const RowState* st;
+  const float* g;
+  int* rowcnt;          // [T]
+  SpEntry* list;        // [T][NSP]
+  int* cntj;            // [V] (null without grad_weight)
+  int64_t T, Tp, H, V, v0, vs, vsp, ld_d;
+  int first, last;
+  float dh_div;
+  int bf16_lane;
+  float* keys_out;      // parity export (only the recompute runs), [T][ld_keys]
+  int64_t ld_keys;
+};
+hipError_t launch_class_slice(const ClassSliceArgs& a, hipStream_t s);
+
+// The sparse rows' products after the last slice: the weight gradient from
+// per-vocabulary-row buckets of the entries, the hidden gradient of every
+// sparse and empty position.
+struct SparseGradArgs {
+  int dtype;
+  const void* W;        // [V][H]
+  const void* h_perm;   // [T][H] permuted rows
+  const int* perm;
+  const GradCounts* cnt;
+  const int* rowcnt;
+  const SpEntry* list;
+  int* cntj;            // [V] entry counts (consumed)
+  int* offj;            // [V + 1] scratch: bucket offsets
+  int* scan_sums;       // scratch of scan_sums_ints(V)
+  SpEntry* bucket;      // [T][NSP] scratch
+  void* grad_hidden;    // [T][H] or null
+  float* grad_weight;   // [V][H] or null
+  int accumulate_w;
+  int64_t T, H, V;
+  float dh_div;
+};
+hipError_t launch_sparse_grads(const SparseGradArgs& a, hipStream_t s);
 
 // Gradients of one chunk of the fused policy step, from the chunk's stored
 // keys (no recompute product): dz token-major and vocab-major, the chunk's

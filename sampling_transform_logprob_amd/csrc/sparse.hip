@@ -1,0 +1,503 @@
+// The backward's row classes and its products over sparse dz.
+//
+// dz = c (1[j == y] - q) / T is nonzero only on a row's support, so for a
+// row bounded by top-k (or a small min-p / top-p support) the two gradient
+// products dH = dz W and dW = dz^T h are sums over a handful of vocabulary
+// rows.  Rows whose support holds at most NSP tokens take these sums
+// directly; the others go through the matrix-core products (kernels.hip).
+//
+//   1. classification: every row is dense, sparse or empty (no gradient);
+//      the rows are placed dense first, then sparse, then empty, each class
+//      in row order (a block count, one scan, a placement pass), and the
+//      hidden states are gathered into that order;
+//   2. the recompute product (EpiGrad) writes the dense rows' dz and appends
+//      each sparse row's nonzero dz to its entry list, counting the entries
+//      of every vocabulary row;
+//   3. weight gradient: an exclusive scan of the per-vocabulary-row counts,
+//      a pass that files each entry into its vocabulary row's bucket, and one
+//      workgroup per vocabulary row that sums its bucket's dz h[t] terms in
+//      increasing token position (a fixed order), onto the dense product's
+//      result or the caller's dW when there is one, else onto zero;
+//   4. hidden gradient: one workgroup per sparse row that sums its entries'
+//      dz W[j] terms in increasing vocabulary order; empty rows get zeros.
+//
+// Every order of summation is fixed (entries are ordered by their index
+// before they are summed), so the results are deterministic although the
+// entry lists are filled with atomics.
+#include "kernels.hpp"
+
+namespace stce {
+namespace {
+
+constexpr int CB = 1024;  // rows per classification block (256 threads x 4)
+
+__device__ inline int grad_class(const RowState& rs, float g) {
+  if ((rs.flags & (ROW_VALID | ROW_IN_SUPPORT)) != (ROW_VALID | ROW_IN_SUPPORT) || g == 0.f) return GRAD_EMPTY;
+  if (!(rs.flags & ROW_FILTERED) || rs.n > NSP) return GRAD_DENSE;
+  return GRAD_SPARSE;
+}
+
+// Inclusive scan over the 256 threads of a workgroup (4 waves): wave scans
+// by shuffles, then the wave totals through LDS.  All threads must call it.
+__device__ inline int block_incl_scan(int v, int* scratch) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  __syncthreads();
+  if (lane == 63) scratch[w] = v;
+  __syncthreads();
+  int off = 0;
+  for (int i = 0; i < w; ++i) off += scratch[i];
+  return v + off;
+}
+
+// Per block of CB rows: how many rows of each class.
+__global__ __launch_bounds__(256) void class_count_kernel(const RowState* st, const float* g, int64_t T,
+                                                          int* blk) {
+  __shared__ int scr[4];
+  const int64_t r0 = (int64_t)blockIdx.x * CB + threadIdx.x * 4;
+  int c[3] = {0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (r0 + i < T) ++c[grad_class(st[r0 + i], g[r0 + i])];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int s = block_incl_scan(c[k], scr);
+    if (threadIdx.x == 255) blk[blockIdx.x * 3 + k] = s;
+  }
+}
+
+// One workgroup: exclusive scan of the block counts (in place, per class)
+// and the class totals.
+__global__ __launch_bounds__(1024) void class_scan_kernel(int* blk, int nblk, GradCounts* cnt) {
+  __shared__ int part[1024 * 3];
+  __shared__ int tot[3];
+  const int t = threadIdx.x;
+  // thread t scans blocks [t * per, (t + 1) * per)
+  const int per = (nblk + 1023) / 1024;
+  int s[3] = {0, 0, 0};
+  for (int b = t * per; b < min(nblk, (t + 1) * per); ++b)
+#pragma unroll
+    for (int k = 0; k < 3; ++k) s[k] += blk[b * 3 + k];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) part[t * 3 + k] = s[k];
+  __syncthreads();
+  if (t < 3) {
+    int run = 0;
+    for (int i = 0; i < 1024; ++i) {
+      const int x = part[i * 3 + t];
+      part[i * 3 + t] = run;
+      run += x;
+    }
+    tot[t] = run;
+  }
+  __syncthreads();
+  int run[3] = {part[t * 3], part[t * 3 + 1], part[t * 3 + 2]};
+  for (int b = t * per; b < min(nblk, (t + 1) * per); ++b)
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int x = blk[b * 3 + k];
+      blk[b * 3 + k] = run[k];
+      run[k] += x;
+    }
+  if (t == 0) {
+    GradCounts c;
+    c.dense = tot[0];
+    c.sparse = tot[1];
+    c.active = tot[0] + tot[1];
+    c.pad = 0;
+    *cnt = c;
+  }
+}
+
+// Places every row at its permuted position (dense, then sparse, then empty;
+// row order within a class) and clears the position's entry counter.
+__global__ __launch_bounds__(256) void class_place_kernel(const RowState* st, const float* g, int64_t T,
+                                                          const int* blk, const GradCounts* cnt, int* perm,
+                                                          int* rowcnt) {
+  __shared__ int scr[4];
+  const int64_t r0 = (int64_t)blockIdx.x * CB + threadIdx.x * 4;
+  int cls[4];
+  int c[3] = {0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    cls[i] = r0 + i < T ? grad_class(st[r0 + i], g[r0 + i]) : -1;
+    if (cls[i] >= 0) ++c[cls[i]];
+  }
+  const GradCounts n = *cnt;
+  const int cls_base[3] = {0, n.dense, n.active};
+  int pos[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) pos[k] = cls_base[k] + blk[blockIdx.x * 3 + k] + block_incl_scan(c[k], scr) - c[k];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (cls[i] >= 0) {
+      const int p = pos[cls[i]]++;
+      perm[p] = (int)(r0 + i);
+      rowcnt[p] = 0;
+    }
+}
+
+// out[n] = in[perm[n]], rows of H elements (H a multiple of 8, 16-byte rows).
+template <class E>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const E* in, const int* perm, int64_t T, int64_t H,
+                                                          E* out) {
+  constexpr int EPV = 16 / (int)sizeof(E);
+  const int64_t per_row = H / EPV;
+  const int64_t total = T * per_row;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
+    const int64_t n = i / per_row, c = i - n * per_row;
+    ((u32x4*)(out + n * H))[c] = ((const u32x4*)(in + (int64_t)perm[n] * H))[c];
+  }
+}
+
+__global__ void fill_i32_kernel(int* p, int64_t n, int v) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
+}
+
+// Exclusive scan of x[0, n) into y[0, n] (y[n] = total) in three launches:
+// per-block sums (SB elements a block), one workgroup scanning them, and a
+// pass that scans each block from its base.
+constexpr int SB = 4096;
+
+__global__ __launch_bounds__(256) void scan_sums_kernel(const int* x, int64_t n, int* sums) {
+  __shared__ int scr[4];
+  const int64_t b0 = (int64_t)blockIdx.x * SB + threadIdx.x * 16;
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (b0 + i < n) s += x[b0 + i];
+  s = block_incl_scan(s, scr);
+  if (threadIdx.x == 255) sums[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(1024) void scan_top_kernel(int* sums, int nb, int* total) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int per = (nb + 1023) / 1024;
+  int s = 0;
+  for (int b = t * per; b < min(nb, (t + 1) * per); ++b) s += sums[b];
+  part[t] = s;
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int i = 0; i < 1024; ++i) {
+      const int v = part[i];
+      part[i] = run;
+      run += v;
+    }
+    *total = run;
+  }
+  __syncthreads();
+  int run = part[t];
+  for (int b = t * per; b < min(nb, (t + 1) * per); ++b) {
+    const int v = sums[b];
+    sums[b] = run;
+    run += v;
+  }
+}
+
+__global__ __launch_bounds__(256) void scan_apply_kernel(const int* x, int64_t n, const int* sums, int* y) {
+  __shared__ int scr[4];
+  const int64_t b0 = (int64_t)blockIdx.x * SB + threadIdx.x * 16;
+  int v[16];
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = b0 + i < n ? x[b0 + i] : 0;
+    s += v[i];
+  }
+  int run = sums[blockIdx.x] + block_incl_scan(s, scr) - s;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (b0 + i < n) {
+      y[b0 + i] = run;
+      run += v[i];
+    }
+}
+
+// Files the entries of the sparse positions into their vocabulary rows'
+// buckets: bucket[off[j] + slot] = (position, dz), the slot taken by counting
+// cntj[j] back down to zero (the order inside a bucket is arbitrary here and
+// fixed by the summing kernel).  One wave per position.
+__global__ __launch_bounds__(256) void bucket_fill_kernel(const GradCounts* cnt, int64_t T, const int* rowcnt,
+                                                          const SpEntry* list, const int* off, int* cntj,
+                                                          SpEntry* bucket) {
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const GradCounts c = *cnt;
+  if (n < c.dense || n >= c.active || n >= T) return;
+  const int ne = min(rowcnt[n], NSP);
+  for (int i = lane; i < ne; i += 64) {
+    const SpEntry e = list[n * NSP + i];
+    const int slot = atomicSub(cntj + e.idx, 1) - 1;
+    bucket[off[e.idx] + slot] = SpEntry{(int32_t)n, e.v};
+  }
+}
+
+// Orders the ne entries of src (distinct indices) by increasing index into
+// dst, both in LDS: entry i goes to the number of entries with a smaller
+// index.  256 threads; the caller synchronizes before and after.
+__device__ inline void rank_order(const SpEntry* src, int ne, SpEntry* dst) {
+  for (int i = threadIdx.x; i < ne; i += 256) {
+    const SpEntry e = src[i];
+    int r = 0;
+    for (int k = 0; k < ne; ++k) r += src[k].idx < e.idx ? 1 : 0;
+    dst[r] = e;
+  }
+}
+
+template <class E>
+__device__ inline void load8(const E* p, float (&x)[8]) {
+  if constexpr (sizeof(E) == 2) {
+    const bf16x8 v = *(const bf16x8*)p;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = (float)v[k];
+  } else {
+    const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[k] = a[k];
+      x[4 + k] = b[k];
+    }
+  }
+}
+
+// acc[k] += e.v * X[e.idx, c0 + k] over the ordered entries e = ord[0 .. ne),
+// in that order, fp32 fmas; the rows of eight entries are loaded before their
+// fmas so that the loads overlap (the order of the sums is unchanged).
+template <class E>
+__device__ inline void ordered_sum(const SpEntry* ord, int ne, const E* X, int64_t H, int64_t c0, float (&acc)[8]) {
+  int r = 0;
+  for (; r + 8 <= ne; r += 8) {
+    float x[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) load8(X + (int64_t)ord[r + u].idx * H + c0, x[u]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float v = ord[r + u].v;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(v, x[u][k], acc[k]);
+    }
+  }
+  for (; r < ne; ++r) {
+    float x[8];
+    load8(X + (int64_t)ord[r].idx * H + c0, x);
+    const float v = ord[r].v;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(v, x[k], acc[k]);
+  }
+}
+
+constexpr int ORDER_CAP = 1024;   // entries a weight-gradient bucket orders in LDS
+constexpr int WIN = 4096;         // token positions per window beyond that
+
+// Weight gradient rows from the buckets: one workgroup per vocabulary row j,
+//   dW[j, :] = base + sum over the bucket's entries, in increasing token
+//              position n, of dz * h_perm[n, :]  (fp32),
+// base = dW[j, :] when the dense product wrote it or the caller accumulates,
+// else 0.  Rows with an empty bucket are left alone, or zeroed when nothing
+// else writes them.  Buckets larger than ORDER_CAP entries are summed window
+// by window of WIN positions, each entry placed at its position in LDS.
+template <class E>
+__global__ __launch_bounds__(256) void sparse_dw_kernel(const int* off, const SpEntry* bucket, const E* h, int64_t H,
+                                                        const GradCounts* cnt, int accumulate, float* dW,
+                                                        int64_t T) {
+  __shared__ SpEntry ord[ORDER_CAP];
+  __shared__ SpEntry raw[ORDER_CAP];
+  __shared__ float win[WIN];
+  const int64_t j = blockIdx.x;
+  const int o0 = off[j], ne = off[j + 1] - o0;
+  const bool from_mem = accumulate || cnt->dense > 0;
+  float* row = dW + j * H;
+  if (ne == 0) {
+    if (!from_mem)
+      for (int64_t c = threadIdx.x * 4; c < H; c += 256 * 4) *(f32x4*)(row + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  if (ne <= ORDER_CAP) {
+    for (int i = threadIdx.x; i < ne; i += 256) raw[i] = bucket[o0 + i];
+    __syncthreads();
+    rank_order(raw, ne, ord);
+    __syncthreads();
+    for (int64_t c0 = threadIdx.x * 8; c0 < H; c0 += 256 * 8) {
+      float acc[8];
+      if (from_mem) {
+        const f32x4 a = *(const f32x4*)(row + c0), b = *(const f32x4*)(row + c0 + 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[k] = a[k];
+          acc[4 + k] = b[k];
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+      }
+      ordered_sum(ord, ne, h, H, c0, acc);
+      *(f32x4*)(row + c0) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      *(f32x4*)(row + c0 + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    }
+    return;
+  }
+  // a large bucket (a token in many rows' supports): windows of positions
+  for (int64_t c0 = threadIdx.x * 8; c0 - threadIdx.x * 8 < H; c0 += 256 * 8) {
+    const bool mine = c0 < H;
+    float acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+    if (mine && from_mem) {
+      const f32x4 a = *(const f32x4*)(row + c0), b = *(const f32x4*)(row + c0 + 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[k] = a[k];
+        acc[4 + k] = b[k];
+      }
+    }
+    for (int64_t w0 = 0; w0 < T; w0 += WIN) {
+      __syncthreads();
+      for (int i = threadIdx.x; i < WIN; i += 256) win[i] = 0.f;
+      __syncthreads();
+      for (int i = threadIdx.x; i < ne; i += 256) {
+        const SpEntry e = bucket[o0 + i];
+        if (e.idx >= w0 && e.idx < w0 + WIN) win[e.idx - w0] = e.v;
+      }
+      __syncthreads();
+      if (mine) {
+        const int lim = (int)min((int64_t)WIN, T - w0);
+        for (int r = 0; r < lim; ++r) {
+          const float v = win[r];
+          if (v == 0.f) continue;  // no entry (a zero entry adds nothing)
+          float x[8];
+          load8(h + (w0 + r) * H + c0, x);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(v, x[k], acc[k]);
+        }
+      }
+    }
+    if (mine) {
+      *(f32x4*)(row + c0) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      *(f32x4*)(row + c0 + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    }
+  }
+}
+
+// Hidden gradient rows of the sparse and empty positions: one workgroup per
+// permuted position n >= dense (row t = perm[n]):
+//   dH[t, :] = (sum over the entries, in increasing vocabulary row j, of
+//              dz * W[j, :]) / div   in the hidden dtype; zeros for empty rows.
+template <class E>
+__global__ __launch_bounds__(256) void sparse_dh_kernel(const int* perm, const GradCounts* cnt, const int* rowcnt,
+                                                        const SpEntry* list, const E* W, int64_t H, float div,
+                                                        E* dH, int64_t T) {
+  __shared__ SpEntry raw[NSP];
+  __shared__ SpEntry ord[NSP];
+  const int64_t n = blockIdx.x;
+  const GradCounts c = *cnt;
+  if (n < c.dense || n >= T) return;
+  const int64_t t = perm[n];
+  E* out = dH + t * H;
+  const int ne = n < c.active ? min(rowcnt[n], NSP) : 0;
+  for (int i = threadIdx.x; i < ne; i += 256) raw[i] = list[n * NSP + i];
+  __syncthreads();
+  rank_order(raw, ne, ord);
+  __syncthreads();
+  for (int64_t c0 = threadIdx.x * 8; c0 < H; c0 += 256 * 8) {
+    float acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+    ordered_sum(ord, ne, W, H, c0, acc);
+    if (div != 1.f)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = acc[k] / div;
+    if constexpr (sizeof(E) == 2) {
+      bf16x8 o;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = (bf16)acc[k];
+      *(bf16x8*)(out + c0) = o;
+    } else {
+      *(f32x4*)(out + c0) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      *(f32x4*)(out + c0 + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_grad_classes(const RowState* st, const float* g, int64_t T, int* blk, GradCounts* cnt, int* perm,
+                               int* rowcnt, hipStream_t s) {
+  ProfScope ps(KIND_CLASSIFY, s);
+  const unsigned nb = (unsigned)ceil_div(T, CB);
+  hipLaunchKernelGGL(class_count_kernel, dim3(nb), dim3(256), 0, s, st, g, T, blk);
+  hipLaunchKernelGGL(class_scan_kernel, dim3(1), dim3(1024), 0, s, blk, (int)nb, cnt);
+  hipLaunchKernelGGL(class_place_kernel, dim3(nb), dim3(256), 0, s, st, g, T, blk, cnt, perm, rowcnt);
+  return hipGetLastError();
+}
+
+size_t grad_class_blk_ints(int64_t T) { return 3 * (size_t)ceil_div(T, CB); }
+
+hipError_t launch_gather_rows(int dtype, const void* in, const int* perm, int64_t T, int64_t H, void* out,
+                              hipStream_t s) {
+  const int64_t total = T * H / (dtype == 1 ? 8 : 4);
+  const unsigned blocks = (unsigned)(ceil_div(total, 256) < 8192 ? ceil_div(total, 256) : 8192);
+  if (dtype == 1)
+    hipLaunchKernelGGL(gather_rows_kernel<bf16>, dim3(blocks), dim3(256), 0, s, (const bf16*)in, perm, T, H,
+                       (bf16*)out);
+  else
+    hipLaunchKernelGGL(gather_rows_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)in, perm, T, H,
+                       (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int* p, int64_t n, int v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)(ceil_div(n, 256) < 4096 ? ceil_div(n, 256) : 4096);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(blocks), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+size_t scan_sums_ints(int64_t n) { return (size_t)ceil_div(n, SB) + 1; }
+
+hipError_t launch_exclusive_scan(const int* x, int64_t n, int* sums, int* y, hipStream_t s) {
+  const unsigned nb = (unsigned)ceil_div(n, SB);
+  hipLaunchKernelGGL(scan_sums_kernel, dim3(nb), dim3(256), 0, s, x, n, sums);
+  hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(1024), 0, s, sums, (int)nb, y + n);
+  hipLaunchKernelGGL(scan_apply_kernel, dim3(nb), dim3(256), 0, s, x, n, sums, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_grads(const SparseGradArgs& a, hipStream_t s) {
+  hipError_t e;
+  if (a.grad_weight) {
+    {
+      ProfScope ps(KIND_SPARSE_DW, s);
+      if ((e = launch_exclusive_scan(a.cntj, a.V, a.scan_sums, a.offj, s))) return e;
+      hipLaunchKernelGGL(bucket_fill_kernel, dim3((unsigned)ceil_div(a.T, 4)), dim3(256), 0, s, a.cnt, a.T, a.rowcnt,
+                         a.list, a.offj, a.cntj, a.bucket);
+      if (a.dtype == 1)
+        hipLaunchKernelGGL(sparse_dw_kernel<bf16>, dim3((unsigned)a.V), dim3(256), 0, s, a.offj, a.bucket,
+                           (const bf16*)a.h_perm, a.H, a.cnt, a.accumulate_w, a.grad_weight, a.T);
+      else
+        hipLaunchKernelGGL(sparse_dw_kernel<float>, dim3((unsigned)a.V), dim3(256), 0, s, a.offj, a.bucket,
+                           (const float*)a.h_perm, a.H, a.cnt, a.accumulate_w, a.grad_weight, a.T);
+    }
+    if ((e = hipGetLastError())) return e;
+  }
+  if (a.grad_hidden) {
+    ProfScope ps(KIND_SPARSE_DH, s);
+    if (a.dtype == 1)
+      hipLaunchKernelGGL(sparse_dh_kernel<bf16>, dim3((unsigned)a.T), dim3(256), 0, s, a.perm, a.cnt, a.rowcnt,
+                         a.list, (const bf16*)a.W, a.H, a.dh_div, (bf16*)a.grad_hidden, a.T);
+    else
+      hipLaunchKernelGGL(sparse_dh_kernel<float>, dim3((unsigned)a.T), dim3(256), 0, s, a.perm, a.cnt, a.rowcnt,
+                         a.list, (const float*)a.W, a.H, a.dh_div, (float*)a.grad_hidden, a.T);
+    if ((e = hipGetLastError())) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace stce

@@ -1,0 +1,128 @@
+"""The backward's row classes: rows whose support holds at most NSP = 128
+tokens take the sparse products (their dz entries summed one by one), larger
+supports the matrix-core products, rows with no gradient neither.  Every
+mix is held to the oracle (gradients within 1e-2 relative Frobenius error)
+and to run-to-run bitwise equality."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import GRAD_RTOL, dev, meta_of, rel_fro, say, targets, to_gpu
+from sampling_transform_logprob_amd import binding, workloads
+from sampling_transform_logprob_amd.workloads import round_bf16
+
+pytestmark = pytest.mark.gpu
+
+NSP = 128
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    binding.load()
+
+
+def _oracle_grads(w, y, g, keys):
+    ref = oracle.forward(w["h"], w["W"], y, w["temperature"], w["top_k"], w["top_p"], w["min_p"], keys=keys)
+    return ref, oracle.backward(w["h"], w["W"], y, ref, g, w["temperature"])
+
+
+def test_mixed_classes_and_the_class_boundary():
+    """One batch with every class: top-k NSP and NSP + 1 (the two sides of
+    the class boundary), top-p over most of the row (dense), top-k 20
+    (sparse), unfiltered rows (dense), targets out of support and a zero
+    upstream gradient (empty); several vocabulary slices."""
+    T, V = 240, 12000
+    w = workloads.make("headline", T=T)
+    w["W"] = w["W"][:V]
+    w["V"] = V
+    kind = np.arange(T) % 6
+    w["top_k"] = np.select([kind == 0, kind == 1, kind == 2, kind == 3], [NSP, NSP + 1, 20, 0], 0).astype(np.int32)
+    w["top_p"] = np.where(kind == 4, 0.95, 1.0).astype(np.float32)
+    w["min_p"] = np.zeros(T, np.float32)
+    y = targets(w)
+    y[kind == 5] = w["target_uniform"][kind == 5] % V                 # unfiltered rows
+    G0 = to_gpu(w, y)
+    keys = binding.scaled_logits(G0["h"], G0["W"], G0["temperature"]).cpu().numpy()
+    out = np.nonzero(kind == 2)[0][::3]                                # some top-20 rows: target out of support
+    for r in out:
+        y[r] = int(oracle.order_row(keys[r])[-1])
+    g = np.random.Generator(np.random.PCG64(5)).standard_normal(T)
+    g[7::17] = 0.0                                                     # zero upstream gradient
+    G = to_gpu(w, y)
+    say(f"classes: T={T} V={V}")
+    lp, st = binding.forward(G["h"], G["W"], G["target"], **meta_of(G))
+    gg = torch.from_numpy(g.astype(np.float32)).to(dev())
+    gh, gw = binding.backward(G["h"], G["W"], G["target"], st, gg, **meta_of(G), vocab_slice=4096)
+    gh2, gw2 = binding.backward(G["h"], G["W"], G["target"], st, gg, **meta_of(G), vocab_slice=4096)
+    torch.cuda.synchronize()
+    assert torch.equal(gh, gh2) and torch.equal(gw, gw2)
+    info = binding.decode_state(st)
+    n = info["n"]
+    assert (n[kind == 0] == NSP).all() and (n[kind == 1] == NSP + 1).all()
+    ref, (dH, dW) = _oracle_grads(w, y, g, keys)
+    assert np.array_equal(n, ref["n"])
+    rh, rw = rel_fro(gh.float().cpu().numpy(), dH), rel_fro(gw.cpu().numpy(), dW)
+    say(f"  dH rel {rh:.2e} dW rel {rw:.2e}; out-of-support rows {int((~ref['in_support']).sum())}")
+    assert rh < GRAD_RTOL and rw < GRAD_RTOL
+    ghc = gh.float().cpu().numpy()
+    assert not ghc[~ref["in_support"]].any() and not ghc[g == 0].any()
+
+
+def test_accumulate_and_single_outputs():
+    """Sparse rows only (top-k 20): the weight gradient added onto the
+    caller's array, and each gradient requested alone."""
+    T, V = 200, 9000
+    w = workloads.make("headline", T=T)
+    w["W"] = w["W"][:V]
+    w["V"] = V
+    y = targets(w)
+    G = to_gpu(w, y)
+    lp, st = binding.forward(G["h"], G["W"], G["target"], **meta_of(G))
+    g = torch.full((T,), -1.0 / T, device=dev())
+    gh, gw = binding.backward(G["h"], G["W"], G["target"], st, g, **meta_of(G))
+    base = torch.randn(V, w["H"], device=dev())
+    _, acc = binding.backward(G["h"], G["W"], G["target"], st, g, **meta_of(G), need_hidden=False,
+                              grad_weight=base.clone(), accumulate_grad_weight=True)
+    gh_only, none_w = binding.backward(G["h"], G["W"], G["target"], st, g, **meta_of(G), need_weight=False)
+    none_h, gw_only = binding.backward(G["h"], G["W"], G["target"], st, g, **meta_of(G), need_hidden=False)
+    torch.cuda.synchronize()
+    assert none_w is None and none_h is None
+    assert torch.equal(gh_only, gh) and torch.equal(gw_only, gw)
+    assert torch.allclose(acc, base + gw, rtol=0, atol=1e-6)
+    rows_hit = (gw != 0).any(1)
+    assert torch.equal(acc[~rows_hit], base[~rows_hit])            # untouched rows keep the caller's values
+    say(f"  accumulate: {int(rows_hit.sum())} vocabulary rows receive sparse terms")
+
+
+def test_a_token_in_every_support_takes_the_windowed_bucket():
+    """One vocabulary row dominates every logit row, so it lies in all 5000
+    supports: its weight-gradient bucket (5000 entries) exceeds the 1024 the
+    kernel orders in LDS and is summed window by window of positions."""
+    rng = np.random.Generator(np.random.PCG64(8))
+    T, H, V = 5000, 64, 3000
+    h = round_bf16(rng.standard_normal((T, H)).astype(np.float32) + 2.0)
+    W = round_bf16((rng.standard_normal((V, H)) * 0.05).astype(np.float32))
+    W[17] = round_bf16(np.full(H, 0.05, np.float32))                 # h . W[17] ~ 6.4: in every top-8
+    w = dict(h=h, W=W, temperature=np.full(T, 0.9, np.float32), top_k=np.full(T, 8, np.int32),
+             top_p=np.ones(T, np.float32), min_p=np.zeros(T, np.float32), dtype="bf16", u=rng.random(T),
+             filtered=True, V=V)
+    y = targets(w)
+    g = rng.standard_normal(T)
+    G = to_gpu(w, y)
+    lp, st = binding.forward(G["h"], G["W"], G["target"], **meta_of(G))
+    gg = torch.from_numpy(g.astype(np.float32)).to(dev())
+    gh, gw = binding.backward(G["h"], G["W"], G["target"], st, gg, **meta_of(G))
+    gh2, gw2 = binding.backward(G["h"], G["W"], G["target"], st, gg, **meta_of(G))
+    keys = binding.scaled_logits(G["h"], G["W"], G["temperature"]).cpu().numpy()
+    torch.cuda.synchronize()
+    assert torch.equal(gw, gw2) and torch.equal(gh, gh2)
+    assert (keys.argmax(1) == 17).all()                              # so token 17 is in every support
+    ref, (dH, dW) = _oracle_grads(w, y, g, keys)
+    rh, rw = rel_fro(gh.float().cpu().numpy(), dH), rel_fro(gw.cpu().numpy(), dW)
+    say(f"windowed bucket: T={T} dH rel {rh:.2e} dW rel {rw:.2e} (row 17 rel "
+        f"{rel_fro(gw[17].cpu().numpy(), dW[17]):.2e})")
+    assert rh < GRAD_RTOL and rw < GRAD_RTOL
+    assert rel_fro(gw[17].cpu().numpy(), dW[17]) < 1e-4
