@@ -125,4 +125,4 @@ def test_a_token_in_every_support_takes_the_windowed_bucket():
     say(f"windowed bucket: T={T} dH rel {rh:.2e} dW rel {rw:.2e} (row 17 rel "
         f"{rel_fro(gw[17].cpu().numpy(), dW[17]):.2e})")
     assert rh < GRAD_RTOL and rw < GRAD_RTOL
-    assert rel_fro(gw[17].cpu().numpy(), dW[17]) < 1e-4
+    assert rel_fro(gw[17].cpu().numpy(), dW[17]) < GRAD_RTOL     # the windowed row itself (dz is bf16)
