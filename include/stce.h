@@ -186,6 +186,25 @@ stce_status stce_schedule(const stce_problem *prob, int64_t *chunk_rows, int64_t
 stce_status stce_forward(const stce_problem *prob, float *logprob, void *state,
                          int64_t *dev_status, void *ws, size_t ws_bytes, void *stream);
 
+/* Forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and results as stce_forward, bit for bit, with its
+ * workspace in a static device array of the library (stce_noalloc_scratch_bytes()
+ * = 64 MiB, one copy per device, held until the process ends) instead of a
+ * caller workspace.  It calls no hipMalloc, hipFree or allocating routine
+ * and creates no stream or event: one chunk buffer, every chunk's selection
+ * on `stream` after its projection.  The chunk is prob->chunk_rows when that
+ * workspace fits the array, else the largest that fits (the chunking changes
+ * no bit of the result); a problem whose forward needs more than the array
+ * with one row per chunk is rejected with STCE_E_WORKSPACE (its vocabulary
+ * is then beyond ~12 million tokens).  Every call on a device shares that
+ * device's array, which keeps the last call's contents (the forward writes
+ * every byte it reads): calls that overlap on one device, on different
+ * streams or threads, race and must be ordered by the caller. */
+size_t stce_noalloc_scratch_bytes(void);
+stce_status stce_forward_noalloc(const stce_problem *prob, float *logprob, void *state, int64_t *dev_status,
+                                 void *stream);
+
 /* Forward with side outputs of the same sweep (align "architecture v2:
  * proposal", section 5.4 A: the entropy comes from the forward's sweep, no
  * extra product).  Each pointer of `side` is a device array [T] fp32, or

@@ -30,7 +30,7 @@ SYMBOLS = (
     "stce_scaled_logits", "stce_support_from_logits", "stce_support_workspace_bytes",
     "stce_decode_state", "stce_status_string", "stce_last_error", "stce_profile_attach", "stce_schedule",
     "stce_policy_loss", "stce_forward_with_side", "stce_fused_workspace_bytes", "stce_fused_policy_step",
-    "stce_recompute_keys",
+    "stce_recompute_keys", "stce_forward_noalloc", "stce_noalloc_scratch_bytes",
 )
 KERNEL_KINDS = {1: "validate", 2: "projection", 3: "select", 4: "dlogits", 5: "grad_weight",
                 6: "grad_hidden", 7: "transpose", 8: "partials", 9: "policy_loss", 10: "dz_keys",
@@ -99,6 +99,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "stce_forward": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
         "stce_backward": (ctypes.c_int, [P, vp, vp, vp, vp, i32, vp, vp, sz, vp]),
         "stce_recompute_keys": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
+        "stce_forward_noalloc": (ctypes.c_int, [P, vp, vp, vp, vp]),
+        "stce_noalloc_scratch_bytes": (sz, []),
         "stce_scaled_logits": (ctypes.c_int, [P, i64, i64, vp, vp, sz, vp]),
         "stce_support_from_logits": (ctypes.c_int, [vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "stce_support_workspace_bytes": (sz, [i64, i64]),
@@ -251,6 +253,25 @@ def forward(hidden, weight, target, temperature=None, top_k=None, top_p=None, mi
         _raise_rows(status, "stce_forward", dict(temperature=keep[3], top_k=keep[4], top_p=keep[5],
                                                  min_p=keep[6], target=keep[2]))
     return (logprob, state, outs) if side else (logprob, state)
+
+
+def forward_noalloc(hidden, weight, target, temperature=None, top_k=None, top_p=None, min_p=None, *,
+                    chunk_rows: int = 0, check: bool = True, ignore_index: Optional[int] = None,
+                    pre_gemm_temperature: Optional[float] = None, lane: str = "fp32"):
+    """``forward`` through ``stce_forward_noalloc``: the library's static
+    scratch instead of a workspace (the outputs are still allocated here)."""
+    prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, chunk_rows,
+                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane)
+    T = prob.T
+    dev = hidden.device
+    logprob = torch.empty(T, dtype=torch.float32, device=dev)
+    state = torch.empty(T * STATE_BYTES_PER_ROW, dtype=torch.uint8, device=dev)
+    status = torch.empty(1, dtype=torch.int64, device=dev)
+    _check(load().stce_forward_noalloc(ctypes.byref(prob), _ptr(logprob), _ptr(state), _ptr(status), _stream()))
+    if check:
+        _raise_rows(status, "stce_forward_noalloc", dict(temperature=keep[3], top_k=keep[4], top_p=keep[5],
+                                                         min_p=keep[6], target=keep[2]))
+    return logprob, state
 
 
 def backward(hidden, weight, target, state, grad_logprob, temperature=None, top_k=None, top_p=None,

@@ -5,12 +5,20 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <unordered_map>
 
 #include "../../include/stce.h"
 #include "kernels.hpp"
 
 using namespace stce;
+
+// Scratch of stce_forward_noalloc: the workspace of its forward, one copy per
+// device (each device that runs the library holds it until the process
+// ends).  Host code never names it directly: the device address comes from
+// hipGetSymbolAddress (noalloc_scratch below).
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -93,7 +101,7 @@ stce_status check_shapes(const stce_problem* p) {
   return STCE_OK;
 }
 
-Layout plan(const stce_problem* p) {
+Layout plan(const stce_problem* p, bool single_buffer = false) {
   Layout L{};
   const int64_t T = p->T, V = p->V, H = p->H;
   const size_t es = elt_size(p->dtype);
@@ -104,7 +112,7 @@ Layout plan(const stce_problem* p) {
   // two chunk buffers when there is more than one chunk: the selection of
   // chunk c (side stream) reads one while the projection of chunk c + 1
   // writes the other
-  L.nbuf = T > L.C ? 2 : 1;
+  L.nbuf = (T > L.C && !single_buffer) ? 2 : 1;
   L.buf_tile = align_up(4 * (size_t)L.C * L.ldt);
   L.buf_part = align_up(sizeof(TilePart) * (size_t)L.C * L.ntv);
   L.buf_sy = align_up(4 * (size_t)L.C);
@@ -357,9 +365,15 @@ stce_status stce_forward(const stce_problem* p, float* logprob, void* state, int
   return stce_forward_with_side(p, logprob, state, nullptr, dev_status, ws, ws_bytes, stream);
 }
 
-stce_status stce_forward_with_side(const stce_problem* p, float* logprob, void* state,
-                                   const stce_side_outputs* side_out, int64_t* dev_status, void* ws,
-                                   size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward; single_stream: one chunk buffer, every chunk's selection on
+// the caller's stream after its projection (no side stream, so nothing is
+// created on the first call).
+stce_status forward_impl(const stce_problem* p, float* logprob, void* state, const stce_side_outputs* side_out,
+                         int64_t* dev_status, void* ws, size_t ws_bytes, void* stream, bool single_stream) {
   stce_status s = check_shapes(p);
   if (s) return s;
   if ((s = check_inputs(p))) return s;
@@ -370,7 +384,7 @@ stce_status stce_forward_with_side(const stce_problem* p, float* logprob, void* 
   if ((so_lse && !aligned(so_lse, 4)) || (so_hf && !aligned(so_hf, 4)) || (so_hs && !aligned(so_hs, 4)))
     return fail(STCE_E_ARG, "side outputs must be 4-byte aligned");
   const int want_ent = (so_hf || so_hs) ? 1 : 0;
-  const Layout L = plan(p);
+  const Layout L = plan(p, single_stream);
   if ((s = check_ws(ws, ws_bytes, L.fwd))) return s;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e;
@@ -443,6 +457,78 @@ stce_status stce_forward_with_side(const stce_problem* p, float* logprob, void* 
   // runs them in order)
   if (side && (e = hipStreamWaitEvent(st, side->done(nch - 1), 0))) return hip_fail(e, "join");
   return STCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+stce_status stce_forward_with_side(const stce_problem* p, float* logprob, void* state,
+                                   const stce_side_outputs* side_out, int64_t* dev_status, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  return forward_impl(p, logprob, state, side_out, dev_status, ws, ws_bytes, stream, false);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device address of this device's copy of `scratch`, looked up once per
+// device with that device current and kept.
+std::mutex g_noalloc_mu;
+std::unordered_map<int, void*> g_noalloc_ptr;
+
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  auto it = g_noalloc_ptr.find(dev);
+  if (it == g_noalloc_ptr.end()) {
+    void* ptr = nullptr;
+    if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    it = g_noalloc_ptr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t stce_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+stce_status stce_forward_noalloc(const stce_problem* p, float* logprob, void* state, int64_t* dev_status,
+                                 void* stream) {
+  stce_status s = check_shapes(p);
+  if (s) return s;
+  // the problem's chunk when its workspace fits the scratch, else the largest
+  // chunk that does (single buffer, selection on the caller's stream)
+  stce_problem q = *p;
+  if (plan(&q, true).fwd > kNoallocScratchBytes) {
+    int64_t lo = 0, hi = q.chunk_rows > 0 ? q.chunk_rows : (q.T < 4096 ? q.T : 4096);
+    while (lo < hi) {  // largest C in [1, hi] whose workspace fits (0 if none)
+      const int64_t mid = (lo + hi + 1) / 2;
+      q.chunk_rows = mid;
+      if (plan(&q, true).fwd <= kNoallocScratchBytes)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    if (lo == 0) {
+      q.chunk_rows = 1;
+      return fail(STCE_E_WORKSPACE,
+                  "stce_forward_noalloc: even one row per chunk needs %zu bytes of forward workspace (T=%lld, "
+                  "V=%lld); its static scratch holds %zu bytes: use stce_forward with a caller workspace",
+                  plan(&q, true).fwd, (long long)q.T, (long long)q.V, kNoallocScratchBytes);
+    }
+    q.chunk_rows = lo;
+  }
+  void* ws = nullptr;
+  hipError_t e = noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, "scratch address");
+  return forward_impl(&q, logprob, state, nullptr, dev_status, ws, kNoallocScratchBytes, stream, true);
 }
 
 }  // extern "C"

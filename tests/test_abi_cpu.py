@@ -122,6 +122,17 @@ def test_pre_gemm_temperature_excludes_the_per_row_array(lib):
                              torch.ones(2), pre_gemm_temperature=0.7)
 
 
+def test_noalloc_forward_rejects_what_its_scratch_cannot_hold(lib):
+    """stce_forward_noalloc keeps its workspace in a 64 MiB static array;
+    a vocabulary whose single-row chunk needs more is rejected before any
+    device call (the pointers here are never dereferenced)."""
+    assert lib.stce_noalloc_scratch_bytes() == 64 << 20
+    p = _prob(T=4, H=64, V=20_000_000)
+    p.hidden, p.weight, p.target = 16, 16, 16
+    st = lib.stce_forward_noalloc(ctypes.byref(p), ctypes.c_void_p(16), ctypes.c_void_p(16), None, None)
+    assert st == 3 and b"static scratch" in lib.stce_last_error()
+
+
 def test_forward_rejects_null_and_small_workspace_before_launch(lib):
     p = _prob()
     st = lib.stce_forward(ctypes.byref(p), None, None, None, None, 0, None)
