@@ -54,6 +54,12 @@ struct Layout {
   int64_t C, ldt, ntv, nbuf;                               // forward
   size_t f_flags, f_tile, f_part, f_sy, f_hs, fwd;
   size_t buf_tile, buf_part, buf_sy;                       // bytes per chunk buffer
+  // candidates of top-k-bounded rows, per chunk buffer (when the shapes allow
+  // the candidate path): keys, tile-local ids, tile bounds; and, shared by the
+  // chunks, the rows to re-project, their count and their gathered hidden rows
+  bool cand;
+  size_t f_ckey, f_cid, f_cbound, f_fail, f_fcnt, f_fbh;
+  size_t buf_ckey, buf_cid, buf_cbound;
   int64_t Vs, Vsp, Tp;                                      // backward
   size_t b_flags, b_hT, b_WT, b_d, b_dT, b_dh, b_hs, bwd;
   // backward with row classes (bf16): counts, permutation, per-position
@@ -121,7 +127,20 @@ Layout plan(const stce_problem* p, bool single_buffer = false) {
   L.f_tile = o;  o += L.nbuf * L.buf_tile;
   L.f_part = o;  o += L.nbuf * L.buf_part;
   L.f_sy = o;    o += L.nbuf * L.buf_sy;
-  L.f_hs = o;    o += hs_bytes(p);
+  L.f_hs = o;    o = align_up(o + hs_bytes(p));
+  // the candidate path exists for these shapes (validation marks the rows)
+  L.cand = V > CAP && L.ntv <= 2 * CAP;
+  if (L.cand) {
+    L.buf_ckey = align_up(4 * (size_t)L.ntv * 2 * L.C * 8);
+    L.buf_cid = align_up((size_t)L.ntv * 2 * L.C * 8);
+    L.buf_cbound = align_up(4 * (size_t)L.C * L.ntv);
+    L.f_ckey = o;   o += L.nbuf * L.buf_ckey;
+    L.f_cid = o;    o += L.nbuf * L.buf_cid;
+    L.f_cbound = o; o += L.nbuf * L.buf_cbound;
+    L.f_fail = o;   o = align_up(o + 4 * (size_t)L.C);
+    L.f_fcnt = o;   o = align_up(o + 4);
+    L.f_fbh = o;    o = align_up(o + es * (size_t)L.C * H);
+  }
   L.fwd = o;
 
   // bf16 keeps dz vocab-major only (the hidden gradient reads it MN-major);
@@ -392,11 +411,13 @@ stce_status forward_impl(const stce_problem* p, float* logprob, void* state, con
   if (dev_status && (e = launch_fill_i64(dev_status, STCE_STATUS_NONE, st))) return hip_fail(e, "status fill");
   if ((e = launch_validate(p->T, p->V, p->flags & STCE_PROBLEM_IGNORE_INDEX, p->ignore_index, p->temperature,
                            p->top_k, p->top_p, p->min_p, p->target, flags, dev_status,
-                           st)))
+                           st, L.cand ? 1 : 0)))
     return hip_fail(e, "validate");
   const size_t es = elt_size(p->dtype);
   const void* hid = nullptr;
   if ((e = hidden_for_products(p, ws, L.f_hs, 0, p->T, &hid, nullptr, st))) return hip_fail(e, "prescale hidden");
+  int* fail_rows = L.cand ? at<int>(ws, L.f_fail) : nullptr;
+  int* fail_cnt = L.cand ? at<int>(ws, L.f_fcnt) : nullptr;
   const int64_t nch = ceil_div(p->T, L.C);
   SideCtx* side = nullptr;
   if (L.nbuf == 2 && (e = side_ctx(&side))) return hip_fail(e, "side stream");
@@ -424,6 +445,12 @@ stce_status forward_impl(const stce_problem* p, float* logprob, void* state, con
     a.s_y = at<float>(ws, L.f_sy + b * L.buf_sy);
     a.want_ent = want_ent;
     a.bf16_lane = bf16_lane(p);
+    if (L.cand) {
+      a.ckey = at<float>(ws, L.f_ckey + b * L.buf_ckey);
+      a.cid = at<uint8_t>(ws, L.f_cid + b * L.buf_cid);
+      a.cbound = at<float>(ws, L.f_cbound + b * L.buf_cbound);
+      a.cld = L.C;
+    }
     if ((e = launch_fwd_projection(a, st))) return hip_fail(e, "projection");
     hipStream_t ss = st;
     if (side) {
@@ -431,6 +458,7 @@ stce_status forward_impl(const stce_problem* p, float* logprob, void* state, con
       if ((e = hipEventRecord(side->fork(c), st)) || (e = hipStreamWaitEvent(ss, side->fork(c), 0)))
         return hip_fail(e, "fork to the side stream");
     }
+    if (L.cand && (e = launch_fill_i32(fail_cnt, 1, 0, ss))) return hip_fail(e, "clear the re-projection count");
     SelParams sp{};
     sp.tile = a.tile;
     sp.ld = L.ldt;
@@ -449,8 +477,45 @@ stce_status forward_impl(const stce_problem* p, float* logprob, void* state, con
     sp.ent_full = so_hf ? so_hf + c0 : nullptr;
     sp.ent_supp = so_hs ? so_hs + c0 : nullptr;
     sp.round_lp_bf16 = bf16_lane(p);
+    if (L.cand) {
+      sp.ckey = a.ckey;
+      sp.cid = a.cid;
+      sp.cbound = a.cbound;
+      sp.cld = a.cld;
+      sp.fail_rows = fail_rows;
+      sp.fail_cnt = fail_cnt;
+    }
     launch_select(sp, (int)nc, ss);
     if ((e = hipGetLastError())) return hip_fail(e, "select");
+    if (L.cand) {
+      // rows whose candidates could not decide their support: their hidden
+      // rows gathered, projected again with every key stored into the
+      // chunk's buffer (the same kernel gives the same keys), and selected
+      // from the keys
+      void* fbh = at<char>(ws, L.f_fbh);
+      if ((e = launch_gather_rows_dev(p->dtype, (const char*)hid + es * (size_t)c0 * p->H, fail_rows, fail_cnt, nc,
+                                      p->H, fbh, ss)))
+        return hip_fail(e, "gather rows to re-project");
+      FwdArgs fa = a;
+      fa.h = fbh;
+      fa.store_all = 1;
+      fa.ckey = nullptr;
+      fa.cid = nullptr;
+      fa.cbound = nullptr;
+      fa.rowmap = fail_rows;
+      fa.n_dev = fail_cnt;
+      if ((e = launch_fwd_projection(fa, ss))) return hip_fail(e, "re-projection");
+      SelParams fp = sp;
+      fp.ckey = nullptr;
+      fp.cid = nullptr;
+      fp.cbound = nullptr;
+      fp.fail_rows = nullptr;
+      fp.fail_cnt = nullptr;
+      fp.rowmap = fail_rows;
+      fp.n_dev = fail_cnt;
+      launch_select(fp, (int)nc, ss);
+      if ((e = hipGetLastError())) return hip_fail(e, "re-selection");
+    }
     if (side && (e = hipEventRecord(side->done(c), ss))) return hip_fail(e, "selection event");
   }
   // join: the caller's stream waits for the last selection (the side stream

@@ -17,8 +17,18 @@ enum : uint32_t {
   ROW_VALID = 1u,      // metadata passed validation
   ROW_FILTERED = 2u,   // at least one of top-k / top-p / min-p is active
   ROW_IN_SUPPORT = 4u, // the target lies in the row's support
-  ROW_IGNORED = 8u     // inactive row (target equals the problem's ignore_index)
+  ROW_IGNORED = 8u,    // inactive row (target equals the problem's ignore_index)
+  // forward flag only (never in the state): a row bounded by top-k whose
+  // projection keeps candidates instead of its fp32 keys (KCAND)
+  ROW_CAND = 16u
 };
+
+// Top-k-bounded rows with 0 < k <= KCAND (and at least k vocabulary tiles, at
+// most 2 CAP of them: the selection's tile-maximum bound search) keep, per
+// (row, 256-token tile), the two largest keys of each of the 8 lanes that
+// hold the tile's 256 logits (16 candidates) and the largest key that is
+// not a candidate, instead of the row's fp32 keys.
+constexpr int KCAND = 256;
 
 // Per-row state written by the forward, read by the backward (32 bytes).
 // Field order is the one of stce_row_info in stce.h.

@@ -92,8 +92,14 @@ constexpr float LOG2E = 1.4426950408889634f;
 // ---------------------------------------------------------------------------
 // Forward projection epilogue.  M = vocabulary, N = tokens of the chunk.
 // For each (token, 256-wide vocabulary tile): applies the temperature,
-// optionally stores the fp32 keys (rows flagged ROW_FILTERED, or all rows),
-// writes the tile's (max, sum exp(s - max), min) and captures the target key.
+// stores the fp32 keys (rows flagged ROW_FILTERED but not ROW_CAND, or all
+// rows with store_all), or, for ROW_CAND rows, the tile's candidates: each
+// of the 8 lanes holding the token's 256 logits of the tile keeps its two
+// largest keys (the lower token id first among equal keys) and the largest
+// of the rest; the 16 keys and their tile-local ids are stored, and the
+// largest non-candidate key over the 8 lanes as the tile's bound (every key
+// above the bound is a candidate).  Writes the tile's (max, sum exp(s - max),
+// min) and captures the target key.
 // ---------------------------------------------------------------------------
 template <bool Ent>
 struct EpiLogits {
@@ -110,27 +116,42 @@ struct EpiLogits {
   int V;                   // valid vocabulary rows
   int N;                   // valid tokens
   int bf16_lane;           // keys of the bf16 value lane
-  static constexpr int LDS_BYTES = 2 * GN * 4 * 4;  // cross-wave merge
+  // candidates of ROW_CAND rows: ckey / cid [ntv][2][cld][8] (tile, half of
+  // the tile held by wave row wm, token, lane quad * 2 + rank), cbound
+  // [cld][ntv]; null when no row is a candidate row
+  float* ckey = nullptr;
+  uint8_t* cid = nullptr;
+  float* cbound = nullptr;
+  int64_t cld = 0;
+  // re-projection of chosen rows: column n carries row rowmap[n]'s metadata
+  // and only columns below *n_dev exist (null: identity, N)
+  const int* rowmap = nullptr;
+  const int* n_dev = nullptr;
+  static constexpr int LDS_BYTES = 2 * GN * 5 * 4;  // cross-wave merge
 
   __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem, char*) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
     const int mb = m0 + wm * 128;
     const bool full = m0 + GM <= V;
-    float pmx[ACC_J], psm[ACC_J], pmn[ACC_J], pen[ACC_J];
+    const int Nn = n_dev ? min(N, *n_dev) : N;
+    float pmx[ACC_J], psm[ACC_J], pmn[ACC_J], pen[ACC_J], pbd[ACC_J];
     // Every per-token load comes first: loads and stores share one in-order
     // counter, so a load issued after a column's key stores would make the
     // wave wait for all of them to complete before the next column.
     float tv[ACC_J];
-    bool stv[ACC_J];
+    bool stv[ACC_J], cnd[ACC_J];
     int64_t tgv[ACC_J];
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) {
       const int n = n0 + acc_col(wn, j, col);
-      const bool nv = n < N;
-      tv[j] = (nv && temp) ? temp[n] : 1.0f;
-      stv[j] = nv && (store_all || (flags[n] & ROW_FILTERED));
-      tgv[j] = (nv && target && s_y) ? target[n] : -1;
+      const bool nv = n < Nn;
+      const int rn = (nv && rowmap) ? rowmap[n] : n;
+      const uint32_t f = (nv && flags) ? flags[rn] : 0u;
+      tv[j] = (nv && temp) ? temp[rn] : 1.0f;
+      cnd[j] = nv && !store_all && ckey && (f & ROW_CAND);
+      stv[j] = nv && (store_all || ((f & ROW_FILTERED) && !cnd[j]));
+      tgv[j] = (nv && target && s_y) ? target[rn] : -1;
     }
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) {
@@ -154,6 +175,31 @@ struct EpiLogits {
               mx = fmaxf(mx, acc[i][j][r]);
               mn = fminf(mn, acc[i][j][r]);
             }
+      }
+      float bnd = -STCE_INF;  // the lane's largest non-candidate key
+      if (cnd[j]) {
+        // the lane's two largest keys, visited in increasing token id (a
+        // later equal key does not displace an earlier one)
+        float a = -STCE_INF, b = -STCE_INF, c = -STCE_INF;
+        int ia = 0, ib = 0;
+#pragma unroll
+        for (int i = 0; i < ACC_I; ++i)
+#pragma unroll
+          for (int r = 0; r < ACC_R; ++r) {
+            const int ml = wm * 128 + i * 16 + quad * 4 + r;
+            const float v = (full || m0 + ml < V) ? acc[i][j][r] : -STCE_INF;
+            const bool ga = v > a, gb = v > b;
+            c = gb ? b : fmaxf(c, v);
+            b = ga ? a : (gb ? v : b);
+            ib = ga ? ia : (gb ? ml : ib);
+            a = ga ? v : a;
+            ia = ga ? ml : ia;
+          }
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const int64_t rec = ((int64_t)(m0 / VTILE) * 2 + wm) * cld + n;
+        *(f32x2*)(ckey + rec * 8 + quad * 2) = f32x2{a, b};
+        *(uint16_t*)(cid + rec * 8 + quad * 2) = (uint16_t)(ia | (ib << 8));
+        bnd = c;
       }
       if (stv[j]) {
         float* rowp = tile + (int64_t)n * ld;
@@ -214,23 +260,26 @@ struct EpiLogits {
           lse_merge(mx, sm, omx, osm);
         }
         mn = fminf(mn, omn);
+        bnd = fmaxf(bnd, __shfl_xor(bnd, o));
       }
       pmx[j] = mx;
       psm[j] = sm;
       pmn[j] = mn;
       pen[j] = en;
+      pbd[j] = bnd;
     }
     // merge the two waves that share these tokens (wm = 0 and 1)
     __syncthreads();
-    float* red = (float*)smem;  // [2][256][4]
+    float* red = (float*)smem;  // [2][256][5]
     if (quad == 0) {
 #pragma unroll
       for (int j = 0; j < ACC_J; ++j) {
         const int tok = acc_col(wn, j, col);
-        red[(wm * 256 + tok) * 4 + 0] = pmx[j];
-        red[(wm * 256 + tok) * 4 + 1] = psm[j];
-        red[(wm * 256 + tok) * 4 + 2] = pmn[j];
-        if (Ent) red[(wm * 256 + tok) * 4 + 3] = pen[j];
+        red[(wm * 256 + tok) * 5 + 0] = pmx[j];
+        red[(wm * 256 + tok) * 5 + 1] = psm[j];
+        red[(wm * 256 + tok) * 5 + 2] = pmn[j];
+        if (Ent) red[(wm * 256 + tok) * 5 + 3] = pen[j];
+        red[(wm * 256 + tok) * 5 + 4] = pbd[j];
       }
     }
     __syncthreads();
@@ -239,20 +288,21 @@ struct EpiLogits {
       for (int j = 0; j < ACC_J; ++j) {
         const int tok = acc_col(wn, j, col);
         const int n = n0 + tok;
-        if (n < N) {
-          float mx = red[tok * 4 + 0], sm = red[tok * 4 + 1], en = 0.f;
+        if (n < Nn) {
+          float mx = red[tok * 5 + 0], sm = red[tok * 5 + 1], en = 0.f;
           if (Ent) {
-            en = red[tok * 4 + 3];
-            lse_ent_merge(mx, sm, en, red[(256 + tok) * 4 + 0], red[(256 + tok) * 4 + 1], red[(256 + tok) * 4 + 3]);
+            en = red[tok * 5 + 3];
+            lse_ent_merge(mx, sm, en, red[(256 + tok) * 5 + 0], red[(256 + tok) * 5 + 1], red[(256 + tok) * 5 + 3]);
           } else {
-            lse_merge(mx, sm, red[(256 + tok) * 4 + 0], red[(256 + tok) * 4 + 1]);
+            lse_merge(mx, sm, red[(256 + tok) * 5 + 0], red[(256 + tok) * 5 + 1]);
           }
           TilePart tp;
           tp.mx = mx;
           tp.sum = sm;
-          tp.mn = fminf(red[tok * 4 + 2], red[(256 + tok) * 4 + 2]);
+          tp.mn = fminf(red[tok * 5 + 2], red[(256 + tok) * 5 + 2]);
           tp.ent = en;
           part[(int64_t)n * ntv + m0 / VTILE] = tp;
+          if (cnd[j]) cbound[(int64_t)n * ntv + m0 / VTILE] = fmaxf(red[tok * 5 + 4], red[(256 + tok) * 5 + 4]);
         }
       }
     }

@@ -9,7 +9,7 @@ namespace {
 // ---------------------------------------------------------------------------
 __global__ void validate_kernel(int64_t T, int64_t V, int ignore, int64_t ignore_index, const float* temp,
                                 const int32_t* top_k, const float* top_p, const float* min_p,
-                                const int64_t* target, uint32_t* flags, int64_t* status) {
+                                const int64_t* target, uint32_t* flags, int64_t* status, int cand_ok) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
   const float tt = temp ? temp[t] : 1.0f;
@@ -25,7 +25,10 @@ __global__ void validate_kernel(int64_t T, int64_t V, int ignore, int64_t ignore
   else if (!(mp >= 0.0f && mp <= 1.0f)) field = 4;
   else if (!ign && (y < 0 || y >= V)) field = 5;
   const bool filtered = (k > 0 && (int64_t)k < V) || p < 1.0f || mp > 0.0f;
-  flags[t] = field ? 0u : (ROW_VALID | (filtered ? ROW_FILTERED : 0u) | (ign ? ROW_IGNORED : 0u));
+  const int64_t ntv = (V + VTILE - 1) / VTILE;
+  const bool cand = cand_ok && k > 0 && (int64_t)k < V && k <= KCAND && k <= ntv && ntv <= 2 * CAP;
+  flags[t] = field ? 0u
+                   : (ROW_VALID | (filtered ? ROW_FILTERED : 0u) | (ign ? ROW_IGNORED : 0u) | (cand ? ROW_CAND : 0u));
   if (field && status) atomicMin((unsigned long long*)status, (unsigned long long)((t << 8) | field));
 }
 
@@ -119,6 +122,22 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* in, int
       o[k] = lo | (hi << 16);
     }
     *(u32x4*)(out + (c + e) * ld_out + r0 + rb * 8) = o;
+  }
+}
+
+// out[r] = in[rowmap[r]] for r < *n_dev: rows of H elements, H a multiple of
+// 8 (16-byte rows); a grid-stride loop over nmax rows.
+template <class E>
+__global__ __launch_bounds__(256) void gather_rows_dev_kernel(const E* in, const int* rowmap, const int* n_dev,
+                                                              int64_t nmax, int64_t H, E* out) {
+  constexpr int EPV = 16 / (int)sizeof(E);
+  const int64_t per_row = H / EPV;
+  const int64_t n = min(nmax, (int64_t)*n_dev);
+  const int64_t total = n * per_row;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += stride) {
+    const int64_t r = i / per_row, c = i - r * per_row;
+    ((u32x4*)(out + r * H))[c] = ((const u32x4*)(in + (int64_t)rowmap[r] * H))[c];
   }
 }
 
@@ -395,10 +414,10 @@ hipError_t launch_gemm_splitk(const Main& mn, const Epi& ep, int64_t tiles_m, in
 hipError_t launch_validate(int64_t T, int64_t V, int ignore, int64_t ignore_index, const float* temp,
                            const int32_t* top_k, const float* top_p,
                            const float* min_p, const int64_t* target, uint32_t* flags, int64_t* status,
-                           hipStream_t s) {
+                           hipStream_t s, int cand_ok) {
   ProfScope ps(1, s);
   hipLaunchKernelGGL(validate_kernel, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, s, T, V, ignore,
-                     ignore_index, temp, top_k, top_p, min_p, target, flags, status);
+                     ignore_index, temp, top_k, top_p, min_p, target, flags, status, cand_ok);
   return hipGetLastError();
 }
 
@@ -442,6 +461,20 @@ hipError_t launch_prescale(int dtype, const void* in, int64_t n, float t, void* 
   return hipGetLastError();
 }
 
+hipError_t launch_gather_rows_dev(int dtype, const void* in, const int* rowmap, const int* n_dev, int64_t nmax,
+                                  int64_t H, void* out, hipStream_t s) {
+  const int64_t total = nmax * H / (dtype == 1 ? 8 : 4);
+  const unsigned blocks = (unsigned)(ceil_div(total, 256) < 2048 ? ceil_div(total, 256) : 2048);
+  if (blocks == 0) return hipSuccess;
+  if (dtype == 1)
+    hipLaunchKernelGGL(gather_rows_dev_kernel<bf16>, dim3(blocks), dim3(256), 0, s, (const bf16*)in, rowmap, n_dev,
+                       nmax, H, (bf16*)out);
+  else
+    hipLaunchKernelGGL(gather_rows_dev_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)in, rowmap, n_dev,
+                       nmax, H, (float*)out);
+  return hipGetLastError();
+}
+
 hipError_t launch_transpose_f32(const float* in, int64_t ld_in, int64_t R, int64_t Cc, float* out,
                                 int64_t ld_out, int64_t R_pad, hipStream_t s) {
   ProfScope ps(7, s);
@@ -475,14 +508,22 @@ hipError_t fwd_projection_impl(const FwdArgs& a, hipStream_t s) {
   ep.bf16_lane = a.bf16_lane;
   ep.V = (int)a.V;
   ep.N = (int)a.rows;
+  ep.ckey = a.ckey;
+  ep.cid = a.cid;
+  ep.cbound = a.cbound;
+  ep.cld = a.cld;
+  ep.rowmap = a.rowmap;
+  ep.n_dev = a.n_dev;
+  DynLimits dyn{};
+  dyn.n_lim = a.n_dev;
   const int64_t tm = ceil_div(a.V, GM), tn = ceil_div(a.rows, GN);
   ProfScope ps(2, s);
   if (a.dtype == 1) {
     MainBf16 mn{(const bf16*)a.W, a.H, (int)a.V, (const bf16*)a.h, a.H, (int)a.rows, (int)a.H};
-    return launch_gemm(mn, ep, tm, tn, s);
+    return launch_gemm(mn, ep, tm, tn, s, dyn);
   }
   MainF32 mn{(const float*)a.W, a.H, (int)a.V, (const float*)a.h, a.H, (int)a.rows, (int)a.H};
-  return launch_gemm(mn, ep, tm, tn, s);
+  return launch_gemm(mn, ep, tm, tn, s, dyn);
 }
 }  // namespace
 

@@ -22,12 +22,14 @@ struct ProfScope {
   ~ProfScope() { prof_end(s); }
 };
 
-// Per-row metadata validation: flags[t] = ROW_VALID | ROW_FILTERED or 0, and
-// the first bad (row << 8 | field) into *status with an atomic min.
+// Per-row metadata validation: flags[t] = ROW_VALID | ROW_FILTERED | ... or
+// 0, and the first bad (row << 8 | field) into *status with an atomic min.
+// cand_ok: mark top-k-bounded rows ROW_CAND (the forward keeps candidates for
+// them instead of their keys).
 hipError_t launch_validate(int64_t T, int64_t V, int ignore, int64_t ignore_index, const float* temp,
                            const int32_t* top_k, const float* top_p,
                            const float* min_p, const int64_t* target, uint32_t* flags, int64_t* status,
-                           hipStream_t s);
+                           hipStream_t s, int cand_ok = 0);
 hipError_t launch_fill_i64(int64_t* p, int64_t v, hipStream_t s);
 
 // out[c][r] = in[r][c] for r < R, c < Cc; zeros for R <= r < R_pad.
@@ -63,8 +65,22 @@ struct FwdArgs {
   float* s_y;
   int want_ent;  // tile partials carry the entropy sums
   int bf16_lane; // keys of the bf16 value lane
+  // candidates of ROW_CAND rows (null: none kept), token stride cld
+  float* ckey;
+  uint8_t* cid;
+  float* cbound;
+  int64_t cld;
+  // re-projection of chosen rows: column n is row rowmap[n] (its metadata),
+  // columns from *n_dev on do nothing
+  const int* rowmap;
+  const int* n_dev;
 };
 hipError_t launch_fwd_projection(const FwdArgs& a, hipStream_t s);
+
+// out[r] = in[rowmap[r]] for r < *n_dev (rows of H elements of the dtype, 1
+// bf16 or 2 fp32); rows up to nmax are covered by the launch.
+hipError_t launch_gather_rows_dev(int dtype, const void* in, const int* rowmap, const int* n_dev, int64_t nmax,
+                                  int64_t H, void* out, hipStream_t s);
 
 // Per-row policy-gradient loss: objective 1 = CISPO, 2 = clipped surrogate.
 hipError_t launch_policy_loss(int objective, float eps_low, float eps_high, float scale, const float* adv,

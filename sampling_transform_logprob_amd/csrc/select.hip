@@ -120,6 +120,7 @@ struct Shared {
   int c;             // chosen bin
   int c_p;           // bin where top-p crosses (NB if not found)
   uint32_t nbin;     // tokens in the chosen bin
+  int fail;          // the row's candidates cannot decide its support
   uint32_t above;    // tokens ahead of the window
   double mabove;     // their mass
   double Z;          // full-row mass
@@ -134,21 +135,31 @@ static_assert(sizeof(Shared) <= 32 * 1024, "selection LDS must fit beside a proj
 // two projection waves of a SIMD.
 __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
   __shared__ Shared S;
+  // row: where the keys, partials and target key are; orow: whose metadata
+  // and outputs (the same row unless re-selecting chosen rows)
   const int row = blockIdx.x, tid = threadIdx.x, w = tid >> 6;
+  if (P.n_dev && row >= *P.n_dev) return;
+  const int orow = P.rowmap ? P.rowmap[row] : row;
   const int V = P.V;
-  const uint32_t fl = P.flags[row];
+  const uint32_t fl = P.flags[orow];
   if (!(fl & ROW_VALID)) {
     if (tid == 0) {
       const float nan = __builtin_nanf("");
-      P.logprob[row] = nan;
+      P.logprob[orow] = nan;
       RowState rs{};
-      P.state[row] = rs;
-      if (P.lse_full) P.lse_full[row] = nan;
-      if (P.ent_full) P.ent_full[row] = nan;
-      if (P.ent_supp) P.ent_supp[row] = nan;
+      P.state[orow] = rs;
+      if (P.lse_full) P.lse_full[orow] = nan;
+      if (P.ent_full) P.ent_full[orow] = nan;
+      if (P.ent_supp) P.ent_supp[orow] = nan;
     }
     return;
   }
+  // a top-k row whose keys were not stored: its support comes from the
+  // projection's candidates, or the row is handed to the re-projection
+  const bool cand = P.ckey && (fl & ROW_CAND);
+  auto fail_row = [&]() {
+    if (tid == 0) P.fail_rows[atomicAdd(P.fail_cnt, 1)] = row;
+  };
 
   // ---- row maximum, minimum and full log-sum-exp from the tile partials
   const TilePart* pp = P.part + (int64_t)row * P.ntv;
@@ -175,14 +186,14 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
       if (pp[t].mx != -F_INF) es += exp(d) * ((double)pp[t].ent + d * (double)pp[t].sum);
     }
     h_full = log(zfull) - block_reduce(es, AddD{}, S.sd) / zfull;
-    if (tid == 0 && P.ent_full) P.ent_full[row] = (float)h_full;
+    if (tid == 0 && P.ent_full) P.ent_full[orow] = (float)h_full;
   }
-  if (tid == 0 && P.lse_full) P.lse_full[row] = (float)lse_full;
+  if (tid == 0 && P.lse_full) P.lse_full[orow] = (float)lse_full;
 
   // an inactive row's target is no token, so the projection left no key
   // for it: its state records 0
   const float sy = (fl & ROW_IGNORED) ? 0.0f : P.s_y[row];
-  const int64_t y = P.target[row];
+  const int64_t y = P.target[orow];
   RowState rs;
   rs.m = m;
   rs.lse_full = (float)lse_full;
@@ -196,16 +207,16 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
       rs.flags = ROW_VALID | ROW_IN_SUPPORT;
       rs.lse_s = rs.lse_full;
       if (fl & ROW_IGNORED) rs.flags = ROW_VALID | ROW_IGNORED;
-      P.logprob[row] = lane_logprob(P, (fl & ROW_IGNORED) ? 0.0f : (float)fmin((double)sy - lse_full, 0.0));
-      P.state[row] = rs;
-      if (P.ent_supp) P.ent_supp[row] = (float)h_full;
+      P.logprob[orow] = lane_logprob(P, (fl & ROW_IGNORED) ? 0.0f : (float)fmin((double)sy - lse_full, 0.0));
+      P.state[orow] = rs;
+      if (P.ent_supp) P.ent_supp[orow] = (float)h_full;
     }
     return;
   }
 
-  const int k = P.top_k ? P.top_k[row] : 0;
-  const float p = P.top_p ? P.top_p[row] : 1.0f;
-  const float mp = P.min_p ? P.min_p[row] : 0.0f;
+  const int k = P.top_k ? P.top_k[orow] : 0;
+  const float p = P.top_p ? P.top_p[orow] : 1.0f;
+  const float mp = P.min_p ? P.min_p[orow] : 0.0f;
   const bool k_on = k > 0 && k < V, p_on = p < 1.0f, m_on = mp > 0.0f;
   const double thr = m_on ? log((double)mp) : -D_INF;
   const float* rp = P.tile + (int64_t)row * P.ld;
@@ -295,7 +306,33 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
       const int nt = S.ntiles;
       auto pred = [&](float s, uint32_t key, int) { return (!kb || key >= bkey) && (!m_on || (double)s - m64 >= thr); };
       int n;
-      if (nt <= TLIST) {
+      if (cand) {
+        // the candidates of the candidate tiles; every token at or above the
+        // bound is among them when each tile's largest non-candidate key is
+        // below it (ROW_CAND rows always have the bound: kb)
+        if (tid == 0) {
+          S.cnt = 0;
+          S.fail = nt > TLIST;
+        }
+        __syncthreads();
+        const int ntl = min(nt, TLIST);
+        for (int q = tid; q < ntl; q += ST)
+          if (order_key(P.cbound[(int64_t)row * P.ntv + S.tiles[q]]) >= bkey) S.fail = 1;
+        for (int q = tid; q < ntl * 16; q += ST) {
+          const int t = (int)S.tiles[q >> 4], e = q & 15;
+          const int64_t rec = ((int64_t)t * 2 + (e >> 3)) * P.cld + row;
+          const float sv = P.ckey[rec * 8 + (e & 7)];
+          const int v = t * VTILE + P.cid[rec * 8 + (e & 7)];
+          const uint32_t key = order_key(sv);
+          if (v < V && pred(sv, key, v)) {
+            const int i = atomicAdd(&S.cnt, 1);
+            if (i < CAP) S.u.cand[i] = composite(key, (uint32_t)v);
+          }
+        }
+        __syncthreads();
+        n = S.fail ? CAP + 1 : S.cnt;
+        __syncthreads();
+      } else if (nt <= TLIST) {
         if (tid == 0) S.cnt = 0;
         __syncthreads();
         for (int q = tid; q < nt * (VTILE / 4); q += ST) {
@@ -329,6 +366,10 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
     }
   }
 
+  if (nw < 0 && cand) {  // no bounded window from the candidates
+    fail_row();
+    return;
+  }
   if (nw < 0) {
     // ---- value histogram of (m - s): counts and fp64 masses per bin
     const float range = m - smin;
@@ -526,6 +567,22 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
     if (nm < n_loc) n_loc = nm;
   }
   if (n_loc < 1) n_loc = 1;
+  // number of window tokens up to and including the first at which the
+  // running mass (from the thread's base, in window order, as the top-p scan
+  // below sums it) reaches pz; INT32_MAX if no window token does
+  auto crossing = [&](double b0, double pz) -> int {
+    int loc = INT32_MAX;
+    double run = b0;
+    for (int i = lo; i < hi; ++i) {
+      run += exp((double)key_value(comp_key(S.u.cand[i])) - m64);
+      if (run >= pz) {
+        loc = i;
+        break;
+      }
+    }
+    const int idx = block_reduce(loc, MinI{}, S.si);
+    return idx != INT32_MAX ? idx + 1 : INT32_MAX;
+  };
   // mass of the first `upto` window tokens, summed in the same order as the
   // top-p scan below
   auto mass_upto = [&](int upto, double* dst) {
@@ -545,6 +602,17 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
     mass_upto(n_loc, &S.mass_o);
     if (S.mass_o < (double)p * z32 * (1.0 - 1e-3)) {
       need_p = false;
+    } else if (cand) {
+      // no keys to sum the exact row mass from: the crossing must be the
+      // same for every row mass within the partials' error of z32
+      const int np_lo = crossing(base, (double)p * z32 * (1.0 - 1e-3));
+      const int np_hi = crossing(base, (double)p * z32 * (1.0 + 1e-3));
+      if (np_lo != np_hi || np_lo == INT32_MAX) {
+        fail_row();
+        return;
+      }
+      need_p = false;
+      if (np_lo < n_loc) n_loc = np_lo;
     } else {
       double zl = 0.0;
       for (int q = tid; q < nv4; q += ST) {
@@ -572,6 +640,7 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
     if (np < n_loc) n_loc = np;
   }
   mass_upto(n_loc, &S.mass_s);
+  // (past this point the row is decided; everything below reads the window)
   if (P.ent_supp) {
     // sum over the support of e^(s - m) (s - m): from the window when the
     // support starts at the top of the order, else one membership pass
@@ -600,7 +669,7 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
       }
     }
     const double E = block_reduce(es, AddD{}, S.sd);
-    if (tid == 0) P.ent_supp[row] = (float)(log(S.mass_s) - E / S.mass_s);
+    if (tid == 0) P.ent_supp[orow] = (float)(log(S.mass_s) - E / S.mass_s);
   }
   if (tid == 0) {
     const uint64_t bc = S.u.cand[n_loc - 1];
@@ -613,8 +682,8 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
     const bool ign = (fl & ROW_IGNORED) != 0;
     const bool in = !ign && (ky > rs.key_thr || (ky == rs.key_thr && y <= (int64_t)rs.id_thr));
     rs.flags = ROW_VALID | ROW_FILTERED | (in ? ROW_IN_SUPPORT : 0u) | (ign ? ROW_IGNORED : 0u);
-    P.logprob[row] = lane_logprob(P, ign ? 0.0f : (in ? (float)fmin((double)sy - lse_s, 0.0) : -F_INF));
-    P.state[row] = rs;
+    P.logprob[orow] = lane_logprob(P, ign ? 0.0f : (in ? (float)fmin((double)sy - lse_s, 0.0) : -F_INF));
+    P.state[orow] = rs;
   }
 }
 

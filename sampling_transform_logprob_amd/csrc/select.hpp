@@ -15,7 +15,12 @@
 //   * whole row, when V <= CAP;
 //   * bounded candidates: tokens >= the k-th largest tile maximum (a lower
 //     bound of the k-th largest key, since the tile maxima are distinct
-//     tokens) and passing min-p -- a prefix that contains the support;
+//     tokens) and passing min-p -- a prefix that contains the support; for a
+//     top-k row whose keys were not stored, from the projection's per-tile
+//     candidates when every candidate tile's bound (its largest key that is
+//     not a candidate) lies below the k-th largest tile maximum, so that the
+//     candidates hold every token of that prefix (else the row is re-projected
+//     with its keys stored and selected again);
 //   * value histogram: NB bins of (m - s) over the row with per-bin counts and
 //     fp64 masses; the first bin where a filter crosses is the window;
 //   * radix refinement of that bin on the 64-bit composite (key, ~id), 8 bits
@@ -53,6 +58,21 @@ struct SelParams {
   float* ent_full;          // entropy of softmax(s) over the row
   float* ent_supp;          // entropy of the filtered distribution on the support
   int round_lp_bf16;        // the bf16 value lane: logprob rounded to bf16
+  // candidates of ROW_CAND rows (the projection's layout; null: every
+  // filtered row's keys are in `tile`): a row decides its support from them
+  // when they provably hold every token its window needs, else it is added to
+  // fail_rows (fail_cnt counts them) and writes nothing
+  const float* ckey;
+  const uint8_t* cid;
+  const float* cbound;
+  int64_t cld;
+  int* fail_rows;
+  int* fail_cnt;
+  // re-selection of chosen rows: row r reads keys, partials and target key
+  // at r but takes the metadata of row rowmap[r] and writes its outputs
+  // there; rows from *n_dev on do nothing (null: identity, all rows)
+  const int* rowmap;
+  const int* n_dev;
 };
 
 void launch_select(const SelParams& p, int rows, hipStream_t stream);
