@@ -264,8 +264,16 @@ def _meta(R, top_k, top_p, min_p):
 # --------------------------------------------------------------------------
 # forward and backward
 # --------------------------------------------------------------------------
+def _logits(h_rows, W, lane, w_scale):
+    """The lane's logits of the given rows: fp64 ``h W^T``, or the fp8 lane's
+    ``(h8 W8^T) sW a`` (``W`` then holds e4m3 codes)."""
+    if lane == "fp8":
+        return fp8_logits(h_rows, W, w_scale)
+    return chunk_logits(h_rows, W)
+
+
 def forward(h, W, target, temperature=None, top_k=None, top_p=None, min_p=None,
-            keys=None, rows=None, ignore_index=None, lane="fp32") -> dict:
+            keys=None, rows=None, ignore_index=None, lane="fp32", w_scale=None) -> dict:
     """Selected logprob on the filtered support, per row.
 
     ``h`` [T, H] and ``W`` [V, H] hold the operand values (bf16 or fp32 values,
@@ -278,7 +286,9 @@ def forward(h, W, target, temperature=None, top_k=None, top_p=None, min_p=None,
     logprob 0 and an exactly zero gradient; their support and side outputs
     are still computed.  ``lane="bf16"``: the bf16 value program (keys from
     ``bf16_lane_keys``, values taken from those keys, logprob rounded to
-    bf16); the default is the fp32 program.
+    bf16); ``lane="fp8"``: ``W`` holds e4m3 codes with per-row scales
+    ``w_scale`` and the hidden rows are quantized per row (``fp8_logits``);
+    the default is the fp32 program.
 
     Returns per selected row: ``logprob`` (fp64, -inf out of support),
     ``lse`` (log-sum-exp of z/T over the support), ``n``, ``key_thr``,
@@ -296,8 +306,8 @@ def forward(h, W, target, temperature=None, top_k=None, top_p=None, min_p=None,
     temp = np.ones(T, np.float32) if temperature is None else np.asarray(temperature, np.float32)
     tk, tp, mp = _meta(T, top_k, top_p, min_p)
     _check_temperature(temp[rows])
-    assert lane in ("fp32", "bf16"), lane
-    z = chunk_logits(h[rows], W)                              # fp64 [R, V]
+    assert lane in ("fp32", "bf16", "fp8"), lane
+    z = _logits(h[rows], W, lane, w_scale)                    # fp64 [R, V]
     if keys is not None:
         s32 = canonical_f32(keys)
     elif lane == "bf16":
@@ -305,7 +315,7 @@ def forward(h, W, target, temperature=None, top_k=None, top_p=None, min_p=None,
     else:
         s32 = scale_logits(z, temp[rows])
     # values: fp64 z / T, or in the bf16 lane the bf16 keys themselves
-    u = z / temp[rows].astype(np.float64)[:, None] if lane == "fp32" else s32.astype(np.float64)
+    u = s32.astype(np.float64) if lane == "bf16" else z / temp[rows].astype(np.float64)[:, None]
     R, V = z.shape
     tgt = np.asarray(target, np.int64)[rows]
     ignored = np.zeros(R, bool) if ignore_index is None else tgt == int(ignore_index)
@@ -345,7 +355,7 @@ def _entropy(x) -> tuple:
     return lse, float(-(np.exp(logp) * logp).sum())
 
 
-def dlogits(h, W, target, fwd: dict, grad_logprob, temperature=None) -> np.ndarray:
+def dlogits(h, W, target, fwd: dict, grad_logprob, temperature=None, w_scale=None) -> np.ndarray:
     """``dz[r, j] = g_r (1[j = y_r] - q_rj) / T_r`` on the rows of ``fwd``.
 
     ``q`` is the softmax of ``z / T`` restricted to the support (in the bf16
@@ -355,9 +365,10 @@ def dlogits(h, W, target, fwd: dict, grad_logprob, temperature=None) -> np.ndarr
     rows = fwd["rows"]
     T = np.asarray(h).shape[0]
     temp = np.ones(T, np.float32) if temperature is None else np.asarray(temperature, np.float32)
-    z = chunk_logits(np.asarray(h)[rows], W)
+    lane = fwd.get("lane", "fp32")
+    z = _logits(np.asarray(h)[rows], W, lane, w_scale)
     t64 = temp[rows].astype(np.float64)
-    u = z / t64[:, None] if fwd.get("lane", "fp32") == "fp32" else fwd["keys"].astype(np.float64)
+    u = fwd["keys"].astype(np.float64) if lane == "bf16" else z / t64[:, None]
     g = np.asarray(grad_logprob, np.float64)[rows]
     tgt = np.asarray(target, np.int64)[rows]
     dz = np.zeros_like(z)
@@ -372,14 +383,20 @@ def dlogits(h, W, target, fwd: dict, grad_logprob, temperature=None) -> np.ndarr
     return dz
 
 
-def backward(h, W, target, fwd: dict, grad_logprob, temperature=None):
+def backward(h, W, target, fwd: dict, grad_logprob, temperature=None, w_scale=None):
     """VJP of ``sum_r g_r * logprob_r`` with respect to ``h`` and ``W``.
 
     Returns ``(dH, dW)``: ``dH`` [len(rows), H] for the rows of ``fwd`` and
-    ``dW`` [V, H] summed over those rows.
+    ``dW`` [V, H] summed over those rows.  In the fp8 lane the quantizations
+    pass gradients unchanged (straight through): ``dH = dz W_deq`` and
+    ``dW = dz^T h_deq``, the gradients of the product's dequantized operands.
     """
-    dz = dlogits(h, W, target, fwd, grad_logprob, temperature)
-    return gradient_products(dz, np.asarray(h)[fwd["rows"]], W)
+    dz = dlogits(h, W, target, fwd, grad_logprob, temperature, w_scale)
+    hr = np.asarray(h)[fwd["rows"]]
+    if fwd.get("lane", "fp32") == "fp8":
+        W = fp8_dequant_weight(W, w_scale)
+        hr = fp8_dequant_rows(hr)
+    return gradient_products(dz, hr, W)
 
 
 def gradient_products(dz, h, W):
@@ -427,6 +444,96 @@ def backward_pre_gemm(h_scaled, W, target, fwd: dict, grad_logprob, temperature)
     ``dH = (dz W) / T`` and ``dW = dz^T h_scaled``, ``dz = g (onehot - q)``."""
     dH, dW = backward(h_scaled, W, target, fwd, grad_logprob)
     return dH / float(np.float32(temperature)), dW
+
+
+# --------------------------------------------------------------------------
+# fp8 lm_head lane
+# --------------------------------------------------------------------------
+# [xorl#74] "What this PR does" 4 rejects FP8 lm_head weights with one
+# actionable error; scoring such a head in place of that rejection is read
+# here as follows (the pages give no formula).  The weight arrives quantized
+# per vocabulary row: e4m3 codes W8 (the OCP "e4m3fn" format: 1 sign, 4
+# exponent bits with bias 7, 3 mantissa bits, no infinities, largest finite
+# value 448) and one fp32 scale sW[j]: W_deq[j, k] = sW[j] * W8[j, k].
+# The hidden states are quantized per row to the same format, so that both
+# operands of the product are fp8: a[t] = fl32(max_k |h[t, k]| / 448) (1 for
+# an all-zero row) and h8[t, k] = e4m3(clamp(fl32(h[t, k] / a[t]), -448, 448))
+# with rounding to nearest, ties to even.  The logits are
+# z[t, j] = (sum_k h8[t, k] W8[j, k]) * sW[j] * a[t], the keys and the
+# support program follow as in the fp32 lane.  The gradients treat both
+# quantizations as identity (straight through): dz as in the fp32 lane, and
+# the product's two operands are the dequantized values, so
+# dH = dz W_deq and dW = dz^T h_deq with h_deq[t, k] = a[t] h8[t, k] (exact
+# products of an fp32 scale and an e4m3 value, kept in fp64 here).
+
+E4M3_MAX = 448.0
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """uint8 e4m3fn codes of fp32 values with |x| <= 448, rounded to nearest
+    with ties to even (the format's definition: subnormals m * 2^-9, normals
+    (1 + m/8) * 2^(e - 7) for biased exponents e = 1 .. 15)."""
+    x = np.asarray(x, np.float32).astype(np.float64)
+    assert np.all(np.abs(x) <= E4M3_MAX), "e4m3 input beyond the largest finite value"
+    sign = (np.signbit(x)).astype(np.uint32) << 7
+    a = np.abs(x)
+    out = np.zeros(a.shape, np.uint32)
+    sub = a < 2.0 ** -6
+    out[sub] = np.rint(a[sub] * 2.0 ** 9).astype(np.uint32)           # 0 .. 8 (8 is the smallest normal)
+    nrm = ~sub
+    e = np.floor(np.log2(np.where(nrm, a, 1.0))).astype(np.int64)
+    q = np.rint(a * np.exp2(3.0 - e))                                   # 8 .. 16, exact scaling
+    carry = q == 16.0
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, 8.0, q)
+    code = ((e + 7) << 3) | (q.astype(np.int64) - 8)
+    out[nrm] = code[nrm].astype(np.uint32)
+    return (out | sign).astype(np.uint8)
+
+
+def e4m3_decode(code) -> np.ndarray:
+    """fp64 values of e4m3fn codes (0x7F / 0xFF, the NaN codes, are not
+    accepted)."""
+    c = np.asarray(code, np.uint8).astype(np.int64)
+    assert not np.any((c & 0x7F) == 0x7F), "e4m3 NaN code"
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return sign * mag
+
+
+def fp8_quantize_rows(h):
+    """Per-row quantization of the hidden states: (codes [T, H] uint8,
+    scales a [T] fp32) with a = fl32(amax / 448) (1 for a zero row) and
+    codes = e4m3(clamp(fl32(h / a), -448, 448))."""
+    h32 = np.asarray(h, np.float32)
+    amax = np.abs(h32).max(axis=1).astype(np.float64)
+    a = np.where(amax > 0, (amax / E4M3_MAX).astype(np.float32), np.float32(1.0)).astype(np.float32)
+    x = (h32.astype(np.float64) / a.astype(np.float64)[:, None]).astype(np.float32)
+    x = np.clip(x, -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    return e4m3_encode(x), a
+
+
+def fp8_dequant_weight(w8, w_scale) -> np.ndarray:
+    """W_deq = sW[j] * W8[j, k] (fp64: the product of an fp32 scale and an
+    e4m3 value is exact)."""
+    return e4m3_decode(w8) * np.asarray(w_scale, np.float32).astype(np.float64)[:, None]
+
+
+def fp8_dequant_rows(h) -> np.ndarray:
+    """h_deq = a[t] * h8[t, k], the quantized hidden rows' values (fp64,
+    exact)."""
+    h8, a = fp8_quantize_rows(h)
+    return e4m3_decode(h8) * a.astype(np.float64)[:, None]
+
+
+def fp8_logits(h, w8, w_scale) -> np.ndarray:
+    """``z = (h8 W8^T) * sW * a`` in fp64 for the fp8 lane (products of e4m3
+    values are exact; the sum is fp64)."""
+    h8, a = fp8_quantize_rows(h)
+    acc = e4m3_decode(h8) @ e4m3_decode(w8).T
+    return acc * np.asarray(w_scale, np.float32).astype(np.float64)[None, :] * a.astype(np.float64)[:, None]
 
 
 OBJECTIVES = ("cispo", "clip")

@@ -80,9 +80,20 @@ MUTANTS = {
         "            lp = float(lp)",
         ["test_bf16_lane_logprob_is_the_bf16_log_softmax_of_the_keys"]),
     "bf16 lane gradient from the fp64 logits": (
-        '    u = z / t64[:, None] if fwd.get("lane", "fp32") == "fp32" else fwd["keys"].astype(np.float64)',
+        '    u = fwd["keys"].astype(np.float64) if lane == "bf16" else z / t64[:, None]',
         "    u = z / t64[:, None]",
         ["test_bf16_lane_gradient_is_the_straight_through_vjp"]),
+    "e4m3 rounding ties away from zero": (
+        "    q = np.rint(a * np.exp2(3.0 - e))                                   # 8 .. 16, exact scaling",
+        "    q = np.floor(a * np.exp2(3.0 - e) + 0.5)",
+        ["test_e4m3_encode_matches_torch_and_ties_to_even"]),
+    "fp8 dW from the unquantized hidden rows": (
+        "        hr = fp8_dequant_rows(hr)\n", "",
+        ["test_fp8_lane_gradient_is_the_straight_through_vjp"]),
+    "fp8 logits miss the row scale": (
+        "    return acc * np.asarray(w_scale, np.float32).astype(np.float64)[None, :] * a.astype(np.float64)[:, None]",
+        "    return acc * np.asarray(w_scale, np.float32).astype(np.float64)[None, :]",
+        ["test_fp8_logits_reduce_to_the_plain_product_on_exact_operands"]),
 }
 
 

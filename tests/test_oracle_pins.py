@@ -772,3 +772,104 @@ def test_bf16_lane_gradient_is_the_straight_through_vjp(rng):
     L.backward()
     np.testing.assert_allclose(dH, th.grad.numpy(), rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(dW, tW.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- fp8 lane
+def test_e4m3_encode_matches_torch_and_ties_to_even():
+    """The encoder against torch's float8_e4m3fn cast (round to nearest,
+    ties to even) over every magnitude of the format, subnormals, exact ties
+    and the largest finite value; decode(encode(x)) is that cast's value."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.Generator(np.random.PCG64(88))
+    mag = np.exp2(rng.uniform(-12, np.log2(448.0), 40000))
+    x = (mag * rng.choice([-1.0, 1.0], mag.size)).astype(np.float32)
+    x = np.clip(x, -448, 448).astype(np.float32)
+    vals = oracle.e4m3_decode(np.arange(256, dtype=np.uint8)[(np.arange(256) & 0x7F) != 0x7F])
+    pos = np.unique(np.abs(vals))
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)              # exact ties between neighbours
+    x = np.concatenate([x, mids, -mids, np.float32([0.0, -0.0, 448.0, -448.0, 2.0 ** -9, 2.0 ** -10, 1.0625])])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn)
+    assert np.array_equal(oracle.e4m3_encode(x), ref.view(torch.uint8).numpy())
+    assert np.array_equal(oracle.e4m3_decode(oracle.e4m3_encode(x)), ref.float().numpy().astype(np.float64))
+    assert oracle.e4m3_encode(np.float32([1.0625]))[0] == 0x38                   # tie down to even (1.0)
+    assert oracle.e4m3_encode(np.float32([1.1875]))[0] == 0x3A                   # tie up to even (1.25)
+
+
+def test_e4m3_decode_is_the_format_on_every_code():
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes & 0x7F) != 0x7F]                              # the two NaN codes excluded
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(oracle.e4m3_decode(codes), ref.astype(np.float64))
+    assert oracle.e4m3_decode(np.uint8([0x7E]))[0] == 448.0 and oracle.e4m3_decode(np.uint8([0x01]))[0] == 2.0 ** -9
+
+
+def test_fp8_row_quantization_closed_forms():
+    """The row maximum maps to +-448 exactly; a zero row keeps scale 1 and
+    zero codes; every value lies within half an e4m3 step of its code times
+    the scale."""
+    rng = np.random.Generator(np.random.PCG64(89))
+    h = (rng.standard_normal((6, 40)) * rng.uniform(0.01, 50, (6, 1))).astype(np.float32)
+    h[3] = 0.0
+    codes, a = oracle.fp8_quantize_rows(h)
+    amax = np.abs(h).max(1)
+    for t in range(6):
+        if t == 3:
+            assert a[t] == 1.0 and not codes[t].any()
+            continue
+        assert a[t] == np.float32(amax[t] / np.float32(448.0))
+        k = int(np.argmax(np.abs(h[t])))
+        assert oracle.e4m3_decode(codes[t, k:k + 1])[0] == np.copysign(448.0, h[t, k])
+    deq = oracle.fp8_dequant_rows(h).astype(np.float64)
+    step = np.maximum(np.exp2(np.floor(np.log2(np.maximum(np.abs(h) / a[:, None], 2.0 ** -6))) - 3), 2.0 ** -9)
+    assert np.all(np.abs(deq - h) <= 0.5 * step * a[:, None] * (1 + 1e-6) + 1e-30)
+
+
+def test_fp8_logits_reduce_to_the_plain_product_on_exact_operands():
+    """Hidden rows whose values are e4m3 values times a power of two with the
+    row maximum 448 times it quantize exactly, and a power-of-two weight
+    scale dequantizes exactly: the fp8 lane's logits are then h W_deq^T."""
+    rng = np.random.Generator(np.random.PCG64(90))
+    pos = np.unique(np.abs(oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8))))
+    hv = rng.choice(pos, (5, 32)) * rng.choice([-1, 1], (5, 32))
+    hv[:, 0] = 448.0
+    h = (hv * np.exp2(rng.integers(-4, 3, (5, 1)))).astype(np.float32)
+    w8 = rng.integers(0, 0x7E, (9, 32)).astype(np.uint8) | (rng.integers(0, 2, (9, 32)) << 7).astype(np.uint8)
+    w_scale = np.exp2(rng.integers(-8, -2, 9)).astype(np.float32)
+    assert np.array_equal(oracle.fp8_dequant_rows(h), h.astype(np.float64))
+    z = oracle.fp8_logits(h, w8, w_scale)
+    ref = h.astype(np.float64) @ oracle.fp8_dequant_weight(w8, w_scale).T
+    np.testing.assert_allclose(z, ref, rtol=1e-15, atol=0)
+
+
+def test_fp8_lane_gradient_is_the_straight_through_vjp():
+    """fp64 autograd of the selected logprob with the product's operands
+    taken as the dequantized values (quantization passes gradients
+    unchanged): dH = dz W_deq, dW = dz^T h_deq."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.Generator(np.random.PCG64(91))
+    T, H, V = 4, 16, 30
+    h = rng.standard_normal((T, H)).astype(np.float32)
+    w8 = (rng.integers(0x20, 0x50, (V, H)) | (rng.integers(0, 2, (V, H)) << 7)).astype(np.uint8)
+    w_scale = rng.uniform(0.01, 0.05, V).astype(np.float32)
+    temp = rng.uniform(0.6, 1.4, T).astype(np.float32)
+    meta = dict(top_k=np.array([0, 5, 0, 7]), top_p=np.array([1.0, 1.0, 0.8, 1.0], np.float32))
+    f0 = oracle.forward(h, w8, np.zeros(T, np.int64), temp, **meta, lane="fp8", w_scale=w_scale)
+    y = np.array([oracle.order_row(f0["keys"][t])[1] for t in range(T)])
+    f = oracle.forward(h, w8, y, temp, **meta, lane="fp8", w_scale=w_scale)
+    assert f["in_support"].all()
+    g = rng.standard_normal(T)
+    dH, dW = oracle.backward(h, w8, y, f, g, temp, w_scale=w_scale)
+    hq = torch.tensor(oracle.fp8_dequant_rows(h), requires_grad=True)
+    wq = torch.tensor(oracle.fp8_dequant_weight(w8, w_scale), requires_grad=True)
+    # the lane's logits from the dequantized operands: h_deq W_deq^T = (h8 W8^T) sW a
+    u = (hq @ wq.T) / torch.tensor(temp.astype(np.float64))[:, None]
+    loss = 0.0
+    for t in range(T):
+        mask = torch.tensor(oracle.in_support(f["keys"][t], int(f["key_thr"][t]), int(f["id_thr"][t])))
+        loss = loss + float(g[t]) * (u[t, y[t]] - torch.logsumexp(u[t][mask], 0))
+    loss.backward()
+    np.testing.assert_allclose(dH, hq.grad.numpy(), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(dW, wq.grad.numpy(), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(oracle.fp8_logits(h, w8, w_scale),
+                               (hq @ wq.T).detach().numpy(), rtol=1e-13, atol=1e-15)
