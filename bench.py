@@ -139,10 +139,139 @@ def row_classes(info, g, nsp=128):
 KERNEL_SYMBOLS = {
     # kernel kind -> epilogue name in its (mangled or demangled) symbol; the bf16 main loop
     "projection": "EpiLogits",
-    "dlogits": "EpiDlogits",
+    "dlogits": "EpiGrad",
     "grad_weight": "EpiStore",
     "grad_hidden": "EpiAccum",
 }
+
+# kernel-trace labels: (substring of the symbol, label), first match wins
+TRACE_LABELS = [
+    ("EpiLogits", "gemm: forward projection + keys or candidates + tile partials (EpiLogits)"),
+    ("EpiGrad", "gemm: backward recompute + dz entries / dense dz^T (EpiGrad)"),
+    ("EpiStore", "gemm: grad_weight of the dense rows (EpiStore)"),
+    ("EpiAccumT", "gemm: grad_hidden of the dense rows as dH^T (EpiAccumT)"),
+    ("EpiDlogits", "gemm: backward recompute + dz^T, fp32 operands (EpiDlogits)"),
+    ("sparse_dw_kernel", "sparse grad_weight rows from the dz entry buckets"),
+    ("sparse_dh_kernel", "sparse grad_hidden rows from the dz entries"),
+    ("select_kernel", "select: support program + logprob"),
+    ("class_", "backward row classes (count, scan, place)"),
+    ("gather_rows", "row gathers (permuted hidden rows; rows to re-project)"),
+    ("bucket_fill", "dz entries filed into vocabulary-row buckets"),
+    ("scan_", "exclusive scans (bucket offsets)"),
+    ("transpose", "transpose (W^T, dense rows only)"),
+    ("validate_kernel", "validate metadata"),
+    ("fill_", "small fills (counters, status)"),
+]
+
+
+def mfma_busy_summary(args):
+    """Writes profiles/<config>_gemm_mfma_busy.md from one `rocprofv3 --pmc
+    SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE` run over this
+    bench: per product, the clock (GRBM_GUI_ACTIVE / 8 XCDs / duration) and
+    the matrix pipe's busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over
+    GRBM_GUI_ACTIVE / 8 x 1024 SIMDs), averaged over the launches that did
+    work."""
+    import csv
+    import glob
+    d = args.mfma_busy_summary
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    assert len(files) == 1, f"expected one counter_collection.csv in {d}, found {files}"
+    disp = {}
+    for r in csv.DictReader(open(files[0])):
+        kn = r["Kernel_Name"]
+        if "gemm_kernel" not in kn:
+            continue
+        e = disp.setdefault(r["Dispatch_Id"], {"name": kn})
+        e[r["Counter_Name"]] = float(r["Counter_Value"])
+        if "Start_Timestamp" in r and r["Start_Timestamp"]:
+            e["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    groups = {}
+    for e in disp.values():
+        label = next((lab for key, lab in TRACE_LABELS if key in e["name"]), e["name"][:60])
+        groups.setdefault(label, []).append(e)
+    lines = [f"# Matrix-pipe busy fraction and clock per product: {args.config} fwd+bwd", "",
+             "Command (from the repository root, on one MI355X):", "", "```",
+             "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE --output-format csv "
+             f"-d <D> -- python3 bench.py --steps 1 --warmup 2 --profile-steps 1 --no-cpu-baseline --config {args.config}",
+             f"python3 bench.py --mfma-busy-summary <D> --config {args.config}", "```", "",
+             "clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+             "(GRBM_GUI_ACTIVE / 8 x 1024 SIMDs); averaged over the launches of the last two steps that did work "
+             "(an empty re-projection returns at once).", "",
+             "| product | launches | avg ms (under counters) | clock GHz | MFMA busy |", "|---|---|---|---|---|"]
+    for label, es in sorted(groups.items()):
+        big = max(x.get("GRBM_GUI_ACTIVE", 0.0) for x in es)
+        work = [x for x in es if x.get("GRBM_GUI_ACTIVE", 0.0) >= 0.01 * big]
+        work = work[len(work) // 2:] if len(work) > 1 else work        # the later (warm) launches
+        if not work:
+            continue
+        g = np.mean([x.get("GRBM_GUI_ACTIVE", 0.0) for x in work])
+        busy = np.mean([x.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / max(x.get("GRBM_GUI_ACTIVE", 1.0) / 8 * 1024, 1.0)
+                        for x in work])
+        ns = [x["ns"] for x in work if "ns" in x]
+        ms = f"{np.mean(ns) / 1e6:.3f}" if ns else "n/a"
+        clock = f"{g / 8 / np.mean(ns):.2f}" if ns else "n/a"
+        lines.append(f"| {label} | {len(work)} | {ms} | {clock} | {busy:.3f} |")
+    lines.append("")
+    out = os.path.join(ROOT, "profiles", f"{args.config}_gemm_mfma_busy.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def kernel_stats_summary(args):
+    """Writes profiles/<config>_fwd_bwd_kernel_stats.md from the
+    *kernel_stats.csv of `rocprofv3 --kernel-trace --stats --output-format
+    csv` over this bench."""
+    import csv
+    import glob
+    d = args.kernel_stats_summary
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    assert len(files) == 1, f"expected one kernel_stats.csv in {d}, found {files}"
+    agg = {}
+    total = 0.0
+    for r in csv.DictReader(open(files[0])):
+        ns = float(r["TotalDurationNs"])
+        total += ns
+        if "stce" in r["Name"]:
+            label = next((lab for key, lab in TRACE_LABELS if key in r["Name"]), None)
+        else:
+            label = "(torch kernels of the untimed input preparation: target sampling, copies)"
+        label = label or r["Name"][:80]
+        a = agg.setdefault(label, [0, 0.0])
+        a[0] += int(r["Calls"])
+        a[1] += ns
+    lines = [f"# Kernel statistics: {args.config} fwd+bwd", "",
+             "Command (from the repository root, on one MI355X):", "", "```",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d <D> -o {args.config} -- python3 bench.py "
+             f"--steps 3 --warmup 1 --no-cpu-baseline --config {args.config}",
+             f"python3 bench.py --kernel-stats-summary <D> --config {args.config}", "```", "",
+             "| kernel | calls | avg ms | total ms | % of traced GPU time |", "|---|---|---|---|---|"]
+    for label, (calls, ns) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        avg = f"{ns / calls / 1e6:.3f}" if calls and "torch" not in label else ""
+        lines.append(f"| {label} | {calls} | {avg} | {ns / 1e6:.2f} | {100 * ns / total:.2f} |")
+    lines += ["", "The trace covers the warm-up step, the 3 timed steps and the 3 steps of the per-kernel pass "
+              "(7 steps). Averages include the warm-up step's launches, taken while the clock ramps up.", ""]
+    # the projection kernel also runs each chunk's re-projection (side stream,
+    # usually no row): split its launches by stream from the kernel trace
+    traces = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if len(traces) == 1:
+        rows = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Stream_Id"])
+                      for r in csv.DictReader(open(traces[0])) if "EpiLogits" in r["Kernel_Name"])
+        if rows:
+            main = rows[0][2]
+            for name, sel in (("on the caller's stream (the chunks' projections)", lambda st: st == main),
+                              ("on the side stream (re-projections)", lambda st: st != main)):
+                ds = [(e - b) / 1e6 for b, e, st in rows if sel(st)]
+                if ds:
+                    lines.append(f"EpiLogits launches {name}: {len(ds)}, average {sum(ds) / len(ds):.3f} ms, "
+                                 f"median {sorted(ds)[len(ds) // 2]:.3f} ms.")
+            lines += ["", "A re-projection with no row to project exits at once (0.02 ms when it runs alone); one "
+                      "that overlaps the next chunk's projection waits for compute-unit slots behind it, so its "
+                      "span is that projection's and its work nearly none.", ""]
+    out = os.path.join(ROOT, "profiles", f"{args.config}_fwd_bwd_kernel_stats.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
 
 
 def source_digest():
@@ -193,6 +322,11 @@ def _counter_rows(path, name_part):
             kn = r["Kernel_Name"]
             if name_part in kn and "gemm_kernel" in kn and "MainBf16" in kn:
                 out.append(float(r["Counter_Value"]))
+    # launches that did work: a re-projection with no row to project shares
+    # the projection's symbol but returns at once (a counter near zero)
+    if out and name_part is not None:
+        big = max(out)
+        out = [v for v in out if v >= 0.01 * big]
     return out
 
 
@@ -312,7 +446,13 @@ def main():
                     help="run a plain 1 GiB device copy (scale of the HBM byte counters) and exit")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write the HBM traffic summary of --traffic-kernel from rocprofv3 --pmc outputs and exit")
-    ap.add_argument("--traffic-kernel", default="dlogits")
+    ap.add_argument("--traffic-kernel", default="projection")
+    ap.add_argument("--mfma-busy-summary", metavar="DIR",
+                    help="write the matrix-pipe busy summary of --config from a rocprofv3 --pmc csv output "
+                         "directory and exit")
+    ap.add_argument("--kernel-stats-summary", metavar="DIR",
+                    help="write the kernel statistics summary of --config from a rocprofv3 --stats csv output "
+                         "directory and exit")
     ap.add_argument("--library-reference", action="store_true",
                     help="time the step's four products as plain torch.mm calls (vendor library) and exit")
     ap.add_argument("--side-outputs", action="store_true",
@@ -334,6 +474,12 @@ def main():
         sys.exit(2)
     if args.traffic_summary:
         traffic_summary(args)
+        return
+    if args.kernel_stats_summary:
+        kernel_stats_summary(args)
+        return
+    if args.mfma_busy_summary:
+        mfma_busy_summary(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",

@@ -31,7 +31,9 @@
  *
  * Logits are computed in fp32 from bf16 (or fp32) operands and are never
  * rounded to bf16 (align "architecture v2: proposal", section 5.4 A: an fp32
- * head needs fp32 output, not fp32 compute).  The backward forms
+ * head needs fp32 output, not fp32 compute).  The fp8 lane (STCE_DT_FP8)
+ * scores an e4m3 head: its products take e4m3 operands, scaled back to fp32
+ * logits (see stce_problem.weight_scale).  The backward forms
  * dz = g * (1[j == y] - q) / T with q the softmax on the support, rounds dz
  * to the operand dtype and runs the two gradient products on it (same
  * section: bf16 dlogits are what lets the dh product run on the matrix
@@ -74,7 +76,11 @@ extern "C" {
 
 typedef enum {
   STCE_DT_BF16 = 1, /* hidden and weight are bf16 (the fast path) */
-  STCE_DT_F32 = 2   /* hidden and weight are fp32 */
+  STCE_DT_F32 = 2,  /* hidden and weight are fp32 */
+  STCE_DT_FP8 = 3   /* the fp8 lane: weight of e4m3 codes [V, H] (uint8) with
+                       per-row fp32 scales stce_problem.weight_scale; hidden
+                       bf16 [T, H], quantized per row by the library; H a
+                       multiple of 16 */
 } stce_dtype;
 
 typedef enum {
@@ -156,7 +162,31 @@ typedef struct stce_problem {
                             two such as Ts = 0.5 divides exactly, so it gives
                             the bits of the per-row convention with every row
                             at Ts (barring overflow and subnormals).  Ignored
-                            without the flag. */
+                            without the flag.  Not with STCE_DT_FP8. */
+  const float *weight_scale; /* STCE_DT_FP8 only (ignored otherwise): [V] fp32 scales
+                            of the weight's rows, 4-byte aligned.  xorl pull
+                            request 74, "What this PR does" item 4, refuses an
+                            FP8 head and gives no formula for scoring one; this
+                            lane is one reading of it.  The weight is OCP e4m3
+                            ("e4m3fn": bias 7, 3 mantissa bits, largest finite
+                            448, no infinities; the NaN codes 0x7F / 0xFF must
+                            not occur) with W_deq[j, k] = weight_scale[j] *
+                            W8[j, k].  Each hidden row is quantized the same way,
+                            per row: a[t] = fl32(max_k |h[t, k]| / 448) (1 for
+                            an all-zero row) and h8[t, k] = e4m3(clamp(fl32(h[t,
+                            k] / a[t]), -448, 448)), nearest with ties to even
+                            (stce_fp8_quantize_rows).  Logits z = fl32(fl32(acc
+                            * weight_scale[j]) * a[t]) with acc the fp32
+                            matrix-core sum of the e4m3 products; then the
+                            temperature, support and logprob of the fp32 lane.
+                            Gradients pass both quantizations unchanged
+                            (straight through): dH = dz . W_deq and dW = dz^T .
+                            h_deq with h_deq = a h8, both products on the
+                            matrix cores with bf16 operands (dz, and the
+                            dequantized W_deq and h_deq, rounded to bf16);
+                            grad_hidden is bf16.  Neither the bf16 value lane,
+                            the pre-GEMM temperature nor the fused policy step
+                            take this lane. */
 } stce_problem;
 
 /* Per-row state size in bytes for T rows (STCE_STATE_BYTES_PER_ROW * T). */
@@ -240,7 +270,8 @@ stce_status stce_forward_with_side(const stce_problem *prob, float *logprob, voi
  * is out of support or whose metadata is invalid; with the scalar pre-GEMM
  * temperature dz = g (1[j == y] - q) and the hidden gradient is divided by
  * Ts) and writes
- *   grad_hidden [T, H] in the hidden dtype (overwritten; NULL = skip) and
+ *   grad_hidden [T, H] in the hidden dtype, bf16 for the fp8 lane
+ *                (overwritten; NULL = skip) and
  *   grad_weight [V, H] fp32 (overwritten, or added to when
  *                accumulate_grad_weight != 0; NULL = skip).
  * `prob` must describe the same inputs as the forward that wrote `state`
@@ -323,6 +354,8 @@ stce_status stce_decode_state(const void *host_state, int64_t nrows, stce_row_in
 #define STCE_KERNEL_CLASSIFY 13    /* backward: row classes (dense, sparse, empty) and their order */
 #define STCE_KERNEL_SPARSE_DW 14   /* backward: weight-gradient rows from the sparse rows' dz entries */
 #define STCE_KERNEL_SPARSE_DH 15   /* backward: hidden-gradient rows of the sparse and empty rows */
+#define STCE_KERNEL_REPROJECT 16   /* forward: projection of the rows whose candidates could not decide */
+#define STCE_KERNEL_QUANTIZE 17    /* fp8 lane: per-row e4m3 quantization of hidden rows */
 typedef struct stce_profile {
   int32_t capacity;
   int32_t count;
@@ -416,6 +449,17 @@ stce_status stce_fused_policy_step(const stce_problem *prob, const stce_pg_param
                                    void *state, float *loss, float *ratio, const stce_side_outputs *side,
                                    void *grad_hidden, float *grad_weight, int32_t accumulate_grad_weight,
                                    int64_t *dev_status, void *ws, size_t ws_bytes, void *stream);
+
+/* The fp8 lane's per-row quantization (stce_problem.weight_scale) of R rows
+ * of bf16 x [R, H] (H a multiple of 16, 16-byte aligned): scales[r] =
+ * fl32(max_k |x[r, k]| / 448) (1 for an all-zero row) and codes[r, k] =
+ * e4m3(clamp(fl32(x[r, k] / scales[r]), -448, 448)), nearest with ties to
+ * even.  The forward and backward apply it to the hidden rows; a caller may
+ * use it to produce a weight's codes and scales from a bf16 weight.  codes
+ * [R, H] uint8 (16-byte aligned) and scales [R] fp32 are the caller's.
+ * Enqueued on `stream`; host errors as stce_forward.  R = 0 does nothing. */
+stce_status stce_fp8_quantize_rows(const void *x, int64_t R, int64_t H, uint8_t *codes, float *scales,
+                                   void *stream);
 
 /* Human-readable name of a status code (static string). */
 const char *stce_status_string(stce_status status);

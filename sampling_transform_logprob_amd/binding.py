@@ -23,19 +23,21 @@ FLAG_VALID, FLAG_FILTERED, FLAG_IN_SUPPORT, FLAG_IGNORED = 1, 2, 4, 8
 PROBLEM_IGNORE_INDEX, PROBLEM_PRE_GEMM_TEMPERATURE, PROBLEM_BF16_LANE = 1, 2, 4
 LANES = {"fp32": 0, "bf16": PROBLEM_BF16_LANE}
 STATE_BYTES_PER_ROW = 32
-DT_BF16, DT_F32 = 1, 2
+DT_BF16, DT_F32, DT_FP8 = 1, 2, 3
+# dtypes a weight of e4m3 codes may come in (the fp8 lane)
+FP8_WEIGHT_DTYPES = (torch.uint8, torch.float8_e4m3fn)
 
 SYMBOLS = (
     "stce_state_bytes", "stce_workspace_bytes", "stce_forward", "stce_backward",
     "stce_scaled_logits", "stce_support_from_logits", "stce_support_workspace_bytes",
     "stce_decode_state", "stce_status_string", "stce_last_error", "stce_profile_attach", "stce_schedule",
     "stce_policy_loss", "stce_forward_with_side", "stce_fused_workspace_bytes", "stce_fused_policy_step",
-    "stce_recompute_keys", "stce_forward_noalloc", "stce_noalloc_scratch_bytes",
+    "stce_recompute_keys", "stce_forward_noalloc", "stce_noalloc_scratch_bytes", "stce_fp8_quantize_rows",
 )
 KERNEL_KINDS = {1: "validate", 2: "projection", 3: "select", 4: "dlogits", 5: "grad_weight",
                 6: "grad_hidden", 7: "transpose", 8: "partials", 9: "policy_loss", 10: "dz_keys",
                 11: "split_sum", 12: "prescale", 13: "classify", 14: "sparse_grad_weight",
-                15: "sparse_grad_hidden"}
+                15: "sparse_grad_hidden", 16: "reproject", 17: "quantize"}
 PG_OBJECTIVES = {"cispo": 1, "clip": 2}
 
 
@@ -47,6 +49,7 @@ class Problem(ctypes.Structure):
         ("temperature", ctypes.c_void_p), ("top_k", ctypes.c_void_p), ("top_p", ctypes.c_void_p),
         ("min_p", ctypes.c_void_p), ("chunk_rows", ctypes.c_int64), ("vocab_slice", ctypes.c_int64),
         ("ignore_index", ctypes.c_int64), ("pre_gemm_temperature", ctypes.c_float),
+        ("weight_scale", ctypes.c_void_p),
     ]
 
 
@@ -101,6 +104,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "stce_recompute_keys": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
         "stce_forward_noalloc": (ctypes.c_int, [P, vp, vp, vp, vp]),
         "stce_noalloc_scratch_bytes": (sz, []),
+        "stce_fp8_quantize_rows": (ctypes.c_int, [vp, i64, i64, vp, vp, vp]),
         "stce_scaled_logits": (ctypes.c_int, [P, i64, i64, vp, vp, sz, vp]),
         "stce_support_from_logits": (ctypes.c_int, [vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "stce_support_workspace_bytes": (sz, [i64, i64]),
@@ -153,33 +157,48 @@ def _meta(name, t, T, dtype, device):
 
 def make_problem(hidden, weight, target, temperature=None, top_k=None, top_p=None, min_p=None,
                  chunk_rows: int = 0, vocab_slice: int = 0, ignore_index: Optional[int] = None,
-                 pre_gemm_temperature: Optional[float] = None, lane: str = "fp32"):
+                 pre_gemm_temperature: Optional[float] = None, lane: str = "fp32",
+                 weight_scale: Optional[torch.Tensor] = None):
     """Checked ``stce_problem`` plus the tensors it points into (kept alive).
 
     ``temperature`` is the per-row tensor applied to the logits after the
     product; ``pre_gemm_temperature`` is instead one scalar applied to the
     hidden states before it (the two do not combine).  ``lane="bf16"`` runs
     the bf16 value program (bf16 keys; the logprob, still an fp32 tensor,
-    holds bf16 values, so ``.bfloat16()`` is exact)."""
+    holds bf16 values, so ``.bfloat16()`` is exact).  A weight of e4m3 codes
+    (``torch.uint8`` or ``torch.float8_e4m3fn``) with ``weight_scale`` (fp32
+    [V]) and bf16 hidden states selects the fp8 lane."""
     if lane not in LANES:
         raise ValueError(f"lane must be one of {tuple(LANES)}")
     if pre_gemm_temperature is not None and temperature is not None:
         raise ValueError("pass either a per-row temperature tensor or pre_gemm_temperature, not both")
     if hidden.dim() != 2 or weight.dim() != 2 or hidden.shape[1] != weight.shape[1]:
         raise ValueError(f"hidden [T, H] and weight [V, H] expected, got {tuple(hidden.shape)}, {tuple(weight.shape)}")
-    if hidden.dtype != weight.dtype:
-        raise TypeError(f"hidden ({hidden.dtype}) and weight ({weight.dtype}) must share a dtype")
-    dt = {torch.bfloat16: DT_BF16, torch.float32: DT_F32}.get(hidden.dtype)
-    if dt is None:
-        raise TypeError(
-            f"unsupported LM-head dtype {hidden.dtype}: scoring takes bf16 or fp32 hidden/weight "
-            "(keep a bf16/fp32 copy of a quantized lm_head.weight for scoring)")
+    if weight.dtype in FP8_WEIGHT_DTYPES:
+        if hidden.dtype != torch.bfloat16:
+            raise TypeError(f"the fp8 lane takes bf16 hidden states, got {hidden.dtype}")
+        if weight_scale is None:
+            raise ValueError("an e4m3 weight needs weight_scale (fp32 [V])")
+        dt = DT_FP8
+        weight = weight.view(torch.uint8)
+    else:
+        if weight_scale is not None:
+            raise ValueError("weight_scale is for an e4m3 weight only")
+        if hidden.dtype != weight.dtype:
+            raise TypeError(f"hidden ({hidden.dtype}) and weight ({weight.dtype}) must share a dtype")
+        dt = {torch.bfloat16: DT_BF16, torch.float32: DT_F32}.get(hidden.dtype)
+        if dt is None:
+            raise TypeError(
+                f"unsupported LM-head dtype {hidden.dtype}: scoring takes bf16 or fp32 hidden/weight, or an "
+                "e4m3 weight with per-row scales (the fp8 lane)")
     if hidden.device.type != "cuda" or weight.device != hidden.device:
         raise ValueError("hidden and weight must be on the same GPU")
     T, H = hidden.shape
     V = weight.shape[0]
     dev = hidden.device
     hidden, weight = hidden.contiguous(), weight.contiguous()
+    if weight_scale is not None:
+        weight_scale = _meta("weight_scale", weight_scale, V, torch.float32, dev)
     target = _meta("target", target, T, torch.int64, dev)
     if target is None:
         raise ValueError("target is required")
@@ -193,7 +212,9 @@ def make_problem(hidden, weight, target, temperature=None, top_k=None, top_p=Non
         flags |= PROBLEM_PRE_GEMM_TEMPERATURE
     prob = Problem(T, H, V, dt, flags, *[t.data_ptr() if t is not None else None for t in keep], chunk_rows,
                    vocab_slice, 0 if ignore_index is None else int(ignore_index),
-                   0.0 if pre_gemm_temperature is None else float(pre_gemm_temperature))
+                   0.0 if pre_gemm_temperature is None else float(pre_gemm_temperature),
+                   None if weight_scale is None else weight_scale.data_ptr())
+    keep.append(weight_scale)
     return prob, keep
 
 
@@ -224,14 +245,15 @@ def _raise_rows(status: torch.Tensor, what: str, tensors: dict) -> None:
 def forward(hidden, weight, target, temperature=None, top_k=None, top_p=None, min_p=None, *,
             chunk_rows: int = 0, check: bool = True, workspace: Optional[torch.Tensor] = None,
             side: bool = False, ignore_index: Optional[int] = None, pre_gemm_temperature: Optional[float] = None,
-            lane: str = "fp32"):
+            lane: str = "fp32", weight_scale: Optional[torch.Tensor] = None):
     """Selected logprob per row and the 32-byte-per-row state for backward.
 
     With ``side=True`` also returns a dict of the sweep's side outputs
     (``lse_full``, ``entropy_full``, ``entropy_support``, fp32 [T]).
     """
     prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, chunk_rows,
-                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane)
+                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane,
+                              weight_scale=weight_scale)
     T = prob.T
     fwd_b, _ = workspace_bytes(prob)
     dev = hidden.device
@@ -257,11 +279,13 @@ def forward(hidden, weight, target, temperature=None, top_k=None, top_p=None, mi
 
 def forward_noalloc(hidden, weight, target, temperature=None, top_k=None, top_p=None, min_p=None, *,
                     chunk_rows: int = 0, check: bool = True, ignore_index: Optional[int] = None,
-                    pre_gemm_temperature: Optional[float] = None, lane: str = "fp32"):
+                    pre_gemm_temperature: Optional[float] = None, lane: str = "fp32",
+                    weight_scale: Optional[torch.Tensor] = None):
     """``forward`` through ``stce_forward_noalloc``: the library's static
     scratch instead of a workspace (the outputs are still allocated here)."""
     prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, chunk_rows,
-                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane)
+                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane,
+                              weight_scale=weight_scale)
     T = prob.T
     dev = hidden.device
     logprob = torch.empty(T, dtype=torch.float32, device=dev)
@@ -278,10 +302,12 @@ def backward(hidden, weight, target, state, grad_logprob, temperature=None, top_
              min_p=None, *, need_hidden: bool = True, need_weight: bool = True,
              grad_weight: Optional[torch.Tensor] = None, accumulate_grad_weight: bool = False,
              vocab_slice: int = 0, workspace: Optional[torch.Tensor] = None, ignore_index: Optional[int] = None,
-             pre_gemm_temperature: Optional[float] = None, lane: str = "fp32"):
+             pre_gemm_temperature: Optional[float] = None, lane: str = "fp32",
+             weight_scale: Optional[torch.Tensor] = None):
     """(grad_hidden [T, H] in hidden's dtype, grad_weight [V, H] fp32)."""
     prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, 0, vocab_slice,
-                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane)
+                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane,
+                              weight_scale=weight_scale)
     T, H, V = prob.T, prob.H, prob.V
     dev = hidden.device
     if grad_logprob.shape != (T,) or grad_logprob.dtype != torch.float32 or grad_logprob.device != dev:
@@ -307,11 +333,13 @@ def backward(hidden, weight, target, state, grad_logprob, temperature=None, top_
 
 def recompute_keys(hidden, weight, target, state, grad_logprob, temperature=None, top_k=None, top_p=None,
                    min_p=None, *, vocab_slice: int = 0, ignore_index: Optional[int] = None,
-                   pre_gemm_temperature: Optional[float] = None, lane: str = "fp32"):
+                   pre_gemm_temperature: Optional[float] = None, lane: str = "fp32",
+                   weight_scale: Optional[torch.Tensor] = None):
     """fp32 keys [T, V] recomputed by the backward's product, exported by that
     launch itself (parity: they must equal the forward's bit for bit)."""
     prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, 0, vocab_slice,
-                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane)
+                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane,
+                              weight_scale=weight_scale)
     dev = hidden.device
     if state.numel() != prob.T * STATE_BYTES_PER_ROW or state.dtype != torch.uint8:
         raise ValueError("state must be the uint8 [T*32] tensor written by forward")
@@ -325,7 +353,8 @@ def recompute_keys(hidden, weight, target, state, grad_logprob, temperature=None
 
 
 def scaled_logits(hidden, weight, temperature=None, row0: int = 0, nrows: Optional[int] = None, *,
-                  pre_gemm_temperature: Optional[float] = None, lane: str = "fp32"):
+                  pre_gemm_temperature: Optional[float] = None, lane: str = "fp32",
+                  weight_scale: Optional[torch.Tensor] = None):
     """fp32 keys of rows [row0, row0 + nrows) from the forward's kernel:
     s = fl32(h W^T) / T per row, or fl32((h / Ts) W^T) with the scalar
     pre-GEMM temperature Ts; in the bf16 lane the bf16 keys."""
@@ -333,12 +362,25 @@ def scaled_logits(hidden, weight, temperature=None, row0: int = 0, nrows: Option
     nrows = T - row0 if nrows is None else nrows
     target = torch.zeros(T, dtype=torch.int64, device=hidden.device)
     prob, keep = make_problem(hidden, weight, target, temperature, pre_gemm_temperature=pre_gemm_temperature,
-                              lane=lane)
+                              lane=lane, weight_scale=weight_scale)
     fwd_b, _ = workspace_bytes(prob)
     ws = torch.empty(max(fwd_b, 1), dtype=torch.uint8, device=hidden.device)
     out = torch.empty(nrows, prob.V, dtype=torch.float32, device=hidden.device)
     _check(load().stce_scaled_logits(ctypes.byref(prob), row0, nrows, _ptr(out), _ptr(ws), ws.numel(), _stream()))
     return out
+
+
+def fp8_quantize_rows(x: torch.Tensor):
+    """(codes uint8 [R, H], scales fp32 [R]): the fp8 lane's per-row e4m3
+    quantization of bf16 rows ``x`` [R, H] (H a multiple of 16)."""
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or x.device.type != "cuda":
+        raise ValueError("x must be a bf16 [R, H] tensor on a GPU")
+    x = x.contiguous()
+    R, H = x.shape
+    codes = torch.empty(R, H, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(R, dtype=torch.float32, device=x.device)
+    _check(load().stce_fp8_quantize_rows(_ptr(x), R, H, _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales
 
 
 def support_from_logits(s, target, top_k=None, top_p=None, min_p=None, *, check: bool = True):

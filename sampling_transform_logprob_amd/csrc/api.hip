@@ -60,12 +60,16 @@ struct Layout {
   bool cand;
   size_t f_ckey, f_cid, f_cbound, f_fail, f_fcnt, f_fbh;
   size_t buf_ckey, buf_cid, buf_cbound;
+  // fp8 lane: the chunk's quantized hidden rows and their scales, per buffer
+  size_t f_h8, f_ha, buf_h8, buf_ha;
   int64_t Vs, Vsp, Tp;                                      // backward
   size_t b_flags, b_hT, b_WT, b_d, b_dT, b_dh, b_hs, bwd;
   // backward with row classes (bf16): counts, permutation, per-position
   // entry counters, classification scratch, permuted hidden rows, entry
   // lists, per-vocabulary-row counts and bucket offsets, scan scratch, buckets
   size_t b_cnt, b_perm, b_rowcnt, b_blk, b_hperm, b_list, b_cntj, b_offj, b_sums, b_bucket;
+  // fp8 lane: the quantized hidden rows in permuted order and their scales
+  size_t b_h8, b_ha;
 };
 
 // The scalar pre-GEMM temperature: the problem's hidden states are replaced
@@ -74,7 +78,13 @@ bool pre_gemm(const stce_problem* p) { return (p->flags & STCE_PROBLEM_PRE_GEMM_
 // The bf16 value lane: bf16 keys and a bf16 logprob.
 int bf16_lane(const stce_problem* p) { return (p->flags & STCE_PROBLEM_BF16_LANE) ? 1 : 0; }
 
-size_t elt_size(int dtype) { return dtype == STCE_DT_BF16 ? 2 : 4; }
+// The fp8 lane: e4m3 weight codes with per-row scales, bf16 hidden states
+// quantized per row by the library.
+bool fp8(const stce_problem* p) { return p->dtype == STCE_DT_FP8; }
+// bytes of a hidden (and hidden-gradient) element
+size_t elt_size(int dtype) { return dtype == STCE_DT_F32 ? 4 : 2; }
+// bytes of an element of the forward product's operands
+size_t op_size(int dtype) { return dtype == STCE_DT_FP8 ? 1 : elt_size(dtype); }
 size_t hs_bytes(const stce_problem* p) {
   return pre_gemm(p) ? align_up(elt_size(p->dtype) * (size_t)p->T * (size_t)p->H) : 0;
 }
@@ -87,14 +97,18 @@ stce_status check_shapes(const stce_problem* p) {
     return fail(STCE_E_ARG, "pre_gemm_temperature=%g must be finite and > 0", (double)p->pre_gemm_temperature);
   if ((p->flags & STCE_PROBLEM_IGNORE_INDEX) && p->ignore_index >= 0 && p->ignore_index < p->V)
     return fail(STCE_E_ARG, "ignore_index=%lld is a token id of [0, V)", (long long)p->ignore_index);
-  if (p->dtype != STCE_DT_BF16 && p->dtype != STCE_DT_F32)
+  if (p->dtype != STCE_DT_BF16 && p->dtype != STCE_DT_F32 && p->dtype != STCE_DT_FP8)
     return fail(STCE_E_UNSUPPORTED,
-                "unsupported operand dtype %d: hidden and weight must both be bf16 (STCE_DT_BF16) or fp32 "
-                "(STCE_DT_F32); quantized (e.g. fp8) LM heads are not scored -- keep an fp32/bf16 copy of "
-                "lm_head.weight for scoring",
+                "unsupported operand dtype %d: expected bf16 (STCE_DT_BF16), fp32 (STCE_DT_F32) or an e4m3 "
+                "weight with per-row scales and bf16 hidden states (STCE_DT_FP8)",
                 (int)p->dtype);
   if (bf16_lane(p) && p->dtype != STCE_DT_BF16)
     return fail(STCE_E_UNSUPPORTED, "the bf16 value lane (STCE_PROBLEM_BF16_LANE) takes bf16 hidden and weight");
+  if (fp8(p) && pre_gemm(p))
+    return fail(STCE_E_UNSUPPORTED,
+                "the fp8 lane takes per-row (post-GEMM) temperatures, not the scalar pre-GEMM temperature");
+  if (fp8(p) && p->H % 16 != 0)
+    return fail(STCE_E_ARG, "H=%lld: the fp8 lane takes a multiple of 16", (long long)p->H);
   // the weight-gradient product reads dz^T K-major with a row length of T
   // padded to 64, through a buffer resource of 256 such rows whose byte
   // count is 32-bit: 512 * round_up(T, 64) must stay below 2^31
@@ -139,13 +153,20 @@ Layout plan(const stce_problem* p, bool single_buffer = false) {
     L.f_cbound = o; o += L.nbuf * L.buf_cbound;
     L.f_fail = o;   o = align_up(o + 4 * (size_t)L.C);
     L.f_fcnt = o;   o = align_up(o + 4);
-    L.f_fbh = o;    o = align_up(o + es * (size_t)L.C * H);
+    L.f_fbh = o;    o = align_up(o + op_size(p->dtype) * (size_t)L.C * H);
+  }
+  if (fp8(p)) {
+    L.buf_h8 = align_up((size_t)L.C * H);
+    L.buf_ha = align_up(4 * (size_t)L.C);
+    L.f_h8 = o;     o += L.nbuf * L.buf_h8;
+    L.f_ha = o;     o += L.nbuf * L.buf_ha;
   }
   L.fwd = o;
 
   // bf16 keeps dz vocab-major only (the hidden gradient reads it MN-major);
-  // fp32, whose products take K-major operands only, keeps it both ways
-  const bool bf = p->dtype == STCE_DT_BF16;
+  // fp32, whose products take K-major operands only, keeps it both ways; the
+  // fp8 lane's gradient products are bf16 ones (dequantized operands)
+  const bool bf = p->dtype != STCE_DT_F32;
   if (p->vocab_slice > 0) {
     L.Vs = p->vocab_slice;
   } else {
@@ -167,7 +188,7 @@ Layout plan(const stce_problem* p, bool single_buffer = false) {
   L.b_WT = o;    o = align_up(o + es * (size_t)H * L.Vsp);
   L.b_d = o;     o = align_up(o + (bf ? 0 : es * (size_t)L.Tp * L.Vsp));
   L.b_dT = o;    o = align_up(o + es * (size_t)L.Vsp * L.Tp);
-  L.b_dh = o;    o = align_up(o + (p->dtype == STCE_DT_BF16 ? 4 * (size_t)T * H : 0));
+  L.b_dh = o;    o = align_up(o + (bf ? 4 * (size_t)T * H : 0));
   L.b_hs = o;    o = align_up(o + hs_bytes(p));
   if (bf) {
     L.b_cnt = o;    o = align_up(o + sizeof(GradCounts));
@@ -180,6 +201,10 @@ Layout plan(const stce_problem* p, bool single_buffer = false) {
     L.b_offj = o;   o = align_up(o + 4 * ((size_t)V + 1));
     L.b_sums = o;   o = align_up(o + 4 * scan_sums_ints(V));
     L.b_bucket = o; o = align_up(o + sizeof(SpEntry) * (size_t)T * NSP);
+  }
+  if (fp8(p)) {
+    L.b_h8 = o;     o = align_up(o + (size_t)T * H);
+    L.b_ha = o;     o = align_up(o + 4 * (size_t)T);
   }
   L.bwd = o;
   return L;
@@ -265,6 +290,8 @@ stce_status check_inputs(const stce_problem* p) {
   if (!aligned(p->hidden, 16) || !aligned(p->weight, 16))
     return fail(STCE_E_ARG, "hidden and weight must be 16-byte aligned");
   if (!aligned(p->target, 8)) return fail(STCE_E_ARG, "target must be 8-byte aligned");
+  if (fp8(p) && (!p->weight_scale || !aligned(p->weight_scale, 4)))
+    return fail(STCE_E_ARG, "the fp8 lane needs weight_scale, [V] fp32, 4-byte aligned");
   if ((p->temperature && !aligned(p->temperature, 4)) || (p->top_k && !aligned(p->top_k, 4)) ||
       (p->top_p && !aligned(p->top_p, 4)) || (p->min_p && !aligned(p->min_p, 4)))
     return fail(STCE_E_ARG, "metadata arrays must be 4-byte aligned");
@@ -431,6 +458,15 @@ stce_status forward_impl(const stce_problem* p, float* logprob, void* state, con
     a.dtype = p->dtype;
     a.W = p->weight;
     a.h = (const char*)hid + es * (size_t)c0 * p->H;
+    if (fp8(p)) {  // the chunk's hidden rows quantized into buffer b
+      uint8_t* h8 = at<uint8_t>(ws, L.f_h8 + b * L.buf_h8);
+      float* ha = at<float>(ws, L.f_ha + b * L.buf_ha);
+      if ((e = launch_fp8_quantize_rows((const bf16*)a.h, nullptr, nc, p->H, h8, ha, nullptr, st)))
+        return hip_fail(e, "quantize hidden rows");
+      a.h = h8;
+      a.row_scale = p->weight_scale;
+      a.col_scale = ha;
+    }
     a.H = p->H;
     a.V = p->V;
     a.rows = nc;
@@ -493,8 +529,7 @@ stce_status forward_impl(const stce_problem* p, float* logprob, void* state, con
       // chunk's buffer (the same kernel gives the same keys), and selected
       // from the keys
       void* fbh = at<char>(ws, L.f_fbh);
-      if ((e = launch_gather_rows_dev(p->dtype, (const char*)hid + es * (size_t)c0 * p->H, fail_rows, fail_cnt, nc,
-                                      p->H, fbh, ss)))
+      if ((e = launch_gather_rows_dev(p->dtype, a.h, fail_rows, fail_cnt, nc, p->H, fbh, ss)))
         return hip_fail(e, "gather rows to re-project");
       FwdArgs fa = a;
       fa.h = fbh;
@@ -600,10 +635,11 @@ stce_status stce_forward_noalloc(const stce_problem* p, float* logprob, void* st
 
 namespace {
 
-// The bf16 backward with row classes: classification of the rows (dense,
-// sparse, empty) and their permutation, the hidden rows gathered into that
-// order, per vocabulary slice the recompute product and the dense rows' two
-// products, then the sparse rows' products over their dz entries.
+// The bf16 (and fp8 lane) backward with row classes: classification of the
+// rows (dense, sparse, empty) and their permutation, the hidden rows gathered
+// into that order (fp8: quantized into it, and dequantized for the weight
+// gradient), per vocabulary slice the recompute product and the dense rows'
+// two products, then the sparse rows' products over their dz entries.
 stce_status backward_classed(const stce_problem* p, const Layout& L, const float* grad_logprob, const void* state,
                              const void* hid, float dh_div, void* grad_hidden, float* grad_weight,
                              int32_t accumulate_grad_weight, void* ws, hipStream_t st, float* keys_out) {
@@ -618,12 +654,25 @@ stce_status backward_classed(const stce_problem* p, const Layout& L, const float
   if ((e = launch_grad_classes((const RowState*)state, grad_logprob, p->T, at<int>(ws, L.b_blk), cnt, perm, rowcnt,
                                st)))
     return hip_fail(e, "row classes");
-  if ((e = launch_gather_rows(1, hid, perm, p->T, p->H, h_perm, st))) return hip_fail(e, "gather hidden rows");
+  uint8_t* h8_perm = fp8(p) ? at<uint8_t>(ws, L.b_h8) : nullptr;
+  float* ha = fp8(p) ? at<float>(ws, L.b_ha) : nullptr;
+  if (fp8(p))  // the hidden rows quantized in permuted order, and dequantized
+    e = launch_fp8_quantize_rows((const bf16*)hid, perm, p->T, p->H, h8_perm, ha, h_perm, st);
+  else
+    e = launch_gather_rows(1, hid, perm, p->T, p->H, h_perm, st);
+  if (e) return hip_fail(e, "gather hidden rows");
   if (want_w && (e = launch_fill_i32(cntj, p->V, 0, st))) return hip_fail(e, "clear counts");
   const int64_t nsl = ceil_div(p->V, L.Vs);
   for (int64_t si = 0; si < nsl; ++si) {
     ClassSliceArgs a{};
-    a.W = (const bf16*)p->weight;
+    if (fp8(p)) {
+      a.W8 = (const uint8_t*)p->weight;
+      a.w_scale = p->weight_scale;
+      a.h8_perm = h8_perm;
+      a.h_scale = ha;
+    } else {
+      a.W = (const bf16*)p->weight;
+    }
     a.h_perm = h_perm;
     a.perm = perm;
     a.cnt = cnt;
@@ -658,8 +707,9 @@ stce_status backward_classed(const stce_problem* p, const Layout& L, const float
   }
   if (keys_out) return STCE_OK;
   SparseGradArgs sa{};
-  sa.dtype = 1;
+  sa.dtype = fp8(p) ? DT_FP8 : DT_BF16;
   sa.W = p->weight;
+  sa.w_scale = p->weight_scale;
   sa.h_perm = h_perm;
   sa.perm = perm;
   sa.cnt = cnt;
@@ -707,7 +757,7 @@ stce_status backward_impl(const stce_problem* p, const float* grad_logprob, cons
   const void* hid = nullptr;
   float dh_div = 1.0f;
   if ((e = hidden_for_products(p, ws, L.b_hs, 0, p->T, &hid, &dh_div, st))) return hip_fail(e, "prescale hidden");
-  if (p->dtype == STCE_DT_BF16)
+  if (p->dtype != STCE_DT_F32)
     return backward_classed(p, L, grad_logprob, state, hid, dh_div, grad_hidden, grad_weight, accumulate_grad_weight,
                             ws, st, keys_out);
   if (grad_weight && !keys_out) {
@@ -790,6 +840,15 @@ stce_status stce_scaled_logits(const stce_problem* p, int64_t row0, int64_t nrow
     a.dtype = p->dtype;
     a.W = p->weight;
     a.h = (const char*)hid + es * (size_t)c0 * p->H;
+    if (fp8(p)) {
+      uint8_t* h8 = at<uint8_t>(ws, L.f_h8);
+      float* ha = at<float>(ws, L.f_ha);
+      hipError_t eq = launch_fp8_quantize_rows((const bf16*)a.h, nullptr, nc, p->H, h8, ha, nullptr, st);
+      if (eq) return hip_fail(eq, "quantize hidden rows");
+      a.h = h8;
+      a.row_scale = p->weight_scale;
+      a.col_scale = ha;
+    }
     a.H = p->H;
     a.V = p->V;
     a.rows = nc;
@@ -867,6 +926,7 @@ stce_status stce_fused_workspace_bytes(const stce_problem* p, size_t* bytes, siz
   stce_status s = check_shapes(p);
   if (s) return s;
   if (!bytes) return fail(STCE_E_ARG, "bytes is NULL");
+  if (fp8(p)) return fail(STCE_E_UNSUPPORTED, "the fused policy step takes bf16 or fp32 operands (not the fp8 lane)");
   *bytes = plan_fused(p).total;
   if (min_bytes) *min_bytes = plan_fused(p, 1).total;
   return STCE_OK;
@@ -880,6 +940,7 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
   if (s) return s;
   if ((s = check_inputs(p))) return s;
   if ((s = check_pg(pg))) return s;
+  if (fp8(p)) return fail(STCE_E_UNSUPPORTED, "the fused policy step takes bf16 or fp32 operands (not the fp8 lane)");
   if (!pg->advantages || !pg->old_logprob || !logprob || !state || !loss)
     return fail(STCE_E_ARG, "advantages, old_logprob, logprob, state and loss are required");
   if (!aligned(pg->advantages, 4) || !aligned(pg->old_logprob, 4) || !aligned(logprob, 4) || !aligned(loss, 4) ||
@@ -1033,6 +1094,19 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
     if ((e = launch_fused_chunk_grads(ga, st))) return hip_fail(e, "fused gradients");
   }
   return STCE_OK;
+}
+
+stce_status stce_fp8_quantize_rows(const void* x, int64_t R, int64_t H, uint8_t* codes, float* scales,
+                                   void* stream) {
+  if (R < 0 || R > INT32_MAX) return fail(STCE_E_ARG, "R=%lld out of range [0, 2^31)", (long long)R);
+  if (H < 16 || H % 16 != 0 || H > (1 << 20))
+    return fail(STCE_E_ARG, "H=%lld must be a positive multiple of 16 (<= 2^20)", (long long)H);
+  if (R == 0) return STCE_OK;
+  if (!x || !codes || !scales) return fail(STCE_E_ARG, "x, codes and scales are required");
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+    return fail(STCE_E_ARG, "x and codes must be 16-byte aligned, scales 4-byte aligned");
+  hipError_t e = launch_fp8_quantize_rows((const bf16*)x, nullptr, R, H, codes, scales, nullptr, (hipStream_t)stream);
+  return e ? hip_fail(e, "quantize rows") : STCE_OK;
 }
 
 stce_status stce_policy_loss(const stce_pg_params* pg, int64_t T, const float* logprob, float* loss,

@@ -12,6 +12,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// operand dtypes (stce_dtype): hidden and weight bf16, both fp32, or bf16
+// hidden with an e4m3 weight and per-row weight scales (the fp8 lane)
+enum : int { DT_BF16 = 1, DT_F32 = 2, DT_FP8 = 3 };
+
 // Row flags kept in the per-row state and in the forward's flag array.
 enum : uint32_t {
   ROW_VALID = 1u,      // metadata passed validation
@@ -103,6 +107,33 @@ __device__ inline uint64_t composite(uint32_t key, uint32_t id) {
 }
 __device__ inline uint32_t comp_key(uint64_t c) { return (uint32_t)(c >> 32); }
 __device__ inline uint32_t comp_id(uint64_t c) { return 0xffffffffu - (uint32_t)c; }
+
+// The OCP e4m3 format ("e4m3fn": sign, 4 exponent bits with bias 7, 3
+// mantissa bits, subnormals m 2^-9, largest finite value 448, no
+// infinities), written from its definition.  Encoding rounds to nearest
+// with ties to even and takes |x| <= 448; the matrix cores read the same
+// codes.
+constexpr float E4M3_MAX = 448.0f;
+
+__device__ inline uint32_t e4m3_encode(float x) {
+  const uint32_t s = (__builtin_bit_cast(uint32_t, x) >> 24) & 0x80u;
+  const float a = __builtin_fabsf(x);
+  if (a < 0x1p-6f) return s | (uint32_t)__builtin_rintf(a * 512.0f);  // 0 .. 8 (8: the smallest normal)
+  int e = (int)((__builtin_bit_cast(uint32_t, a) >> 23) & 0xffu) - 127;
+  float q = __builtin_rintf(__builtin_ldexpf(a, 3 - e));                // 8 .. 16, exact scaling
+  if (q == 16.0f) {
+    ++e;
+    q = 8.0f;
+  }
+  return s | (uint32_t)((e + 7) << 3) | ((uint32_t)q - 8u);
+}
+
+__device__ inline float e4m3_decode(uint32_t c) {
+  const int e = (int)((c >> 3) & 15u);
+  const float m = (float)(c & 7u);
+  const float v = e ? __builtin_ldexpf(1.0f + m * 0.125f, e - 7) : m * 0x1p-9f;
+  return (c & 0x80u) ? -v : v;
+}
 
 __host__ __device__ constexpr int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -89,6 +89,24 @@ __device__ inline void keys_column(AccTile& acc, int j, float t, bool bf16_lane)
 
 constexpr float LOG2E = 1.4426950408889634f;
 
+// fp8 lane: the products of e4m3 codes scaled back, z = fl32(fl32(acc sW[m])
+// a[n]), for the lane's rows of column j; sw[i][r] holds sW of row
+// acc_row(wm, i, r, quad) (no contraction: each product is rounded).
+__device__ inline void load_row_scales(const float* row_scale, int mb, int quad, int rows, float (&sw)[ACC_I][ACC_R]) {
+#pragma unroll
+  for (int i = 0; i < ACC_I; ++i) {
+    const int m = mb + i * 16 + quad * 4;
+#pragma unroll
+    for (int r = 0; r < ACC_R; ++r) sw[i][r] = m + r < rows ? row_scale[m + r] : 0.0f;
+  }
+}
+__device__ inline void scale_column_fp8(AccTile& acc, int j, const float (&sw)[ACC_I][ACC_R], float a) {
+#pragma unroll
+  for (int i = 0; i < ACC_I; ++i)
+#pragma unroll
+    for (int r = 0; r < ACC_R; ++r) acc[i][j][r] = __fmul_rn(__fmul_rn(acc[i][j][r], sw[i][r]), a);
+}
+
 // ---------------------------------------------------------------------------
 // Forward projection epilogue.  M = vocabulary, N = tokens of the chunk.
 // For each (token, 256-wide vocabulary tile): applies the temperature,
@@ -127,6 +145,10 @@ struct EpiLogits {
   // and only columns below *n_dev exist (null: identity, N)
   const int* rowmap = nullptr;
   const int* n_dev = nullptr;
+  // fp8 lane: per vocabulary row weight scales [V] and per token row scales
+  // (indexed like the metadata), or null
+  const float* row_scale = nullptr;
+  const float* col_scale = nullptr;
   static constexpr int LDS_BYTES = 2 * GN * 5 * 4;  // cross-wave merge
 
   __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem, char*) const {
@@ -139,7 +161,7 @@ struct EpiLogits {
     // Every per-token load comes first: loads and stores share one in-order
     // counter, so a load issued after a column's key stores would make the
     // wave wait for all of them to complete before the next column.
-    float tv[ACC_J];
+    float tv[ACC_J], av[ACC_J];
     bool stv[ACC_J], cnd[ACC_J];
     int64_t tgv[ACC_J];
 #pragma unroll
@@ -149,13 +171,17 @@ struct EpiLogits {
       const int rn = (nv && rowmap) ? rowmap[n] : n;
       const uint32_t f = (nv && flags) ? flags[rn] : 0u;
       tv[j] = (nv && temp) ? temp[rn] : 1.0f;
+      av[j] = (nv && col_scale) ? col_scale[rn] : 1.0f;
       cnd[j] = nv && !store_all && ckey && (f & ROW_CAND);
       stv[j] = nv && (store_all || ((f & ROW_FILTERED) && !cnd[j]));
       tgv[j] = (nv && target && s_y) ? target[rn] : -1;
     }
+    float sw[ACC_I][ACC_R];
+    if (row_scale) load_row_scales(row_scale, mb, quad, V, sw);
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) {
       const int n = n0 + acc_col(wn, j, col);
+      if (row_scale) scale_column_fp8(acc, j, sw, av[j]);
       keys_column(acc, j, tv[j], bf16_lane);
       float mx = -STCE_INF, mn = STCE_INF;
       if (full) {
@@ -467,6 +493,10 @@ struct EpiGrad {
   int* cntj;                // [V] or null (no weight gradient)
   float* keys_out = nullptr;  // parity export of the keys, [rows][ld_keys] (null in production)
   int64_t ld_keys = 0;
+  // fp8 lane: weight scales of the slice's rows [Vs] and per-row hidden
+  // scales [rows] (indexed by row, not position), or null
+  const float* row_scale = nullptr;
+  const float* col_scale = nullptr;
   static constexpr int LDS_BYTES = 128 * GN * 2;
 
   __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem, char* smem1) const {
@@ -477,7 +507,7 @@ struct EpiGrad {
     const bool any_dense = n0 < nd;  // uniform over the workgroup
     bf16* stg = (bf16*)(wmu ? smem1 : smem);
     // every per-token load first (loads and stores share one in-order counter)
-    float tv[ACC_J], cv[ACC_J], thr[ACC_J], nlv[ACC_J];
+    float tv[ACC_J], cv[ACC_J], thr[ACC_J], nlv[ACC_J], av[ACC_J];
     int idt[ACC_J], yv[ACC_J], rowv[ACC_J];
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) {
@@ -494,15 +524,19 @@ struct EpiGrad {
       }
       rowv[j] = t;
       tv[j] = tt;
+      av[j] = (t >= 0 && col_scale) ? col_scale[t] : 1.0f;
       cv[j] = c;
       thr[j] = (rs.flags & ROW_FILTERED) ? key_value(rs.key_thr) : -STCE_INF;
       idt[j] = rs.id_thr;
       nlv[j] = -rs.lse_s * LOG2E;
       yv[j] = y;
     }
+    float sw[ACC_I][ACC_R];
+    if (row_scale) load_row_scales(row_scale, m0 + wmu * 128, quad, Vs, sw);
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) {
       const int n = n0 + acc_col(wn, j, col);
+      if (row_scale) scale_column_fp8(acc, j, sw, av[j]);
       keys_column(acc, j, tv[j], bf16_lane);
       if (keys_out && rowv[j] >= 0) {
 #pragma unroll

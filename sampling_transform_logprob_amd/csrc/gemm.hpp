@@ -356,6 +356,113 @@ struct MainBf16T {
 using MainBf16 = MainBf16T<false, false>;
 
 // ---------------------------------------------------------------------------
+// fp8 main loop (MFMA): e4m3 operands, both K-major, C[m, n] = sum_k A[m, k]
+// B[n, k] with the 16x16x128 fp8 matrix instruction (twice the bf16 rate).
+// A k-tile is 128 elements = 128 bytes of a row, the bf16 loop's tile row
+// size, so the loads, the LDS layout and its swizzle are the bf16 loop's; a
+// k-tile is one k-step, whose fragment per 16-row block is 32 bytes a lane
+// (chunks 2q and 2q + 1 of the row, q = lane / 16).  Both operands take the
+// same byte-to-lane mapping, so every product pairs equal k.  The 32 MFMAs
+// of a k-tile (each 4 times the work of a bf16 16x16x32) cover the next
+// tile's fragment reads of the other wave of the SIMD; the loads of tile
+// kt + 2 go out right after the barrier that frees the stage of tile kt.
+// K (bytes) is a multiple of 16; chunks past K read as zeros.
+// ---------------------------------------------------------------------------
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+struct MainFp8 {
+  static constexpr int ROWB = 128;
+  static constexpr int TILEB = GM * ROWB;
+  static constexpr int STAGEB = 2 * TILEB;
+  static constexpr int LPW = 4;
+  static constexpr int DYN_LDS = 0;
+  static constexpr int EPI_LDS_MAX = STAGEB;
+  const uint8_t* A;
+  int64_t lda;  // bytes
+  int M;
+  const uint8_t* B;
+  int64_t ldb;
+  int N;
+  int K;        // bytes (elements)
+
+  __device__ inline void limit_k(int k) { K = min(K, k); }
+  __device__ static char* stage0() { return MainBf16::stage0(); }
+  __device__ static char* stage1() { return MainBf16::stage1(); }
+  __device__ static char* epilogue_lds(char*) { return stage0(); }
+  __device__ static char* epilogue_lds1(char*) { return stage1(); }
+
+  __device__ inline void run(AccTile& acc, int m0, int n0, char*) const {
+    char* const S0 = stage0();
+    char* const S1 = stage1();
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = w >> 2, wn = w & 3;
+    const int rowsA = min(M - m0, GM), rowsB = min(N - n0, GN);
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)m0 * lda), (short)0, rowsA * (int)lda, RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(B + (int64_t)n0 * ldb), (short)0, rowsB * (int)ldb, RSRC_WORD3);
+    const int lrow = lane >> 3, lpc = lane & 7;
+    const int ce = lpc ^ lds_swz(lrow), co = lpc ^ lds_swz(lrow + 8);
+    const int rA = (w * LPW * 8 + lrow) * (int)lda, rB = (w * LPW * 8 + lrow) * (int)ldb;
+    const int stepA = 8 * (int)lda, stepB = 8 * (int)ldb;
+    const int nk = (K + ROWB - 1) / ROWB;
+    auto issue = [&](int sg, int kt) __attribute__((always_inline)) {
+      char* st = (sg ? S1 : S0) + w * LPW * 1024;
+      const int k0 = kt * ROWB;
+      const bool ine = k0 + ce * 16 < K, ino = k0 + co * 16 < K;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const bool in = (i & 1) ? ino : ine;
+        const int c16 = ((i & 1) ? co : ce) * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, STCE_LDS(st + i * 1024), 16, in ? rA + i * stepA + c16 : 0x7ffffff0,
+                                                 k0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, STCE_LDS(st + TILEB + i * 1024), 16,
+                                                 in ? rB + i * stepB + c16 : 0x7ffffff0, k0, 0, 0);
+      }
+    };
+    const int frow = lane & 15, fq = lane >> 4, sw = lds_swz(frow);
+    const int offA = (wm * 128 + frow) * ROWB, offB = TILEB + (wn * 64 + frow) * ROWB;
+    const int c0 = ((2 * fq) ^ sw) * 16, c1 = ((2 * fq + 1) ^ sw) * 16;
+    auto frag = [&](const char* base) __attribute__((always_inline)) {
+      const u32x4 lo = *(const u32x4*)(base + c0), hi = *(const u32x4*)(base + c1);
+      return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto tile = [&](int sg, int kt) __attribute__((always_inline)) {
+      const char* st = sg ? S1 : S0;
+      i32x8 fb[ACC_J];
+#pragma unroll
+      for (int j = 0; j < ACC_J; ++j) fb[j] = frag(st + offB + j * 16 * ROWB);
+#pragma unroll
+      for (int i = 0; i < ACC_I; ++i) {
+        const i32x8 fa = frag(st + offA + i * 16 * ROWB);
+#pragma unroll
+        for (int j = 0; j < ACC_J; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+      }
+      // tile kt + 1 has landed and every wave is done reading stage sg:
+      // refill it with tile kt + 2
+      __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
+      __syncthreads();
+      issue(sg, kt + 2);
+    };
+    issue(0, 0);
+    issue(1, 1);
+    __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
+    __syncthreads();
+    // an even number of k-tiles (an odd count gets one all-zero tile) so that
+    // every read and load names its stage at compile time
+    const int nk2 = (nk + 1) & ~1;
+    for (int kt = 0; kt < nk2; kt += 2) {
+      tile(0, kt);
+      tile(1, kt + 1);
+    }
+    __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
+    __syncthreads();  // the epilogue may reuse the LDS
+  }
+};
+
+// ---------------------------------------------------------------------------
 // fp32 main loop (plain fused multiply-adds, same accumulator layout).  Used
 // for fp32 operands, where shapes are small; each output element accumulates
 // its k terms in order with one fma each.

@@ -125,8 +125,71 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* in, int
   }
 }
 
-// out[r] = in[rowmap[r]] for r < *n_dev: rows of H elements, H a multiple of
-// 8 (16-byte rows); a grid-stride loop over nmax rows.
+// fp8 lane: one workgroup per hidden row t = perm[n] (n without perm): its
+// absolute maximum, the row scale a[t] = fl32(amax / 448) (1 for a zero row),
+// the e4m3 codes q[n, :] of clamp(fl32(h[t, :] / a[t]), +-448) and, with deq,
+// the dequantized row deq[n, :] = bf16(fl32(a[t] e4m3(q[n, :]))); 8 elements
+// per thread at a time.
+__global__ __launch_bounds__(256) void fp8_quantize_rows_kernel(const bf16* h, int64_t H, const int* perm,
+                                                                uint8_t* q, float* scale, bf16* deq) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  __shared__ float red[4];
+  const int64_t n = blockIdx.x;
+  const int64_t t = perm ? perm[n] : n;
+  const bf16* hr = h + t * H;
+  float mx = 0.0f;
+  for (int64_t c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    const bf16x8 v = *(const bf16x8*)(hr + c);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mx = fmaxf(mx, __builtin_fabsf((float)v[k]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float a = mx > 0.0f ? mx / E4M3_MAX : 1.0f;
+  if (threadIdx.x == 0) scale[t] = a;
+  uint8_t* qr = q + n * H;
+  for (int64_t c = threadIdx.x * 8; c < H; c += 256 * 8) {
+    const bf16x8 v = *(const bf16x8*)(hr + c);
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float x = fminf(fmaxf((float)v[k] / a, -E4M3_MAX), E4M3_MAX);
+      w[k >> 2] |= e4m3_encode(x) << (8 * (k & 3));
+    }
+    *(u32x2*)(qr + c) = u32x2{w[0], w[1]};
+    if (deq) {
+      bf16x8 o;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = (bf16)__fmul_rn(a, e4m3_decode((w[k >> 2] >> (8 * (k & 3))) & 0xffu));
+      *(bf16x8*)(deq + n * H + c) = o;
+    }
+  }
+}
+
+// out[c][r] = bf16(fl32(scale[r] e4m3(in[r][c]))) through a 64 x 64 LDS tile;
+// zeros for R <= r < R_pad.
+__global__ void fp8_dequant_transpose_kernel(const uint8_t* in, const float* scale, int64_t ld_in, int64_t R,
+                                             int64_t Cc, bf16* out, int64_t ld_out, int64_t R_pad, const int* skip) {
+  if (skip && *skip == 0) return;
+  __shared__ bf16 tile[64][65];
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < R && c < Cc) ? (bf16)__fmul_rn(scale[r], e4m3_decode(in[r * ld_in + c])) : (bf16)0.0f;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < Cc && r < R_pad) out[c * ld_out + r] = tile[tx][i];
+  }
+}
+
+// out[r] = in[rowmap[r]] for r < *n_dev: rows of H elements, 16-byte rows;
+// a grid-stride loop over nmax rows.
 template <class E>
 __global__ __launch_bounds__(256) void gather_rows_dev_kernel(const E* in, const int* rowmap, const int* n_dev,
                                                               int64_t nmax, int64_t H, E* out) {
@@ -461,12 +524,31 @@ hipError_t launch_prescale(int dtype, const void* in, int64_t n, float t, void* 
   return hipGetLastError();
 }
 
+hipError_t launch_fp8_quantize_rows(const bf16* h, const int* perm, int64_t T, int64_t H, uint8_t* q, float* a,
+                                    bf16* deq, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  ProfScope ps(KIND_QUANTIZE, s);
+  hipLaunchKernelGGL(fp8_quantize_rows_kernel, dim3((unsigned)T), dim3(256), 0, s, h, H, perm, q, a, deq);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_dequant_transpose(const uint8_t* in, const float* scale, int64_t ld_in, int64_t R, int64_t Cc,
+                                        bf16* out, int64_t ld_out, int64_t R_pad, const int* skip, hipStream_t s) {
+  ProfScope ps(KIND_TRANSPOSE, s);
+  hipLaunchKernelGGL(fp8_dequant_transpose_kernel, dim3((unsigned)ceil_div(R_pad, 64), (unsigned)ceil_div(Cc, 64)),
+                     dim3(256), 0, s, in, scale, ld_in, R, Cc, out, ld_out, R_pad, skip);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather_rows_dev(int dtype, const void* in, const int* rowmap, const int* n_dev, int64_t nmax,
                                   int64_t H, void* out, hipStream_t s) {
-  const int64_t total = nmax * H / (dtype == 1 ? 8 : 4);
+  const int64_t total = nmax * H / (dtype == 1 ? 8 : dtype == 3 ? 16 : 4);
   const unsigned blocks = (unsigned)(ceil_div(total, 256) < 2048 ? ceil_div(total, 256) : 2048);
   if (blocks == 0) return hipSuccess;
-  if (dtype == 1)
+  if (dtype == 3)
+    hipLaunchKernelGGL(gather_rows_dev_kernel<uint8_t>, dim3(blocks), dim3(256), 0, s, (const uint8_t*)in, rowmap,
+                       n_dev, nmax, H, (uint8_t*)out);
+  else if (dtype == 1)
     hipLaunchKernelGGL(gather_rows_dev_kernel<bf16>, dim3(blocks), dim3(256), 0, s, (const bf16*)in, rowmap, n_dev,
                        nmax, H, (bf16*)out);
   else
@@ -514,10 +596,18 @@ hipError_t fwd_projection_impl(const FwdArgs& a, hipStream_t s) {
   ep.cld = a.cld;
   ep.rowmap = a.rowmap;
   ep.n_dev = a.n_dev;
+  // a re-projection's column tiles past the device count of its rows do
+  // nothing (an empty launch: every workgroup returns at once)
   DynLimits dyn{};
   dyn.n_lim = a.n_dev;
   const int64_t tm = ceil_div(a.V, GM), tn = ceil_div(a.rows, GN);
-  ProfScope ps(2, s);
+  ep.row_scale = a.row_scale;
+  ep.col_scale = a.col_scale;
+  ProfScope ps(a.n_dev ? KIND_REPROJECT : KIND_PROJECTION, s);
+  if (a.dtype == DT_FP8) {
+    MainFp8 mn{(const uint8_t*)a.W, a.H, (int)a.V, (const uint8_t*)a.h, a.H, (int)a.rows, (int)a.H};
+    return launch_gemm(mn, ep, tm, tn, s, dyn);
+  }
   if (a.dtype == 1) {
     MainBf16 mn{(const bf16*)a.W, a.H, (int)a.V, (const bf16*)a.h, a.H, (int)a.rows, (int)a.H};
     return launch_gemm(mn, ep, tm, tn, s, dyn);
@@ -651,11 +741,18 @@ hipError_t launch_class_slice(const ClassSliceArgs& a, hipStream_t s) {
     ep.cntj = a.keys_out ? nullptr : a.cntj;
     ep.keys_out = a.keys_out;
     ep.ld_keys = a.ld_keys;
-    MainBf16 mn{a.W + a.v0 * a.H, a.H, (int)a.vs, a.h_perm, a.H, (int)a.T, (int)a.H};
     DynLimits dyn{};
     dyn.n_lim = a.keys_out ? nullptr : &a.cnt->active;
     ProfScope ps(KIND_DLOGITS, s);
-    e = launch_gemm(mn, ep, ceil_div(a.vsp, GM), ceil_div(a.Tp, GN), s, dyn);
+    if (a.W8) {  // fp8 lane: the forward's e4m3 product and scaling
+      ep.row_scale = a.w_scale + a.v0;
+      ep.col_scale = a.h_scale;
+      MainFp8 mn{a.W8 + a.v0 * a.H, a.H, (int)a.vs, a.h8_perm, a.H, (int)a.T, (int)a.H};
+      e = launch_gemm(mn, ep, ceil_div(a.vsp, GM), ceil_div(a.Tp, GN), s, dyn);
+    } else {
+      MainBf16 mn{a.W + a.v0 * a.H, a.H, (int)a.vs, a.h_perm, a.H, (int)a.T, (int)a.H};
+      e = launch_gemm(mn, ep, ceil_div(a.vsp, GM), ceil_div(a.Tp, GN), s, dyn);
+    }
     if (e != hipSuccess) return e;
   }
   if (a.keys_out) return hipSuccess;
@@ -673,7 +770,11 @@ hipError_t launch_class_slice(const ClassSliceArgs& a, hipStream_t s) {
   // 3. dense rows' hidden gradient, summed over slices in order:
   //    dH^T[:, n] += W_slice^T . dz^T[:, n] for dense positions n, written to row perm[n]
   if (a.grad_hidden) {
-    e = launch_transpose_bf16(a.W + a.v0 * a.H, a.H, a.vs, a.H, a.WT, a.ld_d, a.vsp, s, &a.cnt->dense);
+    if (a.W8)  // fp8 lane: the dequantized weight, rounded to bf16, as the product's operand
+      e = launch_fp8_dequant_transpose(a.W8 + a.v0 * a.H, a.w_scale + a.v0, a.H, a.vs, a.H, a.WT, a.ld_d, a.vsp,
+                                       &a.cnt->dense, s);
+    else
+      e = launch_transpose_bf16(a.W + a.v0 * a.H, a.H, a.vs, a.H, a.WT, a.ld_d, a.vsp, s, &a.cnt->dense);
     if (e != hipSuccess) return e;
     EpiAccumT<bf16> ep{a.dh_sum, a.H, (bf16*)a.grad_hidden, (int)a.H, (int)a.T, a.first, a.last, a.dh_div};
     ep.rowmap = a.perm;

@@ -10,7 +10,8 @@ namespace stce {
 enum : int {
   KIND_VALIDATE = 1, KIND_PROJECTION = 2, KIND_SELECT = 3, KIND_DLOGITS = 4, KIND_GRAD_WEIGHT = 5,
   KIND_GRAD_HIDDEN = 6, KIND_TRANSPOSE = 7, KIND_PARTIALS = 8, KIND_POLICY_LOSS = 9, KIND_DZ_KEYS = 10,
-  KIND_SPLIT_SUM = 11, KIND_PRESCALE = 12, KIND_CLASSIFY = 13, KIND_SPARSE_DW = 14, KIND_SPARSE_DH = 15
+  KIND_SPLIT_SUM = 11, KIND_PRESCALE = 12, KIND_CLASSIFY = 13, KIND_SPARSE_DW = 14, KIND_SPARSE_DH = 15,
+  KIND_REPROJECT = 16, KIND_QUANTIZE = 17
 };
 
 // Launch-timing hook (no-op unless a profile is attached to this thread).
@@ -74,11 +75,28 @@ struct FwdArgs {
   // columns from *n_dev on do nothing
   const int* rowmap;
   const int* n_dev;
+  // fp8 lane (dtype 3): W holds e4m3 codes, h the chunk's quantized hidden
+  // rows; weight scales [V] and the chunk's row scales (indexed like temp)
+  const float* row_scale;
+  const float* col_scale;
 };
 hipError_t launch_fwd_projection(const FwdArgs& a, hipStream_t s);
 
+// fp8 lane: for n < T, row t = perm[n] (t = n without perm) of the bf16
+// hidden states h (H a multiple of 16): a[t] = fl32(max_k |h[t, k]| / 448)
+// (1 for a zero row), q[n, k] = e4m3(clamp(fl32(h[t, k] / a[t]), -448, 448))
+// and, when deq is not null, deq[n, k] = bf16(fl32(a[t] e4m3(q[n, k]))).
+hipError_t launch_fp8_quantize_rows(const bf16* h, const int* perm, int64_t T, int64_t H, uint8_t* q, float* a,
+                                    bf16* deq, hipStream_t s);
+// out[c][r] = bf16(fl32(scale[r] * e4m3(in[r][c]))) for r < R, zeros for
+// R <= r < R_pad (the transposed dequantized weight of a slice); nothing when
+// skip is not null and *skip == 0.
+hipError_t launch_fp8_dequant_transpose(const uint8_t* in, const float* scale, int64_t ld_in, int64_t R, int64_t Cc,
+                                        bf16* out, int64_t ld_out, int64_t R_pad, const int* skip, hipStream_t s);
+
 // out[r] = in[rowmap[r]] for r < *n_dev (rows of H elements of the dtype, 1
-// bf16 or 2 fp32); rows up to nmax are covered by the launch.
+// bf16, 2 fp32 or 3 e4m3 codes, 16-byte rows); rows up to nmax are covered
+// by the launch.
 hipError_t launch_gather_rows_dev(int dtype, const void* in, const int* rowmap, const int* n_dev, int64_t nmax,
                                   int64_t H, void* out, hipStream_t s);
 
@@ -135,7 +153,14 @@ hipError_t launch_exclusive_scan(const int* x, int64_t n, int* sums, int* y, hip
 // One vocabulary slice of the classed backward: the recompute product (dense
 // rows' dz^T, sparse rows' entries) and the dense rows' two products.
 struct ClassSliceArgs {
-  const bf16* W;        // full weight [V][H]
+  const bf16* W;        // full weight [V][H] (bf16)
+  // fp8 lane: the weight's e4m3 codes [V][H] and scales [V], the hidden
+  // rows' codes in permuted order [T][H] and their scales [rows] (h_perm then
+  // holds the dequantized hidden rows, the weight gradient's operand)
+  const uint8_t* W8;
+  const float* w_scale;
+  const uint8_t* h8_perm;
+  const float* h_scale;
   const bf16* h_perm;   // [T][H] hidden rows in permuted order
   const int* perm;
   const GradCounts* cnt;
@@ -165,8 +190,9 @@ hipError_t launch_class_slice(const ClassSliceArgs& a, hipStream_t s);
 // per-vocabulary-row buckets of the entries, the hidden gradient of every
 // sparse and empty position.
 struct SparseGradArgs {
-  int dtype;
+  int dtype;            // 1 bf16, 2 fp32, 3 fp8 lane (W e4m3 codes with w_scale)
   const void* W;        // [V][H]
+  const float* w_scale; // [V] (fp8 lane)
   const void* h_perm;   // [T][H] permuted rows
   const int* perm;
   const GradCounts* cnt;

@@ -268,16 +268,34 @@ __device__ inline void load8(const E* p, float (&x)[8]) {
   }
 }
 
+// fp8 lane: x[k] = fl32(sc * e4m3(p[k])), the dequantized weight element.
+__device__ inline void load8(const uint8_t* p, float sc, float (&x)[8]) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 w = *(const u32x2*)p;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) x[k] = __fmul_rn(sc, e4m3_decode((w[k >> 2] >> (8 * (k & 3))) & 0xffu));
+}
+
+template <class E>
+__device__ inline void load8_row(const E* X, const float* xs, int64_t row, int64_t H, int64_t c0, float (&x)[8]) {
+  if constexpr (sizeof(E) == 1)
+    load8(X + row * H + c0, xs[row], x);
+  else
+    load8(X + row * H + c0, x);
+}
+
 // acc[k] += e.v * X[e.idx, c0 + k] over the ordered entries e = ord[0 .. ne),
 // in that order, fp32 fmas; the rows of eight entries are loaded before their
 // fmas so that the loads overlap (the order of the sums is unchanged).
+// X of e4m3 codes takes the per-row scales xs.
 template <class E>
-__device__ inline void ordered_sum(const SpEntry* ord, int ne, const E* X, int64_t H, int64_t c0, float (&acc)[8]) {
+__device__ inline void ordered_sum(const SpEntry* ord, int ne, const E* X, int64_t H, int64_t c0, float (&acc)[8],
+                                   const float* xs = nullptr) {
   int r = 0;
   for (; r + 8 <= ne; r += 8) {
     float x[8][8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) load8(X + (int64_t)ord[r + u].idx * H + c0, x[u]);
+    for (int u = 0; u < 8; ++u) load8_row(X, xs, (int64_t)ord[r + u].idx, H, c0, x[u]);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const float v = ord[r + u].v;
@@ -287,7 +305,7 @@ __device__ inline void ordered_sum(const SpEntry* ord, int ne, const E* X, int64
   }
   for (; r < ne; ++r) {
     float x[8];
-    load8(X + (int64_t)ord[r].idx * H + c0, x);
+    load8_row(X, xs, (int64_t)ord[r].idx, H, c0, x);
     const float v = ord[r].v;
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(v, x[k], acc[k]);
@@ -305,15 +323,9 @@ constexpr int WIN = 4096;         // token positions per window beyond that
 // else writes them.  Buckets larger than ORDER_CAP entries are summed window
 // by window of WIN positions, each entry placed at its position in LDS.
 template <class E>
-__global__ __launch_bounds__(256) void sparse_dw_kernel(const int* off, const SpEntry* bucket, const E* h, int64_t H,
-                                                        const GradCounts* cnt, int accumulate, float* dW,
-                                                        int64_t T) {
-  __shared__ SpEntry ord[ORDER_CAP];
-  __shared__ SpEntry raw[ORDER_CAP];
-  __shared__ float win[WIN];
-  const int64_t j = blockIdx.x;
+__device__ inline void sparse_dw_row(int64_t j, const int* off, const SpEntry* bucket, const E* h, int64_t H,
+                                     bool from_mem, float* dW, int64_t T, SpEntry* ord, SpEntry* raw, float* win) {
   const int o0 = off[j], ne = off[j + 1] - o0;
-  const bool from_mem = accumulate || cnt->dense > 0;
   float* row = dW + j * H;
   if (ne == 0) {
     if (!from_mem)
@@ -386,21 +398,38 @@ __global__ __launch_bounds__(256) void sparse_dw_kernel(const int* off, const Sp
   }
 }
 
+// Weight-gradient rows j = blockIdx.x, + gridDim.x, ... (sparse_dw_row).
+template <class E>
+__global__ __launch_bounds__(256) void sparse_dw_kernel(const int* off, const SpEntry* bucket, const E* h, int64_t H,
+                                                        const GradCounts* cnt, int accumulate, float* dW, int64_t T,
+                                                        int64_t V) {
+  __shared__ SpEntry ord[ORDER_CAP];
+  __shared__ SpEntry raw[ORDER_CAP];
+  __shared__ float win[WIN];
+  const bool from_mem = accumulate || cnt->dense > 0;
+  for (int64_t j = blockIdx.x; j < V; j += gridDim.x) {
+    sparse_dw_row(j, off, bucket, h, H, from_mem, dW, T, ord, raw, win);
+    __syncthreads();  // the row's LDS before the next row's
+  }
+}
+
 // Hidden gradient rows of the sparse and empty positions: one workgroup per
 // permuted position n >= dense (row t = perm[n]):
 //   dH[t, :] = (sum over the entries, in increasing vocabulary row j, of
 //              dz * W[j, :]) / div   in the hidden dtype; zeros for empty rows.
-template <class E>
+// An e4m3 weight (E = uint8_t) is read dequantized, fl32(w_scale[j] code),
+// and the hidden gradient is bf16.
+template <class E, class O>
 __global__ __launch_bounds__(256) void sparse_dh_kernel(const int* perm, const GradCounts* cnt, const int* rowcnt,
-                                                        const SpEntry* list, const E* W, int64_t H, float div,
-                                                        E* dH, int64_t T) {
+                                                        const SpEntry* list, const E* W, const float* w_scale,
+                                                        int64_t H, float div, O* dH, int64_t T) {
   __shared__ SpEntry raw[NSP];
   __shared__ SpEntry ord[NSP];
   const int64_t n = blockIdx.x;
   const GradCounts c = *cnt;
   if (n < c.dense || n >= T) return;
   const int64_t t = perm[n];
-  E* out = dH + t * H;
+  O* out = dH + t * H;
   const int ne = n < c.active ? min(rowcnt[n], NSP) : 0;
   for (int i = threadIdx.x; i < ne; i += 256) raw[i] = list[n * NSP + i];
   __syncthreads();
@@ -410,11 +439,11 @@ __global__ __launch_bounds__(256) void sparse_dh_kernel(const int* perm, const G
     float acc[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-    ordered_sum(ord, ne, W, H, c0, acc);
+    ordered_sum(ord, ne, W, H, c0, acc, w_scale);
     if (div != 1.f)
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[k] = acc[k] / div;
-    if constexpr (sizeof(E) == 2) {
+    if constexpr (sizeof(O) == 2) {
       bf16x8 o;
 #pragma unroll
       for (int k = 0; k < 8; ++k) o[k] = (bf16)acc[k];
@@ -478,23 +507,28 @@ hipError_t launch_sparse_grads(const SparseGradArgs& a, hipStream_t s) {
       if ((e = launch_exclusive_scan(a.cntj, a.V, a.scan_sums, a.offj, s))) return e;
       hipLaunchKernelGGL(bucket_fill_kernel, dim3((unsigned)ceil_div(a.T, 4)), dim3(256), 0, s, a.cnt, a.T, a.rowcnt,
                          a.list, a.offj, a.cntj, a.bucket);
-      if (a.dtype == 1)
-        hipLaunchKernelGGL(sparse_dw_kernel<bf16>, dim3((unsigned)a.V), dim3(256), 0, s, a.offj, a.bucket,
-                           (const bf16*)a.h_perm, a.H, a.cnt, a.accumulate_w, a.grad_weight, a.T);
+      // a few workgroups per compute unit, each looping over vocabulary rows
+      const unsigned g = (unsigned)(a.V < 4096 ? a.V : 4096);
+      if (a.dtype != DT_F32)  // bf16 rows (the fp8 lane's are the dequantized hidden rows)
+        hipLaunchKernelGGL(sparse_dw_kernel<bf16>, dim3(g), dim3(256), 0, s, a.offj, a.bucket, (const bf16*)a.h_perm,
+                           a.H, a.cnt, a.accumulate_w, a.grad_weight, a.T, a.V);
       else
-        hipLaunchKernelGGL(sparse_dw_kernel<float>, dim3((unsigned)a.V), dim3(256), 0, s, a.offj, a.bucket,
-                           (const float*)a.h_perm, a.H, a.cnt, a.accumulate_w, a.grad_weight, a.T);
+        hipLaunchKernelGGL(sparse_dw_kernel<float>, dim3(g), dim3(256), 0, s, a.offj, a.bucket,
+                           (const float*)a.h_perm, a.H, a.cnt, a.accumulate_w, a.grad_weight, a.T, a.V);
     }
     if ((e = hipGetLastError())) return e;
   }
   if (a.grad_hidden) {
     ProfScope ps(KIND_SPARSE_DH, s);
-    if (a.dtype == 1)
-      hipLaunchKernelGGL(sparse_dh_kernel<bf16>, dim3((unsigned)a.T), dim3(256), 0, s, a.perm, a.cnt, a.rowcnt,
-                         a.list, (const bf16*)a.W, a.H, a.dh_div, (bf16*)a.grad_hidden, a.T);
+    if (a.dtype == DT_FP8)
+      hipLaunchKernelGGL((sparse_dh_kernel<uint8_t, bf16>), dim3((unsigned)a.T), dim3(256), 0, s, a.perm, a.cnt,
+                         a.rowcnt, a.list, (const uint8_t*)a.W, a.w_scale, a.H, a.dh_div, (bf16*)a.grad_hidden, a.T);
+    else if (a.dtype == DT_BF16)
+      hipLaunchKernelGGL((sparse_dh_kernel<bf16, bf16>), dim3((unsigned)a.T), dim3(256), 0, s, a.perm, a.cnt,
+                         a.rowcnt, a.list, (const bf16*)a.W, nullptr, a.H, a.dh_div, (bf16*)a.grad_hidden, a.T);
     else
-      hipLaunchKernelGGL(sparse_dh_kernel<float>, dim3((unsigned)a.T), dim3(256), 0, s, a.perm, a.cnt, a.rowcnt,
-                         a.list, (const float*)a.W, a.H, a.dh_div, (float*)a.grad_hidden, a.T);
+      hipLaunchKernelGGL((sparse_dh_kernel<float, float>), dim3((unsigned)a.T), dim3(256), 0, s, a.perm, a.cnt,
+                         a.rowcnt, a.list, (const float*)a.W, nullptr, a.H, a.dh_div, (float*)a.grad_hidden, a.T);
     if ((e = hipGetLastError())) return e;
   }
   return hipSuccess;

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "stce.h")
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(stce_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(stce_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -34,9 +34,22 @@ def test_library_exports_every_declared_function(lib):
     assert set(names) == set(binding.SYMBOLS)
 
 
-def test_struct_layouts_match_header():
-    assert ctypes.sizeof(binding.Problem) == 120
+def test_struct_layouts_match_header(tmp_path):
+    assert ctypes.sizeof(binding.Problem) == 128
     assert ctypes.sizeof(binding.RowInfo) == binding.STATE_BYTES_PER_ROW
+    # the binding's field offsets against the C compiler's for the header
+    fields = [f for f, _ in binding.Problem._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "stce.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(stce_problem));\n'
+                   + "".join(f'  printf("%zu\\n", offsetof(stce_problem, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert out[0] == ctypes.sizeof(binding.Problem)
+    assert out[1:] == [getattr(binding.Problem, f).offset for f in fields]
 
 
 def _prob(**kw):
@@ -60,8 +73,44 @@ def test_workspace_sizes_are_host_computable(lib):
 
 
 def test_unsupported_dtype_is_one_actionable_error(lib):
-    with pytest.raises(binding.StceError, match="UNSUPPORTED.*fp8"):
+    with pytest.raises(binding.StceError, match="UNSUPPORTED.*dtype 7.*STCE_DT_FP8"):
         binding.workspace_bytes(_prob(dtype=7))
+
+
+def test_fp8_lane_host_checks(lib):
+    """The fp8 lane: H a multiple of 16, weight_scale required, neither the
+    bf16 value lane, the pre-GEMM temperature nor the fused step; its
+    workspaces add the quantized hidden rows (codes and scales)."""
+    fp8 = binding.DT_FP8
+    with pytest.raises(binding.StceError, match="H=72.*multiple of 16"):
+        binding.workspace_bytes(_prob(dtype=fp8, H=72))
+    with pytest.raises(binding.StceError, match="UNSUPPORTED.*bf16 value lane"):
+        binding.workspace_bytes(_prob(dtype=fp8, flags=binding.PROBLEM_BF16_LANE))
+    with pytest.raises(binding.StceError, match="UNSUPPORTED.*pre-GEMM"):
+        binding.workspace_bytes(_prob(dtype=fp8, flags=binding.PROBLEM_PRE_GEMM_TEMPERATURE,
+                                      pre_gemm_temperature=0.5))
+    with pytest.raises(binding.StceError, match="UNSUPPORTED.*fused"):
+        binding.fused_workspace_bytes(_prob(dtype=fp8))
+    p = _prob(dtype=fp8)
+    p.hidden, p.weight, p.target = 16, 16, 16          # fake, never dereferenced
+    st = lib.stce_forward(ctypes.byref(p), ctypes.c_void_p(16), ctypes.c_void_p(16), None, None, 0, None)
+    assert st == 1 and b"weight_scale" in lib.stce_last_error()
+    T, H, V = 1000, 128, 5000
+    f8, b8 = binding.workspace_bytes(_prob(T=T, H=H, V=V, dtype=fp8))
+    f16, b16 = binding.workspace_bytes(_prob(T=T, H=H, V=V, dtype=binding.DT_BF16))
+    up = lambda x: -(-x // 256) * 256  # noqa: E731
+    # forward: codes and scales of one chunk buffer (one chunk here); the
+    # rows to re-project are gathered as codes (1 byte, not 2)
+    assert f8 - f16 == up(T * H) + up(4 * T) - (up(2 * T * H) - up(T * H))
+    # backward: the permuted codes and the per-row scales
+    assert b8 - b16 == up(T * H) + up(4 * T)
+    for R, H_, msg in ((-1, 64, b"R=-1"), (4, 24, b"H=24")):
+        assert lib.stce_fp8_quantize_rows(ctypes.c_void_p(16), R, H_, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                          None) == 1
+        assert msg in lib.stce_last_error()
+    assert lib.stce_fp8_quantize_rows(None, 0, 64, None, None, None) == 0
+    st = lib.stce_fp8_quantize_rows(ctypes.c_void_p(16), 4, 64, ctypes.c_void_p(24), ctypes.c_void_p(16), None)
+    assert st == 1 and b"aligned" in lib.stce_last_error()
 
 
 @pytest.mark.parametrize("kw,msg", [
