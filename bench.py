@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 
 
@@ -99,9 +100,10 @@ def cpu_baseline(w, y, rows):
         cores = os.cpu_count()
     sel = np.arange(rows)
     g = np.full(w["T"], -1.0 / w["T"])
+    kw = dict(lane="fp8", w_scale=w["w_scale"]) if w["dtype"] == "fp8" else {}
     t0 = time.perf_counter()
-    f = oracle.forward(w["h"], w["W"], y, w["temperature"], w["top_k"], w["top_p"], w["min_p"], rows=sel)
-    oracle.backward(w["h"], w["W"], y, f, g, w["temperature"])
+    f = oracle.forward(w["h"], w["W"], y, w["temperature"], w["top_k"], w["top_p"], w["min_p"], rows=sel, **kw)
+    oracle.backward(w["h"], w["W"], y, f, g, w["temperature"], w_scale=kw.get("w_scale"))
     dt = time.perf_counter() - t0
     return dict(value=rows / dt, unit="scored tokens/s", cores=int(cores), kind="oracle",
                 sample=f"first {rows} rows of the same workload, forward + backward (their grad_hidden rows "
@@ -502,13 +504,23 @@ def main():
     log(f"[bench] generating {args.config} inputs")
     w = workloads.make(args.config)
     T, H, V = w["T"], w["H"], w["V"]
+    fp8 = w["dtype"] == "fp8"
     dt = torch.float32 if w["dtype"] == "f32" else torch.bfloat16
     h = torch.from_numpy(w["h"]).to(dev).to(dt)
-    W = torch.from_numpy(w["W"]).to(dev).to(dt)
+    W = torch.from_numpy(w["W"]).to(dev) if fp8 else torch.from_numpy(w["W"]).to(dev).to(dt)
+    w_scale = torch.from_numpy(w["w_scale"]).to(dev) if fp8 else None
     meta = dict(temperature=torch.from_numpy(w["temperature"]).to(dev), top_k=torch.from_numpy(w["top_k"]).to(dev),
                 top_p=torch.from_numpy(w["top_p"]).to(dev), min_p=torch.from_numpy(w["min_p"]).to(dev))
     log("[bench] drawing targets from the filtered distributions")
-    if w["filtered"]:
+    if w["filtered"] and fp8:
+        # input preparation with torch's own e4m3 conversion: the dequantized
+        # operands of the lane (rows of h scaled by amax / 448)
+        a = (h.float().abs().amax(1, keepdim=True) / 448.0).clamp_min(1e-30)
+        h_deq = (h.float() / a).clamp(-448, 448).to(torch.float8_e4m3fn).float() * a
+        W_deq = W.view(torch.float8_e4m3fn).float() * w_scale[:, None]
+        target = sample_targets_gpu(h_deq, W_deq, meta, w["u"])
+        del h_deq, W_deq
+    elif w["filtered"]:
         target = sample_targets_gpu(h, W, meta, w["u"])
     else:
         target = torch.from_numpy(w["target_uniform"]).to(dev)
@@ -517,7 +529,7 @@ def main():
     ts = args.pre_gemm_temperature
     prob, keep = binding.make_problem(h, W, target, None if ts is not None else meta["temperature"], meta["top_k"],
                                       meta["top_p"], meta["min_p"], args.chunk_rows, args.vocab_slice,
-                                      pre_gemm_temperature=ts, lane=args.lane)
+                                      pre_gemm_temperature=ts, lane=args.lane, weight_scale=w_scale)
     fwd_b, bwd_b = binding.workspace_bytes(prob)
     ws_f = torch.empty(fwd_b, dtype=torch.uint8, device=dev)
     ws_b = torch.empty(bwd_b, dtype=torch.uint8, device=dev)
@@ -633,7 +645,7 @@ def main():
     # runs over the rows with a gradient, the two gradient products over the
     # dense rows; sparse rows' gradients are sums over their dz entries
     classes = row_classes(binding.decode_state(state), g.cpu().numpy())
-    classed = dt == torch.bfloat16 and not args.fused
+    classed = dt == torch.bfloat16 and not args.fused    # bf16 and the fp8 lane
     t_act = classes["dense"] + classes["sparse"] if classed else T
     t_dense = classes["dense"] if classed else T
     per_step_flop = {"projection": 2.0 * T * H * V, "dlogits": 2.0 * t_act * H * V,
@@ -651,6 +663,11 @@ def main():
             stats[k]["tflops"] = per_launch[k] / (a.mean() * 1e-3) / 1e12
     dom = max((k for k in stats if k in per_launch), key=lambda k: stats[k]["total_ms_per_step"])
     achieved = stats[dom]["tflops"]
+    # the fp8 lane's projection and recompute run on e4m3 operands (the fp8
+    # peak), its two gradient products on bf16 ones
+    peak_of = {k: (PEAK_FP8_TFLOPS if fp8 and k in ("projection", "dlogits") else PEAK_BF16_TFLOPS)
+               for k in per_step_flop}
+    t_at_peak = sum(f / (peak_of[k] * 1e12) for k, f in per_step_flop.items())
 
     # matrix-core flop the step performs (the dense formulation would perform
     # 8 T H V: forward, recompute, dH, dW over every row)
@@ -670,9 +687,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if dt == torch.bfloat16 else "f32",
-        "data": "synthetic (seeded PCG64; h ~ N(0,1), W ~ N(0,0.02^2), bf16; targets drawn from the filtered "
-                "distributions)",
+        "dtype": "fp8" if fp8 else "bf16" if dt == torch.bfloat16 else "f32",
+        "data": ("synthetic (seeded PCG64; h ~ N(0,1) bf16; W e4m3 codes drawn as bit fields, exponent field "
+                 "14 - Geometric(1/2), uniform mantissa and sign, row scales 1.4e-4 * 2^U(-1/2, 1/2); targets drawn "
+                 "from the filtered distributions)" if fp8 else
+                 "synthetic (seeded PCG64; h ~ N(0,1), W ~ N(0,0.02^2), bf16; targets drawn from the filtered "
+                 "distributions)"),
         "config": {"workload": f"{args.config}: T={T} scored tokens, H={H}, V={V}, temperature "
                                f"{'per-row' if args.config != 'headline' else 0.7}, top_k "
                                f"{int(w['top_k'].max())}, top_p {float(w['top_p'].min())}, min_p "
@@ -683,18 +703,20 @@ def main():
                                   if args.fused else "")
                                + ("; forward side outputs (full LSE, entropies)" if args.side_outputs else "")
                                + ("; bf16 value lane" if args.lane == "bf16" else "")
+                               + ("; fp8 lane: e4m3 weight with per-row scales, hidden rows quantized per row, "
+                                  "logits and recompute on fp8 matrix cores, gradient products bf16" if fp8 else "")
                                + (f"; scalar pre-GEMM temperature {ts} in place of the per-row one"
                                   if ts is not None else ""),
                    "T": T, "H": H, "V": V, "chunk_rows": C, "vocab_slice": Vs},
-        "mfma_peak_frac": flop_step / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "mfma_peak_frac": t_at_peak / (ms_step * 1e-3),
         "mfma_flop_per_step": flop_step,
         "tflops_performed": flop_step / (ms_step * 1e-3) / 1e12,
         "tflops_8thv": 8.0 * T * H * V / (ms_step * 1e-3) / 1e12,
         "dense_equivalent_frac_8thv": 8.0 * T * H * V / (ms_step * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "tflops_6thv": 6.0 * T * H * V / (ms_step * 1e-3) / 1e12,
         "row_classes": classes if classed else None,
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak_of[dom],
+                     "unit": "TFLOP/s", "frac": achieved / peak_of[dom],
                      "traffic": read_traffic(dom, args.config)},
         "kernels": stats,
         "targets_in_support": in_support,

@@ -592,18 +592,20 @@ def policy_loss(logprob, advantages, old_logprob, objective="cispo", eps_low=0.2
     return dict(loss=loss * sc, g=g * sc, ratio=ratio)
 
 
-def sample_targets(h, W, temperature, top_k, top_p, min_p, u, rows=None) -> np.ndarray:
+def sample_targets(h, W, temperature, top_k, top_p, min_p, u, rows=None, lane="fp32", w_scale=None) -> np.ndarray:
     """Draw one target per row from its filtered distribution.
 
     Inverse CDF along the order pi over ``q`` (softmax of z/T on the
     support), with the caller's uniforms ``u`` in [0, 1).  ``rows`` limits
-    the draw to a subset of rows (returned in that order).
+    the draw to a subset of rows (returned in that order).  ``lane="fp8"``
+    takes the fp8 lane's logits (``W`` of e4m3 codes, row scales
+    ``w_scale``).
     """
     T = np.asarray(h).shape[0]
     rows = np.arange(T) if rows is None else np.asarray(rows)
     temp = np.ones(T, np.float32) if temperature is None else np.asarray(temperature, np.float32)
     tk, tp, mp = _meta(T, top_k, top_p, min_p)
-    z = chunk_logits(np.asarray(h)[rows], W)
+    z = _logits(np.asarray(h)[rows], W, "fp8" if lane == "fp8" else "fp32", w_scale)
     s32 = scale_logits(z, temp[rows])
     uu = z / temp[rows].astype(np.float64)[:, None]
     out = np.empty(len(rows), np.int64)

@@ -30,18 +30,28 @@ def dev():
 def to_gpu(w, y):
     dt = torch.float32 if w["dtype"] == "f32" else torch.bfloat16
     d = dev()
-    return dict(
-        h=torch.from_numpy(w["h"]).to(d).to(dt), W=torch.from_numpy(w["W"]).to(d).to(dt),
+    fp8 = w["dtype"] == "fp8"
+    out = dict(
+        h=torch.from_numpy(w["h"]).to(d).to(dt),
+        W=torch.from_numpy(w["W"]).to(d) if fp8 else torch.from_numpy(w["W"]).to(d).to(dt),
         target=torch.from_numpy(np.asarray(y, np.int64)).to(d),
         temperature=torch.from_numpy(w["temperature"]).to(d), top_k=torch.from_numpy(w["top_k"]).to(d),
         top_p=torch.from_numpy(w["top_p"]).to(d), min_p=torch.from_numpy(w["min_p"]).to(d))
+    out["weight_scale"] = torch.from_numpy(w["w_scale"]).to(d) if fp8 else None
+    return out
+
+
+def lane_of(w):
+    """The oracle's lane name and keyword arguments for a workload."""
+    return ("fp8", dict(w_scale=w["w_scale"])) if w["dtype"] == "fp8" else ("fp32", {})
 
 
 def targets(w, rows=None):
     if not w["filtered"]:
         return w["target_uniform"] if rows is None else w["target_uniform"][rows]
+    lane, kw = lane_of(w)
     return oracle.sample_targets(w["h"], w["W"], w["temperature"], w["top_k"], w["top_p"], w["min_p"], w["u"],
-                                 rows=rows)
+                                 rows=rows, lane=lane, **kw)
 
 
 def meta_of(g):
