@@ -127,21 +127,26 @@ def filter_binding(info, w):
     return out
 
 
-def row_classes(info, g, nsp=128):
+def row_classes(info, g, tiled_on, nsp=128):
     """Rows of each backward class, by the library's rule: a row with a
     gradient (target in its support, valid metadata, nonzero upstream
     gradient) is sparse when its support holds at most nsp tokens, dense
-    otherwise (unfiltered rows included); the others are empty."""
+    otherwise (unfiltered rows included), and a sparse row with a tile list
+    is tiled (its keys recomputed on those tiles only); the others are
+    empty.  Also the (row, tile) pairs of the tiled rows."""
     fl = info["flags"]
     active = ((fl & 1) != 0) & ((fl & 4) != 0) & (g != 0)
     dense = active & (((fl & 2) == 0) | (info["n"] > nsp))
-    return {"dense": int(dense.sum()), "sparse": int((active & ~dense).sum()), "empty": int((~active).sum())}
+    tiled = active & ~dense & (info["ntile"] > 0) & tiled_on
+    return {"dense": int(dense.sum()), "sparse": int((active & ~dense & ~tiled).sum()), "tiled": int(tiled.sum()),
+            "empty": int((~active).sum()), "tile_pairs": int(info["ntile"][tiled].sum())}
 
 
 KERNEL_SYMBOLS = {
     # kernel kind -> epilogue name in its (mangled or demangled) symbol; the bf16 main loop
     "projection": "EpiLogits",
-    "dlogits": "EpiGrad",
+    "dlogits": "EpiGradT<false, false>",
+    "tile_recompute": "gemm_worklist",
     "grad_weight": "EpiStore",
     "grad_hidden": "EpiAccum",
 }
@@ -149,7 +154,11 @@ KERNEL_SYMBOLS = {
 # kernel-trace labels: (substring of the symbol, label), first match wins
 TRACE_LABELS = [
     ("EpiLogits", "gemm: forward projection + keys or candidates + tile partials (EpiLogits)"),
-    ("EpiGrad", "gemm: backward recompute + dz entries / dense dz^T (EpiGrad)"),
+    ("gemm_worklist", "gemm: tile recompute of the tiled rows on their listed tiles + dz entries (EpiGrad)"),
+    ("EpiGrad", "gemm: whole-vocabulary recompute + dz entries / dense dz^T (EpiGrad)"),
+    ("tile_count", "tile recompute work lists (count, work items, fill)"),
+    ("tile_work", "tile recompute work lists (count, work items, fill)"),
+    ("tile_fill", "tile recompute work lists (count, work items, fill)"),
     ("EpiStore", "gemm: grad_weight of the dense rows (EpiStore)"),
     ("EpiAccumT", "gemm: grad_hidden of the dense rows as dH^T (EpiAccumT)"),
     ("EpiDlogits", "gemm: backward recompute + dz^T, fp32 operands (EpiDlogits)"),
@@ -644,11 +653,14 @@ def main():
     # the backward's row classes (bf16 unfused step): the recompute product
     # runs over the rows with a gradient, the two gradient products over the
     # dense rows; sparse rows' gradients are sums over their dz entries
-    classes = row_classes(binding.decode_state(state), g.cpu().numpy())
     classed = dt == torch.bfloat16 and not args.fused    # bf16 and the fp8 lane
-    t_act = classes["dense"] + classes["sparse"] if classed else T
+    tiled_on = classed and -(-V // 256) <= 65535 and T * H * (1 if fp8 else 2) < 2 ** 31 - 1 - 2 ** 22
+    classes = row_classes(binding.decode_state(state), g.cpu().numpy(), tiled_on)
+    t_full = classes["dense"] + classes["sparse"] if classed else T
     t_dense = classes["dense"] if classed else T
-    per_step_flop = {"projection": 2.0 * T * H * V, "dlogits": 2.0 * t_act * H * V,
+    # the tile recompute forms 256 keys of H-long products per (row, tile) pair
+    per_step_flop = {"projection": 2.0 * T * H * V, "dlogits": 2.0 * t_full * H * V,
+                     "tile_recompute": 2.0 * classes["tile_pairs"] * 256 * H if classed else 0.0,
                      "grad_weight": 2.0 * t_dense * H * V, "grad_hidden": 2.0 * t_dense * H * V}
     if args.fused:
         per_step_flop = {k: 2.0 * T * H * V for k in ("projection", "grad_weight", "grad_hidden")}
@@ -665,7 +677,7 @@ def main():
     achieved = stats[dom]["tflops"]
     # the fp8 lane's projection and recompute run on e4m3 operands (the fp8
     # peak), its two gradient products on bf16 ones
-    peak_of = {k: (PEAK_FP8_TFLOPS if fp8 and k in ("projection", "dlogits") else PEAK_BF16_TFLOPS)
+    peak_of = {k: (PEAK_FP8_TFLOPS if fp8 and k in ("projection", "dlogits", "tile_recompute") else PEAK_BF16_TFLOPS)
                for k in per_step_flop}
     t_at_peak = sum(f / (peak_of[k] * 1e12) for k, f in per_step_flop.items())
 

@@ -121,8 +121,16 @@ typedef enum {
                                     identity: q comes from the bf16 keys.  Without a
                                     bf16 hidden/weight: STCE_E_UNSUPPORTED. */
 
-/* Bytes of per-row state stce_forward writes and stce_backward reads. */
-#define STCE_STATE_BYTES_PER_ROW 32
+/* Bytes of per-row state stce_forward writes and stce_backward reads.  A
+ * state of T rows holds T 32-byte records (stce_row_info, in row order), then
+ * T 64-byte lists of the vocabulary tiles (256 tokens each) that can hold the
+ * row's support tokens: the tiles whose largest key reaches the row's last
+ * support key, at most 31 of them (a count, then the tile indices in
+ * increasing order; count 0 when there are more, on unfiltered rows, and when
+ * the vocabulary has more than 65,535 tiles).  The backward recomputes the
+ * keys of a sparse row with such a list on its tiles only.  Neither part is
+ * of size [T, V]. */
+#define STCE_STATE_BYTES_PER_ROW 96
 
 typedef struct stce_problem {
   int64_t T;             /* rows (scored tokens), 1 <= T <= 2^22 - 64 (the products
@@ -209,8 +217,9 @@ stce_status stce_schedule(const stce_problem *prob, int64_t *chunk_rows, int64_t
  * y_t is in the support S_t, else -inf, with s = fl32(h W^T) / T per row
  * (or the keys of the convention prob->flags selects: scalar pre-GEMM
  * temperature, bf16 value lane, which also rounds logprob to bf16).
- * Writes logprob [T] fp32 and state [T * 32 bytes] (support boundary,
- * filtered log-sum-exp, flags) for stce_backward.  dev_status: one int64
+ * Writes logprob [T] fp32 and state [T * STCE_STATE_BYTES_PER_ROW bytes]
+ * (support boundary, filtered log-sum-exp, flags, support tiles) for
+ * stce_backward.  dev_status: one int64
  * (may be NULL).  ws: at least the forward workspace size, 256-byte
  * aligned. */
 stce_status stce_forward(const stce_problem *prob, float *logprob, void *state,
@@ -304,7 +313,8 @@ stce_status stce_recompute_keys(const stce_problem *prob, const float *grad_logp
  * the same selection kernel as
  * stce_forward.  Metadata pointers as in stce_problem (NULL = off), target
  * [R] required.  Writes logprob [R] (= min(s_y - lse_S, 0) or -inf) and
- * state [R * 32 bytes].  ws: at least stce_support_workspace_bytes(R, V). */
+ * state [R * STCE_STATE_BYTES_PER_ROW bytes].  ws: at least
+ * stce_support_workspace_bytes(R, V). */
 stce_status stce_support_from_logits(const float *s, int64_t R, int64_t V, const int32_t *top_k,
                                      const float *top_p, const float *min_p, const int64_t *target,
                                      float *logprob, void *state, int64_t *dev_status, void *ws,
@@ -313,12 +323,13 @@ stce_status stce_support_from_logits(const float *s, int64_t R, int64_t V, const
 /* Workspace bytes for stce_support_from_logits. */
 size_t stce_support_workspace_bytes(int64_t R, int64_t V);
 
-/* Decoding of the 32-byte per-row state (for tests and diagnostics).  The
- * state holds, per row: the boundary key (order-preserving uint32 image of
+/* Decoding of the 32-byte per-row records of a state (for tests and
+ * diagnostics).  A record holds: the boundary key (order-preserving uint32 image of
  * the last support token's fp32 key), the boundary token id, the support
  * size n (V for an unfiltered row, whose boundary is then 0 / V - 1), the
  * filtered and full log-sum-exp, the row maximum, the target's key (0 on
- * inactive ignore_index rows) and flags.  Reads `nrows` entries of a HOST copy of the state. */
+ * inactive ignore_index rows) and flags.  Reads the first `nrows` records of
+ * a HOST copy of a state (its first nrows * 32 bytes). */
 typedef struct stce_row_info {
   uint32_t key_thr;
   int32_t id_thr;
@@ -356,6 +367,8 @@ stce_status stce_decode_state(const void *host_state, int64_t nrows, stce_row_in
 #define STCE_KERNEL_SPARSE_DH 15   /* backward: hidden-gradient rows of the sparse and empty rows */
 #define STCE_KERNEL_REPROJECT 16   /* forward: projection of the rows whose candidates could not decide */
 #define STCE_KERNEL_QUANTIZE 17    /* fp8 lane: per-row e4m3 quantization of hidden rows */
+#define STCE_KERNEL_TILE_LISTS 18  /* backward: per-tile lists of the rows whose keys are recomputed there */
+#define STCE_KERNEL_TILE_RECOMPUTE 19 /* backward: recompute of those rows' keys on their listed tiles */
 typedef struct stce_profile {
   int32_t capacity;
   int32_t count;

@@ -22,7 +22,9 @@ FIELDS = {1: "temperature", 2: "top_k", 3: "top_p", 4: "min_p", 5: "target"}
 FLAG_VALID, FLAG_FILTERED, FLAG_IN_SUPPORT, FLAG_IGNORED = 1, 2, 4, 8
 PROBLEM_IGNORE_INDEX, PROBLEM_PRE_GEMM_TEMPERATURE, PROBLEM_BF16_LANE = 1, 2, 4
 LANES = {"fp32": 0, "bf16": PROBLEM_BF16_LANE}
-STATE_BYTES_PER_ROW = 32
+STATE_BYTES_PER_ROW = 96      # a 32-byte record, then (after all T records) a 64-byte tile list
+RECORD_BYTES = 32
+NTILE = 31
 DT_BF16, DT_F32, DT_FP8 = 1, 2, 3
 # dtypes a weight of e4m3 codes may come in (the fp8 lane)
 FP8_WEIGHT_DTYPES = (torch.uint8, torch.float8_e4m3fn)
@@ -37,7 +39,8 @@ SYMBOLS = (
 KERNEL_KINDS = {1: "validate", 2: "projection", 3: "select", 4: "dlogits", 5: "grad_weight",
                 6: "grad_hidden", 7: "transpose", 8: "partials", 9: "policy_loss", 10: "dz_keys",
                 11: "split_sum", 12: "prescale", 13: "classify", 14: "sparse_grad_weight",
-                15: "sparse_grad_hidden", 16: "reproject", 17: "quantize"}
+                15: "sparse_grad_hidden", 16: "reproject", 17: "quantize", 18: "tile_lists",
+                19: "tile_recompute"}
 PG_OBJECTIVES = {"cispo": 1, "clip": 2}
 
 
@@ -335,8 +338,10 @@ def recompute_keys(hidden, weight, target, state, grad_logprob, temperature=None
                    min_p=None, *, vocab_slice: int = 0, ignore_index: Optional[int] = None,
                    pre_gemm_temperature: Optional[float] = None, lane: str = "fp32",
                    weight_scale: Optional[torch.Tensor] = None):
-    """fp32 keys [T, V] recomputed by the backward's product, exported by that
-    launch itself (parity: they must equal the forward's bit for bit)."""
+    """fp32 keys [T, V] recomputed by the backward's products, exported by
+    those launches themselves (parity: they must equal the forward's bit for
+    bit).  A row whose keys the backward recomputes on its listed tiles only
+    gets those tiles' keys; its other entries stay NaN."""
     prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, 0, vocab_slice,
                               ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane,
                               weight_scale=weight_scale)
@@ -345,7 +350,7 @@ def recompute_keys(hidden, weight, target, state, grad_logprob, temperature=None
         raise ValueError("state must be the uint8 [T*32] tensor written by forward")
     _, bwd_b = workspace_bytes(prob)
     ws = torch.empty(max(bwd_b, 1), dtype=torch.uint8, device=dev)
-    out = torch.empty(prob.T, prob.V, dtype=torch.float32, device=dev)
+    out = torch.full((prob.T, prob.V), float("nan"), dtype=torch.float32, device=dev)
     g = grad_logprob.contiguous()
     _check(load().stce_recompute_keys(ctypes.byref(prob), _ptr(g), _ptr(state), _ptr(out), _ptr(ws), ws.numel(),
                                       _stream()))
@@ -515,7 +520,8 @@ def fused_policy_step(hidden, weight, target, advantages, old_logprob, temperatu
 
 
 def decode_state(state: torch.Tensor) -> dict:
-    """Per-row state fields as numpy arrays (copies the state to the host)."""
+    """Per-row state fields as numpy arrays (copies the state to the host),
+    with ``ntile`` and ``tiles`` [T, 31] from the rows' tile lists."""
     import numpy as np
     host = state.detach().cpu().contiguous()
     n = host.numel() // STATE_BYTES_PER_ROW
@@ -524,7 +530,20 @@ def decode_state(state: torch.Tensor) -> dict:
     arr = np.frombuffer(bytes(out), dtype=np.dtype([
         ("key_thr", "<u4"), ("id_thr", "<i4"), ("n", "<i4"), ("flags", "<u4"),
         ("lse_support", "<f4"), ("lse_full", "<f4"), ("row_max", "<f4"), ("target_key", "<f4")]))
-    return {k: arr[k].copy() for k in arr.dtype.names}
+    d = {k: arr[k].copy() for k in arr.dtype.names}
+    tl = host[n * RECORD_BYTES:].numpy().view(np.uint16).reshape(n, 1 + NTILE)
+    d["ntile"] = tl[:, 0].astype(np.int64)
+    d["tiles"] = tl[:, 1:].astype(np.int64)
+    return d
+
+
+def state_prefix(state: torch.Tensor, rows: int) -> torch.Tensor:
+    """The state bytes of the first ``rows`` rows (their records, then their
+    tile lists), comparable with the state of a call over those rows only."""
+    T = state.numel() // STATE_BYTES_PER_ROW
+    rec = state[: T * RECORD_BYTES][: rows * RECORD_BYTES]
+    til = state[T * RECORD_BYTES:][: rows * (STATE_BYTES_PER_ROW - RECORD_BYTES)]
+    return torch.cat([rec, til])
 
 
 class ScoreFunction(torch.autograd.Function):

@@ -14,7 +14,27 @@ FLAGS = [
     "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 arithmetic stays off: scalar fp32 code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # per-kernel register, LDS and scratch figures (checked below)
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+
+
+def scratch_kernels(remarks: str) -> list:
+    """(kernel, bytes per lane) of every kernel the compiler gave private
+    scratch memory (register spills or private arrays): in the products such
+    memory costs an order of magnitude of their time, and the entry point
+    that allocates nothing must not need it."""
+    import re
+    out, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out
 
 
 def build(verbose: bool = False) -> str:
@@ -26,6 +46,10 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building libstce.so")
+    bad = scratch_kernels(res.stderr)
+    if bad:
+        os.remove(LIB + ".tmp")
+        raise RuntimeError("kernels with private scratch memory: " + ", ".join(f"{n} ({b} B/lane)" for n, b in bad))
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

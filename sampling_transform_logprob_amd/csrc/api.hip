@@ -70,6 +70,9 @@ struct Layout {
   size_t b_cnt, b_perm, b_rowcnt, b_blk, b_hperm, b_list, b_cntj, b_offj, b_sums, b_bucket;
   // fp8 lane: the quantized hidden rows in permuted order and their scales
   size_t b_h8, b_ha;
+  // tile recompute work lists (when tiled(p)): per-tile counts, fill
+  // counters, offsets, work counts and work offsets, and the buckets
+  size_t b_tcnt, b_tfill, b_toff, b_twork, b_twoff, b_tbucket;
 };
 
 // The scalar pre-GEMM temperature: the problem's hidden states are replaced
@@ -77,6 +80,20 @@ struct Layout {
 bool pre_gemm(const stce_problem* p) { return (p->flags & STCE_PROBLEM_PRE_GEMM_TEMPERATURE) != 0; }
 // The bf16 value lane: bf16 keys and a bf16 logprob.
 int bf16_lane(const stce_problem* p) { return (p->flags & STCE_PROBLEM_BF16_LANE) ? 1 : 0; }
+
+// The per-row tile lists follow the T per-row records in the state; they
+// exist when a tile index fits 16 bits.
+bool tiles_ok(int64_t V) { return ceil_div(V, VTILE) <= 65535; }
+RowTiles* state_tiles(void* state, int64_t T, int64_t V) {
+  return tiles_ok(V) ? (RowTiles*)((char*)state + sizeof(RowState) * (size_t)T) : nullptr;
+}
+
+// The tile recompute (sparse rows with tile lists): bf16 and fp8 operands,
+// tile lists present, and hidden rows addressable with 32-bit offsets.
+bool tiled(const stce_problem* p) {
+  const int64_t hb = p->T * p->H * (p->dtype == STCE_DT_FP8 ? 1 : 2);
+  return p->dtype != STCE_DT_F32 && tiles_ok(p->V) && hb < (int64_t)INT32_MAX - (1 << 22);
+}
 
 // The fp8 lane: e4m3 weight codes with per-row scales, bf16 hidden states
 // quantized per row by the library.
@@ -205,6 +222,14 @@ Layout plan(const stce_problem* p, bool single_buffer = false) {
   if (fp8(p)) {
     L.b_h8 = o;     o = align_up(o + (size_t)T * H);
     L.b_ha = o;     o = align_up(o + 4 * (size_t)T);
+  }
+  if (tiled(p)) {
+    L.b_tcnt = o;   o = align_up(o + 4 * (size_t)L.ntv);
+    L.b_tfill = o;  o = align_up(o + 4 * (size_t)L.ntv);
+    L.b_toff = o;   o = align_up(o + 4 * ((size_t)L.ntv + 1));
+    L.b_twork = o;  o = align_up(o + 4 * (size_t)L.ntv);
+    L.b_twoff = o;  o = align_up(o + 4 * ((size_t)L.ntv + 1));
+    L.b_tbucket = o; o = align_up(o + 4 * (size_t)NTILE * T);
   }
   L.bwd = o;
   return L;
@@ -386,6 +411,7 @@ stce_status stce_profile_attach(stce_profile* prof) {
 }
 
 
+static_assert(STCE_STATE_BYTES_PER_ROW == STATE_BYTES_PER_ROW, "state layout");
 size_t stce_state_bytes(int64_t T) { return T > 0 ? (size_t)T * STCE_STATE_BYTES_PER_ROW : 0; }
 
 stce_status stce_workspace_bytes(const stce_problem* prob, size_t* fwd, size_t* bwd) {
@@ -508,6 +534,7 @@ stce_status forward_impl(const stce_problem* p, float* logprob, void* state, con
     sp.min_p = p->min_p ? p->min_p + c0 : nullptr;
     sp.logprob = logprob + c0;
     sp.state = (RowState*)state + c0;
+    sp.tiles = tiles_ok(p->V) ? state_tiles(state, p->T, p->V) + c0 : nullptr;
     sp.V = (int)p->V;
     sp.lse_full = so_lse ? so_lse + c0 : nullptr;
     sp.ent_full = so_hf ? so_hf + c0 : nullptr;
@@ -651,8 +678,9 @@ stce_status backward_classed(const stce_problem* p, const Layout& L, const float
   bf16* h_perm = at<bf16>(ws, L.b_hperm);
   SpEntry* list = at<SpEntry>(ws, L.b_list);
   const bool want_w = grad_weight && !keys_out;
-  if ((e = launch_grad_classes((const RowState*)state, grad_logprob, p->T, at<int>(ws, L.b_blk), cnt, perm, rowcnt,
-                               st)))
+  const RowTiles* tl = tiled(p) ? state_tiles((void*)state, p->T, p->V) : nullptr;
+  if ((e = launch_grad_classes((const RowState*)state, tl, grad_logprob, p->T, at<int>(ws, L.b_blk), cnt, perm,
+                               rowcnt, st)))
     return hip_fail(e, "row classes");
   uint8_t* h8_perm = fp8(p) ? at<uint8_t>(ws, L.b_h8) : nullptr;
   float* ha = fp8(p) ? at<float>(ws, L.b_ha) : nullptr;
@@ -704,6 +732,47 @@ stce_status backward_classed(const stce_problem* p, const Layout& L, const float
     a.keys_out = keys_out;
     a.ld_keys = p->V;
     if ((e = launch_class_slice(a, st))) return hip_fail(e, "backward slice");
+  }
+  if (tl) {  // the tiled rows' keys on their tiles
+    TiledArgs ta{};
+    if (fp8(p)) {
+      ta.W8 = (const uint8_t*)p->weight;
+      ta.w_scale = p->weight_scale;
+      ta.h8_perm = h8_perm;
+      ta.h_scale = ha;
+    } else {
+      ta.W = (const bf16*)p->weight;
+      ta.h_perm = h_perm;
+    }
+    ta.perm = perm;
+    ta.cnt = cnt;
+    ta.temp = p->temperature;
+    ta.target = p->target;
+    ta.st = (const RowState*)state;
+    ta.g = grad_logprob;
+    ta.rowcnt = rowcnt;
+    ta.list = list;
+    ta.cntj = want_w ? cntj : nullptr;
+    ta.T = p->T;
+    ta.H = p->H;
+    ta.V = p->V;
+    ta.bf16_lane = bf16_lane(p);
+    ta.keys_out = keys_out;
+    ta.ld_keys = p->V;
+    TileListArgs& la = ta.lists;
+    la.perm = perm;
+    la.cnt = cnt;
+    la.tiles = tl;
+    la.T = p->T;
+    la.ntv = L.ntv;
+    la.tcnt = at<int>(ws, L.b_tcnt);
+    la.tfill = at<int>(ws, L.b_tfill);
+    la.toff = at<int>(ws, L.b_toff);
+    la.twork = at<int>(ws, L.b_twork);
+    la.twoff = at<int>(ws, L.b_twoff);
+    la.sums = at<int>(ws, L.b_sums);
+    la.bucket = at<int>(ws, L.b_tbucket);
+    if ((e = launch_tiled_recompute(ta, st))) return hip_fail(e, "tile recompute");
   }
   if (keys_out) return STCE_OK;
   SparseGradArgs sa{};
@@ -909,6 +978,7 @@ stce_status stce_support_from_logits(const float* sk, int64_t R, int64_t V, cons
   sp.min_p = min_p;
   sp.logprob = logprob;
   sp.state = (RowState*)state;
+  sp.tiles = state_tiles(state, R, V);
   sp.V = (int)V;
   launch_select(sp, (int)R, st);
   if ((e = hipGetLastError())) return hip_fail(e, "select");
@@ -1031,6 +1101,7 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
     sp.min_p = p->min_p ? p->min_p + c0 : nullptr;
     sp.logprob = logprob + c0;
     sp.state = (RowState*)state + c0;
+    sp.tiles = tiles_ok(p->V) ? state_tiles(state, p->T, p->V) + c0 : nullptr;
     sp.V = (int)p->V;
     sp.lse_full = so_lse ? so_lse + c0 : nullptr;
     sp.ent_full = so_hf ? so_hf + c0 : nullptr;

@@ -48,6 +48,21 @@ struct RowState {
 };
 static_assert(sizeof(RowState) == 32, "row state must be 32 bytes");
 
+// The vocabulary tiles (VTILE columns each) that can hold a row's support
+// tokens: every tile whose maximum key reaches the row's last support key,
+// in increasing order, when there are at most NTILE of them (n = 0 otherwise,
+// and on unfiltered or invalid rows).  Written by the selection after the
+// per-row records (the state holds T RowState records, then T RowTiles), read
+// by the backward, which recomputes such a row's keys on these tiles only.
+constexpr int NTILE = 31;
+struct RowTiles {
+  uint16_t n;
+  uint16_t t[NTILE];
+};
+static_assert(sizeof(RowTiles) == 64, "tile list must be 64 bytes");
+// bytes of state per row: the record and the tile list
+constexpr int STATE_BYTES_PER_ROW = (int)(sizeof(RowState) + sizeof(RowTiles));
+
 // Partial statistics of one (row, 256-wide vocabulary tile) block, written by
 // the projection epilogue: tile maximum, sum of exp(s - tile max), tile
 // minimum, and (when entropies are requested, else 0) the sum of
@@ -65,18 +80,20 @@ constexpr int VTILE = 256;  // vocabulary columns per partial
 // row's support, so a row whose support holds at most NSP tokens ("sparse")
 // has at most NSP nonzero dz entries: the recompute emits them as
 // (vocabulary row, value) entries and the two gradient products take them
-// one by one.  Rows with a larger support ("dense") go through the matrix-core
-// products; rows with no gradient (target out of support, invalid or ignored
-// metadata, zero upstream gradient) are "empty".
+// one by one.  A sparse row with a tile list ("tiled") has its keys
+// recomputed on those tiles only.  Rows with a larger support ("dense") go
+// through the matrix-core products; rows with no gradient (target out of
+// support, invalid or ignored metadata, zero upstream gradient) are "empty".
 constexpr int NSP = 128;
-enum : int { GRAD_DENSE = 0, GRAD_SPARSE = 1, GRAD_EMPTY = 2 };
+enum : int { GRAD_DENSE = 0, GRAD_SPARSE = 1, GRAD_TILED = 2, GRAD_EMPTY = 3, GRAD_CLASSES = 4 };
 
 // Row counts of the classes, written on the device by the classification:
-// rows are placed in the order dense, sparse, empty, each in row order, so
-// dense rows take permuted positions [0, dense) and sparse ones
-// [dense, active).
+// rows are placed in the order dense, sparse, tiled, empty, each in row
+// order, so dense rows take permuted positions [0, dense), sparse ones
+// [dense, full) and tiled ones [full, active).  The whole-vocabulary
+// recompute covers [0, full), the tile recompute [full, active).
 struct GradCounts {
-  int dense, sparse, active, pad;
+  int dense, full, active, pad;
 };
 
 // One nonzero dz entry: a vocabulary row (or, in a weight-gradient bucket,

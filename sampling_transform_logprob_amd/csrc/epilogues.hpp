@@ -465,7 +465,10 @@ struct EpiDlogits {
 // Backward recompute epilogue with row classes (bf16 operands).  M =
 // vocabulary rows of one slice (local m, global v0 + m), N = permuted token
 // positions: position n holds row perm[n]; positions [0, dense) are dense
-// rows, [dense, active) sparse rows, the rest empty (GradCounts).  Recomputes
+// rows, [dense, full) sparse rows, [full, active) tiled rows, the rest empty
+// (GradCounts).  The whole-vocabulary recompute leaves the tiled rows alone;
+// the tile recompute (colpos set) takes its columns' positions from colpos
+// and treats them as the sparse rows.  Recomputes
 // the keys exactly as EpiLogits does and re-derives support membership from
 // the saved boundary, as EpiDlogits does, with the same dz arithmetic
 //   dz[t, v] = c_t (1[v == y_t] - exp(s - lse_S) 1[v in S_t]),  c_t = g_t / T_t.
@@ -477,7 +480,11 @@ struct EpiDlogits {
 // (list[n * NSP + slot], slot from rowcnt[n]), and counted per vocabulary row
 // in cntj for the weight gradient's buckets.
 // ---------------------------------------------------------------------------
-struct EpiGrad {
+// FP8: the fp8 lane's scalings (row_scale, col_scale); TILED: the tile
+// recompute's column positions (colpos).  Both are compile-time so that the
+// bf16 whole-vocabulary instance carries neither.
+template <bool FP8, bool TILED>
+struct EpiGradT {
   const int* perm;          // [N] permuted position -> row
   const GradCounts* cnt;
   const float* temp;        // [rows] or null
@@ -497,21 +504,29 @@ struct EpiGrad {
   // scales [rows] (indexed by row, not position), or null
   const float* row_scale = nullptr;
   const float* col_scale = nullptr;
+  // tile recompute: column c < ncols is position colpos[c] (a tiled row)
+  const int* colpos = nullptr;
+  int ncols = 0;
   static constexpr int LDS_BYTES = 128 * GN * 2;
 
   __device__ inline void operator()(AccTile& acc, int m0, int n0, char* smem, char* smem1) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 2, wn = w & 3, quad = lane >> 4, col = lane & 15;
     const int wmu = __builtin_amdgcn_readfirstlane(wm);
-    const int nd = cnt->dense, na = cnt->active;
-    const bool any_dense = n0 < nd;  // uniform over the workgroup
+    // rows with a gradient this product forms: dense and sparse ones, or the
+    // tiled ones of colpos; the whole-vocabulary product exports no keys of
+    // the tiled rows (the tile recompute exports theirs)
+    const int nd = cnt->dense, nf = cnt->full, na = TILED ? cnt->active : nf, nt = cnt->active;
+    const bool any_dense = !TILED && n0 < nd;  // uniform over the workgroup
     bf16* stg = (bf16*)(wmu ? smem1 : smem);
     // every per-token load first (loads and stores share one in-order counter)
     float tv[ACC_J], cv[ACC_J], thr[ACC_J], nlv[ACC_J], av[ACC_J];
-    int idt[ACC_J], yv[ACC_J], rowv[ACC_J];
+    int idt[ACC_J], yv[ACC_J], rowv[ACC_J], nv[ACC_J];
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) {
-      const int n = n0 + acc_col(wn, j, col);
+      const int cc = n0 + acc_col(wn, j, col);
+      const int n = TILED ? (cc < ncols ? colpos[cc] : N) : cc;
+      nv[j] = n;
       const int t = n < N ? perm[n] : -1;  // the row at this position
       RowState rs{};
       float tt = 1.0f, c = 0.f;
@@ -524,7 +539,7 @@ struct EpiGrad {
       }
       rowv[j] = t;
       tv[j] = tt;
-      av[j] = (t >= 0 && col_scale) ? col_scale[t] : 1.0f;
+      if constexpr (FP8) av[j] = t >= 0 ? col_scale[t] : 1.0f;
       cv[j] = c;
       thr[j] = (rs.flags & ROW_FILTERED) ? key_value(rs.key_thr) : -STCE_INF;
       idt[j] = rs.id_thr;
@@ -532,13 +547,13 @@ struct EpiGrad {
       yv[j] = y;
     }
     float sw[ACC_I][ACC_R];
-    if (row_scale) load_row_scales(row_scale, m0 + wmu * 128, quad, Vs, sw);
+    if constexpr (FP8) load_row_scales(row_scale, m0 + wmu * 128, quad, Vs, sw);
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) {
-      const int n = n0 + acc_col(wn, j, col);
-      if (row_scale) scale_column_fp8(acc, j, sw, av[j]);
+      const int n = nv[j];
+      if constexpr (FP8) scale_column_fp8(acc, j, sw, av[j]);
       keys_column(acc, j, tv[j], bf16_lane);
-      if (keys_out && rowv[j] >= 0) {
+      if (keys_out && rowv[j] >= 0 && (TILED || n < nf || n >= nt)) {
 #pragma unroll
         for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
@@ -551,7 +566,7 @@ struct EpiGrad {
       const int it = idt[j], y = yv[j];
       const bool live = c != 0.f;
       const bool dense = n < nd, sparse = live && !dense && n < na;
-      const int nl_ = n - n0;
+      const int nl_ = n - n0;  // (the dense staging column: whole-vocabulary product only)
 #pragma unroll
       for (int i = 0; i < ACC_I; ++i) {
         const int base = m0 + wmu * 128 + i * 16;  // the wave's 16 rows (uniform)

@@ -114,7 +114,11 @@ __device__ inline int mn_swz(int k) { return (k & 3) | (((k >> 3) & 1) << 2); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-template <bool A_MN, bool B_MN>
+// B_GATHER (K-major B only): B row r of the tile is row brow[r] of B (r < N),
+// through one buffer resource over nrecB bytes of B (< 2^31 - 2^22, so row
+// offsets and the tail sentinel stay in 32 bits): the tile recompute's
+// gathered hidden rows.
+template <bool A_MN, bool B_MN, bool B_GATHER = false>
 struct MainBf16T {
   static constexpr int LDS_BYTES = 2 * 2 * GM * GK * 2;  // 2 stages x (A, B) x 32 KB
   static constexpr int ROWB = GK * 2;                     // 128-byte K-major tile rows
@@ -133,6 +137,8 @@ struct MainBf16T {
   int N;
   int K;  // K-major operands: multiple of 8
   int ka = 0, kb = 0;  // MN-major operands: k-rows that exist (0: K); lda, ldb < 2^24
+  const int* brow = nullptr;  // B_GATHER: the tile's B rows
+  int nrecB = 0;              // B_GATHER: bytes of B
 
   // the same product over k-columns dk .. K of this one (split-K)
   __device__ inline void shift_k(int64_t dk) {
@@ -184,8 +190,10 @@ struct MainBf16T {
     const int rowsA = min(M - m0, GM), rowsB = min(N - n0, GN);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)m0 * lda), (short)0,
                                                                         A_MN ? 0 : rowsA * (int)lda * 2, RSRC_WORD3);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void*)(B + (int64_t)n0 * ldb), (short)0,
-                                                                        B_MN ? 0 : rowsB * (int)ldb * 2, RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t rb =
+        B_GATHER ? __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, nrecB, RSRC_WORD3)
+                 : __builtin_amdgcn_make_buffer_rsrc((void*)(B + (int64_t)n0 * ldb), (short)0,
+                                                     B_MN ? 0 : rowsB * (int)ldb * 2, RSRC_WORD3);
     // K-major loads: instruction i of wave w fills rows (w*LPW + i)*8 .. +8
     // of a tile; lane l covers row + l/8 and physical chunk l%8, i.e.
     // logical chunk (l%8) ^ swz(row); the swizzle uses row bits 1..3, bit 3
@@ -194,6 +202,15 @@ struct MainBf16T {
     const int ce = lpc ^ lds_swz(lrow), co = lpc ^ lds_swz(lrow + 8);
     const int rA = (w * LPW * 8 + lrow) * (int)lda * 2, rB = (w * LPW * 8 + lrow) * (int)ldb * 2;
     const int stepA = 8 * (int)lda * 2, stepB = 8 * (int)ldb * 2;
+    // B_GATHER: byte offset of each load's row (-1: past the tile's rows)
+    int rBg[LPW];
+    if constexpr (B_GATHER) {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int r = n0 + w * LPW * 8 + i * 8 + lrow;
+        rBg[i] = r < N ? brow[r] * (int)ldb * 2 : -1;
+      }
+    }
     // MN-major loads: instruction i of wave w fills k-rows (w*LPW + i)*2 .. +2;
     // lane l covers k-row + l/32, physical 32-byte chunk (l%32)/2, half l%2.
     // The swizzle of those rows depends on i only through its parity, so
@@ -239,6 +256,9 @@ struct MainBf16T {
         if constexpr (B_MN)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rbk, STCE_LDS(st + TILEB + i * 1024), 16, mnoB[i & 1],
                                                    (i & ~1) * 4 * (int)ldb, 0, 0);
+        else if constexpr (B_GATHER)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, STCE_LDS(st + TILEB + i * 1024), 16,
+                                                   (in && rBg[i] >= 0) ? rBg[i] + c16 : 0x7ffffff0, so, 0, 0);
         else
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, STCE_LDS(st + TILEB + i * 1024), 16,
                                                    in ? rB + i * stepB + c16 : 0x7ffffff0, so, 0, 0);
@@ -354,6 +374,7 @@ struct MainBf16T {
   }
 };
 using MainBf16 = MainBf16T<false, false>;
+using MainBf16G = MainBf16T<false, false, true>;
 
 // ---------------------------------------------------------------------------
 // fp8 main loop (MFMA): e4m3 operands, both K-major, C[m, n] = sum_k A[m, k]
@@ -370,7 +391,8 @@ using MainBf16 = MainBf16T<false, false>;
 // ---------------------------------------------------------------------------
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-struct MainFp8 {
+template <bool B_GATHER = false>
+struct MainFp8T {
   static constexpr int ROWB = 128;
   static constexpr int TILEB = GM * ROWB;
   static constexpr int STAGEB = 2 * TILEB;
@@ -384,6 +406,8 @@ struct MainFp8 {
   int64_t ldb;
   int N;
   int K;        // bytes (elements)
+  const int* brow = nullptr;  // B_GATHER: the tile's B rows (as MainBf16T)
+  int nrecB = 0;              // B_GATHER: bytes of B
 
   __device__ inline void limit_k(int k) { K = min(K, k); }
   __device__ static char* stage0() { return MainBf16::stage0(); }
@@ -401,11 +425,21 @@ struct MainFp8 {
     const __amdgpu_buffer_rsrc_t ra =
         __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)m0 * lda), (short)0, rowsA * (int)lda, RSRC_WORD3);
     const __amdgpu_buffer_rsrc_t rb =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(B + (int64_t)n0 * ldb), (short)0, rowsB * (int)ldb, RSRC_WORD3);
+        B_GATHER ? __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, nrecB, RSRC_WORD3)
+                 : __builtin_amdgcn_make_buffer_rsrc((void*)(B + (int64_t)n0 * ldb), (short)0, rowsB * (int)ldb,
+                                                     RSRC_WORD3);
     const int lrow = lane >> 3, lpc = lane & 7;
     const int ce = lpc ^ lds_swz(lrow), co = lpc ^ lds_swz(lrow + 8);
     const int rA = (w * LPW * 8 + lrow) * (int)lda, rB = (w * LPW * 8 + lrow) * (int)ldb;
     const int stepA = 8 * (int)lda, stepB = 8 * (int)ldb;
+    int rBg[LPW];
+    if constexpr (B_GATHER) {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int r = n0 + w * LPW * 8 + i * 8 + lrow;
+        rBg[i] = r < N ? brow[r] * (int)ldb : -1;
+      }
+    }
     const int nk = (K + ROWB - 1) / ROWB;
     auto issue = [&](int sg, int kt) __attribute__((always_inline)) {
       char* st = (sg ? S1 : S0) + w * LPW * 1024;
@@ -417,8 +451,12 @@ struct MainFp8 {
         const int c16 = ((i & 1) ? co : ce) * 16;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, STCE_LDS(st + i * 1024), 16, in ? rA + i * stepA + c16 : 0x7ffffff0,
                                                  k0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, STCE_LDS(st + TILEB + i * 1024), 16,
-                                                 in ? rB + i * stepB + c16 : 0x7ffffff0, k0, 0, 0);
+        if constexpr (B_GATHER)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, STCE_LDS(st + TILEB + i * 1024), 16,
+                                                   (in && rBg[i] >= 0) ? rBg[i] + c16 : 0x7ffffff0, k0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, STCE_LDS(st + TILEB + i * 1024), 16,
+                                                   in ? rB + i * stepB + c16 : 0x7ffffff0, k0, 0, 0);
       }
     };
     const int frow = lane & 15, fq = lane >> 4, sw = lds_swz(frow);
@@ -461,6 +499,9 @@ struct MainFp8 {
     __syncthreads();  // the epilogue may reuse the LDS
   }
 };
+
+using MainFp8 = MainFp8T<false>;
+using MainFp8G = MainFp8T<true>;
 
 // ---------------------------------------------------------------------------
 // fp32 main loop (plain fused multiply-adds, same accumulator layout).  Used
@@ -567,6 +608,47 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(Main mainloop, Epi ep
     for (int j = 0; j < ACC_J; ++j) acc[i][j] = f32x4{};
   mainloop.run(acc, tm * GM, tn * GN, smem);
   epi(acc, tm * GM, tn * GN, Main::epilogue_lds(smem), Main::epilogue_lds1(smem));
+}
+
+// A product over work items whose B rows are gathered: A tile j (rows j GM ..)
+// pairs with the B rows listed for it, GN at a time.  woff: exclusive scan of
+// the tiles' work-item counts (woff[ntiles] = the total); item w of tile j
+// takes rows[boff[j] + (w - woff[j]) GN ..] up to cnt[j] rows.  Workgroups
+// past the total return at once (the grid is sized for the most items).
+struct WorkList {
+  const int* woff;   // [ntiles + 1]
+  const int* cnt;    // [ntiles]
+  const int* boff;   // [ntiles]
+  const int* rows;
+  int ntiles;
+};
+
+template <class Main, class Epi>
+__global__ __launch_bounds__(GTHREADS, 1) void gemm_worklist_kernel(Main mainloop, Epi epi, WorkList wl) {
+  const int w = blockIdx.x;
+  if (w >= wl.woff[wl.ntiles]) return;
+  int lo = 0, hi = wl.ntiles - 1;  // the largest j with woff[j] <= w
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (wl.woff[mid] <= w)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int j = lo, it = w - wl.woff[j];
+  const int* rows = wl.rows + wl.boff[j] + it * GN;
+  const int ncol = min(GN, wl.cnt[j] - it * GN);
+  mainloop.brow = rows;
+  mainloop.N = ncol;
+  epi.colpos = rows;
+  epi.ncols = ncol;
+  AccTile acc;
+#pragma unroll
+  for (int i = 0; i < ACC_I; ++i)
+#pragma unroll
+    for (int jj = 0; jj < ACC_J; ++jj) acc[i][jj] = f32x4{};
+  mainloop.run(acc, j * GM, 0, nullptr);
+  epi(acc, j * GM, 0, Main::epilogue_lds(nullptr), Main::epilogue_lds1(nullptr));
 }
 
 }  // namespace stce

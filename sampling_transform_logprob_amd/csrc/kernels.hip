@@ -472,6 +472,15 @@ hipError_t launch_gemm_splitk(const Main& mn, const Epi& ep, int64_t tiles_m, in
   return hipGetLastError();
 }
 
+template <class Main, class Epi>
+hipError_t launch_gemm_worklist(const Main& mn, const Epi& ep, const WorkList& wl, int64_t max_items, hipStream_t s) {
+  if (max_items <= 0) return hipSuccess;
+  auto kern = gemm_worklist_kernel<Main, Epi>;
+  static_assert(gemm_dyn_lds<Main, Epi>() == 0, "the work-list product takes no dynamic LDS");
+  hipLaunchKernelGGL(kern, dim3((unsigned)max_items), dim3(GTHREADS), 0, s, mn, ep, wl);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_validate(int64_t T, int64_t V, int ignore, int64_t ignore_index, const float* temp,
@@ -721,35 +730,40 @@ hipError_t launch_class_slice(const ClassSliceArgs& a, hipStream_t s) {
   hipError_t e;
   // 1. recompute the slice's keys: dense rows' dz^T, sparse rows' entries
   {
-    EpiGrad ep{};
-    ep.perm = a.perm;
-    ep.cnt = a.cnt;
-    ep.temp = a.temp;
-    ep.target = a.target;
-    ep.st = a.st;
-    ep.g = a.g;
-    ep.dT = a.dT;
-    ep.ld_dT = a.Tp;
-    ep.v0 = (int)a.v0;
-    ep.Vs = (int)a.vs;
-    ep.Vs_pad = (int)a.vsp;
-    ep.N = (int)a.T;
-    ep.N_pad = (int)a.Tp;
-    ep.bf16_lane = a.bf16_lane;
-    ep.rowcnt = a.rowcnt;
-    ep.list = a.list;
-    ep.cntj = a.keys_out ? nullptr : a.cntj;
-    ep.keys_out = a.keys_out;
-    ep.ld_keys = a.ld_keys;
+    auto fill = [&](auto& ep) {
+      ep.perm = a.perm;
+      ep.cnt = a.cnt;
+      ep.temp = a.temp;
+      ep.target = a.target;
+      ep.st = a.st;
+      ep.g = a.g;
+      ep.dT = a.dT;
+      ep.ld_dT = a.Tp;
+      ep.v0 = (int)a.v0;
+      ep.Vs = (int)a.vs;
+      ep.Vs_pad = (int)a.vsp;
+      ep.N = (int)a.T;
+      ep.N_pad = (int)a.Tp;
+      ep.bf16_lane = a.bf16_lane;
+      ep.rowcnt = a.rowcnt;
+      ep.list = a.list;
+      ep.cntj = a.keys_out ? nullptr : a.cntj;
+      ep.keys_out = a.keys_out;
+      ep.ld_keys = a.ld_keys;
+    };
     DynLimits dyn{};
-    dyn.n_lim = a.keys_out ? nullptr : &a.cnt->active;
+    dyn.n_lim = a.keys_out ? nullptr : &a.cnt->full;  // dense and sparse rows (tiled ones: the tile recompute)
     ProfScope ps(KIND_DLOGITS, s);
     if (a.W8) {  // fp8 lane: the forward's e4m3 product and scaling
+      EpiGradT<true, false> ep{};
+      fill(ep);
       ep.row_scale = a.w_scale + a.v0;
       ep.col_scale = a.h_scale;
       MainFp8 mn{a.W8 + a.v0 * a.H, a.H, (int)a.vs, a.h8_perm, a.H, (int)a.T, (int)a.H};
       e = launch_gemm(mn, ep, ceil_div(a.vsp, GM), ceil_div(a.Tp, GN), s, dyn);
     } else {
+      EpiGradT<false, false> ep{};
+      fill(ep);
       MainBf16 mn{a.W + a.v0 * a.H, a.H, (int)a.vs, a.h_perm, a.H, (int)a.T, (int)a.H};
       e = launch_gemm(mn, ep, ceil_div(a.vsp, GM), ceil_div(a.Tp, GN), s, dyn);
     }
@@ -850,6 +864,55 @@ hipError_t fused_grads_impl(const FusedGradArgs& a, hipStream_t s) {
 hipError_t launch_fused_chunk_grads(const FusedGradArgs& a, hipStream_t s) {
   if (a.dtype == 1) return fused_grads_impl<bf16, MainBf16>(a, s);
   return fused_grads_impl<float, MainF32>(a, s);
+}
+
+
+hipError_t launch_tiled_recompute(const TiledArgs& a, hipStream_t s) {
+  static_assert(TILE_COLS == GN, "a work item is one N tile of the product");
+  hipError_t e;
+  {
+    ProfScope ps(KIND_TILE_LISTS, s);
+    if ((e = launch_tile_lists(a.lists, s))) return e;
+  }
+  auto fill = [&](auto& ep) {
+    ep.perm = a.perm;
+    ep.cnt = a.cnt;
+    ep.temp = a.temp;
+    ep.target = a.target;
+    ep.st = a.st;
+    ep.g = a.g;
+    ep.dT = nullptr;  // no dense row here
+    ep.ld_dT = 0;
+    ep.v0 = 0;
+    ep.Vs = (int)a.V;
+    ep.Vs_pad = (int)round_up(a.V, 64);
+    ep.N = (int)a.T;
+    ep.N_pad = (int)round_up(a.T, 64);
+    ep.bf16_lane = a.bf16_lane;
+    ep.rowcnt = a.rowcnt;
+    ep.list = a.list;
+    ep.cntj = a.keys_out ? nullptr : a.cntj;
+    ep.keys_out = a.keys_out;
+    ep.ld_keys = a.ld_keys;
+  };
+  const WorkList wl{a.lists.twoff, a.lists.tcnt, a.lists.toff, a.lists.bucket, (int)a.lists.ntv};
+  // most work items: a tile's items are ceil(count / GN) <= count / GN + 1
+  const int64_t items = a.lists.ntv + ceil_div(NTILE * a.T, GN);
+  ProfScope ps(KIND_TILE_RECOMPUTE, s);
+  if (a.W8) {
+    EpiGradT<true, true> ep{};
+    fill(ep);
+    ep.row_scale = a.w_scale;
+    ep.col_scale = a.h_scale;
+    MainFp8G mn{a.W8, a.H, (int)a.V, a.h8_perm, a.H, 0, (int)a.H};
+    mn.nrecB = (int)(a.T * a.H);
+    return launch_gemm_worklist(mn, ep, wl, items, s);
+  }
+  EpiGradT<false, true> ep{};
+  fill(ep);
+  MainBf16G mn{a.W, a.H, (int)a.V, a.h_perm, a.H, 0, (int)a.H};
+  mn.nrecB = (int)(a.T * a.H * 2);
+  return launch_gemm_worklist(mn, ep, wl, items, s);
 }
 
 }  // namespace stce

@@ -11,7 +11,7 @@ enum : int {
   KIND_VALIDATE = 1, KIND_PROJECTION = 2, KIND_SELECT = 3, KIND_DLOGITS = 4, KIND_GRAD_WEIGHT = 5,
   KIND_GRAD_HIDDEN = 6, KIND_TRANSPOSE = 7, KIND_PARTIALS = 8, KIND_POLICY_LOSS = 9, KIND_DZ_KEYS = 10,
   KIND_SPLIT_SUM = 11, KIND_PRESCALE = 12, KIND_CLASSIFY = 13, KIND_SPARSE_DW = 14, KIND_SPARSE_DH = 15,
-  KIND_REPROJECT = 16, KIND_QUANTIZE = 17
+  KIND_REPROJECT = 16, KIND_QUANTIZE = 17, KIND_TILE_LISTS = 18, KIND_TILE_RECOMPUTE = 19
 };
 
 // Launch-timing hook (no-op unless a profile is attached to this thread).
@@ -135,12 +135,33 @@ hipError_t launch_bwd_slice(const BwdSliceArgs& a, hipStream_t s);
 
 // ---- the backward with row classes (bf16 operands; sparse.hip) ----------
 // Classification: counts of the classes into *cnt, the permutation perm
-// (permuted position -> row: dense rows, then sparse, then empty, each in row
-// order) and a cleared entry counter per position.  blk: scratch of
+// (permuted position -> row: dense rows, then sparse, tiled and empty ones,
+// each in row order) and a cleared entry counter per position.  tl: the
+// rows' tile lists (null: no row is tiled).  blk: scratch of
 // grad_class_blk_ints(T) ints.
 size_t grad_class_blk_ints(int64_t T);
-hipError_t launch_grad_classes(const RowState* st, const float* g, int64_t T, int* blk, GradCounts* cnt, int* perm,
-                               int* rowcnt, hipStream_t s);
+hipError_t launch_grad_classes(const RowState* st, const RowTiles* tl, const float* g, int64_t T, int* blk,
+                               GradCounts* cnt, int* perm, int* rowcnt, hipStream_t s);
+
+// Work lists of the tile recompute: per vocabulary tile j < ntv, the tiled
+// positions listing it (bucket[toff[j] .. toff[j] + tcnt[j])) and its work
+// items (twoff: exclusive scan of ceil(tcnt / TILE_COLS), twoff[ntv] the
+// total).  tfill: scratch [ntv]; sums: scratch of scan_sums_ints(ntv).
+constexpr int TILE_COLS = 256;  // positions per work item: the product's N tile
+struct TileListArgs {
+  const int* perm;
+  const GradCounts* cnt;
+  const RowTiles* tiles;  // [T] by row
+  int64_t T, ntv;
+  int* tcnt;              // [ntv]
+  int* tfill;             // [ntv]
+  int* toff;              // [ntv + 1]
+  int* twork;             // [ntv]
+  int* twoff;             // [ntv + 1]
+  int* sums;
+  int* bucket;            // [NTILE * T]
+};
+hipError_t launch_tile_lists(const TileListArgs& a, hipStream_t s);
 // out[n] = in[perm[n]] for rows of H elements of the dtype (1 bf16, 2 fp32).
 hipError_t launch_gather_rows(int dtype, const void* in, const int* perm, int64_t T, int64_t H, void* out,
                               hipStream_t s);
@@ -185,6 +206,36 @@ struct ClassSliceArgs {
   int64_t ld_keys;
 };
 hipError_t launch_class_slice(const ClassSliceArgs& a, hipStream_t s);
+
+// The tile recompute: the keys of the tiled rows (positions [full, active))
+// on the vocabulary tiles their lists name, gathered GN positions at a time
+// per tile, with the recompute epilogue of the whole-vocabulary product
+// (their dz entries and per-vocabulary-row counts).  The hidden rows are
+// read by permuted position: the product addresses them with 32-bit offsets,
+// so T H bytes (fp8 codes) or 2 T H bytes (bf16) must stay below 2^31 - 2^22.
+struct TiledArgs {
+  const bf16* W;          // [V][H] bf16, or null with W8
+  const uint8_t* W8;      // fp8 lane: [V][H] codes
+  const float* w_scale;   // fp8 lane: [V]
+  const bf16* h_perm;     // [T][H] permuted hidden rows (bf16)
+  const uint8_t* h8_perm; // fp8 lane: their codes
+  const float* h_scale;   // fp8 lane: [rows] by row
+  const int* perm;
+  const GradCounts* cnt;
+  const float* temp;
+  const int64_t* target;
+  const RowState* st;
+  const float* g;
+  int* rowcnt;
+  SpEntry* list;
+  int* cntj;              // [V] or null
+  int64_t T, H, V;
+  int bf16_lane;
+  float* keys_out;        // parity export (their listed tiles only), or null
+  int64_t ld_keys;
+  TileListArgs lists;
+};
+hipError_t launch_tiled_recompute(const TiledArgs& a, hipStream_t s);
 
 // The sparse rows' products after the last slice: the weight gradient from
 // per-vocabulary-row buckets of the entries, the hidden gradient of every

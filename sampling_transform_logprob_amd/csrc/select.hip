@@ -148,6 +148,7 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
       P.logprob[orow] = nan;
       RowState rs{};
       P.state[orow] = rs;
+      if (P.tiles) P.tiles[orow] = RowTiles{};
       if (P.lse_full) P.lse_full[orow] = nan;
       if (P.ent_full) P.ent_full[orow] = nan;
       if (P.ent_supp) P.ent_supp[orow] = nan;
@@ -209,6 +210,7 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
       if (fl & ROW_IGNORED) rs.flags = ROW_VALID | ROW_IGNORED;
       P.logprob[orow] = lane_logprob(P, (fl & ROW_IGNORED) ? 0.0f : (float)fmin((double)sy - lse_full, 0.0));
       P.state[orow] = rs;
+      if (P.tiles) P.tiles[orow] = RowTiles{};
       if (P.ent_supp) P.ent_supp[orow] = (float)h_full;
     }
     return;
@@ -670,6 +672,38 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
     }
     const double E = block_reduce(es, AddD{}, S.sd);
     if (tid == 0) P.ent_supp[orow] = (float)(log(S.mass_s) - E / S.mass_s);
+  }
+  // The vocabulary tiles that can hold a support token: those whose maximum
+  // reaches the last support key (a superset of the support's tiles, from the
+  // partials), in increasing order; kept when there are at most NTILE.
+  if (P.tiles) {
+    const float kv = key_value(comp_key(S.u.cand[n_loc - 1]));
+    RowTiles* rt = P.tiles + orow;
+    const int lane = tid & 63;
+    int base = 0;
+    __syncthreads();
+    for (int t0 = 0; t0 < P.ntv && base <= NTILE; t0 += ST) {
+      const int t = t0 + tid;
+      const bool hit = t < P.ntv && pp[t].mx >= kv;
+      const uint64_t bal = __ballot(hit);
+      if (lane == 0) S.si[w] = __popcll(bal);
+      __syncthreads();
+      int off = base, tot = 0;
+#pragma unroll
+      for (int q = 0; q < ST / 64; ++q) {
+        off += q < w ? S.si[q] : 0;
+        tot += S.si[q];
+      }
+      const int at = off + __popcll(bal & ((1ull << lane) - 1ull));
+      if (hit && at < NTILE) rt->t[at] = (uint16_t)t;
+      __syncthreads();  // S.si is rewritten by the next pass
+      base += tot;
+    }
+    // unused entries (all of them when there are too many tiles) are zero, so
+    // the state's bytes are a function of the inputs
+    const int keep = base <= NTILE ? base : 0;
+    if (tid >= keep && tid < NTILE) rt->t[tid] = 0;
+    if (tid == 0) rt->n = (uint16_t)keep;
   }
   if (tid == 0) {
     const uint64_t bc = S.u.cand[n_loc - 1];

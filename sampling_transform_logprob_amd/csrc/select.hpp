@@ -52,6 +52,7 @@ struct SelParams {
   const float* min_p;       // [R] or null
   float* logprob;           // [R]
   RowState* state;          // [R]
+  RowTiles* tiles;          // [R] or null (more than 65,535 vocabulary tiles)
   int V;
   // side outputs, each [R] or null; the entropies need the partials' sums
   float* lse_full;          // log-sum-exp of the keys over the row

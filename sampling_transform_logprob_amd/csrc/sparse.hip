@@ -6,13 +6,17 @@
 // rows.  Rows whose support holds at most NSP tokens take these sums
 // directly; the others go through the matrix-core products (kernels.hip).
 //
-//   1. classification: every row is dense, sparse or empty (no gradient);
-//      the rows are placed dense first, then sparse, then empty, each class
-//      in row order (a block count, one scan, a placement pass), and the
-//      hidden states are gathered into that order;
+//   1. classification: every row is dense, sparse, tiled (sparse, with a
+//      list of the vocabulary tiles that can hold its support) or empty (no
+//      gradient); the rows are placed in that class order, each class in row
+//      order (a block count, one scan, a placement pass), and the hidden
+//      states are gathered into that order;
 //   2. the recompute product (EpiGrad) writes the dense rows' dz and appends
 //      each sparse row's nonzero dz to its entry list, counting the entries
-//      of every vocabulary row;
+//      of every vocabulary row; the tiled rows' keys are recomputed on their
+//      listed tiles only (a product over (tile, rows) work items: per tile
+//      the positions listing it, filed by a count, a scan and a fill pass),
+//      with the same epilogue;
 //   3. weight gradient: an exclusive scan of the per-vocabulary-row counts,
 //      a pass that files each entry into its vocabulary row's bucket, and one
 //      workgroup per vocabulary row that sums its bucket's dz h[t] terms in
@@ -31,10 +35,11 @@ namespace {
 
 constexpr int CB = 1024;  // rows per classification block (256 threads x 4)
 
-__device__ inline int grad_class(const RowState& rs, float g) {
+// ntile: the row's tile-list length (0: none, or tile recompute off)
+__device__ inline int grad_class(const RowState& rs, float g, int ntile) {
   if ((rs.flags & (ROW_VALID | ROW_IN_SUPPORT)) != (ROW_VALID | ROW_IN_SUPPORT) || g == 0.f) return GRAD_EMPTY;
   if (!(rs.flags & ROW_FILTERED) || rs.n > NSP) return GRAD_DENSE;
-  return GRAD_SPARSE;
+  return ntile > 0 ? GRAD_TILED : GRAD_SPARSE;
 }
 
 // Inclusive scan over the 256 threads of a workgroup (4 waves): wave scans
@@ -55,59 +60,62 @@ __device__ inline int block_incl_scan(int v, int* scratch) {
 }
 
 // Per block of CB rows: how many rows of each class.
-__global__ __launch_bounds__(256) void class_count_kernel(const RowState* st, const float* g, int64_t T,
-                                                          int* blk) {
+__global__ __launch_bounds__(256) void class_count_kernel(const RowState* st, const RowTiles* tl, const float* g,
+                                                          int64_t T, int* blk) {
   __shared__ int scr[4];
   const int64_t r0 = (int64_t)blockIdx.x * CB + threadIdx.x * 4;
-  int c[3] = {0, 0, 0};
+  int c[GRAD_CLASSES] = {0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    if (r0 + i < T) ++c[grad_class(st[r0 + i], g[r0 + i])];
+    if (r0 + i < T) ++c[grad_class(st[r0 + i], g[r0 + i], tl ? tl[r0 + i].n : 0)];
 #pragma unroll
-  for (int k = 0; k < 3; ++k) {
+  for (int k = 0; k < GRAD_CLASSES; ++k) {
     const int s = block_incl_scan(c[k], scr);
-    if (threadIdx.x == 255) blk[blockIdx.x * 3 + k] = s;
+    if (threadIdx.x == 255) blk[blockIdx.x * GRAD_CLASSES + k] = s;
   }
 }
 
 // One workgroup: exclusive scan of the block counts (in place, per class)
 // and the class totals.
 __global__ __launch_bounds__(1024) void class_scan_kernel(int* blk, int nblk, GradCounts* cnt) {
-  __shared__ int part[1024 * 3];
-  __shared__ int tot[3];
+  constexpr int NC = GRAD_CLASSES;
+  __shared__ int part[1024 * NC];
+  __shared__ int tot[NC];
   const int t = threadIdx.x;
   // thread t scans blocks [t * per, (t + 1) * per)
   const int per = (nblk + 1023) / 1024;
-  int s[3] = {0, 0, 0};
+  int s[NC] = {0, 0, 0, 0};
   for (int b = t * per; b < min(nblk, (t + 1) * per); ++b)
 #pragma unroll
-    for (int k = 0; k < 3; ++k) s[k] += blk[b * 3 + k];
+    for (int k = 0; k < NC; ++k) s[k] += blk[b * NC + k];
 #pragma unroll
-  for (int k = 0; k < 3; ++k) part[t * 3 + k] = s[k];
+  for (int k = 0; k < NC; ++k) part[t * NC + k] = s[k];
   __syncthreads();
-  if (t < 3) {
+  if (t < NC) {
     int run = 0;
     for (int i = 0; i < 1024; ++i) {
-      const int x = part[i * 3 + t];
-      part[i * 3 + t] = run;
+      const int x = part[i * NC + t];
+      part[i * NC + t] = run;
       run += x;
     }
     tot[t] = run;
   }
   __syncthreads();
-  int run[3] = {part[t * 3], part[t * 3 + 1], part[t * 3 + 2]};
+  int run[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) run[k] = part[t * NC + k];
   for (int b = t * per; b < min(nblk, (t + 1) * per); ++b)
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int x = blk[b * 3 + k];
-      blk[b * 3 + k] = run[k];
+    for (int k = 0; k < NC; ++k) {
+      const int x = blk[b * NC + k];
+      blk[b * NC + k] = run[k];
       run[k] += x;
     }
   if (t == 0) {
     GradCounts c;
-    c.dense = tot[0];
-    c.sparse = tot[1];
-    c.active = tot[0] + tot[1];
+    c.dense = tot[GRAD_DENSE];
+    c.full = c.dense + tot[GRAD_SPARSE];
+    c.active = c.full + tot[GRAD_TILED];
     c.pad = 0;
     *cnt = c;
   }
@@ -115,23 +123,24 @@ __global__ __launch_bounds__(1024) void class_scan_kernel(int* blk, int nblk, Gr
 
 // Places every row at its permuted position (dense, then sparse, then empty;
 // row order within a class) and clears the position's entry counter.
-__global__ __launch_bounds__(256) void class_place_kernel(const RowState* st, const float* g, int64_t T,
-                                                          const int* blk, const GradCounts* cnt, int* perm,
+__global__ __launch_bounds__(256) void class_place_kernel(const RowState* st, const RowTiles* tl, const float* g,
+                                                          int64_t T, const int* blk, const GradCounts* cnt, int* perm,
                                                           int* rowcnt) {
   __shared__ int scr[4];
   const int64_t r0 = (int64_t)blockIdx.x * CB + threadIdx.x * 4;
   int cls[4];
-  int c[3] = {0, 0, 0};
+  int c[GRAD_CLASSES] = {0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    cls[i] = r0 + i < T ? grad_class(st[r0 + i], g[r0 + i]) : -1;
+    cls[i] = r0 + i < T ? grad_class(st[r0 + i], g[r0 + i], tl ? tl[r0 + i].n : 0) : -1;
     if (cls[i] >= 0) ++c[cls[i]];
   }
   const GradCounts n = *cnt;
-  const int cls_base[3] = {0, n.dense, n.active};
-  int pos[3];
+  const int cls_base[GRAD_CLASSES] = {0, n.dense, n.full, n.active};
+  int pos[GRAD_CLASSES];
 #pragma unroll
-  for (int k = 0; k < 3; ++k) pos[k] = cls_base[k] + blk[blockIdx.x * 3 + k] + block_incl_scan(c[k], scr) - c[k];
+  for (int k = 0; k < GRAD_CLASSES; ++k)
+    pos[k] = cls_base[k] + blk[blockIdx.x * GRAD_CLASSES + k] + block_incl_scan(c[k], scr) - c[k];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (cls[i] >= 0) {
@@ -455,19 +464,71 @@ __global__ __launch_bounds__(256) void sparse_dh_kernel(const int* perm, const G
   }
 }
 
+// Tile recompute work lists.  tile_count: per vocabulary tile, how many tiled
+// positions list it; tile_fill: each listing position appended to its tile's
+// bucket (order within a bucket is free: a key does not depend on its
+// column); tile_work: product work items per tile (GN positions each).
+// (a list is at most NTILE long and names tiles below ntv when the forward
+// wrote it; both are enforced so that no other state can index past them)
+__global__ __launch_bounds__(256) void tile_count_kernel(const int* perm, const GradCounts* cnt, const RowTiles* tl,
+                                                         int64_t T, int64_t ntv, int* tcnt) {
+  const GradCounts c = *cnt;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t n = c.full + (int64_t)blockIdx.x * 256 + threadIdx.x; n < c.active && n < T; n += stride) {
+    const RowTiles& r = tl[perm[n]];
+    const int nt = min((int)r.n, NTILE);
+    for (int i = 0; i < nt; ++i)
+      if (r.t[i] < ntv) atomicAdd(tcnt + r.t[i], 1);
+  }
+}
+
+__global__ __launch_bounds__(256) void tile_fill_kernel(const int* perm, const GradCounts* cnt, const RowTiles* tl,
+                                                        int64_t T, int64_t ntv, const int* toff, int* tfill,
+                                                        int* bucket) {
+  const GradCounts c = *cnt;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t n = c.full + (int64_t)blockIdx.x * 256 + threadIdx.x; n < c.active && n < T; n += stride) {
+    const RowTiles& r = tl[perm[n]];
+    const int nt = min((int)r.n, NTILE);
+    for (int i = 0; i < nt; ++i) {
+      const int j = r.t[i];
+      if (j < ntv) bucket[toff[j] + atomicAdd(tfill + j, 1)] = (int)n;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void tile_work_kernel(const int* tcnt, int64_t ntv, int* twork) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j < ntv) twork[j] = (tcnt[j] + TILE_COLS - 1) / TILE_COLS;
+}
+
 }  // namespace
 
-hipError_t launch_grad_classes(const RowState* st, const float* g, int64_t T, int* blk, GradCounts* cnt, int* perm,
-                               int* rowcnt, hipStream_t s) {
-  ProfScope ps(KIND_CLASSIFY, s);
-  const unsigned nb = (unsigned)ceil_div(T, CB);
-  hipLaunchKernelGGL(class_count_kernel, dim3(nb), dim3(256), 0, s, st, g, T, blk);
-  hipLaunchKernelGGL(class_scan_kernel, dim3(1), dim3(1024), 0, s, blk, (int)nb, cnt);
-  hipLaunchKernelGGL(class_place_kernel, dim3(nb), dim3(256), 0, s, st, g, T, blk, cnt, perm, rowcnt);
+hipError_t launch_tile_lists(const TileListArgs& a, hipStream_t s) {
+  hipError_t e;
+  if ((e = launch_fill_i32(a.tcnt, a.ntv, 0, s)) || (e = launch_fill_i32(a.tfill, a.ntv, 0, s))) return e;
+  const unsigned g = (unsigned)(ceil_div(a.T, 256) < 4096 ? ceil_div(a.T, 256) : 4096);
+  hipLaunchKernelGGL(tile_count_kernel, dim3(g), dim3(256), 0, s, a.perm, a.cnt, a.tiles, a.T, a.ntv, a.tcnt);
+  if ((e = launch_exclusive_scan(a.tcnt, a.ntv, a.sums, a.toff, s))) return e;
+  hipLaunchKernelGGL(tile_work_kernel, dim3((unsigned)ceil_div(a.ntv, 256)), dim3(256), 0, s, a.tcnt, a.ntv,
+                     a.twork);
+  if ((e = launch_exclusive_scan(a.twork, a.ntv, a.sums, a.twoff, s))) return e;
+  hipLaunchKernelGGL(tile_fill_kernel, dim3(g), dim3(256), 0, s, a.perm, a.cnt, a.tiles, a.T, a.ntv, a.toff,
+                     a.tfill, a.bucket);
   return hipGetLastError();
 }
 
-size_t grad_class_blk_ints(int64_t T) { return 3 * (size_t)ceil_div(T, CB); }
+hipError_t launch_grad_classes(const RowState* st, const RowTiles* tl, const float* g, int64_t T, int* blk,
+                               GradCounts* cnt, int* perm, int* rowcnt, hipStream_t s) {
+  ProfScope ps(KIND_CLASSIFY, s);
+  const unsigned nb = (unsigned)ceil_div(T, CB);
+  hipLaunchKernelGGL(class_count_kernel, dim3(nb), dim3(256), 0, s, st, tl, g, T, blk);
+  hipLaunchKernelGGL(class_scan_kernel, dim3(1), dim3(1024), 0, s, blk, (int)nb, cnt);
+  hipLaunchKernelGGL(class_place_kernel, dim3(nb), dim3(256), 0, s, st, tl, g, T, blk, cnt, perm, rowcnt);
+  return hipGetLastError();
+}
+
+size_t grad_class_blk_ints(int64_t T) { return GRAD_CLASSES * (size_t)ceil_div(T, CB); }
 
 hipError_t launch_gather_rows(int dtype, const void* in, const int* perm, int64_t T, int64_t H, void* out,
                               hipStream_t s) {

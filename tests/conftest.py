@@ -13,7 +13,9 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running test")
 
 
-@pytest.fixture(scope="session")
+@pytest.fixture
 def rng():
+    # a fresh generator per test: a test's inputs do not depend on which
+    # tests ran before it in the same process
     import numpy as np
     return np.random.Generator(np.random.PCG64(20261203))

@@ -88,3 +88,67 @@ def check_logprob(lp_gpu, ref):
     err = float(np.abs(lp[fin] - ref["logprob"][fin]).max()) if fin.any() else 0.0
     assert err < LOGPROB_ATOL, f"logprob max abs error {err}"
     return err
+
+
+NSP = 128
+
+
+def tiled_rows(info, g, V, dtype):
+    """Rows whose keys the backward recomputes on their listed tiles only (the
+    library's class rule): valid, target in support, filtered, at most NSP
+    support tokens, nonzero upstream gradient, a tile list, bf16 or fp8
+    operands."""
+    fl = info["flags"]
+    ok = ((fl & binding.FLAG_VALID) != 0) & ((fl & binding.FLAG_IN_SUPPORT) != 0) & (np.asarray(g) != 0)
+    sparse = ok & ((fl & binding.FLAG_FILTERED) != 0) & (info["n"] <= NSP)
+    return sparse & (info["ntile"] > 0) & (dtype != "f32") & (-(-V // 256) <= 65535)
+
+
+def check_tile_lists(info, keys, V):
+    """Each filtered row's tile list, against the tiles whose largest key
+    (of the forward's own keys) reaches its last support key: equal when
+    there are at most 31 of them, empty otherwise; and every support token
+    lies in a listed tile."""
+    T = keys.shape[0]
+    ntv = -(-V // 256)
+    pad = np.full((T, ntv * 256), -np.inf, np.float32)
+    pad[:, :V] = keys
+    tmax = pad.reshape(T, ntv, 256).max(2)
+    for r in range(T):
+        filt = (info["flags"][r] & binding.FLAG_FILTERED) != 0 and (info["flags"][r] & binding.FLAG_VALID) != 0
+        if not filt:
+            assert info["ntile"][r] == 0, r
+            continue
+        kthr = keys[r, info["id_thr"][r]]                        # the last support token's key
+        want = np.nonzero(tmax[r] >= kthr)[0]
+        got = info["tiles"][r, :info["ntile"][r]]
+        if len(want) <= 31:
+            assert np.array_equal(got, want), (r, got, want)
+        else:
+            assert info["ntile"][r] == 0, r
+
+
+def check_recomputed_keys(rk, fk, info, g, y, V, dtype):
+    """The backward's recomputed keys (NaN where it formed none) against the
+    forward's, bit for bit: every row's keys, but a tiled row's only on its
+    listed tiles (and none elsewhere); the target key and the row maximum
+    against the forward's state.  Returns (keys formed, tiled rows)."""
+    rkc, fkc = np.asarray(rk), np.asarray(fk)
+    T = fkc.shape[0]
+    tiled = tiled_rows(info, g, V, dtype)
+    formed = np.ones((T, V), bool)
+    for r in np.nonzero(tiled)[0]:
+        formed[r] = False
+        for j in info["tiles"][r, :info["ntile"][r]]:
+            formed[r, 256 * j:256 * (j + 1)] = True
+    assert np.array_equal(rkc[formed].view(np.int32), fkc[formed].view(np.int32)), \
+        "recomputed keys differ from the forward's"
+    assert np.isnan(rkc[~formed]).all()
+    y = np.asarray(y)
+    fy = formed[np.arange(T), y]
+    assert fy[tiled].all()                                        # a tiled row's target lies in its tiles
+    sy = rkc[np.arange(T), y]
+    assert np.array_equal(sy[fy].view(np.int32), info["target_key"][fy].view(np.int32))
+    mx = np.where(formed, rkc, -np.inf).max(1)
+    assert np.array_equal(mx.view(np.int32), info["row_max"].view(np.int32))
+    return int(formed.sum()), int(tiled.sum())

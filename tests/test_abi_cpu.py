@@ -36,7 +36,8 @@ def test_library_exports_every_declared_function(lib):
 
 def test_struct_layouts_match_header(tmp_path):
     assert ctypes.sizeof(binding.Problem) == 128
-    assert ctypes.sizeof(binding.RowInfo) == binding.STATE_BYTES_PER_ROW
+    assert ctypes.sizeof(binding.RowInfo) == binding.RECORD_BYTES
+    assert binding.STATE_BYTES_PER_ROW == binding.RECORD_BYTES + 2 * (1 + binding.NTILE)
     # the binding's field offsets against the C compiler's for the header
     fields = [f for f, _ in binding.Problem._fields_]
     src = tmp_path / "layout.c"
@@ -69,7 +70,7 @@ def test_workspace_sizes_are_host_computable(lib):
     # selection of one chunk overlaps the projection of the next) plus the
     # per-row flags: nothing scales with T x V
     assert f2 < 2 * (512 * 101 * 4 + 512 * 16 + 512 * 4) + 100000 * 4 + 4096
-    assert lib.stce_state_bytes(10) == 320
+    assert lib.stce_state_bytes(10) == 960
 
 
 def test_unsupported_dtype_is_one_actionable_error(lib):
@@ -213,9 +214,12 @@ def test_decode_state_roundtrip(lib):
                                       ("lse", "<f4"), ("lsef", "<f4"), ("m", "<f4"), ("sy", "<f4")]))
     raw["id_thr"] = [5, 6, 7]
     raw["n"] = [1, 2, 3]
+    tiles = np.zeros((3, 32), np.uint16)
+    tiles[1, :3] = [2, 9, 4000]                      # row 1 lists tiles 9 and 4000
     torch = pytest.importorskip("torch")
-    d = binding.decode_state(torch.from_numpy(raw.view(np.uint8).copy()))
+    d = binding.decode_state(torch.from_numpy(np.concatenate([raw.view(np.uint8), tiles.view(np.uint8).ravel()])))
     assert list(d["id_thr"]) == [5, 6, 7] and list(d["n"]) == [1, 2, 3]
+    assert list(d["ntile"]) == [0, 2, 0] and list(d["tiles"][1, :2]) == [9, 4000]
 
 
 def test_policy_loss_rejects_bad_parameters_before_launch(lib):

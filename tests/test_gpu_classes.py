@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import GRAD_RTOL, dev, meta_of, rel_fro, say, targets, to_gpu
+from gpu_helpers import GRAD_RTOL, dev, meta_of, rel_fro, say, targets, tiled_rows, to_gpu
 from sampling_transform_logprob_amd import binding, workloads
 from sampling_transform_logprob_amd.workloads import round_bf16
 
@@ -126,3 +126,46 @@ def test_a_token_in_every_support_takes_the_windowed_bucket():
         f"{rel_fro(gw[17].cpu().numpy(), dW[17]):.2e})")
     assert rh < GRAD_RTOL and rw < GRAD_RTOL
     assert rel_fro(gw[17].cpu().numpy(), dW[17]) < GRAD_RTOL     # the windowed row itself (dz is bf16)
+
+
+@pytest.mark.parametrize("name,T,V", [("headline", 300, 30000), ("headline_fp8", 260, 20000), ("ties", 280, 20000)])
+def test_tile_recompute_equals_the_whole_vocabulary_recompute(name, T, V):
+    """A sparse row with a tile list has its keys recomputed on the listed
+    tiles only.  The same state with every list cleared sends those rows
+    through the whole-vocabulary recompute; both must give the same dz
+    entries.  dH sums a row's entries in vocabulary order, so it is bitwise
+    equal; dW sums a vocabulary row's entries in permuted-position order,
+    and clearing the lists moves tiled rows behind the other sparse rows, so
+    dW is bitwise equal when every sparse row is tiled (the placement does
+    not change) and otherwise equal up to fp32 summation order."""
+    w = workloads.make(name, T=T)
+    w["W"] = w["W"][:V]
+    if w.get("w_scale") is not None:
+        w["w_scale"] = w["w_scale"][:V]
+    w["V"] = V
+    y = targets(w)
+    G = to_gpu(w, y)
+    ws = {"weight_scale": G["weight_scale"]} if G["weight_scale"] is not None else {}
+    lp, st = binding.forward(G["h"], G["W"], G["target"], **meta_of(G), **ws)
+    g = torch.from_numpy(np.random.Generator(np.random.PCG64(T)).standard_normal(T).astype(np.float32)).to(dev())
+    st_full = st.clone()
+    st_full[T * binding.RECORD_BYTES:] = 0                         # no tile lists
+    gh, gw = binding.backward(G["h"], G["W"], G["target"], st, g, **meta_of(G), **ws, vocab_slice=8192)
+    gh0, gw0 = binding.backward(G["h"], G["W"], G["target"], st_full, g, **meta_of(G), **ws, vocab_slice=8192)
+    torch.cuda.synchronize()
+    info = binding.decode_state(st)
+    tiled = tiled_rows(info, g.cpu().numpy(), V, w["dtype"])
+    say(f"tile recompute {name}: T={T} V={V}: {int(tiled.sum())} tiled rows, "
+        f"{int(info['ntile'][tiled].sum())} (row, tile) pairs of {T * (-(-V // 256))}")
+    assert tiled.sum() > (T // 3 if name != "ties" else 0)
+    assert torch.equal(gh, gh0)
+    fl = info["flags"]
+    active = ((fl & binding.FLAG_VALID) != 0) & ((fl & binding.FLAG_IN_SUPPORT) != 0) & (g.cpu().numpy() != 0)
+    sparse = active & ((fl & binding.FLAG_FILTERED) != 0) & (info["n"] <= NSP)
+    if np.array_equal(sparse, tiled):
+        assert torch.equal(gw, gw0)
+    else:
+        err = (gw - gw0).abs().max().item() / gw0.abs().max().item()
+        say(f"  dW: placement differs ({int((sparse & ~tiled).sum())} sparse rows without a list); "
+            f"max difference {err:.1e} of the largest entry")
+        assert err < 1e-5

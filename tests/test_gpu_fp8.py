@@ -15,7 +15,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import (GRAD_RTOL, check_logprob, check_support, dev, meta_of, rel_fro, say, targets, to_gpu)
+from gpu_helpers import (GRAD_RTOL, check_logprob, check_recomputed_keys, check_support, check_tile_lists, dev,
+                         meta_of, rel_fro, say, targets, to_gpu)
 from sampling_transform_logprob_amd import binding, workloads
 from sampling_transform_logprob_amd.workloads import round_bf16
 
@@ -145,10 +146,11 @@ def test_fp8_workload_parity(name, T, V, dense):
     rk = binding.recompute_keys(G["h"], G["W"], G["target"], st, gg, **meta_of(G), weight_scale=ws)
     torch.cuda.synchronize()
     kc = keys.cpu().numpy()
-    assert torch.equal(rk.view(torch.int32), keys.view(torch.int32)), "recomputed keys differ from the forward's"
+    info = binding.decode_state(st)
+    check_tile_lists(info, kc, V)
+    check_recomputed_keys(rk.cpu().numpy(), kc, info, g, y, V, "fp8")
     ref = oracle.forward(w["h"], w["W"], y, w["temperature"], w["top_k"], w["top_p"], w["min_p"], keys=kc,
                          lane="fp8", w_scale=w["w_scale"])
-    info = binding.decode_state(st)
     near = check_support(info, ref, name)
     err = check_logprob(lp.cpu().numpy(), ref)
     dH, dW = oracle.backward(w["h"], w["W"], y, ref, g, w["temperature"], w_scale=w["w_scale"])
@@ -200,4 +202,4 @@ def test_fp8_rows_the_candidates_cannot_decide_are_reprojected():
     assert (kc[crowd].argsort(1)[:, -4:] < 4).all()
     lp1, st1 = binding.forward(G["h"][:40], G["W"], G["target"][:40],
                                **{k: v[:40] for k, v in meta_of(G).items()}, weight_scale=ws, chunk_rows=1)
-    assert torch.equal(lp1.view(torch.int32), lp[:40].view(torch.int32)) and torch.equal(st1, st[:40 * 32])
+    assert torch.equal(lp1.view(torch.int32), lp[:40].view(torch.int32)) and torch.equal(st1, binding.state_prefix(st, 40))
