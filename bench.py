@@ -190,9 +190,9 @@ def mfma_busy_summary(args):
     disp = {}
     for r in csv.DictReader(open(files[0])):
         kn = r["Kernel_Name"]
-        if "gemm_kernel" not in kn:
+        if "gemm_kernel" not in kn and "gemm_worklist_kernel" not in kn:
             continue
-        e = disp.setdefault(r["Dispatch_Id"], {"name": kn})
+        e = disp.setdefault(r["Dispatch_Id"], {"name": kn, "id": int(r["Dispatch_Id"])})
         e[r["Counter_Name"]] = float(r["Counter_Value"])
         if "Start_Timestamp" in r and r["Start_Timestamp"]:
             e["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
@@ -206,15 +206,14 @@ def mfma_busy_summary(args):
              f"-d <D> -- python3 bench.py --steps 1 --warmup 2 --profile-steps 1 --no-cpu-baseline --config {args.config}",
              f"python3 bench.py --mfma-busy-summary <D> --config {args.config}", "```", "",
              "clock = GRBM_GUI_ACTIVE / 8 XCDs / duration; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
-             "(GRBM_GUI_ACTIVE / 8 x 1024 SIMDs); averaged over the launches of the last two steps that did work "
-             "(an empty re-projection returns at once).", "",
+             "(GRBM_GUI_ACTIVE / 8 x 1024 SIMDs); averaged over the launches of the later half of the run (the "
+             "counters serialize the launches). A product's launches that ran at least a quarter of its longest "
+             "are its full launches; the shorter ones (re-projections of a few rows, launches with no work) are "
+             "listed apart. Products none of whose launches ran a matrix instruction (above 0.05 ms) had no "
+             "work (no dense rows) and are not listed.", "",
              "| product | launches | avg ms (under counters) | clock GHz | MFMA busy |", "|---|---|---|---|---|"]
-    for label, es in sorted(groups.items()):
-        big = max(x.get("GRBM_GUI_ACTIVE", 0.0) for x in es)
-        work = [x for x in es if x.get("GRBM_GUI_ACTIVE", 0.0) >= 0.01 * big]
-        work = work[len(work) // 2:] if len(work) > 1 else work        # the later (warm) launches
-        if not work:
-            continue
+
+    def row(label, work):
         g = np.mean([x.get("GRBM_GUI_ACTIVE", 0.0) for x in work])
         busy = np.mean([x.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / max(x.get("GRBM_GUI_ACTIVE", 1.0) / 8 * 1024, 1.0)
                         for x in work])
@@ -222,6 +221,19 @@ def mfma_busy_summary(args):
         ms = f"{np.mean(ns) / 1e6:.3f}" if ns else "n/a"
         clock = f"{g / 8 / np.mean(ns):.2f}" if ns else "n/a"
         lines.append(f"| {label} | {len(work)} | {ms} | {clock} | {busy:.3f} |")
+
+    for label, es in sorted(groups.items()):
+        es = sorted(es, key=lambda x: x.get("id", 0))
+        es = es[len(es) // 2:] if len(es) > 1 else es                  # the later (warm) launches
+        if not es or max(x.get("ns", 0.0) for x in es) < 5e4 or not any(
+                x.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) > 0 for x in es):
+            continue
+        longest = max(x.get("ns", 0.0) for x in es)
+        full = [x for x in es if x.get("ns", 0.0) >= 0.25 * longest]
+        short = [x for x in es if 5e4 <= x.get("ns", 0.0) < 0.25 * longest]
+        row(label, full)
+        if short:
+            row(label + ", short launches", short)
     lines.append("")
     out = os.path.join(ROOT, "profiles", f"{args.config}_gemm_mfma_busy.md")
     with open(out, "w") as f:
@@ -331,7 +343,7 @@ def _counter_rows(path, name_part):
                     out.append(float(r["Counter_Value"]))
                 continue
             kn = r["Kernel_Name"]
-            if name_part in kn and "gemm_kernel" in kn and "MainBf16" in kn:
+            if name_part in kn and ("gemm_kernel" in kn or "gemm_worklist_kernel" in kn) and "MainF32" not in kn:
                 out.append(float(r["Counter_Value"]))
     # launches that did work: a re-projection with no row to project shares
     # the projection's symbol but returns at once (a counter near zero)

@@ -412,12 +412,18 @@ template <class E>
 __global__ __launch_bounds__(256) void sparse_dw_kernel(const int* off, const SpEntry* bucket, const E* h, int64_t H,
                                                         const GradCounts* cnt, int accumulate, float* dW, int64_t T,
                                                         int64_t V) {
-  __shared__ SpEntry ord[ORDER_CAP];
-  __shared__ SpEntry raw[ORDER_CAP];
-  __shared__ float win[WIN];
+  // the ordering buffers and the window are never used by the same row: one
+  // 16 KB region (more workgroups per compute unit to hide the row loads)
+  __shared__ union {
+    struct {
+      SpEntry ord[ORDER_CAP];
+      SpEntry raw[ORDER_CAP];
+    } o;
+    float win[WIN];
+  } L;
   const bool from_mem = accumulate || cnt->dense > 0;
   for (int64_t j = blockIdx.x; j < V; j += gridDim.x) {
-    sparse_dw_row(j, off, bucket, h, H, from_mem, dW, T, ord, raw, win);
+    sparse_dw_row(j, off, bucket, h, H, from_mem, dW, T, L.o.ord, L.o.raw, L.win);
     __syncthreads();  // the row's LDS before the next row's
   }
 }
@@ -469,30 +475,65 @@ __global__ __launch_bounds__(256) void sparse_dh_kernel(const int* perm, const G
 // bucket (order within a bucket is free: a key does not depend on its
 // column); tile_work: product work items per tile (GN positions each).
 // (a list is at most NTILE long and names tiles below ntv when the forward
-// wrote it; both are enforced so that no other state can index past them)
+// wrote it; both are enforced so that no other state can index past them).
+// With at most TH_LDS tiles a workgroup counts its rows' tiles in LDS and
+// adds each nonzero count to the global one once (the lists of thousands of
+// rows name the same few hundred tiles), and the fill reserves each tile's
+// range of slots once per workgroup the same way.
+constexpr int TH_LDS = 8192;
+constexpr int TROWS = 1024;  // positions per workgroup of the count and the fill
+
 __global__ __launch_bounds__(256) void tile_count_kernel(const int* perm, const GradCounts* cnt, const RowTiles* tl,
                                                          int64_t T, int64_t ntv, int* tcnt) {
+  __shared__ int hist[TH_LDS];
   const GradCounts c = *cnt;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t n = c.full + (int64_t)blockIdx.x * 256 + threadIdx.x; n < c.active && n < T; n += stride) {
+  const bool lds = ntv <= TH_LDS;
+  if (lds)
+    for (int j = threadIdx.x; j < ntv; j += 256) hist[j] = 0;
+  __syncthreads();
+  const int64_t n0 = c.full + (int64_t)blockIdx.x * TROWS;
+  for (int64_t n = n0 + threadIdx.x; n < n0 + TROWS && n < c.active && n < T; n += 256) {
     const RowTiles& r = tl[perm[n]];
     const int nt = min((int)r.n, NTILE);
-    for (int i = 0; i < nt; ++i)
-      if (r.t[i] < ntv) atomicAdd(tcnt + r.t[i], 1);
+    for (int i = 0; i < nt; ++i) {
+      const int j = r.t[i];
+      if (j < ntv) atomicAdd(lds ? hist + j : tcnt + j, 1);
+    }
   }
+  __syncthreads();
+  if (lds)
+    for (int j = threadIdx.x; j < ntv; j += 256)
+      if (hist[j]) atomicAdd(tcnt + j, hist[j]);
 }
 
 __global__ __launch_bounds__(256) void tile_fill_kernel(const int* perm, const GradCounts* cnt, const RowTiles* tl,
                                                         int64_t T, int64_t ntv, const int* toff, int* tfill,
                                                         int* bucket) {
+  __shared__ int hist[TH_LDS];
   const GradCounts c = *cnt;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t n = c.full + (int64_t)blockIdx.x * 256 + threadIdx.x; n < c.active && n < T; n += stride) {
+  const bool lds = ntv <= TH_LDS;
+  const int64_t n0 = c.full + (int64_t)blockIdx.x * TROWS;
+  if (lds) {
+    for (int j = threadIdx.x; j < ntv; j += 256) hist[j] = 0;
+    __syncthreads();
+    for (int64_t n = n0 + threadIdx.x; n < n0 + TROWS && n < c.active && n < T; n += 256) {
+      const RowTiles& r = tl[perm[n]];
+      const int nt = min((int)r.n, NTILE);
+      for (int i = 0; i < nt; ++i)
+        if (r.t[i] < ntv) atomicAdd(hist + r.t[i], 1);
+    }
+    __syncthreads();
+    // this workgroup's range of each tile's bucket
+    for (int j = threadIdx.x; j < ntv; j += 256)
+      if (hist[j]) hist[j] = toff[j] + atomicAdd(tfill + j, hist[j]);
+    __syncthreads();
+  }
+  for (int64_t n = n0 + threadIdx.x; n < n0 + TROWS && n < c.active && n < T; n += 256) {
     const RowTiles& r = tl[perm[n]];
     const int nt = min((int)r.n, NTILE);
     for (int i = 0; i < nt; ++i) {
       const int j = r.t[i];
-      if (j < ntv) bucket[toff[j] + atomicAdd(tfill + j, 1)] = (int)n;
+      if (j < ntv) bucket[lds ? atomicAdd(hist + j, 1) : toff[j] + atomicAdd(tfill + j, 1)] = (int)n;
     }
   }
 }
@@ -507,7 +548,9 @@ __global__ __launch_bounds__(256) void tile_work_kernel(const int* tcnt, int64_t
 hipError_t launch_tile_lists(const TileListArgs& a, hipStream_t s) {
   hipError_t e;
   if ((e = launch_fill_i32(a.tcnt, a.ntv, 0, s)) || (e = launch_fill_i32(a.tfill, a.ntv, 0, s))) return e;
-  const unsigned g = (unsigned)(ceil_div(a.T, 256) < 4096 ? ceil_div(a.T, 256) : 4096);
+  // one workgroup per TROWS positions of the whole row range (those past the
+  // tiled ones return at once)
+  const unsigned g = (unsigned)ceil_div(a.T, TROWS);
   hipLaunchKernelGGL(tile_count_kernel, dim3(g), dim3(256), 0, s, a.perm, a.cnt, a.tiles, a.T, a.ntv, a.tcnt);
   if ((e = launch_exclusive_scan(a.tcnt, a.ntv, a.sums, a.toff, s))) return e;
   hipLaunchKernelGGL(tile_work_kernel, dim3((unsigned)ceil_div(a.ntv, 256)), dim3(256), 0, s, a.tcnt, a.ntv,
