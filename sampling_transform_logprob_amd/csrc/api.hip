@@ -289,6 +289,9 @@ FusedLayout plan_fused(const stce_problem* p, int64_t gmax = INT64_MAX) {
   L.G = (int64_t)(kSliceBudgetBytes / ((double)es * (double)L.Vp * (double)L.C));
   if (L.G > nch) L.G = nch;
   if (L.G > gmax) L.G = gmax;
+  // the weight-gradient product reads the group's dz^T K-major with a row
+  // length of G C through 32-bit offsets over 256 rows: G C < 2^22
+  if (L.G * L.C >= (int64_t)1 << 22) L.G = (((int64_t)1 << 22) - 1) / L.C;
   if (L.G < 1) L.G = 1;
   size_t o = 0;
   L.flags = o; o = align_up(o + 4 * (size_t)T);

@@ -24,15 +24,15 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_traffic_follows_the_source_digest(monkeypatch):
-    kernels = ["projection", "dlogits", "grad_weight", "grad_hidden"]
-    for k in kernels:
-        path = bench.traffic_file(k, "headline")
+    cases = [(k, c) for k in ("projection", "tile_recompute") for c in ("headline", "headline_fp8")]
+    for k, c in cases:
+        path = bench.traffic_file(k, c)
         assert os.path.exists(path), path
         stamped = [l.split(":", 1)[1].strip() for l in open(path) if l.startswith("source_sha256:")]
         assert len(stamped) == 1 and len(stamped[0]) == 64
-    fresh = {k: bench.read_traffic(k, "headline") for k in kernels}
+    fresh = {kc: bench.read_traffic(*kc) for kc in cases}
     if all(v is not None for v in fresh.values()):
-        for k, v in fresh.items():
-            assert v > 1e9, (k, v)          # several GB per launch at the headline shape
+        for kc, v in fresh.items():
+            assert v > 1e9, (kc, v)         # several GB per launch at the headline shape
     monkeypatch.setattr(bench, "source_digest", lambda: "0" * 64)
-    assert all(bench.read_traffic(k, "headline") is None for k in kernels)
+    assert all(bench.read_traffic(*kc) is None for kc in cases)
