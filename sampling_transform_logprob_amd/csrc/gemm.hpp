@@ -466,34 +466,64 @@ struct MainFp8T {
       const u32x4 lo = *(const u32x4*)(base + c0), hi = *(const u32x4*)(base + c1);
       return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    auto tile = [&](int sg, int kt) __attribute__((always_inline)) {
-      const char* st = sg ? S1 : S0;
-      i32x8 fb[ACC_J];
+    // Fragments: B's four of a tile double-buffered by stage (fb[sg]); A's
+    // eight through a ring of four, read three ahead (A fragment i of a tile
+    // in slot i % 4, so every slot index is a compile-time constant).  A
+    // k-tile: before MFMA block i (four MFMAs), A fragment i + 3 is read;
+    // fragments 8.. are the next tile's, in the other stage, so the barrier
+    // sits before block 5, once every read of this stage has landed (A
+    // fragment 7 was read before block 4) and this wave's loads of the next
+    // tile are in.  After it the freed stage is refilled with tile kt + 2 and
+    // the next tile's B fragments and A fragments 0..2 are read while blocks
+    // 5..7 (12 MFMAs) run.
+    i32x8 fb[2][ACC_J], fa[4];
+    auto rdA = [&](const char* st, int i) __attribute__((always_inline)) {
+      return frag(st + offA + i * 16 * ROWB);
+    };
+    auto mma = [&](const i32x8& a, const i32x8 (&b)[ACC_J], int i) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < ACC_J; ++j) fb[j] = frag(st + offB + j * 16 * ROWB);
+      for (int j = 0; j < ACC_J; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+    };
+    auto tile = [&](auto sg_c, int kt) __attribute__((always_inline)) {
+      constexpr int sg = decltype(sg_c)::value;
+      const char* st = sg ? S1 : S0;
+      const char* nx = sg ? S0 : S1;
 #pragma unroll
       for (int i = 0; i < ACC_I; ++i) {
-        const i32x8 fa = frag(st + offA + i * 16 * ROWB);
+        if (i == 5) {
+          __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
+          __syncthreads();
+          __builtin_amdgcn_sched_barrier(0);
+          issue(sg, kt + 2);
 #pragma unroll
-        for (int j = 0; j < ACC_J; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+          for (int j = 0; j < ACC_J; ++j) fb[1 - sg][j] = frag(nx + offB + j * 16 * ROWB);
+        }
+        if (i + 3 < ACC_I)
+          fa[(i + 3) & 3] = rdA(st, i + 3);
+        else
+          fa[(i + 3) & 3] = rdA(nx, i + 3 - ACC_I);
+        mma(fa[i & 3], fb[sg], i);
+        if (i == 4) __builtin_amdgcn_sched_barrier(0);
       }
-      // tile kt + 1 has landed and every wave is done reading stage sg:
-      // refill it with tile kt + 2
-      __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
-      __syncthreads();
-      issue(sg, kt + 2);
     };
     issue(0, 0);
     issue(1, 1);
     __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
     __syncthreads();
+#pragma unroll
+    for (int j = 0; j < ACC_J; ++j) fb[0][j] = frag(S0 + offB + j * 16 * ROWB);
+#pragma unroll
+    for (int i = 0; i < 3; ++i) fa[i] = rdA(S0, i);
     // an even number of k-tiles (an odd count gets one all-zero tile) so that
-    // every read and load names its stage at compile time
+    // every read and load names its stage at compile time; the last pair's
+    // loads and next-tile reads fall past K or read a stage nobody uses
     const int nk2 = (nk + 1) & ~1;
+    using Z_ = std::integral_constant<int, 0>;
+    using O_ = std::integral_constant<int, 1>;
     for (int kt = 0; kt < nk2; kt += 2) {
-      tile(0, kt);
-      tile(1, kt + 1);
+      tile(Z_{}, kt);
+      tile(O_{}, kt + 1);
     }
     __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
     __syncthreads();  // the epilogue may reuse the LDS
