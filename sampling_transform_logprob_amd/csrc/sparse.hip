@@ -322,6 +322,52 @@ __device__ inline void ordered_sum(const SpEntry* ord, int ne, const E* X, int64
 }
 
 constexpr int ORDER_CAP = 1024;   // entries a weight-gradient bucket orders in LDS
+constexpr int WAVE_MAX = 64;      // entries a row summed by one wave orders in its lanes
+
+// One wave's up to WAVE_MAX entries (lane l < ne holds entry l; distinct
+// indices), placed in increasing index order: lane s gets the entry of rank
+// s (its rank by comparison with every other, then a lane permute).
+__device__ inline void wave_order(int ne, int& idx, float& v) {
+  const int lane = threadIdx.x & 63;
+  int r = lane;
+  if (lane < ne) {
+    r = 0;
+    for (int k = 0; k < ne; ++k) r += __builtin_amdgcn_readlane(idx, k) < idx ? 1 : 0;
+  }
+  idx = __builtin_amdgcn_ds_permute(r * 4, idx);
+  v = __int_as_float(__builtin_amdgcn_ds_permute(r * 4, __float_as_int(v)));
+}
+
+// acc[k] += v_s * X[idx_s, c0 + k] for the ordered entries s = 0 .. ne of a
+// wave (lane s holds entry s), in that order: ordered_sum's arithmetic.  The
+// entries are read with readlane (a uniform lane index, whatever the exec
+// mask: the last column pass may leave lanes idle).
+template <class E>
+__device__ inline void wave_ordered_sum(int ne, int idx, float v, const E* X, const float* xs, int64_t H, int64_t c0,
+                                        float (&acc)[8]) {
+  int s = 0;
+  for (; s + 4 <= ne; s += 4) {
+    float x[4][8], vs[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = __builtin_amdgcn_readlane(idx, s + u);
+      vs[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), s + u));
+      load8_row(X, xs, (int64_t)row, H, c0, x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(vs[u], x[u][k], acc[k]);
+  }
+  for (; s < ne; ++s) {
+    float x[8];
+    const int row = __builtin_amdgcn_readlane(idx, s);
+    const float vv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), s));
+    load8_row(X, xs, (int64_t)row, H, c0, x);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(vv, x[k], acc[k]);
+  }
+}
 constexpr int WIN = 4096;         // token positions per window beyond that
 
 // Weight gradient rows from the buckets: one workgroup per vocabulary row j,
@@ -407,7 +453,8 @@ __device__ inline void sparse_dw_row(int64_t j, const int* off, const SpEntry* b
   }
 }
 
-// Weight-gradient rows j = blockIdx.x, + gridDim.x, ... (sparse_dw_row).
+// Weight-gradient rows j = blockIdx.x, + gridDim.x, ... (sparse_dw_row) whose
+// bucket holds more than WAVE_MAX entries.
 template <class E>
 __global__ __launch_bounds__(256) void sparse_dw_kernel(const int* off, const SpEntry* bucket, const E* h, int64_t H,
                                                         const GradCounts* cnt, int accumulate, float* dW, int64_t T,
@@ -423,6 +470,7 @@ __global__ __launch_bounds__(256) void sparse_dw_kernel(const int* off, const Sp
   } L;
   const bool from_mem = accumulate || cnt->dense > 0;
   for (int64_t j = blockIdx.x; j < V; j += gridDim.x) {
+    if (off[j + 1] - off[j] <= WAVE_MAX) continue;  // (sparse_dw_wave_kernel's rows; uniform)
     sparse_dw_row(j, off, bucket, h, H, from_mem, dW, T, L.o.ord, L.o.raw, L.win);
     __syncthreads();  // the row's LDS before the next row's
   }
@@ -443,9 +491,10 @@ __global__ __launch_bounds__(256) void sparse_dh_kernel(const int* perm, const G
   const int64_t n = blockIdx.x;
   const GradCounts c = *cnt;
   if (n < c.dense || n >= T) return;
+  const int ne = n < c.active ? min(rowcnt[n], NSP) : 0;
+  if (ne <= WAVE_MAX) return;  // (sparse_dh_wave_kernel's rows)
   const int64_t t = perm[n];
   O* out = dH + t * H;
-  const int ne = n < c.active ? min(rowcnt[n], NSP) : 0;
   for (int i = threadIdx.x; i < ne; i += 256) raw[i] = list[n * NSP + i];
   __syncthreads();
   rank_order(raw, ne, ord);
@@ -466,6 +515,89 @@ __global__ __launch_bounds__(256) void sparse_dh_kernel(const int* perm, const G
     } else {
       *(f32x4*)(out + c0) = f32x4{acc[0], acc[1], acc[2], acc[3]};
       *(f32x4*)(out + c0 + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    }
+  }
+}
+
+// The rows with at most WAVE_MAX entries, one wave per row (the common case:
+// a top-k row's support, a vocabulary row reached by a few supports), with
+// no workgroup barrier, so that many rows' load chains are in flight at once.
+// Same order of summation, hence the same results, as the workgroup kernels.
+template <class E>
+__global__ __launch_bounds__(256) void sparse_dw_wave_kernel(const int* off, const SpEntry* bucket, const E* h,
+                                                             int64_t H, const GradCounts* cnt, int accumulate,
+                                                             float* dW, int64_t V) {
+  const int lane = threadIdx.x & 63;
+  const bool from_mem = accumulate || cnt->dense > 0;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  for (int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); j < V; j += nw) {
+    const int o0 = off[j], ne = off[j + 1] - o0;
+    if (ne > WAVE_MAX || (ne == 0 && from_mem)) continue;
+    int idx = 0;
+    float v = 0.f;
+    if (lane < ne) {
+      const SpEntry e = bucket[o0 + lane];
+      idx = e.idx;
+      v = e.v;
+    }
+    wave_order(ne, idx, v);
+    float* row = dW + j * H;
+    for (int64_t c0 = lane * 8; c0 < H; c0 += 64 * 8) {
+      float acc[8];
+      if (from_mem) {
+        const f32x4 a = *(const f32x4*)(row + c0), b = *(const f32x4*)(row + c0 + 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[k] = a[k];
+          acc[4 + k] = b[k];
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+      }
+      wave_ordered_sum(ne, idx, v, h, (const float*)nullptr, H, c0, acc);
+      *(f32x4*)(row + c0) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      *(f32x4*)(row + c0 + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    }
+  }
+}
+
+template <class E, class O>
+__global__ __launch_bounds__(256) void sparse_dh_wave_kernel(const int* perm, const GradCounts* cnt, const int* rowcnt,
+                                                             const SpEntry* list, const E* W, const float* w_scale,
+                                                             int64_t H, float div, O* dH, int64_t T) {
+  const int lane = threadIdx.x & 63;
+  const GradCounts c = *cnt;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  for (int64_t n = c.dense + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); n < T; n += nw) {
+    const int ne = n < c.active ? min(rowcnt[n], NSP) : 0;
+    if (ne > WAVE_MAX) continue;
+    int idx = 0;
+    float v = 0.f;
+    if (lane < ne) {
+      const SpEntry e = list[n * NSP + lane];
+      idx = e.idx;
+      v = e.v;
+    }
+    wave_order(ne, idx, v);
+    O* out = dH + (int64_t)perm[n] * H;
+    for (int64_t c0 = lane * 8; c0 < H; c0 += 64 * 8) {
+      float acc[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+      wave_ordered_sum(ne, idx, v, W, w_scale, H, c0, acc);
+      if (div != 1.f)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = acc[k] / div;
+      if constexpr (sizeof(O) == 2) {
+        bf16x8 o;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = (bf16)acc[k];
+        *(bf16x8*)(out + c0) = o;
+      } else {
+        *(f32x4*)(out + c0) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        *(f32x4*)(out + c0 + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+      }
     }
   }
 }
@@ -611,19 +743,36 @@ hipError_t launch_sparse_grads(const SparseGradArgs& a, hipStream_t s) {
       if ((e = launch_exclusive_scan(a.cntj, a.V, a.scan_sums, a.offj, s))) return e;
       hipLaunchKernelGGL(bucket_fill_kernel, dim3((unsigned)ceil_div(a.T, 4)), dim3(256), 0, s, a.cnt, a.T, a.rowcnt,
                          a.list, a.offj, a.cntj, a.bucket);
-      // a few workgroups per compute unit, each looping over vocabulary rows
+      // rows with few entries one wave each, then the rest one workgroup
+      // each; both loop over the vocabulary rows, each taking its own
+      const unsigned gw = (unsigned)(ceil_div(a.V, 4) < 8192 ? ceil_div(a.V, 4) : 8192);
       const unsigned g = (unsigned)(a.V < 4096 ? a.V : 4096);
-      if (a.dtype != DT_F32)  // bf16 rows (the fp8 lane's are the dequantized hidden rows)
+      if (a.dtype != DT_F32) {  // bf16 rows (the fp8 lane's are the dequantized hidden rows)
+        hipLaunchKernelGGL(sparse_dw_wave_kernel<bf16>, dim3(gw), dim3(256), 0, s, a.offj, a.bucket,
+                           (const bf16*)a.h_perm, a.H, a.cnt, a.accumulate_w, a.grad_weight, a.V);
         hipLaunchKernelGGL(sparse_dw_kernel<bf16>, dim3(g), dim3(256), 0, s, a.offj, a.bucket, (const bf16*)a.h_perm,
                            a.H, a.cnt, a.accumulate_w, a.grad_weight, a.T, a.V);
-      else
+      } else {
+        hipLaunchKernelGGL(sparse_dw_wave_kernel<float>, dim3(gw), dim3(256), 0, s, a.offj, a.bucket,
+                           (const float*)a.h_perm, a.H, a.cnt, a.accumulate_w, a.grad_weight, a.V);
         hipLaunchKernelGGL(sparse_dw_kernel<float>, dim3(g), dim3(256), 0, s, a.offj, a.bucket,
                            (const float*)a.h_perm, a.H, a.cnt, a.accumulate_w, a.grad_weight, a.T, a.V);
+      }
     }
     if ((e = hipGetLastError())) return e;
   }
   if (a.grad_hidden) {
     ProfScope ps(KIND_SPARSE_DH, s);
+    const unsigned gw = (unsigned)(ceil_div(a.T, 4) < 8192 ? ceil_div(a.T, 4) : 8192);
+    if (a.dtype == DT_FP8)
+      hipLaunchKernelGGL((sparse_dh_wave_kernel<uint8_t, bf16>), dim3(gw), dim3(256), 0, s, a.perm, a.cnt,
+                         a.rowcnt, a.list, (const uint8_t*)a.W, a.w_scale, a.H, a.dh_div, (bf16*)a.grad_hidden, a.T);
+    else if (a.dtype == DT_BF16)
+      hipLaunchKernelGGL((sparse_dh_wave_kernel<bf16, bf16>), dim3(gw), dim3(256), 0, s, a.perm, a.cnt,
+                         a.rowcnt, a.list, (const bf16*)a.W, nullptr, a.H, a.dh_div, (bf16*)a.grad_hidden, a.T);
+    else
+      hipLaunchKernelGGL((sparse_dh_wave_kernel<float, float>), dim3(gw), dim3(256), 0, s, a.perm, a.cnt,
+                         a.rowcnt, a.list, (const float*)a.W, nullptr, a.H, a.dh_div, (float*)a.grad_hidden, a.T);
     if (a.dtype == DT_FP8)
       hipLaunchKernelGGL((sparse_dh_kernel<uint8_t, bf16>), dim3((unsigned)a.T), dim3(256), 0, s, a.perm, a.cnt,
                          a.rowcnt, a.list, (const uint8_t*)a.W, a.w_scale, a.H, a.dh_div, (bf16*)a.grad_hidden, a.T);
