@@ -410,7 +410,7 @@ typedef struct stce_pg_params {
   float scale;              /* multiplies losses and gradients, e.g. 1 / a constant denominator */
   const float *advantages;  /* [T] */
   const float *old_logprob; /* [T] logprob of the target under the behaviour policy */
-  const void *state;        /* [T * 32] from the forward, or NULL: rows it marks inactive
+  const void *state;        /* [T * STCE_STATE_BYTES_PER_ROW] from the forward, or NULL: rows it marks inactive
                                (ignore_index) get loss 0, gradient 0 and ratio 0 */
 } stce_pg_params;
 stce_status stce_policy_loss(const stce_pg_params *pg, int64_t T, const float *logprob, float *loss,

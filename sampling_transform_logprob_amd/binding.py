@@ -249,7 +249,7 @@ def forward(hidden, weight, target, temperature=None, top_k=None, top_p=None, mi
             chunk_rows: int = 0, check: bool = True, workspace: Optional[torch.Tensor] = None,
             side: bool = False, ignore_index: Optional[int] = None, pre_gemm_temperature: Optional[float] = None,
             lane: str = "fp32", weight_scale: Optional[torch.Tensor] = None):
-    """Selected logprob per row and the 32-byte-per-row state for backward.
+    """Selected logprob per row and the per-row state for backward.
 
     With ``side=True`` also returns a dict of the sweep's side outputs
     (``lse_full``, ``entropy_full``, ``entropy_support``, fp32 [T]).

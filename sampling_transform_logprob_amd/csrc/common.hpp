@@ -34,7 +34,8 @@ enum : uint32_t {
 // not a candidate, instead of the row's fp32 keys.
 constexpr int KCAND = 256;
 
-// Per-row state written by the forward, read by the backward (32 bytes).
+// Per-row record of the state written by the forward, read by the backward
+// (32 bytes; the tile lists follow the T records).
 // Field order is the one of stce_row_info in stce.h.
 struct RowState {
   uint32_t key_thr;  // key of the last support token (0 on unfiltered rows)
