@@ -297,14 +297,17 @@ stce_status stce_backward(const stce_problem *prob, const float *grad_logprob, c
 stce_status stce_scaled_logits(const stce_problem *prob, int64_t row0, int64_t nrows, float *s_out,
                                void *ws, size_t ws_bytes, void *stream);
 
-/* Parity entry: the recompute product of stce_backward, launched as
- * stce_backward launches it (same kernel, same vocabulary slices and
- * arguments), which in this call also writes the fp32 keys it recomputes,
- * keys_out [T, V] row-major; no gradient product runs.  The keys must equal
- * the forward's bit for bit (the recompute closed-form VJP of xorl pull
+/* Parity entry: the recompute products of stce_backward, launched as
+ * stce_backward launches them (same kernels, same vocabulary slices and
+ * arguments), which in this call also write the fp32 keys they recompute
+ * into keys_out [T, V] row-major; no gradient product runs.  The keys must
+ * equal the forward's bit for bit (the recompute closed-form VJP of xorl pull
  * request 74, "What this PR does" item 2, takes its support from the state
- * and re-derives membership from these keys).  Arguments and workspace as
- * stce_backward; keys_out is required. */
+ * and re-derives membership from these keys).  A row the backward recomputes
+ * on its listed tiles only (a sparse row with a tile list, see
+ * STCE_STATE_BYTES_PER_ROW) gets the keys of those tiles; its other entries
+ * are not written.  Every other row gets all V keys.  Arguments and
+ * workspace as stce_backward; keys_out is required. */
 stce_status stce_recompute_keys(const stce_problem *prob, const float *grad_logprob, const void *state,
                                 float *keys_out, void *ws, size_t ws_bytes, void *stream);
 
