@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import GRAD_RTOL, dev, meta_of, rel_fro, say, targets, tiled_rows, to_gpu
+from gpu_helpers import GRAD_RTOL, check_tile_lists, dev, meta_of, rel_fro, say, targets, tiled_rows, to_gpu
 from sampling_transform_logprob_amd import binding, workloads
 from sampling_transform_logprob_amd.workloads import round_bf16
 
@@ -169,3 +169,48 @@ def test_tile_recompute_equals_the_whole_vocabulary_recompute(name, T, V):
         say(f"  dW: placement differs ({int((sparse & ~tiled).sum())} sparse rows without a list); "
             f"max difference {err:.1e} of the largest entry")
         assert err < 1e-5
+
+
+def test_tile_lists_at_the_31_tile_bound():
+    """Rows whose support spans 30, 31 and 32 vocabulary tiles: one peak
+    token per tile (distinct heights, far above the rest), top-k equal to
+    the number of peaks.  The lists hold 30 and 31 tiles; a 32-tile support
+    keeps no list and its row takes the whole-vocabulary recompute.  Both
+    kinds agree with the oracle and with the lists cleared."""
+    rng = np.random.Generator(np.random.PCG64(31))
+    ntv, H = 40, 64
+    V = ntv * 256
+    T = H                                                  # one hidden coordinate per row
+    m_of = np.array([30, 31, 32])[np.arange(T) % 3]
+    # row r's hidden state is the unit vector e_r, so its keys are column r
+    # of W: small noise, and one peak per chosen tile, of distinct heights
+    h = np.eye(T, H, dtype=np.float32)
+    W = (rng.standard_normal((V, H)) * 0.01).astype(np.float32)
+    for r in range(T):
+        tiles = rng.choice(ntv, m_of[r], replace=False)
+        toks = tiles * 256 + rng.integers(0, 256, m_of[r])
+        W[toks, r] = 5.0 + 0.25 * np.arange(m_of[r], dtype=np.float32)   # bf16-exact heights
+    h, W = round_bf16(h), round_bf16(W)
+    w = dict(h=h, W=W, temperature=np.ones(T, np.float32), top_k=m_of.astype(np.int32),
+             top_p=np.ones(T, np.float32), min_p=np.zeros(T, np.float32), dtype="bf16",
+             u=rng.random(T), filtered=True, V=V)
+    y = targets(w)
+    G = to_gpu(w, y)
+    lp, st = binding.forward(G["h"], G["W"], G["target"], **meta_of(G))
+    g = torch.from_numpy(rng.standard_normal(T).astype(np.float32)).to(dev())
+    gh, gw = binding.backward(G["h"], G["W"], G["target"], st, g, **meta_of(G))
+    st_full = st.clone()
+    st_full[T * binding.RECORD_BYTES:] = 0
+    gh0, gw0 = binding.backward(G["h"], G["W"], G["target"], st_full, g, **meta_of(G))
+    keys = binding.scaled_logits(G["h"], G["W"], G["temperature"]).cpu().numpy()
+    torch.cuda.synchronize()
+    info = binding.decode_state(st)
+    check_tile_lists(info, keys, V)
+    assert np.array_equal(info["n"], m_of)
+    assert np.array_equal(info["ntile"], np.where(m_of <= 31, m_of, 0))
+    ref, (dH, dW) = _oracle_grads(w, y, g.cpu().numpy(), keys)
+    rh, rw = rel_fro(gh.float().cpu().numpy(), dH), rel_fro(gw.cpu().numpy(), dW)
+    say(f"31-tile bound: lists {sorted(set(info['ntile'].tolist()))}; dH rel {rh:.2e} dW rel {rw:.2e}")
+    assert rh < GRAD_RTOL and rw < GRAD_RTOL
+    assert torch.equal(gh, gh0)
+    assert (gw - gw0).abs().max().item() <= 1e-5 * gw0.abs().max().item()
