@@ -459,7 +459,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="headline")
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=None,
+                    help="rows of the CPU oracle's sample (default 512; 256 in the fp8 lane, whose oracle also "
+                         "decodes the whole e4m3 weight in fp64): about 10-30 s of CPU work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=3,
                     help="steps of the separate pass that records HIP events around each launch")
@@ -747,9 +749,10 @@ def main():
         "binding_filter_rows": binds,
     }
     if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline: oracle on {args.cpu_rows} rows")
+        rows = args.cpu_rows or (256 if fp8 else 512)
+        log(f"[bench] cpu baseline: oracle on {rows} rows")
         w_np = dict(w)
-        out["cpu_baseline"] = cpu_baseline(w_np, target.cpu().numpy(), args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(w_np, target.cpu().numpy(), rows)
     print(json.dumps(out), flush=True)
 
 
