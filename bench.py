@@ -93,11 +93,21 @@ class HipEvents:
 def cpu_baseline(w, y, rows):
     """fp64 oracle (as it stands) on a bounded sample of the same rows."""
     import oracle
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
+        info = threadpool_info()
+        cores = max([p.get("num_threads", 1) for p in info] or [os.cpu_count()])
+        blas = ", ".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in info
+                                 if p.get("user_api") == "blas"})) or blas
     except Exception:  # noqa: BLE001
         cores = os.cpu_count()
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu_model)
+    except OSError:
+        pass
     sel = np.arange(rows)
     g = np.full(w["T"], -1.0 / w["T"])
     kw = dict(lane="fp8", w_scale=w["w_scale"]) if w["dtype"] == "fp8" else {}
@@ -107,7 +117,8 @@ def cpu_baseline(w, y, rows):
     dt = time.perf_counter() - t0
     return dict(value=rows / dt, unit="scored tokens/s", cores=int(cores), kind="oracle",
                 sample=f"first {rows} rows of the same workload, forward + backward (their grad_hidden rows "
-                       f"and their whole grad_weight contribution), fp64 numpy, {dt:.1f} s")
+                       f"and their whole grad_weight contribution), fp64 numpy, {dt:.1f} s",
+                cpu_model=cpu_model, blas=blas)
 
 
 def filter_binding(info, w):
@@ -456,8 +467,8 @@ def library_reference(reps=5):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="headline")
     ap.add_argument("--cpu-rows", type=int, default=None,
                     help="rows of the CPU oracle's sample (default 512; 256 in the fp8 lane, whose oracle also "
