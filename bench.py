@@ -170,6 +170,8 @@ TRACE_LABELS = [
     ("tile_count", "tile recompute work lists (count, work items, fill)"),
     ("tile_work", "tile recompute work lists (count, work items, fill)"),
     ("tile_fill", "tile recompute work lists (count, work items, fill)"),
+    ("keys_entries", "fused step: tiled rows' dz entries from the chunk keys"),
+    ("place_entries", "fused step: tiled rows' dz entries placed by position"),
     ("EpiStore", "gemm: grad_weight of the dense rows (EpiStore)"),
     ("EpiAccumT", "gemm: grad_hidden of the dense rows as dH^T (EpiAccumT)"),
     ("EpiDlogits", "gemm: backward recompute + dz^T, fp32 operands (EpiDlogits)"),
@@ -672,22 +674,28 @@ def main():
     # 2 T H V per step (the fused step has no dlogits product), spread over
     # the launches observed
     C, Vs = binding.schedule(prob)
+    # the fused step's path: with row classes for bf16 operands with a filter
+    # and for the fp8 lane, dense otherwise
+    any_filter = any(meta[k] is not None for k in ("top_k", "top_p", "min_p"))
+    fused_classed = args.fused and dt == torch.bfloat16 and (fp8 or any_filter)
     if args.fused:
         C = min(-(-(args.chunk_rows or 4096) // 64) * 64, -(-T // 64) * 64)
-        Vs = None
-    # the backward's row classes (bf16 unfused step): the recompute product
-    # runs over the rows with a gradient, the two gradient products over the
-    # dense rows; sparse rows' gradients are sums over their dz entries
-    classed = dt == torch.bfloat16 and not args.fused    # bf16 and the fp8 lane
+        Vs = Vs if fused_classed else None
+    # the backward's row classes (bf16 and the fp8 lane): the recompute
+    # product runs over the rows with a gradient, the two gradient products
+    # over the dense rows; sparse rows' gradients are sums over their dz
+    # entries, the tiled rows' formed from their listed tiles (recomputed, or
+    # in the fused step read from the chunk's keys)
+    classed = dt == torch.bfloat16 and (not args.fused or fused_classed)
     tiled_on = classed and -(-V // 256) <= 65535 and T * H * (1 if fp8 else 2) < 2 ** 31 - 1 - 2 ** 22
     classes = row_classes(binding.decode_state(state), g.cpu().numpy(), tiled_on)
     t_full = classes["dense"] + classes["sparse"] if classed else T
     t_dense = classes["dense"] if classed else T
     # the tile recompute forms 256 keys of H-long products per (row, tile) pair
     per_step_flop = {"projection": 2.0 * T * H * V, "dlogits": 2.0 * t_full * H * V,
-                     "tile_recompute": 2.0 * classes["tile_pairs"] * 256 * H if classed else 0.0,
+                     "tile_recompute": 2.0 * classes["tile_pairs"] * 256 * H if classed and not args.fused else 0.0,
                      "grad_weight": 2.0 * t_dense * H * V, "grad_hidden": 2.0 * t_dense * H * V}
-    if args.fused:
+    if args.fused and not fused_classed:
         per_step_flop = {k: 2.0 * T * H * V for k in ("projection", "grad_weight", "grad_hidden")}
     stats = {}
     per_launch = {}
@@ -736,7 +744,9 @@ def main():
                                f"{float(w['min_p'].max())}; forward + backward (grad_hidden, grad_weight)"
                                + ("" if args.policy_loss == "none" else
                                   f" of the {args.policy_loss} policy-gradient token loss")
-                               + ("; fused step: dlogits formed in the forward's sweep, no recompute product"
+                               + ("; fused step: the tiled rows' dz entries from the chunks' keys, no tile "
+                                  "recompute" if fused_classed else
+                                  "; fused step: dlogits formed in the forward's sweep, no recompute product"
                                   if args.fused else "")
                                + ("; forward side outputs (full LSE, entropies)" if args.side_outputs else "")
                                + ("; bf16 value lane" if args.lane == "bf16" else "")

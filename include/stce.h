@@ -372,6 +372,7 @@ stce_status stce_decode_state(const void *host_state, int64_t nrows, stce_row_in
 #define STCE_KERNEL_QUANTIZE 17    /* fp8 lane: per-row e4m3 quantization of hidden rows */
 #define STCE_KERNEL_TILE_LISTS 18  /* backward: per-tile lists of the rows whose keys are recomputed there */
 #define STCE_KERNEL_TILE_RECOMPUTE 19 /* backward: recompute of those rows' keys on their listed tiles */
+#define STCE_KERNEL_KEYS_ENTRIES 20 /* fused step: those rows' dz entries from the stored keys, and their placement */
 typedef struct stce_profile {
   int32_t capacity;
   int32_t count;
@@ -422,44 +423,63 @@ stce_status stce_policy_loss(const stce_pg_params *pg, int64_t T, const float *l
 /* Fused head + policy-gradient step (align "architecture v2: proposal",
  * section 5.4 A: the "Fused" row of its GEMM-count table and "Why the
  * in-chunk form works for this loss").  The token coefficient needs only the
- * new logprob, which a chunk has just computed, so dlogits is formed inside
- * the forward's sweep and no product is recomputed: 2 products for a frozen
- * head (logits, dH), 3 for a trainable one (plus dW), against 3 and 4 for
- * stce_forward + stce_policy_loss + stce_backward.  Per chunk of rows, on
- * `stream`:
- *   1. the projection keeps the fp32 keys of every row of the chunk;
+ * new logprob, which a chunk has just computed, so dlogits can be formed
+ * inside the forward's sweep from the chunk's keys instead of a recompute.
+ * Per chunk of rows, on `stream`:
+ *   1. the projection keeps the fp32 keys of every row of the chunk (fp8
+ *      lane: the chunk's hidden rows quantized first, as in stce_forward);
  *   2. the support program and selected logprob as in stce_forward (side
  *      outputs as in stce_forward_with_side, `side` may be NULL);
- *   3. the token loss, its gradient and the ratio as in stce_policy_loss;
- *   4. dz = g (1[j == y] - q) / T from the stored keys, with the arithmetic
- *      of stce_backward's recompute, so dz equals that path's bit for bit;
- *   5. grad_hidden rows of the chunk = dz . W (split over the vocabulary,
- *      fp32 partials summed in split order); the vocab-major dz of a group of
- *      consecutive chunks is kept (as many as 8 GB hold: all of them at the
- *      sizes below), and at a group's end grad_weight (+)= dz^T . h with the
- *      group's rows as the reduction.
+ *   3. the token loss, its gradient g and the ratio as in stce_policy_loss;
+ *   4. dlogits from the stored keys, with the arithmetic of stce_backward's
+ *      recompute (so equal to it bit for bit), on one of two paths:
+ *   - with row classes, when the operands are bf16 and a filter is given
+ *     (top_k, top_p or min_p not NULL), or on the fp8 lane: the rows
+ *     stce_backward would recompute on their listed tiles only (support of
+ *     at most 128 tokens, a tile list in the state) take their dz entries
+ *     from the chunk's keys; after the sweep the backward of stce_backward
+ *     runs with g, without that tile recompute (its other rows: dense ones
+ *     through the recompute product and the two gradient products over
+ *     those rows only, sparse ones through their support).  The gradients
+ *     are then bitwise stce_backward's on the same inputs.  A batch whose
+ *     rows are all top-k rows (as at T = 16384, V = 151936, top_k 20) makes
+ *     the matrix products one: the projection;
+ *   - dense, for fp32 operands or bf16 with no filter (every row's support
+ *     is the whole vocabulary, so every row's dz is dense): dz of every row
+ *     from the keys; the chunk's grad_hidden rows = dz . W (split over the
+ *     vocabulary, fp32 partials summed in split order); the vocab-major dz of
+ *     a group of consecutive chunks is kept (as many as 8 GB hold: all of
+ *     them at the sizes below), and at a group's end grad_weight (+)= dz^T . h
+ *     with the group's rows as the reduction: 2 products for a frozen head
+ *     (logits, dH), 3 for a trainable one (plus dW), against 3 and 4 for
+ *     stce_forward + stce_policy_loss + stce_backward.  The gradients differ
+ *     from the unfused sequence's only by fp32 summation order.
  * Outputs: logprob, state (as stce_forward), loss and ratio (as
  * stce_policy_loss; ratio may be NULL), and the gradients of sum_t loss[t]:
- * grad_hidden [T][H] in the operand dtype and grad_weight [V][H] fp32
- * (overwritten, or added to when accumulate_grad_weight is nonzero); either
- * may be NULL, both NULL = forward and loss only.  logprob, state and loss are
- * bitwise those of the unfused sequence on the same inputs; the gradients
- * differ from its only by fp32 summation order.  pg->state is not read (the
- * step's own state marks inactive rows).  The chunk size is
- * prob->chunk_rows rounded up to a multiple of 64 (default 4096); the
- * workspace (256-byte aligned device memory, stce_fused_workspace_bytes;
- * 11.9 GB at T = 16384, H = 5120, V = 151936, 8.2 GB at its minimum) holds
- * the fp32 keys of two chunks (a chunk's selection runs on a side stream of
- * the library's while the next chunk is projected, joined by event waits as
- * in stce_forward), the group's vocab-major dz (with bf16 operands the only
- * copy: the hidden gradient is formed transposed and reads it as it is; fp32
- * also keeps a chunk's token-major copy), the transposed weight (and for
- * fp32 the transposed hidden), the split partials, and with the scalar
- * pre-GEMM temperature h / Ts.  A workspace between *min_bytes (one
- * chunk per group) and *bytes keeps as many chunks per group as it holds;
- * the grouping changes only the order of dW's fp32 sums.  Host errors as stce_forward, stce_backward and
- * stce_policy_loss, and V must be below 2^29 (the chunk's key rows are read
- * through 32-bit buffer offsets). */
+ * grad_hidden [T][H] in the hidden dtype (bf16 on the fp8 lane) and
+ * grad_weight [V][H] fp32 (overwritten, or added to when
+ * accumulate_grad_weight is nonzero); either may be NULL, both NULL =
+ * forward and loss only.  logprob, state and loss are bitwise those of the
+ * unfused sequence on the same inputs.  pg->state is not read (the step's own
+ * state marks inactive rows).  The chunk size is prob->chunk_rows rounded up
+ * to a multiple of 64 (default 4096).  Workspace: 256-byte aligned device
+ * memory of stce_fused_workspace_bytes (which of the paths a problem takes
+ * depends only on its dtype and which filter pointers are set).  Both paths
+ * hold the fp32 keys of two chunks (a chunk's selection runs on a side stream
+ * of the library's while the next chunk is projected, joined by event waits
+ * as in stce_forward), and with the scalar pre-GEMM temperature h / Ts.  With
+ * row classes, then, the rows' g and dz entry lists, and stce_backward's
+ * workspace in the space the keys leave (bytes == min_bytes; 7.1 GB at
+ * T = 16384, H = 5120, V = 151936, bf16 or fp8).  Dense: the group's vocab-major dz (with
+ * bf16 operands the only copy: the hidden gradient is formed transposed and
+ * reads it as it is; fp32 also keeps a chunk's token-major copy), the
+ * transposed weight (and for fp32 the transposed hidden) and the split
+ * partials (11.9 GB at those sizes, 8.2 GB at its minimum); a workspace
+ * between *min_bytes (one chunk per group) and *bytes keeps as many chunks
+ * per group as it holds, which changes only the order of dW's fp32 sums.
+ * Host errors as stce_forward, stce_backward and stce_policy_loss, and V must
+ * be below 2^29 (the chunk's key rows are read through 32-bit buffer
+ * offsets). */
 stce_status stce_fused_workspace_bytes(const stce_problem *prob, size_t *bytes, size_t *min_bytes);
 stce_status stce_fused_policy_step(const stce_problem *prob, const stce_pg_params *pg, float *logprob,
                                    void *state, float *loss, float *ratio, const stce_side_outputs *side,

@@ -40,7 +40,7 @@ KERNEL_KINDS = {1: "validate", 2: "projection", 3: "select", 4: "dlogits", 5: "g
                 6: "grad_hidden", 7: "transpose", 8: "partials", 9: "policy_loss", 10: "dz_keys",
                 11: "split_sum", 12: "prescale", 13: "classify", 14: "sparse_grad_weight",
                 15: "sparse_grad_hidden", 16: "reproject", 17: "quantize", 18: "tile_lists",
-                19: "tile_recompute"}
+                19: "tile_recompute", 20: "keys_entries"}
 PG_OBJECTIVES = {"cispo": 1, "clip": 2}
 
 
@@ -470,16 +470,19 @@ def fused_policy_step(hidden, weight, target, advantages, old_logprob, temperatu
                       grad_weight: Optional[torch.Tensor] = None, accumulate_grad_weight: bool = False,
                       side: bool = False, chunk_rows: int = 0, ignore_index: Optional[int] = None,
                       check: bool = True, workspace: Optional[torch.Tensor] = None,
-                      pre_gemm_temperature: Optional[float] = None, lane: str = "fp32"):
+                      pre_gemm_temperature: Optional[float] = None, lane: str = "fp32",
+                      weight_scale: Optional[torch.Tensor] = None):
     """The fused head + policy-gradient step (dlogits formed in the forward's
-    sweep, no recompute).  Returns a dict with ``loss``, ``logprob``,
+    sweep from the chunk's keys).  Returns a dict with ``loss``, ``logprob``,
     ``ratio`` (fp32 [T]), ``state``, ``grad_hidden`` ([T, H], hidden's dtype,
     or None), ``grad_weight`` (fp32 [V, H] or None) and, with ``side=True``,
-    ``lse_full``, ``entropy_full``, ``entropy_support``."""
+    ``lse_full``, ``entropy_full``, ``entropy_support``.  An e4m3 ``weight``
+    (uint8 codes) with ``weight_scale`` takes the fp8 lane."""
     if objective not in PG_OBJECTIVES:
         raise ValueError(f"objective must be one of {tuple(PG_OBJECTIVES)}")
     prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, chunk_rows,
-                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane)
+                              ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane,
+                              weight_scale=weight_scale)
     T, H, V = prob.T, prob.H, prob.V
     dev = hidden.device
     adv = _meta("advantages", advantages, T, torch.float32, dev)

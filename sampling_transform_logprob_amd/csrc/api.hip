@@ -313,6 +313,66 @@ FusedLayout plan_fused(const stce_problem* p, int64_t gmax = INT64_MAX) {
   return L;
 }
 
+// The fused step's paths.  With row classes (bf16 operands with a filter
+// given, or the fp8 lane) the sweep keeps of each chunk what the classed
+// backward needs: its rows' upstream gradients, and the tiled rows' dz
+// entries formed from the chunk's keys; the classed backward then runs as in
+// stce_backward, without the tile recompute.  Dense (fp32 operands, or bf16
+// with no filter: every row's support is the whole vocabulary): dz of every
+// row from the chunk's keys, and the two gradient products over all rows.
+bool fused_classed(const stce_problem* p) {
+  return p->dtype != STCE_DT_F32 && (fp8(p) || p->top_k || p->top_p || p->min_p);
+}
+
+// Workspace of the classed fused step: the rows' upstream gradients, the
+// per-row dz entry lists and counts and the per-vocabulary-row entry counts
+// (kept from the sweep to the backward), the pre-GEMM hidden, then one
+// region that holds the sweep's buffers (row flags; one or two chunks' keys,
+// tile partials and target keys; fp8: their quantized hidden rows) and,
+// once the sweep is done, the backward's (offsets from `uni`).
+struct FusedClassLayout {
+  int64_t C, ldt, ntv, nbuf;
+  size_t g, list_row, rowcnt_row, cntj, hs, uni;
+  size_t flags, tile, part, sy, h8, ha;
+  size_t buf_tile, buf_part, buf_sy, buf_h8, buf_ha;
+  Layout B;
+  size_t total;
+};
+
+FusedClassLayout plan_fused_classed(const stce_problem* p) {
+  FusedClassLayout L{};
+  const int64_t T = p->T, V = p->V, H = p->H;
+  L.C = round_up(p->chunk_rows > 0 ? p->chunk_rows : kDefaultChunk, 64);
+  if (L.C > round_up(T, 64)) L.C = round_up(T, 64);
+  L.ldt = round_up(V, 4);
+  L.ntv = ceil_div(V, VTILE);
+  L.nbuf = ceil_div(T, L.C) > 1 ? 2 : 1;
+  size_t o = 0;
+  L.g = o;          o = align_up(o + 4 * (size_t)T);
+  L.list_row = o;   o = align_up(o + sizeof(SpEntry) * (size_t)T * NSP);
+  L.rowcnt_row = o; o = align_up(o + 4 * (size_t)T);
+  L.cntj = o;       o = align_up(o + 4 * (size_t)V);
+  L.hs = o;         o = align_up(o + hs_bytes(p));
+  L.uni = o;
+  size_t u = 0;
+  L.buf_tile = align_up(4 * (size_t)L.C * L.ldt);
+  L.buf_part = align_up(sizeof(TilePart) * (size_t)L.C * L.ntv);
+  L.buf_sy = align_up(4 * (size_t)L.C);
+  L.flags = u;  u = align_up(u + 4 * (size_t)T);
+  L.tile = u;   u += L.nbuf * L.buf_tile;
+  L.part = u;   u += L.nbuf * L.buf_part;
+  L.sy = u;     u += L.nbuf * L.buf_sy;
+  if (fp8(p)) {
+    L.buf_h8 = align_up((size_t)L.C * H);
+    L.buf_ha = align_up(4 * (size_t)L.C);
+    L.h8 = u;   u += L.nbuf * L.buf_h8;
+    L.ha = u;   u += L.nbuf * L.buf_ha;
+  }
+  L.B = plan(p);
+  L.total = L.uni + (u > L.B.bwd ? u : L.B.bwd);
+  return L;
+}
+
 stce_status check_inputs(const stce_problem* p) {
   if (!p->hidden || !p->weight || !p->target) return fail(STCE_E_ARG, "hidden, weight and target are required");
   if (!aligned(p->hidden, 16) || !aligned(p->weight, 16))
@@ -670,14 +730,24 @@ namespace {
 // into that order (fp8: quantized into it, and dequantized for the weight
 // gradient), per vocabulary slice the recompute product and the dense rows'
 // two products, then the sparse rows' products over their dz entries.
+// The tiled rows' dz entries formed before the backward (the fused step,
+// from its chunks' keys): per-row lists and counts, and the per-vocabulary-
+// row counts that already include them.
+struct PreEntries {
+  const SpEntry* list_row;
+  const int* rowcnt_row;
+  int* cntj;
+};
+
 stce_status backward_classed(const stce_problem* p, const Layout& L, const float* grad_logprob, const void* state,
                              const void* hid, float dh_div, void* grad_hidden, float* grad_weight,
-                             int32_t accumulate_grad_weight, void* ws, hipStream_t st, float* keys_out) {
+                             int32_t accumulate_grad_weight, void* ws, hipStream_t st, float* keys_out,
+                             const PreEntries* pre = nullptr) {
   hipError_t e;
   GradCounts* cnt = at<GradCounts>(ws, L.b_cnt);
   int* perm = at<int>(ws, L.b_perm);
   int* rowcnt = at<int>(ws, L.b_rowcnt);
-  int* cntj = at<int>(ws, L.b_cntj);
+  int* cntj = pre ? pre->cntj : at<int>(ws, L.b_cntj);
   bf16* h_perm = at<bf16>(ws, L.b_hperm);
   SpEntry* list = at<SpEntry>(ws, L.b_list);
   const bool want_w = grad_weight && !keys_out;
@@ -685,6 +755,8 @@ stce_status backward_classed(const stce_problem* p, const Layout& L, const float
   if ((e = launch_grad_classes((const RowState*)state, tl, grad_logprob, p->T, at<int>(ws, L.b_blk), cnt, perm,
                                rowcnt, st)))
     return hip_fail(e, "row classes");
+  if (pre && tl && (e = launch_place_entries(perm, cnt, pre->rowcnt_row, pre->list_row, rowcnt, list, p->T, st)))
+    return hip_fail(e, "place the tiled rows' entries");
   uint8_t* h8_perm = fp8(p) ? at<uint8_t>(ws, L.b_h8) : nullptr;
   float* ha = fp8(p) ? at<float>(ws, L.b_ha) : nullptr;
   if (fp8(p))  // the hidden rows quantized in permuted order, and dequantized
@@ -692,7 +764,7 @@ stce_status backward_classed(const stce_problem* p, const Layout& L, const float
   else
     e = launch_gather_rows(1, hid, perm, p->T, p->H, h_perm, st);
   if (e) return hip_fail(e, "gather hidden rows");
-  if (want_w && (e = launch_fill_i32(cntj, p->V, 0, st))) return hip_fail(e, "clear counts");
+  if (want_w && !pre && (e = launch_fill_i32(cntj, p->V, 0, st))) return hip_fail(e, "clear counts");
   const int64_t nsl = ceil_div(p->V, L.Vs);
   for (int64_t si = 0; si < nsl; ++si) {
     ClassSliceArgs a{};
@@ -736,7 +808,7 @@ stce_status backward_classed(const stce_problem* p, const Layout& L, const float
     a.ld_keys = p->V;
     if ((e = launch_class_slice(a, st))) return hip_fail(e, "backward slice");
   }
-  if (tl) {  // the tiled rows' keys on their tiles
+  if (tl && !pre) {  // the tiled rows' keys on their tiles
     TiledArgs ta{};
     if (fp8(p)) {
       ta.W8 = (const uint8_t*)p->weight;
@@ -874,6 +946,106 @@ stce_status backward_impl(const stce_problem* p, const float* grad_logprob, cons
   return STCE_OK;
 }
 
+// Buffers of the fused step's sweep: the row flags, and per chunk buffer
+// the chunk's keys, tile partials and target keys (fp8 lane: its quantized
+// hidden rows and their scales).
+struct SweepBufs {
+  int64_t C, ldt, ntv, nbuf;
+  uint32_t* flags;
+  char *tile, *part, *sy, *h8, *ha;
+  size_t buf_tile, buf_part, buf_sy, buf_h8, buf_ha;
+};
+
+// The fused step's sweep over chunks of C rows.  Chunk c: (fp8: its hidden
+// rows quantized) the projection keeping every key into buffer c % nbuf,
+// then the selection and selected logprob on the side stream when there are
+// two buffers, overlapping chunk c + 1's projection; once the caller's
+// stream has waited for it, after(c, c0, nc, keys) enqueues the chunk's own
+// work there.  Buffer reuse: chunk c + 1's projection is enqueued after
+// chunk c - 1's wait and after(), so it overwrites nothing still read.
+template <class After>
+stce_status fused_sweep(const stce_problem* p, const SweepBufs& B, const void* hid, float* logprob, void* state,
+                        const stce_side_outputs* side_out, hipStream_t st, After after) {
+  hipError_t e;
+  float* so_lse = side_out ? side_out->lse_full : nullptr;
+  float* so_hf = side_out ? side_out->entropy_full : nullptr;
+  float* so_hs = side_out ? side_out->entropy_support : nullptr;
+  const size_t es = elt_size(p->dtype);
+  const int64_t nch = ceil_div(p->T, B.C);
+  SideCtx* side = nullptr;
+  if (B.nbuf == 2 && (e = side_ctx(&side))) return hip_fail(e, "side stream");
+  auto rows_of = [&](int64_t c) { return p->T - c * B.C < B.C ? p->T - c * B.C : B.C; };
+  auto project_select = [&](int64_t c) -> stce_status {
+    const int64_t c0 = c * B.C, nc = rows_of(c), b = c % B.nbuf;
+    FwdArgs a{};
+    a.dtype = p->dtype;
+    a.W = p->weight;
+    a.h = (const char*)hid + es * (size_t)c0 * p->H;
+    hipError_t e2;
+    if (fp8(p)) {
+      uint8_t* h8 = (uint8_t*)B.h8 + b * B.buf_h8;
+      float* ha = (float*)(B.ha + b * B.buf_ha);
+      if ((e2 = launch_fp8_quantize_rows((const bf16*)a.h, nullptr, nc, p->H, h8, ha, nullptr, st)))
+        return hip_fail(e2, "quantize hidden rows");
+      a.h = h8;
+      a.row_scale = p->weight_scale;
+      a.col_scale = ha;
+    }
+    a.H = p->H;
+    a.V = p->V;
+    a.rows = nc;
+    a.tile = (float*)(B.tile + b * B.buf_tile);
+    a.ld = B.ldt;
+    a.temp = p->temperature ? p->temperature + c0 : nullptr;
+    a.target = p->target + c0;
+    a.flags = B.flags + c0;
+    a.store_all = 1;
+    a.part = (TilePart*)(B.part + b * B.buf_part);
+    a.ntv = (int)B.ntv;
+    a.s_y = (float*)(B.sy + b * B.buf_sy);
+    a.want_ent = (so_hf || so_hs) ? 1 : 0;
+    a.bf16_lane = bf16_lane(p);
+    if ((e2 = launch_fwd_projection(a, st))) return hip_fail(e2, "projection");
+    hipStream_t ss = st;
+    if (side) {
+      ss = side->stream;
+      if ((e2 = hipEventRecord(side->fork(c), st)) || (e2 = hipStreamWaitEvent(ss, side->fork(c), 0)))
+        return hip_fail(e2, "fork to the side stream");
+    }
+    SelParams sp{};
+    sp.tile = a.tile;
+    sp.ld = B.ldt;
+    sp.part = a.part;
+    sp.ntv = (int)B.ntv;
+    sp.s_y = a.s_y;
+    sp.flags = B.flags + c0;
+    sp.target = p->target + c0;
+    sp.top_k = p->top_k ? p->top_k + c0 : nullptr;
+    sp.top_p = p->top_p ? p->top_p + c0 : nullptr;
+    sp.min_p = p->min_p ? p->min_p + c0 : nullptr;
+    sp.logprob = logprob + c0;
+    sp.state = (RowState*)state + c0;
+    sp.tiles = tiles_ok(p->V) ? state_tiles(state, p->T, p->V) + c0 : nullptr;
+    sp.V = (int)p->V;
+    sp.lse_full = so_lse ? so_lse + c0 : nullptr;
+    sp.ent_full = so_hf ? so_hf + c0 : nullptr;
+    sp.ent_supp = so_hs ? so_hs + c0 : nullptr;
+    sp.round_lp_bf16 = bf16_lane(p);
+    launch_select(sp, (int)nc, ss);
+    if ((e2 = hipGetLastError())) return hip_fail(e2, "select");
+    if (side && (e2 = hipEventRecord(side->done(c), ss))) return hip_fail(e2, "selection event");
+    return STCE_OK;
+  };
+  stce_status s;
+  if ((s = project_select(0))) return s;
+  for (int64_t c = 0; c < nch; ++c) {
+    if (c + 1 < nch && (s = project_select(c + 1))) return s;
+    if (side && (e = hipStreamWaitEvent(st, side->done(c), 0))) return hip_fail(e, "join");
+    if ((s = after(c, c * B.C, rows_of(c), (const float*)(B.tile + (c % B.nbuf) * B.buf_tile)))) return s;
+  }
+  return STCE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -999,7 +1171,11 @@ stce_status stce_fused_workspace_bytes(const stce_problem* p, size_t* bytes, siz
   stce_status s = check_shapes(p);
   if (s) return s;
   if (!bytes) return fail(STCE_E_ARG, "bytes is NULL");
-  if (fp8(p)) return fail(STCE_E_UNSUPPORTED, "the fused policy step takes bf16 or fp32 operands (not the fp8 lane)");
+  if (fused_classed(p)) {
+    *bytes = plan_fused_classed(p).total;
+    if (min_bytes) *min_bytes = *bytes;
+    return STCE_OK;
+  }
   *bytes = plan_fused(p).total;
   if (min_bytes) *min_bytes = plan_fused(p, 1).total;
   return STCE_OK;
@@ -1013,7 +1189,6 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
   if (s) return s;
   if ((s = check_inputs(p))) return s;
   if ((s = check_pg(pg))) return s;
-  if (fp8(p)) return fail(STCE_E_UNSUPPORTED, "the fused policy step takes bf16 or fp32 operands (not the fp8 lane)");
   if (!pg->advantages || !pg->old_logprob || !logprob || !state || !loss)
     return fail(STCE_E_ARG, "advantages, old_logprob, logprob, state and loss are required");
   if (!aligned(pg->advantages, 4) || !aligned(pg->old_logprob, 4) || !aligned(logprob, 4) || !aligned(loss, 4) ||
@@ -1021,26 +1196,104 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
     return fail(STCE_E_ARG, "arrays must be 4-byte aligned (state 16-byte)");
   if ((grad_hidden && !aligned(grad_hidden, 16)) || (grad_weight && !aligned(grad_weight, 16)))
     return fail(STCE_E_ARG, "gradient outputs must be 16-byte aligned");
-  float* so_lse = side_out ? side_out->lse_full : nullptr;
-  float* so_hf = side_out ? side_out->entropy_full : nullptr;
-  float* so_hs = side_out ? side_out->entropy_support : nullptr;
-  if ((so_lse && !aligned(so_lse, 4)) || (so_hf && !aligned(so_hf, 4)) || (so_hs && !aligned(so_hs, 4)))
+  if (side_out && ((side_out->lse_full && !aligned(side_out->lse_full, 4)) ||
+                   (side_out->entropy_full && !aligned(side_out->entropy_full, 4)) ||
+                   (side_out->entropy_support && !aligned(side_out->entropy_support, 4))))
     return fail(STCE_E_ARG, "side outputs must be 4-byte aligned");
-  // a workspace below the default keeps fewer chunks per weight-gradient
-  // group: each further chunk of a group adds exactly G1.Vp * G1.C elements
   if (4 * round_up(p->V, 4) >= (int64_t)INT32_MAX)
     return fail(STCE_E_ARG, "V=%lld: the fused step takes V < 2^29", (long long)p->V);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  auto validate = [&](uint32_t* flags) -> stce_status {
+    hipError_t e2;
+    if (dev_status && (e2 = launch_fill_i64(dev_status, STCE_STATUS_NONE, st))) return hip_fail(e2, "status fill");
+    if ((e2 = launch_validate(p->T, p->V, p->flags & STCE_PROBLEM_IGNORE_INDEX, p->ignore_index, p->temperature,
+                              p->top_k, p->top_p, p->min_p, p->target, flags, dev_status, st)))
+      return hip_fail(e2, "validate");
+    return STCE_OK;
+  };
+  auto chunk_loss = [&](int64_t c0, int64_t nc, float* g) -> stce_status {
+    hipError_t e2 = launch_policy_loss(pg->objective, pg->eps_low, pg->eps_high, pg->scale, pg->advantages + c0,
+                                       pg->old_logprob + c0, (const RowState*)state + c0, nc, logprob + c0,
+                                       loss + c0, g, ratio ? ratio + c0 : nullptr, st);
+    return e2 ? hip_fail(e2, "policy loss") : STCE_OK;
+  };
+
+  if (fused_classed(p)) {
+    const FusedClassLayout L = plan_fused_classed(p);
+    if ((s = check_ws(ws, ws_bytes, L.total))) return s;
+    char* uni = at<char>(ws, L.uni);
+    SweepBufs B{};
+    B.C = L.C;
+    B.ldt = L.ldt;
+    B.ntv = L.ntv;
+    B.nbuf = L.nbuf;
+    B.flags = (uint32_t*)(uni + L.flags);
+    B.tile = uni + L.tile;
+    B.part = uni + L.part;
+    B.sy = uni + L.sy;
+    B.h8 = uni + L.h8;
+    B.ha = uni + L.ha;
+    B.buf_tile = L.buf_tile;
+    B.buf_part = L.buf_part;
+    B.buf_sy = L.buf_sy;
+    B.buf_h8 = L.buf_h8;
+    B.buf_ha = L.buf_ha;
+    if ((s = validate(B.flags))) return s;
+    const void* hid = nullptr;
+    float dh_div = 1.0f;
+    if ((e = hidden_for_products(p, ws, L.hs, 0, p->T, &hid, &dh_div, st))) return hip_fail(e, "prescale hidden");
+    const bool want_grad = grad_hidden || grad_weight;
+    float* g = at<float>(ws, L.g);
+    int* cntj = at<int>(ws, L.cntj);
+    const RowTiles* tl = tiled(p) ? state_tiles(state, p->T, p->V) : nullptr;
+    if (want_grad && grad_weight && (e = launch_fill_i32(cntj, p->V, 0, st))) return hip_fail(e, "clear counts");
+    s = fused_sweep(p, B, hid, logprob, state, side_out, st,
+                    [&](int64_t, int64_t c0, int64_t nc, const float* keys) -> stce_status {
+                      stce_status s2 = chunk_loss(c0, nc, g + c0);
+                      if (s2 || !want_grad || !tl) return s2;
+                      KeysEntriesArgs ka{};
+                      ka.keys = keys;
+                      ka.ld = L.ldt;
+                      ka.rows = nc;
+                      ka.c0 = c0;
+                      ka.V = p->V;
+                      ka.st = (const RowState*)state;
+                      ka.tiles = tl;
+                      ka.g = g;
+                      ka.temp = p->temperature;
+                      ka.target = p->target;
+                      ka.list_row = at<SpEntry>(ws, L.list_row);
+                      ka.rowcnt_row = at<int>(ws, L.rowcnt_row);
+                      ka.cntj = grad_weight ? cntj : nullptr;
+                      hipError_t e2 = launch_keys_entries(ka, st);
+                      return e2 ? hip_fail(e2, "dz entries from the keys") : STCE_OK;
+                    });
+    if (s || !want_grad) return s;
+    const PreEntries pre{at<SpEntry>(ws, L.list_row), at<int>(ws, L.rowcnt_row), cntj};
+    return backward_classed(p, L.B, g, state, hid, dh_div, grad_hidden, grad_weight, accumulate_grad_weight, uni,
+                            st, nullptr, &pre);
+  }
+
+  // a workspace below the default keeps fewer chunks per weight-gradient
+  // group: each further chunk of a group adds exactly G1.Vp * G1.C elements
   const FusedLayout G1 = plan_fused(p, 1);
   if ((s = check_ws(ws, ws_bytes, G1.total))) return s;
   const size_t per_chunk = elt_size(p->dtype) * (size_t)G1.Vp * (size_t)G1.C;
   const FusedLayout L = plan_fused(p, 1 + (int64_t)((ws_bytes - G1.total) / per_chunk));
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e;
-  uint32_t* flags = at<uint32_t>(ws, L.flags);
-  if (dev_status && (e = launch_fill_i64(dev_status, STCE_STATUS_NONE, st))) return hip_fail(e, "status fill");
-  if ((e = launch_validate(p->T, p->V, p->flags & STCE_PROBLEM_IGNORE_INDEX, p->ignore_index, p->temperature,
-                           p->top_k, p->top_p, p->min_p, p->target, flags, dev_status, st)))
-    return hip_fail(e, "validate");
+  SweepBufs B{};
+  B.C = L.C;
+  B.ldt = L.ldt;
+  B.ntv = L.ntv;
+  B.nbuf = L.nbuf;
+  B.flags = at<uint32_t>(ws, L.flags);
+  B.tile = at<char>(ws, L.tile);
+  B.part = at<char>(ws, L.part);
+  B.sy = at<char>(ws, L.sy);
+  B.buf_tile = L.buf_tile;
+  B.buf_part = L.buf_part;
+  B.buf_sy = L.buf_sy;
+  if ((s = validate(B.flags))) return s;
   const size_t es = elt_size(p->dtype);
   const void* hid = nullptr;
   float dh_div = 1.0f;
@@ -1058,116 +1311,48 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
       return hip_fail(e, "transpose hidden");
   }
   const int64_t nch = ceil_div(p->T, L.C);
-  SideCtx* side = nullptr;
-  if (L.nbuf == 2 && (e = side_ctx(&side))) return hip_fail(e, "side stream");
-  auto rows_of = [&](int64_t c) { return p->T - c * L.C < L.C ? p->T - c * L.C : L.C; };
-  // the chunk's keys (every row: the gradient needs them all), then its
-  // selection and selected logprob, on the side stream when there is one
-  auto project_select = [&](int64_t c) -> stce_status {
-    const int64_t c0 = c * L.C, nc = rows_of(c), b = c % L.nbuf;
-    FwdArgs a{};
-    a.dtype = p->dtype;
-    a.W = p->weight;
-    a.h = (const char*)hid + es * (size_t)c0 * p->H;
-    a.H = p->H;
-    a.V = p->V;
-    a.rows = nc;
-    a.tile = at<float>(ws, L.tile + b * L.buf_tile);
-    a.ld = L.ldt;
-    a.temp = p->temperature ? p->temperature + c0 : nullptr;
-    a.target = p->target + c0;
-    a.flags = flags + c0;
-    a.store_all = 1;
-    a.part = at<TilePart>(ws, L.part + b * L.buf_part);
-    a.ntv = (int)L.ntv;
-    a.s_y = at<float>(ws, L.sy + b * L.buf_sy);
-    a.want_ent = (so_hf || so_hs) ? 1 : 0;
-    a.bf16_lane = bf16_lane(p);
-    hipError_t e2;
-    if ((e2 = launch_fwd_projection(a, st))) return hip_fail(e2, "projection");
-    hipStream_t ss = st;
-    if (side) {
-      ss = side->stream;
-      if ((e2 = hipEventRecord(side->fork(c), st)) || (e2 = hipStreamWaitEvent(ss, side->fork(c), 0)))
-        return hip_fail(e2, "fork to the side stream");
-    }
-    SelParams sp{};
-    sp.tile = a.tile;
-    sp.ld = L.ldt;
-    sp.part = a.part;
-    sp.ntv = (int)L.ntv;
-    sp.s_y = a.s_y;
-    sp.flags = flags + c0;
-    sp.target = p->target + c0;
-    sp.top_k = p->top_k ? p->top_k + c0 : nullptr;
-    sp.top_p = p->top_p ? p->top_p + c0 : nullptr;
-    sp.min_p = p->min_p ? p->min_p + c0 : nullptr;
-    sp.logprob = logprob + c0;
-    sp.state = (RowState*)state + c0;
-    sp.tiles = tiles_ok(p->V) ? state_tiles(state, p->T, p->V) + c0 : nullptr;
-    sp.V = (int)p->V;
-    sp.lse_full = so_lse ? so_lse + c0 : nullptr;
-    sp.ent_full = so_hf ? so_hf + c0 : nullptr;
-    sp.ent_supp = so_hs ? so_hs + c0 : nullptr;
-    sp.round_lp_bf16 = bf16_lane(p);
-    launch_select(sp, (int)nc, ss);
-    if ((e2 = hipGetLastError())) return hip_fail(e2, "select");
-    if (side && (e2 = hipEventRecord(side->done(c), ss))) return hip_fail(e2, "selection event");
-    return STCE_OK;
-  };
-  if ((s = project_select(0))) return s;
-  for (int64_t c = 0; c < nch; ++c) {
-    const int64_t c0 = c * L.C, nc = rows_of(c), b = c % L.nbuf;
-    // the next chunk's projection overlaps this chunk's selection; it writes
-    // the other buffer, whose readers (chunk c - 1's selection and dz) are
-    // done: the first is waited for below, the second is earlier on `st`
-    if (c + 1 < nch && (s = project_select(c + 1))) return s;
-    if (side && (e = hipStreamWaitEvent(st, side->done(c), 0))) return hip_fail(e, "join");
-    // the token loss of the chunk's rows
-    RowState* stc = (RowState*)state + c0;
-    float* g = at<float>(ws, L.g);
-    if ((e = launch_policy_loss(pg->objective, pg->eps_low, pg->eps_high, pg->scale, pg->advantages + c0,
-                                pg->old_logprob + c0, stc, nc, logprob + c0, loss + c0, g,
-                                ratio ? ratio + c0 : nullptr, st)))
-      return hip_fail(e, "policy loss");
-    if (!grad_hidden && !grad_weight) continue;
-    // dlogits formed from the chunk's keys, then its dH rows and its share
-    // of dW
-    FusedGradArgs ga{};
-    ga.dtype = p->dtype;
-    ga.keys = at<float>(ws, L.tile + b * L.buf_tile);
-    ga.ld_keys = L.ldt;
-    ga.temp = p->temperature ? p->temperature + c0 : nullptr;
-    ga.target = p->target + c0;
-    ga.st = stc;
-    ga.g = g;
-    ga.d = at<char>(ws, L.d);
-    ga.dT = at<char>(ws, L.dT);
-    ga.ld_dT = L.G * L.C;
-    ga.dT_col = (c % L.G) * L.C;
-    ga.WT = at<char>(ws, L.WT);
-    ga.hT = at<char>(ws, L.hT);
-    ga.h = hid;
-    ga.T = p->T;
-    ga.dh_part = at<float>(ws, L.dhp);
-    ga.splits = (int)L.S;
-    ga.ks = L.ks;
-    ga.grad_hidden = grad_hidden ? (char*)grad_hidden + es * (size_t)c0 * p->H : nullptr;
-    ga.grad_weight = grad_weight;
-    ga.accumulate_w = (c >= L.G || accumulate_grad_weight) ? 1 : 0;
-    ga.rows = nc;
-    ga.rows_pad = round_up(nc, 64);
-    ga.dw = (c % L.G == L.G - 1 || c == nch - 1) ? 1 : 0;
-    ga.dw_c0 = (c / L.G) * L.G * L.C;
-    ga.dw_k = c0 - ga.dw_c0 + ga.rows_pad;
-    ga.Tp = L.Tp;
-    ga.H = p->H;
-    ga.V = p->V;
-    ga.V_pad = L.Vp;
-    ga.dh_div = dh_div;
-    if ((e = launch_fused_chunk_grads(ga, st))) return hip_fail(e, "fused gradients");
-  }
-  return STCE_OK;
+  float* g = at<float>(ws, L.g);
+  return fused_sweep(p, B, hid, logprob, state, side_out, st,
+                     [&](int64_t c, int64_t c0, int64_t nc, const float* keys) -> stce_status {
+                       // the token loss of the chunk's rows, then dlogits from
+                       // the chunk's keys, its dH rows and its share of dW
+                       stce_status s2 = chunk_loss(c0, nc, g);
+                       if (s2 || (!grad_hidden && !grad_weight)) return s2;
+                       FusedGradArgs ga{};
+                       ga.dtype = p->dtype;
+                       ga.keys = keys;
+                       ga.ld_keys = L.ldt;
+                       ga.temp = p->temperature ? p->temperature + c0 : nullptr;
+                       ga.target = p->target + c0;
+                       ga.st = (const RowState*)state + c0;
+                       ga.g = g;
+                       ga.d = at<char>(ws, L.d);
+                       ga.dT = at<char>(ws, L.dT);
+                       ga.ld_dT = L.G * L.C;
+                       ga.dT_col = (c % L.G) * L.C;
+                       ga.WT = at<char>(ws, L.WT);
+                       ga.hT = at<char>(ws, L.hT);
+                       ga.h = hid;
+                       ga.T = p->T;
+                       ga.dh_part = at<float>(ws, L.dhp);
+                       ga.splits = (int)L.S;
+                       ga.ks = L.ks;
+                       ga.grad_hidden = grad_hidden ? (char*)grad_hidden + es * (size_t)c0 * p->H : nullptr;
+                       ga.grad_weight = grad_weight;
+                       ga.accumulate_w = (c >= L.G || accumulate_grad_weight) ? 1 : 0;
+                       ga.rows = nc;
+                       ga.rows_pad = round_up(nc, 64);
+                       ga.dw = (c % L.G == L.G - 1 || c == nch - 1) ? 1 : 0;
+                       ga.dw_c0 = (c / L.G) * L.G * L.C;
+                       ga.dw_k = c0 - ga.dw_c0 + ga.rows_pad;
+                       ga.Tp = L.Tp;
+                       ga.H = p->H;
+                       ga.V = p->V;
+                       ga.V_pad = L.Vp;
+                       ga.dh_div = dh_div;
+                       hipError_t e2 = launch_fused_chunk_grads(ga, st);
+                       return e2 ? hip_fail(e2, "fused gradients") : STCE_OK;
+                     });
 }
 
 stce_status stce_fp8_quantize_rows(const void* x, int64_t R, int64_t H, uint8_t* codes, float* scales,

@@ -11,7 +11,8 @@ enum : int {
   KIND_VALIDATE = 1, KIND_PROJECTION = 2, KIND_SELECT = 3, KIND_DLOGITS = 4, KIND_GRAD_WEIGHT = 5,
   KIND_GRAD_HIDDEN = 6, KIND_TRANSPOSE = 7, KIND_PARTIALS = 8, KIND_POLICY_LOSS = 9, KIND_DZ_KEYS = 10,
   KIND_SPLIT_SUM = 11, KIND_PRESCALE = 12, KIND_CLASSIFY = 13, KIND_SPARSE_DW = 14, KIND_SPARSE_DH = 15,
-  KIND_REPROJECT = 16, KIND_QUANTIZE = 17, KIND_TILE_LISTS = 18, KIND_TILE_RECOMPUTE = 19
+  KIND_REPROJECT = 16, KIND_QUANTIZE = 17, KIND_TILE_LISTS = 18, KIND_TILE_RECOMPUTE = 19,
+  KIND_KEYS_ENTRIES = 20
 };
 
 // Launch-timing hook (no-op unless a profile is attached to this thread).
@@ -260,6 +261,29 @@ struct SparseGradArgs {
   float dh_div;
 };
 hipError_t launch_sparse_grads(const SparseGradArgs& a, hipStream_t s);
+
+// The fused step's tiled rows of one chunk: their dz entries from the
+// chunk's stored keys [rows][ld] (rows c0 .. c0 + rows of the batch) on their
+// listed tiles, into per-row lists list_row [T][NSP] and counts rowcnt_row
+// [T] (only tiled rows are written), counting entries per vocabulary row
+// into cntj [V] when it is not null.  g [T]: the rows' upstream gradients.
+struct KeysEntriesArgs {
+  const float* keys;
+  int64_t ld, rows, c0, V;
+  const RowState* st;     // [T]
+  const RowTiles* tiles;  // [T]
+  const float* g;         // [T]
+  const float* temp;      // [T] or null
+  const int64_t* target;  // [T]
+  SpEntry* list_row;
+  int* rowcnt_row;
+  int* cntj;
+};
+hipError_t launch_keys_entries(const KeysEntriesArgs& a, hipStream_t s);
+// Their lists in permuted-position order once the rows are classified:
+// positions [full, active) take rowcnt_row and list_row of row perm[n].
+hipError_t launch_place_entries(const int* perm, const GradCounts* cnt, const int* rowcnt_row,
+                                const SpEntry* list_row, int* rowcnt, SpEntry* list, int64_t T, hipStream_t s);
 
 // Gradients of one chunk of the fused policy step, from the chunk's stored
 // keys (no recompute product): dz token-major and vocab-major, the chunk's

@@ -28,6 +28,7 @@
 // Every order of summation is fixed (entries are ordered by their index
 // before they are summed), so the results are deterministic although the
 // entry lists are filled with atomics.
+#include "epilogues.hpp"
 #include "kernels.hpp"
 
 namespace stce {
@@ -148,6 +149,78 @@ __global__ __launch_bounds__(256) void class_place_kernel(const RowState* st, co
       perm[p] = (int)(r0 + i);
       rowcnt[p] = 0;
     }
+}
+
+// The fused step's tiled rows: their dz entries formed from the chunk's
+// stored keys (the forward's, which the recompute would reproduce bit for
+// bit) on their listed tiles, with the recompute epilogue's arithmetic, into
+// per-row lists (list_row[t], rowcnt_row[t]: indexed by row, the positions
+// being known only once every chunk is classified), counting the entries of
+// every vocabulary row into cntj (when not null).  One wave per row of the
+// chunk; a tile is 256 keys, four a lane.  The class rule is grad_class's,
+// so exactly the rows the classification will call tiled are listed.
+__global__ __launch_bounds__(256) void keys_entries_kernel(const float* keys, int64_t ld, int64_t rows, int64_t c0,
+                                                           const RowState* st, const RowTiles* tl, const float* g,
+                                                           const float* temp, const int64_t* target, int V,
+                                                           int ntv, SpEntry* list_row, int* rowcnt_row,
+                                                           int* cntj) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int64_t t = c0 + r;
+  const RowState rs = st[t];
+  const float gt = g[t];
+  const int nlist = tl[t].n;
+  if (grad_class(rs, gt, nlist) != GRAD_TILED) return;
+  const float c = gt / (temp ? temp[t] : 1.0f);
+  const float thr = key_value(rs.key_thr), nl = -rs.lse_s * LOG2E;
+  const int idt = rs.id_thr, y = (int)target[t];
+  const float* kr = keys + r * ld;
+  SpEntry* out = list_row + t * NSP;
+  int cnt = 0;
+  for (int i = 0; i < min(nlist, NTILE); ++i) {
+    const int tile = tl[t].t[i];
+    if (tile >= ntv) continue;
+    const int v = tile * VTILE + lane * 4;
+    // (a row holds ld >= V keys, ld a multiple of 4: the group of four is in
+    // the row; keys at or past V are masked)
+    const f32x4 x = v < V ? *(const f32x4*)(kr + v) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int vg = v + e;
+      const float sv = x[e];
+      const bool in = ((sv > thr) | ((sv == thr) & (vg <= idt))) && vg < V;
+      const float q = in ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv, LOG2E, nl)) : 0.f;
+      const float dv = c * ((vg == y ? 1.f : 0.f) - q);
+      const uint64_t b = __ballot(in);  // (every lane of the wave is active)
+      const int slot = cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0));
+      if (in && slot < NSP) {
+        // rounded to bf16 like every dz entry
+        out[slot] = SpEntry{vg, (float)(bf16)dv};
+        if (cntj) atomicAdd(cntj + vg, 1);
+      }
+      cnt += __builtin_popcountll(b);
+    }
+  }
+  if (lane == 0) rowcnt_row[t] = cnt;
+}
+
+// The tiled positions' entry lists, copied from the per-row lists into
+// permuted-position order: rowcnt[n] = rowcnt_row[perm[n]] and its entries,
+// for n in [full, active).  One wave per position.
+__global__ __launch_bounds__(256) void place_entries_kernel(const int* perm, const GradCounts* cnt,
+                                                            const int* rowcnt_row, const SpEntry* list_row,
+                                                            int* rowcnt, SpEntry* list, int64_t T) {
+  const int lane = threadIdx.x & 63;
+  const GradCounts c = *cnt;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  for (int64_t n = c.full + (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+       n < c.active && n < T; n += nw) {
+    const int64_t t = perm[n];
+    const int k = rowcnt_row[t];
+    if (lane == 0) rowcnt[n] = k;
+    for (int i = lane; i < min(k, NSP); i += 64) list[n * NSP + i] = list_row[t * NSP + i];
+  }
 }
 
 // out[n] = in[perm[n]], rows of H elements (H a multiple of 8, 16-byte rows).
@@ -732,6 +805,24 @@ hipError_t launch_exclusive_scan(const int* x, int64_t n, int* sums, int* y, hip
   hipLaunchKernelGGL(scan_sums_kernel, dim3(nb), dim3(256), 0, s, x, n, sums);
   hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(1024), 0, s, sums, (int)nb, y + n);
   hipLaunchKernelGGL(scan_apply_kernel, dim3(nb), dim3(256), 0, s, x, n, sums, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_keys_entries(const KeysEntriesArgs& a, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  ProfScope ps(KIND_KEYS_ENTRIES, s);
+  hipLaunchKernelGGL(keys_entries_kernel, dim3((unsigned)ceil_div(a.rows, 4)), dim3(256), 0, s, a.keys, a.ld, a.rows,
+                     a.c0, a.st, a.tiles, a.g, a.temp, a.target, (int)a.V, (int)ceil_div(a.V, VTILE), a.list_row,
+                     a.rowcnt_row, a.cntj);
+  return hipGetLastError();
+}
+
+hipError_t launch_place_entries(const int* perm, const GradCounts* cnt, const int* rowcnt_row,
+                                const SpEntry* list_row, int* rowcnt, SpEntry* list, int64_t T, hipStream_t s) {
+  ProfScope ps(KIND_KEYS_ENTRIES, s);
+  const unsigned blocks = (unsigned)(ceil_div(T, 4) < 8192 ? ceil_div(T, 4) : 8192);
+  hipLaunchKernelGGL(place_entries_kernel, dim3(blocks), dim3(256), 0, s, perm, cnt, rowcnt_row, list_row, rowcnt,
+                     list, T);
   return hipGetLastError();
 }
 

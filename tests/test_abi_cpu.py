@@ -80,8 +80,9 @@ def test_unsupported_dtype_is_one_actionable_error(lib):
 
 def test_fp8_lane_host_checks(lib):
     """The fp8 lane: H a multiple of 16, weight_scale required, neither the
-    bf16 value lane, the pre-GEMM temperature nor the fused step; its
-    workspaces add the quantized hidden rows (codes and scales)."""
+    bf16 value lane nor the pre-GEMM temperature; its workspaces add the
+    quantized hidden rows (codes and scales), and its fused step takes the
+    path with row classes (one workspace size)."""
     fp8 = binding.DT_FP8
     with pytest.raises(binding.StceError, match="H=72.*multiple of 16"):
         binding.workspace_bytes(_prob(dtype=fp8, H=72))
@@ -90,8 +91,8 @@ def test_fp8_lane_host_checks(lib):
     with pytest.raises(binding.StceError, match="UNSUPPORTED.*pre-GEMM"):
         binding.workspace_bytes(_prob(dtype=fp8, flags=binding.PROBLEM_PRE_GEMM_TEMPERATURE,
                                       pre_gemm_temperature=0.5))
-    with pytest.raises(binding.StceError, match="UNSUPPORTED.*fused"):
-        binding.fused_workspace_bytes(_prob(dtype=fp8))
+    full, least = binding.fused_workspace_bytes(_prob(dtype=fp8))
+    assert full == least > 0
     p = _prob(dtype=fp8)
     p.hidden, p.weight, p.target = 16, 16, 16          # fake, never dereferenced
     st = lib.stce_forward(ctypes.byref(p), ctypes.c_void_p(16), ctypes.c_void_p(16), None, None, 0, None)
@@ -260,6 +261,27 @@ def test_fused_workspace_is_host_computable_and_chunk_bounded(lib):
     assert nmin == n - 2 * Vp * 512 * (-(-100000 // 512) - 1)
     n2 = binding.fused_workspace_bytes(_prob(T=100000, chunk_rows=100))[1]   # rounded up to 128 rows
     assert n2 > binding.fused_workspace_bytes(_prob(T=100000, chunk_rows=64))[1]
+
+
+def test_fused_workspace_of_the_classed_path(lib):
+    """A bf16 problem with a filter array takes the fused step's path with
+    row classes: one size (no weight-gradient groups), holding the rows'
+    gradients and entry lists, the per-vocabulary-row counts, and the larger
+    of the sweep's buffers and the backward's workspace."""
+    T, H, V = 16384, 5120, 151936
+    dense, _ = binding.fused_workspace_bytes(_prob(T=T, H=H, V=V))
+    for kw in (dict(top_k=16), dict(top_p=16), dict(min_p=16), dict(top_k=16, dtype=binding.DT_FP8)):
+        full, least = binding.fused_workspace_bytes(_prob(T=T, H=H, V=V, **kw))
+        _, bwd = binding.workspace_bytes(_prob(T=T, H=H, V=V, **kw))
+        C, ldt, ntv = 4096, V, -(-V // 256)
+        sweep = 4 * T + 2 * (4 * C * ldt + 16 * C * ntv + 4 * C)
+        kept = 4 * T + 8 * 128 * T + 4 * T + 4 * V
+        assert full == least, kw
+        assert kept + max(sweep, bwd) <= full < kept + max(sweep, bwd) + 4096, kw
+        assert full < dense
+    # fp32 operands keep the dense path whatever the filters
+    f32, f32min = binding.fused_workspace_bytes(_prob(T=T, H=H, V=V, dtype=binding.DT_F32, top_k=16))
+    assert f32 > f32min
 
 
 def test_fused_step_rejects_bad_arguments_before_launch(lib):

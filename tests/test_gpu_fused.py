@@ -1,6 +1,9 @@
 """GPU parity of the fused head + policy-gradient step, through the C ABI.
 The step forms dlogits inside the forward's sweep from the chunk's stored
-keys, so no logits product is recomputed.
+keys.  With row classes (bf16 operands with a filter given, or the fp8
+lane) it forms the tiled rows' dz entries from the keys and then runs the
+classed backward without its tile recompute; dense (fp32, or bf16 with no
+filter) it forms every row's dz and needs no recompute product at all.
 
 * Against the oracle (forward, token loss and VJP in fp64) at the core's
   bar: logprob within 2e-3, the summed loss within 1e-3 relative, and
@@ -14,6 +17,13 @@ keys, so no logits product is recomputed.
     recompute's, but the products reduce in another order;
   - inactive, invalid and out-of-support rows, a frozen head, weight-gradient
     accumulation and the side outputs are all covered.
+* With row classes the gradients equal the unfused sequence's bit for bit
+  (the tiled rows' entries are formed from keys equal to the recompute's,
+  every other row goes through the same backward), on batches that mix
+  every class within a chunk, on the fp8 lane, for a frozen head and with
+  weight-gradient accumulation.
+* The dense path, taken by bf16 problems with no filter arrays, against the
+  oracle and against the unfused sequence.
 * At the full headline size, in the default schedule, the same comparison
   with the unfused path.
 """
@@ -92,14 +102,17 @@ def test_fused_step_matches_oracle(name, T, V, objective, chunk):
     assert rl < 1e-3 and rh < GRAD_RTOL and rw < GRAD_RTOL
 
 
-def _unfused(G, A, old, objective, sc, ignore_index=None, side=False, gw0=None):
-    r = binding.forward(G["h"], G["W"], G["target"], **meta_of(G), check=False, side=side,
-                        ignore_index=ignore_index)
+def _unfused(G, A, old, objective, sc, ignore_index=None, side=False, gw0=None, meta=None, need_weight=True):
+    meta = meta_of(G) if meta is None else meta
+    ws = G.get("weight_scale")
+    r = binding.forward(G["h"], G["W"], G["target"], **meta, check=False, side=side,
+                        ignore_index=ignore_index, weight_scale=ws)
     lp, st = r[0], r[1]
     loss, g, ratio = binding.policy_loss(lp, A, old, objective, EL, EH, sc, st)
     gw = None if gw0 is None else gw0.clone()
-    gh, gw = binding.backward(G["h"], G["W"], G["target"], st, g, **meta_of(G), grad_weight=gw,
-                              accumulate_grad_weight=gw0 is not None, ignore_index=ignore_index)
+    gh, gw = binding.backward(G["h"], G["W"], G["target"], st, g, **meta, grad_weight=gw,
+                              accumulate_grad_weight=gw0 is not None, ignore_index=ignore_index,
+                              weight_scale=ws, need_weight=need_weight)
     out = dict(logprob=lp, state=st, loss=loss, ratio=ratio, grad_hidden=gh, grad_weight=gw)
     if side:
         out.update(r[2])
@@ -220,3 +233,144 @@ def test_many_chunks_equal_the_unfused_sequence():
     rw = rel_fro(f["grad_weight"].cpu().numpy(), u["grad_weight"].cpu().numpy())
     say(f"  bitwise logprob/state/loss/ratio; dH rel {rh:.2e}  dW rel {rw:.2e}")
     assert rh < 1e-3 and rw < 1e-5
+
+
+def _classed_case(name, T, V):
+    """A small batch of the named workload whose chunks mix every row class:
+    every fifth row unfiltered (its support the whole vocabulary: dense),
+    every seventh a top-p row of a wide support (over 128 tokens: dense),
+    every eleventh a top-64 row (sparse where its support spreads past 31
+    tiles), the rest top-k rows (tiled); one row's target outside its
+    support, one invalid row."""
+    w = workloads.make(name, T=T)
+    if V is not None and V < w["V"]:
+        w["W"], w["V"] = w["W"][:V], V
+        if w.get("w_scale") is not None:
+            w["w_scale"] = w["w_scale"][:V]
+        w["target_uniform"] = w["target_uniform"] % V
+    w["top_k"][::5], w["top_p"][::5], w["min_p"][::5] = 0, 1.0, 0.0
+    w["top_k"][3::7], w["top_p"][3::7] = 0, 0.9
+    w["top_k"][6::11] = 64            # past 31 tiles when V is large: the sparse class
+    y = np.asarray(targets(w), np.int64) % w["W"].shape[0]
+    G = to_gpu(w, y)
+    # row 1: top-2 with the target at the lowest logit (the oracle's)
+    if w["dtype"] == "fp8":
+        z1 = oracle.fp8_logits(w["h"][1:2], w["W"], w["w_scale"])[0]
+    else:
+        z1 = w["W"].astype(np.float64) @ w["h"][1].astype(np.float64)
+    G["top_k"][1], G["top_p"][1] = 2, 1.0
+    G["target"][1] = int(np.argmin(z1))
+    G["top_p"][2] = 1.5                                   # invalid metadata
+    return w, y, G
+
+
+@pytest.mark.parametrize("name,T,V,chunk", [
+    ("headline", 300, 5000, 64),      # 5 chunks, the last of 44 rows
+    ("headline", 200, 3000, 0),       # one chunk
+    ("top_p", 260, 6000, 128),
+    ("headline_fp8", 300, 30000, 128),
+])
+def test_classed_fused_step_equals_the_unfused_sequence_bitwise(name, T, V, chunk):
+    w, y, G = _classed_case(name, T, V)
+    V = w["W"].shape[0]
+    ws = G.get("weight_scale")
+    lp0, st0 = binding.forward(G["h"], G["W"], G["target"], **meta_of(G), check=False, weight_scale=ws)
+    A, old = _pg_inputs(lp0.cpu().numpy(), 23)
+    A, old = torch.from_numpy(A).to(dev()), torch.from_numpy(old).to(dev())
+    sc = 1.0 / T
+    u = _unfused(G, A, old, "clip", sc)
+    full, least = binding.fused_workspace_bytes(binding.make_problem(G["h"], G["W"], G["target"], **meta_of(G),
+                                                                     weight_scale=ws)[0])
+    assert full == least                                  # the classed path's workspace has no groups
+    f = binding.fused_policy_step(G["h"], G["W"], G["target"], A, old, **meta_of(G), objective="clip",
+                                  eps_low=EL, eps_high=EH, scale=sc, chunk_rows=chunk, check=False,
+                                  weight_scale=ws)
+    info = binding.decode_state(f["state"])
+    fl = info["flags"]
+    live = ((fl & binding.FLAG_VALID) != 0) & ((fl & binding.FLAG_IN_SUPPORT) != 0)
+    filt = live & ((fl & binding.FLAG_FILTERED) != 0)
+    tiled = filt & (info["n"] <= 128) & (info["ntile"] > 0)
+    say(f"classed fused vs unfused: {name} T={T} V={V} chunk={chunk or 'default'}: rows dense "
+        f"{int((live & ~filt).sum() + (filt & (info['n'] > 128)).sum())}, tiled {int(tiled.sum())}, sparse "
+        f"{int((filt & (info['n'] <= 128) & (info['ntile'] == 0)).sum())}, no gradient {int((~live).sum())}")
+    assert tiled.sum() > 0 and (live & ~filt).sum() > 0 and (~live).sum() >= 2
+    if V > 31 * 256:
+        assert (filt & (info["n"] <= 128) & (info["ntile"] == 0)).sum() > 0
+    for k in ("logprob", "state", "loss", "ratio", "grad_hidden", "grad_weight"):
+        assert _same(f[k], u[k]), k
+    # a frozen head: the same hidden gradient; weight-gradient accumulation:
+    # the same sum onto the same start
+    fz = binding.fused_policy_step(G["h"], G["W"], G["target"], A, old, **meta_of(G), objective="clip",
+                                   eps_low=EL, eps_high=EH, scale=sc, chunk_rows=chunk, need_weight=False,
+                                   check=False, weight_scale=ws)
+    assert fz["grad_weight"] is None and _same(fz["grad_hidden"], u["grad_hidden"])
+    gw0 = torch.randn(V, w["H"], device=dev(), dtype=torch.float32)
+    ua = _unfused(G, A, old, "clip", sc, gw0=gw0)
+    fa = binding.fused_policy_step(G["h"], G["W"], G["target"], A, old, **meta_of(G), objective="clip",
+                                   eps_low=EL, eps_high=EH, scale=sc, chunk_rows=chunk, grad_weight=gw0.clone(),
+                                   accumulate_grad_weight=True, check=False, weight_scale=ws)
+    assert _same(fa["grad_weight"], ua["grad_weight"])
+    say("  bitwise: logprob, state, loss, ratio, grad_hidden, grad_weight; frozen head; accumulation")
+
+
+def test_classed_fused_step_matches_the_oracle_on_the_fp8_lane():
+    w, y, G = _classed_case("headline_fp8", 160, 20000)
+    G["top_p"][2] = float(w["top_p"][2])                 # (the oracle takes valid metadata only)
+    V = w["W"].shape[0]
+    ws = G["weight_scale"]
+    say(f"classed fused step vs oracle, fp8 lane: T=160 H={w['H']} V={V}")
+    keys = binding.scaled_logits(G["h"], G["W"], G["temperature"], weight_scale=ws).cpu().numpy()
+    meta = {k: G[k].cpu().numpy() for k in ("top_k", "top_p", "min_p")}
+    yy = G["target"].cpu().numpy()
+    ref = oracle.forward(w["h"], w["W"], yy, w["temperature"], meta["top_k"], meta["top_p"], meta["min_p"],
+                         keys=keys, lane="fp8", w_scale=w["w_scale"])
+    A, old = _pg_inputs(ref["logprob"], 29)
+    sc = 1.0 / 160
+    out = binding.fused_policy_step(G["h"], G["W"], G["target"], torch.from_numpy(A).to(dev()),
+                                    torch.from_numpy(old).to(dev()), **meta_of(G), objective="cispo",
+                                    eps_low=EL, eps_high=EH, scale=sc, chunk_rows=64, check=False, weight_scale=ws)
+    fin = np.isfinite(ref["logprob"])
+    lp = out["logprob"].cpu().numpy()
+    assert np.array_equal(np.isfinite(lp), fin)
+    err = float(np.abs(lp[fin] - ref["logprob"][fin]).max())
+    pg = oracle.policy_loss(ref["logprob"], A, old, "cispo", EL, EH, sc)
+    dH, dW = oracle.backward(w["h"], w["W"], yy, ref, pg["g"], w["temperature"], w_scale=w["w_scale"])
+    rh = rel_fro(out["grad_hidden"].float().cpu().numpy(), dH)
+    rw = rel_fro(out["grad_weight"].cpu().numpy(), dW)
+    say(f"  logprob err {err:.2e}  dH rel {rh:.2e}  dW rel {rw:.2e}")
+    assert err < 2e-3 and rh < GRAD_RTOL and rw < GRAD_RTOL
+
+
+def test_dense_fused_path_without_filters():
+    """bf16 with no filter arrays: every row's support is the vocabulary, the
+    step takes its dense path (dz of every row, two gradient products),
+    against the oracle and the unfused sequence."""
+    w, y, G = _setup("headline", 200, 4096)
+    V = w["W"].shape[0]
+    T = 200
+    y = np.asarray(w["target_uniform"], np.int64) % V
+    G["target"] = torch.from_numpy(y).to(dev())
+    none = dict(temperature=G["temperature"], top_k=None, top_p=None, min_p=None)
+    prob, _ = binding.make_problem(G["h"], G["W"], G["target"], **none, chunk_rows=64)
+    full, least = binding.fused_workspace_bytes(prob)
+    assert full > least                                   # the dense path's grouped workspace
+    say(f"dense fused path (no filters): headline T={T} V={V}")
+    keys = binding.scaled_logits(G["h"], G["W"], G["temperature"]).cpu().numpy()
+    zk, op, zm = np.zeros(T, np.int32), np.ones(T, np.float32), np.zeros(T, np.float32)
+    ref = oracle.forward(w["h"], w["W"], y, w["temperature"], zk, op, zm, keys=keys)
+    A, old = _pg_inputs(ref["logprob"], 31)
+    A, old = torch.from_numpy(A).to(dev()), torch.from_numpy(old).to(dev())
+    sc = 1.0 / T
+    f = binding.fused_policy_step(G["h"], G["W"], G["target"], A, old, **none, objective="cispo", eps_low=EL,
+                                  eps_high=EH, scale=sc, chunk_rows=64)
+    u = _unfused(G, A, old, "cispo", sc, meta=none)
+    for k in ("logprob", "state", "loss", "ratio"):
+        assert _same(f[k], u[k]), k
+    pg = oracle.policy_loss(ref["logprob"], A.cpu().numpy(), old.cpu().numpy(), "cispo", EL, EH, sc)
+    dH, dW = oracle.backward(w["h"], w["W"], y, ref, pg["g"], w["temperature"])
+    rh = rel_fro(f["grad_hidden"].float().cpu().numpy(), dH)
+    rw = rel_fro(f["grad_weight"].cpu().numpy(), dW)
+    ruh = rel_fro(f["grad_hidden"].float().cpu().numpy(), u["grad_hidden"].float().cpu().numpy())
+    ruw = rel_fro(f["grad_weight"].cpu().numpy(), u["grad_weight"].cpu().numpy())
+    say(f"  vs oracle: dH rel {rh:.2e}  dW rel {rw:.2e}; vs unfused: dH rel {ruh:.2e}  dW rel {ruw:.2e}")
+    assert rh < GRAD_RTOL and rw < GRAD_RTOL and ruh < 1e-3 and ruw < 1e-5
