@@ -142,15 +142,18 @@ def row_classes(info, g, tiled_on, nsp=128):
     """Rows of each backward class, by the library's rule: a row with a
     gradient (target in its support, valid metadata, nonzero upstream
     gradient) is sparse when its support holds at most nsp tokens, dense
-    otherwise (unfiltered rows included), and a sparse row with a tile list
-    is tiled (its keys recomputed on those tiles only); the others are
-    empty.  Also the (row, tile) pairs of the tiled rows."""
+    otherwise (unfiltered rows included); a sparse row whose support the
+    state lists is listed (its dz from the stored keys), else one with a
+    tile list is tiled (its keys recomputed on those tiles only); the others
+    are empty.  Also the (row, tile) pairs of the tiled rows."""
     fl = info["flags"]
     active = ((fl & 1) != 0) & ((fl & 4) != 0) & (g != 0)
     dense = active & (((fl & 2) == 0) | (info["n"] > nsp))
-    tiled = active & ~dense & (info["ntile"] > 0) & tiled_on
-    return {"dense": int(dense.sum()), "sparse": int((active & ~dense & ~tiled).sum()), "tiled": int(tiled.sum()),
-            "empty": int((~active).sum()), "tile_pairs": int(info["ntile"][tiled].sum())}
+    listed = active & ~dense & ((fl & 32) != 0)
+    tiled = active & ~dense & ~listed & (info["ntile"] > 0) & tiled_on
+    return {"dense": int(dense.sum()), "sparse": int((active & ~dense & ~listed & ~tiled).sum()),
+            "listed": int(listed.sum()), "tiled": int(tiled.sum()), "empty": int((~active).sum()),
+            "tile_pairs": int(info["ntile"][tiled].sum())}
 
 
 KERNEL_SYMBOLS = {
@@ -170,8 +173,7 @@ TRACE_LABELS = [
     ("tile_count", "tile recompute work lists (count, work items, fill)"),
     ("tile_work", "tile recompute work lists (count, work items, fill)"),
     ("tile_fill", "tile recompute work lists (count, work items, fill)"),
-    ("keys_entries", "fused step: tiled rows' dz entries from the chunk keys"),
-    ("place_entries", "fused step: tiled rows' dz entries placed by position"),
+    ("listed_entries", "listed rows' dz entries from the state's support lists"),
     ("EpiStore", "gemm: grad_weight of the dense rows (EpiStore)"),
     ("EpiAccumT", "gemm: grad_hidden of the dense rows as dH^T (EpiAccumT)"),
     ("EpiDlogits", "gemm: backward recompute + dz^T, fp32 operands (EpiDlogits)"),
@@ -678,14 +680,14 @@ def main():
     # and for the fp8 lane, dense otherwise
     any_filter = any(meta[k] is not None for k in ("top_k", "top_p", "min_p"))
     fused_classed = args.fused and dt == torch.bfloat16 and (fp8 or any_filter)
-    if args.fused:
+    if args.fused and not fused_classed:
         C = min(-(-(args.chunk_rows or 4096) // 64) * 64, -(-T // 64) * 64)
-        Vs = Vs if fused_classed else None
+        Vs = None
     # the backward's row classes (bf16 and the fp8 lane): the recompute
     # product runs over the rows with a gradient, the two gradient products
     # over the dense rows; sparse rows' gradients are sums over their dz
-    # entries, the tiled rows' formed from their listed tiles (recomputed, or
-    # in the fused step read from the chunk's keys)
+    # entries, formed from the keys the state lists, or recomputed on their
+    # listed tiles, or in the whole-vocabulary recompute
     classed = dt == torch.bfloat16 and (not args.fused or fused_classed)
     tiled_on = classed and -(-V // 256) <= 65535 and T * H * (1 if fp8 else 2) < 2 ** 31 - 1 - 2 ** 22
     classes = row_classes(binding.decode_state(state), g.cpu().numpy(), tiled_on)
@@ -693,7 +695,7 @@ def main():
     t_dense = classes["dense"] if classed else T
     # the tile recompute forms 256 keys of H-long products per (row, tile) pair
     per_step_flop = {"projection": 2.0 * T * H * V, "dlogits": 2.0 * t_full * H * V,
-                     "tile_recompute": 2.0 * classes["tile_pairs"] * 256 * H if classed and not args.fused else 0.0,
+                     "tile_recompute": 2.0 * classes["tile_pairs"] * 256 * H if classed else 0.0,
                      "grad_weight": 2.0 * t_dense * H * V, "grad_hidden": 2.0 * t_dense * H * V}
     if args.fused and not fused_classed:
         per_step_flop = {k: 2.0 * T * H * V for k in ("projection", "grad_weight", "grad_hidden")}
@@ -744,8 +746,7 @@ def main():
                                f"{float(w['min_p'].max())}; forward + backward (grad_hidden, grad_weight)"
                                + ("" if args.policy_loss == "none" else
                                   f" of the {args.policy_loss} policy-gradient token loss")
-                               + ("; fused step: the tiled rows' dz entries from the chunks' keys, no tile "
-                                  "recompute" if fused_classed else
+                               + ("; fused step (forward, loss and backward in one call)" if fused_classed else
                                   "; fused step: dlogits formed in the forward's sweep, no recompute product"
                                   if args.fused else "")
                                + ("; forward side outputs (full LSE, entropies)" if args.side_outputs else "")

@@ -127,10 +127,15 @@ typedef enum {
  * row's support tokens: the tiles whose largest key reaches the row's last
  * support key, at most 31 of them (a count, then the tile indices in
  * increasing order; count 0 when there are more, on unfiltered rows, and when
- * the vocabulary has more than 65,535 tiles).  The backward recomputes the
- * keys of a sparse row with such a list on its tiles only.  Neither part is
- * of size [T, V]. */
-#define STCE_STATE_BYTES_PER_ROW 96
+ * the vocabulary has more than 65,535 tiles), then T 1024-byte support lists:
+ * for a filtered row whose support of at most 128 tokens the selection holds
+ * whole when it decides it (as for a top-k row decided from the projection's
+ * candidates), its tokens as (int32 token id, fp32 key) pairs in decreasing
+ * key order, increasing id among equal keys (flag bit 5 of the record then
+ * set); zeros past the support and on every other row.  The backward forms a
+ * listed row's dz from those keys, and recomputes the keys of a sparse row
+ * with a tile list on its tiles only.  No part is of size [T, V]. */
+#define STCE_STATE_BYTES_PER_ROW 1120
 
 typedef struct stce_problem {
   int64_t T;             /* rows (scored tokens), 1 <= T <= 2^22 - 64 (the products
@@ -306,7 +311,9 @@ stce_status stce_scaled_logits(const stce_problem *prob, int64_t row0, int64_t n
  * and re-derives membership from these keys).  A row the backward recomputes
  * on its listed tiles only (a sparse row with a tile list, see
  * STCE_STATE_BYTES_PER_ROW) gets the keys of those tiles; its other entries
- * are not written.  Every other row gets all V keys.  Arguments and
+ * are not written, and neither is any key of a row whose support the state
+ * lists (the backward recomputes none of them).  Every other row gets all V
+ * keys.  Arguments and
  * workspace as stce_backward; keys_out is required. */
 stce_status stce_recompute_keys(const stce_problem *prob, const float *grad_logprob, const void *state,
                                 float *keys_out, void *ws, size_t ws_bytes, void *stream);
@@ -338,7 +345,7 @@ typedef struct stce_row_info {
   int32_t id_thr;
   int32_t n;
   uint32_t flags; /* bit 0 valid metadata, bit 1 filtered row, bit 2 target in support,
-                     bit 3 inactive (ignore_index) row */
+                     bit 3 inactive (ignore_index) row, bit 5 support listed in the state */
   float lse_support;
   float lse_full;
   float row_max;
@@ -372,7 +379,7 @@ stce_status stce_decode_state(const void *host_state, int64_t nrows, stce_row_in
 #define STCE_KERNEL_QUANTIZE 17    /* fp8 lane: per-row e4m3 quantization of hidden rows */
 #define STCE_KERNEL_TILE_LISTS 18  /* backward: per-tile lists of the rows whose keys are recomputed there */
 #define STCE_KERNEL_TILE_RECOMPUTE 19 /* backward: recompute of those rows' keys on their listed tiles */
-#define STCE_KERNEL_KEYS_ENTRIES 20 /* fused step: those rows' dz entries from the stored keys, and their placement */
+#define STCE_KERNEL_LISTED_ENTRIES 20 /* backward: dz entries of the rows whose support the state lists */
 typedef struct stce_profile {
   int32_t capacity;
   int32_t count;
@@ -424,62 +431,55 @@ stce_status stce_policy_loss(const stce_pg_params *pg, int64_t T, const float *l
  * section 5.4 A: the "Fused" row of its GEMM-count table and "Why the
  * in-chunk form works for this loss").  The token coefficient needs only the
  * new logprob, which a chunk has just computed, so dlogits can be formed
- * inside the forward's sweep from the chunk's keys instead of a recompute.
- * Per chunk of rows, on `stream`:
- *   1. the projection keeps the fp32 keys of every row of the chunk (fp8
- *      lane: the chunk's hidden rows quantized first, as in stce_forward);
- *   2. the support program and selected logprob as in stce_forward (side
- *      outputs as in stce_forward_with_side, `side` may be NULL);
- *   3. the token loss, its gradient g and the ratio as in stce_policy_loss;
- *   4. dlogits from the stored keys, with the arithmetic of stce_backward's
- *      recompute (so equal to it bit for bit), on one of two paths:
+ * from keys the forward's sweep keeps instead of a recompute.  Two paths:
  *   - with row classes, when the operands are bf16 and a filter is given
- *     (top_k, top_p or min_p not NULL), or on the fp8 lane: the rows
- *     stce_backward would recompute on their listed tiles only (support of
- *     at most 128 tokens, a tile list in the state) take their dz entries
- *     from the chunk's keys; after the sweep the backward of stce_backward
- *     runs with g, without that tile recompute (its other rows: dense ones
- *     through the recompute product and the two gradient products over
- *     those rows only, sparse ones through their support).  The gradients
- *     are then bitwise stce_backward's on the same inputs.  A batch whose
- *     rows are all top-k rows (as at T = 16384, V = 151936, top_k 20) makes
- *     the matrix products one: the projection;
+ *     (top_k, top_p or min_p not NULL), or on the fp8 lane: stce_forward
+ *     (side outputs as in stce_forward_with_side, `side` may be NULL), the
+ *     token loss, its gradient g and the ratio as in stce_policy_loss, then
+ *     stce_backward of g, in one call on `stream`.  The sweep keeps each
+ *     small support with its keys in the state (see
+ *     STCE_STATE_BYTES_PER_ROW), from which the backward forms those rows'
+ *     dlogits with no recompute; only the other rows are recomputed.  Every
+ *     output is bitwise that of the unfused sequence on the same inputs;
  *   - dense, for fp32 operands or bf16 with no filter (every row's support
- *     is the whole vocabulary, so every row's dz is dense): dz of every row
- *     from the keys; the chunk's grad_hidden rows = dz . W (split over the
- *     vocabulary, fp32 partials summed in split order); the vocab-major dz of
- *     a group of consecutive chunks is kept (as many as 8 GB hold: all of
- *     them at the sizes below), and at a group's end grad_weight (+)= dz^T . h
- *     with the group's rows as the reduction: 2 products for a frozen head
- *     (logits, dH), 3 for a trainable one (plus dW), against 3 and 4 for
- *     stce_forward + stce_policy_loss + stce_backward.  The gradients differ
- *     from the unfused sequence's only by fp32 summation order.
+ *     is the whole vocabulary, so every row's dz is dense), per chunk of
+ *     rows: the projection keeps the fp32 keys of every row of the chunk;
+ *     the support program and logprob as in stce_forward; the token loss;
+ *     dz = g (1[j == y] - q) / T from the stored keys, with the arithmetic
+ *     of stce_backward's recompute (so equal to it bit for bit); the chunk's
+ *     grad_hidden rows = dz . W (split over the vocabulary, fp32 partials
+ *     summed in split order); the vocab-major dz of a group of consecutive
+ *     chunks is kept (as many as 8 GB hold: all of them at the sizes below),
+ *     and at a group's end grad_weight (+)= dz^T . h with the group's rows as
+ *     the reduction.  2 products for a frozen head (logits, dH), 3 for a
+ *     trainable one (plus dW), against 3 and 4 for stce_forward +
+ *     stce_policy_loss + stce_backward; logprob, state and loss are bitwise
+ *     those of the unfused sequence, the gradients differ from its only by
+ *     fp32 summation order.
  * Outputs: logprob, state (as stce_forward), loss and ratio (as
  * stce_policy_loss; ratio may be NULL), and the gradients of sum_t loss[t]:
  * grad_hidden [T][H] in the hidden dtype (bf16 on the fp8 lane) and
  * grad_weight [V][H] fp32 (overwritten, or added to when
  * accumulate_grad_weight is nonzero); either may be NULL, both NULL =
- * forward and loss only.  logprob, state and loss are bitwise those of the
- * unfused sequence on the same inputs.  pg->state is not read (the step's own
- * state marks inactive rows).  The chunk size is prob->chunk_rows rounded up
- * to a multiple of 64 (default 4096).  Workspace: 256-byte aligned device
- * memory of stce_fused_workspace_bytes (which of the paths a problem takes
- * depends only on its dtype and which filter pointers are set).  Both paths
- * hold the fp32 keys of two chunks (a chunk's selection runs on a side stream
- * of the library's while the next chunk is projected, joined by event waits
- * as in stce_forward), and with the scalar pre-GEMM temperature h / Ts.  With
- * row classes, then, the rows' g and dz entry lists, and stce_backward's
- * workspace in the space the keys leave (bytes == min_bytes; 7.1 GB at
- * T = 16384, H = 5120, V = 151936, bf16 or fp8).  Dense: the group's vocab-major dz (with
- * bf16 operands the only copy: the hidden gradient is formed transposed and
- * reads it as it is; fp32 also keeps a chunk's token-major copy), the
- * transposed weight (and for fp32 the transposed hidden) and the split
- * partials (11.9 GB at those sizes, 8.2 GB at its minimum); a workspace
- * between *min_bytes (one chunk per group) and *bytes keeps as many chunks
- * per group as it holds, which changes only the order of dW's fp32 sums.
- * Host errors as stce_forward, stce_backward and stce_policy_loss, and V must
- * be below 2^29 (the chunk's key rows are read through 32-bit buffer
- * offsets). */
+ * forward and loss only.  pg->state is not read (the step's own state marks
+ * inactive rows).  Workspace: 256-byte aligned device memory of
+ * stce_fused_workspace_bytes (which path a problem takes depends only on its
+ * dtype and which filter pointers are set).  With row classes: g [T], then
+ * one region holding stce_forward's workspace and afterwards stce_backward's
+ * (bytes == min_bytes; 7.1 GB at T = 16384, H = 5120, V = 151936).  Dense
+ * (chunk: prob->chunk_rows rounded up to a multiple of 64, default 4096):
+ * the fp32 keys of two chunks (a chunk's selection runs on a side stream of
+ * the library's while the next chunk is projected, joined by event waits as
+ * in stce_forward), the group's vocab-major dz (with bf16 operands the only
+ * copy: the hidden gradient is formed transposed and reads it as it is;
+ * fp32 also keeps a chunk's token-major copy), the transposed weight (and
+ * for fp32 the transposed hidden), the split partials and, with the scalar
+ * pre-GEMM temperature, h / Ts (11.9 GB at those sizes, 8.2 GB at its
+ * minimum); a workspace between *min_bytes (one chunk per group) and *bytes
+ * keeps as many chunks per group as it holds, which changes only the order
+ * of dW's fp32 sums.  Host errors as stce_forward, stce_backward and
+ * stce_policy_loss, and V must be below 2^29 (the dense path reads a chunk's
+ * key rows through 32-bit buffer offsets). */
 stce_status stce_fused_workspace_bytes(const stce_problem *prob, size_t *bytes, size_t *min_bytes);
 stce_status stce_fused_policy_step(const stce_problem *prob, const stce_pg_params *pg, float *logprob,
                                    void *state, float *loss, float *ratio, const stce_side_outputs *side,

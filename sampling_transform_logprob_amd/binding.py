@@ -19,12 +19,15 @@ LIB_PATH = os.path.join(_HERE, "libstce.so")
 
 STATUS_NONE = (1 << 63) - 1
 FIELDS = {1: "temperature", 2: "top_k", 3: "top_p", 4: "min_p", 5: "target"}
-FLAG_VALID, FLAG_FILTERED, FLAG_IN_SUPPORT, FLAG_IGNORED = 1, 2, 4, 8
+FLAG_VALID, FLAG_FILTERED, FLAG_IN_SUPPORT, FLAG_IGNORED, FLAG_LISTED = 1, 2, 4, 8, 32
 PROBLEM_IGNORE_INDEX, PROBLEM_PRE_GEMM_TEMPERATURE, PROBLEM_BF16_LANE = 1, 2, 4
 LANES = {"fp32": 0, "bf16": PROBLEM_BF16_LANE}
-STATE_BYTES_PER_ROW = 96      # a 32-byte record, then (after all T records) a 64-byte tile list
+# a 32-byte record, then (after all T records) a 64-byte tile list, then a
+# support list of NSP (token id, key) pairs
 RECORD_BYTES = 32
 NTILE = 31
+NSP = 128
+STATE_BYTES_PER_ROW = RECORD_BYTES + 2 * (1 + NTILE) + 8 * NSP
 DT_BF16, DT_F32, DT_FP8 = 1, 2, 3
 # dtypes a weight of e4m3 codes may come in (the fp8 lane)
 FP8_WEIGHT_DTYPES = (torch.uint8, torch.float8_e4m3fn)
@@ -40,7 +43,7 @@ KERNEL_KINDS = {1: "validate", 2: "projection", 3: "select", 4: "dlogits", 5: "g
                 6: "grad_hidden", 7: "transpose", 8: "partials", 9: "policy_loss", 10: "dz_keys",
                 11: "split_sum", 12: "prescale", 13: "classify", 14: "sparse_grad_weight",
                 15: "sparse_grad_hidden", 16: "reproject", 17: "quantize", 18: "tile_lists",
-                19: "tile_recompute", 20: "keys_entries"}
+                19: "tile_recompute", 20: "listed_entries"}
 PG_OBJECTIVES = {"cispo": 1, "clip": 2}
 
 
@@ -316,7 +319,7 @@ def backward(hidden, weight, target, state, grad_logprob, temperature=None, top_
     if grad_logprob.shape != (T,) or grad_logprob.dtype != torch.float32 or grad_logprob.device != dev:
         raise ValueError("grad_logprob must be fp32 [T] on the hidden's device")
     if state.numel() != T * STATE_BYTES_PER_ROW or state.dtype != torch.uint8:
-        raise ValueError("state must be the uint8 [T*32] tensor written by forward")
+        raise ValueError(f"state must be the uint8 [T*{STATE_BYTES_PER_ROW}] tensor written by forward")
     g = grad_logprob.contiguous()
     _, bwd_b = workspace_bytes(prob)
     ws = workspace if workspace is not None else torch.empty(max(bwd_b, 1), dtype=torch.uint8, device=dev)
@@ -347,7 +350,7 @@ def recompute_keys(hidden, weight, target, state, grad_logprob, temperature=None
                               weight_scale=weight_scale)
     dev = hidden.device
     if state.numel() != prob.T * STATE_BYTES_PER_ROW or state.dtype != torch.uint8:
-        raise ValueError("state must be the uint8 [T*32] tensor written by forward")
+        raise ValueError(f"state must be the uint8 [T*{STATE_BYTES_PER_ROW}] tensor written by forward")
     _, bwd_b = workspace_bytes(prob)
     ws = torch.empty(max(bwd_b, 1), dtype=torch.uint8, device=dev)
     out = torch.full((prob.T, prob.V), float("nan"), dtype=torch.float32, device=dev)
@@ -524,7 +527,8 @@ def fused_policy_step(hidden, weight, target, advantages, old_logprob, temperatu
 
 def decode_state(state: torch.Tensor) -> dict:
     """Per-row state fields as numpy arrays (copies the state to the host),
-    with ``ntile`` and ``tiles`` [T, 31] from the rows' tile lists."""
+    with ``ntile`` and ``tiles`` [T, 31] from the rows' tile lists, and
+    ``support_ids`` / ``support_keys`` [T, 128] from their support lists."""
     import numpy as np
     host = state.detach().cpu().contiguous()
     n = host.numel() // STATE_BYTES_PER_ROW
@@ -534,19 +538,26 @@ def decode_state(state: torch.Tensor) -> dict:
         ("key_thr", "<u4"), ("id_thr", "<i4"), ("n", "<i4"), ("flags", "<u4"),
         ("lse_support", "<f4"), ("lse_full", "<f4"), ("row_max", "<f4"), ("target_key", "<f4")]))
     d = {k: arr[k].copy() for k in arr.dtype.names}
-    tl = host[n * RECORD_BYTES:].numpy().view(np.uint16).reshape(n, 1 + NTILE)
+    tb = 2 * (1 + NTILE)
+    tl = host[n * RECORD_BYTES:n * (RECORD_BYTES + tb)].numpy().view(np.uint16).reshape(n, 1 + NTILE)
     d["ntile"] = tl[:, 0].astype(np.int64)
     d["tiles"] = tl[:, 1:].astype(np.int64)
+    sl = host[n * (RECORD_BYTES + tb):].numpy().view(np.int32).reshape(n, NSP, 2)
+    d["support_ids"] = sl[:, :, 0].astype(np.int64)
+    d["support_keys"] = sl[:, :, 1].copy().view(np.float32)
     return d
 
 
 def state_prefix(state: torch.Tensor, rows: int) -> torch.Tensor:
-    """The state bytes of the first ``rows`` rows (their records, then their
-    tile lists), comparable with the state of a call over those rows only."""
+    """The state bytes of the first ``rows`` rows (their records, their tile
+    lists, then their support lists), comparable with the state of a call
+    over those rows only."""
     T = state.numel() // STATE_BYTES_PER_ROW
+    tb, sb = 2 * (1 + NTILE), 8 * NSP
     rec = state[: T * RECORD_BYTES][: rows * RECORD_BYTES]
-    til = state[T * RECORD_BYTES:][: rows * (STATE_BYTES_PER_ROW - RECORD_BYTES)]
-    return torch.cat([rec, til])
+    til = state[T * RECORD_BYTES: T * (RECORD_BYTES + tb)][: rows * tb]
+    sup = state[T * (RECORD_BYTES + tb):][: rows * sb]
+    return torch.cat([rec, til, sup])
 
 
 class ScoreFunction(torch.autograd.Function):

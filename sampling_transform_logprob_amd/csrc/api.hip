@@ -87,6 +87,10 @@ bool tiles_ok(int64_t V) { return ceil_div(V, VTILE) <= 65535; }
 RowTiles* state_tiles(void* state, int64_t T, int64_t V) {
   return tiles_ok(V) ? (RowTiles*)((char*)state + sizeof(RowState) * (size_t)T) : nullptr;
 }
+// The per-row support lists follow the tile lists (present for every V).
+RowSupport* state_support(void* state, int64_t T) {
+  return (RowSupport*)((char*)state + (sizeof(RowState) + sizeof(RowTiles)) * (size_t)T);
+}
 
 // The tile recompute (sparse rows with tile lists): bf16 and fp8 operands,
 // tile lists present, and hidden rows addressable with 32-bit offsets.
@@ -314,63 +318,24 @@ FusedLayout plan_fused(const stce_problem* p, int64_t gmax = INT64_MAX) {
 }
 
 // The fused step's paths.  With row classes (bf16 operands with a filter
-// given, or the fp8 lane) the sweep keeps of each chunk what the classed
-// backward needs: its rows' upstream gradients, and the tiled rows' dz
-// entries formed from the chunk's keys; the classed backward then runs as in
-// stce_backward, without the tile recompute.  Dense (fp32 operands, or bf16
-// with no filter: every row's support is the whole vocabulary): dz of every
-// row from the chunk's keys, and the two gradient products over all rows.
+// given, or the fp8 lane) the backward forms the dz entries of rows whose
+// support the state lists from the keys the forward kept there, so the
+// step is the forward, the token loss and the classed backward in one call.
+// Dense (fp32 operands, or bf16 with no filter: every row's support is the
+// whole vocabulary): dz of every row from the chunk's keys, and the two
+// gradient products over all rows, with no recompute product.
 bool fused_classed(const stce_problem* p) {
   return p->dtype != STCE_DT_F32 && (fp8(p) || p->top_k || p->top_p || p->min_p);
 }
 
-// Workspace of the classed fused step: the rows' upstream gradients, the
-// per-row dz entry lists and counts and the per-vocabulary-row entry counts
-// (kept from the sweep to the backward), the pre-GEMM hidden, then one
-// region that holds the sweep's buffers (row flags; one or two chunks' keys,
-// tile partials and target keys; fp8: their quantized hidden rows) and,
-// once the sweep is done, the backward's (offsets from `uni`).
-struct FusedClassLayout {
-  int64_t C, ldt, ntv, nbuf;
-  size_t g, list_row, rowcnt_row, cntj, hs, uni;
-  size_t flags, tile, part, sy, h8, ha;
-  size_t buf_tile, buf_part, buf_sy, buf_h8, buf_ha;
-  Layout B;
-  size_t total;
-};
-
-FusedClassLayout plan_fused_classed(const stce_problem* p) {
-  FusedClassLayout L{};
-  const int64_t T = p->T, V = p->V, H = p->H;
-  L.C = round_up(p->chunk_rows > 0 ? p->chunk_rows : kDefaultChunk, 64);
-  if (L.C > round_up(T, 64)) L.C = round_up(T, 64);
-  L.ldt = round_up(V, 4);
-  L.ntv = ceil_div(V, VTILE);
-  L.nbuf = ceil_div(T, L.C) > 1 ? 2 : 1;
-  size_t o = 0;
-  L.g = o;          o = align_up(o + 4 * (size_t)T);
-  L.list_row = o;   o = align_up(o + sizeof(SpEntry) * (size_t)T * NSP);
-  L.rowcnt_row = o; o = align_up(o + 4 * (size_t)T);
-  L.cntj = o;       o = align_up(o + 4 * (size_t)V);
-  L.hs = o;         o = align_up(o + hs_bytes(p));
-  L.uni = o;
-  size_t u = 0;
-  L.buf_tile = align_up(4 * (size_t)L.C * L.ldt);
-  L.buf_part = align_up(sizeof(TilePart) * (size_t)L.C * L.ntv);
-  L.buf_sy = align_up(4 * (size_t)L.C);
-  L.flags = u;  u = align_up(u + 4 * (size_t)T);
-  L.tile = u;   u += L.nbuf * L.buf_tile;
-  L.part = u;   u += L.nbuf * L.buf_part;
-  L.sy = u;     u += L.nbuf * L.buf_sy;
-  if (fp8(p)) {
-    L.buf_h8 = align_up((size_t)L.C * H);
-    L.buf_ha = align_up(4 * (size_t)L.C);
-    L.h8 = u;   u += L.nbuf * L.buf_h8;
-    L.ha = u;   u += L.nbuf * L.buf_ha;
-  }
-  L.B = plan(p);
-  L.total = L.uni + (u > L.B.bwd ? u : L.B.bwd);
-  return L;
+// Workspace of the classed fused step: the rows' upstream gradients, then
+// one region that holds stce_forward's workspace and, once the forward is
+// done, stce_backward's.
+size_t fused_classed_bytes(const stce_problem* p, size_t* region) {
+  const Layout L = plan(p);
+  const size_t off = align_up(4 * (size_t)p->T);
+  if (region) *region = off;
+  return off + (L.fwd > L.bwd ? L.fwd : L.bwd);
 }
 
 stce_status check_inputs(const stce_problem* p) {
@@ -598,6 +563,7 @@ stce_status forward_impl(const stce_problem* p, float* logprob, void* state, con
     sp.logprob = logprob + c0;
     sp.state = (RowState*)state + c0;
     sp.tiles = tiles_ok(p->V) ? state_tiles(state, p->T, p->V) + c0 : nullptr;
+    sp.support = state_support(state, p->T) + c0;
     sp.V = (int)p->V;
     sp.lse_full = so_lse ? so_lse + c0 : nullptr;
     sp.ent_full = so_hf ? so_hf + c0 : nullptr;
@@ -726,28 +692,20 @@ stce_status stce_forward_noalloc(const stce_problem* p, float* logprob, void* st
 namespace {
 
 // The bf16 (and fp8 lane) backward with row classes: classification of the
-// rows (dense, sparse, empty) and their permutation, the hidden rows gathered
-// into that order (fp8: quantized into it, and dequantized for the weight
-// gradient), per vocabulary slice the recompute product and the dense rows'
-// two products, then the sparse rows' products over their dz entries.
-// The tiled rows' dz entries formed before the backward (the fused step,
-// from its chunks' keys): per-row lists and counts, and the per-vocabulary-
-// row counts that already include them.
-struct PreEntries {
-  const SpEntry* list_row;
-  const int* rowcnt_row;
-  int* cntj;
-};
-
+// rows (dense, sparse, listed, tiled, empty) and their permutation, the
+// hidden rows gathered into that order (fp8: quantized into it, and
+// dequantized for the weight gradient), the listed rows' dz entries from the
+// state's support lists, per vocabulary slice the recompute product and the
+// dense rows' two products, the tiled rows' recompute on their tiles, then
+// the sparse products over every row's dz entries.
 stce_status backward_classed(const stce_problem* p, const Layout& L, const float* grad_logprob, const void* state,
                              const void* hid, float dh_div, void* grad_hidden, float* grad_weight,
-                             int32_t accumulate_grad_weight, void* ws, hipStream_t st, float* keys_out,
-                             const PreEntries* pre = nullptr) {
+                             int32_t accumulate_grad_weight, void* ws, hipStream_t st, float* keys_out) {
   hipError_t e;
   GradCounts* cnt = at<GradCounts>(ws, L.b_cnt);
   int* perm = at<int>(ws, L.b_perm);
   int* rowcnt = at<int>(ws, L.b_rowcnt);
-  int* cntj = pre ? pre->cntj : at<int>(ws, L.b_cntj);
+  int* cntj = at<int>(ws, L.b_cntj);
   bf16* h_perm = at<bf16>(ws, L.b_hperm);
   SpEntry* list = at<SpEntry>(ws, L.b_list);
   const bool want_w = grad_weight && !keys_out;
@@ -755,8 +713,6 @@ stce_status backward_classed(const stce_problem* p, const Layout& L, const float
   if ((e = launch_grad_classes((const RowState*)state, tl, grad_logprob, p->T, at<int>(ws, L.b_blk), cnt, perm,
                                rowcnt, st)))
     return hip_fail(e, "row classes");
-  if (pre && tl && (e = launch_place_entries(perm, cnt, pre->rowcnt_row, pre->list_row, rowcnt, list, p->T, st)))
-    return hip_fail(e, "place the tiled rows' entries");
   uint8_t* h8_perm = fp8(p) ? at<uint8_t>(ws, L.b_h8) : nullptr;
   float* ha = fp8(p) ? at<float>(ws, L.b_ha) : nullptr;
   if (fp8(p))  // the hidden rows quantized in permuted order, and dequantized
@@ -764,7 +720,12 @@ stce_status backward_classed(const stce_problem* p, const Layout& L, const float
   else
     e = launch_gather_rows(1, hid, perm, p->T, p->H, h_perm, st);
   if (e) return hip_fail(e, "gather hidden rows");
-  if (want_w && !pre && (e = launch_fill_i32(cntj, p->V, 0, st))) return hip_fail(e, "clear counts");
+  if (want_w && (e = launch_fill_i32(cntj, p->V, 0, st))) return hip_fail(e, "clear counts");
+  // the listed rows' entries from the support lists (no recompute)
+  if (!keys_out && (e = launch_listed_entries(perm, cnt, (const RowState*)state, state_support((void*)state, p->T),
+                                              grad_logprob, p->temperature, p->target, p->V, rowcnt, list,
+                                              want_w ? cntj : nullptr, p->T, st)))
+    return hip_fail(e, "listed rows' entries");
   const int64_t nsl = ceil_div(p->V, L.Vs);
   for (int64_t si = 0; si < nsl; ++si) {
     ClassSliceArgs a{};
@@ -808,7 +769,7 @@ stce_status backward_classed(const stce_problem* p, const Layout& L, const float
     a.ld_keys = p->V;
     if ((e = launch_class_slice(a, st))) return hip_fail(e, "backward slice");
   }
-  if (tl && !pre) {  // the tiled rows' keys on their tiles
+  if (tl) {  // the tiled rows' keys on their tiles
     TiledArgs ta{};
     if (fp8(p)) {
       ta.W8 = (const uint8_t*)p->weight;
@@ -1026,6 +987,7 @@ stce_status fused_sweep(const stce_problem* p, const SweepBufs& B, const void* h
     sp.logprob = logprob + c0;
     sp.state = (RowState*)state + c0;
     sp.tiles = tiles_ok(p->V) ? state_tiles(state, p->T, p->V) + c0 : nullptr;
+    sp.support = state_support(state, p->T) + c0;
     sp.V = (int)p->V;
     sp.lse_full = so_lse ? so_lse + c0 : nullptr;
     sp.ent_full = so_hf ? so_hf + c0 : nullptr;
@@ -1154,6 +1116,7 @@ stce_status stce_support_from_logits(const float* sk, int64_t R, int64_t V, cons
   sp.logprob = logprob;
   sp.state = (RowState*)state;
   sp.tiles = state_tiles(state, R, V);
+  sp.support = state_support(state, R);
   sp.V = (int)V;
   launch_select(sp, (int)R, st);
   if ((e = hipGetLastError())) return hip_fail(e, "select");
@@ -1172,7 +1135,7 @@ stce_status stce_fused_workspace_bytes(const stce_problem* p, size_t* bytes, siz
   if (s) return s;
   if (!bytes) return fail(STCE_E_ARG, "bytes is NULL");
   if (fused_classed(p)) {
-    *bytes = plan_fused_classed(p).total;
+    *bytes = fused_classed_bytes(p, nullptr);
     if (min_bytes) *min_bytes = *bytes;
     return STCE_OK;
   }
@@ -1220,59 +1183,17 @@ stce_status stce_fused_policy_step(const stce_problem* p, const stce_pg_params* 
   };
 
   if (fused_classed(p)) {
-    const FusedClassLayout L = plan_fused_classed(p);
-    if ((s = check_ws(ws, ws_bytes, L.total))) return s;
-    char* uni = at<char>(ws, L.uni);
-    SweepBufs B{};
-    B.C = L.C;
-    B.ldt = L.ldt;
-    B.ntv = L.ntv;
-    B.nbuf = L.nbuf;
-    B.flags = (uint32_t*)(uni + L.flags);
-    B.tile = uni + L.tile;
-    B.part = uni + L.part;
-    B.sy = uni + L.sy;
-    B.h8 = uni + L.h8;
-    B.ha = uni + L.ha;
-    B.buf_tile = L.buf_tile;
-    B.buf_part = L.buf_part;
-    B.buf_sy = L.buf_sy;
-    B.buf_h8 = L.buf_h8;
-    B.buf_ha = L.buf_ha;
-    if ((s = validate(B.flags))) return s;
-    const void* hid = nullptr;
-    float dh_div = 1.0f;
-    if ((e = hidden_for_products(p, ws, L.hs, 0, p->T, &hid, &dh_div, st))) return hip_fail(e, "prescale hidden");
-    const bool want_grad = grad_hidden || grad_weight;
-    float* g = at<float>(ws, L.g);
-    int* cntj = at<int>(ws, L.cntj);
-    const RowTiles* tl = tiled(p) ? state_tiles(state, p->T, p->V) : nullptr;
-    if (want_grad && grad_weight && (e = launch_fill_i32(cntj, p->V, 0, st))) return hip_fail(e, "clear counts");
-    s = fused_sweep(p, B, hid, logprob, state, side_out, st,
-                    [&](int64_t, int64_t c0, int64_t nc, const float* keys) -> stce_status {
-                      stce_status s2 = chunk_loss(c0, nc, g + c0);
-                      if (s2 || !want_grad || !tl) return s2;
-                      KeysEntriesArgs ka{};
-                      ka.keys = keys;
-                      ka.ld = L.ldt;
-                      ka.rows = nc;
-                      ka.c0 = c0;
-                      ka.V = p->V;
-                      ka.st = (const RowState*)state;
-                      ka.tiles = tl;
-                      ka.g = g;
-                      ka.temp = p->temperature;
-                      ka.target = p->target;
-                      ka.list_row = at<SpEntry>(ws, L.list_row);
-                      ka.rowcnt_row = at<int>(ws, L.rowcnt_row);
-                      ka.cntj = grad_weight ? cntj : nullptr;
-                      hipError_t e2 = launch_keys_entries(ka, st);
-                      return e2 ? hip_fail(e2, "dz entries from the keys") : STCE_OK;
-                    });
-    if (s || !want_grad) return s;
-    const PreEntries pre{at<SpEntry>(ws, L.list_row), at<int>(ws, L.rowcnt_row), cntj};
-    return backward_classed(p, L.B, g, state, hid, dh_div, grad_hidden, grad_weight, accumulate_grad_weight, uni,
-                            st, nullptr, &pre);
+    size_t off = 0;
+    const size_t need = fused_classed_bytes(p, &off);
+    if ((s = check_ws(ws, ws_bytes, need))) return s;
+    float* g = at<float>(ws, 0);
+    void* region = at<char>(ws, off);
+    const size_t rb = ws_bytes - off;
+    if ((s = forward_impl(p, logprob, state, side_out, dev_status, region, rb, stream, false))) return s;
+    if ((s = chunk_loss(0, p->T, g))) return s;
+    if (!grad_hidden && !grad_weight) return STCE_OK;
+    return backward_impl(p, g, state, grad_hidden, grad_weight, accumulate_grad_weight, nullptr, region, rb, stream,
+                         nullptr);
   }
 
   // a workspace below the default keeps fewer chunks per weight-gradient

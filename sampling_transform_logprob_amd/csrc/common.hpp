@@ -24,7 +24,10 @@ enum : uint32_t {
   ROW_IGNORED = 8u,    // inactive row (target equals the problem's ignore_index)
   // forward flag only (never in the state): a row bounded by top-k whose
   // projection keeps candidates instead of its fp32 keys (KCAND)
-  ROW_CAND = 16u
+  ROW_CAND = 16u,
+  // state flag: the row's support is stored in the state with its keys
+  // (RowState's support list, below)
+  ROW_LISTED = 32u
 };
 
 // Top-k-bounded rows with 0 < k <= KCAND (and at least k vocabulary tiles, at
@@ -35,7 +38,8 @@ enum : uint32_t {
 constexpr int KCAND = 256;
 
 // Per-row record of the state written by the forward, read by the backward
-// (32 bytes; the tile lists follow the T records).
+// (32 bytes; the tile lists and then the support lists follow the T
+// records).
 // Field order is the one of stce_row_info in stce.h.
 struct RowState {
   uint32_t key_thr;  // key of the last support token (0 on unfiltered rows)
@@ -61,8 +65,6 @@ struct RowTiles {
   uint16_t t[NTILE];
 };
 static_assert(sizeof(RowTiles) == 64, "tile list must be 64 bytes");
-// bytes of state per row: the record and the tile list
-constexpr int STATE_BYTES_PER_ROW = (int)(sizeof(RowState) + sizeof(RowTiles));
 
 // Partial statistics of one (row, 256-wide vocabulary tile) block, written by
 // the projection epilogue: tile maximum, sum of exp(s - tile max), tile
@@ -81,20 +83,22 @@ constexpr int VTILE = 256;  // vocabulary columns per partial
 // row's support, so a row whose support holds at most NSP tokens ("sparse")
 // has at most NSP nonzero dz entries: the recompute emits them as
 // (vocabulary row, value) entries and the two gradient products take them
-// one by one.  A sparse row with a tile list ("tiled") has its keys
-// recomputed on those tiles only.  Rows with a larger support ("dense") go
+// one by one.  A sparse row whose support the state lists ("listed") takes
+// its entries from the stored keys; one with a tile list ("tiled") has its
+// keys recomputed on those tiles only.  Rows with a larger support ("dense") go
 // through the matrix-core products; rows with no gradient (target out of
 // support, invalid or ignored metadata, zero upstream gradient) are "empty".
 constexpr int NSP = 128;
-enum : int { GRAD_DENSE = 0, GRAD_SPARSE = 1, GRAD_TILED = 2, GRAD_EMPTY = 3, GRAD_CLASSES = 4 };
+enum : int { GRAD_DENSE = 0, GRAD_SPARSE = 1, GRAD_LISTED = 2, GRAD_TILED = 3, GRAD_EMPTY = 4, GRAD_CLASSES = 5 };
 
 // Row counts of the classes, written on the device by the classification:
-// rows are placed in the order dense, sparse, tiled, empty, each in row
-// order, so dense rows take permuted positions [0, dense), sparse ones
-// [dense, full) and tiled ones [full, active).  The whole-vocabulary
-// recompute covers [0, full), the tile recompute [full, active).
+// rows are placed in the order dense, sparse, listed, tiled, empty, each in
+// row order, so dense rows take permuted positions [0, dense), sparse ones
+// [dense, full), listed ones [full, listed) and tiled ones [listed, active).
+// The whole-vocabulary recompute covers [0, full), the tile recompute
+// [listed, active); listed rows need no recompute.
 struct GradCounts {
-  int dense, full, active, pad;
+  int dense, full, listed, active;
 };
 
 // One nonzero dz entry: a vocabulary row (or, in a weight-gradient bucket,
@@ -103,6 +107,20 @@ struct SpEntry {
   int32_t idx;
   float v;
 };
+
+// A filtered row's support of at most NSP tokens as (token id, key) pairs, in
+// decreasing key order (increasing id among equal keys), when the selection
+// holds all of it at its decision (no token ahead of its window, as for a
+// top-k row decided from its candidates); the row is then flagged ROW_LISTED
+// and the backward forms its dz entries from these keys, recomputing none.
+// Entries past the support, and every entry of other rows, are zero.  The
+// state holds T RowState records, then T RowTiles, then T support lists.
+struct RowSupport {
+  SpEntry e[NSP];
+};
+static_assert(sizeof(RowSupport) == 1024, "support list must be 1 KB");
+// bytes of state per row: the record, the tile list and the support list
+constexpr int STATE_BYTES_PER_ROW = (int)(sizeof(RowState) + sizeof(RowTiles) + sizeof(RowSupport));
 
 // Order-preserving map of an fp32 key to uint32: a larger float gives a
 // larger unsigned integer; -0 and +0 map to the same value.

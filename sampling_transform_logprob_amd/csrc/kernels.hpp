@@ -12,7 +12,7 @@ enum : int {
   KIND_GRAD_HIDDEN = 6, KIND_TRANSPOSE = 7, KIND_PARTIALS = 8, KIND_POLICY_LOSS = 9, KIND_DZ_KEYS = 10,
   KIND_SPLIT_SUM = 11, KIND_PRESCALE = 12, KIND_CLASSIFY = 13, KIND_SPARSE_DW = 14, KIND_SPARSE_DH = 15,
   KIND_REPROJECT = 16, KIND_QUANTIZE = 17, KIND_TILE_LISTS = 18, KIND_TILE_RECOMPUTE = 19,
-  KIND_KEYS_ENTRIES = 20
+  KIND_LISTED_ENTRIES = 20
 };
 
 // Launch-timing hook (no-op unless a profile is attached to this thread).
@@ -136,13 +136,20 @@ hipError_t launch_bwd_slice(const BwdSliceArgs& a, hipStream_t s);
 
 // ---- the backward with row classes (bf16 operands; sparse.hip) ----------
 // Classification: counts of the classes into *cnt, the permutation perm
-// (permuted position -> row: dense rows, then sparse, tiled and empty ones,
-// each in row order) and a cleared entry counter per position.  tl: the
-// rows' tile lists (null: no row is tiled).  blk: scratch of
+// (permuted position -> row: dense rows, then sparse, listed, tiled and
+// empty ones, each in row order) and a cleared entry counter per position.
+// tl: the rows' tile lists (null: no row is tiled).  blk: scratch of
 // grad_class_blk_ints(T) ints.
 size_t grad_class_blk_ints(int64_t T);
 hipError_t launch_grad_classes(const RowState* st, const RowTiles* tl, const float* g, int64_t T, int* blk,
                                GradCounts* cnt, int* perm, int* rowcnt, hipStream_t s);
+
+// The listed rows' dz entries (positions [full, listed)) from the support
+// lists of the state, into list / rowcnt by position and, when cntj is not
+// null, the per-vocabulary-row counts.  g [T]: upstream gradients by row.
+hipError_t launch_listed_entries(const int* perm, const GradCounts* cnt, const RowState* st, const RowSupport* sup,
+                                 const float* g, const float* temp, const int64_t* target, int64_t V, int* rowcnt,
+                                 SpEntry* list, int* cntj, int64_t T, hipStream_t s);
 
 // Work lists of the tile recompute: per vocabulary tile j < ntv, the tiled
 // positions listing it (bucket[toff[j] .. toff[j] + tcnt[j])) and its work
@@ -261,29 +268,6 @@ struct SparseGradArgs {
   float dh_div;
 };
 hipError_t launch_sparse_grads(const SparseGradArgs& a, hipStream_t s);
-
-// The fused step's tiled rows of one chunk: their dz entries from the
-// chunk's stored keys [rows][ld] (rows c0 .. c0 + rows of the batch) on their
-// listed tiles, into per-row lists list_row [T][NSP] and counts rowcnt_row
-// [T] (only tiled rows are written), counting entries per vocabulary row
-// into cntj [V] when it is not null.  g [T]: the rows' upstream gradients.
-struct KeysEntriesArgs {
-  const float* keys;
-  int64_t ld, rows, c0, V;
-  const RowState* st;     // [T]
-  const RowTiles* tiles;  // [T]
-  const float* g;         // [T]
-  const float* temp;      // [T] or null
-  const int64_t* target;  // [T]
-  SpEntry* list_row;
-  int* rowcnt_row;
-  int* cntj;
-};
-hipError_t launch_keys_entries(const KeysEntriesArgs& a, hipStream_t s);
-// Their lists in permuted-position order once the rows are classified:
-// positions [full, active) take rowcnt_row and list_row of row perm[n].
-hipError_t launch_place_entries(const int* perm, const GradCounts* cnt, const int* rowcnt_row,
-                                const SpEntry* list_row, int* rowcnt, SpEntry* list, int64_t T, hipStream_t s);
 
 // Gradients of one chunk of the fused policy step, from the chunk's stored
 // keys (no recompute product): dz token-major and vocab-major, the chunk's

@@ -131,6 +131,13 @@ struct Shared {
 // a selection workgroup fits beside a projection workgroup only within 32 KB.
 static_assert(sizeof(Shared) <= 32 * 1024, "selection LDS must fit beside a projection workgroup");
 
+// A row with no support list: all of its entries zero, so that the state's
+// bytes are a function of the inputs.
+__device__ inline void clear_support(const SelParams& P, int orow) {
+  if (!P.support) return;
+  for (int i = threadIdx.x; i < NSP; i += ST) P.support[orow].e[i] = SpEntry{0, 0.0f};
+}
+
 // At most 96 VGPRs (5 waves per SIMD): one of these waves fits beside the
 // two projection waves of a SIMD.
 __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
@@ -143,6 +150,7 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
   const int V = P.V;
   const uint32_t fl = P.flags[orow];
   if (!(fl & ROW_VALID)) {
+    clear_support(P, orow);
     if (tid == 0) {
       const float nan = __builtin_nanf("");
       P.logprob[orow] = nan;
@@ -201,6 +209,7 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
   rs.s_y = sy;
 
   if (!(fl & ROW_FILTERED)) {  // identity program: the support is the whole row
+    clear_support(P, orow);
     if (tid == 0) {
       rs.key_thr = 0u;
       rs.id_thr = V - 1;
@@ -705,6 +714,21 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
     if (tid >= keep && tid < NTILE) rt->t[tid] = 0;
     if (tid == 0) rt->n = (uint16_t)keep;
   }
+  // The support with its keys, when the window holds all of it (no token
+  // ahead of it) and it has at most NSP tokens: the window's first n_loc
+  // tokens, already in decreasing (key, -id) order.
+  const bool listed = P.support && above == 0 && n_loc <= NSP;
+  if (P.support) {
+    SpEntry* sl = P.support[orow].e;
+    for (int i = tid; i < NSP; i += ST) {
+      SpEntry e{0, 0.0f};
+      if (listed && i < n_loc) {
+        const uint64_t c = S.u.cand[i];
+        e = SpEntry{(int32_t)comp_id(c), key_value(comp_key(c))};
+      }
+      sl[i] = e;
+    }
+  }
   if (tid == 0) {
     const uint64_t bc = S.u.cand[n_loc - 1];
     rs.key_thr = comp_key(bc);
@@ -715,7 +739,8 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
     const uint32_t ky = order_key(sy);
     const bool ign = (fl & ROW_IGNORED) != 0;
     const bool in = !ign && (ky > rs.key_thr || (ky == rs.key_thr && y <= (int64_t)rs.id_thr));
-    rs.flags = ROW_VALID | ROW_FILTERED | (in ? ROW_IN_SUPPORT : 0u) | (ign ? ROW_IGNORED : 0u);
+    rs.flags = ROW_VALID | ROW_FILTERED | (in ? ROW_IN_SUPPORT : 0u) | (ign ? ROW_IGNORED : 0u) |
+               (listed ? ROW_LISTED : 0u);
     P.logprob[orow] = lane_logprob(P, ign ? 0.0f : (in ? (float)fmin((double)sy - lse_s, 0.0) : -F_INF));
     P.state[orow] = rs;
   }

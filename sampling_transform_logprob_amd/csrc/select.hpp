@@ -53,6 +53,7 @@ struct SelParams {
   float* logprob;           // [R]
   RowState* state;          // [R]
   RowTiles* tiles;          // [R] or null (more than 65,535 vocabulary tiles)
+  RowSupport* support;      // [R] support lists (every row's written), or null
   int V;
   // side outputs, each [R] or null; the entropies need the partials' sums
   float* lse_full;          // log-sum-exp of the keys over the row

@@ -40,6 +40,7 @@ constexpr int CB = 1024;  // rows per classification block (256 threads x 4)
 __device__ inline int grad_class(const RowState& rs, float g, int ntile) {
   if ((rs.flags & (ROW_VALID | ROW_IN_SUPPORT)) != (ROW_VALID | ROW_IN_SUPPORT) || g == 0.f) return GRAD_EMPTY;
   if (!(rs.flags & ROW_FILTERED) || rs.n > NSP) return GRAD_DENSE;
+  if (rs.flags & ROW_LISTED) return GRAD_LISTED;
   return ntile > 0 ? GRAD_TILED : GRAD_SPARSE;
 }
 
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(256) void class_count_kernel(const RowState* st, co
                                                           int64_t T, int* blk) {
   __shared__ int scr[4];
   const int64_t r0 = (int64_t)blockIdx.x * CB + threadIdx.x * 4;
-  int c[GRAD_CLASSES] = {0, 0, 0, 0};
+  int c[GRAD_CLASSES] = {};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     if (r0 + i < T) ++c[grad_class(st[r0 + i], g[r0 + i], tl ? tl[r0 + i].n : 0)];
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(1024) void class_scan_kernel(int* blk, int nblk, Gr
   const int t = threadIdx.x;
   // thread t scans blocks [t * per, (t + 1) * per)
   const int per = (nblk + 1023) / 1024;
-  int s[NC] = {0, 0, 0, 0};
+  int s[NC] = {};
   for (int b = t * per; b < min(nblk, (t + 1) * per); ++b)
 #pragma unroll
     for (int k = 0; k < NC; ++k) s[k] += blk[b * NC + k];
@@ -116,28 +117,29 @@ __global__ __launch_bounds__(1024) void class_scan_kernel(int* blk, int nblk, Gr
     GradCounts c;
     c.dense = tot[GRAD_DENSE];
     c.full = c.dense + tot[GRAD_SPARSE];
-    c.active = c.full + tot[GRAD_TILED];
-    c.pad = 0;
+    c.listed = c.full + tot[GRAD_LISTED];
+    c.active = c.listed + tot[GRAD_TILED];
     *cnt = c;
   }
 }
 
-// Places every row at its permuted position (dense, then sparse, then empty;
-// row order within a class) and clears the position's entry counter.
+// Places every row at its permuted position (dense, sparse, listed, tiled,
+// then empty; row order within a class) and clears the position's entry
+// counter.
 __global__ __launch_bounds__(256) void class_place_kernel(const RowState* st, const RowTiles* tl, const float* g,
                                                           int64_t T, const int* blk, const GradCounts* cnt, int* perm,
                                                           int* rowcnt) {
   __shared__ int scr[4];
   const int64_t r0 = (int64_t)blockIdx.x * CB + threadIdx.x * 4;
   int cls[4];
-  int c[GRAD_CLASSES] = {0, 0, 0, 0};
+  int c[GRAD_CLASSES] = {};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     cls[i] = r0 + i < T ? grad_class(st[r0 + i], g[r0 + i], tl ? tl[r0 + i].n : 0) : -1;
     if (cls[i] >= 0) ++c[cls[i]];
   }
   const GradCounts n = *cnt;
-  const int cls_base[GRAD_CLASSES] = {0, n.dense, n.full, n.active};
+  const int cls_base[GRAD_CLASSES] = {0, n.dense, n.full, n.listed, n.active};
   int pos[GRAD_CLASSES];
 #pragma unroll
   for (int k = 0; k < GRAD_CLASSES; ++k)
@@ -151,75 +153,45 @@ __global__ __launch_bounds__(256) void class_place_kernel(const RowState* st, co
     }
 }
 
-// The fused step's tiled rows: their dz entries formed from the chunk's
-// stored keys (the forward's, which the recompute would reproduce bit for
-// bit) on their listed tiles, with the recompute epilogue's arithmetic, into
-// per-row lists (list_row[t], rowcnt_row[t]: indexed by row, the positions
-// being known only once every chunk is classified), counting the entries of
-// every vocabulary row into cntj (when not null).  One wave per row of the
-// chunk; a tile is 256 keys, four a lane.  The class rule is grad_class's,
-// so exactly the rows the classification will call tiled are listed.
-__global__ __launch_bounds__(256) void keys_entries_kernel(const float* keys, int64_t ld, int64_t rows, int64_t c0,
-                                                           const RowState* st, const RowTiles* tl, const float* g,
-                                                           const float* temp, const int64_t* target, int V,
-                                                           int ntv, SpEntry* list_row, int* rowcnt_row,
-                                                           int* cntj) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (r >= rows) return;
-  const int64_t t = c0 + r;
-  const RowState rs = st[t];
-  const float gt = g[t];
-  const int nlist = tl[t].n;
-  if (grad_class(rs, gt, nlist) != GRAD_TILED) return;
-  const float c = gt / (temp ? temp[t] : 1.0f);
-  const float thr = key_value(rs.key_thr), nl = -rs.lse_s * LOG2E;
-  const int idt = rs.id_thr, y = (int)target[t];
-  const float* kr = keys + r * ld;
-  SpEntry* out = list_row + t * NSP;
-  int cnt = 0;
-  for (int i = 0; i < min(nlist, NTILE); ++i) {
-    const int tile = tl[t].t[i];
-    if (tile >= ntv) continue;
-    const int v = tile * VTILE + lane * 4;
-    // (a row holds ld >= V keys, ld a multiple of 4: the group of four is in
-    // the row; keys at or past V are masked)
-    const f32x4 x = v < V ? *(const f32x4*)(kr + v) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int vg = v + e;
-      const float sv = x[e];
-      const bool in = ((sv > thr) | ((sv == thr) & (vg <= idt))) && vg < V;
-      const float q = in ? __builtin_amdgcn_exp2f(__builtin_fmaf(sv, LOG2E, nl)) : 0.f;
-      const float dv = c * ((vg == y ? 1.f : 0.f) - q);
-      const uint64_t b = __ballot(in);  // (every lane of the wave is active)
-      const int slot = cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0));
-      if (in && slot < NSP) {
-        // rounded to bf16 like every dz entry
-        out[slot] = SpEntry{vg, (float)(bf16)dv};
-        if (cntj) atomicAdd(cntj + vg, 1);
-      }
-      cnt += __builtin_popcountll(b);
-    }
-  }
-  if (lane == 0) rowcnt_row[t] = cnt;
-}
-
-// The tiled positions' entry lists, copied from the per-row lists into
-// permuted-position order: rowcnt[n] = rowcnt_row[perm[n]] and its entries,
-// for n in [full, active).  One wave per position.
-__global__ __launch_bounds__(256) void place_entries_kernel(const int* perm, const GradCounts* cnt,
-                                                            const int* rowcnt_row, const SpEntry* list_row,
-                                                            int* rowcnt, SpEntry* list, int64_t T) {
+// The listed rows' dz entries from the support the forward stored with its
+// keys (no key is recomputed): position n in [full, listed), row t =
+// perm[n], one entry per support token j with the recompute epilogue's
+// arithmetic, bf16(c (1[j == y] - exp2(s_j log2 e - lse_S log2 e))),
+// c = g / T; the per-vocabulary-row counts into cntj when it is not null.
+// (A list entry naming no token of [0, V) is skipped, so that no state can
+// index past the vocabulary.)  One wave per position, a lane per support
+// token (n <= NSP).
+__global__ __launch_bounds__(256) void listed_entries_kernel(const int* perm, const GradCounts* cnt,
+                                                             const RowState* st, const RowSupport* sup,
+                                                             const float* g, const float* temp,
+                                                             const int64_t* target, int V, int* rowcnt,
+                                                             SpEntry* list, int* cntj, int64_t T) {
   const int lane = threadIdx.x & 63;
   const GradCounts c = *cnt;
   const int64_t nw = (int64_t)gridDim.x * 4;
   for (int64_t n = c.full + (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-       n < c.active && n < T; n += nw) {
+       n < c.listed && n < T; n += nw) {
     const int64_t t = perm[n];
-    const int k = rowcnt_row[t];
+    const RowState rs = st[t];
+    const int ns = min(rs.n, NSP);
+    const float cf = g[t] / (temp ? temp[t] : 1.0f), nl = -rs.lse_s * LOG2E;
+    const int y = (int)target[t];
+    int k = 0;
+    for (int i0 = 0; i0 < ns; i0 += 64) {  // (uniform: every lane runs each pass)
+      const int i = i0 + lane;
+      const SpEntry e = i < ns ? sup[t].e[i] : SpEntry{-1, 0.0f};
+      const bool in = (uint32_t)e.idx < (uint32_t)V;
+      const uint64_t b = __ballot(in);
+      const int slot = k + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0));
+      if (in) {
+        const float q = __builtin_amdgcn_exp2f(__builtin_fmaf(e.v, LOG2E, nl));
+        const float dv = cf * ((e.idx == y ? 1.f : 0.f) - q);
+        list[n * NSP + slot] = SpEntry{e.idx, (float)(bf16)dv};
+        if (cntj) atomicAdd(cntj + e.idx, 1);
+      }
+      k += __builtin_popcountll(b);
+    }
     if (lane == 0) rowcnt[n] = k;
-    for (int i = lane; i < min(k, NSP); i += 64) list[n * NSP + i] = list_row[t * NSP + i];
   }
 }
 
@@ -696,7 +668,7 @@ __global__ __launch_bounds__(256) void tile_count_kernel(const int* perm, const 
   if (lds)
     for (int j = threadIdx.x; j < ntv; j += 256) hist[j] = 0;
   __syncthreads();
-  const int64_t n0 = c.full + (int64_t)blockIdx.x * TROWS;
+  const int64_t n0 = c.listed + (int64_t)blockIdx.x * TROWS;
   for (int64_t n = n0 + threadIdx.x; n < n0 + TROWS && n < c.active && n < T; n += 256) {
     const RowTiles& r = tl[perm[n]];
     const int nt = min((int)r.n, NTILE);
@@ -717,7 +689,7 @@ __global__ __launch_bounds__(256) void tile_fill_kernel(const int* perm, const G
   __shared__ int hist[TH_LDS];
   const GradCounts c = *cnt;
   const bool lds = ntv <= TH_LDS;
-  const int64_t n0 = c.full + (int64_t)blockIdx.x * TROWS;
+  const int64_t n0 = c.listed + (int64_t)blockIdx.x * TROWS;
   if (lds) {
     for (int j = threadIdx.x; j < ntv; j += 256) hist[j] = 0;
     __syncthreads();
@@ -808,21 +780,13 @@ hipError_t launch_exclusive_scan(const int* x, int64_t n, int* sums, int* y, hip
   return hipGetLastError();
 }
 
-hipError_t launch_keys_entries(const KeysEntriesArgs& a, hipStream_t s) {
-  if (a.rows <= 0) return hipSuccess;
-  ProfScope ps(KIND_KEYS_ENTRIES, s);
-  hipLaunchKernelGGL(keys_entries_kernel, dim3((unsigned)ceil_div(a.rows, 4)), dim3(256), 0, s, a.keys, a.ld, a.rows,
-                     a.c0, a.st, a.tiles, a.g, a.temp, a.target, (int)a.V, (int)ceil_div(a.V, VTILE), a.list_row,
-                     a.rowcnt_row, a.cntj);
-  return hipGetLastError();
-}
-
-hipError_t launch_place_entries(const int* perm, const GradCounts* cnt, const int* rowcnt_row,
-                                const SpEntry* list_row, int* rowcnt, SpEntry* list, int64_t T, hipStream_t s) {
-  ProfScope ps(KIND_KEYS_ENTRIES, s);
+hipError_t launch_listed_entries(const int* perm, const GradCounts* cnt, const RowState* st, const RowSupport* sup,
+                                 const float* g, const float* temp, const int64_t* target, int64_t V, int* rowcnt,
+                                 SpEntry* list, int* cntj, int64_t T, hipStream_t s) {
+  ProfScope ps(KIND_LISTED_ENTRIES, s);
   const unsigned blocks = (unsigned)(ceil_div(T, 4) < 8192 ? ceil_div(T, 4) : 8192);
-  hipLaunchKernelGGL(place_entries_kernel, dim3(blocks), dim3(256), 0, s, perm, cnt, rowcnt_row, list_row, rowcnt,
-                     list, T);
+  hipLaunchKernelGGL(listed_entries_kernel, dim3(blocks), dim3(256), 0, s, perm, cnt, st, sup, g, temp, target,
+                     (int)V, rowcnt, list, cntj, T);
   return hipGetLastError();
 }
 

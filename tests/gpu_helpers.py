@@ -93,15 +93,67 @@ def check_logprob(lp_gpu, ref):
 NSP = 128
 
 
-def tiled_rows(info, g, V, dtype):
-    """Rows whose keys the backward recomputes on their listed tiles only (the
-    library's class rule): valid, target in support, filtered, at most NSP
-    support tokens, nonzero upstream gradient, a tile list, bf16 or fp8
-    operands."""
+def _sparse_rows(info, g):
     fl = info["flags"]
     ok = ((fl & binding.FLAG_VALID) != 0) & ((fl & binding.FLAG_IN_SUPPORT) != 0) & (np.asarray(g) != 0)
-    sparse = ok & ((fl & binding.FLAG_FILTERED) != 0) & (info["n"] <= NSP)
-    return sparse & (info["ntile"] > 0) & (dtype != "f32") & (-(-V // 256) <= 65535)
+    return ok & ((fl & binding.FLAG_FILTERED) != 0) & (info["n"] <= NSP)
+
+
+def listed_rows(info, g, dtype):
+    """Rows whose dz the backward forms from the support the state lists (the
+    library's class rule): valid, target in support, filtered, at most NSP
+    support tokens, nonzero upstream gradient, the listed flag, bf16 or fp8
+    operands."""
+    return _sparse_rows(info, g) & ((info["flags"] & binding.FLAG_LISTED) != 0) & (dtype != "f32")
+
+
+def tiled_rows(info, g, V, dtype):
+    """Rows whose keys the backward recomputes on their listed tiles only (the
+    library's class rule): as listed_rows but with no support list, and a
+    tile list."""
+    return (_sparse_rows(info, g) & ((info["flags"] & binding.FLAG_LISTED) == 0) & (info["ntile"] > 0)
+            & (dtype != "f32") & (-(-V // 256) <= 65535))
+
+
+def unlisted(st, T):
+    """A copy of a state with every row's listed flag cleared: the backward
+    then takes those rows' keys from the recompute again."""
+    s = st.clone()
+    rec = s[: T * binding.RECORD_BYTES].view(torch.int32).view(T, 8)
+    rec[:, 3] &= ~binding.FLAG_LISTED
+    return s
+
+
+def without_lists(st, T):
+    """A copy of a state with neither tile lists nor support lists: every
+    sparse row goes through the whole-vocabulary recompute."""
+    s = unlisted(st, T)
+    s[T * binding.RECORD_BYTES:] = 0
+    return s
+
+
+def check_support_lists(info, keys):
+    """A listed row's support list holds its n support tokens in decreasing
+    (key, -id) order with the forward's keys bit for bit, and zeros after;
+    every other row's list is zero."""
+    T = keys.shape[0]
+    listed = (info["flags"] & binding.FLAG_LISTED) != 0
+    for r in range(T):
+        ids, ks = info["support_ids"][r], info["support_keys"][r]
+        if not listed[r]:
+            assert not ids.any() and not ks.view(np.int32).any(), r
+            continue
+        n = int(info["n"][r])
+        assert n <= NSP and (info["flags"][r] & binding.FLAG_FILTERED), r
+        row = keys[r]
+        kthr, ithr = row[info["id_thr"][r]], info["id_thr"][r]
+        idx = np.arange(row.shape[0])
+        want = np.nonzero((row > kthr) | ((row == kthr) & (idx <= ithr)))[0]
+        want = want[np.lexsort((want, -row[want].astype(np.float64)))]
+        assert np.array_equal(ids[:n], want), (r, ids[:n], want)
+        assert np.array_equal(ks[:n], row[want]), r          # (equal floats: the lists keep +0 for -0)
+        assert not ids[n:].any() and not ks[n:].view(np.int32).any(), r
+    return int(listed.sum())
 
 
 def check_tile_lists(info, keys, V):
@@ -131,12 +183,15 @@ def check_tile_lists(info, keys, V):
 def check_recomputed_keys(rk, fk, info, g, y, V, dtype):
     """The backward's recomputed keys (NaN where it formed none) against the
     forward's, bit for bit: every row's keys, but a tiled row's only on its
-    listed tiles (and none elsewhere); the target key and the row maximum
-    against the forward's state.  Returns (keys formed, tiled rows)."""
+    listed tiles (and none elsewhere) and none of a listed row's; the target
+    key and the row maximum against the forward's state.  Returns (keys
+    formed, tiled rows)."""
     rkc, fkc = np.asarray(rk), np.asarray(fk)
     T = fkc.shape[0]
     tiled = tiled_rows(info, g, V, dtype)
+    listed = listed_rows(info, g, dtype)
     formed = np.ones((T, V), bool)
+    formed[listed] = False
     for r in np.nonzero(tiled)[0]:
         formed[r] = False
         for j in info["tiles"][r, :info["ntile"][r]]:
@@ -150,5 +205,5 @@ def check_recomputed_keys(rk, fk, info, g, y, V, dtype):
     sy = rkc[np.arange(T), y]
     assert np.array_equal(sy[fy].view(np.int32), info["target_key"][fy].view(np.int32))
     mx = np.where(formed, rkc, -np.inf).max(1)
-    assert np.array_equal(mx.view(np.int32), info["row_max"].view(np.int32))
+    assert np.array_equal(mx[~listed].view(np.int32), info["row_max"][~listed].view(np.int32))
     return int(formed.sum()), int(tiled.sum())

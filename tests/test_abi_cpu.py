@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function(lib):
 def test_struct_layouts_match_header(tmp_path):
     assert ctypes.sizeof(binding.Problem) == 128
     assert ctypes.sizeof(binding.RowInfo) == binding.RECORD_BYTES
-    assert binding.STATE_BYTES_PER_ROW == binding.RECORD_BYTES + 2 * (1 + binding.NTILE)
+    assert binding.STATE_BYTES_PER_ROW == binding.RECORD_BYTES + 2 * (1 + binding.NTILE) + 8 * binding.NSP
     # the binding's field offsets against the C compiler's for the header
     fields = [f for f, _ in binding.Problem._fields_]
     src = tmp_path / "layout.c"
@@ -70,7 +70,7 @@ def test_workspace_sizes_are_host_computable(lib):
     # selection of one chunk overlaps the projection of the next) plus the
     # per-row flags: nothing scales with T x V
     assert f2 < 2 * (512 * 101 * 4 + 512 * 16 + 512 * 4) + 100000 * 4 + 4096
-    assert lib.stce_state_bytes(10) == 960
+    assert lib.stce_state_bytes(10) == 11200
 
 
 def test_unsupported_dtype_is_one_actionable_error(lib):
@@ -215,12 +215,18 @@ def test_decode_state_roundtrip(lib):
                                       ("lse", "<f4"), ("lsef", "<f4"), ("m", "<f4"), ("sy", "<f4")]))
     raw["id_thr"] = [5, 6, 7]
     raw["n"] = [1, 2, 3]
+    raw["flags"] = [0, 0, 32]
     tiles = np.zeros((3, 32), np.uint16)
     tiles[1, :3] = [2, 9, 4000]                      # row 1 lists tiles 9 and 4000
+    sup = np.zeros((3, 128), np.dtype([("id", "<i4"), ("key", "<f4")]))
+    sup[2, :2] = [(17, 2.5), (3, -1.25)]             # row 2 lists its support {17, 3}
     torch = pytest.importorskip("torch")
-    d = binding.decode_state(torch.from_numpy(np.concatenate([raw.view(np.uint8), tiles.view(np.uint8).ravel()])))
+    d = binding.decode_state(torch.from_numpy(np.concatenate([raw.view(np.uint8), tiles.view(np.uint8).ravel(),
+                                                              sup.view(np.uint8).ravel()])))
     assert list(d["id_thr"]) == [5, 6, 7] and list(d["n"]) == [1, 2, 3]
     assert list(d["ntile"]) == [0, 2, 0] and list(d["tiles"][1, :2]) == [9, 4000]
+    assert list(d["flags"] & binding.FLAG_LISTED) == [0, 0, 32]
+    assert list(d["support_ids"][2, :3]) == [17, 3, 0] and list(d["support_keys"][2, :2]) == [2.5, -1.25]
 
 
 def test_policy_loss_rejects_bad_parameters_before_launch(lib):
@@ -264,20 +270,17 @@ def test_fused_workspace_is_host_computable_and_chunk_bounded(lib):
 
 
 def test_fused_workspace_of_the_classed_path(lib):
-    """A bf16 problem with a filter array takes the fused step's path with
-    row classes: one size (no weight-gradient groups), holding the rows'
-    gradients and entry lists, the per-vocabulary-row counts, and the larger
-    of the sweep's buffers and the backward's workspace."""
+    """A bf16 problem with a filter array (or the fp8 lane) takes the fused
+    step's path with row classes: one size (no weight-gradient groups), the
+    rows' gradients and then the larger of the forward's and the backward's
+    workspaces, which the step uses one after the other."""
     T, H, V = 16384, 5120, 151936
     dense, _ = binding.fused_workspace_bytes(_prob(T=T, H=H, V=V))
-    for kw in (dict(top_k=16), dict(top_p=16), dict(min_p=16), dict(top_k=16, dtype=binding.DT_FP8)):
+    for kw in (dict(top_k=16), dict(top_p=16), dict(min_p=16), dict(top_k=16, dtype=binding.DT_FP8),
+               dict(dtype=binding.DT_FP8)):
         full, least = binding.fused_workspace_bytes(_prob(T=T, H=H, V=V, **kw))
-        _, bwd = binding.workspace_bytes(_prob(T=T, H=H, V=V, **kw))
-        C, ldt, ntv = 4096, V, -(-V // 256)
-        sweep = 4 * T + 2 * (4 * C * ldt + 16 * C * ntv + 4 * C)
-        kept = 4 * T + 8 * 128 * T + 4 * T + 4 * V
-        assert full == least, kw
-        assert kept + max(sweep, bwd) <= full < kept + max(sweep, bwd) + 4096, kw
+        fwd, bwd = binding.workspace_bytes(_prob(T=T, H=H, V=V, **kw))
+        assert full == least == 4 * T + max(fwd, bwd), kw
         assert full < dense
     # fp32 operands keep the dense path whatever the filters
     f32, f32min = binding.fused_workspace_bytes(_prob(T=T, H=H, V=V, dtype=binding.DT_F32, top_k=16))

@@ -1,14 +1,18 @@
 """The backward's row classes: rows whose support holds at most NSP = 128
 tokens take the sparse products (their dz entries summed one by one), larger
-supports the matrix-core products, rows with no gradient neither.  Every
-mix is held to the oracle (gradients within 1e-2 relative Frobenius error)
-and to run-to-run bitwise equality."""
+supports the matrix-core products, rows with no gradient neither.  A sparse
+row's entries come from the support the state lists with its keys, else
+from its keys recomputed on its listed tiles, else from the whole-vocabulary
+recompute; the three give the same entries.  Every mix is held to the oracle
+(gradients within 1e-2 relative Frobenius error) and to run-to-run bitwise
+equality."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_helpers import GRAD_RTOL, check_tile_lists, dev, meta_of, rel_fro, say, targets, tiled_rows, to_gpu
+from gpu_helpers import (GRAD_RTOL, check_support_lists, check_tile_lists, dev, listed_rows, meta_of, rel_fro, say,
+                         targets, tiled_rows, to_gpu, unlisted, without_lists)
 from sampling_transform_logprob_amd import binding, workloads
 from sampling_transform_logprob_amd.workloads import round_bf16
 
@@ -129,15 +133,16 @@ def test_a_token_in_every_support_takes_the_windowed_bucket():
 
 
 @pytest.mark.parametrize("name,T,V", [("headline", 300, 30000), ("headline_fp8", 260, 20000), ("ties", 280, 20000)])
-def test_tile_recompute_equals_the_whole_vocabulary_recompute(name, T, V):
-    """A sparse row with a tile list has its keys recomputed on the listed
-    tiles only.  The same state with every list cleared sends those rows
-    through the whole-vocabulary recompute; both must give the same dz
-    entries.  dH sums a row's entries in vocabulary order, so it is bitwise
-    equal; dW sums a vocabulary row's entries in permuted-position order,
-    and clearing the lists moves tiled rows behind the other sparse rows, so
-    dW is bitwise equal when every sparse row is tiled (the placement does
-    not change) and otherwise equal up to fp32 summation order."""
+def test_listed_tiled_and_whole_vocabulary_entries_agree(name, T, V):
+    """A sparse row whose support the state lists takes its dz entries from
+    the listed keys; the same state with the listed flags cleared recomputes
+    its keys on its listed tiles, and with the tile lists cleared too in the
+    whole-vocabulary recompute.  All three must give the same entries.  dH
+    sums a row's entries in vocabulary order, so it is bitwise equal; dW
+    sums a vocabulary row's entries in permuted-position order, which the
+    three placements keep when every sparse row is listed and tiled (then
+    dW is bitwise equal) and otherwise change (equal up to fp32 summation
+    order)."""
     w = workloads.make(name, T=T)
     w["W"] = w["W"][:V]
     if w.get("w_scale") is not None:
@@ -148,35 +153,42 @@ def test_tile_recompute_equals_the_whole_vocabulary_recompute(name, T, V):
     ws = {"weight_scale": G["weight_scale"]} if G["weight_scale"] is not None else {}
     lp, st = binding.forward(G["h"], G["W"], G["target"], **meta_of(G), **ws)
     g = torch.from_numpy(np.random.Generator(np.random.PCG64(T)).standard_normal(T).astype(np.float32)).to(dev())
-    st_full = st.clone()
-    st_full[T * binding.RECORD_BYTES:] = 0                         # no tile lists
+    st_tiled, st_full = unlisted(st, T), without_lists(st, T)
     gh, gw = binding.backward(G["h"], G["W"], G["target"], st, g, **meta_of(G), **ws, vocab_slice=8192)
+    gh1, gw1 = binding.backward(G["h"], G["W"], G["target"], st_tiled, g, **meta_of(G), **ws, vocab_slice=8192)
     gh0, gw0 = binding.backward(G["h"], G["W"], G["target"], st_full, g, **meta_of(G), **ws, vocab_slice=8192)
+    keys = binding.scaled_logits(G["h"], G["W"], G["temperature"], **ws).cpu().numpy()
     torch.cuda.synchronize()
     info = binding.decode_state(st)
-    tiled = tiled_rows(info, g.cpu().numpy(), V, w["dtype"])
-    say(f"tile recompute {name}: T={T} V={V}: {int(tiled.sum())} tiled rows, "
+    gc = g.cpu().numpy()
+    nlisted = check_support_lists(info, keys)
+    listed = listed_rows(info, gc, w["dtype"])
+    tiled = tiled_rows(binding.decode_state(st_tiled), gc, V, w["dtype"])
+    say(f"listed / tiled / whole-vocabulary {name}: T={T} V={V}: {nlisted} rows list their support "
+        f"({int(listed.sum())} with a gradient); without the lists {int(tiled.sum())} tiled rows, "
         f"{int(info['ntile'][tiled].sum())} (row, tile) pairs of {T * (-(-V // 256))}")
-    assert tiled.sum() > (T // 3 if name != "ties" else 0)
-    assert torch.equal(gh, gh0)
+    assert listed.sum() > (T // 3 if name != "ties" else 0) and tiled.sum() > (T // 3 if name != "ties" else 0)
+    assert torch.equal(gh, gh1) and torch.equal(gh, gh0)
     fl = info["flags"]
-    active = ((fl & binding.FLAG_VALID) != 0) & ((fl & binding.FLAG_IN_SUPPORT) != 0) & (g.cpu().numpy() != 0)
+    active = ((fl & binding.FLAG_VALID) != 0) & ((fl & binding.FLAG_IN_SUPPORT) != 0) & (gc != 0)
     sparse = active & ((fl & binding.FLAG_FILTERED) != 0) & (info["n"] <= NSP)
-    if np.array_equal(sparse, tiled):
-        assert torch.equal(gw, gw0)
-    else:
-        err = (gw - gw0).abs().max().item() / gw0.abs().max().item()
-        say(f"  dW: placement differs ({int((sparse & ~tiled).sum())} sparse rows without a list); "
-            f"max difference {err:.1e} of the largest entry")
-        assert err < 1e-5
+    for other, label in ((gw1, "tiled"), (gw0, "whole-vocabulary")):
+        if np.array_equal(sparse, listed) and np.array_equal(sparse, tiled):
+            assert torch.equal(gw, other), label
+        else:
+            err = (gw - other).abs().max().item() / other.abs().max().item()
+            say(f"  dW against the {label} path: placement differs; max difference {err:.1e} of the largest entry")
+            assert err < 1e-5, label
 
 
 def test_tile_lists_at_the_31_tile_bound():
     """Rows whose support spans 30, 31 and 32 vocabulary tiles: one peak
     token per tile (distinct heights, far above the rest), top-k equal to
     the number of peaks.  The lists hold 30 and 31 tiles; a 32-tile support
-    keeps no list and its row takes the whole-vocabulary recompute.  Both
-    kinds agree with the oracle and with the lists cleared."""
+    keeps no list.  The rows list their supports; with the listed flags
+    cleared the 30- and 31-tile rows take the tile recompute and the 32-tile
+    rows the whole-vocabulary one.  Every path agrees with the oracle and
+    with the lists cleared."""
     rng = np.random.Generator(np.random.PCG64(31))
     ntv, H = 40, 64
     V = ntv * 256
@@ -199,18 +211,21 @@ def test_tile_lists_at_the_31_tile_bound():
     lp, st = binding.forward(G["h"], G["W"], G["target"], **meta_of(G))
     g = torch.from_numpy(rng.standard_normal(T).astype(np.float32)).to(dev())
     gh, gw = binding.backward(G["h"], G["W"], G["target"], st, g, **meta_of(G))
-    st_full = st.clone()
-    st_full[T * binding.RECORD_BYTES:] = 0
-    gh0, gw0 = binding.backward(G["h"], G["W"], G["target"], st_full, g, **meta_of(G))
+    gh1, gw1 = binding.backward(G["h"], G["W"], G["target"], unlisted(st, T), g, **meta_of(G))
+    gh0, gw0 = binding.backward(G["h"], G["W"], G["target"], without_lists(st, T), g, **meta_of(G))
     keys = binding.scaled_logits(G["h"], G["W"], G["temperature"]).cpu().numpy()
     torch.cuda.synchronize()
     info = binding.decode_state(st)
     check_tile_lists(info, keys, V)
+    check_support_lists(info, keys)
     assert np.array_equal(info["n"], m_of)
     assert np.array_equal(info["ntile"], np.where(m_of <= 31, m_of, 0))
     ref, (dH, dW) = _oracle_grads(w, y, g.cpu().numpy(), keys)
     rh, rw = rel_fro(gh.float().cpu().numpy(), dH), rel_fro(gw.cpu().numpy(), dW)
     say(f"31-tile bound: lists {sorted(set(info['ntile'].tolist()))}; dH rel {rh:.2e} dW rel {rw:.2e}")
     assert rh < GRAD_RTOL and rw < GRAD_RTOL
-    assert torch.equal(gh, gh0)
+    rh1, rw1 = rel_fro(gh1.float().cpu().numpy(), dH), rel_fro(gw1.cpu().numpy(), dW)
+    assert rh1 < GRAD_RTOL and rw1 < GRAD_RTOL                       # the tile recompute (lists unused)
+    assert torch.equal(gh, gh0) and torch.equal(gh, gh1)
     assert (gw - gw0).abs().max().item() <= 1e-5 * gw0.abs().max().item()
+    assert (gw - gw1).abs().max().item() <= 1e-5 * gw1.abs().max().item()

@@ -15,7 +15,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import (GRAD_RTOL, check_logprob, check_recomputed_keys, check_support, check_tile_lists, dev,
+from gpu_helpers import (GRAD_RTOL, check_logprob, check_recomputed_keys, check_support, check_support_lists,
+                         check_tile_lists, dev,
                          meta_of, rel_fro, say, targets, to_gpu)
 from sampling_transform_logprob_amd import binding, workloads
 from sampling_transform_logprob_amd.workloads import round_bf16
@@ -148,6 +149,7 @@ def test_fp8_workload_parity(name, T, V, dense):
     kc = keys.cpu().numpy()
     info = binding.decode_state(st)
     check_tile_lists(info, kc, V)
+    check_support_lists(info, kc)
     check_recomputed_keys(rk.cpu().numpy(), kc, info, g, y, V, "fp8")
     ref = oracle.forward(w["h"], w["W"], y, w["temperature"], w["top_k"], w["top_p"], w["min_p"], keys=kc,
                          lane="fp8", w_scale=w["w_scale"])

@@ -1,9 +1,10 @@
 """GPU parity of the fused head + policy-gradient step, through the C ABI.
-The step forms dlogits inside the forward's sweep from the chunk's stored
-keys.  With row classes (bf16 operands with a filter given, or the fp8
-lane) it forms the tiled rows' dz entries from the keys and then runs the
-classed backward without its tile recompute; dense (fp32, or bf16 with no
-filter) it forms every row's dz and needs no recompute product at all.
+The step forms dlogits from keys the forward's sweep keeps.  With row
+classes (bf16 operands with a filter given, or the fp8 lane) the sweep keeps
+each small support with its keys in the state and the step is the forward,
+the loss and the classed backward in one call; dense (fp32, or bf16 with no
+filter) it forms every row's dz from the chunk's keys and needs no recompute
+product at all.
 
 * Against the oracle (forward, token loss and VJP in fp64) at the core's
   bar: logprob within 2e-3, the summed loss within 1e-3 relative, and
@@ -17,10 +18,9 @@ filter) it forms every row's dz and needs no recompute product at all.
     recompute's, but the products reduce in another order;
   - inactive, invalid and out-of-support rows, a frozen head, weight-gradient
     accumulation and the side outputs are all covered.
-* With row classes the gradients equal the unfused sequence's bit for bit
-  (the tiled rows' entries are formed from keys equal to the recompute's,
-  every other row goes through the same backward), on batches that mix
-  every class within a chunk, on the fp8 lane, for a frozen head and with
+* With row classes every output equals the unfused sequence's bit for bit,
+  on batches that mix every class within a chunk (listed, tiled, sparse,
+  dense, no gradient), on the fp8 lane, for a frozen head and with
   weight-gradient accumulation.
 * The dense path, taken by bf16 problems with no filter arrays, against the
   oracle and against the unfused sequence.
@@ -239,9 +239,11 @@ def _classed_case(name, T, V):
     """A small batch of the named workload whose chunks mix every row class:
     every fifth row unfiltered (its support the whole vocabulary: dense),
     every seventh a top-p row of a wide support (over 128 tokens: dense),
-    every eleventh a top-64 row (sparse where its support spreads past 31
-    tiles), the rest top-k rows (tiled); one row's target outside its
-    support, one invalid row."""
+    every eleventh a top-64 row, every thirteenth a top-120 row (more tokens
+    than the vocabulary has tiles, so decided from a histogram: its support
+    is not listed, and it is tiled, or sparse past 31 tiles), the rest top-k
+    rows (their supports listed); one row's target outside its support, one
+    invalid row."""
     w = workloads.make(name, T=T)
     if V is not None and V < w["V"]:
         w["W"], w["V"] = w["W"][:V], V
@@ -250,7 +252,8 @@ def _classed_case(name, T, V):
         w["target_uniform"] = w["target_uniform"] % V
     w["top_k"][::5], w["top_p"][::5], w["min_p"][::5] = 0, 1.0, 0.0
     w["top_k"][3::7], w["top_p"][3::7] = 0, 0.9
-    w["top_k"][6::11] = 64            # past 31 tiles when V is large: the sparse class
+    w["top_k"][6::11] = 64
+    w["top_k"][9::13], w["top_p"][9::13], w["min_p"][9::13] = 120, 1.0, 0.0
     y = np.asarray(targets(w), np.int64) % w["W"].shape[0]
     G = to_gpu(w, y)
     # row 1: top-2 with the target at the lowest logit (the oracle's)
@@ -266,7 +269,7 @@ def _classed_case(name, T, V):
 
 @pytest.mark.parametrize("name,T,V,chunk", [
     ("headline", 300, 5000, 64),      # 5 chunks, the last of 44 rows
-    ("headline", 200, 3000, 0),       # one chunk
+    ("headline", 200, 6000, 0),       # one chunk (V above the selection's whole-row window of 3712 tokens)
     ("top_p", 260, 6000, 128),
     ("headline_fp8", 300, 30000, 128),
 ])
@@ -289,13 +292,16 @@ def test_classed_fused_step_equals_the_unfused_sequence_bitwise(name, T, V, chun
     fl = info["flags"]
     live = ((fl & binding.FLAG_VALID) != 0) & ((fl & binding.FLAG_IN_SUPPORT) != 0)
     filt = live & ((fl & binding.FLAG_FILTERED) != 0)
-    tiled = filt & (info["n"] <= 128) & (info["ntile"] > 0)
+    small = filt & (info["n"] <= 128)
+    listed = small & ((fl & binding.FLAG_LISTED) != 0)
+    tiled = small & ~listed & (info["ntile"] > 0)
+    sparse = small & ~listed & (info["ntile"] == 0)
     say(f"classed fused vs unfused: {name} T={T} V={V} chunk={chunk or 'default'}: rows dense "
-        f"{int((live & ~filt).sum() + (filt & (info['n'] > 128)).sum())}, tiled {int(tiled.sum())}, sparse "
-        f"{int((filt & (info['n'] <= 128) & (info['ntile'] == 0)).sum())}, no gradient {int((~live).sum())}")
-    assert tiled.sum() > 0 and (live & ~filt).sum() > 0 and (~live).sum() >= 2
-    if V > 31 * 256:
-        assert (filt & (info["n"] <= 128) & (info["ntile"] == 0)).sum() > 0
+        f"{int((live & ~filt).sum() + (filt & (info['n'] > 128)).sum())}, listed {int(listed.sum())}, tiled "
+        f"{int(tiled.sum())}, sparse {int(sparse.sum())}, no gradient {int((~live).sum())}")
+    assert (tiled | sparse).sum() > 0 and (live & ~filt).sum() > 0 and (~live).sum() >= 2
+    if name.startswith("headline"):                       # top-k rows decided from their candidates
+        assert listed.sum() > 0
     for k in ("logprob", "state", "loss", "ratio", "grad_hidden", "grad_weight"):
         assert _same(f[k], u[k]), k
     # a frozen head: the same hidden gradient; weight-gradient accumulation:

@@ -11,12 +11,16 @@ and the row maximum the forward stored in its per-row state, over
 multi-chunk forwards and multi-slice backwards, in every lane convention.
 A tiled row's keys are recomputed on its listed tiles only: the list must be
 exactly the tiles whose largest key reaches the row's last support key, and
-the row's other keys are not formed."""
+the row's other keys are not formed.  A row whose support the state lists
+with its keys has none recomputed: its list must hold the forward's keys of
+its support; with the listed flags cleared, the same rows take the tile
+recompute, whose keys are checked the same way."""
 import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import check_recomputed_keys, check_tile_lists, dev, meta_of, say, targets, to_gpu
+from gpu_helpers import (check_recomputed_keys, check_support_lists, check_tile_lists, dev, meta_of, say, targets,
+                         to_gpu, unlisted)
 from sampling_transform_logprob_amd import binding, workloads
 
 pytestmark = pytest.mark.gpu
@@ -49,6 +53,8 @@ def test_recomputed_keys_are_the_forwards(name, T, V, chunk, vslice, opts):
     lp, st = binding.forward(G["h"], G["W"], G["target"], **meta, chunk_rows=chunk, **opts)
     g = torch.from_numpy(np.random.Generator(np.random.PCG64(T)).standard_normal(T).astype(np.float32)).to(dev())
     rk = binding.recompute_keys(G["h"], G["W"], G["target"], st, g, **meta, vocab_slice=vslice, **opts)
+    st_u = unlisted(st, T)
+    rku = binding.recompute_keys(G["h"], G["W"], G["target"], st_u, g, **meta, vocab_slice=vslice, **opts)
     fk = binding.scaled_logits(G["h"], G["W"], meta["temperature"],
                                **{k: v for k, v in opts.items() if k in ("lane", "pre_gemm_temperature")})
     torch.cuda.synchronize()
@@ -57,6 +63,10 @@ def test_recomputed_keys_are_the_forwards(name, T, V, chunk, vslice, opts):
     info = binding.decode_state(st)
     fkc = fk.cpu().numpy()
     check_tile_lists(info, fkc, V)
+    nlisted = check_support_lists(info, fkc)
     nformed, ntiled = check_recomputed_keys(rk.cpu().numpy(), fkc, info, g.cpu().numpy(), y, V, w["dtype"])
-    say(f"  {nformed} keys equal ({ntiled} tiled rows, {T * V - nformed} keys not formed); target keys and "
-        f"row maxima equal the forward's state")
+    nformed_u, ntiled_u = check_recomputed_keys(rku.cpu().numpy(), fkc, binding.decode_state(st_u),
+                                                g.cpu().numpy(), y, V, w["dtype"])
+    say(f"  {nlisted} rows list their support with the forward's keys; {nformed} keys equal ({ntiled} tiled "
+        f"rows, {T * V - nformed} keys not formed); with the lists unused {nformed_u} keys equal ({ntiled_u} "
+        f"tiled rows); target keys and row maxima equal the forward's state")
