@@ -413,6 +413,62 @@ __device__ inline void wave_ordered_sum(int ne, int idx, float v, const E* X, co
     for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(vv, x[k], acc[k]);
   }
 }
+// Four consecutive elements of a hidden row as fp32 (8-byte bf16 or 16-byte
+// fp32 loads).
+template <class E>
+__device__ inline void load4(const E* p, float (&x)[4]) {
+  if constexpr (sizeof(E) == 2) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    const bf16x4 v = *(const bf16x4*)p;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = (float)v[k];
+  } else {
+    const f32x4 a = *(const f32x4*)p;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = a[k];
+  }
+}
+
+// wave_ordered_sum's arithmetic on the columns ca .. ca + 4 (acc[0..4)) and
+// cb .. cb + 4 (acc[4..8)) of each entry's row: the same sums, each element
+// over the entries in order.
+template <class E>
+__device__ inline void wave_ordered_sum_split(int ne, int idx, float v, const E* X, int64_t H, int64_t ca,
+                                              int64_t cb, float (&acc)[8]) {
+  int s = 0;
+  for (; s + 4 <= ne; s += 4) {
+    float x[4][8], vs[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t row = __builtin_amdgcn_readlane(idx, s + u);
+      vs[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), s + u));
+      float a[4], b[4];
+      load4(X + row * H + ca, a);
+      load4(X + row * H + cb, b);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[u][k] = a[k];
+        x[u][4 + k] = b[k];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = __builtin_fmaf(vs[u], x[u][k], acc[k]);
+  }
+  for (; s < ne; ++s) {
+    const int64_t row = __builtin_amdgcn_readlane(idx, s);
+    const float vv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), s));
+    float a[4], b[4];
+    load4(X + row * H + ca, a);
+    load4(X + row * H + cb, b);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[k] = __builtin_fmaf(vv, a[k], acc[k]);
+      acc[4 + k] = __builtin_fmaf(vv, b[k], acc[4 + k]);
+    }
+  }
+}
 constexpr int WIN = 4096;         // token positions per window beyond that
 
 // Weight gradient rows from the buckets: one workgroup per vocabulary row j,
@@ -587,10 +643,15 @@ __global__ __launch_bounds__(256) void sparse_dw_wave_kernel(const int* off, con
     }
     wave_order(ne, idx, v);
     float* row = dW + j * H;
-    for (int64_t c0 = lane * 8; c0 < H; c0 += 64 * 8) {
+    // a pass covers 512 columns: lane l the groups of four at 4 l and
+    // 256 + 4 l, so that each fp32 store instruction writes 1 KB of the row
+    // contiguously (whole cache lines) and each row load reads 512 B
+    for (int64_t c0 = 0; c0 < H; c0 += 512) {
+      const int64_t ca = c0 + 4 * lane, cb = ca + 256;
+      const bool ia = ca < H, ib = cb < H;  // (H is a multiple of 8)
       float acc[8];
       if (from_mem) {
-        const f32x4 a = *(const f32x4*)(row + c0), b = *(const f32x4*)(row + c0 + 4);
+        const f32x4 a = ia ? *(const f32x4*)(row + ca) : f32x4{}, b = ib ? *(const f32x4*)(row + cb) : f32x4{};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           acc[k] = a[k];
@@ -600,9 +661,9 @@ __global__ __launch_bounds__(256) void sparse_dw_wave_kernel(const int* off, con
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[k] = 0.f;
       }
-      wave_ordered_sum(ne, idx, v, h, (const float*)nullptr, H, c0, acc);
-      *(f32x4*)(row + c0) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      *(f32x4*)(row + c0 + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+      wave_ordered_sum_split(ne, idx, v, h, H, ia ? ca : 0, ib ? cb : 0, acc);
+      if (ia) *(f32x4*)(row + ca) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      if (ib) *(f32x4*)(row + cb) = f32x4{acc[4], acc[5], acc[6], acc[7]};
     }
   }
 }
