@@ -38,7 +38,27 @@ stce_status hip_fail(hipError_t e, const char* what) {
   return fail(STCE_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr int64_t kDefaultChunk = 4096;   // forward rows per chunk
+constexpr int kComputeUnits = 256;       // MI355X (gfx950): 8 XCDs of 32
+// Default rows per chunk: 256 times the number n of token tiles (16 .. 12)
+// whose projection, V/256 x n output tiles of 256 x 256, best fills whole
+// waves of one workgroup per compute unit (a chunk's last wave otherwise
+// leaves most of the chip idle); a smaller n must fill them half a percent
+// better to be taken.  At V = 151,936 (594 vocabulary tiles) 16 token tiles
+// make 37.1 waves and 15 make 34.8: 3,840 rows.
+int64_t default_chunk(int64_t V) {
+  const int64_t mt = (V + 255) / 256;
+  int64_t best = 16;
+  double best_fill = 0.0;
+  for (int64_t nt = 16; nt >= 12; --nt) {
+    const int64_t tiles = mt * nt;
+    const double fill = (double)tiles / (double)((tiles + kComputeUnits - 1) / kComputeUnits * kComputeUnits);
+    if (fill > best_fill + 0.005) {
+      best_fill = fill;
+      best = nt;
+    }
+  }
+  return best * 256;
+}
 // Default backward slice: the widest (multiple of 256) whose dz (T x V_s
 // elements for bf16 operands; twice that for fp32, which also keeps it
 // vocab-major) fits in this many bytes.  Wider slices mean fewer
@@ -146,7 +166,7 @@ Layout plan(const stce_problem* p, bool single_buffer = false) {
   Layout L{};
   const int64_t T = p->T, V = p->V, H = p->H;
   const size_t es = elt_size(p->dtype);
-  L.C = p->chunk_rows > 0 ? p->chunk_rows : kDefaultChunk;
+  L.C = p->chunk_rows > 0 ? p->chunk_rows : default_chunk(p->V);
   if (L.C > T) L.C = T;
   L.ldt = round_up(V, 4);
   L.ntv = ceil_div(V, VTILE);
@@ -270,7 +290,9 @@ FusedLayout plan_fused(const stce_problem* p, int64_t gmax = INT64_MAX) {
   const int64_t T = p->T, V = p->V, H = p->H;
   const size_t es = elt_size(p->dtype);
   L.Tp = round_up(T, 64);
-  L.C = round_up(p->chunk_rows > 0 ? p->chunk_rows : kDefaultChunk, 64);
+  // (the dense path keeps 4,096 rows by default: its group of chunks' dz
+  // is sized in whole chunks, which a chunk that does not divide T pads)
+  L.C = round_up(p->chunk_rows > 0 ? p->chunk_rows : 4096, 64);
   if (L.C > L.Tp) L.C = L.Tp;
   L.ldt = round_up(V, 4);
   L.ntv = ceil_div(V, VTILE);
@@ -663,7 +685,8 @@ stce_status stce_forward_noalloc(const stce_problem* p, float* logprob, void* st
   // chunk that does (single buffer, selection on the caller's stream)
   stce_problem q = *p;
   if (plan(&q, true).fwd > kNoallocScratchBytes) {
-    int64_t lo = 0, hi = q.chunk_rows > 0 ? q.chunk_rows : (q.T < 4096 ? q.T : 4096);
+    const int64_t dc = default_chunk(q.V);
+    int64_t lo = 0, hi = q.chunk_rows > 0 ? q.chunk_rows : (q.T < dc ? q.T : dc);
     while (lo < hi) {  // largest C in [1, hi] whose workspace fits (0 if none)
       const int64_t mid = (lo + hi + 1) / 2;
       q.chunk_rows = mid;
