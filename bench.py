@@ -153,7 +153,7 @@ def row_classes(info, g, tiled_on, nsp=128):
     tiled = active & ~dense & ~listed & (info["ntile"] > 0) & tiled_on
     return {"dense": int(dense.sum()), "sparse": int((active & ~dense & ~listed & ~tiled).sum()),
             "listed": int(listed.sum()), "tiled": int(tiled.sum()), "empty": int((~active).sum()),
-            "tile_pairs": int(info["ntile"][tiled].sum())}
+            "tile_pairs": int(info["ntile"][tiled].sum()), "entries": int(info["n"][active & ~dense].sum())}
 
 
 KERNEL_SYMBOLS = {
@@ -163,6 +163,9 @@ KERNEL_SYMBOLS = {
     "tile_recompute": "gemm_worklist",
     "grad_weight": "EpiStore",
     "grad_hidden": "EpiAccum",
+    # the HBM-bound sums of the backward (their wave kernels)
+    "sparse_grad_weight": "sparse_dw_wave_kernel",
+    "sparse_grad_hidden": "sparse_dh_wave_kernel",
 }
 
 # kernel-trace labels: (substring of the symbol, label), first match wins
@@ -177,8 +180,10 @@ TRACE_LABELS = [
     ("EpiStore", "gemm: grad_weight of the dense rows (EpiStore)"),
     ("EpiAccumT", "gemm: grad_hidden of the dense rows as dH^T (EpiAccumT)"),
     ("EpiDlogits", "gemm: backward recompute + dz^T, fp32 operands (EpiDlogits)"),
-    ("sparse_dw_kernel", "sparse grad_weight rows from the dz entry buckets"),
-    ("sparse_dh_kernel", "sparse grad_hidden rows from the dz entries"),
+    ("sparse_dw_wave", "sparse grad_weight rows of at most 64 entries (one wave per vocabulary row)"),
+    ("sparse_dw_kernel", "sparse grad_weight rows of more than 64 entries (one workgroup per vocabulary row)"),
+    ("sparse_dh_wave", "sparse grad_hidden rows of at most 64 entries (one wave per row)"),
+    ("sparse_dh_kernel", "sparse grad_hidden rows of more than 64 entries (one workgroup per row)"),
     ("select_kernel", "select: support program + logprob"),
     ("class_", "backward row classes (count, scan, place)"),
     ("gather_rows", "row gathers (permuted hidden rows; rows to re-project)"),
@@ -358,7 +363,8 @@ def _counter_rows(path, name_part):
                     out.append(float(r["Counter_Value"]))
                 continue
             kn = r["Kernel_Name"]
-            if name_part in kn and ("gemm_kernel" in kn or "gemm_worklist_kernel" in kn) and "MainF32" not in kn:
+            gemm = ("gemm_kernel" in kn or "gemm_worklist_kernel" in kn) and "MainF32" not in kn
+            if name_part in kn and (gemm or name_part.startswith("sparse_")):
                 out.append(float(r["Counter_Value"]))
     # launches that did work: a re-projection with no row to project shares
     # the projection's symbol but returns at once (a counter near zero)
@@ -716,6 +722,24 @@ def main():
                for k in per_step_flop}
     t_at_peak = sum(f / (peak_of[k] * 1e12) for k, f in per_step_flop.items())
 
+    # the backward's HBM-bound sums: algorithmic bytes of a launch over its
+    # average duration, against the 8 TB/s peak (E dz entries of the sparse
+    # rows: dW writes every fp32 row and gathers a hidden row per entry, dH
+    # gathers a weight row per entry and writes the non-dense rows)
+    hbm_kernels = {}
+    if classed:
+        E, T_sp = classes["entries"], T - classes["dense"]
+        ew = 1 if fp8 else 2
+        algo = {"sparse_grad_weight": 4.0 * V * H + 2.0 * E * H + 24.0 * E,
+                "sparse_grad_hidden": float(ew) * E * H + 2.0 * T_sp * H + 8.0 * E,
+                "listed_entries": 16.0 * E}
+        for k, b in algo.items():
+            if k in stats:
+                per = b / stats[k]["launches"]
+                gbs = per / (stats[k]["avg_ms"] * 1e-3) / 1e9
+                hbm_kernels[k] = {"bound": "hbm", "bytes_per_launch": per, "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                  "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": read_traffic(k, args.config)}
+
     # matrix-core flop the step performs (the dense formulation would perform
     # 8 T H V: forward, recompute, dH, dW over every row)
     flop_step = sum(per_step_flop.values())
@@ -767,6 +791,7 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved / peak_of[dom],
                      "traffic": read_traffic(dom, args.config)},
         "kernels": stats,
+        "hbm_kernels": hbm_kernels,
         "targets_in_support": in_support,
         "binding_filter_rows": binds,
     }
