@@ -24,7 +24,7 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_traffic_follows_the_source_digest(monkeypatch):
-    cases = [(k, c) for k in ("projection", "tile_recompute") for c in ("headline", "headline_fp8")]
+    cases = [(k, c) for k in ("projection", "sparse_grad_weight") for c in ("headline", "headline_fp8")]
     for k, c in cases:
         path = bench.traffic_file(k, c)
         assert os.path.exists(path), path
