@@ -138,7 +138,7 @@ def filter_binding(info, w):
     return out
 
 
-def row_classes(info, g, tiled_on, nsp=128):
+def row_classes(info, g, tiled_on, nsp=128, lists=True):
     """Rows of each backward class, by the library's rule: a row with a
     gradient (target in its support, valid metadata, nonzero upstream
     gradient) is sparse when its support holds at most nsp tokens, dense
@@ -149,7 +149,7 @@ def row_classes(info, g, tiled_on, nsp=128):
     fl = info["flags"]
     active = ((fl & 1) != 0) & ((fl & 4) != 0) & (g != 0)
     dense = active & (((fl & 2) == 0) | (info["n"] > nsp))
-    listed = active & ~dense & ((fl & 32) != 0)
+    listed = active & ~dense & ((fl & 32) != 0) & lists
     tiled = active & ~dense & ~listed & (info["ntile"] > 0) & tiled_on
     return {"dense": int(dense.sum()), "sparse": int((active & ~dense & ~listed & ~tiled).sum()),
             "listed": int(listed.sum()), "tiled": int(tiled.sum()), "empty": int((~active).sum()),
@@ -514,6 +514,9 @@ def main():
     ap.add_argument("--pre-gemm-temperature", type=float, default=None,
                     help="one scalar temperature applied to the hidden states before the projection, in place "
                          "of the workload's per-row temperature applied after it")
+    ap.add_argument("--recompute-all", action="store_true",
+                    help="the backward recomputes every row's keys (the recompute closed-form VJP for every row), "
+                         "ignoring the support lists the forward keeps in the state")
     args = ap.parse_args()
     if args.fused and args.policy_loss == "none":
         print("--fused needs --policy-loss cispo|clip", file=sys.stderr)
@@ -573,7 +576,8 @@ def main():
     ts = args.pre_gemm_temperature
     prob, keep = binding.make_problem(h, W, target, None if ts is not None else meta["temperature"], meta["top_k"],
                                       meta["top_p"], meta["min_p"], args.chunk_rows, args.vocab_slice,
-                                      pre_gemm_temperature=ts, lane=args.lane, weight_scale=w_scale)
+                                      pre_gemm_temperature=ts, lane=args.lane, weight_scale=w_scale,
+                                      recompute_all=args.recompute_all)
     fwd_b, bwd_b = binding.workspace_bytes(prob)
     ws_f = torch.empty(fwd_b, dtype=torch.uint8, device=dev)
     ws_b = torch.empty(bwd_b, dtype=torch.uint8, device=dev)
@@ -696,7 +700,7 @@ def main():
     # listed tiles, or in the whole-vocabulary recompute
     classed = dt == torch.bfloat16 and (not args.fused or fused_classed)
     tiled_on = classed and -(-V // 256) <= 65535 and T * H * (1 if fp8 else 2) < 2 ** 31 - 1 - 2 ** 22
-    classes = row_classes(binding.decode_state(state), g.cpu().numpy(), tiled_on)
+    classes = row_classes(binding.decode_state(state), g.cpu().numpy(), tiled_on, lists=not args.recompute_all)
     t_full = classes["dense"] + classes["sparse"] if classed else T
     t_dense = classes["dense"] if classed else T
     # the tile recompute forms 256 keys of H-long products per (row, tile) pair
@@ -778,7 +782,9 @@ def main():
                                + ("; fp8 lane: e4m3 weight with per-row scales, hidden rows quantized per row, "
                                   "logits and recompute on fp8 matrix cores, gradient products bf16" if fp8 else "")
                                + (f"; scalar pre-GEMM temperature {ts} in place of the per-row one"
-                                  if ts is not None else ""),
+                                  if ts is not None else "")
+                               + ("; every row's keys recomputed (support lists unused)" if args.recompute_all
+                                  else ""),
                    "T": T, "H": H, "V": V, "chunk_rows": C, "vocab_slice": Vs},
         "mfma_peak_frac": t_at_peak / (ms_step * 1e-3),
         "mfma_flop_per_step": flop_step,

@@ -120,6 +120,15 @@ typedef enum {
                                     a bf16 tensor).  Gradients treat both roundings as
                                     identity: q comes from the bf16 keys.  Without a
                                     bf16 hidden/weight: STCE_E_UNSUPPORTED. */
+#define STCE_PROBLEM_RECOMPUTE_ALL 8 /* the backward recomputes the keys of every row
+                                        with a gradient, as xorl pull request 74's
+                                        recompute closed-form VJP ("What this PR does"
+                                        item 2) does, ignoring the support lists of
+                                        the state (see STCE_STATE_BYTES_PER_ROW); the
+                                        gradients are the same bit for bit when every
+                                        listed row has a tile list (the rows then keep
+                                        their places), else equal up to fp32 summation
+                                        order.  No effect on the forward. */
 
 /* Bytes of per-row state stce_forward writes and stce_backward reads.  A
  * state of T rows holds T 32-byte records (stce_row_info, in row order), then

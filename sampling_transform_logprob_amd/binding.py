@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libstce.so")
 STATUS_NONE = (1 << 63) - 1
 FIELDS = {1: "temperature", 2: "top_k", 3: "top_p", 4: "min_p", 5: "target"}
 FLAG_VALID, FLAG_FILTERED, FLAG_IN_SUPPORT, FLAG_IGNORED, FLAG_LISTED = 1, 2, 4, 8, 32
-PROBLEM_IGNORE_INDEX, PROBLEM_PRE_GEMM_TEMPERATURE, PROBLEM_BF16_LANE = 1, 2, 4
+PROBLEM_IGNORE_INDEX, PROBLEM_PRE_GEMM_TEMPERATURE, PROBLEM_BF16_LANE, PROBLEM_RECOMPUTE_ALL = 1, 2, 4, 8
 LANES = {"fp32": 0, "bf16": PROBLEM_BF16_LANE}
 # a 32-byte record, then (after all T records) a 64-byte tile list, then a
 # support list of NSP (token id, key) pairs
@@ -164,7 +164,7 @@ def _meta(name, t, T, dtype, device):
 def make_problem(hidden, weight, target, temperature=None, top_k=None, top_p=None, min_p=None,
                  chunk_rows: int = 0, vocab_slice: int = 0, ignore_index: Optional[int] = None,
                  pre_gemm_temperature: Optional[float] = None, lane: str = "fp32",
-                 weight_scale: Optional[torch.Tensor] = None):
+                 weight_scale: Optional[torch.Tensor] = None, recompute_all: bool = False):
     """Checked ``stce_problem`` plus the tensors it points into (kept alive).
 
     ``temperature`` is the per-row tensor applied to the logits after the
@@ -216,6 +216,8 @@ def make_problem(hidden, weight, target, temperature=None, top_k=None, top_p=Non
     flags = (0 if ignore_index is None else PROBLEM_IGNORE_INDEX) | LANES[lane]
     if pre_gemm_temperature is not None:
         flags |= PROBLEM_PRE_GEMM_TEMPERATURE
+    if recompute_all:
+        flags |= PROBLEM_RECOMPUTE_ALL
     prob = Problem(T, H, V, dt, flags, *[t.data_ptr() if t is not None else None for t in keep], chunk_rows,
                    vocab_slice, 0 if ignore_index is None else int(ignore_index),
                    0.0 if pre_gemm_temperature is None else float(pre_gemm_temperature),
@@ -309,11 +311,13 @@ def backward(hidden, weight, target, state, grad_logprob, temperature=None, top_
              grad_weight: Optional[torch.Tensor] = None, accumulate_grad_weight: bool = False,
              vocab_slice: int = 0, workspace: Optional[torch.Tensor] = None, ignore_index: Optional[int] = None,
              pre_gemm_temperature: Optional[float] = None, lane: str = "fp32",
-             weight_scale: Optional[torch.Tensor] = None):
-    """(grad_hidden [T, H] in hidden's dtype, grad_weight [V, H] fp32)."""
+             weight_scale: Optional[torch.Tensor] = None, recompute_all: bool = False):
+    """(grad_hidden [T, H] in hidden's dtype, grad_weight [V, H] fp32).
+    ``recompute_all`` recomputes every row's keys, ignoring the support
+    lists the state holds."""
     prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, 0, vocab_slice,
                               ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane,
-                              weight_scale=weight_scale)
+                              weight_scale=weight_scale, recompute_all=recompute_all)
     T, H, V = prob.T, prob.H, prob.V
     dev = hidden.device
     if grad_logprob.shape != (T,) or grad_logprob.dtype != torch.float32 or grad_logprob.device != dev:

@@ -132,7 +132,8 @@ size_t hs_bytes(const stce_problem* p) {
 
 stce_status check_shapes(const stce_problem* p) {
   if (!p) return fail(STCE_E_ARG, "problem is NULL");
-  if (p->flags & ~(STCE_PROBLEM_IGNORE_INDEX | STCE_PROBLEM_PRE_GEMM_TEMPERATURE | STCE_PROBLEM_BF16_LANE))
+  if (p->flags & ~(STCE_PROBLEM_IGNORE_INDEX | STCE_PROBLEM_PRE_GEMM_TEMPERATURE | STCE_PROBLEM_BF16_LANE |
+                   STCE_PROBLEM_RECOMPUTE_ALL))
     return fail(STCE_E_ARG, "problem.flags=%d has unknown bits", (int)p->flags);
   if (pre_gemm(p) && !(__builtin_isfinite(p->pre_gemm_temperature) && p->pre_gemm_temperature > 0.0f))
     return fail(STCE_E_ARG, "pre_gemm_temperature=%g must be finite and > 0", (double)p->pre_gemm_temperature);
@@ -733,8 +734,9 @@ stce_status backward_classed(const stce_problem* p, const Layout& L, const float
   SpEntry* list = at<SpEntry>(ws, L.b_list);
   const bool want_w = grad_weight && !keys_out;
   const RowTiles* tl = tiled(p) ? state_tiles((void*)state, p->T, p->V) : nullptr;
-  if ((e = launch_grad_classes((const RowState*)state, tl, grad_logprob, p->T, at<int>(ws, L.b_blk), cnt, perm,
-                               rowcnt, st)))
+  const int use_lists = (p->flags & STCE_PROBLEM_RECOMPUTE_ALL) ? 0 : 1;
+  if ((e = launch_grad_classes((const RowState*)state, tl, grad_logprob, p->T, use_lists, at<int>(ws, L.b_blk), cnt,
+                               perm, rowcnt, st)))
     return hip_fail(e, "row classes");
   uint8_t* h8_perm = fp8(p) ? at<uint8_t>(ws, L.b_h8) : nullptr;
   float* ha = fp8(p) ? at<float>(ws, L.b_ha) : nullptr;
@@ -745,7 +747,7 @@ stce_status backward_classed(const stce_problem* p, const Layout& L, const float
   if (e) return hip_fail(e, "gather hidden rows");
   if (want_w && (e = launch_fill_i32(cntj, p->V, 0, st))) return hip_fail(e, "clear counts");
   // the listed rows' entries from the support lists (no recompute)
-  if (!keys_out && (e = launch_listed_entries(perm, cnt, (const RowState*)state, state_support((void*)state, p->T),
+  if (use_lists && !keys_out && (e = launch_listed_entries(perm, cnt, (const RowState*)state, state_support((void*)state, p->T),
                                               grad_logprob, p->temperature, p->target, p->V, rowcnt, list,
                                               want_w ? cntj : nullptr, p->T, st)))
     return hip_fail(e, "listed rows' entries");

@@ -138,10 +138,12 @@ hipError_t launch_bwd_slice(const BwdSliceArgs& a, hipStream_t s);
 // Classification: counts of the classes into *cnt, the permutation perm
 // (permuted position -> row: dense rows, then sparse, listed, tiled and
 // empty ones, each in row order) and a cleared entry counter per position.
-// tl: the rows' tile lists (null: no row is tiled).  blk: scratch of
+// tl: the rows' tile lists (null: no row is tiled); use_lists 0: no row is
+// listed (their support lists are ignored).  blk: scratch of
 // grad_class_blk_ints(T) ints.
 size_t grad_class_blk_ints(int64_t T);
-hipError_t launch_grad_classes(const RowState* st, const RowTiles* tl, const float* g, int64_t T, int* blk,
+hipError_t launch_grad_classes(const RowState* st, const RowTiles* tl, const float* g, int64_t T, int use_lists,
+                               int* blk,
                                GradCounts* cnt, int* perm, int* rowcnt, hipStream_t s);
 
 // The listed rows' dz entries (positions [full, listed)) from the support

@@ -36,11 +36,12 @@ namespace {
 
 constexpr int CB = 1024;  // rows per classification block (256 threads x 4)
 
-// ntile: the row's tile-list length (0: none, or tile recompute off)
-__device__ inline int grad_class(const RowState& rs, float g, int ntile) {
+// ntile: the row's tile-list length (0: none, or tile recompute off);
+// lists 0: the row's support list is not used
+__device__ inline int grad_class(const RowState& rs, float g, int ntile, int lists) {
   if ((rs.flags & (ROW_VALID | ROW_IN_SUPPORT)) != (ROW_VALID | ROW_IN_SUPPORT) || g == 0.f) return GRAD_EMPTY;
   if (!(rs.flags & ROW_FILTERED) || rs.n > NSP) return GRAD_DENSE;
-  if (rs.flags & ROW_LISTED) return GRAD_LISTED;
+  if (lists && (rs.flags & ROW_LISTED)) return GRAD_LISTED;
   return ntile > 0 ? GRAD_TILED : GRAD_SPARSE;
 }
 
@@ -63,13 +64,13 @@ __device__ inline int block_incl_scan(int v, int* scratch) {
 
 // Per block of CB rows: how many rows of each class.
 __global__ __launch_bounds__(256) void class_count_kernel(const RowState* st, const RowTiles* tl, const float* g,
-                                                          int64_t T, int* blk) {
+                                                          int64_t T, int lists, int* blk) {
   __shared__ int scr[4];
   const int64_t r0 = (int64_t)blockIdx.x * CB + threadIdx.x * 4;
   int c[GRAD_CLASSES] = {};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    if (r0 + i < T) ++c[grad_class(st[r0 + i], g[r0 + i], tl ? tl[r0 + i].n : 0)];
+    if (r0 + i < T) ++c[grad_class(st[r0 + i], g[r0 + i], tl ? tl[r0 + i].n : 0, lists)];
 #pragma unroll
   for (int k = 0; k < GRAD_CLASSES; ++k) {
     const int s = block_incl_scan(c[k], scr);
@@ -127,15 +128,15 @@ __global__ __launch_bounds__(1024) void class_scan_kernel(int* blk, int nblk, Gr
 // then empty; row order within a class) and clears the position's entry
 // counter.
 __global__ __launch_bounds__(256) void class_place_kernel(const RowState* st, const RowTiles* tl, const float* g,
-                                                          int64_t T, const int* blk, const GradCounts* cnt, int* perm,
-                                                          int* rowcnt) {
+                                                          int64_t T, int lists, const int* blk, const GradCounts* cnt,
+                                                          int* perm, int* rowcnt) {
   __shared__ int scr[4];
   const int64_t r0 = (int64_t)blockIdx.x * CB + threadIdx.x * 4;
   int cls[4];
   int c[GRAD_CLASSES] = {};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    cls[i] = r0 + i < T ? grad_class(st[r0 + i], g[r0 + i], tl ? tl[r0 + i].n : 0) : -1;
+    cls[i] = r0 + i < T ? grad_class(st[r0 + i], g[r0 + i], tl ? tl[r0 + i].n : 0, lists) : -1;
     if (cls[i] >= 0) ++c[cls[i]];
   }
   const GradCounts n = *cnt;
@@ -799,13 +800,14 @@ hipError_t launch_tile_lists(const TileListArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_grad_classes(const RowState* st, const RowTiles* tl, const float* g, int64_t T, int* blk,
-                               GradCounts* cnt, int* perm, int* rowcnt, hipStream_t s) {
+hipError_t launch_grad_classes(const RowState* st, const RowTiles* tl, const float* g, int64_t T, int use_lists,
+                               int* blk, GradCounts* cnt, int* perm, int* rowcnt, hipStream_t s) {
   ProfScope ps(KIND_CLASSIFY, s);
   const unsigned nb = (unsigned)ceil_div(T, CB);
-  hipLaunchKernelGGL(class_count_kernel, dim3(nb), dim3(256), 0, s, st, tl, g, T, blk);
+  hipLaunchKernelGGL(class_count_kernel, dim3(nb), dim3(256), 0, s, st, tl, g, T, use_lists, blk);
   hipLaunchKernelGGL(class_scan_kernel, dim3(1), dim3(1024), 0, s, blk, (int)nb, cnt);
-  hipLaunchKernelGGL(class_place_kernel, dim3(nb), dim3(256), 0, s, st, tl, g, T, blk, cnt, perm, rowcnt);
+  hipLaunchKernelGGL(class_place_kernel, dim3(nb), dim3(256), 0, s, st, tl, g, T, use_lists, blk, cnt, perm,
+                     rowcnt);
   return hipGetLastError();
 }
 

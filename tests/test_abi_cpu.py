@@ -116,7 +116,7 @@ def test_fp8_lane_host_checks(lib):
 
 
 @pytest.mark.parametrize("kw,msg", [
-    (dict(T=0), "T=0"), (dict(H=12), "H=12"), (dict(V=0), "V=0"), (dict(flags=8), "flags"),
+    (dict(T=0), "T=0"), (dict(H=12), "H=12"), (dict(V=0), "V=0"), (dict(flags=16), "flags"),
     (dict(flags=1, ignore_index=5), "ignore_index=5"),
     (dict(chunk_rows=-1), "chunk_rows"),
     # 512 * round_up(T, 64) bytes must fit a 32-bit buffer record count
@@ -125,6 +125,13 @@ def test_fp8_lane_host_checks(lib):
 def test_bad_shapes_are_rejected(lib, kw, msg):
     with pytest.raises(binding.StceError, match=msg):
         binding.workspace_bytes(_prob(**kw))
+
+
+def test_recompute_all_flag_is_accepted_and_changes_no_size(lib):
+    """The flag that makes the backward recompute every row changes neither
+    workspace (the recompute's buffers exist for every problem)."""
+    base = binding.workspace_bytes(_prob(T=1000, H=64, V=5000))
+    assert binding.workspace_bytes(_prob(T=1000, H=64, V=5000, flags=binding.PROBLEM_RECOMPUTE_ALL)) == base
 
 
 def test_largest_row_count_is_accepted(lib):

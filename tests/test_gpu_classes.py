@@ -157,6 +157,9 @@ def test_listed_tiled_and_whole_vocabulary_entries_agree(name, T, V):
     gh, gw = binding.backward(G["h"], G["W"], G["target"], st, g, **meta_of(G), **ws, vocab_slice=8192)
     gh1, gw1 = binding.backward(G["h"], G["W"], G["target"], st_tiled, g, **meta_of(G), **ws, vocab_slice=8192)
     gh0, gw0 = binding.backward(G["h"], G["W"], G["target"], st_full, g, **meta_of(G), **ws, vocab_slice=8192)
+    # the problem flag that ignores the lists: the listed flags cleared
+    ghr, gwr = binding.backward(G["h"], G["W"], G["target"], st, g, **meta_of(G), **ws, vocab_slice=8192,
+                                recompute_all=True)
     keys = binding.scaled_logits(G["h"], G["W"], G["temperature"], **ws).cpu().numpy()
     torch.cuda.synchronize()
     info = binding.decode_state(st)
@@ -169,6 +172,7 @@ def test_listed_tiled_and_whole_vocabulary_entries_agree(name, T, V):
         f"{int(info['ntile'][tiled].sum())} (row, tile) pairs of {T * (-(-V // 256))}")
     assert listed.sum() > (T // 3 if name != "ties" else 0) and tiled.sum() > (T // 3 if name != "ties" else 0)
     assert torch.equal(gh, gh1) and torch.equal(gh, gh0)
+    assert torch.equal(ghr, gh1) and torch.equal(gwr, gw1)
     fl = info["flags"]
     active = ((fl & binding.FLAG_VALID) != 0) & ((fl & binding.FLAG_IN_SUPPORT) != 0) & (gc != 0)
     sparse = active & ((fl & binding.FLAG_FILTERED) != 0) & (info["n"] <= NSP)
