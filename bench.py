@@ -657,6 +657,30 @@ def main():
     ms_step = t_start.elapsed_time(t_end) / args.steps
     per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
 
+    # the same step with every row's keys recomputed (the support lists the
+    # state holds unused): the recompute closed-form VJP for every row, timed
+    # apart so that the line carries both
+    recompute_all = None
+    if not args.fused and not args.recompute_all and dt == torch.bfloat16:
+        prob_r, keep_r = binding.make_problem(h, W, target, None if ts is not None else meta["temperature"],
+                                              meta["top_k"], meta["top_p"], meta["min_p"], args.chunk_rows,
+                                              args.vocab_slice, pre_gemm_temperature=ts, lane=args.lane,
+                                              weight_scale=w_scale, recompute_all=True)
+        P_main, P = P, ctypes.byref(prob_r)
+        n_r = max(1, min(args.steps, 10))
+        step()
+        r_start, r_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        r_start.record()
+        for _ in range(n_r):
+            step()
+        r_end.record()
+        torch.cuda.synchronize()
+        P = P_main
+        ms_r = r_start.elapsed_time(r_end) / n_r
+        recompute_all = {"ms_per_step": ms_r, "value": T / (ms_r * 1e-3), "steps": n_r}
+        log(f"[bench] with every row recomputed: {ms_r:.3f} ms per step over {n_r} steps")
+
     # per-kernel figures: a separate pass with HIP events recorded around each
     # launch on its stream (stce_profile_attach)
     prof_steps = max(1, min(args.steps, args.profile_steps))
@@ -798,6 +822,7 @@ def main():
                      "traffic": read_traffic(dom, args.config)},
         "kernels": stats,
         "hbm_kernels": hbm_kernels,
+        "recompute_all": recompute_all,
         "targets_in_support": in_support,
         "binding_filter_rows": binds,
     }
