@@ -137,11 +137,10 @@ typedef enum {
  * support key, at most 31 of them (a count, then the tile indices in
  * increasing order; count 0 when there are more, on unfiltered rows, and when
  * the vocabulary has more than 65,535 tiles), then T 1024-byte support lists:
- * for a filtered row whose support of at most 128 tokens the selection holds
- * whole when it decides it (as for a top-k row decided from the projection's
- * candidates), its tokens as (int32 token id, fp32 key) pairs in decreasing
- * key order, increasing id among equal keys (flag bit 5 of the record then
- * set); zeros past the support and on every other row.  The backward forms a
+ * for a filtered row whose support has at most 128 tokens, its tokens as
+ * (int32 token id, fp32 key) pairs in decreasing key order, increasing id
+ * among equal keys (flag bit 5 of the record then set); zeros past the
+ * support and on every other row.  The backward forms a
  * listed row's dz from those keys, and recomputes the keys of a sparse row
  * with a tile list on its tiles only.  No part is of size [T, V]. */
 #define STCE_STATE_BYTES_PER_ROW 1120

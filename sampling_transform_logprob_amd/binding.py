@@ -478,7 +478,7 @@ def fused_policy_step(hidden, weight, target, advantages, old_logprob, temperatu
                       side: bool = False, chunk_rows: int = 0, ignore_index: Optional[int] = None,
                       check: bool = True, workspace: Optional[torch.Tensor] = None,
                       pre_gemm_temperature: Optional[float] = None, lane: str = "fp32",
-                      weight_scale: Optional[torch.Tensor] = None):
+                      weight_scale: Optional[torch.Tensor] = None, recompute_all: bool = False):
     """The fused head + policy-gradient step (dlogits formed in the forward's
     sweep from the chunk's keys).  Returns a dict with ``loss``, ``logprob``,
     ``ratio`` (fp32 [T]), ``state``, ``grad_hidden`` ([T, H], hidden's dtype,
@@ -489,7 +489,7 @@ def fused_policy_step(hidden, weight, target, advantages, old_logprob, temperatu
         raise ValueError(f"objective must be one of {tuple(PG_OBJECTIVES)}")
     prob, keep = make_problem(hidden, weight, target, temperature, top_k, top_p, min_p, chunk_rows,
                               ignore_index=ignore_index, pre_gemm_temperature=pre_gemm_temperature, lane=lane,
-                              weight_scale=weight_scale)
+                              weight_scale=weight_scale, recompute_all=recompute_all)
     T, H, V = prob.T, prob.H, prob.V
     dev = hidden.device
     adv = _meta("advantages", advantages, T, torch.float32, dev)

@@ -109,10 +109,11 @@ struct SpEntry {
 };
 
 // A filtered row's support of at most NSP tokens as (token id, key) pairs, in
-// decreasing key order (increasing id among equal keys), when the selection
-// holds all of it at its decision (no token ahead of its window, as for a
-// top-k row decided from its candidates); the row is then flagged ROW_LISTED
-// and the backward forms its dz entries from these keys, recomputing none.
+// decreasing key order (increasing id among equal keys): the selection's
+// window when it starts at the top of the order (a top-k row decided from
+// its candidates), else gathered from the row's stored keys.  The row is
+// then flagged ROW_LISTED and the backward forms its dz entries from these
+// keys, recomputing none.
 // Entries past the support, and every entry of other rows, are zero.  The
 // state holds T RowState records, then T RowTiles, then T support lists.
 struct RowSupport {

@@ -714,15 +714,42 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
     if (tid >= keep && tid < NTILE) rt->t[tid] = 0;
     if (tid == 0) rt->n = (uint16_t)keep;
   }
-  // The support with its keys, when the window holds all of it (no token
-  // ahead of it) and it has at most NSP tokens: the window's first n_loc
-  // tokens, already in decreasing (key, -id) order.
-  const bool listed = P.support && above == 0 && n_loc <= NSP;
+  // The support with its keys when it has at most NSP tokens: the window's
+  // first n_loc tokens, already in decreasing (key, -id) order, when no
+  // token lies ahead of the window; else (a row decided from a histogram,
+  // whose keys are stored) one membership pass gathers every token at or
+  // above the boundary into the window's space, and they are sorted.
+  const uint64_t bcomp = S.u.cand[n_loc - 1];  // the boundary: the last support token
+  const int n_sup = (int)above + n_loc;
+  bool listed = P.support && n_sup <= NSP && (above == 0 || !cand);
+  if (listed && above > 0) {
+    __syncthreads();  // (every read of the window is done)
+    if (tid == 0) S.cnt = 0;
+    __syncthreads();
+    for (int q = tid; q < nv4; q += ST) {
+      const f32x4 x = *(const f32x4*)(rp + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * q + e;
+        if (v < V) {
+          const uint64_t c = composite(order_key(x[e]), (uint32_t)v);
+          if (c >= bcomp) {
+            const int i = atomicAdd(&S.cnt, 1);
+            if (i < NSP) S.u.cand[i] = c;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const int got = S.cnt;
+    bitonic_desc(S.u.cand, min(got, NSP));
+    listed = got == n_sup;  // (always, as the boundary is a composite of the row's own keys)
+  }
   if (P.support) {
     SpEntry* sl = P.support[orow].e;
     for (int i = tid; i < NSP; i += ST) {
       SpEntry e{0, 0.0f};
-      if (listed && i < n_loc) {
+      if (listed && i < n_sup) {
         const uint64_t c = S.u.cand[i];
         e = SpEntry{(int32_t)comp_id(c), key_value(comp_key(c))};
       }
@@ -730,10 +757,10 @@ __global__ __launch_bounds__(ST, 5) void select_kernel(SelParams P) {
     }
   }
   if (tid == 0) {
-    const uint64_t bc = S.u.cand[n_loc - 1];
+    const uint64_t bc = bcomp;
     rs.key_thr = comp_key(bc);
     rs.id_thr = (int32_t)comp_id(bc);
-    rs.n = (int32_t)(above + (uint32_t)n_loc);
+    rs.n = (int32_t)n_sup;
     const double lse_s = m64 + log(S.mass_s);
     rs.lse_s = (float)lse_s;
     const uint32_t ky = order_key(sy);

@@ -102,7 +102,8 @@ def test_fused_step_matches_oracle(name, T, V, objective, chunk):
     assert rl < 1e-3 and rh < GRAD_RTOL and rw < GRAD_RTOL
 
 
-def _unfused(G, A, old, objective, sc, ignore_index=None, side=False, gw0=None, meta=None, need_weight=True):
+def _unfused(G, A, old, objective, sc, ignore_index=None, side=False, gw0=None, meta=None, need_weight=True,
+             recompute_all=False):
     meta = meta_of(G) if meta is None else meta
     ws = G.get("weight_scale")
     r = binding.forward(G["h"], G["W"], G["target"], **meta, check=False, side=side,
@@ -112,7 +113,7 @@ def _unfused(G, A, old, objective, sc, ignore_index=None, side=False, gw0=None, 
     gw = None if gw0 is None else gw0.clone()
     gh, gw = binding.backward(G["h"], G["W"], G["target"], st, g, **meta, grad_weight=gw,
                               accumulate_grad_weight=gw0 is not None, ignore_index=ignore_index,
-                              weight_scale=ws, need_weight=need_weight)
+                              weight_scale=ws, need_weight=need_weight, recompute_all=recompute_all)
     out = dict(logprob=lp, state=st, loss=loss, ratio=ratio, grad_hidden=gh, grad_weight=gw)
     if side:
         out.update(r[2])
@@ -240,10 +241,10 @@ def _classed_case(name, T, V):
     every fifth row unfiltered (its support the whole vocabulary: dense),
     every seventh a top-p row of a wide support (over 128 tokens: dense),
     every eleventh a top-64 row, every thirteenth a top-120 row (more tokens
-    than the vocabulary has tiles, so decided from a histogram: its support
-    is not listed, and it is tiled, or sparse past 31 tiles), the rest top-k
-    rows (their supports listed); one row's target outside its support, one
-    invalid row."""
+    than the vocabulary has tiles, so decided from a histogram), the rest
+    top-k rows; one row's target outside its support, one invalid row.  The
+    small supports are listed in the state; with every row recomputed they
+    are tiled, or sparse past 31 tiles."""
     w = workloads.make(name, T=T)
     if V is not None and V < w["V"]:
         w["W"], w["V"] = w["W"][:V], V
@@ -294,16 +295,23 @@ def test_classed_fused_step_equals_the_unfused_sequence_bitwise(name, T, V, chun
     filt = live & ((fl & binding.FLAG_FILTERED) != 0)
     small = filt & (info["n"] <= 128)
     listed = small & ((fl & binding.FLAG_LISTED) != 0)
-    tiled = small & ~listed & (info["ntile"] > 0)
-    sparse = small & ~listed & (info["ntile"] == 0)
+    tiled = small & (info["ntile"] > 0)                  # (with every row recomputed)
+    sparse = small & (info["ntile"] == 0)
     say(f"classed fused vs unfused: {name} T={T} V={V} chunk={chunk or 'default'}: rows dense "
         f"{int((live & ~filt).sum() + (filt & (info['n'] > 128)).sum())}, listed {int(listed.sum())}, tiled "
         f"{int(tiled.sum())}, sparse {int(sparse.sum())}, no gradient {int((~live).sum())}")
-    assert (tiled | sparse).sum() > 0 and (live & ~filt).sum() > 0 and (~live).sum() >= 2
-    if name.startswith("headline"):                       # top-k rows decided from their candidates
-        assert listed.sum() > 0
+    assert np.array_equal(listed, small)                  # every small support is listed
+    assert listed.sum() > 0 and (live & ~filt).sum() > 0 and (~live).sum() >= 2
     for k in ("logprob", "state", "loss", "ratio", "grad_hidden", "grad_weight"):
         assert _same(f[k], u[k]), k
+    # every row recomputed (tile or whole-vocabulary recompute) in both
+    fr = binding.fused_policy_step(G["h"], G["W"], G["target"], A, old, **meta_of(G), objective="clip",
+                                   eps_low=EL, eps_high=EH, scale=sc, chunk_rows=chunk, check=False,
+                                   weight_scale=ws, recompute_all=True)
+    ur = _unfused(G, A, old, "clip", sc, recompute_all=True)
+    for k in ("grad_hidden", "grad_weight"):
+        assert _same(fr[k], ur[k]), k
+    assert _same(fr["grad_hidden"], u["grad_hidden"])    # a row's dH sums its entries in vocabulary order
     # a frozen head: the same hidden gradient; weight-gradient accumulation:
     # the same sum onto the same start
     fz = binding.fused_policy_step(G["h"], G["W"], G["target"], A, old, **meta_of(G), objective="clip",
