@@ -504,8 +504,27 @@ struct MainFp8T {
         else
           fa[(i + 3) & 3] = rdA(nx, i + 3 - ACC_I);
         mma(fa[i & 3], fb[sg], i);
-        if (i == 4) __builtin_amdgcn_sched_barrier(0);
+        if (i == 4) {
+          // blocks 0..4: one A read (16 bytes) after every two MFMAs, so
+          // no read sits next to the MFMA that consumes it
+#pragma unroll
+          for (int q = 0; q < 10; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+      // blocks 5..7: the next tile's 14 fragment reads and the 8 loads of
+      // tile kt + 2 between the 12 MFMAs
+#pragma unroll
+      for (int q = 0; q < 12; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (q < 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (q < 2 * LPW) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global->LDS load
+      }
+      __builtin_amdgcn_sched_barrier(0);
     };
     issue(0, 0);
     issue(1, 1);
@@ -513,8 +532,14 @@ struct MainFp8T {
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) fb[0][j] = frag(S0 + offB + j * 16 * ROWB);
+    // (in the loop's order, B then A 0, 1, 2, so that the wait at the
+    // loop's head is for B and A fragment 0 only)
 #pragma unroll
-    for (int i = 0; i < 3; ++i) fa[i] = rdA(S0, i);
+    for (int i = 0; i < 3; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      fa[i] = rdA(S0, i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // an even number of k-tiles (an odd count gets one all-zero tile) so that
     // every read and load names its stage at compile time; the last pair's
     // loads and next-tile reads fall past K or read a stage nobody uses
@@ -620,6 +645,25 @@ struct DynLimits {
   const int* k_lim = nullptr;
 };
 
+// Holds every 32-bit word of a kernel argument in scalar registers from this
+// point on, so the argument's scalar loads have completed here.  Scalar-cache
+// loads share the LDS wait counter but complete out of order: while one is in
+// flight, a wait for an LDS read can only be a wait for everything.  With the
+// epilogue's argument loads still in flight at the main loop, the compiler
+// makes the loop's first fragment wait (at every iteration) a wait for all of
+// the previous tile's reads.
+template <int N>
+struct ArgWords {
+  uint32_t w[N];
+};
+template <class T>
+__device__ inline void hold_in_sgprs(const T& x) {
+  static_assert(sizeof(T) % 4 == 0, "argument of whole words");
+  const auto a = __builtin_bit_cast(ArgWords<sizeof(T) / 4>, x);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) asm volatile("" ::"s"(a.w[i]));
+}
+
 template <class Main, class Epi>
 __global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(Main mainloop, Epi epi, TileMap map, DynLimits dyn) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -636,6 +680,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_kernel(Main mainloop, Epi ep
   for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) acc[i][j] = f32x4{};
+  hold_in_sgprs(epi);
   mainloop.run(acc, tm * GM, tn * GN, smem);
   epi(acc, tm * GM, tn * GN, Main::epilogue_lds(smem), Main::epilogue_lds1(smem));
 }
@@ -677,6 +722,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_worklist_kernel(Main mainloo
   for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
     for (int jj = 0; jj < ACC_J; ++jj) acc[i][jj] = f32x4{};
+  hold_in_sgprs(epi);
   mainloop.run(acc, j * GM, 0, nullptr);
   epi(acc, j * GM, 0, Main::epilogue_lds(nullptr), Main::epilogue_lds1(nullptr));
 }

@@ -405,6 +405,7 @@ __global__ __launch_bounds__(GTHREADS, 1) void gemm_splitk_kernel(Main mainloop,
   for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
     for (int j = 0; j < ACC_J; ++j) acc[i][j] = f32x4{};
+  hold_in_sgprs(ep);
   mn.run(acc, tm * GM, tn * GN, smem);
   ep(acc, tm * GM, tn * GN, Main::epilogue_lds(smem), Main::epilogue_lds1(smem));
 }
