@@ -292,8 +292,11 @@ def kernel_stats_summary(args):
     for label, (calls, ns) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
         avg = f"{ns / calls / 1e6:.3f}" if calls and "torch" not in label else ""
         lines.append(f"| {label} | {calls} | {avg} | {ns / 1e6:.2f} | {100 * ns / total:.2f} |")
-    lines += ["", "The trace covers the warm-up step, the 3 timed steps and the 3 steps of the per-kernel pass "
-              "(7 steps). Averages include the warm-up step's launches, taken while the clock ramps up.", ""]
+    n_steps = agg.get("validate metadata", (0, 0))[0]  # one metadata check per step
+    lines += ["", f"The trace covers {n_steps} steps: the warm-up step, the 3 timed steps, the step with every "
+              "row's keys recomputed (one untimed step and 3 timed ones; not run with --recompute-all or "
+              "--fused) and the 3 steps of the per-kernel pass. Averages include the warm-up step's launches, "
+              "taken while the clock ramps up.", ""]
     # the projection kernel also runs each chunk's re-projection (side stream,
     # usually no row): split its launches by stream from the kernel trace
     traces = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
