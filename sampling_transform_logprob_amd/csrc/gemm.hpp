@@ -483,7 +483,10 @@ struct MainFp8T {
     auto mma = [&](const i32x8& a, const i32x8 (&b)[ACC_J], int i) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < ACC_J; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[j], acc[i][j], 0, 0, 0, 127, 0, 127);
+        // (constant zero scale operands: the compiler emits the unscaled
+        // v_mfma_f32_16x16x128_f8f6f4, plain e4m3 products, 1% faster here
+        // than the scaled form with unit scales)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
     };
     auto tile = [&](auto sg_c, int kt) __attribute__((always_inline)) {
       constexpr int sg = decltype(sg_c)::value;
