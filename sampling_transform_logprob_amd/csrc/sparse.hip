@@ -663,8 +663,10 @@ __global__ __launch_bounds__(256) void sparse_dw_wave_kernel(const int* off, con
         for (int k = 0; k < 8; ++k) acc[k] = 0.f;
       }
       wave_ordered_sum_split(ne, idx, v, h, H, ia ? ca : 0, ib ? cb : 0, acc);
-      if (ia) *(f32x4*)(row + ca) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      if (ib) *(f32x4*)(row + cb) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+      // (nontemporal: nothing here reads dW again, and the stream of it
+      // should not displace the hidden rows the gathers hit in the cache)
+      if (ia) __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, (f32x4*)(row + ca));
+      if (ib) __builtin_nontemporal_store(f32x4{acc[4], acc[5], acc[6], acc[7]}, (f32x4*)(row + cb));
     }
   }
 }
@@ -700,10 +702,10 @@ __global__ __launch_bounds__(256) void sparse_dh_wave_kernel(const int* perm, co
         bf16x8 o;
 #pragma unroll
         for (int k = 0; k < 8; ++k) o[k] = (bf16)acc[k];
-        *(bf16x8*)(out + c0) = o;
+        __builtin_nontemporal_store(o, (bf16x8*)(out + c0));  // (written once, read by the caller)
       } else {
-        *(f32x4*)(out + c0) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-        *(f32x4*)(out + c0 + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+        __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, (f32x4*)(out + c0));
+        __builtin_nontemporal_store(f32x4{acc[4], acc[5], acc[6], acc[7]}, (f32x4*)(out + c0 + 4));
       }
     }
   }
