@@ -150,13 +150,26 @@ __global__ __launch_bounds__(256) void fp8_quantize_rows_kernel(const bf16* h, i
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float a = mx > 0.0f ? mx / E4M3_MAX : 1.0f;
   if (threadIdx.x == 0) scale[t] = a;
+  // fl32(h / a) by the correction step of quot_fast where it is exact (the
+  // eight values and a inside its range; zeros, which would lose the sign
+  // of -0, and tiny or huge values take the IEEE division)
+  const float r = 1.0f / a;
+  const bool a_ok = a >= 0x1p-30f && a <= 0x1p+30f;
   uint8_t* qr = q + n * H;
   for (int64_t c = threadIdx.x * 8; c < H; c += 256 * 8) {
     const bf16x8 v = *(const bf16x8*)(hr + c);
+    float lo = STCE_INF, hi = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      lo = fminf(lo, __builtin_fabsf((float)v[k]));
+      hi = fmaxf(hi, __builtin_fabsf((float)v[k]));
+    }
+    const bool fast = a_ok && lo >= 0x1p-90f && hi <= 0x1p+90f;
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const float x = fminf(fmaxf((float)v[k] / a, -E4M3_MAX), E4M3_MAX);
+      const float hv = (float)v[k];
+      const float x = fminf(fmaxf(fast ? quot_fast(hv, a, r) : hv / a, -E4M3_MAX), E4M3_MAX);
       w[k >> 2] |= e4m3_encode(x) << (8 * (k & 3));
     }
     *(u32x2*)(qr + c) = u32x2{w[0], w[1]};
