@@ -289,12 +289,19 @@ stce_status stce_forward_with_side(const stce_problem *prob, float *logprob, voi
  * VJP of xorl pull request 74, "What this PR does" item 2 (nothing of size
  * [T, V] kept from the forward; exactly zero gradient for out-of-support
  * rows, item 4; weight gradients written once per vocabulary slice,
- * self-review pass).  Recomputes the logits of
- * every vocabulary slice bit-for-bit as the forward did, reads the support
- * from `state`, forms dz = g (1[j == y] - q) / T (zero on rows whose target
- * is out of support or whose metadata is invalid; with the scalar pre-GEMM
+ * self-review pass).  Reads the support from `state` and forms
+ * dz = g (1[j == y] - q) / T on it (zero on rows whose target is out of
+ * support or whose metadata is invalid; with the scalar pre-GEMM
  * temperature dz = g (1[j == y] - q) and the hidden gradient is divided by
- * Ts) and writes
+ * Ts).  The keys q comes from are the forward's, bit for bit: a row whose
+ * support the state lists takes them from that list, a row with a tile list
+ * recomputes them on those vocabulary tiles only, every other row with a
+ * gradient on every vocabulary slice (all rows with
+ * STCE_PROBLEM_RECOMPUTE_ALL); the recompute runs the forward's product
+ * main loop (same k order) and temperature step.  A filtered row whose
+ * support holds at most 128 tokens adds its dz entries to dH and dW as
+ * ordered sums; larger supports run the matrix-core products over their
+ * vocabulary-major dz.  Writes
  *   grad_hidden [T, H] in the hidden dtype, bf16 for the fp8 lane
  *                (overwritten; NULL = skip) and
  *   grad_weight [V, H] fp32 (overwritten, or added to when

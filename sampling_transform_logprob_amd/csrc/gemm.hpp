@@ -7,7 +7,7 @@
 //   weight grad  dW[v, :] = dz^T[v, :] . h[:, :]     (M = vocab, N = H, K = tokens; h MN-major)
 //   hidden grad  dH^T[:, t] = W^T[:, :] . dz^T[:, t] (M = H, N = tokens, K = vocab; dz^T MN-major,
 //                                                     W^T a transposed copy)
-// The fp32 main loop (plain fmas, small shapes) takes K-major operands only.
+// The fp32 main loop (16x16x4 fp32 matrix instruction) takes K-major operands only.
 //
 // Block tile 256 x 256, k-tile 64, 512 threads = 8 waves (2 per SIMD) in a
 // 2 (m) x 4 (n) grid, each wave owning a 128 x 64 sub-tile = 8 x 4 blocks of
@@ -562,13 +562,23 @@ using MainFp8 = MainFp8T<false>;
 using MainFp8G = MainFp8T<true>;
 
 // ---------------------------------------------------------------------------
-// fp32 main loop (plain fused multiply-adds, same accumulator layout).  Used
-// for fp32 operands, where shapes are small; each output element accumulates
-// its k terms in order with one fma each.
+// fp32 main loop (MFMA): fp32 operands, both K-major, on the 16x16x4 fp32
+// matrix instruction, same accumulator layout as the bf16 loop.  A k-slab of
+// BK = 16 columns goes through registers into LDS rows of 20 floats (80
+// bytes: 16-byte aligned, and the 16 rows of a fragment read fall on 16
+// distinct groups of four banks).  Lane l of a wave reads the four
+// consecutive columns 4 (l / 16) .. +4 of its fragment row with one 16-byte
+// read; matrix step s (s < 4) of the slab then multiplies column 4 g + s of
+// lane group g = l / 16, which the instruction takes as its k index g.  So an
+// output element sums its k terms four per instruction, in an order fixed by
+// k alone (every tile position, chunk and launch gives the same bits).
+// K is a multiple of 4; columns at or past K read as zeros, rows past M (N)
+// repeat the last row (their outputs are dropped by the epilogues).
 // ---------------------------------------------------------------------------
 struct MainF32 {
   static constexpr int BK = 16;
-  static constexpr int LDS_BYTES = 2 * GM * (BK + 1) * 4;
+  static constexpr int LDR = 20;  // floats per LDS row
+  static constexpr int LDS_BYTES = 2 * GM * LDR * 4;
   static constexpr int DYN_LDS = LDS_BYTES;  // dynamic LDS, shared with the epilogue
   static constexpr int EPI_LDS_MAX = 160 * 1024;
   // one epilogue LDS buffer, shared with the main loop (no second one)
@@ -593,39 +603,37 @@ struct MainF32 {
   __device__ inline void run(AccTile& acc, int m0, int n0, char* smem) const {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 2, wn = w & 3;
-    float* sa = (float*)smem;              // [256][17]
-    float* sb = sa + GM * (BK + 1);         // [256][17]
+    float* sa = (float*)smem;  // [256][LDR]
+    float* sb = sa + GM * LDR;  // [256][LDR]
     // thread t loads half a row: row t / 2, columns (t & 1) * 8 .. + 8
     const int lr = tid >> 1, lc = (tid & 1) * 8;
     const float* ga = A + (int64_t)min(m0 + lr, M - 1) * lda + lc;
     const float* gb = B + (int64_t)min(n0 + lr, N - 1) * ldb + lc;
+    // fragment reads: row lane % 16 of each 16-row block, columns 4 (lane / 16) .. +4
+    const float* fra = sa + (wm * 128 + (lane & 15)) * LDR + 4 * (lane >> 4);
+    const float* frb = sb + (wn * 64 + (lane & 15)) * LDR + 4 * (lane >> 4);
     for (int k0 = 0; k0 < K; k0 += BK) {
 #pragma unroll
       for (int c = 0; c < 8; c += 4) {
         const bool in = k0 + lc + c < K;
-        f32x4 va = in ? *(const f32x4*)(ga + k0 + c) : f32x4{0, 0, 0, 0};
-        f32x4 vb = in ? *(const f32x4*)(gb + k0 + c) : f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sa[lr * (BK + 1) + lc + c + e] = va[e];
-          sb[lr * (BK + 1) + lc + c + e] = vb[e];
-        }
+        const f32x4 va = in ? *(const f32x4*)(ga + k0 + c) : f32x4{0, 0, 0, 0};
+        const f32x4 vb = in ? *(const f32x4*)(gb + k0 + c) : f32x4{0, 0, 0, 0};
+        *(f32x4*)(sa + lr * LDR + lc + c) = va;
+        *(f32x4*)(sb + lr * LDR + lc + c) = vb;
       }
       __syncthreads();
-#pragma unroll 4
-      for (int kk = 0; kk < BK; ++kk) {
-        float bv[ACC_J];
+      f32x4 fa[ACC_I], fb[ACC_J];
 #pragma unroll
-        for (int j = 0; j < ACC_J; ++j) bv[j] = sb[acc_col(wn, j, lane & 15) * (BK + 1) + kk];
+      for (int i = 0; i < ACC_I; ++i) fa[i] = *(const f32x4*)(fra + i * 16 * LDR);
+#pragma unroll
+      for (int j = 0; j < ACC_J; ++j) fb[j] = *(const f32x4*)(frb + j * 16 * LDR);
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int i = 0; i < ACC_I; ++i)
 #pragma unroll
-          for (int r = 0; r < ACC_R; ++r) {
-            const float av = sa[acc_row(wm, i, r, lane >> 4) * (BK + 1) + kk];
-#pragma unroll
-            for (int j = 0; j < ACC_J; ++j) acc[i][j][r] = __builtin_fmaf(av, bv[j], acc[i][j][r]);
-          }
-      }
+          for (int j = 0; j < ACC_J; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[i][st], fb[j][st], acc[i][j], 0, 0, 0);
       __syncthreads();
     }
   }
