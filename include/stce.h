@@ -160,10 +160,19 @@ typedef struct stce_problem {
   const int32_t *top_k;  /* [T] >= 0; 0 or >= V = off; or NULL = off */
   const float *top_p;    /* [T] in (0, 1]; 1 = off; or NULL = off */
   const float *min_p;    /* [T] in [0, 1]; 0 = off; or NULL = off */
-  int64_t chunk_rows;    /* forward rows per chunk; 0 = library default: 256 n rows,
-                            n in 12 .. 16 the number of 256-token tiles whose
-                            projection best fills whole waves of the 256 compute
-                            units (3,840 at V = 151,936; 4,096 for most V) */
+  int64_t chunk_rows;    /* forward rows per chunk; 0 = library default: T when
+                            T <= 4,096, else two chunks (the first one's
+                            selection runs beside the second one's projection)
+                            of about T / 2 rows, a multiple of 256 chosen so
+                            that the two projections' last waves of tiles
+                            leave the fewest compute units idle (8,448 at
+                            T = 16,384, V = 151,936); more, smaller chunks when
+                            two chunk buffers of fp32 keys (4 C V bytes each)
+                            would exceed 12 GB.  The forward workspace holds
+                            two such buffers.  The fp8 lane: 256 n rows, n in
+                            12 .. 16 the number of 256-token tiles whose
+                            projection best fills whole waves of the 256
+                            compute units (3,840 at V = 151,936). */
   int64_t vocab_slice;   /* backward vocabulary columns per slice; 0 = default */
   int64_t ignore_index;  /* with STCE_PROBLEM_IGNORE_INDEX: a target equal to it
                             (a value outside [0, V), e.g. -100) marks an inactive

@@ -39,25 +39,65 @@ stce_status hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int kComputeUnits = 256;       // MI355X (gfx950): 8 XCDs of 32
-// Default rows per chunk: 256 times the number n of token tiles (16 .. 12)
-// whose projection, V/256 x n output tiles of 256 x 256, best fills whole
-// waves of one workgroup per compute unit (a chunk's last wave otherwise
-// leaves most of the chip idle); a smaller n must fill them half a percent
-// better to be taken.  At V = 151,936 (594 vocabulary tiles) 16 token tiles
-// make 37.1 waves and 15 make 34.8: 3,840 rows.
-int64_t default_chunk(int64_t V) {
-  const int64_t mt = (V + 255) / 256;
-  int64_t best = 16;
-  double best_fill = 0.0;
-  for (int64_t nt = 16; nt >= 12; --nt) {
-    const int64_t tiles = mt * nt;
-    const double fill = (double)tiles / (double)((tiles + kComputeUnits - 1) / kComputeUnits * kComputeUnits);
-    if (fill > best_fill + 0.005) {
-      best_fill = fill;
-      best = nt;
+// Bytes the default chunking lets the two chunk buffers' fp32 keys take.
+constexpr double kChunkBudgetBytes = 12e9;
+// Idle fraction of the last wave of a projection over V x n tiles of
+// 256 x 256 (one workgroup per compute unit).
+double tail_waste(int64_t V, int64_t n) {
+  const int64_t tiles = ((V + 255) / 256) * n;
+  return (double)((tiles + kComputeUnits - 1) / kComputeUnits * kComputeUnits - tiles) / kComputeUnits;
+}
+// Default rows per chunk.  At most 4,096 rows: one chunk.  Otherwise two:
+// the first chunk's selection runs on the side stream beside the second's
+// projection, the second's after it.  Every further chunk adds a launch
+// tail and a selection beside a projection, which cost more than the
+// larger exposed selection saves (T = 16,384, V = 151,936, median step,
+// interleaved on one box: five chunks 23.34-23.37 ms, three 23.08-23.25,
+// two 22.69-22.73; on another box two 22.87-22.96, one 23.58-23.61).  The
+// split is 256 n1 + 256 n2 rows, n1 the half of the token tiles or up to two
+// more, with the least idle compute in the two launches' last waves.  When
+// the two buffers' keys would exceed kChunkBudgetBytes, more and smaller
+// chunks.  The fp8 lane's projection runs twice as fast while its selection
+// does not, so the selection it leaves exposed weighs more there: it keeps
+// 256 n rows, n in 12 .. 16 the token-tile count whose projection best fills
+// whole waves (a smaller n must fill them half a percent better to be
+// taken): at V = 151,936, 3,840 rows, 14.55 against 14.69 ms per step for
+// two chunks (interleaved, one box).
+int64_t default_chunk(int64_t T, int64_t V, bool fp8_lane) {
+  if (fp8_lane) {
+    int64_t best = 16;
+    double best_fill = 0.0;
+    for (int64_t nt = 16; nt >= 12; --nt) {
+      const int64_t tiles = ((V + 255) / 256) * nt;
+      const double fill = (double)tiles / (double)((tiles + kComputeUnits - 1) / kComputeUnits * kComputeUnits);
+      if (fill > best_fill + 0.005) {
+        best_fill = fill;
+        best = nt;
+      }
     }
+    return best * 256;
   }
-  return best * 256;
+  if (T <= 4096) return T;
+  const double ld4 = 4.0 * (double)((V + 3) / 4 * 4);
+  const int64_t nt = (T + 255) / 256;
+  if (2.0 * ld4 * 256.0 * (double)((nt + 1) / 2) <= kChunkBudgetBytes) {
+    int64_t best = (nt + 1) / 2;
+    double best_w = 2.0;
+    for (int64_t n1 = (nt + 1) / 2; n1 < nt && n1 <= (nt + 1) / 2 + 2; ++n1) {
+      if (2.0 * ld4 * 256.0 * (double)n1 > kChunkBudgetBytes) break;
+      const double w = tail_waste(V, n1) + tail_waste(V, nt - n1);
+      if (w < best_w - 1e-9) {
+        best_w = w;
+        best = n1;
+      }
+    }
+    return best * 256;
+  }
+  for (int64_t n = 3;; ++n) {
+    const int64_t C = (T + n - 1) / n;
+    const int64_t C256 = (C + 255) / 256 * 256;
+    if (2.0 * ld4 * (double)C256 <= kChunkBudgetBytes || C256 <= 256) return C256;
+  }
 }
 // Default backward slice: the widest (multiple of 256) whose dz (T x V_s
 // elements for bf16 operands; twice that for fp32, which also keeps it
@@ -167,7 +207,7 @@ Layout plan(const stce_problem* p, bool single_buffer = false) {
   Layout L{};
   const int64_t T = p->T, V = p->V, H = p->H;
   const size_t es = elt_size(p->dtype);
-  L.C = p->chunk_rows > 0 ? p->chunk_rows : default_chunk(p->V);
+  L.C = p->chunk_rows > 0 ? p->chunk_rows : default_chunk(p->T, p->V, fp8(p));
   if (L.C > T) L.C = T;
   L.ldt = round_up(V, 4);
   L.ntv = ceil_div(V, VTILE);
@@ -686,7 +726,7 @@ stce_status stce_forward_noalloc(const stce_problem* p, float* logprob, void* st
   // chunk that does (single buffer, selection on the caller's stream)
   stce_problem q = *p;
   if (plan(&q, true).fwd > kNoallocScratchBytes) {
-    const int64_t dc = default_chunk(q.V);
+    const int64_t dc = default_chunk(q.T, q.V, fp8(&q));
     int64_t lo = 0, hi = q.chunk_rows > 0 ? q.chunk_rows : (q.T < dc ? q.T : dc);
     while (lo < hi) {  // largest C in [1, hi] whose workspace fits (0 if none)
       const int64_t mid = (lo + hi + 1) / 2;
