@@ -73,6 +73,42 @@ def test_workspace_sizes_are_host_computable(lib):
     assert lib.stce_state_bytes(10) == 11200
 
 
+def _last_wave_idle(V, n):
+    """Idle fraction of the last wave of one workgroup per compute unit over
+    ceil(V / 256) x n output tiles (256 compute units)."""
+    tiles = -(-V // 256) * n
+    return (-(-tiles // 256) * 256 - tiles) / 256
+
+
+def test_default_chunking(lib):
+    """Default rows per forward chunk (stce_schedule): one chunk up to 4,096
+    rows; else two chunks of about T / 2 rows, a multiple of 256 at most two
+    token tiles above the half, with the least idle compute over the two
+    launches' last waves; more chunks once two buffers of fp32 keys
+    (4 C round_up(V, 4) bytes each) would exceed 12 GB; the fp8 lane keeps
+    256 n rows, n in 12 .. 16 filling whole waves best (3,840 at
+    V = 151,936).  The forward workspace holds the two key buffers."""
+    for T in (1, 300, 4096):
+        assert binding.schedule(_prob(T=T, H=512, V=151936))[0] == T
+    T, V = 16384, 151936
+    C = binding.schedule(_prob(T=T, H=5120, V=V))[0]
+    nt, half = T // 256, T // 512
+    assert C % 256 == 0 and half * 256 <= C <= (half + 2) * 256 and C < T
+    waste = {n: _last_wave_idle(V, n) + _last_wave_idle(V, nt - n) for n in range(half, half + 3)}
+    assert waste[C // 256] == min(waste.values())
+    assert C == 8448                                                   # 33 + 31 token tiles
+    ld = -(-V // 4) * 4
+    assert binding.workspace_bytes(_prob(T=T, H=5120, V=V))[0] >= 2 * 4 * C * ld
+    fp8 = _prob(T=T, H=5120, V=V, dtype=binding.DT_FP8, weight_scale=16)
+    assert binding.schedule(fp8)[0] == 3840
+    # tie-stress shape: two 16,384-row buffers of keys would be 16.9 GB
+    T, V = 32768, 129280
+    C = binding.schedule(_prob(T=T, H=7168, V=V))[0]
+    assert -(-T // C) >= 3 and 2 * 4 * C * (-(-V // 4) * 4) <= 12e9 and C % 256 == 0
+    # an explicit chunk is kept
+    assert binding.schedule(_prob(T=T, H=7168, V=V, chunk_rows=4096))[0] == 4096
+
+
 def test_unsupported_dtype_is_one_actionable_error(lib):
     with pytest.raises(binding.StceError, match="UNSUPPORTED.*dtype 7.*STCE_DT_FP8"):
         binding.workspace_bytes(_prob(dtype=7))
